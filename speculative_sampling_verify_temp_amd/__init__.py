@@ -1,0 +1,253 @@
+"""Speculative-sampling verify step on MI355X (gfx950): Python binding.
+
+A thin ctypes layer over libsdverify.so (the C ABI in include/sd_verify.h).
+It only marshals arguments: torch tensors provide device memory and the
+current HIP stream; every step of the verify runs in the HIP kernels.  There
+is no fallback: if the library is missing, importing this package raises.
+
+Functions mirror the C entry points:
+    verify_sample(...)   -> sd_verify_sample
+    verify_greedy(...)   -> sd_verify_greedy
+    workspace_bytes(...) -> sd_verify_workspace_bytes
+    strerror(code)       -> sd_strerror
+    debug_process_rows(...), debug_uniforms(...)  (test exports)
+"""
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libsdverify.so")
+
+SD_OK, SD_EINVAL, SD_EWORKSPACE, SD_EHIP, SD_EUNSUPPORTED = 0, -1, -2, -3, -4
+SD_F32, SD_BF16 = 0, 1
+SD_NO_BONUS, SD_PENALTY_PRIOR_ONLY = 1, 2
+SD_ST_BAD_K, SD_ST_BAD_TEMP, SD_ST_BAD_DRAFT_ID, SD_ST_NONFINITE = 1, 2, 4, 8
+SD_ST_BAD_PRIOR, SD_ST_Q_ZERO, SD_ST_RESID_ZERO = 16, 32, 64
+SD_ST_INVALID_MASK = 0xF
+SD_NSTAT = 8
+SD_MAX_K = 32
+STAT_NAMES = ("d", "theta", "p_x", "q_x", "pi_x", "u", "v", "S")
+
+
+class SdVerifyArgs(ctypes.Structure):
+    _fields_ = [
+        ("target_logits", ctypes.c_void_p),
+        ("draft_logits", ctypes.c_void_p),
+        ("ld_target", ctypes.c_int64),
+        ("ld_draft", ctypes.c_int64),
+        ("dtype", ctypes.c_int32),
+        ("B", ctypes.c_int32),
+        ("K_max", ctypes.c_int32),
+        ("V", ctypes.c_int32),
+        ("draft_ids", ctypes.c_void_p),
+        ("k_per_row", ctypes.c_void_p),
+        ("temperature", ctypes.c_void_p),
+        ("top_p", ctypes.c_float),
+        ("rep_penalty", ctypes.c_float),
+        ("tv_budget", ctypes.c_float),
+        ("prior_ids", ctypes.c_void_p),
+        ("prior_offsets", ctypes.c_void_p),
+        ("seed", ctypes.c_uint64),
+        ("offset", ctypes.c_uint64),
+        ("flags", ctypes.c_uint32),
+    ]
+
+
+class SdVerifyError(RuntimeError):
+    def __init__(self, code, what):
+        super().__init__(f"{what}: {strerror(code)} ({code})")
+        self.code = code
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            f"{LIB_PATH} is missing: build it with "
+            "`python speculative_sampling_verify_temp_amd/build.py` "
+            "(there is no CPU fallback)")
+    lib = ctypes.CDLL(LIB_PATH)
+    P, I32, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
+    A = ctypes.POINTER(SdVerifyArgs)
+    lib.sd_verify_workspace_bytes.argtypes = [A, ctypes.POINTER(SZ)]
+    lib.sd_verify_workspace_bytes.restype = ctypes.c_int
+    lib.sd_verify_sample.argtypes = [A, P, SZ, P, P, P, P, P]
+    lib.sd_verify_sample.restype = ctypes.c_int
+    lib.sd_verify_greedy.argtypes = [A, P, SZ, P, P, P, P, P]
+    lib.sd_verify_greedy.restype = ctypes.c_int
+    lib.sd_strerror.argtypes = [ctypes.c_int]
+    lib.sd_strerror.restype = ctypes.c_char_p
+    lib.sd_debug_process_rows.argtypes = [A, P, SZ, P, P, P]
+    lib.sd_debug_process_rows.restype = ctypes.c_int
+    lib.sd_debug_run_phase.argtypes = [A, P, SZ, ctypes.c_int, P, P, P, P, P]
+    lib.sd_debug_run_phase.restype = ctypes.c_int
+    lib.sd_debug_uniforms.argtypes = [ctypes.c_uint64, ctypes.c_uint64, I32, I32, P, P, P]
+    lib.sd_debug_uniforms.restype = ctypes.c_int
+    return lib
+
+
+lib = _load()
+
+
+def strerror(code):
+    return lib.sd_strerror(int(code)).decode()
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    import torch
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _dtype_code(t):
+    import torch
+    if t.dtype == torch.float32:
+        return SD_F32
+    if t.dtype in (torch.bfloat16, torch.int16, torch.uint16):
+        return SD_BF16
+    raise TypeError(f"logits must be float32 or bfloat16 (got {t.dtype})")
+
+
+def _rows_ld(t, name):
+    """[B][R][V] tensor with unit element stride and rows packed per request."""
+    if t.dim() != 3 or t.stride(2) != 1 or (t.shape[0] > 1 and t.stride(0) != t.shape[1] * t.stride(1)):
+        raise ValueError(f"{name} must be [B][rows][V] with rows laid out back to back")
+    return t.stride(1) if t.shape[1] > 1 else max(t.stride(1), t.shape[2])
+
+
+def make_args(target, draft, draft_ids, k_per_row=None, temperature=None, top_p=1.0,
+              rep_penalty=1.0, prior_ids=None, prior_offsets=None, tv_budget=0.0,
+              seed=0, offset=0, flags=0):
+    """Fill the C argument struct from tensors (device pointers, strides)."""
+    B, K1, V = target.shape
+    a = SdVerifyArgs()
+    a.target_logits = target.data_ptr()
+    a.ld_target = _rows_ld(target, "target")
+    a.dtype = _dtype_code(target)
+    if draft is not None and draft.numel() > 0:
+        if _dtype_code(draft) != a.dtype:
+            raise TypeError("target and draft logits must share a dtype")
+        a.draft_logits = draft.data_ptr()
+        a.ld_draft = _rows_ld(draft, "draft")
+    else:
+        a.draft_logits = None
+        a.ld_draft = a.ld_target
+    a.B, a.K_max, a.V = B, K1 - 1, V
+    a.draft_ids = draft_ids.data_ptr() if draft_ids is not None and draft_ids.numel() else None
+    a.k_per_row = None if k_per_row is None else k_per_row.data_ptr()
+    a.temperature = None if temperature is None else temperature.data_ptr()
+    a.top_p, a.rep_penalty, a.tv_budget = float(top_p), float(rep_penalty), float(tv_budget)
+    a.prior_ids = None if prior_ids is None else prior_ids.data_ptr()
+    a.prior_offsets = None if prior_offsets is None else prior_offsets.data_ptr()
+    a.seed = int(seed) & (2**64 - 1)
+    a.offset = int(offset) & (2**64 - 1)
+    a.flags = int(flags)
+    return a
+
+
+def workspace_bytes(args):
+    n = ctypes.c_size_t()
+    rc = lib.sd_verify_workspace_bytes(ctypes.byref(args), ctypes.byref(n))
+    if rc != SD_OK:
+        raise SdVerifyError(rc, "sd_verify_workspace_bytes")
+    return n.value
+
+
+def alloc_workspace(args, device):
+    import torch
+    return torch.zeros(max(1, workspace_bytes(args)), dtype=torch.uint8, device=device)
+
+
+def verify_sample(target, draft, draft_ids, k_per_row=None, temperature=None, top_p=1.0,
+                  rep_penalty=1.0, prior_ids=None, prior_offsets=None, tv_budget=0.0,
+                  seed=0, offset=0, flags=0, stats=False, workspace=None, out=None,
+                  stream=None):
+    """Sampling verify on device tensors; returns (accepted, tokens, status, stats).
+
+    out: optional dict of preallocated outputs (accepted, tokens, status, stats).
+    """
+    import torch
+    args = make_args(target, draft, draft_ids, k_per_row, temperature, top_p, rep_penalty,
+                     prior_ids, prior_offsets, tv_budget, seed, offset, flags)
+    dev = target.device
+    B, K1 = args.B, args.K_max + 1
+    if workspace is None:
+        workspace = alloc_workspace(args, dev)
+    o = out or {}
+    acc = o.get("accepted") if o.get("accepted") is not None else torch.empty(B, dtype=torch.int32, device=dev)
+    tok = o.get("tokens") if o.get("tokens") is not None else torch.empty((B, K1), dtype=torch.int32, device=dev)
+    st = o.get("status") if o.get("status") is not None else torch.empty(B, dtype=torch.int32, device=dev)
+    sts = None
+    if stats:
+        sts = o.get("stats") if o.get("stats") is not None else torch.empty((B, K1, SD_NSTAT), dtype=torch.float32, device=dev)
+    rc = lib.sd_verify_sample(ctypes.byref(args), _ptr(workspace), workspace.numel(),
+                              _ptr(acc), _ptr(tok), _ptr(st), _ptr(sts), _stream(stream))
+    if rc != SD_OK:
+        raise SdVerifyError(rc, "sd_verify_sample")
+    return acc, tok, st, sts
+
+
+def verify_greedy(target, draft_ids, k_per_row=None, rep_penalty=1.0, prior_ids=None,
+                  prior_offsets=None, flags=0, workspace=None, argmax=False, out=None,
+                  stream=None):
+    """Greedy verify; returns (accepted, tokens, status, argmax or None)."""
+    import torch
+    args = make_args(target, None, draft_ids, k_per_row, None, 1.0, rep_penalty,
+                     prior_ids, prior_offsets, 0.0, 0, 0, flags)
+    dev = target.device
+    B, K1 = args.B, args.K_max + 1
+    if workspace is None:
+        workspace = alloc_workspace(args, dev)
+    o = out or {}
+    acc = o.get("accepted") if o.get("accepted") is not None else torch.empty(B, dtype=torch.int32, device=dev)
+    tok = o.get("tokens") if o.get("tokens") is not None else torch.empty((B, K1), dtype=torch.int32, device=dev)
+    st = o.get("status") if o.get("status") is not None else torch.empty(B, dtype=torch.int32, device=dev)
+    am = torch.empty((B, K1), dtype=torch.int32, device=dev) if argmax else None
+    rc = lib.sd_verify_greedy(ctypes.byref(args), _ptr(workspace), workspace.numel(),
+                              _ptr(acc), _ptr(tok), _ptr(st), _ptr(am), _stream(stream))
+    if rc != SD_OK:
+        raise SdVerifyError(rc, "sd_verify_greedy")
+    return acc, tok, st, am
+
+
+def debug_process_rows(target, draft, draft_ids, k_per_row=None, temperature=None, top_p=1.0,
+                       rep_penalty=1.0, prior_ids=None, prior_offsets=None, flags=0,
+                       stream=None):
+    """Processed (penalized, tempered, truncated, renormalized) p and q rows."""
+    import torch
+    args = make_args(target, draft, draft_ids, k_per_row, temperature, top_p, rep_penalty,
+                     prior_ids, prior_offsets, 0.0, 0, 0, flags)
+    dev = target.device
+    ws = alloc_workspace(args, dev)
+    B, K1, V = target.shape
+    p = torch.zeros((B, K1, V), dtype=torch.float32, device=dev)
+    q = torch.zeros((B, max(K1 - 1, 0), V), dtype=torch.float32, device=dev)
+    rc = lib.sd_debug_process_rows(ctypes.byref(args), _ptr(ws), ws.numel(), _ptr(p),
+                                   _ptr(q) if q.numel() else None, _stream(stream))
+    if rc != SD_OK:
+        raise SdVerifyError(rc, "sd_debug_process_rows")
+    return p, q
+
+
+def run_phase(args, workspace, phase, accepted, tokens, status=None, stats=None,
+              stream=None):
+    """One phase (0 rows, 1 TV, 2 finalize) of sd_verify_sample, for timing."""
+    rc = lib.sd_debug_run_phase(ctypes.byref(args), _ptr(workspace), workspace.numel(),
+                                int(phase), _ptr(accepted), _ptr(tokens), _ptr(status),
+                                _ptr(stats), _stream(stream))
+    if rc != SD_OK:
+        raise SdVerifyError(rc, "sd_debug_run_phase")
+
+
+def debug_uniforms(seed, offset, B, npos, device="cuda", stream=None):
+    import torch
+    u = torch.empty((B, npos), dtype=torch.float32, device=device)
+    v = torch.empty((B, npos), dtype=torch.float32, device=device)
+    rc = lib.sd_debug_uniforms(int(seed) & (2**64 - 1), int(offset) & (2**64 - 1), B, npos,
+                               _ptr(u), _ptr(v), _stream(stream))
+    if rc != SD_OK:
+        raise SdVerifyError(rc, "sd_debug_uniforms")
+    return u, v
