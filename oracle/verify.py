@@ -32,9 +32,10 @@ Readings where the pages are silent (each is listed in the design doc):
     draft prefix x_0..x_{j-1} (flag PENALTY_PRIOR_ONLY drops the prefix);
   * order of steps: penalty, then division by the row temperature, softmax,
     then top-p and renormalization, for both p and q;
-  * top-p: order tokens by processed logit descending, ties by id ascending
-    (the order of exact probabilities); keep a token iff the probability mass
-    strictly before it is < top_p; top_p = 1 disables truncation;
+  * top-p: keep a token iff the mass of the strictly more probable tokens
+    is < top_p (tokens tied at the boundary are all kept); probabilities
+    are compared through the processed logits; top_p = 1 disables
+    truncation;
   * theta = 1 when d <= D (covers d = 0), else D/d; d is clamped to <= 1;
   * acceptance is tested as u * q(x) < pi(x), equal to u < min(1, pi/q) for
     q(x) > 0, with no division;
@@ -108,26 +109,32 @@ def softmax64(keys, temperature):
 def top_p_filter(keys, p, top_p):
     """Nucleus truncation and renormalization ([SDN] "Warum...": p, q after top-p).
 
-    Order: processed logit descending, id ascending (the order of the exact
-    probabilities, since p is strictly increasing in the processed logit).
-    Keep a token iff the mass strictly before it is < top_p; renormalize.
-    Returns (p_tilde, margin) where margin = min over tokens of
-    |mass_before - top_p| (inf when top_p >= 1, i.e. truncation is off).
+    Reading (the pages give no boundary rule): a token is kept iff the total
+    probability of the tokens that are strictly more probable than it is
+    < top_p.  Probabilities are compared through the processed logits (p is
+    strictly increasing in them), so tokens tied with the boundary token are
+    all kept: the nucleus is the smallest set of the form {x : p(x) >= tau}
+    whose mass reaches top_p, a function of the distribution alone.
+    Returns (p_tilde, margin) where margin = min over distinct logit values of
+    |mass strictly above - top_p| (inf when top_p >= 1: truncation off).
     Parity unpinned by the pages (the boundary rule is a reading); pinned by
-    brute force against a plain enumeration in tests.
+    brute force against a direct O(V^2) enumeration in tests.
     """
     if top_p >= 1.0:
         return p, np.inf
-    ids = np.arange(p.size)
-    order = np.lexsort((ids, -np.asarray(keys, dtype=np.float64)))
-    ps = p[order]
-    before = np.concatenate(([0.0], np.cumsum(ps)[:-1]))
+    k64 = np.asarray(keys, dtype=np.float64)
+    order = np.argsort(-k64, kind="stable")
+    ks, ps = k64[order], p[order]
+    csum = np.concatenate(([0.0], np.cumsum(ps)))
+    # first sorted position of each element's group of equal keys
+    new_group = np.concatenate(([True], ks[1:] != ks[:-1]))
+    group_start = np.maximum.accumulate(np.where(new_group, np.arange(ks.size), 0))
+    above = csum[group_start]
     tp = np.float64(np.float32(top_p))
-    keep_sorted = before < tp
     keep = np.zeros(p.size, dtype=bool)
-    keep[order[keep_sorted]] = True
+    keep[order[above < tp]] = True
     pk = np.where(keep, p, 0.0)
-    margin = float(np.min(np.abs(before - tp)))
+    margin = float(np.min(np.abs(above[new_group] - tp)))
     return pk / pk.sum(), margin
 
 

@@ -4,7 +4,8 @@
 //   k_row_prepare  one workgroup per processed row (target j <= K_r, draft
 //                  j < K_r): penalty -> max M and normalizer Z of
 //                  exp2((key - M) log2e / T); for top-p, an exact radix
-//                  select of the cut over fixed-point masses.
+//                  select of the cut key over fixed-point masses (tokens
+//                  tied with the boundary token are kept).
 //   k_pair_tv      one workgroup per position j < K_r: TV(p_j, q_j) over the
 //                  processed, truncated rows (skipped when theta cannot
 //                  depend on d and no statistics are requested).
@@ -37,8 +38,11 @@ __device__ __forceinline__ int row_index(const Args& a, int r, bool target, int 
   return r * (2 * a.K_max + 1) + (target ? j : a.K_max + 1 + j);
 }
 
+// Top-p membership: every token whose key is at least the cut key is kept
+// (tokens tied at the boundary included).
 __device__ __forceinline__ bool kept(const RowStat& s, uint32_t o, int id) {
-  return s.kord == KEEP_ALL || o > s.kord || (o == s.kord && id <= s.idcut);
+  (void)id;
+  return s.kord == KEEP_ALL || o >= s.kord;
 }
 
 // Block-wide inclusive scan of one uint64 per thread (fixed order).
@@ -104,39 +108,6 @@ __device__ void find_crossing(const uint64_t* hm, const uint32_t* hc, int nbins,
   __syncthreads();
   beta_out = nbins - 1 - pos;
   above_out = sbuf[0];
-  __syncthreads();
-}
-
-// Ascending count scan over id bins: the bin holding the need-th smallest id
-// (1-based need); returns the count of ids in bins below it via below_out.
-template <int NT>
-__device__ void find_count_bin(const uint32_t* hc, int nbins, uint32_t need, int& bin_out,
-                               uint32_t& below_out, uint64_t* sbuf, int* sint) {
-  const int per = nbins >= NT ? nbins / NT : 1;
-  const int t = threadIdx.x;
-  const bool active = t * per < nbins;
-  uint64_t own = 0;
-  if (active)
-    for (int q = 0; q < per; ++q) own += hc[t * per + q];
-  if (t == 0) sint[0] = INT_MAX;
-  const uint64_t incl = block_incl_scan_u64<NT>(own, sbuf);
-  uint64_t run = incl - own;
-  int found = INT_MAX;
-  uint64_t below = 0;
-  if (active)
-    for (int q = 0; q < per; ++q) {
-      const int b = t * per + q;
-      if (run + hc[b] >= need) { found = b; below = run; break; }
-      run += hc[b];
-    }
-  __syncthreads();
-  if (found != INT_MAX) atomicMin(&sint[0], found);
-  __syncthreads();
-  const int b = sint[0];
-  if (found == b) sbuf[0] = below;
-  __syncthreads();
-  bin_out = b;
-  below_out = (uint32_t)sbuf[0];
   __syncthreads();
 }
 
@@ -288,63 +259,12 @@ __global__ __launch_bounds__(NT_ROW) void k_row_prepare(Args a, RowStat* rs, int
     __syncthreads();
     int b3;
     find_crossing<NT>(hmass, hcnt, 256, above, TP, b3, above, su, si);
+    // The cut key's group (all tokens tied at it) is kept whole.
     const uint32_t kord = (pre24 << 8) | (uint32_t)b3;
-    const uint32_t n_tie = hcnt[b3];
-    const uint64_t E = hmass[b3] / n_tie;
-    __syncthreads();
-
-    // Tokens tied at kord are kept in ascending id order while the mass
-    // before them stays below TP.
-    uint32_t t_keep = n_tie;
-    if (E > 0) {
-      double est = ceil((TP - (double)above) / (double)E) - 1.0;
-      uint64_t t = est > 0.0 ? (uint64_t)est : 0;
-      if (t > n_tie) t = n_tie;
-      while (t < n_tie && (double)(above + t * E) < TP) ++t;
-      while (t > 1 && (double)(above + (t - 1) * E) >= TP) --t;
-      t_keep = (uint32_t)(t < 1 ? 1 : t);
-    }
-    int idcut = INT_MAX;
-    if (t_keep < n_tie) {
-      // Level A: id bits [18:9] among the tied tokens; level B: bits [8:0].
-      for (int b = threadIdx.x; b < 1024; b += NT) hcnt[b] = 0;
-      __syncthreads();
-      for (int k = threadIdx.x; k < nvec; k += NT) {
-        float z[VEC];
-        load8<DT>(row, k, V, z);
-        if (pen) apply_penalty8(bm, k, 0, a.rep, z);
-#pragma unroll
-        for (int e = 0; e < VEC; ++e) {
-          const int id = k * VEC + e;
-          if (id < V && ord_key(z[e]) == kord) atomicAdd(&hcnt[id >> 9], 1u);
-        }
-      }
-      __syncthreads();
-      int ba;
-      uint32_t below;
-      find_count_bin<NT>(hcnt, 1024, t_keep, ba, below, su, si);
-      for (int b = threadIdx.x; b < 512; b += NT) hcnt[b] = 0;
-      __syncthreads();
-      const int k0 = (ba << 9) / VEC, k1 = min(nvec, ((ba + 1) << 9) / VEC);
-      for (int k = k0 + threadIdx.x; k < k1; k += NT) {
-        float z[VEC];
-        load8<DT>(row, k, V, z);
-        if (pen) apply_penalty8(bm, k, 0, a.rep, z);
-#pragma unroll
-        for (int e = 0; e < VEC; ++e) {
-          const int id = k * VEC + e;
-          if (id < V && ord_key(z[e]) == kord) atomicAdd(&hcnt[id & 511], 1u);
-        }
-      }
-      __syncthreads();
-      int bb;
-      uint32_t below2;
-      find_count_bin<NT>(hcnt, 512, t_keep - below, bb, below2, su, si);
-      idcut = (ba << 9) | bb;
-    }
     out.kord = kord;
-    out.idcut = idcut;
-    out.Zk = (double)(above + (uint64_t)t_keep * E) * exp2(-(double)sh);
+    out.idcut = INT_MAX;
+    out.Zk = (double)(above + hmass[b3]) * exp2(-(double)sh);
+    __syncthreads();
   }
 
   if (threadIdx.x == 0) {

@@ -37,8 +37,8 @@ struct RowStat {
   float M;        // largest processed key (penalized logit, before 1/T)
   float c;        // log2(e) / T
   double Zk;      // sum over kept tokens of exp2((key - M) * c)
-  uint32_t kord;  // top-p cut: orderable key of the last kept token (KEEP_ALL: none)
-  int32_t idcut;  // tokens with orderable key == kord are kept iff id <= idcut
+  uint32_t kord;  // top-p cut: tokens with orderable key >= kord are kept (KEEP_ALL: none)
+  int32_t idcut;  // unused (kept for layout)
   uint32_t flags; // NONFINITE
   float kx;       // processed key of the draft token x_j (rows j < K_r)
 };

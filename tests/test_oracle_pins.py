@@ -239,9 +239,8 @@ def _topp_bruteforce(keys, p, top_p):
     V = len(p)
     keep = np.zeros(V, bool)
     for k in range(V):
-        before = sum(p[i] for i in range(V)
-                     if keys[i] > keys[k] or (keys[i] == keys[k] and i < k))
-        keep[k] = before < top_p
+        above = sum(p[i] for i in range(V) if keys[i] > keys[k])
+        keep[k] = above < top_p
     pk = np.where(keep, p, 0.0)
     return pk / pk.sum()
 
@@ -265,14 +264,19 @@ def test_top_p_special_cases():
     keys = np.array([1.0, 3.0, 3.0, 2.0], np.float32)
     p = ov.softmax64(keys, 1.0)
     one, _ = ov.top_p_filter(keys, p, 1e-9)
-    assert one.tolist() == [0.0, 1.0, 0.0, 0.0]      # top-1, lowest id among ties
+    assert one.tolist() == [0.0, 0.5, 0.5, 0.0]      # the tied maxima are both kept
+    two, _ = ov.top_p_filter(keys, p, 0.5)
+    assert two.tolist() == [0.0, 0.5, 0.5, 0.0]      # mass above the pair is 0 < 0.5
+    p2 = ov.softmax64(np.array([1.0, 3.0, 2.5, 2.0], np.float32), 1.0)
+    three, _ = ov.top_p_filter(np.array([1.0, 3.0, 2.5, 2.0], np.float32), p2, p2[1] + 1e-12)
+    assert (three > 0).tolist() == [False, True, True, False]
     full, m = ov.top_p_filter(keys, p, 1.0)
     assert np.array_equal(full, p) and m == np.inf
 
 
 def test_tiny_top_p_reduces_sampling_to_greedy():
-    # one-hot p and q: sampling verify with D = 0 and draft ids = argmax q
-    # is greedy verify.
+    # one-hot p and q (continuous logits: no tied maxima): sampling verify
+    # with D = 0 and draft ids = argmax q is greedy verify.
     for seed in range(6):
         w = random_case(seed, B=4, K_max=3, V=50, sigma=2.0, corr=0.9,
                         n_prior=3, rep_penalty=1.3, top_p=1e-7)
