@@ -1,17 +1,25 @@
 // Speculative-sampling verify step on gfx950: kernels and the C ABI.
 //
-// Sampling path, three launches on the caller's stream:
-//   k_row_prepare  one workgroup per processed row (target j <= K_r, draft
-//                  j < K_r): penalty -> max M and normalizer Z of
-//                  exp2((key - M) log2e / T); for top-p, an exact radix
-//                  select of the cut key over fixed-point masses (tokens
-//                  tied with the boundary token are kept).
-//   k_pair_tv      one workgroup per position j < K_r: TV(p_j, q_j) over the
-//                  processed, truncated rows (skipped when theta cannot
-//                  depend on d and no statistics are requested).
-//   k_finalize     one workgroup per request: theta, pi, Philox uniforms,
-//                  acceptance, first rejection, then the inverse-CDF draw of
-//                  the correction or bonus token by a block prefix scan.
+// Single-pass sampling path (bf16 logits, top-p on, V <= 155648), two
+// launches on the caller's stream:
+//   k_pair_fast      one 1024-thread workgroup per position pair (target j,
+//                    draft j) and one per bonus row.  The target row is held
+//                    in registers (19 x 16 bytes per thread); its max,
+//                    normalizer and exact top-p cut come from a histogram of
+//                    bf16 keys.  The draft row streams past it once, building
+//                    its own histogram and saving the draft key of every
+//                    target-nucleus token in LDS.  TV, p(x), q(x), theta,
+//                    pi and the acceptance of position j follow; a rejected
+//                    position draws its correction from the register-held
+//                    data.  Every logit is read from HBM once.  Pairs the
+//                    on-chip path cannot cover (a cut outside the histogram
+//                    window, a huge nucleus, penalized tokens at the cut)
+//                    take the exact multi-pass routines inside the same
+//                    workgroup.
+//   k_fast_finalize  one wave per request: first rejection, emitted tokens,
+//                    status and statistics.
+// General path (fp32, top-p off, larger V), three launches:
+//   k_row_prepare / k_pair_tv / k_finalize built on the same exact routines.
 // Greedy path, two launches: k_greedy_partial (argmax of slices of the
 // target rows) and k_greedy_final (reduce, first mismatch, outputs).
 #include <hip/hip_runtime.h>
@@ -22,109 +30,66 @@
 
 #include "sd_verify.h"
 #include "sdv_device.h"
+#include "sdv_exact.h"
 
 using namespace sdv;
 
 namespace {
 
-constexpr int NT_ROW = 512;                  // row kernels
-constexpr int CHUNK = NT_ROW * VEC;          // logits per block step
-constexpr int HBINS = 4096;                  // radix histogram bins (12 bits)
+constexpr int NT_ROW = 512;                  // general-path row kernels
 constexpr int NT_G = 256;                    // greedy partial kernel
 constexpr int G_SLICE = 8192;                // logits per greedy workgroup
 constexpr int MAX_V = 1 << 19;
+
+// Single-pass kernel geometry.
+constexpr int NT_F = 1024;                   // threads per workgroup
+constexpr int NLOAD = 19;                    // 16-byte target loads per thread
+constexpr int MAXV_FAST = NLOAD * NT_F * VEC;  // 155648 logits
+constexpr int HW = NT_F;                     // histogram window bins (one per thread)
+constexpr int CAPT = 20;                     // target-nucleus slots per lane
+constexpr int PEN_CAP = 512;                 // penalized draft tokens above the floor
+constexpr int PREF = 4;                      // draft loads in flight
+constexpr int Q_HEADROOM = 64;               // draft window bins above the target max
+constexpr int SHP = 40;                      // fixed-point shift of penalized masses
 
 __device__ __forceinline__ int row_index(const Args& a, int r, bool target, int j) {
   return r * (2 * a.K_max + 1) + (target ? j : a.K_max + 1 + j);
 }
 
-// Top-p membership: every token whose key is at least the cut key is kept
-// (tokens tied at the boundary included).
-__device__ __forceinline__ bool kept(const RowStat& s, uint32_t o, int id) {
-  (void)id;
-  return s.kord == KEEP_ALL || o >= s.kord;
-}
-
-// Block-wide inclusive scan of one uint64 per thread (fixed order).
-template <int NT>
-__device__ uint64_t block_incl_scan_u64(uint64_t x, uint64_t* buf) {
-  __syncthreads();
-  buf[threadIdx.x] = x;
-  __syncthreads();
-  for (int o = 1; o < NT; o <<= 1) {
-    const uint64_t y = threadIdx.x >= (unsigned)o ? buf[threadIdx.x - o] : 0;
-    __syncthreads();
-    x += y;
-    buf[threadIdx.x] = x;
-    __syncthreads();
-  }
-  return x;
-}
-
-// Descending scan of histogram bins for the top-p crossing.
-// beta = first non-empty bin (from the top) with above + mass >= TP, or the
-// last non-empty bin if the masses never reach TP.  above_beta = above0 +
-// mass of all bins above beta.  nbins is a multiple of NT or <= NT.
-template <int NT>
-__device__ void find_crossing(const uint64_t* hm, const uint32_t* hc, int nbins,
-                              uint64_t above0, double TP, int& beta_out,
-                              uint64_t& above_out, uint64_t* sbuf, int* sint) {
-  const int per = nbins >= NT ? nbins / NT : 1;
-  const int t = threadIdx.x;
-  const bool active = t * per < nbins;
-  // thread t owns positions [t*per, (t+1)*per) in descending bin order
-  uint64_t own = 0;
-  if (active)
-    for (int q = 0; q < per; ++q) own += hm[nbins - 1 - (t * per + q)];
-  if (t == 0) { sint[0] = INT_MAX; sint[1] = -1; }
-  const uint64_t incl = block_incl_scan_u64<NT>(own, sbuf);
-  const uint64_t excl = incl - own;
-  int first = INT_MAX, lastne = -1;
-  if (active) {
-    uint64_t run = above0 + excl;
-    for (int q = 0; q < per; ++q) {
-      const int pos = t * per + q, b = nbins - 1 - pos;
-      if (hc[b] == 0) continue;
-      lastne = pos;
-      if (first == INT_MAX && (double)(run + hm[b]) >= TP) first = pos;
-      run += hm[b];
-    }
-  }
-  __syncthreads();
-  if (first != INT_MAX) atomicMin(&sint[0], first);
-  if (lastne >= 0) atomicMax(&sint[1], lastne);
-  __syncthreads();
-  int pos = sint[0] != INT_MAX ? sint[0] : sint[1];
-  __syncthreads();
-  // mass above pos: recompute on thread 0 from the owner's exclusive prefix
-  if (t == 0) sint[2] = pos;
-  __syncthreads();
-  pos = sint[2];
-  if (active && pos >= t * per && pos < (t + 1) * per) {
-    uint64_t run = above0 + excl;
-    for (int q = t * per; q < pos; ++q) run += hm[nbins - 1 - q];
-    sbuf[0] = run;   // sbuf is free again after the scan (all reads done)
-  }
-  __syncthreads();
-  beta_out = nbins - 1 - pos;
-  above_out = sbuf[0];
-  __syncthreads();
-}
+__host__ __device__ constexpr size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 // ---------------------------------------------------------------------------
-// k_row_prepare: statistics and top-p cut of one processed row.
+// General path kernels.
 // ---------------------------------------------------------------------------
+
+// LDS of the exact routines after the bitmap: histograms then chunk totals.
+__device__ ExactLds carve_exact(unsigned char* p, double* sd, float* sf, int* si, uint64_t* su) {
+  ExactLds L;
+  L.hmass = reinterpret_cast<uint64_t*>(p);
+  L.hcnt = reinterpret_cast<uint32_t*>(p + HBINS * 8);
+  L.ctot = reinterpret_cast<double*>(p + HBINS * 12);
+  L.su = su;
+  L.sd = sd;
+  L.sf = sf;
+  L.si = si;
+  return L;
+}
+
+size_t exact_lds(int V, int NT) {
+  const int nch = ((V + VEC - 1) / VEC + NT - 1) / NT;
+  return (size_t)HBINS * 12 + (size_t)nch * 8;
+}
+
 template <int DT>
 __global__ __launch_bounds__(NT_ROW) void k_row_prepare(Args a, RowStat* rs, int bm_words) {
   constexpr int NT = NT_ROW;
   extern __shared__ __align__(16) unsigned char smem[];
   uint32_t* bm = reinterpret_cast<uint32_t*>(smem);
-  uint64_t* hmass = reinterpret_cast<uint64_t*>(smem + ((bm_words * 4 + 15) & ~15));
-  uint32_t* hcnt = reinterpret_cast<uint32_t*>(hmass + HBINS);
-  __shared__ double sd[NT / WAVE];
+  __shared__ double sd[NT];
   __shared__ float sf[NT / WAVE];
   __shared__ int si[NT / WAVE + 4];
   __shared__ uint64_t su[NT];
+  const ExactLds L = carve_exact(smem + align_up(bm_words * 4, 16), sd, sf, si, su);
 
   const int nrows = 2 * a.K_max + 1;
   const int r = blockIdx.x / nrows, rho = blockIdx.x % nrows;
@@ -137,140 +102,12 @@ __global__ __launch_bounds__(NT_ROW) void k_row_prepare(Args a, RowStat* rs, int
   if (!(T > 0.0f) || !(T < INFINITY)) return;
   const char* row = is_t ? target_row(a, r, j) : draft_row(a, r, j);
   const float c = 1.4426950408889634f / T;
-  const int V = a.V, nvec = (V + VEC - 1) / VEC;
-  const bool pen = build_penalty_bitmap<NT>(a, r, j, 0, V, bm);
-
-  // Pass 0: max and normalizer (per-thread online rescaling, fp64 totals).
-  float m = -INFINITY;
-  double Z = 0.0;
-  int bad = 0;
-  for (int k = threadIdx.x; k < nvec; k += NT) {
-    float z[VEC];
-    load8<DT>(row, k, V, z);
-    if (pen) apply_penalty8(bm, k, 0, a.rep, z);
-    float vm = -INFINITY;
-#pragma unroll
-    for (int e = 0; e < VEC; ++e) {
-      bad |= nonfinite(z[e]);
-      vm = fmaxf(vm, z[e]);
-    }
-    if (vm > m) {
-      if (m > -INFINITY) Z *= exp2(((double)m - (double)vm) * (double)c);
-      m = vm;
-    }
-    if (m > -INFINITY) {
-      float s[VEC];
-#pragma unroll
-      for (int e = 0; e < VEC; ++e) s[e] = e_rel(z[e], m, c);
-      Z += (double)(((s[0] + s[1]) + (s[2] + s[3])) + ((s[4] + s[5]) + (s[6] + s[7])));
-    }
-  }
-  const float M = block_max<NT>(m, sf);
-  Z = (m > -INFINITY) ? Z * exp2(((double)m - (double)M) * (double)c) : 0.0;
-  const double Zall = block_sum<NT>(Z, sd);
-  bad = block_or<NT>(bad, si);
-  if (!(M > -INFINITY)) bad = 1;
-
-  RowStat out;
-  out.M = M;
-  out.c = c;
-  out.Zk = Zall;
-  out.kord = KEEP_ALL;
-  out.idcut = INT_MAX;
-  out.flags = bad ? NONFINITE : 0;
-  out.kx = 0.0f;
-
-  if (!bad && a.top_p < 1.0f && V > 1) {
-    const int sh = a.fp_shift;
-    const double tp = (double)a.top_p;
-    // Tokens whose key is below L hold at most (1 - top_p)/2 of the mass
-    // together, so the cut lies at or above L; level-1 bins below L's bin are
-    // not histogrammed (they are either fully in or fully out).
-    const double lg = log2((1.0 - tp) * Zall / (2.0 * (double)V));
-    const float L = (float)((double)M + lg / (double)c);
-    const uint32_t binL = (L > -INFINITY) ? (ord_key(L) >> 20) : 0u;
-
-    // Level 1: ord bits [31:20].
-    for (int b = threadIdx.x; b < HBINS; b += NT) { hmass[b] = 0; hcnt[b] = 0; }
-    __syncthreads();
-    uint64_t zfp = 0;
-    for (int k = threadIdx.x; k < nvec; k += NT) {
-      float z[VEC];
-      load8<DT>(row, k, V, z);
-      if (pen) apply_penalty8(bm, k, 0, a.rep, z);
-#pragma unroll
-      for (int e = 0; e < VEC; ++e) {
-        if (k * VEC + e >= V) continue;
-        const uint64_t ef = e_fixed(e_rel(z[e], M, c), sh);
-        zfp += ef;
-        const uint32_t b = ord_key(z[e]) >> 20;
-        if (b >= binL) {
-          atomicAdd(&hcnt[b], 1u);
-          if (ef) atomicAdd(reinterpret_cast<unsigned long long*>(&hmass[b]), (unsigned long long)ef);
-        }
-      }
-    }
-    const uint64_t Zfp = block_sum_u64<NT>(zfp, su);
-    const double TP = tp * (double)Zfp;
-    int b1;
-    uint64_t above;
-    find_crossing<NT>(hmass, hcnt, HBINS, 0, TP, b1, above, su, si);
-
-    // Level 2: ord bits [19:8] among tokens of bin b1.
-    for (int b = threadIdx.x; b < HBINS; b += NT) { hmass[b] = 0; hcnt[b] = 0; }
-    __syncthreads();
-    for (int k = threadIdx.x; k < nvec; k += NT) {
-      float z[VEC];
-      load8<DT>(row, k, V, z);
-      if (pen) apply_penalty8(bm, k, 0, a.rep, z);
-#pragma unroll
-      for (int e = 0; e < VEC; ++e) {
-        if (k * VEC + e >= V) continue;
-        const uint32_t o = ord_key(z[e]);
-        if ((int)(o >> 20) != b1) continue;
-        const uint32_t b = (o >> 8) & 0xFFFu;
-        atomicAdd(&hcnt[b], 1u);
-        const uint64_t ef = e_fixed(e_rel(z[e], M, c), sh);
-        if (ef) atomicAdd(reinterpret_cast<unsigned long long*>(&hmass[b]), (unsigned long long)ef);
-      }
-    }
-    __syncthreads();
-    int b2;
-    find_crossing<NT>(hmass, hcnt, HBINS, above, TP, b2, above, su, si);
-    const uint32_t pre24 = ((uint32_t)b1 << 12) | (uint32_t)b2;
-
-    // Level 3: ord bits [7:0] among tokens with the 24-bit prefix.
-    for (int b = threadIdx.x; b < 256; b += NT) { hmass[b] = 0; hcnt[b] = 0; }
-    __syncthreads();
-    for (int k = threadIdx.x; k < nvec; k += NT) {
-      float z[VEC];
-      load8<DT>(row, k, V, z);
-      if (pen) apply_penalty8(bm, k, 0, a.rep, z);
-#pragma unroll
-      for (int e = 0; e < VEC; ++e) {
-        if (k * VEC + e >= V) continue;
-        const uint32_t o = ord_key(z[e]);
-        if ((o >> 8) != pre24) continue;
-        atomicAdd(&hcnt[o & 0xFFu], 1u);
-        const uint64_t ef = e_fixed(e_rel(z[e], M, c), sh);
-        if (ef) atomicAdd(reinterpret_cast<unsigned long long*>(&hmass[o & 0xFFu]), (unsigned long long)ef);
-      }
-    }
-    __syncthreads();
-    int b3;
-    find_crossing<NT>(hmass, hcnt, 256, above, TP, b3, above, su, si);
-    // The cut key's group (all tokens tied at it) is kept whole.
-    const uint32_t kord = (pre24 << 8) | (uint32_t)b3;
-    out.kord = kord;
-    out.idcut = INT_MAX;
-    out.Zk = (double)(above + hmass[b3]) * exp2(-(double)sh);
-    __syncthreads();
-  }
-
+  const bool pen = build_penalty_bitmap<NT>(a, r, j, 0, a.V, bm);
+  RowStat out = row_stats_dev<DT, NT>(a, row, c, pen, bm, L);
   if (threadIdx.x == 0) {
     if (j < K) {
       const int x = a.ids[(int64_t)r * a.K_max + j];
-      if (x >= 0 && x < V) {
+      if (x >= 0 && x < a.V) {
         float z = load1<DT>(row, x);
         if (pen && ((bm[x >> 5] >> (x & 31)) & 1u)) z = penalize(z, a.rep);
         out.kx = z;
@@ -280,16 +117,14 @@ __global__ __launch_bounds__(NT_ROW) void k_row_prepare(Args a, RowStat* rs, int
   }
 }
 
-// ---------------------------------------------------------------------------
-// k_pair_tv: d_j = TV(p_j, q_j) over the processed, truncated rows.
-// ---------------------------------------------------------------------------
 template <int DT>
-__global__ __launch_bounds__(NT_ROW) void k_pair_tv(Args a, const RowStat* rs, double* dout,
-                                                   int bm_words) {
+__global__ __launch_bounds__(NT_ROW) void k_pair_tv(Args a, const RowStat* rs, double* dout) {
   constexpr int NT = NT_ROW;
   extern __shared__ __align__(16) unsigned char smem[];
   uint32_t* bm = reinterpret_cast<uint32_t*>(smem);
-  __shared__ double sd[NT / WAVE];
+  __shared__ double sd[NT];
+  __shared__ float sf[NT / WAVE];
+  __shared__ int si[NT / WAVE + 4];
   if (a.K_max == 0) return;
   const int r = blockIdx.x / a.K_max, j = blockIdx.x % a.K_max;
   const int K = request_k(a, r);
@@ -301,43 +136,40 @@ __global__ __launch_bounds__(NT_ROW) void k_pair_tv(Args a, const RowStat* rs, d
     if (threadIdx.x == 0) dout[(int64_t)r * a.K_max + j] = 0.0;
     return;
   }
-  const char* trow = target_row(a, r, j);
-  const char* drow = draft_row(a, r, j);
-  const int V = a.V, nvec = (V + VEC - 1) / VEC;
-  const bool pen = build_penalty_bitmap<NT>(a, r, j, 0, V, bm);
-  const float ip = (float)(1.0 / P.Zk), iq = (float)(1.0 / Q.Zk);
-  double acc = 0.0;
-  for (int k = threadIdx.x; k < nvec; k += NT) {
-    float zp[VEC], zq[VEC];
-    load8<DT>(trow, k, V, zp);
-    load8<DT>(drow, k, V, zq);
-    if (pen) {
-      apply_penalty8(bm, k, 0, a.rep, zp);
-      apply_penalty8(bm, k, 0, a.rep, zq);
+  const bool pen = build_penalty_bitmap<NT>(a, r, j, 0, a.V, bm);
+  ExactLds L{};
+  L.sd = sd;
+  L.sf = sf;
+  L.si = si;
+  const double d = pair_tv_dev<DT, NT>(a, target_row(a, r, j), draft_row(a, r, j), P, Q, pen, bm, L);
+  if (threadIdx.x == 0) dout[(int64_t)r * a.K_max + j] = d;
+}
+
+// Request-level checks shared by the finalize kernels.  Returns status bits.
+template <int NT>
+__device__ uint32_t request_status(const Args& a, int r, int K, float T, bool check_temp,
+                                   int* si) {
+  uint32_t st = 0;
+  if (K < 0 || K > a.K_max) st |= SD_ST_BAD_K;
+  if (check_temp && (!(T > 0.0f) || !(T < INFINITY))) st |= SD_ST_BAD_TEMP;
+  int badid = 0, badprior = 0;
+  if (!(st & SD_ST_BAD_K))
+    for (int t = threadIdx.x; t < K; t += NT) {
+      const int x = a.ids[(int64_t)r * a.K_max + t];
+      badid |= (x < 0 || x >= a.V);
     }
-    float s = 0.0f;
-#pragma unroll
-    for (int e = 0; e < VEC; ++e) {
-      const int id = k * VEC + e;
-      const float p = (id < V && kept(P, ord_key(zp[e]), id)) ? e_rel(zp[e], P.M, P.c) * ip : 0.0f;
-      const float q = (id < V && kept(Q, ord_key(zq[e]), id)) ? e_rel(zq[e], Q.M, Q.c) * iq : 0.0f;
-      s += fabsf(p - q);
+  if (a.prior && a.poff) {
+    const int p0 = a.poff[r], p1 = a.poff[r + 1];
+    for (int t = p0 + threadIdx.x; t < p1; t += NT) {
+      const int id = a.prior[t];
+      badprior |= (id < 0 || id >= a.V);
     }
-    acc += (double)s;
   }
-  const double tot = block_sum<NT>(acc, sd);
-  if (threadIdx.x == 0) dout[(int64_t)r * a.K_max + j] = fmin(0.5 * tot, 1.0);
+  if (block_or<NT>(badid, si)) st |= SD_ST_BAD_DRAFT_ID;
+  if (block_or<NT>(badprior, si)) st |= SD_ST_BAD_PRIOR;
+  return st;
 }
 
-// Processed probability of token x from its row statistics, in fp64.
-__device__ __forceinline__ double prob_at(const RowStat& s, float kx, int x, double T) {
-  if (!kept(s, ord_key(kx), x)) return 0.0;
-  return exp(((double)kx - (double)s.M) / T) / s.Zk;
-}
-
-// ---------------------------------------------------------------------------
-// k_finalize: decisions and the correction / bonus draw of one request.
-// ---------------------------------------------------------------------------
 template <int DT>
 __global__ __launch_bounds__(NT_ROW) void k_finalize(Args a, const RowStat* rs, const double* dtv,
                                                     int tv_valid, int bm_words,
@@ -346,47 +178,25 @@ __global__ __launch_bounds__(NT_ROW) void k_finalize(Args a, const RowStat* rs, 
   constexpr int NT = NT_ROW;
   extern __shared__ __align__(16) unsigned char smem[];
   uint32_t* bm = reinterpret_cast<uint32_t*>(smem);
-  double* ctot = reinterpret_cast<double*>(smem + ((bm_words * 4 + 15) & ~15));
-  __shared__ double scan_buf[NT];
+  double* ctot = reinterpret_cast<double*>(smem + align_up(bm_words * 4, 16));
+  __shared__ double sd[NT];
+  __shared__ float sf[NT / WAVE];
   __shared__ int si[NT / WAVE + 4];
-  __shared__ int sh_n;
-  __shared__ int sh_mode;     // 0: residual, 1: bonus / fallback from p_n, 2: none
-  __shared__ double sh_S, sh_t, sh_R;
-  __shared__ int sh_ch;
-  __shared__ int sh_y;
+  __shared__ int sh_n, sh_mode;
   __shared__ uint32_t sh_st;
   __shared__ float sh_stat[(SD_MAX_K + 1) * SD_NSTAT];
 
   const int r = blockIdx.x;
-  const int V = a.V, K1 = a.K_max + 1;
+  const int K1 = a.K_max + 1;
   const int K = request_k(a, r);
   const float T = request_t(a, r);
-
-  // ---- status ----
-  uint32_t st = 0;
-  if (K < 0 || K > a.K_max) st |= SD_ST_BAD_K;
-  if (!(T > 0.0f) || !(T < INFINITY)) st |= SD_ST_BAD_TEMP;
-  int badid = 0, badprior = 0, nonfin = 0;
-  if (!(st & SD_ST_BAD_K))
-    for (int t = threadIdx.x; t < K; t += NT) {
-      const int x = a.ids[(int64_t)r * a.K_max + t];
-      badid |= (x < 0 || x >= V);
-    }
-  if (a.prior && a.poff) {
-    const int p0 = a.poff[r], p1 = a.poff[r + 1];
-    for (int t = p0 + threadIdx.x; t < p1; t += NT) {
-      const int id = a.prior[t];
-      badprior |= (id < 0 || id >= V);
-    }
-  }
+  uint32_t st = request_status<NT>(a, r, K, T, true, si);
+  int nonfin = 0;
   if (!(st & (SD_ST_BAD_K | SD_ST_BAD_TEMP)))
     for (int t = threadIdx.x; t < 2 * K + 1; t += NT) {
       const bool tg = t <= K;
-      const int jj = tg ? t : t - K - 1;
-      nonfin |= (rs[row_index(a, r, tg, jj)].flags & NONFINITE) ? 1 : 0;
+      nonfin |= (rs[row_index(a, r, tg, tg ? t : t - K - 1)].flags & NONFINITE) ? 1 : 0;
     }
-  if (block_or<NT>(badid, si)) st |= SD_ST_BAD_DRAFT_ID;
-  if (block_or<NT>(badprior, si)) st |= SD_ST_BAD_PRIOR;
   if (block_or<NT>(nonfin, si)) st |= SD_ST_NONFINITE;
 
   if (st & SD_ST_INVALID_MASK) {
@@ -400,10 +210,7 @@ __global__ __launch_bounds__(NT_ROW) void k_finalize(Args a, const RowStat* rs, 
     return;
   }
 
-  // ---- decisions (one thread; K <= SD_MAX_K positions) ----
   if (threadIdx.x == 0) {
-    const double Td = (double)T;
-    const double D = (double)a.D;
     int n = K;
     for (int jj = 0; jj <= K; ++jj) {
       float u, v;
@@ -413,145 +220,48 @@ __global__ __launch_bounds__(NT_ROW) void k_finalize(Args a, const RowStat* rs, 
       sv[SD_STAT_U] = u;
       sv[SD_STAT_V] = v;
       if (jj == K) break;
-      const int x = a.ids[(int64_t)r * a.K_max + jj];
       const RowStat P = rs[row_index(a, r, true, jj)], Q = rs[row_index(a, r, false, jj)];
-      const double px = prob_at(P, P.kx, x, Td), qx = prob_at(Q, Q.kx, x, Td);
-      double th;
-      double d = 0.0;
-      if (tv_valid) {
-        d = dtv[(int64_t)r * a.K_max + jj];
-        th = (d <= D) ? 1.0 : D / d;
-      } else {
-        th = (D >= 1.0) ? 1.0 : 0.0;   // D = 0: theta only matters when p = q
-      }
-      const double pix = (1.0 - th) * px + th * qx;
-      if (qx == 0.0) st |= SD_ST_Q_ZERO;
+      const double d = tv_valid ? dtv[(int64_t)r * a.K_max + jj] : 0.0;
+      const Decision dc = decide(P, Q, P.kx, Q.kx, (double)T, (double)a.D, tv_valid != 0, d, u);
+      if (dc.qx == 0.0) st |= SD_ST_Q_ZERO;
       sv[SD_STAT_D] = (float)d;
-      sv[SD_STAT_THETA] = (float)th;
-      sv[SD_STAT_PX] = (float)px;
-      sv[SD_STAT_QX] = (float)qx;
-      sv[SD_STAT_PIX] = (float)pix;
-      if (n == K && !((double)u * qx < pix)) n = jj;
+      sv[SD_STAT_THETA] = (float)dc.th;
+      sv[SD_STAT_PX] = (float)dc.px;
+      sv[SD_STAT_QX] = (float)dc.qx;
+      sv[SD_STAT_PIX] = (float)dc.pix;
+      if (n == K && !dc.accept) n = jj;
     }
     sh_n = n;
     sh_mode = (n < K) ? 0 : ((a.flags & SD_NO_BONUS) ? 2 : 1);
     sh_st = st;
   }
   __syncthreads();
-  const int n = sh_n;
-  int mode = sh_mode;
-
-  // ---- draw: inverse CDF over ascending ids, fp64 block prefix sums ----
+  const int n = sh_n, mode = sh_mode;
+  int y = -1;
   if (mode != 2) {
-    const bool pen = build_penalty_bitmap<NT>(a, r, n, 0, V, bm);
+    const bool pen = build_penalty_bitmap<NT>(a, r, n, 0, a.V, bm);
     const RowStat P = rs[row_index(a, r, true, n)];
-    RowStat Q = P;
-    if (n < K) Q = rs[row_index(a, r, false, n)];
+    const RowStat Q = (n < K) ? rs[row_index(a, r, false, n)] : P;
     const char* trow = target_row(a, r, n);
     const char* drow = (n < K) ? draft_row(a, r, n) : trow;
-    const float ip = (float)(1.0 / P.Zk), iq = (float)(1.0 / Q.Zk);
-    const int nvec = (V + VEC - 1) / VEC;
-    const int nch = (nvec + NT - 1) / NT;
-    const float vn = sh_stat[n * SD_NSTAT + SD_STAT_V];
-
-    auto own_sum = [&](int k, int md, float (&w)[VEC]) -> double {
-      double s = 0.0;
-      if (k < nvec) {
-        float zp[VEC], zq[VEC];
-        load8<DT>(trow, k, V, zp);
-        if (pen) apply_penalty8(bm, k, 0, a.rep, zp);
-        if (md == 0) {
-          load8<DT>(drow, k, V, zq);
-          if (pen) apply_penalty8(bm, k, 0, a.rep, zq);
-        }
-#pragma unroll
-        for (int e = 0; e < VEC; ++e) {
-          const int id = k * VEC + e;
-          float p = (id < V && kept(P, ord_key(zp[e]), id)) ? e_rel(zp[e], P.M, P.c) * ip : 0.0f;
-          if (md == 0) {
-            const float q = (id < V && kept(Q, ord_key(zq[e]), id)) ? e_rel(zq[e], Q.M, Q.c) * iq : 0.0f;
-            p = fmaxf(p - q, 0.0f);
-          }
-          w[e] = p;
-          s += (double)p;
-        }
-      } else {
-#pragma unroll
-        for (int e = 0; e < VEC; ++e) w[e] = 0.0f;
-      }
-      return s;
-    };
-
-    for (int pass = 0; pass < 2; ++pass) {
-      for (int ch = 0; ch < nch; ++ch) {
-        float w[VEC];
-        const double own = own_sum(ch * NT + threadIdx.x, mode, w);
-        const double incl = block_incl_scan<NT>(own, scan_buf);
-        if (threadIdx.x == NT - 1) ctot[ch] = incl;
-      }
-      __syncthreads();
-      if (threadIdx.x == 0) {
-        double S = 0.0;
-        for (int ch = 0; ch < nch; ++ch) S += ctot[ch];
-        sh_S = S;
-        const double t = (double)vn * S;
-        double R = 0.0;
-        int chs = -1, lastpos = -1;
-        double Rlast = 0.0, Racc = 0.0;
-        for (int ch = 0; ch < nch; ++ch) {
-          if (ctot[ch] > 0.0) { lastpos = ch; Rlast = Racc; }
-          if (chs < 0 && Racc + ctot[ch] > t) { chs = ch; R = Racc; }
-          Racc += ctot[ch];
-        }
-        if (chs < 0) { chs = lastpos; R = Rlast; }
-        sh_t = t;
-        sh_R = R;
-        sh_ch = chs;
-      }
-      __syncthreads();
-      if (!(sh_S > 0.0) && mode == 0) {   // zero residual: draw from p_n
-        mode = 1;
-        if (threadIdx.x == 0) sh_st |= SD_ST_RESID_ZERO;
-        __syncthreads();
-        continue;
-      }
-      break;
+    ExactLds L{};
+    L.sd = sd;
+    L.sf = sf;
+    L.si = si;
+    L.ctot = ctot;
+    const Drawn dw = draw_dev<DT, NT>(a, trow, drow, P, Q, mode, sh_stat[n * SD_NSTAT + SD_STAT_V],
+                                      pen, bm, L);
+    y = dw.y;
+    if (threadIdx.x == 0) {
+      sh_stat[n * SD_NSTAT + SD_STAT_S] = (float)dw.S;
+      if (dw.resid_zero) sh_st |= SD_ST_RESID_ZERO;
     }
-
-    if (threadIdx.x == 0) sh_y = -1;
-    if (sh_ch >= 0) {
-      float w[VEC];
-      const int k = sh_ch * NT + threadIdx.x;
-      const double own = own_sum(k, mode, w);
-      const double incl = block_incl_scan<NT>(own, scan_buf);
-      const double prev = threadIdx.x ? scan_buf[threadIdx.x - 1] : 0.0;
-      const double R = sh_R, t = sh_t;
-      __syncthreads();
-      if (threadIdx.x == 0) si[0] = INT_MAX;
-      __syncthreads();
-      if (R + incl > t) atomicMin(&si[0], (int)threadIdx.x);
-      __syncthreads();
-      if ((int)threadIdx.x == si[0]) {
-        double C = R + prev;
-        int y = -1, lastpos = -1;
-        for (int e = 0; e < VEC; ++e) {
-          if (w[e] > 0.0f) lastpos = k * VEC + e;
-          C += (double)w[e];
-          if (C > t) { y = k * VEC + e; break; }
-        }
-        sh_y = (y >= 0) ? y : lastpos;
-      }
-      __syncthreads();
-    }
-    if (threadIdx.x == 0) sh_stat[n * SD_NSTAT + SD_STAT_S] = (float)sh_S;
   }
   __syncthreads();
-
-  // ---- outputs ----
   for (int t = threadIdx.x; t < K1; t += NT) {
     int v = -1;
     if (t < n) v = a.ids[(int64_t)r * a.K_max + t];
-    else if (t == n && mode != 2) v = sh_y;
+    else if (t == n && mode != 2) v = y;
     out_tok[(int64_t)r * K1 + t] = v;
   }
   if (out_stats)
@@ -564,11 +274,783 @@ __global__ __launch_bounds__(NT_ROW) void k_finalize(Args a, const RowStat* rs, 
 }
 
 // ---------------------------------------------------------------------------
-// Debug export of processed rows.
+// Single-pass kernel.
+// ---------------------------------------------------------------------------
+
+struct UnitOut {
+  float d, th, px, qx, pix, u, v, S;
+  int32_t accept, y;
+  uint32_t flags, pad;
+};
+static_assert(sizeof(UnitOut) == 48, "UnitOut layout");
+enum : uint32_t { UO_NONFINITE = 1, UO_QZERO = 2, UO_RESID_ZERO = 4, UO_SLOW = 8, UO_FALLBACK = 16 };
+
+// bf16 value whose 16-bit orderable key is o.
+__device__ __forceinline__ float key_of_ord16(uint32_t o) {
+  const uint32_t b = (o & 0x8000u) ? (o & 0x7FFFu) : (~o & 0xFFFFu);
+  return __uint_as_float(b << 16);
+}
+
+__device__ __forceinline__ uint32_t raw16(const uint4& w, int e) {
+  const uint32_t x = (e >> 1) == 0 ? w.x : (e >> 1) == 1 ? w.y : (e >> 1) == 2 ? w.z : w.w;
+  return (e & 1) ? (x >> 16) : (x & 0xFFFFu);
+}
+
+// Processed keys of the 8 bf16 logits of vector k held in w.
+__device__ __forceinline__ void keys8(const uint4& w, int k, int V, bool pen, const uint32_t* bm,
+                                      float r, float (&z)[VEC]) {
+  const uint32_t u[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    z[2 * e] = __uint_as_float(u[e] << 16);
+    z[2 * e + 1] = __uint_as_float(u[e] & 0xFFFF0000u);
+  }
+  if (k * VEC + VEC > V) {
+#pragma unroll
+    for (int e = 0; e < VEC; ++e)
+      if (k * VEC + e >= V) z[e] = -INFINITY;
+  }
+  if (pen) apply_penalty8(bm, k, 0, r, z);
+}
+
+// 16-bit orderable key of a processed key (top half of ord_key; -0 = +0).
+__device__ __forceinline__ uint32_t ord16f(float z) {
+  const uint32_t u = __float_as_uint(z + 0.0f);
+  return (u ^ ((uint32_t)((int32_t)u >> 31) | 0x80000000u)) >> 16;
+}
+
+// Processed keys of round l (vector k = l * NT_F + lane): tail masking only
+// in rounds that reach past V, penalty only where the bitmap byte is set.
+__device__ __forceinline__ void round_keys(const uint4& w, int l, int k, int V, bool pen,
+                                           const uint32_t* bm, float r, float (&z)[VEC],
+                                           uint32_t& bits) {
+  z[0] = __uint_as_float(w.x << 16);
+  z[1] = __uint_as_float(w.x & 0xFFFF0000u);
+  z[2] = __uint_as_float(w.y << 16);
+  z[3] = __uint_as_float(w.y & 0xFFFF0000u);
+  z[4] = __uint_as_float(w.z << 16);
+  z[5] = __uint_as_float(w.z & 0xFFFF0000u);
+  z[6] = __uint_as_float(w.w << 16);
+  z[7] = __uint_as_float(w.w & 0xFFFF0000u);
+  if ((l + 1) * NT_F * VEC > V) {
+#pragma unroll
+    for (int e = 0; e < VEC; ++e)
+      if (k * VEC + e >= V) z[e] = -INFINITY;
+  }
+  bits = 0u;
+  if (pen) {
+    const int b = k * VEC;
+    bits = (bm[b >> 5] >> (b & 31)) & 0xFFu;
+    if (bits) {
+#pragma unroll
+      for (int e = 0; e < VEC; ++e)
+        if ((bits >> e) & 1u) z[e] = penalize(z[e], r);
+    }
+  }
+}
+
+__device__ __forceinline__ uint32_t pen_bits(bool pen, const uint32_t* bm, int k) {
+  if (!pen) return 0u;
+  const int b = k * VEC;
+  return (bm[b >> 5] >> (b & 31)) & 0xFFu;
+}
+
+// Online max / normalizer update of one 8-logit vector.
+__device__ __forceinline__ void online8(const float (&z)[VEC], float c, float& m, double& Z,
+                                        int& bad) {
+  float vm = -INFINITY;
+#pragma unroll
+  for (int e = 0; e < VEC; ++e) {
+    bad |= nonfinite(z[e]);
+    vm = fmaxf(vm, z[e]);
+  }
+  if (vm > m) {
+    if (m > -INFINITY) Z *= exp2(((double)m - (double)vm) * (double)c);
+    m = vm;
+  }
+  if (m > -INFINITY) {
+    float s[VEC];
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) s[e] = e_rel(z[e], m, c);
+    Z += (double)(((s[0] + s[1]) + (s[2] + s[3])) + ((s[4] + s[5]) + (s[6] + s[7])));
+  }
+}
+
+// Window cut: bin b (one per thread) holds the tokens whose 16-bit key is
+// top - b; unpenalized ones share the bin's exact bf16 key (counts in hc),
+// penalized ones carry fixed-point masses (pm, pc).  Finds the first
+// non-empty bin where the cumulative mass reaches TP.
+struct WCut {
+  int bin;        // -1: the window does not reach TP
+  double zk;      // mass of bins 0..bin
+  int pen_in_bin; // penalized tokens share the crossing bin
+};
+
+template <int NT>
+__device__ WCut window_cut(const uint32_t* hc, const uint64_t* pm, const uint32_t* pc,
+                           uint32_t top, float M, float c, double TP, double* wtot, int* si,
+                           double* sbc) {
+  const int b = threadIdx.x;
+  double mass = 0.0;
+  const uint32_t cnt = hc[b];
+  if (cnt && (uint32_t)b <= top) mass = (double)cnt * (double)e_rel(key_of_ord16(top - b), M, c);
+  mass += (double)pm[b] * 0x1p-40;
+  const double incl = block_incl_scan_fast<NT>(mass, wtot);
+  if (b == 0) si[0] = INT_MAX;
+  __syncthreads();
+  if ((cnt + pc[b]) > 0 && incl >= TP) atomicMin(&si[0], b);
+  __syncthreads();
+  WCut w;
+  w.bin = si[0] == INT_MAX ? -1 : si[0];
+  if (b == w.bin) sbc[0] = incl;
+  __syncthreads();
+  w.zk = w.bin >= 0 ? sbc[0] : 0.0;
+  w.pen_in_bin = w.bin >= 0 ? (int)pc[w.bin] : 0;
+  __syncthreads();
+  return w;
+}
+
+// Unit handled by block u: pairs (r, j) first, then one bonus row per request.
+struct Unit {
+  int r, j;
+  bool bonus;
+};
+
+__device__ __forceinline__ Unit unit_of(const Args& a, int u) {
+  Unit w;
+  const int npairs = a.B * a.K_max;
+  if (u < npairs) {
+    w.r = u / a.K_max;
+    w.j = u % a.K_max;
+    w.bonus = false;
+  } else {
+    w.r = u - npairs;
+    w.j = 0;
+    w.bonus = true;
+  }
+  return w;
+}
+
+// w(i) of one target-nucleus token: mode 0 max(p - q, 0), mode 1 p.
+__device__ __forceinline__ float nucleus_w(float zp, float zq, int mode, float Mp, float ip,
+                                           float kq_cut, float Mq, float iq, float c) {
+  const float pr = e_rel(zp, Mp, c) * ip;
+  if (mode == 1) return pr;
+  const float q = (zq >= kq_cut) ? e_rel(zq, Mq, c) * iq : 0.0f;
+  return fmaxf(pr - q, 0.0f);
+}
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+__global__ __launch_bounds__(NT_F) void k_pair_fast(Args a, UnitOut* uo) {
+  constexpr int NT = NT_F;
+  constexpr int NSLOT = CAPT * NT;
+  constexpr int HIST_P_BYTES = HW * 16;
+  constexpr int REGION_A = (NSLOT * 2 > HIST_P_BYTES) ? NSLOT * 2 : HIST_P_BYTES;
+  __shared__ uint32_t bm[MAXV_FAST / 32];
+  // target histogram before the draft stream, target nucleus keys after it
+  __shared__ __align__(16) unsigned char region_a[REGION_A];
+  __shared__ uint64_t pmq[HW];
+  __shared__ uint32_t hq[HW], pcq[HW];
+  __shared__ uint16_t kq_arr[NSLOT];   // slot (s, lane) at s * NT + lane
+  __shared__ uint8_t pos_arr[NSLOT];   // 8 * round + logit within the lane's 16 bytes
+  __shared__ float penq_key[PEN_CAP];
+  __shared__ double sd[NT];
+  __shared__ double rt[NLOAD + 1];
+  __shared__ double rtw[NLOAD * (NT / WAVE)];
+  __shared__ float sf[NT / WAVE];
+  __shared__ int si[NT / WAVE + 4];
+  __shared__ int s_npen, s_acc;
+  __shared__ double sbc[2];
+  uint64_t* pmp = reinterpret_cast<uint64_t*>(region_a);
+  uint32_t* hp = reinterpret_cast<uint32_t*>(region_a + HW * 8);
+  uint32_t* pcp = reinterpret_cast<uint32_t*>(region_a + HW * 12);
+  uint16_t* kp_arr = reinterpret_cast<uint16_t*>(region_a);
+
+  const int tid = threadIdx.x;
+  const Unit un = unit_of(a, blockIdx.x);
+  const int r = un.r;
+  const bool bonus = un.bonus;
+  const int K = request_k(a, r);
+  if (K < 0 || K > a.K_max) return;
+  const int j = bonus ? K : un.j;
+  if (!bonus && j >= K) return;
+  const float T = request_t(a, r);
+  if (!(T > 0.0f) || !(T < INFINITY)) return;
+  const int V = a.V, nvec = (V + VEC - 1) / VEC;
+  const float c = 1.4426950408889634f / T;
+  const float rep = a.rep;
+  const double tp = (double)a.top_p;
+  const char* trow = target_row(a, r, j);
+  const char* drow = bonus ? trow : draft_row(a, r, j);
+  const uint4* t4 = reinterpret_cast<const uint4*>(trow);
+  const uint4* d4 = reinterpret_cast<const uint4*>(drow);
+
+  // ---- phase A: issue every target load and the first draft loads ----
+  uint4 tr[NLOAD];
+#pragma unroll
+  for (int l = 0; l < NLOAD; ++l) {
+    const int k = l * NT + tid;
+    tr[l] = (k < nvec) ? t4[k] : make_uint4(0u, 0u, 0u, 0u);
+  }
+  uint4 qb[PREF];
+#pragma unroll
+  for (int s = 0; s < PREF; ++s) {
+    const int k = s * NT + tid;
+    qb[s] = (!bonus && k < nvec) ? d4[k] : make_uint4(0u, 0u, 0u, 0u);
+  }
+  const bool pen = build_penalty_bitmap<NT>(a, r, j, 0, V, bm);
+  float u_j, v_j;
+  uniforms(a.seed, a.offset, r, j, u_j, v_j);
+
+  // One pass in load-arrival order: the max, and the normalizer of
+  // exp2(z c - R c) against the lane's first-vector max R (rescaled once to
+  // the row max).  Non-finite data or overflow leave M or Z non-finite, and
+  // such units take the exact route, which classifies them.
+  float m = -INFINITY, Rc = 0.0f;
+  double Z = 0.0;
+#pragma unroll
+  for (int l = 0; l < NLOAD; ++l) {
+    const int k = l * NT + tid;
+    if ((l + 1) * NT * VEC <= V || k < nvec) {
+      float z[VEC];
+      uint32_t bits;
+      round_keys(tr[l], l, k, V, pen, bm, rep, z, bits);
+      const float vm = fmaxf(fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3])),
+                             fmaxf(fmaxf(z[4], z[5]), fmaxf(z[6], z[7])));
+      if (l == 0) Rc = (vm > -INFINITY && vm < INFINITY) ? vm * c : 0.0f;
+      m = fmaxf(m, vm);
+      float s8[VEC];
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) s8[e] = fast_exp2(fmaf(z[e], c, -Rc));
+      Z += (double)(((s8[0] + s8[1]) + (s8[2] + s8[3])) + ((s8[4] + s8[5]) + (s8[6] + s8[7])));
+    }
+  }
+  const float Mp = block_max<NT>(m, sf);
+  const double Zp = block_sum<NT>(Z > 0.0 ? Z * exp2((double)Rc - (double)Mp * (double)c) : 0.0, sd);
+  uint32_t oflags = 0;
+  if (!(Mp > -INFINITY) || !(Mp < INFINITY) || !(Zp > 0.0) || !(Zp < INFINITY)) {
+    oflags = UO_FALLBACK;
+    goto write_out_flags;
+  }
+  {
+  // ---- exact top-p cut of p from a histogram of register-held keys ----
+  // Tokens with exp2((key - M) c) below (1 - top_p) Z / (2V) hold at most
+  // (1 - top_p)/2 of the mass together, so the cut lies above them and they
+  // are not histogrammed.
+  hp[tid] = 0;
+  pcp[tid] = 0;
+  pmp[tid] = 0;
+  hq[tid] = 0;
+  pcq[tid] = 0;
+  pmq[tid] = 0;
+  if (tid == 0) s_npen = 0;
+  __syncthreads();
+  const uint32_t topP = ord16f(Mp);
+  const float Lz = (float)((double)Mp + log2((1.0 - tp) * Zp / (2.0 * (double)V)) / (double)c);
+#pragma unroll
+  for (int l = 0; l < NLOAD; ++l) {
+    const int k = l * NT + tid;
+    if ((l + 1) * NT * VEC <= V || k < nvec) {
+      float z[VEC];
+      uint32_t bits;
+      round_keys(tr[l], l, k, V, pen, bm, rep, z, bits);
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) {
+        if (z[e] >= Lz && !((bits >> e) & 1u)) {
+          const uint32_t b = topP - ord16f(z[e]);
+          if (b < (uint32_t)HW) atomicAdd(&hp[b], 1u);
+        }
+      }
+      if (bits) {   // penalized tokens: off the bf16 grid, carry their masses
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) {
+          if (((bits >> e) & 1u) && z[e] >= Lz) {
+            const uint32_t b = topP - ord16f(z[e]);
+            if (b < (uint32_t)HW) {
+              atomicAdd(&pcp[b], 1u);
+              atomicAdd(reinterpret_cast<unsigned long long*>(&pmp[b]),
+                        (unsigned long long)e_fixed(e_rel(z[e], Mp, c), SHP));
+            }
+          }
+        }
+      }
+    }
+  }
+  __syncthreads();
+  const WCut cp = window_cut<NT>(hp, pmp, pcp, topP, Mp, c, tp * Zp, sd, si, sbc);
+  if (cp.bin < 0 || cp.pen_in_bin) {
+    oflags = UO_FALLBACK;
+    goto write_out_flags;
+  }
+  const float kp_cut = key_of_ord16(topP - (uint32_t)cp.bin);
+  const double Zkp = cp.zk;
+  const float ip = (float)(1.0 / Zkp);
+  __syncthreads();   // region_a switches from the target histogram to nucleus keys
+
+  // ---- phase B: stream the draft row once; every lane files its
+  // target-nucleus tokens (target key, draft key, position) in LDS slots ----
+  // The draft normalizer uses the target max as a fixed reference (one
+  // rescale at the end); the running draft max only serves the floor, which
+  // assumes the smallest possible normalizer (1) and is therefore valid
+  // before the draft max is known.
+  float mq = -INFINITY, Lq = -INFINITY;
+  double Zq = 0.0;
+  int qover = 0, nslot = 0;
+  const uint32_t topQ = topP + Q_HEADROOM;
+  const float Mpc = Mp * c;
+  const float lgq_c = (float)(log2((1.0 - tp) / (2.0 * (double)V)) / (double)c);
+#pragma unroll
+  for (int l = 0; l < NLOAD; ++l) {
+    const uint4 cur = qb[l % PREF];
+    if (l + PREF < NLOAD) {
+      const int k2 = (l + PREF) * NT + tid;
+      qb[l % PREF] = (!bonus && k2 < nvec) ? d4[k2] : make_uint4(0u, 0u, 0u, 0u);
+    }
+    const int k = l * NT + tid;
+    if ((l + 1) * NT * VEC <= V || k < nvec) {
+      float zp[VEC];
+      uint32_t bits;
+      round_keys(tr[l], l, k, V, pen, bm, rep, zp, bits);
+      const uint32_t tw[4] = {tr[l].x, tr[l].y, tr[l].z, tr[l].w};
+      const uint32_t qw[4] = {cur.x, cur.y, cur.z, cur.w};
+      float zq[VEC];
+      if (!bonus) {
+        uint32_t qbits;
+        round_keys(cur, l, k, V, pen, bm, rep, zq, qbits);
+        const float vm = fmaxf(fmaxf(fmaxf(zq[0], zq[1]), fmaxf(zq[2], zq[3])),
+                               fmaxf(fmaxf(zq[4], zq[5]), fmaxf(zq[6], zq[7])));
+        mq = fmaxf(mq, vm);
+        Lq = mq + lgq_c;
+        float s8[VEC];
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) s8[e] = fast_exp2(fmaf(zq[e], c, -Mpc));
+        Zq += (double)(((s8[0] + s8[1]) + (s8[2] + s8[3])) + ((s8[4] + s8[5]) + (s8[6] + s8[7])));
+      }
+      uint32_t nmask = 0u;
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) nmask |= (zp[e] >= kp_cut) ? (1u << e) : 0u;
+      if (nmask) {   // target-nucleus tokens of this vector (a few percent)
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) {
+          if ((nmask >> e) & 1u) {
+            if (nslot < CAPT) {
+              const int sidx = nslot * NT + tid;
+              kp_arr[sidx] = (uint16_t)((e & 1) ? (tw[e >> 1] >> 16) : (tw[e >> 1] & 0xFFFFu));
+              kq_arr[sidx] = (uint16_t)((e & 1) ? (qw[e >> 1] >> 16) : (qw[e >> 1] & 0xFFFFu));
+              pos_arr[sidx] = (uint8_t)(l * VEC + e);
+            }
+            ++nslot;
+          }
+        }
+      }
+      if (!bonus) {
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) {
+          if (zq[e] >= Lq && !((bits >> e) & 1u)) {
+            const uint32_t o16 = ord16f(zq[e]);
+            qover |= (o16 > topQ) ? 1 : 0;
+            const uint32_t b = topQ - o16;
+            if (b < (uint32_t)HW) atomicAdd(&hq[b], 1u);
+          }
+        }
+        if (bits) {   // penalized draft tokens above the floor: exact keys to a list
+#pragma unroll
+          for (int e = 0; e < VEC; ++e) {
+            if (((bits >> e) & 1u) && zq[e] >= Lq) {
+              const uint32_t o16 = ord16f(zq[e]);
+              qover |= (o16 > topQ) ? 1 : 0;
+              if (o16 <= topQ && topQ - o16 < (uint32_t)HW) {
+                const int ix = atomicAdd(&s_npen, 1);
+                if (ix < PEN_CAP) penq_key[ix] = zq[e];
+              }
+            }
+          }
+        }
+      }
+    }
+  }
+
+  const float Mq = block_max<NT>(mq, sf);
+  // sum of exp2(z c - Mp c); relative to the draft max it is scaled once
+  const double Zq_ref = block_sum<NT>(Zq, sd);
+  const double Zqa = Zq_ref * exp2((double)Mpc - (double)Mq * (double)c);
+  const int over = block_or<NT>(qover || nslot > CAPT, si);
+  const int npen = s_npen;
+  // Non-finite draft data, or a fixed reference that overflowed or lost the
+  // whole sum, go to the exact route.
+  const bool ref_ok = bonus || ((Mq > -INFINITY) && (Mq < INFINITY) && Zq_ref > 0x1p-60 &&
+                                Zq_ref < INFINITY);
+  if (over || npen > PEN_CAP || !ref_ok) {
+    oflags = UO_FALLBACK;
+    goto write_out_flags;
+  }
+  float kq_cut = 0.0f, iq = 0.0f;
+  double Zkq = 1.0;
+  if (!bonus) {
+    for (int i = tid; i < npen; i += NT) {
+      const float key = penq_key[i];
+      const uint32_t b = topQ - ord16f(key);
+      atomicAdd(&pcq[b], 1u);
+      atomicAdd(reinterpret_cast<unsigned long long*>(&pmq[b]),
+                (unsigned long long)e_fixed(e_rel(key, Mq, c), SHP));
+    }
+    __syncthreads();
+    const WCut cq = window_cut<NT>(hq, pmq, pcq, topQ, Mq, c, tp * Zqa, sd, si, sbc);
+    if (cq.bin < 0 || cq.pen_in_bin) {
+      oflags = UO_FALLBACK;
+      goto write_out_flags;
+    }
+    kq_cut = key_of_ord16(topQ - (uint32_t)cq.bin);
+    Zkq = cq.zk;
+    iq = (float)(1.0 / Zkq);
+  }
+
+  // Keys of slot s of this lane (penalty re-applied from the bitmap).
+  auto slot_keys = [&](int sidx, float& zp, float& zq, int& id) {
+    const int ps = pos_arr[sidx];
+    id = ((ps >> 3) * NT + tid) * VEC + (ps & 7);
+    zp = __uint_as_float((uint32_t)kp_arr[sidx] << 16);
+    zq = __uint_as_float((uint32_t)kq_arr[sidx] << 16);
+    if (pen && ((bm[id >> 5] >> (id & 31)) & 1u)) {
+      zp = penalize(zp, rep);
+      zq = penalize(zq, rep);
+    }
+  };
+
+  // ---- TV, p(x), q(x), theta, pi, acceptance ----
+  double d = 0.0;
+  if (!bonus) {
+    double acc = 0.0;
+    for (int sl = 0; sl < nslot; ++sl) {
+      float zp, zq;
+      int id;
+      slot_keys(sl * NT + tid, zp, zq, id);
+      acc += (double)nucleus_w(zp, zq, 0, Mp, ip, kq_cut, Mq, iq, c);
+    }
+    d = fmin(block_sum<NT>(acc, sd), 1.0);
+  }
+  UnitOut out;
+  out.d = out.th = out.px = out.qx = out.pix = out.S = 0.0f;
+  out.u = u_j;
+  out.v = v_j;
+  out.accept = 1;
+  out.y = -1;
+  out.flags = 0;
+  out.pad = 0;
+  if (!bonus) {
+    if (tid == 0) {
+      const int x = a.ids[(int64_t)r * a.K_max + j];
+      float kxp = -INFINITY, kxq = -INFINITY;
+      if (x >= 0 && x < V) {
+        kxp = load1<SD_BF16>(trow, x);
+        kxq = load1<SD_BF16>(drow, x);
+        if (pen && ((bm[x >> 5] >> (x & 31)) & 1u)) {
+          kxp = penalize(kxp, rep);
+          kxq = penalize(kxq, rep);
+        }
+      }
+      RowStat P, Q;
+      P.M = Mp; P.c = c; P.Zk = Zkp; P.kord = ord_key(kp_cut);
+      Q.M = Mq; Q.c = c; Q.Zk = Zkq; Q.kord = ord_key(kq_cut);
+      const Decision dc = decide(P, Q, kxp, kxq, (double)T, (double)a.D, true, d, u_j);
+      out.d = (float)d;
+      out.th = (float)dc.th;
+      out.px = (float)dc.px;
+      out.qx = (float)dc.qx;
+      out.pix = (float)dc.pix;
+      out.accept = dc.accept ? 1 : 0;
+      if (dc.qx == 0.0) out.flags |= UO_QZERO;
+      s_acc = out.accept;
+    }
+    __syncthreads();
+    if (s_acc) {
+      if (tid == 0) uo[blockIdx.x] = out;
+      return;
+    }
+  }
+
+  // ---- correction (rejected position) or bonus draw from the nucleus ----
+  // Ascending token ids run over rounds l (ids [8192 l, 8192 l + 8192)), then
+  // lanes, then the 8 logits of a lane; a lane's slots are in round order.
+  int mode = bonus ? 1 : 0;
+  double S = 0.0, t = 0.0, R = 0.0;
+  int lstar = -1;
+  for (int pass = 0; pass < 2; ++pass) {
+    int sl = 0;
+    for (int l = 0; l < NLOAD; ++l) {
+      double s = 0.0;
+      while (sl < nslot && (pos_arr[sl * NT + tid] >> 3) == l) {
+        float zp, zq;
+        int id;
+        slot_keys(sl * NT + tid, zp, zq, id);
+        s += (double)nucleus_w(zp, zq, mode, Mp, ip, kq_cut, Mq, iq, c);
+        ++sl;
+      }
+      s = wave_sum(s);
+      if (tid % WAVE == 0) rtw[l * (NT / WAVE) + tid / WAVE] = s;
+    }
+    __syncthreads();
+    if (tid < NLOAD) {
+      double Rl = 0.0;
+      for (int w = 0; w < NT / WAVE; ++w) Rl += rtw[tid * (NT / WAVE) + w];
+      rt[tid] = Rl;
+    }
+    __syncthreads();
+    S = 0.0;
+    for (int l = 0; l < NLOAD; ++l) S += rt[l];
+    t = (double)v_j * S;
+    double accr = 0.0, alast = 0.0;
+    int last = -1;
+    lstar = -1;
+    for (int l = 0; l < NLOAD; ++l) {
+      if (rt[l] > 0.0) { last = l; alast = accr; }
+      if (lstar < 0 && accr + rt[l] > t) { lstar = l; R = accr; }
+      accr += rt[l];
+    }
+    if (lstar < 0) { lstar = last; R = alast; }
+    __syncthreads();
+    if (!(S > 0.0) && mode == 0) {
+      mode = 1;
+      oflags |= UO_RESID_ZERO;
+      continue;
+    }
+    break;
+  }
+  {
+    // round lstar: lane totals, block scan, then the crossing lane's logits
+    double s = 0.0;
+    int first = -1, cnt = 0;
+    for (int sl = 0; sl < nslot; ++sl) {
+      if ((pos_arr[sl * NT + tid] >> 3) != lstar) continue;
+      if (first < 0) first = sl;
+      ++cnt;
+      float zp, zq;
+      int id;
+      slot_keys(sl * NT + tid, zp, zq, id);
+      s += (double)nucleus_w(zp, zq, mode, Mp, ip, kq_cut, Mq, iq, c);
+    }
+    const double incl = block_incl_scan_fast<NT>(s, sd);
+    if (tid == 0) { si[0] = INT_MAX; si[1] = -1; }
+    __syncthreads();
+    if (lstar >= 0 && R + incl > t) atomicMin(&si[0], tid);
+    __syncthreads();
+    if (tid == si[0]) {
+      double C = R + incl - s;
+      int yy = -1, lastpos = -1;
+      for (int q = 0; q < cnt && yy < 0; ++q) {
+        float zp, zq;
+        int id;
+        slot_keys((first + q) * NT + tid, zp, zq, id);
+        const float wv = nucleus_w(zp, zq, mode, Mp, ip, kq_cut, Mq, iq, c);
+        if (wv > 0.0f) lastpos = id;
+        C += (double)wv;
+        if (C > t) yy = id;
+      }
+      si[1] = yy >= 0 ? yy : lastpos;
+    }
+    __syncthreads();
+    if (tid == 0) {
+      out.y = si[1];
+      out.S = (float)S;
+      out.flags |= oflags;
+      uo[blockIdx.x] = out;
+    }
+    return;
+  }
+  }
+
+write_out_flags:
+  if (tid == 0) {
+    UnitOut o;
+    o.d = o.th = o.px = o.qx = o.pix = o.S = 0.0f;
+    o.u = u_j;
+    o.v = v_j;
+    o.accept = 0;
+    o.y = -1;
+    o.flags = oflags;
+    o.pad = 0;
+    uo[blockIdx.x] = o;
+  }
+}
+
+// Exact multi-pass processing of the units k_pair_fast flagged for it
+// (re-reads their rows); other blocks exit at once.
+__global__ __launch_bounds__(NT_F) void k_pair_fallback(Args a, UnitOut* uo) {
+  constexpr int NT = NT_F;
+  __shared__ uint32_t bm[MAXV_FAST / 32];
+  __shared__ uint64_t hmass[HBINS];
+  __shared__ uint32_t hcnt[HBINS];
+  __shared__ uint64_t su[NT];
+  __shared__ double sd[NT];
+  __shared__ double ctot[64];
+  __shared__ float sf[NT / WAVE];
+  __shared__ int si[NT / WAVE + 4];
+  __shared__ int s_acc;
+  const int tid = threadIdx.x;
+  const Unit un = unit_of(a, blockIdx.x);
+  const int r = un.r;
+  const bool bonus = un.bonus;
+  const int K = request_k(a, r);
+  // Units k_pair_fast skipped (invalid request, position beyond K_r) hold
+  // no output of this call: never act on them.
+  if (K < 0 || K > a.K_max) return;
+  const int j = bonus ? K : un.j;
+  if (!bonus && j >= K) return;
+  const float T = request_t(a, r);
+  if (!(T > 0.0f) || !(T < INFINITY)) return;
+  if (!(uo[blockIdx.x].flags & UO_FALLBACK)) return;
+  const float c = 1.4426950408889634f / T;
+  const char* trow = target_row(a, r, j);
+  const char* drow = bonus ? trow : draft_row(a, r, j);
+  const bool pen = build_penalty_bitmap<NT>(a, r, j, 0, a.V, bm);
+  ExactLds ex;
+  ex.hmass = hmass;
+  ex.hcnt = hcnt;
+  ex.su = su;
+  ex.sd = sd;
+  ex.sf = sf;
+  ex.si = si;
+  ex.ctot = ctot;
+  UnitOut out = uo[blockIdx.x];
+  out.flags = UO_SLOW;
+  out.accept = 1;
+  out.y = -1;
+  const RowStat P = row_stats_dev<SD_BF16, NT>(a, trow, c, pen, bm, ex);
+  if (P.flags & NONFINITE) {
+    if (tid == 0) {
+      out.flags = UO_NONFINITE;
+      uo[blockIdx.x] = out;
+    }
+    return;
+  }
+  if (bonus) {
+    const Drawn dw = draw_dev<SD_BF16, NT>(a, trow, trow, P, P, 1, out.v, pen, bm, ex);
+    if (tid == 0) {
+      out.y = dw.y;
+      out.S = (float)dw.S;
+      uo[blockIdx.x] = out;
+    }
+    return;
+  }
+  const RowStat Q = row_stats_dev<SD_BF16, NT>(a, drow, c, pen, bm, ex);
+  if (Q.flags & NONFINITE) {
+    if (tid == 0) {
+      out.flags = UO_NONFINITE;
+      uo[blockIdx.x] = out;
+    }
+    return;
+  }
+  const double d = pair_tv_dev<SD_BF16, NT>(a, trow, drow, P, Q, pen, bm, ex);
+  if (tid == 0) {
+    const int x = a.ids[(int64_t)r * a.K_max + j];
+    float kxp = -INFINITY, kxq = -INFINITY;
+    if (x >= 0 && x < a.V) {
+      kxp = load1<SD_BF16>(trow, x);
+      kxq = load1<SD_BF16>(drow, x);
+      if (pen && ((bm[x >> 5] >> (x & 31)) & 1u)) {
+        kxp = penalize(kxp, a.rep);
+        kxq = penalize(kxq, a.rep);
+      }
+    }
+    const Decision dc = decide(P, Q, kxp, kxq, (double)T, (double)a.D, true, d, out.u);
+    out.d = (float)d;
+    out.th = (float)dc.th;
+    out.px = (float)dc.px;
+    out.qx = (float)dc.qx;
+    out.pix = (float)dc.pix;
+    out.accept = dc.accept ? 1 : 0;
+    if (dc.qx == 0.0) out.flags |= UO_QZERO;
+    s_acc = out.accept;
+  }
+  __syncthreads();
+  if (!s_acc) {
+    const Drawn dw = draw_dev<SD_BF16, NT>(a, trow, drow, P, Q, 0, out.v, pen, bm, ex);
+    if (tid == 0) {
+      out.y = dw.y;
+      out.S = (float)dw.S;
+      if (dw.resid_zero) out.flags |= UO_RESID_ZERO;
+    }
+  }
+  if (tid == 0) uo[blockIdx.x] = out;
+}
+
+__global__ __launch_bounds__(64) void k_fast_finalize(Args a, const UnitOut* uo, int32_t* out_acc,
+                                                      int32_t* out_tok, uint32_t* out_status,
+                                                      float* out_stats) {
+  constexpr int NT = 64;
+  __shared__ int si[NT / WAVE + 4];
+  const int r = blockIdx.x;
+  const int K1 = a.K_max + 1;
+  const int K = request_k(a, r);
+  const float T = request_t(a, r);
+  uint32_t st = request_status<NT>(a, r, K, T, true, si);
+  const int64_t bonus_idx = (int64_t)a.B * a.K_max + r;
+  int nonfin = 0;
+  if (!(st & (SD_ST_BAD_K | SD_ST_BAD_TEMP))) {
+    for (int t = threadIdx.x; t < K; t += NT)
+      nonfin |= (uo[(int64_t)r * a.K_max + t].flags & UO_NONFINITE) ? 1 : 0;
+    if (threadIdx.x == 0) nonfin |= (uo[bonus_idx].flags & UO_NONFINITE) ? 1 : 0;
+  }
+  if (block_or<NT>(nonfin, si)) st |= SD_ST_NONFINITE;
+  const int64_t base = (int64_t)r * K1;
+  if (st & SD_ST_INVALID_MASK) {
+    for (int t = threadIdx.x; t < K1; t += NT) out_tok[base + t] = -1;
+    if (out_stats)
+      for (int t = threadIdx.x; t < K1 * SD_NSTAT; t += NT) out_stats[base * SD_NSTAT + t] = 0.0f;
+    if (threadIdx.x == 0) {
+      out_acc[r] = -1;
+      if (out_status) out_status[r] = st;
+    }
+    return;
+  }
+  if (threadIdx.x != 0) return;
+  int n = K;
+  for (int jj = 0; jj < K; ++jj) {
+    const UnitOut& o = uo[(int64_t)r * a.K_max + jj];
+    if (o.flags & UO_QZERO) st |= SD_ST_Q_ZERO;
+    if (n == K && !o.accept) n = jj;
+  }
+  const bool emit = !(n == K && (a.flags & SD_NO_BONUS));
+  const UnitOut& src = (n < K) ? uo[(int64_t)r * a.K_max + n] : uo[bonus_idx];
+  if (n < K && (src.flags & UO_RESID_ZERO)) st |= SD_ST_RESID_ZERO;
+  for (int t = 0; t < K1; ++t) {
+    int v = -1;
+    if (t < n) v = a.ids[(int64_t)r * a.K_max + t];
+    else if (t == n && emit) v = src.y;
+    out_tok[base + t] = v;
+  }
+  if (out_stats) {
+    for (int t = 0; t < K1; ++t) {
+      float* sv = out_stats + (base + t) * SD_NSTAT;
+      for (int s = 0; s < SD_NSTAT; ++s) sv[s] = 0.0f;
+      if (t < K) {
+        const UnitOut& o = uo[(int64_t)r * a.K_max + t];
+        sv[SD_STAT_D] = o.d;
+        sv[SD_STAT_THETA] = o.th;
+        sv[SD_STAT_PX] = o.px;
+        sv[SD_STAT_QX] = o.qx;
+        sv[SD_STAT_PIX] = o.pix;
+        sv[SD_STAT_U] = o.u;
+        sv[SD_STAT_V] = o.v;
+      } else if (t == K) {
+        sv[SD_STAT_U] = uo[bonus_idx].u;
+        sv[SD_STAT_V] = uo[bonus_idx].v;
+      }
+      if (t == n && emit) sv[SD_STAT_S] = src.S;
+    }
+  }
+  out_acc[r] = n;
+  if (out_status) out_status[r] = st;
+}
+
+// ---------------------------------------------------------------------------
+// Debug export of processed rows (general-path statistics).
 // ---------------------------------------------------------------------------
 template <int DT>
-__global__ __launch_bounds__(NT_ROW) void k_debug_rows(Args a, const RowStat* rs, int bm_words,
-                                                      float* out_p, float* out_q) {
+__global__ __launch_bounds__(NT_ROW) void k_debug_rows(Args a, const RowStat* rs, float* out_p,
+                                                      float* out_q) {
   constexpr int NT = NT_ROW;
   extern __shared__ __align__(16) unsigned char smem[];
   uint32_t* bm = reinterpret_cast<uint32_t*>(smem);
@@ -596,7 +1078,7 @@ __global__ __launch_bounds__(NT_ROW) void k_debug_rows(Args a, const RowStat* rs
 #pragma unroll
     for (int e = 0; e < VEC; ++e) {
       const int id = k * VEC + e;
-      if (id < V) out[id] = kept(S, ord_key(z[e]), id) ? e_rel(z[e], S.M, S.c) * ip : 0.0f;
+      if (id < V) out[id] = kept(S, ord_key(z[e])) ? e_rel(z[e], S.M, S.c) * ip : 0.0f;
     }
   }
 }
@@ -679,46 +1161,28 @@ __global__ __launch_bounds__(NT_G) void k_greedy_partial(Args a, GPart* parts, i
 __global__ __launch_bounds__(64) void k_greedy_final(Args a, const GPart* parts, int ns,
                                                      int32_t* out_acc, int32_t* out_tok,
                                                      uint32_t* out_status, int32_t* out_argmax) {
+  constexpr int NT = 64;
   __shared__ int g[SD_MAX_K + 1];
-  __shared__ int anynan;
+  __shared__ int si[NT / WAVE + 4];
   const int r = blockIdx.x;
-  const int K1 = a.K_max + 1, V = a.V;
+  const int K1 = a.K_max + 1;
   const int K = request_k(a, r);
-  uint32_t st = 0;
-  if (K < 0 || K > a.K_max) st |= SD_ST_BAD_K;
-  int badid = 0, badprior = 0;
-  if (!st)
-    for (int t = threadIdx.x; t < K; t += 64) {
-      const int x = a.ids[(int64_t)r * a.K_max + t];
-      badid |= (x < 0 || x >= V);
-    }
-  if (a.prior && a.poff) {
-    const int p0 = a.poff[r], p1 = a.poff[r + 1];
-    for (int t = p0 + threadIdx.x; t < p1; t += 64) {
-      const int id = a.prior[t];
-      badprior |= (id < 0 || id >= V);
-    }
-  }
-  if (threadIdx.x == 0) anynan = 0;
-  __syncthreads();
-  if (!st && (int)threadIdx.x <= K) {
+  uint32_t st = request_status<NT>(a, r, K, 1.0f, false, si);
+  int nan = 0;
+  if (!(st & SD_ST_BAD_K) && (int)threadIdx.x <= K) {
     const int jj = threadIdx.x;
     uint32_t bo = 0;
-    int bi = INT_MAX, nan = 0;
+    int bi = INT_MAX;
     for (int s = 0; s < ns; ++s) {
       const GPart p = parts[((int64_t)r * K1 + jj) * ns + s];
       nan |= (int)p.nan;
       if (better(p.ord, p.id, bo, bi)) { bo = p.ord; bi = p.id; }
     }
     g[jj] = bi;
-    if (nan) atomicOr(&anynan, 1);
   }
-  if (__any(badid)) st |= SD_ST_BAD_DRAFT_ID;
-  if (__any(badprior)) st |= SD_ST_BAD_PRIOR;
-  __syncthreads();
-  if (anynan && !(st & SD_ST_BAD_K)) st |= SD_ST_NONFINITE;
+  if (block_or<NT>(nan, si)) st |= SD_ST_NONFINITE;
   if (threadIdx.x != 0) return;
-  int64_t base = (int64_t)r * K1;
+  const int64_t base = (int64_t)r * K1;
   if (st & SD_ST_INVALID_MASK) {
     for (int t = 0; t < K1; ++t) {
       out_tok[base + t] = -1;
@@ -745,10 +1209,8 @@ __global__ __launch_bounds__(64) void k_greedy_final(Args a, const GPart* parts,
 // ---------------------------------------------------------------------------
 // Host side.
 // ---------------------------------------------------------------------------
-size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
-
 struct Layout {
-  size_t rs, dtv, gp, total;
+  size_t rs, dtv, gp, uo, total;
   int ns;
 };
 
@@ -760,6 +1222,7 @@ Layout layout(const sd_verify_args_t* a) {
   L.rs = off;  off = align_up(off + B * (2 * K + 1) * sizeof(RowStat), 256);
   L.dtv = off; off = align_up(off + B * K * sizeof(double), 256);
   L.gp = off;  off = align_up(off + B * (K + 1) * (size_t)L.ns * sizeof(GPart), 256);
+  L.uo = off;  off = align_up(off + B * (K + 1) * sizeof(UnitOut), 256);
   L.total = off;
   return L;
 }
@@ -822,7 +1285,7 @@ Args make_args(const sd_verify_args_t* s) {
 
 int bitmap_words(int V) { return (V + 31) / 32; }
 
-size_t row_lds(int V) { return align_up((size_t)bitmap_words(V) * 4, 16) + HBINS * 12; }
+size_t row_lds(int V) { return align_up((size_t)bitmap_words(V) * 4, 16) + exact_lds(V, NT_ROW); }
 
 size_t fin_lds(int V) {
   const int nch = ((V + VEC - 1) / VEC + NT_ROW - 1) / NT_ROW;
@@ -832,6 +1295,11 @@ size_t fin_lds(int V) {
 int launch_status() {
   const hipError_t e = hipGetLastError();
   return e == hipSuccess ? SD_OK : SD_EHIP;
+}
+
+// The single-pass kernel covers bf16 rows with top-p on and V <= 155648.
+bool use_fast(const Args& a) {
+  return a.dtype == SD_BF16 && a.top_p < 1.0f && a.V <= MAXV_FAST;
 }
 
 template <int DT>
@@ -846,10 +1314,25 @@ bool needs_tv(const Args& a, const float* stats) {
   return stats != nullptr || (a.D > 0.0f && a.D < 1.0f);
 }
 
-// One phase of the sampling path (0: rows, 1: TV, 2: finalize).
+// One phase of the sampling path.  Single-pass path: 0 = k_pair_fast,
+// 1 = k_pair_fallback (exact re-read of flagged units), 2 = k_fast_finalize.  General path: 0 = k_row_prepare,
+// 1 = k_pair_tv (when needed), 2 = k_finalize.
 template <int DT>
 int run_phase(const Args& a, const Layout& L, char* ws, int phase, int32_t* acc, int32_t* tok,
               uint32_t* status, float* stats, hipStream_t st) {
+  if (DT == SD_BF16 && use_fast(a)) {
+    UnitOut* uo = reinterpret_cast<UnitOut*>(ws + L.uo);
+    if (phase == 0) {
+      hipLaunchKernelGGL(k_pair_fast, dim3(a.B * a.K_max + a.B), dim3(NT_F), 0, st, a, uo);
+      return launch_status();
+    }
+    if (phase == 1) {
+      hipLaunchKernelGGL(k_pair_fallback, dim3(a.B * a.K_max + a.B), dim3(NT_F), 0, st, a, uo);
+      return launch_status();
+    }
+    hipLaunchKernelGGL(k_fast_finalize, dim3(a.B), dim3(64), 0, st, a, uo, acc, tok, status, stats);
+    return launch_status();
+  }
   const bool need_tv = needs_tv(a, stats);
   if (phase == 0) return run_prepare<DT>(a, L, ws, st);
   if (phase == 1) {
@@ -857,7 +1340,7 @@ int run_phase(const Args& a, const Layout& L, char* ws, int phase, int32_t* acc,
     hipLaunchKernelGGL(k_pair_tv<DT>, dim3(a.B * a.K_max), dim3(NT_ROW),
                        align_up((size_t)bitmap_words(a.V) * 4, 16), st, a,
                        reinterpret_cast<const RowStat*>(ws + L.rs),
-                       reinterpret_cast<double*>(ws + L.dtv), bitmap_words(a.V));
+                       reinterpret_cast<double*>(ws + L.dtv));
     return launch_status();
   }
   hipLaunchKernelGGL(k_finalize<DT>, dim3(a.B), dim3(NT_ROW), fin_lds(a.V), st, a,
@@ -959,10 +1442,10 @@ int sd_debug_process_rows(const sd_verify_args_t* args, void* workspace, size_t 
   const size_t lds = align_up((size_t)bitmap_words(a.V) * 4, 16);
   if (a.dtype == SD_BF16)
     hipLaunchKernelGGL(k_debug_rows<SD_BF16>, dim3(grid), dim3(NT_ROW), lds, st, a,
-                       reinterpret_cast<const RowStat*>(ws + L.rs), bitmap_words(a.V), out_p, out_q);
+                       reinterpret_cast<const RowStat*>(ws + L.rs), out_p, out_q);
   else
     hipLaunchKernelGGL(k_debug_rows<SD_F32>, dim3(grid), dim3(NT_ROW), lds, st, a,
-                       reinterpret_cast<const RowStat*>(ws + L.rs), bitmap_words(a.V), out_p, out_q);
+                       reinterpret_cast<const RowStat*>(ws + L.rs), out_p, out_q);
   return launch_status();
 }
 

@@ -4,6 +4,7 @@
 #pragma once
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+#include <limits.h>
 #include <math.h>
 
 #include "sd_verify.h"
@@ -125,9 +126,13 @@ __device__ __forceinline__ bool nonfinite(float z) {
   return z != z || z == INFINITY;
 }
 
+// exp2 on the hardware unit (v_exp_f32): results below 2^-126 flush to 0,
+// which only drops tokens whose mass is below 2^-126 of the row max.
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
 // exp2((key - M) * c): the unnormalized probability relative to the row max.
 __device__ __forceinline__ float e_rel(float key, float M, float c) {
-  return exp2f((key - M) * c);
+  return fast_exp2((key - M) * c);
 }
 
 // Fixed-point mass (truncated): deterministic, order-independent sums.
@@ -232,6 +237,58 @@ __device__ int block_or(int x, int* scratch) {
 #pragma unroll
   for (int i = 0; i < NT / WAVE; ++i) s |= scratch[i];
   return s;
+}
+
+// Wave-level inclusive scans (fixed shuffle order).
+__device__ __forceinline__ double wave_incl_scan(double x) {
+  const int l = threadIdx.x % WAVE;
+#pragma unroll
+  for (int o = 1; o < WAVE; o <<= 1) {
+    const double y = __shfl_up(x, o);
+    if (l >= o) x += y;
+  }
+  return x;
+}
+
+__device__ __forceinline__ int wave_incl_scan_int(int x) {
+  const int l = threadIdx.x % WAVE;
+#pragma unroll
+  for (int o = 1; o < WAVE; o <<= 1) {
+    const int y = __shfl_up(x, o);
+    if (l >= o) x += y;
+  }
+  return x;
+}
+
+// Block inclusive scan: wave scans, then the wave totals in order.
+// wtot: NT / WAVE doubles.  Deterministic.
+template <int NT>
+__device__ double block_incl_scan_fast(double x, double* wtot) {
+  const int w = threadIdx.x / WAVE, l = threadIdx.x % WAVE;
+  x = wave_incl_scan(x);
+  __syncthreads();
+  if (l == WAVE - 1) wtot[w] = x;
+  __syncthreads();
+  double off = 0.0;
+  for (int i = 0; i < w; ++i) off += wtot[i];
+  return x + off;
+}
+
+// Block exclusive scan of ints; *total receives the block total.
+template <int NT>
+__device__ int block_excl_scan_int(int x, int* wtot, int* total) {
+  const int w = threadIdx.x / WAVE, l = threadIdx.x % WAVE;
+  const int incl = wave_incl_scan_int(x);
+  __syncthreads();
+  if (l == WAVE - 1) wtot[w] = incl;
+  __syncthreads();
+  int off = 0, tot = 0;
+  for (int i = 0; i < NT / WAVE; ++i) {
+    if (i < w) off += wtot[i];
+    tot += wtot[i];
+  }
+  *total = tot;
+  return off + incl - x;
 }
 
 // Inclusive scan of one double per thread across the block (Hillis-Steele in

@@ -1,0 +1,385 @@
+// Exact row-level building blocks of the verify step, written for one
+// workgroup of NT threads that streams rows from global memory.  They serve
+// the general multi-pass path (any dtype, any V up to 2^19, top-p on or off)
+// and the in-kernel fallback of the single-pass kernel.  Every result is
+// returned to all threads of the block.  Included by sd_verify.hip only.
+#pragma once
+#include "sdv_device.h"
+
+namespace sdv {
+
+constexpr int HBINS = 4096;   // radix histogram bins (12 key bits)
+
+// LDS the exact routines use (carved by the caller).
+struct ExactLds {
+  uint64_t* hmass;   // HBINS
+  uint32_t* hcnt;    // HBINS
+  uint64_t* su;      // NT   (uint64 scan buffer)
+  double* sd;        // NT   (double scan buffer / reduction scratch)
+  float* sf;         // NT / WAVE
+  int* si;           // NT / WAVE + 4
+  double* ctot;      // ceil(nvec / NT) chunk totals of a draw
+};
+
+// Top-p membership: every token whose key is at least the cut key is kept
+// (tokens tied with the boundary token included).
+__device__ __forceinline__ bool kept(const RowStat& s, uint32_t o) {
+  return s.kord == KEEP_ALL || o >= s.kord;
+}
+
+// Processed probability of token x from its row statistics, in fp64.
+__device__ __forceinline__ double prob_at(const RowStat& s, float kx, double T) {
+  if (!kept(s, ord_key(kx))) return 0.0;
+  return exp(((double)kx - (double)s.M) / T) / s.Zk;
+}
+
+template <int NT>
+__device__ uint64_t block_incl_scan_u64(uint64_t x, uint64_t* buf) {
+  __syncthreads();
+  buf[threadIdx.x] = x;
+  __syncthreads();
+  for (int o = 1; o < NT; o <<= 1) {
+    const uint64_t y = threadIdx.x >= (unsigned)o ? buf[threadIdx.x - o] : 0;
+    __syncthreads();
+    x += y;
+    buf[threadIdx.x] = x;
+    __syncthreads();
+  }
+  return x;
+}
+
+// Descending scan of histogram bins for the top-p crossing.
+// beta = first non-empty bin (from the top) with above + mass >= TP, or the
+// last non-empty bin if the masses never reach TP.  above_out = above0 +
+// mass of all bins above beta.  nbins is a multiple of NT or <= NT.
+template <int NT>
+__device__ void find_crossing(const uint64_t* hm, const uint32_t* hc, int nbins,
+                              uint64_t above0, double TP, int& beta_out,
+                              uint64_t& above_out, uint64_t* sbuf, int* sint) {
+  const int per = nbins >= NT ? nbins / NT : 1;
+  const int t = threadIdx.x;
+  const bool active = t * per < nbins;
+  uint64_t own = 0;
+  if (active)
+    for (int q = 0; q < per; ++q) own += hm[nbins - 1 - (t * per + q)];
+  if (t == 0) { sint[0] = INT_MAX; sint[1] = -1; }
+  const uint64_t incl = block_incl_scan_u64<NT>(own, sbuf);
+  const uint64_t excl = incl - own;
+  int first = INT_MAX, lastne = -1;
+  if (active) {
+    uint64_t run = above0 + excl;
+    for (int q = 0; q < per; ++q) {
+      const int pos = t * per + q, b = nbins - 1 - pos;
+      if (hc[b] == 0) continue;
+      lastne = pos;
+      if (first == INT_MAX && (double)(run + hm[b]) >= TP) first = pos;
+      run += hm[b];
+    }
+  }
+  __syncthreads();
+  if (first != INT_MAX) atomicMin(&sint[0], first);
+  if (lastne >= 0) atomicMax(&sint[1], lastne);
+  __syncthreads();
+  const int pos = sint[0] != INT_MAX ? sint[0] : sint[1];
+  if (active && pos >= t * per && pos < (t + 1) * per) {
+    uint64_t run = above0 + excl;
+    for (int q = t * per; q < pos; ++q) run += hm[nbins - 1 - q];
+    sbuf[0] = run;   // the scan's reads of sbuf are complete
+  }
+  __syncthreads();
+  beta_out = nbins - 1 - pos;
+  above_out = sbuf[0];
+  __syncthreads();
+}
+
+// Statistics and top-p cut of one processed row, streaming it from global
+// memory: pass 0 gives the max M and Z = sum exp2((key - M) c) (online per
+// thread, fp64 totals); with top-p, three histogram passes over 12 + 12 + 8
+// bits of the orderable key with fixed-point masses find the cut key.
+template <int DT, int NT>
+__device__ RowStat row_stats_dev(const Args& a, const char* row, float c, bool pen,
+                                 const uint32_t* bm, const ExactLds& L) {
+  const int V = a.V, nvec = (V + VEC - 1) / VEC;
+  float m = -INFINITY;
+  double Z = 0.0;
+  int bad = 0;
+  for (int k = threadIdx.x; k < nvec; k += NT) {
+    float z[VEC];
+    load8<DT>(row, k, V, z);
+    if (pen) apply_penalty8(bm, k, 0, a.rep, z);
+    float vm = -INFINITY;
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) {
+      bad |= nonfinite(z[e]);
+      vm = fmaxf(vm, z[e]);
+    }
+    if (vm > m) {
+      if (m > -INFINITY) Z *= exp2(((double)m - (double)vm) * (double)c);
+      m = vm;
+    }
+    if (m > -INFINITY) {
+      float s[VEC];
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) s[e] = e_rel(z[e], m, c);
+      Z += (double)(((s[0] + s[1]) + (s[2] + s[3])) + ((s[4] + s[5]) + (s[6] + s[7])));
+    }
+  }
+  const float M = block_max<NT>(m, L.sf);
+  Z = (m > -INFINITY) ? Z * exp2(((double)m - (double)M) * (double)c) : 0.0;
+  const double Zall = block_sum<NT>(Z, L.sd);
+  bad = block_or<NT>(bad, L.si);
+  if (!(M > -INFINITY)) bad = 1;
+
+  RowStat out;
+  out.M = M;
+  out.c = c;
+  out.Zk = Zall;
+  out.kord = KEEP_ALL;
+  out.idcut = INT_MAX;
+  out.flags = bad ? NONFINITE : 0;
+  out.kx = 0.0f;
+  if (bad || !(a.top_p < 1.0f) || V <= 1) return out;
+
+  const int sh = a.fp_shift;
+  const double tp = (double)a.top_p;
+  // Tokens whose key is below L hold at most (1 - top_p)/2 of the mass
+  // together, so the cut lies at or above L; level-1 bins below L's bin are
+  // not histogrammed (they are either fully in or fully out).
+  const double lg = log2((1.0 - tp) * Zall / (2.0 * (double)V));
+  const float Lk = (float)((double)M + lg / (double)c);
+  const uint32_t binL = (Lk > -INFINITY) ? (ord_key(Lk) >> 20) : 0u;
+
+  // Level 1: ord bits [31:20].
+  for (int b = threadIdx.x; b < HBINS; b += NT) { L.hmass[b] = 0; L.hcnt[b] = 0; }
+  __syncthreads();
+  uint64_t zfp = 0;
+  for (int k = threadIdx.x; k < nvec; k += NT) {
+    float z[VEC];
+    load8<DT>(row, k, V, z);
+    if (pen) apply_penalty8(bm, k, 0, a.rep, z);
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) {
+      if (k * VEC + e >= V) continue;
+      const uint64_t ef = e_fixed(e_rel(z[e], M, c), sh);
+      zfp += ef;
+      const uint32_t b = ord_key(z[e]) >> 20;
+      if (b >= binL) {
+        atomicAdd(&L.hcnt[b], 1u);
+        if (ef) atomicAdd(reinterpret_cast<unsigned long long*>(&L.hmass[b]), (unsigned long long)ef);
+      }
+    }
+  }
+  const uint64_t Zfp = block_sum_u64<NT>(zfp, L.su);
+  const double TP = tp * (double)Zfp;
+  int b1;
+  uint64_t above;
+  find_crossing<NT>(L.hmass, L.hcnt, HBINS, 0, TP, b1, above, L.su, L.si);
+
+  // Level 2: ord bits [19:8] among tokens of bin b1.
+  for (int b = threadIdx.x; b < HBINS; b += NT) { L.hmass[b] = 0; L.hcnt[b] = 0; }
+  __syncthreads();
+  for (int k = threadIdx.x; k < nvec; k += NT) {
+    float z[VEC];
+    load8<DT>(row, k, V, z);
+    if (pen) apply_penalty8(bm, k, 0, a.rep, z);
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) {
+      if (k * VEC + e >= V) continue;
+      const uint32_t o = ord_key(z[e]);
+      if ((int)(o >> 20) != b1) continue;
+      const uint32_t b = (o >> 8) & 0xFFFu;
+      atomicAdd(&L.hcnt[b], 1u);
+      const uint64_t ef = e_fixed(e_rel(z[e], M, c), sh);
+      if (ef) atomicAdd(reinterpret_cast<unsigned long long*>(&L.hmass[b]), (unsigned long long)ef);
+    }
+  }
+  __syncthreads();
+  int b2;
+  find_crossing<NT>(L.hmass, L.hcnt, HBINS, above, TP, b2, above, L.su, L.si);
+  const uint32_t pre24 = ((uint32_t)b1 << 12) | (uint32_t)b2;
+
+  // Level 3: ord bits [7:0] among tokens with the 24-bit prefix.
+  for (int b = threadIdx.x; b < 256; b += NT) { L.hmass[b] = 0; L.hcnt[b] = 0; }
+  __syncthreads();
+  for (int k = threadIdx.x; k < nvec; k += NT) {
+    float z[VEC];
+    load8<DT>(row, k, V, z);
+    if (pen) apply_penalty8(bm, k, 0, a.rep, z);
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) {
+      if (k * VEC + e >= V) continue;
+      const uint32_t o = ord_key(z[e]);
+      if ((o >> 8) != pre24) continue;
+      atomicAdd(&L.hcnt[o & 0xFFu], 1u);
+      const uint64_t ef = e_fixed(e_rel(z[e], M, c), sh);
+      if (ef) atomicAdd(reinterpret_cast<unsigned long long*>(&L.hmass[o & 0xFFu]), (unsigned long long)ef);
+    }
+  }
+  __syncthreads();
+  int b3;
+  find_crossing<NT>(L.hmass, L.hcnt, 256, above, TP, b3, above, L.su, L.si);
+  // The cut key's group (all tokens tied at it) is kept whole.
+  out.kord = (pre24 << 8) | (uint32_t)b3;
+  out.Zk = (double)(above + L.hmass[b3]) * exp2(-(double)sh);
+  __syncthreads();
+  return out;
+}
+
+// d = TV(p, q) = 1/2 sum |p - q| over the processed, truncated rows.
+template <int DT, int NT>
+__device__ double pair_tv_dev(const Args& a, const char* trow, const char* drow,
+                              const RowStat& P, const RowStat& Q, bool pen,
+                              const uint32_t* bm, const ExactLds& L) {
+  const int V = a.V, nvec = (V + VEC - 1) / VEC;
+  const float ip = (float)(1.0 / P.Zk), iq = (float)(1.0 / Q.Zk);
+  double acc = 0.0;
+  for (int k = threadIdx.x; k < nvec; k += NT) {
+    float zp[VEC], zq[VEC];
+    load8<DT>(trow, k, V, zp);
+    load8<DT>(drow, k, V, zq);
+    if (pen) {
+      apply_penalty8(bm, k, 0, a.rep, zp);
+      apply_penalty8(bm, k, 0, a.rep, zq);
+    }
+    float s = 0.0f;
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) {
+      const int id = k * VEC + e;
+      const float p = (id < V && kept(P, ord_key(zp[e]))) ? e_rel(zp[e], P.M, P.c) * ip : 0.0f;
+      const float q = (id < V && kept(Q, ord_key(zq[e]))) ? e_rel(zq[e], Q.M, Q.c) * iq : 0.0f;
+      s += fabsf(p - q);
+    }
+    acc += (double)s;
+  }
+  return fmin(0.5 * block_sum<NT>(acc, L.sd), 1.0);
+}
+
+struct Drawn {
+  int y;
+  double S;
+  int resid_zero;
+};
+
+// Inverse-CDF draw over ascending token ids with fp64 block prefix sums:
+// mode 0 draws from max(p - q, 0) (falling back to p when that has no
+// mass), mode 1 from p.  Two streaming passes give the chunk totals, then
+// the chunk holding t = v * S is read once more and scanned.
+template <int DT, int NT>
+__device__ Drawn draw_dev(const Args& a, const char* trow, const char* drow, const RowStat& P,
+                          const RowStat& Q, int mode, float v, bool pen, const uint32_t* bm,
+                          const ExactLds& L) {
+  const int V = a.V, nvec = (V + VEC - 1) / VEC;
+  const int nch = (nvec + NT - 1) / NT;
+  const float ip = (float)(1.0 / P.Zk), iq = (float)(1.0 / Q.Zk);
+  Drawn out;
+  out.resid_zero = 0;
+
+  auto own_sum = [&](int k, int md, float (&w)[VEC]) -> double {
+    double s = 0.0;
+    if (k < nvec) {
+      float zp[VEC], zq[VEC];
+      load8<DT>(trow, k, V, zp);
+      if (pen) apply_penalty8(bm, k, 0, a.rep, zp);
+      if (md == 0) {
+        load8<DT>(drow, k, V, zq);
+        if (pen) apply_penalty8(bm, k, 0, a.rep, zq);
+      }
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) {
+        const int id = k * VEC + e;
+        float p = (id < V && kept(P, ord_key(zp[e]))) ? e_rel(zp[e], P.M, P.c) * ip : 0.0f;
+        if (md == 0) {
+          const float q = (id < V && kept(Q, ord_key(zq[e]))) ? e_rel(zq[e], Q.M, Q.c) * iq : 0.0f;
+          p = fmaxf(p - q, 0.0f);
+        }
+        w[e] = p;
+        s += (double)p;
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) w[e] = 0.0f;
+    }
+    return s;
+  };
+
+  double S = 0.0, t = 0.0, R = 0.0;
+  int chs = -1;
+  for (int pass = 0; pass < 2; ++pass) {
+    for (int ch = 0; ch < nch; ++ch) {
+      float w[VEC];
+      const double own = own_sum(ch * NT + threadIdx.x, mode, w);
+      const double incl = block_incl_scan<NT>(own, L.sd);
+      if (threadIdx.x == NT - 1) L.ctot[ch] = incl;
+    }
+    __syncthreads();
+    // every thread reads the same totals in the same order
+    S = 0.0;
+    for (int ch = 0; ch < nch; ++ch) S += L.ctot[ch];
+    t = (double)v * S;
+    double Racc = 0.0, Rlast = 0.0;
+    int lastpos = -1;
+    chs = -1;
+    for (int ch = 0; ch < nch; ++ch) {
+      if (L.ctot[ch] > 0.0) { lastpos = ch; Rlast = Racc; }
+      if (chs < 0 && Racc + L.ctot[ch] > t) { chs = ch; R = Racc; }
+      Racc += L.ctot[ch];
+    }
+    if (chs < 0) { chs = lastpos; R = Rlast; }
+    __syncthreads();
+    if (!(S > 0.0) && mode == 0) {   // zero residual: draw from p
+      mode = 1;
+      out.resid_zero = 1;
+      continue;
+    }
+    break;
+  }
+  out.S = S;
+  out.y = -1;
+  if (chs >= 0) {
+    float w[VEC];
+    const int k = chs * NT + threadIdx.x;
+    const double own = own_sum(k, mode, w);
+    const double incl = block_incl_scan<NT>(own, L.sd);
+    const double prev = threadIdx.x ? L.sd[threadIdx.x - 1] : 0.0;
+    __syncthreads();
+    if (threadIdx.x == 0) { L.si[0] = INT_MAX; L.si[1] = -1; }
+    __syncthreads();
+    if (R + incl > t) atomicMin(&L.si[0], (int)threadIdx.x);
+    __syncthreads();
+    if ((int)threadIdx.x == L.si[0]) {
+      double C = R + prev;
+      int y = -1, lastpos = -1;
+      for (int e = 0; e < VEC; ++e) {
+        if (w[e] > 0.0f) lastpos = k * VEC + e;
+        C += (double)w[e];
+        if (C > t) { y = k * VEC + e; break; }
+      }
+      L.si[1] = (y >= 0) ? y : lastpos;
+    }
+    __syncthreads();
+    out.y = L.si[1];
+    __syncthreads();
+  }
+  return out;
+}
+
+// theta, pi(x), the acceptance test of one position (one thread).
+struct Decision {
+  double px, qx, th, pix;
+  bool accept;
+};
+
+__device__ __forceinline__ Decision decide(const RowStat& P, const RowStat& Q, float kxp,
+                                           float kxq, double T, double D, bool tv_valid,
+                                           double d, float u) {
+  Decision o;
+  o.px = prob_at(P, kxp, T);
+  o.qx = prob_at(Q, kxq, T);
+  if (tv_valid) o.th = (d <= D) ? 1.0 : D / d;
+  else o.th = (D >= 1.0) ? 1.0 : 0.0;   // D = 0: theta only matters when p = q
+  o.pix = (1.0 - o.th) * o.px + o.th * o.qx;
+  o.accept = (double)u * o.qx < o.pix;
+  return o;
+}
+
+}  // namespace sdv

@@ -295,3 +295,23 @@ def test_gpu_chi_square_law():
         assert ss.chisquare(np.bincount(first, minlength=4), N * pis[0]).pvalue > 1e-4
         exp_n = N * np.array([1 - al[0], al[0] * (1 - al[1]), al[0] * al[1]])
         assert ss.chisquare(np.bincount(a, minlength=3), exp_n).pvalue > 1e-4
+
+
+def test_single_pass_fallback_routes():
+    """bf16 + top-p cases that the single-pass kernel hands to its exact
+    fallback: a flat distribution (nucleus larger than the per-lane slots), a
+    draft far above the target (draft window overflow), and heavy penalty
+    sets (penalized tokens near the cut)."""
+    tot = [0, 0]
+    flat = wl.random_case(41, B=3, K_max=2, V=60000, dtype="bf16", sigma=0.05, top_p=0.9, D=0.4)
+    shifted = wl.random_case(42, B=3, K_max=2, V=30000, dtype="bf16", sigma=2.0, top_p=0.9, D=0.4)
+    d = shifted.draft_f32() + 40.0
+    shifted.draft[:] = wl.f32_to_bf16_bits(d)
+    heavy = wl.random_case(43, B=4, K_max=3, V=20000, dtype="bf16", sigma=3.0, top_p=0.95,
+                           n_prior=3000, rep_penalty=1.5, D=0.3)
+    for w in (flat, shifted, heavy):
+        c, f = compare_sample(gpu_sample(w), oracle_sample(w), w)
+        tot[0] += c
+        tot[1] += f
+    print(f"fallback routes: checked {tot[0]}, near-tie {tot[1]}")
+    assert tot[0] >= 4
