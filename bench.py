@@ -12,8 +12,19 @@ phases on torch's current stream so the dominant kernel can be bracketed by
 HIP events inside the timed region.  Prints one JSON line.
 
     python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--no-cpu-baseline]
+                    [--copy-probe BYTES]
+
+`roofline.traffic` is the dominant kernel's HBM bytes per launch from two
+rocprofv3 counter runs (FETCH_SIZE, then WRITE_SIZE) of this script with
+--copy-probe, which runs one plain streaming kernel over BYTES (read BYTES,
+write BYTES) before the warmup so the same counters can be scaled to the
+bytes that kernel is known to move.  `python bench.py --digest-pmc FETCH_CSV WRITE_CSV` turns the two
+counter files into the traffic record; the record names a hash of the kernel
+sources and is ignored (traffic null) once they change.
 """
 import argparse
+import csv
+import hashlib
 import json
 import os
 import platform
@@ -25,7 +36,90 @@ sys.path.insert(0, ROOT)
 
 METRIC = "verified draft positions/sec at V=152064 + achieved HBM GB/s vs peak"
 PEAK_HBM_GBPS = 8000.0
-PHASE_NAMES = ("k_row_prepare", "k_pair_tv", "k_finalize")
+CSRC = os.path.join(ROOT, "speculative_sampling_verify_temp_amd", "csrc")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_k_pair_fast_256x8_V152064.json")
+COPY_KERNEL = "bitwise_not"   # the calibration kernel: reads N bytes, writes N bytes
+WORKLOAD = ("256 requests x K=8, V=152064, bf16 logits, T~U[0.5,1], top-p 0.9, "
+            "penalty 1.1 (128 prior ids + draft prefix), TV budget 0.75")
+
+
+def source_hash():
+    """sha256 over the kernel sources, in name order."""
+    h = hashlib.sha256()
+    for n in sorted(os.listdir(CSRC)):
+        if n.endswith((".hip", ".h")):
+            h.update(n.encode())
+            h.update(open(os.path.join(CSRC, n), "rb").read())
+    return h.hexdigest()
+
+
+def algorithmic_bytes(kernel, w):
+    """Bytes the kernel must move per launch by definition of its work.
+
+    The single-pass kernel and the general row pass read every logit row of
+    the call once; the general TV pass reads the 2K draft-position rows of
+    each request; the fallback re-read, finalize and draw kernels read no
+    logit row unconditionally.
+    """
+    if kernel in ("k_pair_fast", "k_row_prepare"):
+        return w.logit_bytes()
+    if kernel == "k_pair_tv":
+        return 2 * w.K_max * w.V * 2 * w.B
+    return 0
+
+
+def read_counters(path, counter, kernel):
+    """Per-dispatch values of `counter` for the kernels whose name contains
+    `kernel` (rocprofv3 counter CSV)."""
+    out = []
+    with open(path, newline="") as f:
+        for row in csv.DictReader(f):
+            if row["Counter_Name"] == counter and kernel in row["Kernel_Name"]:
+                out.append(float(row["Counter_Value"]))
+    if not out:
+        raise SystemExit(f"no {counter} records for a kernel named like {kernel!r} in {path}")
+    return out
+
+
+def digest_pmc(fetch_csv, write_csv, copy_bytes, out_path):
+    """Traffic record of k_pair_fast from FETCH_SIZE / WRITE_SIZE runs (KiB)."""
+    import numpy as np
+    med = lambda path, ctr, k: float(np.median(read_counters(path, ctr, k)))  # noqa: E731
+    cf, cw = med(fetch_csv, "FETCH_SIZE", COPY_KERNEL), med(write_csv, "WRITE_SIZE", COPY_KERNEL)
+    kf = med(fetch_csv, "FETCH_SIZE", "k_pair_fast(")
+    kw = med(write_csv, "WRITE_SIZE", "k_pair_fast(")
+    sf, sw = copy_bytes / (cf * 1024.0), copy_bytes / (cw * 1024.0)
+    rec = {
+        "kernel": "k_pair_fast", "workload": WORKLOAD, "source_sha256": source_hash(),
+        "copy_kernel": COPY_KERNEL, "copy_bytes": copy_bytes,
+        "copy_fetch_kib": cf, "copy_write_kib": cw,
+        "fetch_scale": sf, "write_scale": sw,
+        "kernel_fetch_kib": kf, "kernel_write_kib": kw,
+        "traffic_bytes": kf * 1024.0 * sf + kw * 1024.0 * sw,
+        "commands": [
+            f"rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/pmc_fetch -o run "
+            f"-- python3 bench.py --steps 3 --warmup 1 --no-cpu-baseline --copy-probe {copy_bytes}",
+            f"rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/pmc_write -o run "
+            f"-- python3 bench.py --steps 3 --warmup 1 --no-cpu-baseline --copy-probe {copy_bytes}",
+            f"python3 bench.py --digest-pmc gpurun_out/pmc_fetch/run_counter_collection.csv "
+            f"gpurun_out/pmc_write/run_counter_collection.csv --copy-probe {copy_bytes}"],
+    }
+    with open(out_path, "w") as f:
+        json.dump(rec, f, indent=1)
+        f.write("\n")
+    print(json.dumps(rec, indent=1))
+
+
+def measured_traffic(kernel):
+    """Counter-derived bytes per launch, or None (no record, other kernel, or
+    the kernel sources changed since the counters were taken)."""
+    try:
+        rec = json.load(open(TRAFFIC_FILE))
+    except (OSError, ValueError):
+        return None
+    if rec.get("kernel") != kernel or rec.get("source_sha256") != source_hash():
+        return None
+    return rec["traffic_bytes"]
 
 
 def cpu_model():
@@ -78,7 +172,15 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe", type=int, default=0,
+                    help="bytes of one plain device copy run before the warmup")
+    ap.add_argument("--digest-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"))
     a = ap.parse_args()
+    if a.digest_pmc:
+        if a.copy_probe <= 0:
+            sys.exit("--digest-pmc needs --copy-probe BYTES (the size the counter runs used)")
+        digest_pmc(a.digest_pmc[0], a.digest_pmc[1], a.copy_probe, TRAFFIC_FILE)
+        return
     if a.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for {a.gpus}): the verify step is "
               "data-parallel over requests and this build has no multi-GPU path; "
@@ -105,9 +207,21 @@ def main():
     tok = torch.empty((w.B, w.K_max + 1), dtype=torch.int32, device=dev)
     st = torch.empty(w.B, dtype=torch.int32, device=dev)
     stream = torch.cuda.current_stream()
+    names = [sdv.phase_kernel(args, ph) for ph in range(3)]
+    phases = [ph for ph in range(3) if names[ph] is not None]
+
+    if a.copy_probe > 0:
+        # A plain streaming kernel of known traffic (reads and writes
+        # copy_probe bytes) for scaling the memory counters; a same-dtype
+        # copy_ would go to a DMA engine and dispatch no kernel.
+        src = torch.ones(a.copy_probe, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        torch.bitwise_not(src, out=dst)
+        torch.cuda.synchronize()
+        del src, dst
 
     def step(evs=None):
-        for ph in range(3):
+        for ph in phases:
             if evs is not None:
                 evs[ph][0].record(stream)
             sdv.run_phase(args, ws, ph, acc, tok, st, None, stream)
@@ -129,19 +243,15 @@ def main():
     end.record(stream)
     torch.cuda.synchronize()
     ms_step = start.elapsed_time(end) / a.steps
-    phase_ms = [float(np.mean([evs[i][ph][0].elapsed_time(evs[i][ph][1]) for i in range(a.steps)]))
-                for ph in range(3)]
+    phase_ms = {names[ph]: float(np.mean([evs[i][ph][0].elapsed_time(evs[i][ph][1])
+                                          for i in range(a.steps)])) for ph in phases}
     status = st.cpu().numpy()
     assert (status & 0xF).sum() == 0, "invalid rows in the bench workload"
 
     positions = w.positions()
     logit_bytes = w.logit_bytes()
-    dom = int(np.argmax(phase_ms))
-    # Algorithmic bytes of the dominant kernel per launch: the row phase and
-    # the whole call read every logit row once; the TV phase reads the 2K
-    # rows of each request; the finalize phase reads no row algorithmically.
-    alg = {0: logit_bytes, 1: 2 * w.K_max * w.V * 2 * w.B, 2: 0}[dom]
-    achieved = alg / (phase_ms[dom] * 1e-3) / 1e9
+    dom = max(phase_ms, key=phase_ms.get)
+    achieved = algorithmic_bytes(dom, w) / (phase_ms[dom] * 1e-3) / 1e9
     line = {
         "metric": METRIC,
         "value": positions / (ms_step * 1e-3),
@@ -155,16 +265,15 @@ def main():
         "vs_baseline": None,
         "dtype": "f32",
         "data": "synthetic",
-        "config": {"workload": "256 requests x K=8, V=152064, bf16 logits, T~U[0.5,1], "
-                               "top-p 0.9, penalty 1.1 (128 prior ids + draft prefix), "
-                               "TV budget 0.75",
+        "config": {"workload": WORKLOAD,
                    "B": w.B, "K": w.K_max, "V": w.V, "input_dtype": "bf16",
                    "logit_bytes_per_call": logit_bytes},
         "call_hbm_gbps": logit_bytes / (ms_step * 1e-3) / 1e9,
-        "phases_ms": dict(zip(PHASE_NAMES, phase_ms)),
-        "roofline": {"kernel": PHASE_NAMES[dom], "bound": "hbm", "achieved": achieved,
+        "phases_ms": phase_ms,
+        "roofline": {"kernel": dom, "bound": "hbm", "achieved": achieved,
                      "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": achieved / PEAK_HBM_GBPS,
-                     "traffic": None},
+                     "traffic": measured_traffic(dom),
+                     "algorithmic_bytes": algorithmic_bytes(dom, w)},
         "mean_accepted": float(acc.float().mean().item()),
     }
     if not a.no_cpu_baseline:

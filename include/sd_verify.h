@@ -175,15 +175,26 @@ int sd_debug_process_rows(const sd_verify_args_t *args, void *workspace,
                           void *stream);
 
 /* Measurement export: run one phase of sd_verify_sample alone, so a caller
- * can bracket a single kernel with events on `stream`.  phase 0 = per-row
- * statistics and top-p cut, 1 = per-position TV distance (no-op when the
- * arguments do not need it), 2 = decisions and draw.  Running phases 0, 1,
+ * can bracket a single kernel with events on `stream`.  Running phases 0, 1,
  * 2 in order on one stream is exactly sd_verify_sample.  Same arguments,
- * workspace and outputs as sd_verify_sample. */
+ * workspace and outputs as sd_verify_sample.  Which kernels the phases are
+ * depends on the arguments (sd_debug_phase_kernel names them):
+ *   single-pass path (bf16, top_p < 1, V <= 155648):
+ *     0 = one pass over every (row, position) pair and bonus row: top-p
+ *         cut, TV, accept test and draw; 1 = exact multi-pass recompute of
+ *         the units phase 0 flagged (every other unit exits at once);
+ *     2 = longest accepted prefix, output tokens and statistics;
+ *   general path: 0 = per-row statistics and top-p cut, 1 = per-position
+ *     TV distance (no launch when not needed), 2 = decisions and draws. */
 int sd_debug_run_phase(const sd_verify_args_t *args, void *workspace,
                        size_t workspace_bytes, int phase, int32_t *out_accepted,
                        int32_t *out_tokens, uint32_t *out_status,
                        float *out_stats, void *stream);
+
+/* Measurement export: the name of the kernel that sd_debug_run_phase
+ * launches for `phase` with these arguments (static storage), or NULL when
+ * that phase launches nothing or the arguments are invalid. */
+const char *sd_debug_phase_kernel(const sd_verify_args_t *args, int phase);
 
 /* Test export: the Philox uniforms u, v for rows 0..B-1 and positions
  * 0..npos-1, written to out_u / out_v [B][npos] (fp32, exact). */

@@ -80,6 +80,8 @@ def _load():
     lib.sd_debug_process_rows.restype = ctypes.c_int
     lib.sd_debug_run_phase.argtypes = [A, P, SZ, ctypes.c_int, P, P, P, P, P]
     lib.sd_debug_run_phase.restype = ctypes.c_int
+    lib.sd_debug_phase_kernel.argtypes = [A, ctypes.c_int]
+    lib.sd_debug_phase_kernel.restype = ctypes.c_char_p
     lib.sd_debug_uniforms.argtypes = [ctypes.c_uint64, ctypes.c_uint64, I32, I32, P, P, P]
     lib.sd_debug_uniforms.restype = ctypes.c_int
     return lib
@@ -234,12 +236,18 @@ def debug_process_rows(target, draft, draft_ids, k_per_row=None, temperature=Non
 
 def run_phase(args, workspace, phase, accepted, tokens, status=None, stats=None,
               stream=None):
-    """One phase (0 rows, 1 TV, 2 finalize) of sd_verify_sample, for timing."""
+    """One phase (0, 1 or 2) of sd_verify_sample, for timing; phase_kernel names it."""
     rc = lib.sd_debug_run_phase(ctypes.byref(args), _ptr(workspace), workspace.numel(),
                                 int(phase), _ptr(accepted), _ptr(tokens), _ptr(status),
                                 _ptr(stats), _stream(stream))
     if rc != SD_OK:
         raise SdVerifyError(rc, "sd_debug_run_phase")
+
+
+def phase_kernel(args, phase):
+    """Name of the kernel run_phase launches for `phase` (None: no launch)."""
+    name = lib.sd_debug_phase_kernel(ctypes.byref(args), int(phase))
+    return name.decode() if name is not None else None
 
 
 def debug_uniforms(seed, offset, B, npos, device="cuda", stream=None):

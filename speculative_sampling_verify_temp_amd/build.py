@@ -19,7 +19,7 @@ SOURCES = ["sd_verify.hip"]
 ARCH = os.environ.get("SDV_OFFLOAD_ARCH", "gfx950")
 
 HIPCC_FLAGS = [
-    "-O3", "-std=c++17", "-fPIC", "-shared",
+    "-O3", "-std=c++20", "-fPIC", "-shared",
     f"--offload-arch={ARCH}",
     # Packed fp32 instructions are kept out of the device code.
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",

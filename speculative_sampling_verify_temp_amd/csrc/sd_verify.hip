@@ -27,6 +27,7 @@
 #include <limits.h>
 #include <math.h>
 #include <string.h>
+#include <utility>
 
 #include "sd_verify.h"
 #include "sdv_device.h"
@@ -40,17 +41,6 @@ constexpr int NT_ROW = 512;                  // general-path row kernels
 constexpr int NT_G = 256;                    // greedy partial kernel
 constexpr int G_SLICE = 8192;                // logits per greedy workgroup
 constexpr int MAX_V = 1 << 19;
-
-// Single-pass kernel geometry.
-constexpr int NT_F = 1024;                   // threads per workgroup
-constexpr int NLOAD = 19;                    // 16-byte target loads per thread
-constexpr int MAXV_FAST = NLOAD * NT_F * VEC;  // 155648 logits
-constexpr int HW = NT_F;                     // histogram window bins (one per thread)
-constexpr int CAPT = 20;                     // target-nucleus slots per lane
-constexpr int PEN_CAP = 512;                 // penalized draft tokens above the floor
-constexpr int PREF = 4;                      // draft loads in flight
-constexpr int Q_HEADROOM = 64;               // draft window bins above the target max
-constexpr int SHP = 40;                      // fixed-point shift of penalized masses
 
 __device__ __forceinline__ int row_index(const Args& a, int r, bool target, int j) {
   return r * (2 * a.K_max + 1) + (target ? j : a.K_max + 1 + j);
@@ -285,129 +275,71 @@ struct UnitOut {
 static_assert(sizeof(UnitOut) == 48, "UnitOut layout");
 enum : uint32_t { UO_NONFINITE = 1, UO_QZERO = 2, UO_RESID_ZERO = 4, UO_SLOW = 8, UO_FALLBACK = 16 };
 
+// Compile-time loop: f.template operator()<I>() for I = 0 .. N-1, so that
+// register arrays indexed by I stay in registers.
+template <int N, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  [&]<int... I>(std::integer_sequence<int, I...>) {
+    (f.template operator()<I>(), ...);
+  }(std::make_integer_sequence<int, N>{});
+}
+
+// Keeps the compiler from sinking a round's arithmetic past later loads
+// (which would keep the round's load registers alive and spill them).
+#define SDV_PIN(x) asm volatile("" : "+v"(x))
+
+typedef int16_t i16x2 __attribute__((ext_vector_type(2)));
+typedef uint16_t u16x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ u16x2 as_u16x2(uint32_t w) { return __builtin_bit_cast(u16x2, w); }
+__device__ __forceinline__ uint32_t as_u32(u16x2 v) { return __builtin_bit_cast(uint32_t, v); }
+
 // bf16 value whose 16-bit orderable key is o.
 __device__ __forceinline__ float key_of_ord16(uint32_t o) {
   const uint32_t b = (o & 0x8000u) ? (o & 0x7FFFu) : (~o & 0xFFFFu);
   return __uint_as_float(b << 16);
 }
 
-__device__ __forceinline__ uint32_t raw16(const uint4& w, int e) {
-  const uint32_t x = (e >> 1) == 0 ? w.x : (e >> 1) == 1 ? w.y : (e >> 1) == 2 ? w.z : w.w;
-  return (e & 1) ? (x >> 16) : (x & 0xFFFFu);
-}
-
-// Processed keys of the 8 bf16 logits of vector k held in w.
-__device__ __forceinline__ void keys8(const uint4& w, int k, int V, bool pen, const uint32_t* bm,
-                                      float r, float (&z)[VEC]) {
-  const uint32_t u[4] = {w.x, w.y, w.z, w.w};
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    z[2 * e] = __uint_as_float(u[e] << 16);
-    z[2 * e + 1] = __uint_as_float(u[e] & 0xFFFF0000u);
-  }
-  if (k * VEC + VEC > V) {
-#pragma unroll
-    for (int e = 0; e < VEC; ++e)
-      if (k * VEC + e >= V) z[e] = -INFINITY;
-  }
-  if (pen) apply_penalty8(bm, k, 0, r, z);
-}
-
-// 16-bit orderable key of a processed key (top half of ord_key; -0 = +0).
+// 16-bit orderable key of a float (top half of the 32-bit orderable key;
+// -0 = +0).  A token's bin is this key: bins are ranges of the 32-bit
+// order, so every key of a higher bin is larger than every key of a lower.
 __device__ __forceinline__ uint32_t ord16f(float z) {
   const uint32_t u = __float_as_uint(z + 0.0f);
   return (u ^ ((uint32_t)((int32_t)u >> 31) | 0x80000000u)) >> 16;
 }
 
-// Processed keys of round l (vector k = l * NT_F + lane): tail masking only
-// in rounds that reach past V, penalty only where the bitmap byte is set.
-__device__ __forceinline__ void round_keys(const uint4& w, int l, int k, int V, bool pen,
-                                           const uint32_t* bm, float r, float (&z)[VEC],
-                                           uint32_t& bits) {
-  z[0] = __uint_as_float(w.x << 16);
-  z[1] = __uint_as_float(w.x & 0xFFFF0000u);
-  z[2] = __uint_as_float(w.y << 16);
-  z[3] = __uint_as_float(w.y & 0xFFFF0000u);
-  z[4] = __uint_as_float(w.z << 16);
-  z[5] = __uint_as_float(w.z & 0xFFFF0000u);
-  z[6] = __uint_as_float(w.w << 16);
-  z[7] = __uint_as_float(w.w & 0xFFFF0000u);
-  if ((l + 1) * NT_F * VEC > V) {
-#pragma unroll
-    for (int e = 0; e < VEC; ++e)
-      if (k * VEC + e >= V) z[e] = -INFINITY;
-  }
-  bits = 0u;
-  if (pen) {
-    const int b = k * VEC;
-    bits = (bm[b >> 5] >> (b & 31)) & 0xFFu;
-    if (bits) {
-#pragma unroll
-      for (int e = 0; e < VEC; ++e)
-        if ((bits >> e) & 1u) z[e] = penalize(z[e], r);
-    }
-  }
+// Orderable keys of the two bf16 values packed in w (-0 keeps its own key,
+// one below +0; the cut search merges the two).
+__device__ __forceinline__ uint32_t ord16x2(uint32_t w) {
+  const i16x2 s = __builtin_bit_cast(i16x2, w) >> (i16x2){15, 15};
+  return w ^ (__builtin_bit_cast(uint32_t, s) | 0x80008000u);
 }
 
-__device__ __forceinline__ uint32_t pen_bits(bool pen, const uint32_t* bm, int k) {
-  if (!pen) return 0u;
-  const int b = k * VEC;
-  return (bm[b >> 5] >> (b & 31)) & 0xFFu;
+// Codes of a row against its anchor t1 = (top key of the window) + 1:
+// 0 above the window, 1..254 the window (key = t1 - code), 255 below.
+__device__ __forceinline__ uint32_t code_of(uint32_t t1x2, uint32_t o2) {
+  const u16x2 d = __builtin_elementwise_sub_sat(as_u16x2(t1x2), as_u16x2(o2));
+  return as_u32(__builtin_elementwise_min(d, (u16x2){255, 255}));
 }
 
-// Online max / normalizer update of one 8-logit vector.
-__device__ __forceinline__ void online8(const float (&z)[VEC], float c, float& m, double& Z,
-                                        int& bad) {
-  float vm = -INFINITY;
-#pragma unroll
-  for (int e = 0; e < VEC; ++e) {
-    bad |= nonfinite(z[e]);
-    vm = fmaxf(vm, z[e]);
-  }
-  if (vm > m) {
-    if (m > -INFINITY) Z *= exp2(((double)m - (double)vm) * (double)c);
-    m = vm;
-  }
-  if (m > -INFINITY) {
-    float s[VEC];
-#pragma unroll
-    for (int e = 0; e < VEC; ++e) s[e] = e_rel(z[e], m, c);
-    Z += (double)(((s[0] + s[1]) + (s[2] + s[3])) + ((s[4] + s[5]) + (s[6] + s[7])));
-  }
+__device__ __forceinline__ uint32_t code1(uint32_t t1, float z) {
+  const uint32_t o = ord16f(z);
+  return o >= t1 ? 0u : (t1 - o > 255u ? 255u : t1 - o);
 }
 
-// Window cut: bin b (one per thread) holds the tokens whose 16-bit key is
-// top - b; unpenalized ones share the bin's exact bf16 key (counts in hc),
-// penalized ones carry fixed-point masses (pm, pc).  Finds the first
-// non-empty bin where the cumulative mass reaches TP.
-struct WCut {
-  int bin;        // -1: the window does not reach TP
-  double zk;      // mass of bins 0..bin
-  int pen_in_bin; // penalized tokens share the crossing bin
-};
+// Bytes of x that are <= t (t <= 254): the top bit of each such byte,
+// exact per byte (no borrow crosses a byte).
+__device__ __forceinline__ uint32_t le_mask(uint32_t x, uint32_t t) {
+  if (t < 127u) {
+    const uint32_t r = (x | 0x80808080u) - (t + 1u) * 0x01010101u;
+    return ~(r | x) & 0x80808080u;
+  }
+  const uint32_t r = ((x & 0x7F7F7F7Fu) | 0x80808080u) - (t - 127u) * 0x01010101u;
+  return ~(r & x) & 0x80808080u;
+}
 
-template <int NT>
-__device__ WCut window_cut(const uint32_t* hc, const uint64_t* pm, const uint32_t* pc,
-                           uint32_t top, float M, float c, double TP, double* wtot, int* si,
-                           double* sbc) {
-  const int b = threadIdx.x;
-  double mass = 0.0;
-  const uint32_t cnt = hc[b];
-  if (cnt && (uint32_t)b <= top) mass = (double)cnt * (double)e_rel(key_of_ord16(top - b), M, c);
-  mass += (double)pm[b] * 0x1p-40;
-  const double incl = block_incl_scan_fast<NT>(mass, wtot);
-  if (b == 0) si[0] = INT_MAX;
-  __syncthreads();
-  if ((cnt + pc[b]) > 0 && incl >= TP) atomicMin(&si[0], b);
-  __syncthreads();
-  WCut w;
-  w.bin = si[0] == INT_MAX ? -1 : si[0];
-  if (b == w.bin) sbc[0] = incl;
-  __syncthreads();
-  w.zk = w.bin >= 0 ? sbc[0] : 0.0;
-  w.pen_in_bin = w.bin >= 0 ? (int)pc[w.bin] : 0;
-  __syncthreads();
-  return w;
+__device__ __forceinline__ uint32_t pk_max(uint32_t a, uint32_t b) {
+  return as_u32(__builtin_elementwise_max(as_u16x2(a), as_u16x2(b)));
 }
 
 // Unit handled by block u: pairs (r, j) first, then one bonus row per request.
@@ -440,33 +372,400 @@ __device__ __forceinline__ float nucleus_w(float zp, float zq, int mode, float M
   return fmaxf(pr - q, 0.0f);
 }
 
-__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
-__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+// Single-pass kernel geometry.
+constexpr int NT_F = 1024;                   // threads per workgroup
+constexpr int NR = 19;                       // 16-byte loads per thread and row
+constexpr int MAXV_FAST = NR * NT_F * VEC;   // 155648 logits
+constexpr int NSAMP = 4;                     // rounds whose block max anchors a row's codes
+constexpr int NSTG = 8;                      // 16-byte loads in flight per thread
+constexpr int UP = 32;                       // window bins above the sample max
+constexpr int NBIN = 256;                    // codes 0..255
+constexpr int NCOPY = 16;                    // histogram copies (bank spreading)
+constexpr int E_CAP = 512;                   // exact-key entries per row
+constexpr int R_CAP = 64;                    // exact entries in the crossing bin
+constexpr int CAPT = 20;                     // nucleus slots per lane
+constexpr int SHP = 40;                      // fixed-point shift of exact-entry masses
+static_assert(NSTG >= NSAMP && NSTG < NR, "load ring");
+
+// Exact-key list of one row: tokens whose key is not their bin's bf16 value
+// (penalized) or lies above the window.
+struct ExactList {
+  float* key;
+  int32_t* id;
+  uint16_t* raw;   // the unprocessed logit (bf16 bits)
+  int* n;
+};
+
+struct Cut {
+  int ok;         // 0: the window does not settle the cut
+  int code;       // crossing bin (0 = above the window)
+  float key;      // boundary key: kept iff key >= this
+  double zk;      // kept mass, relative to exp2(M c)
+};
+
+// Exact top-p cut of a row from its window histogram and exact list.
+// Bins are visited from the top; the first non-empty bin whose cumulative
+// mass reaches tp is the crossing bin.  A crossing bin that holds exact
+// entries is resolved key by key, ties kept together.  Called by the whole
+// block; hist holds NCOPY interleaved copies.
+template <int NT>
+__device__ __forceinline__ Cut code_cut(const uint32_t* hist, const ExactList& ex, int ne, uint32_t t1, float M,
+                        float c, double TP, uint32_t* ecnt, uint64_t* emass, double* wtot,
+                        int* si, double* sbc, float* rkey, double* rmass, int* rid) {
+  const int tid = threadIdx.x;
+  if (tid < NBIN) {
+    ecnt[tid] = 0u;
+    emass[tid] = 0ull;
+  }
+  __syncthreads();
+  for (int i = tid; i < ne; i += NT) {
+    const float k = ex.key[i];
+    const uint32_t b = code1(t1, k);
+    if (b < 255u) {
+      atomicAdd(&ecnt[b], 1u);
+      atomicAdd(reinterpret_cast<unsigned long long*>(&emass[b]),
+                (unsigned long long)e_fixed(e_rel(k, M, c), SHP));
+    }
+  }
+  __syncthreads();
+  uint32_t cnt = 0u;
+  double mass = 0.0;
+  if (tid < NBIN) {
+#pragma unroll
+    for (int q = 0; q < NCOPY; ++q) cnt += hist[tid * NCOPY + ((q + tid) & (NCOPY - 1))];
+    if (tid == 0 || tid == 255) cnt = 0u;   // not window bins
+    if (cnt) mass = (double)cnt * (double)e_rel(key_of_ord16(t1 - tid), M, c);
+    if (tid < 255) mass += (double)emass[tid] * 0x1p-40;
+  }
+  const double incl = block_incl_scan_fast<NT>(mass, wtot);
+  if (tid == 0) si[0] = INT_MAX;
+  __syncthreads();
+  const uint32_t ecb = tid < 255 ? ecnt[tid] : 0u;
+  if (tid < 255 && (cnt + ecb) > 0u && incl >= TP) atomicMin(&si[0], tid);
+  __syncthreads();
+  Cut out;
+  const int b = si[0];
+  out.ok = b != INT_MAX;
+  out.code = b;
+  if (!out.ok) return out;
+  if (tid == b) {
+    sbc[0] = incl;
+    sbc[1] = incl - mass;
+    si[1] = (int)cnt;
+    si[2] = (int)ecb;
+  }
+  __syncthreads();
+  const double c_incl = sbc[0], c_excl = sbc[1];
+  const int gcnt = si[1], necb = si[2];
+  out.key = b > 0 ? key_of_ord16(t1 - b) : 0.0f;
+  out.zk = c_incl;
+  if (necb == 0) {
+    // A +0 crossing bin with a -0 bin just below: the two are one key.
+    if (b < 254 && __float_as_uint(out.key) == 0u) {
+      if (tid == b + 1) {
+        sbc[2] = incl;
+        si[3] = (int)cnt;
+        si[6] = (int)ecb;
+      }
+      __syncthreads();
+      if (si[6] > 0) out.ok = 0;
+      else if (si[3] > 0) {
+        out.zk = sbc[2];
+        out.code = b + 1;
+        out.key = -0.0f;
+      }
+    }
+    return out;
+  }
+  // Exact resolution inside the crossing bin: gather its entries (plus the
+  // bin's unpenalized group), order them canonically (key descending, id
+  // ascending), then the cut is the largest key whose cumulative mass,
+  // ties included, reaches TP.
+  if (necb + 1 > R_CAP) {
+    out.ok = 0;
+    return out;
+  }
+  if (tid == 0) si[4] = 0;
+  __syncthreads();
+  for (int i = tid; i < ne; i += NT) {
+    const float k = ex.key[i];
+    if (code1(t1, k) == (uint32_t)b) {
+      const int s = atomicAdd(&si[4], 1);
+      rkey[s] = k;
+      rid[s] = ex.id[i];
+      rmass[s] = (double)e_rel(k, M, c);
+    }
+  }
+  __syncthreads();
+  int n = si[4];
+  if (tid == 0 && gcnt > 0) {
+    rkey[n] = out.key;
+    rid[n] = -1;
+    rmass[n] = (double)gcnt * (double)e_rel(out.key, M, c);
+  }
+  if (gcnt > 0) ++n;
+  __syncthreads();
+  // canonical order by rank
+  float mk = 0.0f;
+  int mi = 0;
+  double mm = 0.0;
+  int rank = 0;
+  if (tid < n) {
+    mk = rkey[tid];
+    mi = rid[tid];
+    mm = rmass[tid];
+    for (int q = 0; q < n; ++q) {
+      const float kq = rkey[q];
+      const int iq = rid[q];
+      rank += (kq > mk || (kq == mk && iq < mi)) ? 1 : 0;
+    }
+  }
+  __syncthreads();
+  if (tid < n) {
+    rkey[rank] = mk;
+    rmass[rank] = mm;
+  }
+  __syncthreads();
+  if (tid < n) {
+    // cumulative through the end of my tie group, in canonical order
+    double cum = c_excl;
+    const float me = rkey[tid];
+    for (int q = 0; q < n; ++q)
+      if (rkey[q] >= me) cum += rmass[q];
+    sbc[3 + tid] = cum;   // sbc has room for R_CAP + 3
+  }
+  __syncthreads();
+  if (tid == 0) {
+    // largest key reaching TP; else the smallest key of the bin
+    int pick = n - 1;
+    for (int q = 0; q < n; ++q)
+      if (sbc[3 + q] >= TP) {
+        pick = q;
+        break;
+      }
+    // walk to the last entry of the picked tie group (same key)
+    si[5] = pick;
+  }
+  __syncthreads();
+  out.key = rkey[si[5]];
+  out.zk = sbc[3 + si[5]];
+  return out;
+}
+
+__device__ __forceinline__ void exact_push(const ExactList& ex, float key, int id, uint32_t raw) {
+  const int ix = atomicAdd(ex.n, 1);
+  if (ix < E_CAP) {
+    ex.key[ix] = key;
+    ex.id[ix] = id;
+    ex.raw[ix] = (uint16_t)raw;
+  }
+}
+
+// Unprocessed bf16 bits of token id from an exact list (the entry exists).
+__device__ __forceinline__ uint32_t exact_raw(const ExactList& ex, int ne, int id) {
+  uint32_t raw = 0u;
+  for (int i = 0; i < ne; ++i)
+    if (ex.id[i] == id) raw = ex.raw[i];
+  return raw;
+}
+
+// One 8-logit vector of a row: processed keys z, packed orderable keys o,
+// penalty bits.  Elements >= V read as -inf.
+struct Vec8 {
+  float z[VEC];
+  uint32_t o[4];
+  uint32_t w[4];
+  uint32_t bits;
+};
+
+__device__ __forceinline__ void vec8(const uint4& ld, int l, int k, int V, bool pen,
+                                     const uint32_t* bm, float rep, Vec8& v) {
+  v.w[0] = ld.x;
+  v.w[1] = ld.y;
+  v.w[2] = ld.z;
+  v.w[3] = ld.w;
+  if ((l + 1) * NT_F * VEC > V) {
+#pragma unroll
+    for (int e = 0; e < VEC; ++e)
+      if (k * VEC + e >= V) {
+        const uint32_t sh = (e & 1) * 16;
+        v.w[e >> 1] = (v.w[e >> 1] & ~(0xFFFFu << sh)) | (0xFF80u << sh);
+      }
+  }
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    v.z[2 * e] = __uint_as_float(v.w[e] << 16);
+    v.z[2 * e + 1] = __uint_as_float(v.w[e] & 0xFFFF0000u);
+    v.o[e] = ord16x2(v.w[e]);
+  }
+  v.bits = 0u;
+  if (pen) {
+    const int b = k * VEC;
+    v.bits = (bm[b >> 5] >> (b & 31)) & 0xFFu;
+  }
+}
+
+__device__ __forceinline__ float max8(const float (&z)[VEC]) {
+  return fmaxf(fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3])),
+               fmaxf(fmaxf(z[4], z[5]), fmaxf(z[6], z[7])));
+}
+
+// Per-lane running state of one row's stream.
+struct RowAcc {
+  uint32_t mo;     // packed 16-bit orderable keys: max of the unpenalized logits
+  float mpen;      // max of the penalized keys
+  double Z;        // sum of exp2(key c - anchor c)
+};
+
+// Streaming work of one vector of a row against its window: penalty,
+// normalizer, max, codes, histogram, exact entries.  Returns the two code
+// words (bytes: codes of elements 0..3 and 4..7).
+__device__ __forceinline__ uint2 row_vec(Vec8& v, int k, float rep, float c, float gc,
+                                         uint32_t t1, uint32_t hlane, uint32_t* hist,
+                                         const ExactList& ex, RowAcc& acc) {
+  const uint32_t t1x2 = t1 | (t1 << 16);
+  uint32_t cc[4], hc[4], oo[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    cc[e] = code_of(t1x2, v.o[e]);
+    hc[e] = cc[e];
+    oo[e] = v.o[e];
+  }
+  if (v.bits) {   // penalized logits: exact keys, kept out of the count bins and the packed max
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) {
+      if ((v.bits >> e) & 1u) {
+        const float zp = penalize(v.z[e], rep);
+        v.z[e] = zp;
+        acc.mpen = fmaxf(acc.mpen, zp);
+        const uint32_t cd = code1(t1, zp);
+        const uint32_t sh = (e & 1) * 16;
+        cc[e >> 1] = (cc[e >> 1] & ~(0xFFFFu << sh)) | (cd << sh);
+        hc[e >> 1] &= ~(0xFFFFu << sh);   // bin 0: not counted
+        oo[e >> 1] &= ~(0xFFFFu << sh);   // below every key
+        if (cd < 255u) exact_push(ex, zp, k * VEC + e, (v.w[e >> 1] >> sh) & 0xFFFFu);
+      }
+    }
+  }
+  const uint32_t vo = pk_max(pk_max(oo[0], oo[1]), pk_max(oo[2], oo[3]));
+  acc.mo = pk_max(acc.mo, vo);
+  if (as_u32(__builtin_elementwise_sub_sat(as_u16x2(vo), as_u16x2(t1x2 - 0x00010001u))) != 0u) {
+    // unpenalized keys above the window: exact entries
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) {
+      const uint32_t cd = (cc[e >> 1] >> ((e & 1) * 16)) & 0xFFFFu;
+      if (cd == 0u && !((v.bits >> e) & 1u))
+        exact_push(ex, v.z[e], k * VEC + e, (v.w[e >> 1] >> ((e & 1) * 16)) & 0xFFFFu);
+    }
+  }
+  float s[VEC];
+#pragma unroll
+  for (int e = 0; e < VEC; ++e) s[e] = fast_exp2(fmaf(v.z[e], c, -gc));
+  acc.Z += (double)(((s[0] + s[1]) + (s[2] + s[3])) + ((s[4] + s[5]) + (s[6] + s[7])));
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const uint32_t a2 = as_u32(as_u16x2(hc[e]) * (u16x2){NCOPY * 4, NCOPY * 4} +
+                               as_u16x2(hlane | (hlane << 16)));
+    atomicAdd(reinterpret_cast<uint32_t*>(reinterpret_cast<char*>(hist) + (a2 & 0xFFFFu)), 1u);
+    atomicAdd(reinterpret_cast<uint32_t*>(reinterpret_cast<char*>(hist) + (a2 >> 16)), 1u);
+  }
+  return make_uint2(__builtin_amdgcn_perm(cc[1], cc[0], 0x06040200u),
+                    __builtin_amdgcn_perm(cc[3], cc[2], 0x06040200u));
+}
+
+// Largest processed key of a lane's stream.
+__device__ __forceinline__ float row_max(const RowAcc& acc) {
+  const uint32_t o = max(acc.mo & 0xFFFFu, acc.mo >> 16);
+  return fmaxf(key_of_ord16(o), acc.mpen);
+}
+
+__device__ __forceinline__ RowAcc row_acc_init() {
+  RowAcc r;
+  r.mo = 0x007F007Fu;   // orderable key of -inf
+  r.mpen = -INFINITY;
+  r.Z = 0.0;
+  return r;
+}
+
+// Load g of the ring: target round g (g < NR) or draft round g - NR.
+__device__ __forceinline__ uint4 ring_load(const uint4* t4, const uint4* d4, int g, int tid, int nvec,
+                                           bool bonus) {
+  const bool drf = g >= NR;
+  const int k = (drf ? g - NR : g) * NT_F + tid;
+  if (k >= nvec || (drf && bonus)) return make_uint4(0u, 0u, 0u, 0u);
+  return drf ? d4[k] : t4[k];
+}
+
+// Files the target-nucleus tokens of round l (code words cw0, cw1) in the
+// lane's slots with their draft logits (dv; none for a bonus row).
+struct Slots {
+  uint16_t* kp;
+  uint16_t* kq;
+  uint8_t* pos;
+};
+
+__device__ __forceinline__ void file_round(int l, int k, uint32_t cw0, uint32_t cw1, uint4 dv,
+                                           bool has_d, uint32_t bits, uint32_t cut_code,
+                                           float kp_cut, uint32_t t1p, float rep,
+                                           const ExactList& ex, int nep, const Slots& sl,
+                                           int& nslot) {
+  const int tid = threadIdx.x;
+  // candidate logits: code <= cut code; bit 8b + 4h <-> logit 4h + b
+  uint32_t m = (le_mask(cw0, cut_code) >> 7) | (le_mask(cw1, cut_code) >> 3);
+  while (m) {
+    const int p = __builtin_ctz(m);
+    m &= m - 1u;
+    const int e = (p >> 3) | (p & 4);
+    const uint32_t cd = ((p & 4) ? cw1 : cw0) >> ((p >> 3) * 8) & 0xFFu;
+    const bool pe = (bits >> e) & 1u;
+    uint32_t praw;
+    bool keep = cd < cut_code;
+    if (cd == 0u || pe) {   // exact key from the row's exact list
+      praw = exact_raw(ex, nep, k * VEC + e);
+      float kp = __uint_as_float(praw << 16);
+      if (pe) kp = penalize(kp, rep);
+      keep = kp >= kp_cut;
+    } else {
+      const uint32_t o = t1p - cd;
+      praw = (o & 0x8000u) ? (o & 0x7FFFu) : (~o & 0xFFFFu);
+      if (!keep) keep = __uint_as_float(praw << 16) >= kp_cut;
+    }
+    if (!keep) continue;
+    if (nslot < CAPT) {
+      const int sidx = nslot * NT_F + tid;
+      const uint32_t dword = (e >> 1) == 0 ? dv.x : (e >> 1) == 1 ? dv.y : (e >> 1) == 2 ? dv.z : dv.w;
+      sl.kp[sidx] = (uint16_t)praw;
+      sl.kq[sidx] = has_d ? (uint16_t)((dword >> ((e & 1) * 16)) & 0xFFFFu) : (uint16_t)0;
+      sl.pos[sidx] = (uint8_t)(l * VEC + e);
+    }
+    ++nslot;
+  }
+}
 
 __global__ __launch_bounds__(NT_F) void k_pair_fast(Args a, UnitOut* uo) {
   constexpr int NT = NT_F;
   constexpr int NSLOT = CAPT * NT;
-  constexpr int HIST_P_BYTES = HW * 16;
-  constexpr int REGION_A = (NSLOT * 2 > HIST_P_BYTES) ? NSLOT * 2 : HIST_P_BYTES;
   __shared__ uint32_t bm[MAXV_FAST / 32];
-  // target histogram before the draft stream, target nucleus keys after it
-  __shared__ __align__(16) unsigned char region_a[REGION_A];
-  __shared__ uint64_t pmq[HW];
-  __shared__ uint32_t hq[HW], pcq[HW];
-  __shared__ uint16_t kq_arr[NSLOT];   // slot (s, lane) at s * NT + lane
+  __shared__ uint32_t hist[NBIN * NCOPY];
+  __shared__ float ekey[2][E_CAP];
+  __shared__ int32_t eid[2][E_CAP];
+  __shared__ uint16_t eraw[2][E_CAP];
+  __shared__ uint32_t ecnt[NBIN];
+  __shared__ uint64_t emass[NBIN];
+  __shared__ uint16_t kp_arr[NSLOT];   // slot (s, lane) at s * NT + lane
+  __shared__ uint16_t kq_arr[NSLOT];
   __shared__ uint8_t pos_arr[NSLOT];   // 8 * round + logit within the lane's 16 bytes
-  __shared__ float penq_key[PEN_CAP];
-  __shared__ double sd[NT];
-  __shared__ double rt[NLOAD + 1];
-  __shared__ double rtw[NLOAD * (NT / WAVE)];
+  __shared__ float rkey[R_CAP];
+  __shared__ double rmass[R_CAP];
+  __shared__ int rid[R_CAP];
+  __shared__ double sd[NT / WAVE];
+  __shared__ double sbc[R_CAP + 4];
+  __shared__ double rt[NR + 1];
+  __shared__ double rtw[NR * (NT / WAVE)];
   __shared__ float sf[NT / WAVE];
-  __shared__ int si[NT / WAVE + 4];
-  __shared__ int s_npen, s_acc;
-  __shared__ double sbc[2];
-  uint64_t* pmp = reinterpret_cast<uint64_t*>(region_a);
-  uint32_t* hp = reinterpret_cast<uint32_t*>(region_a + HW * 8);
-  uint32_t* pcp = reinterpret_cast<uint32_t*>(region_a + HW * 12);
-  uint16_t* kp_arr = reinterpret_cast<uint16_t*>(region_a);
+  __shared__ int si[NT / WAVE + 8];
+  __shared__ int s_ne[2];
+  __shared__ int s_acc;
 
   const int tid = threadIdx.x;
   const Unit un = unit_of(a, blockIdx.x);
@@ -486,225 +785,177 @@ __global__ __launch_bounds__(NT_F) void k_pair_fast(Args a, UnitOut* uo) {
   const char* drow = bonus ? trow : draft_row(a, r, j);
   const uint4* t4 = reinterpret_cast<const uint4*>(trow);
   const uint4* d4 = reinterpret_cast<const uint4*>(drow);
+  const uint32_t hlane = (uint32_t)(tid & (NCOPY - 1)) * 4u;
+  ExactList exp_, exq;
+  exp_.key = ekey[0];
+  exp_.id = eid[0];
+  exp_.raw = eraw[0];
+  exp_.n = &s_ne[0];
+  exq.key = ekey[1];
+  exq.id = eid[1];
+  exq.raw = eraw[1];
+  exq.n = &s_ne[1];
 
-  // ---- phase A: issue every target load and the first draft loads ----
-  uint4 tr[NLOAD];
-#pragma unroll
-  for (int l = 0; l < NLOAD; ++l) {
-    const int k = l * NT + tid;
-    tr[l] = (k < nvec) ? t4[k] : make_uint4(0u, 0u, 0u, 0u);
+  // One load ring over the target row (rounds 0..NR-1) and then the draft
+  // row (rounds NR..2NR-1): NSTG loads in flight per thread throughout.
+  uint4 stg[NSTG];
+  static_for<NSTG>([&]<int s>() __attribute__((always_inline)) {
+    stg[s] = ring_load(t4, d4, s, tid, nvec, bonus);
+  });
+  if (tid == 0) {
+    s_ne[0] = 0;
+    s_ne[1] = 0;
   }
-  uint4 qb[PREF];
-#pragma unroll
-  for (int s = 0; s < PREF; ++s) {
-    const int k = s * NT + tid;
-    qb[s] = (!bonus && k < nvec) ? d4[k] : make_uint4(0u, 0u, 0u, 0u);
-  }
-  const bool pen = build_penalty_bitmap<NT>(a, r, j, 0, V, bm);
+  for (int i = tid; i < NBIN * NCOPY; i += NT) hist[i] = 0u;
+  const bool pen = build_penalty_bitmap<NT>(a, r, j, 0, V, bm);   // synchronizes
   float u_j, v_j;
   uniforms(a.seed, a.offset, r, j, u_j, v_j);
-
-  // One pass in load-arrival order: the max, and the normalizer of
-  // exp2(z c - R c) against the lane's first-vector max R (rescaled once to
-  // the row max).  Non-finite data or overflow leave M or Z non-finite, and
-  // such units take the exact route, which classifies them.
-  float m = -INFINITY, Rc = 0.0f;
-  double Z = 0.0;
-#pragma unroll
-  for (int l = 0; l < NLOAD; ++l) {
-    const int k = l * NT + tid;
-    if ((l + 1) * NT * VEC <= V || k < nvec) {
-      float z[VEC];
-      uint32_t bits;
-      round_keys(tr[l], l, k, V, pen, bm, rep, z, bits);
-      const float vm = fmaxf(fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3])),
-                             fmaxf(fmaxf(z[4], z[5]), fmaxf(z[6], z[7])));
-      if (l == 0) Rc = (vm > -INFINITY && vm < INFINITY) ? vm * c : 0.0f;
-      m = fmaxf(m, vm);
-      float s8[VEC];
-#pragma unroll
-      for (int e = 0; e < VEC; ++e) s8[e] = fast_exp2(fmaf(z[e], c, -Rc));
-      Z += (double)(((s8[0] + s8[1]) + (s8[2] + s8[3])) + ((s8[4] + s8[5]) + (s8[6] + s8[7])));
-    }
-  }
-  const float Mp = block_max<NT>(m, sf);
-  const double Zp = block_sum<NT>(Z > 0.0 ? Z * exp2((double)Rc - (double)Mp * (double)c) : 0.0, sd);
   uint32_t oflags = 0;
-  if (!(Mp > -INFINITY) || !(Mp < INFINITY) || !(Zp > 0.0) || !(Zp < INFINITY)) {
+
+  // ---- phase A: the target row ----
+  // Anchor: block max of the first NSAMP rounds; the window is the 254
+  // bf16 keys from UP above it downwards.
+  float m0 = -INFINITY;
+  static_for<NSAMP>([&]<int l>() __attribute__((always_inline)) {
+    const int k = l * NT + tid;
+    if (k < nvec) {
+      Vec8 v;
+      vec8(stg[l], l, k, V, pen, bm, rep, v);
+      if (v.bits) {
+#pragma unroll
+        for (int e = 0; e < VEC; ++e)
+          if ((v.bits >> e) & 1u) v.z[e] = penalize(v.z[e], rep);
+      }
+      m0 = fmaxf(m0, max8(v.z));
+    }
+  });
+  const float Gp = block_max<NT>(m0, sf);
+  const bool anchor_ok = Gp > -1e30f && Gp < INFINITY;
+  const uint32_t t1p = anchor_ok ? min(ord16f(Gp) + UP, 0xFFFEu) + 1u : 0xFFFFu;
+  const float gcp = anchor_ok ? Gp * c : 0.0f;
+
+  uint32_t code[NR][2];
+  RowAcc ap = row_acc_init();
+  static_for<NR>([&]<int l>() __attribute__((always_inline)) {
+    const uint4 ld = stg[l % NSTG];
+    stg[l % NSTG] = ring_load(t4, d4, l + NSTG, tid, nvec, bonus);   // next target round, or a draft round
+    const int k = l * NT + tid;
+    code[l][0] = code[l][1] = 0xFFFFFFFFu;
+    if (k < nvec) {
+      Vec8 v;
+      vec8(ld, l, k, V, pen, bm, rep, v);
+      const uint2 cw = row_vec(v, k, rep, c, gcp, t1p, hlane, hist, exp_, ap);
+      code[l][0] = cw.x;
+      code[l][1] = cw.y;
+    }
+    SDV_PIN(ap.mo);
+    SDV_PIN(ap.mpen);
+    SDV_PIN(ap.Z);
+    SDV_PIN(code[l][0]);
+    SDV_PIN(code[l][1]);
+  });
+  const float Mp = block_max<NT>(row_max(ap), sf);
+  const double Zs = block_sum<NT>(ap.Z, sd);
+  const int nep = s_ne[0];
+  Cut cp;
+  cp.ok = 0;
+  if (!anchor_ok || !(Mp > -INFINITY) || !(Mp < INFINITY) || !(Zs > 0.0) || !(Zs < INFINITY) ||
+      nep > E_CAP) {
     oflags = UO_FALLBACK;
     goto write_out_flags;
   }
   {
-  // ---- exact top-p cut of p from a histogram of register-held keys ----
-  // Tokens with exp2((key - M) c) below (1 - top_p) Z / (2V) hold at most
-  // (1 - top_p)/2 of the mass together, so the cut lies above them and they
-  // are not histogrammed.
-  hp[tid] = 0;
-  pcp[tid] = 0;
-  pmp[tid] = 0;
-  hq[tid] = 0;
-  pcq[tid] = 0;
-  pmq[tid] = 0;
-  if (tid == 0) s_npen = 0;
-  __syncthreads();
-  const uint32_t topP = ord16f(Mp);
-  const float Lz = (float)((double)Mp + log2((1.0 - tp) * Zp / (2.0 * (double)V)) / (double)c);
-#pragma unroll
-  for (int l = 0; l < NLOAD; ++l) {
-    const int k = l * NT + tid;
-    if ((l + 1) * NT * VEC <= V || k < nvec) {
-      float z[VEC];
-      uint32_t bits;
-      round_keys(tr[l], l, k, V, pen, bm, rep, z, bits);
-#pragma unroll
-      for (int e = 0; e < VEC; ++e) {
-        if (z[e] >= Lz && !((bits >> e) & 1u)) {
-          const uint32_t b = topP - ord16f(z[e]);
-          if (b < (uint32_t)HW) atomicAdd(&hp[b], 1u);
-        }
-      }
-      if (bits) {   // penalized tokens: off the bf16 grid, carry their masses
-#pragma unroll
-        for (int e = 0; e < VEC; ++e) {
-          if (((bits >> e) & 1u) && z[e] >= Lz) {
-            const uint32_t b = topP - ord16f(z[e]);
-            if (b < (uint32_t)HW) {
-              atomicAdd(&pcp[b], 1u);
-              atomicAdd(reinterpret_cast<unsigned long long*>(&pmp[b]),
-                        (unsigned long long)e_fixed(e_rel(z[e], Mp, c), SHP));
-            }
-          }
-        }
-      }
-    }
-  }
-  __syncthreads();
-  const WCut cp = window_cut<NT>(hp, pmp, pcp, topP, Mp, c, tp * Zp, sd, si, sbc);
-  if (cp.bin < 0 || cp.pen_in_bin) {
+  const double Zp = Zs * exp2((double)gcp - (double)Mp * (double)c);
+  cp = code_cut<NT>(hist, exp_, nep, t1p, Mp, c, tp * Zp, ecnt, emass, sd, si, sbc, rkey, rmass, rid);
+  if (!cp.ok) {
     oflags = UO_FALLBACK;
     goto write_out_flags;
   }
-  const float kp_cut = key_of_ord16(topP - (uint32_t)cp.bin);
+  const float kp_cut = cp.key;
+  const uint32_t cut_code = (uint32_t)cp.code;
   const double Zkp = cp.zk;
   const float ip = (float)(1.0 / Zkp);
-  __syncthreads();   // region_a switches from the target histogram to nucleus keys
+  __syncthreads();
+  for (int i = tid; i < NBIN * NCOPY; i += NT) hist[i] = 0u;
 
-  // ---- phase B: stream the draft row once; every lane files its
-  // target-nucleus tokens (target key, draft key, position) in LDS slots ----
-  // The draft normalizer uses the target max as a fixed reference (one
-  // rescale at the end); the running draft max only serves the floor, which
-  // assumes the smallest possible normalizer (1) and is therefore valid
-  // before the draft max is known.
-  float mq = -INFINITY, Lq = -INFINITY;
-  double Zq = 0.0;
-  int qover = 0, nslot = 0;
-  const uint32_t topQ = topP + Q_HEADROOM;
-  const float Mpc = Mp * c;
-  const float lgq_c = (float)(log2((1.0 - tp) / (2.0 * (double)V)) / (double)c);
-#pragma unroll
-  for (int l = 0; l < NLOAD; ++l) {
-    const uint4 cur = qb[l % PREF];
-    if (l + PREF < NLOAD) {
-      const int k2 = (l + PREF) * NT + tid;
-      qb[l % PREF] = (!bonus && k2 < nvec) ? d4[k2] : make_uint4(0u, 0u, 0u, 0u);
-    }
-    const int k = l * NT + tid;
-    if ((l + 1) * NT * VEC <= V || k < nvec) {
-      float zp[VEC];
-      uint32_t bits;
-      round_keys(tr[l], l, k, V, pen, bm, rep, zp, bits);
-      const uint32_t tw[4] = {tr[l].x, tr[l].y, tr[l].z, tr[l].w};
-      const uint32_t qw[4] = {cur.x, cur.y, cur.z, cur.w};
-      float zq[VEC];
-      if (!bonus) {
-        uint32_t qbits;
-        round_keys(cur, l, k, V, pen, bm, rep, zq, qbits);
-        const float vm = fmaxf(fmaxf(fmaxf(zq[0], zq[1]), fmaxf(zq[2], zq[3])),
-                               fmaxf(fmaxf(zq[4], zq[5]), fmaxf(zq[6], zq[7])));
-        mq = fmaxf(mq, vm);
-        Lq = mq + lgq_c;
-        float s8[VEC];
-#pragma unroll
-        for (int e = 0; e < VEC; ++e) s8[e] = fast_exp2(fmaf(zq[e], c, -Mpc));
-        Zq += (double)(((s8[0] + s8[1]) + (s8[2] + s8[3])) + ((s8[4] + s8[5]) + (s8[6] + s8[7])));
-      }
-      uint32_t nmask = 0u;
-#pragma unroll
-      for (int e = 0; e < VEC; ++e) nmask |= (zp[e] >= kp_cut) ? (1u << e) : 0u;
-      if (nmask) {   // target-nucleus tokens of this vector (a few percent)
-#pragma unroll
-        for (int e = 0; e < VEC; ++e) {
-          if ((nmask >> e) & 1u) {
-            if (nslot < CAPT) {
-              const int sidx = nslot * NT + tid;
-              kp_arr[sidx] = (uint16_t)((e & 1) ? (tw[e >> 1] >> 16) : (tw[e >> 1] & 0xFFFFu));
-              kq_arr[sidx] = (uint16_t)((e & 1) ? (qw[e >> 1] >> 16) : (qw[e >> 1] & 0xFFFFu));
-              pos_arr[sidx] = (uint8_t)(l * VEC + e);
-            }
-            ++nslot;
-          }
-        }
-      }
-      if (!bonus) {
-#pragma unroll
-        for (int e = 0; e < VEC; ++e) {
-          if (zq[e] >= Lq && !((bits >> e) & 1u)) {
-            const uint32_t o16 = ord16f(zq[e]);
-            qover |= (o16 > topQ) ? 1 : 0;
-            const uint32_t b = topQ - o16;
-            if (b < (uint32_t)HW) atomicAdd(&hq[b], 1u);
-          }
-        }
-        if (bits) {   // penalized draft tokens above the floor: exact keys to a list
-#pragma unroll
-          for (int e = 0; e < VEC; ++e) {
-            if (((bits >> e) & 1u) && zq[e] >= Lq) {
-              const uint32_t o16 = ord16f(zq[e]);
-              qover |= (o16 > topQ) ? 1 : 0;
-              if (o16 <= topQ && topQ - o16 < (uint32_t)HW) {
-                const int ix = atomicAdd(&s_npen, 1);
-                if (ix < PEN_CAP) penq_key[ix] = zq[e];
-              }
-            }
-          }
-        }
-      }
-    }
-  }
+  int nslot = 0;
+  Slots slots;
+  slots.kp = kp_arr;
+  slots.kq = kq_arr;
+  slots.pos = pos_arr;
 
-  const float Mq = block_max<NT>(mq, sf);
-  // sum of exp2(z c - Mp c); relative to the draft max it is scaled once
-  const double Zq_ref = block_sum<NT>(Zq, sd);
-  const double Zqa = Zq_ref * exp2((double)Mpc - (double)Mq * (double)c);
-  const int over = block_or<NT>(qover || nslot > CAPT, si);
-  const int npen = s_npen;
-  // Non-finite draft data, or a fixed reference that overflowed or lost the
-  // whole sum, go to the exact route.
-  const bool ref_ok = bonus || ((Mq > -INFINITY) && (Mq < INFINITY) && Zq_ref > 0x1p-60 &&
-                                Zq_ref < INFINITY);
-  if (over || npen > PEN_CAP || !ref_ok) {
-    oflags = UO_FALLBACK;
-    goto write_out_flags;
-  }
-  float kq_cut = 0.0f, iq = 0.0f;
+  // ---- phase B: the draft row (pairs) or the nucleus from the codes (bonus) ----
+  float Mq = 0.0f, kq_cut = 0.0f, iq = 0.0f;
   double Zkq = 1.0;
-  if (!bonus) {
-    for (int i = tid; i < npen; i += NT) {
-      const float key = penq_key[i];
-      const uint32_t b = topQ - ord16f(key);
-      atomicAdd(&pcq[b], 1u);
-      atomicAdd(reinterpret_cast<unsigned long long*>(&pmq[b]),
-                (unsigned long long)e_fixed(e_rel(key, Mq, c), SHP));
-    }
-    __syncthreads();
-    const WCut cq = window_cut<NT>(hq, pmq, pcq, topQ, Mq, c, tp * Zqa, sd, si, sbc);
-    if (cq.bin < 0 || cq.pen_in_bin) {
+  if (bonus) {
+    static_for<NR>([&]<int l>() __attribute__((always_inline)) {
+      const int k = l * NT + tid;
+      if (k < nvec && ((code[l][0] & code[l][1]) != 0xFFFFFFFFu || cut_code >= 255u)) {
+        uint32_t bits = 0u;
+        if (pen) bits = (bm[(k * VEC) >> 5] >> ((k * VEC) & 31)) & 0xFFu;
+        file_round(l, k, code[l][0], code[l][1], make_uint4(0u, 0u, 0u, 0u), false, bits, cut_code,
+                   kp_cut, t1p, rep, exp_, nep, slots, nslot);
+      }
+    });
+  } else {
+    float q0 = -INFINITY;
+    static_for<NSAMP>([&]<int l>() __attribute__((always_inline)) {
+      const int k = l * NT + tid;
+      if (k < nvec) {
+        Vec8 v;
+        vec8(stg[(NR + l) % NSTG], l, k, V, pen, bm, rep, v);
+        if (v.bits) {
+#pragma unroll
+          for (int e = 0; e < VEC; ++e)
+            if ((v.bits >> e) & 1u) v.z[e] = penalize(v.z[e], rep);
+        }
+        q0 = fmaxf(q0, max8(v.z));
+      }
+    });
+    const float Gq = block_max<NT>(q0, sf);   // also orders the hist clearing above
+    const bool anchor_q = Gq > -1e30f && Gq < INFINITY;
+    const uint32_t t1q = anchor_q ? min(ord16f(Gq) + UP, 0xFFFEu) + 1u : 0xFFFFu;
+    const float gcq = anchor_q ? Gq * c : 0.0f;
+    RowAcc aq = row_acc_init();
+    static_for<NR>([&]<int l>() __attribute__((always_inline)) {
+      const uint4 ld = stg[(NR + l) % NSTG];
+      if constexpr (l + NSTG < NR) stg[(NR + l) % NSTG] = ring_load(t4, d4, NR + l + NSTG, tid, nvec, bonus);
+      const int k = l * NT + tid;
+      if (k < nvec) {
+        Vec8 v;
+        vec8(ld, l, k, V, pen, bm, rep, v);
+        const uint32_t bits = v.bits;
+        const uint4 dv = make_uint4(v.w[0], v.w[1], v.w[2], v.w[3]);
+        (void)row_vec(v, k, rep, c, gcq, t1q, hlane, hist, exq, aq);
+        file_round(l, k, code[l][0], code[l][1], dv, true, bits, cut_code, kp_cut, t1p, rep,
+                     exp_, nep, slots, nslot);
+      }
+      SDV_PIN(aq.mo);
+      SDV_PIN(aq.mpen);
+      SDV_PIN(aq.Z);
+    });
+    Mq = block_max<NT>(row_max(aq), sf);
+    const double Zqs = block_sum<NT>(aq.Z, sd);
+    const int neq = s_ne[1];
+    if (!anchor_q || !(Mq > -INFINITY) || !(Mq < INFINITY) || !(Zqs > 0.0) || !(Zqs < INFINITY) ||
+        neq > E_CAP) {
       oflags = UO_FALLBACK;
       goto write_out_flags;
     }
-    kq_cut = key_of_ord16(topQ - (uint32_t)cq.bin);
+    const double Zqa = Zqs * exp2((double)gcq - (double)Mq * (double)c);
+    const Cut cq = code_cut<NT>(hist, exq, neq, t1q, Mq, c, tp * Zqa, ecnt, emass, sd, si, sbc,
+                                rkey, rmass, rid);
+    if (!cq.ok) {
+      oflags = UO_FALLBACK;
+      goto write_out_flags;
+    }
+    kq_cut = cq.key;
     Zkq = cq.zk;
     iq = (float)(1.0 / Zkq);
+  }
+  if (block_or<NT>(nslot > CAPT, si)) {
+    oflags = UO_FALLBACK;
+    goto write_out_flags;
   }
 
   // Keys of slot s of this lane (penalty re-applied from the bitmap).
@@ -779,7 +1030,7 @@ __global__ __launch_bounds__(NT_F) void k_pair_fast(Args a, UnitOut* uo) {
   int lstar = -1;
   for (int pass = 0; pass < 2; ++pass) {
     int sl = 0;
-    for (int l = 0; l < NLOAD; ++l) {
+    for (int l = 0; l < NR; ++l) {
       double s = 0.0;
       while (sl < nslot && (pos_arr[sl * NT + tid] >> 3) == l) {
         float zp, zq;
@@ -792,19 +1043,19 @@ __global__ __launch_bounds__(NT_F) void k_pair_fast(Args a, UnitOut* uo) {
       if (tid % WAVE == 0) rtw[l * (NT / WAVE) + tid / WAVE] = s;
     }
     __syncthreads();
-    if (tid < NLOAD) {
+    if (tid < NR) {
       double Rl = 0.0;
       for (int w = 0; w < NT / WAVE; ++w) Rl += rtw[tid * (NT / WAVE) + w];
       rt[tid] = Rl;
     }
     __syncthreads();
     S = 0.0;
-    for (int l = 0; l < NLOAD; ++l) S += rt[l];
+    for (int l = 0; l < NR; ++l) S += rt[l];
     t = (double)v_j * S;
     double accr = 0.0, alast = 0.0;
     int last = -1;
     lstar = -1;
-    for (int l = 0; l < NLOAD; ++l) {
+    for (int l = 0; l < NR; ++l) {
       if (rt[l] > 0.0) { last = l; alast = accr; }
       if (lstar < 0 && accr + rt[l] > t) { lstar = l; R = accr; }
       accr += rt[l];
@@ -1464,6 +1715,18 @@ int sd_debug_run_phase(const sd_verify_args_t* args, void* workspace, size_t wor
   return a.dtype == SD_BF16
              ? run_phase<SD_BF16>(a, L, ws, phase, out_accepted, out_tokens, out_status, out_stats, st)
              : run_phase<SD_F32>(a, L, ws, phase, out_accepted, out_tokens, out_status, out_stats, st);
+}
+
+const char* sd_debug_phase_kernel(const sd_verify_args_t* args, int phase) {
+  if (check_common(args, true) != SD_OK || phase < 0 || phase > 2) return nullptr;
+  const Args a = make_args(args);
+  if (a.dtype == SD_BF16 && use_fast(a)) {
+    static const char* const fast[3] = {"k_pair_fast", "k_pair_fallback", "k_fast_finalize"};
+    return fast[phase];
+  }
+  if (phase == 0) return "k_row_prepare";
+  if (phase == 1) return (needs_tv(a, nullptr) && a.K_max > 0) ? "k_pair_tv" : nullptr;
+  return "k_finalize";
 }
 
 int sd_debug_uniforms(uint64_t seed, uint64_t offset, int32_t B, int32_t npos, float* out_u,

@@ -188,7 +188,7 @@ __device__ __forceinline__ float wave_max(float x) {
 
 // Sum across the block; every thread gets the result.  scratch: >= NT/64 doubles.
 template <int NT>
-__device__ double block_sum(double x, double* scratch) {
+__device__ __forceinline__ double block_sum(double x, double* scratch) {
   x = wave_sum(x);
   const int w = threadIdx.x / WAVE, l = threadIdx.x % WAVE;
   __syncthreads();
@@ -201,7 +201,7 @@ __device__ double block_sum(double x, double* scratch) {
 }
 
 template <int NT>
-__device__ uint64_t block_sum_u64(uint64_t x, uint64_t* scratch) {
+__device__ __forceinline__ uint64_t block_sum_u64(uint64_t x, uint64_t* scratch) {
   x = wave_sum_u64(x);
   const int w = threadIdx.x / WAVE, l = threadIdx.x % WAVE;
   __syncthreads();
@@ -214,7 +214,7 @@ __device__ uint64_t block_sum_u64(uint64_t x, uint64_t* scratch) {
 }
 
 template <int NT>
-__device__ float block_max(float x, float* scratch) {
+__device__ __forceinline__ float block_max(float x, float* scratch) {
   x = wave_max(x);
   const int w = threadIdx.x / WAVE, l = threadIdx.x % WAVE;
   __syncthreads();
@@ -227,7 +227,7 @@ __device__ float block_max(float x, float* scratch) {
 }
 
 template <int NT>
-__device__ int block_or(int x, int* scratch) {
+__device__ __forceinline__ int block_or(int x, int* scratch) {
   const int w = threadIdx.x / WAVE;
   x = __any(x) ? 1 : 0;
   __syncthreads();
@@ -263,7 +263,7 @@ __device__ __forceinline__ int wave_incl_scan_int(int x) {
 // Block inclusive scan: wave scans, then the wave totals in order.
 // wtot: NT / WAVE doubles.  Deterministic.
 template <int NT>
-__device__ double block_incl_scan_fast(double x, double* wtot) {
+__device__ __forceinline__ double block_incl_scan_fast(double x, double* wtot) {
   const int w = threadIdx.x / WAVE, l = threadIdx.x % WAVE;
   x = wave_incl_scan(x);
   __syncthreads();
@@ -276,7 +276,7 @@ __device__ double block_incl_scan_fast(double x, double* wtot) {
 
 // Block exclusive scan of ints; *total receives the block total.
 template <int NT>
-__device__ int block_excl_scan_int(int x, int* wtot, int* total) {
+__device__ __forceinline__ int block_excl_scan_int(int x, int* wtot, int* total) {
   const int w = threadIdx.x / WAVE, l = threadIdx.x % WAVE;
   const int incl = wave_incl_scan_int(x);
   __syncthreads();
@@ -294,7 +294,7 @@ __device__ int block_excl_scan_int(int x, int* wtot, int* total) {
 // Inclusive scan of one double per thread across the block (Hillis-Steele in
 // LDS, fixed order).  buf: NT doubles.  Returns the inclusive prefix.
 template <int NT>
-__device__ double block_incl_scan(double x, double* buf) {
+__device__ __forceinline__ double block_incl_scan(double x, double* buf) {
   __syncthreads();
   buf[threadIdx.x] = x;
   __syncthreads();
@@ -315,7 +315,7 @@ __device__ double block_incl_scan(double x, double* buf) {
 // PENALTY_PRIOR_ONLY).  Returns whether any bit can be set (block-uniform),
 // i.e. whether the penalty is active for this row.
 template <int NT>
-__device__ bool build_penalty_bitmap(const Args& a, int r, int j, int lo, int nbits,
+__device__ __forceinline__ bool build_penalty_bitmap(const Args& a, int r, int j, int lo, int nbits,
                                      uint32_t* bm) {
   if (a.rep == 1.0f) return false;
   int p0 = 0, p1 = 0;

@@ -96,3 +96,20 @@ def test_greedy_ignores_sampling_only_fields():
     out = ctypes.c_void_p(0x400000)
     assert sdv.lib.sd_verify_greedy(ctypes.byref(a), ctypes.c_void_p(0x500000), 1 << 30,
                                     out, out, None, None, None) == sdv.SD_EINVAL
+
+
+def test_phase_kernel_names_follow_the_path_choice():
+    import speculative_sampling_verify_temp_amd as sdv
+    a = _good_args(sdv)
+    assert [sdv.phase_kernel(a, p) for p in range(3)] == \
+        ["k_pair_fast", "k_pair_fallback", "k_fast_finalize"]
+    a.top_p = 1.0   # no truncation: general path; TV needed for 0 < D < 1
+    assert [sdv.phase_kernel(a, p) for p in range(3)] == \
+        ["k_row_prepare", "k_pair_tv", "k_finalize"]
+    a.tv_budget = 0.0
+    assert sdv.phase_kernel(a, 1) is None
+    a.dtype, a.top_p = sdv.SD_F32, 0.9
+    assert sdv.phase_kernel(a, 0) == "k_row_prepare"
+    assert sdv.phase_kernel(a, 3) is None
+    a.B = 0
+    assert sdv.phase_kernel(a, 0) is None
