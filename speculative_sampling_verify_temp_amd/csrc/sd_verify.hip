@@ -377,7 +377,7 @@ constexpr int NT_F = 1024;                   // threads per workgroup
 constexpr int NR = 19;                       // 16-byte loads per thread and row
 constexpr int MAXV_FAST = NR * NT_F * VEC;   // 155648 logits
 constexpr int NSAMP = 4;                     // rounds whose block max anchors a row's codes
-constexpr int NSTG = 8;                      // 16-byte loads in flight per thread
+constexpr int NSTG = 6;                      // 16-byte loads in flight per thread
 constexpr int UP = 32;                       // window bins above the sample max
 constexpr int NBIN = 256;                    // codes 0..255
 constexpr int NCOPY = 16;                    // histogram copies (bank spreading)
@@ -385,6 +385,7 @@ constexpr int E_CAP = 512;                   // exact-key entries per row
 constexpr int R_CAP = 64;                    // exact entries in the crossing bin
 constexpr int CAPT = 20;                     // nucleus slots per lane
 constexpr int SHP = 40;                      // fixed-point shift of exact-entry masses
+constexpr int FALLBACK_GRID = 256;           // blocks of the exact fallback launch
 static_assert(NSTG >= NSAMP && NSTG < NR, "load ring");
 
 // Exact-key list of one row: tokens whose key is not their bin's bf16 value
@@ -403,22 +404,25 @@ struct Cut {
   double zk;      // kept mass, relative to exp2(M c)
 };
 
-// Exact top-p cut of a row from its window histogram and exact list.
-// Bins are visited from the top; the first non-empty bin whose cumulative
-// mass reaches tp is the crossing bin.  A crossing bin that holds exact
-// entries is resolved key by key, ties kept together.  Called by the whole
-// block; hist holds NCOPY interleaved copies.
-template <int NT>
-__device__ __forceinline__ Cut code_cut(const uint32_t* hist, const ExactList& ex, int ne, uint32_t t1, float M,
-                        float c, double TP, uint32_t* ecnt, uint64_t* emass, double* wtot,
-                        int* si, double* sbc, float* rkey, double* rmass, int* rid) {
-  const int tid = threadIdx.x;
-  if (tid < NBIN) {
-    ecnt[tid] = 0u;
-    emass[tid] = 0ull;
+// Exact top-p cut of a row from its window histogram and exact list, by
+// one wave (the caller's wave 0; no block barriers).  Window bins are
+// visited from the top; the first non-empty bin whose cumulative mass
+// reaches TP is the crossing bin.  A crossing bin that holds exact entries
+// is resolved key by key, ties kept together.  hist holds NCOPY
+// interleaved copies; lane L owns bins 4L .. 4L+3.
+__device__ __forceinline__ Cut wave_cut(const uint32_t* hist, const ExactList& ex, int ne,
+                                        uint32_t t1, float M, float c, double TP, uint32_t* ecnt,
+                                        uint64_t* emass, float* rkey, double* rmass, int* rid,
+                                        int* scnt) {
+  const int lane = threadIdx.x % WAVE;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    ecnt[4 * lane + i] = 0u;
+    emass[4 * lane + i] = 0ull;
   }
-  __syncthreads();
-  for (int i = tid; i < ne; i += NT) {
+  if (lane == 0) *scnt = 0;
+  __builtin_amdgcn_wave_barrier();
+  for (int i = lane; i < ne; i += WAVE) {
     const float k = ex.key[i];
     const uint32_t b = code1(t1, k);
     if (b < 255u) {
@@ -427,51 +431,66 @@ __device__ __forceinline__ Cut code_cut(const uint32_t* hist, const ExactList& e
                 (unsigned long long)e_fixed(e_rel(k, M, c), SHP));
     }
   }
-  __syncthreads();
-  uint32_t cnt = 0u;
-  double mass = 0.0;
-  if (tid < NBIN) {
+  __builtin_amdgcn_wave_barrier();
+  uint32_t cnt[4], ec[4];
+  double mass[4];
+  double lsum = 0.0;
 #pragma unroll
-    for (int q = 0; q < NCOPY; ++q) cnt += hist[tid * NCOPY + ((q + tid) & (NCOPY - 1))];
-    if (tid == 0 || tid == 255) cnt = 0u;   // not window bins
-    if (cnt) mass = (double)cnt * (double)e_rel(key_of_ord16(t1 - tid), M, c);
-    if (tid < 255) mass += (double)emass[tid] * 0x1p-40;
+  for (int i = 0; i < 4; ++i) {
+    const int b = 4 * lane + i;
+    uint32_t n = 0u;
+#pragma unroll
+    for (int q = 0; q < NCOPY; ++q) n += hist[b * NCOPY + ((q + lane) & (NCOPY - 1))];
+    if (b == 0 || b == 255) n = 0u;   // not window bins
+    cnt[i] = n;
+    ec[i] = b < 255 ? ecnt[b] : 0u;
+    double m = n ? (double)n * (double)e_rel(key_of_ord16(t1 - b), M, c) : 0.0;
+    if (b < 255) m += (double)emass[b] * 0x1p-40;
+    mass[i] = m;
+    lsum += m;
   }
-  const double incl = block_incl_scan_fast<NT>(mass, wtot);
-  if (tid == 0) si[0] = INT_MAX;
-  __syncthreads();
-  const uint32_t ecb = tid < 255 ? ecnt[tid] : 0u;
-  if (tid < 255 && (cnt + ecb) > 0u && incl >= TP) atomicMin(&si[0], tid);
-  __syncthreads();
+  const double excl = wave_incl_scan(lsum) - lsum;
+  // first crossing bin of this lane
+  double cum = excl, cin = 0.0, cex = 0.0;
+  int hit = -1;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const double nx = cum + mass[i];
+    if (hit < 0 && (cnt[i] + ec[i]) > 0u && nx >= TP) {
+      hit = i;
+      cin = nx;
+      cex = cum;
+    }
+    cum = nx;
+  }
+  const uint64_t bal = __ballot(hit >= 0);
   Cut out;
-  const int b = si[0];
-  out.ok = b != INT_MAX;
-  out.code = b;
+  out.ok = bal != 0ull;
+  out.code = 0;
+  out.key = 0.0f;
+  out.zk = 0.0;
   if (!out.ok) return out;
-  if (tid == b) {
-    sbc[0] = incl;
-    sbc[1] = incl - mass;
-    si[1] = (int)cnt;
-    si[2] = (int)ecb;
-  }
-  __syncthreads();
-  const double c_incl = sbc[0], c_excl = sbc[1];
-  const int gcnt = si[1], necb = si[2];
+  const int src = __builtin_ctzll(bal);
+  const int hb = __shfl(hit, src);
+  const int b = 4 * src + hb;
+  const double c_incl = __shfl(cin, src), c_excl = __shfl(cex, src);
+  const int gcnt = __shfl((int)(hb == 0 ? cnt[0] : hb == 1 ? cnt[1] : hb == 2 ? cnt[2] : cnt[3]), src);
+  const int necb = __shfl((int)(hb == 0 ? ec[0] : hb == 1 ? ec[1] : hb == 2 ? ec[2] : ec[3]), src);
+  out.code = b;
   out.key = b > 0 ? key_of_ord16(t1 - b) : 0.0f;
   out.zk = c_incl;
   if (necb == 0) {
     // A +0 crossing bin with a -0 bin just below: the two are one key.
     if (b < 254 && __float_as_uint(out.key) == 0u) {
-      if (tid == b + 1) {
-        sbc[2] = incl;
-        si[3] = (int)cnt;
-        si[6] = (int)ecb;
-      }
-      __syncthreads();
-      if (si[6] > 0) out.ok = 0;
-      else if (si[3] > 0) {
-        out.zk = sbc[2];
-        out.code = b + 1;
+      const int b1 = b + 1, l1 = b1 >> 2, i1 = b1 & 3;
+      const int n1 = __shfl((int)(i1 == 0 ? cnt[0] : i1 == 1 ? cnt[1] : i1 == 2 ? cnt[2] : cnt[3]), l1);
+      const int e1 = __shfl((int)(i1 == 0 ? ec[0] : i1 == 1 ? ec[1] : i1 == 2 ? ec[2] : ec[3]), l1);
+      // cumulative through bin b + 1 = through bin b + its mass
+      const double m1 = __shfl(i1 == 0 ? mass[0] : i1 == 1 ? mass[1] : i1 == 2 ? mass[2] : mass[3], l1);
+      if (e1 > 0) out.ok = 0;
+      else if (n1 > 0) {
+        out.zk = c_incl + m1;
+        out.code = b1;
         out.key = -0.0f;
       }
     }
@@ -479,78 +498,82 @@ __device__ __forceinline__ Cut code_cut(const uint32_t* hist, const ExactList& e
   }
   // Exact resolution inside the crossing bin: gather its entries (plus the
   // bin's unpenalized group), order them canonically (key descending, id
-  // ascending), then the cut is the largest key whose cumulative mass,
-  // ties included, reaches TP.
+  // ascending); the cut is the largest key whose cumulative mass, ties
+  // included, reaches TP.
   if (necb + 1 > R_CAP) {
     out.ok = 0;
     return out;
   }
-  if (tid == 0) si[4] = 0;
-  __syncthreads();
-  for (int i = tid; i < ne; i += NT) {
+  for (int i = lane; i < ne; i += WAVE) {
     const float k = ex.key[i];
     if (code1(t1, k) == (uint32_t)b) {
-      const int s = atomicAdd(&si[4], 1);
+      const int s = atomicAdd(scnt, 1);
       rkey[s] = k;
       rid[s] = ex.id[i];
       rmass[s] = (double)e_rel(k, M, c);
     }
   }
-  __syncthreads();
-  int n = si[4];
-  if (tid == 0 && gcnt > 0) {
-    rkey[n] = out.key;
-    rid[n] = -1;
-    rmass[n] = (double)gcnt * (double)e_rel(out.key, M, c);
+  __builtin_amdgcn_wave_barrier();
+  int n = necb;
+  if (gcnt > 0) {
+    if (lane == 0) {
+      rkey[n] = out.key;
+      rid[n] = -1;
+      rmass[n] = (double)gcnt * (double)e_rel(out.key, M, c);
+    }
+    ++n;
   }
-  if (gcnt > 0) ++n;
-  __syncthreads();
-  // canonical order by rank
+  __builtin_amdgcn_wave_barrier();
   float mk = 0.0f;
-  int mi = 0;
   double mm = 0.0;
   int rank = 0;
-  if (tid < n) {
-    mk = rkey[tid];
-    mi = rid[tid];
-    mm = rmass[tid];
+  if (lane < n) {
+    mk = rkey[lane];
+    const int mi = rid[lane];
+    mm = rmass[lane];
     for (int q = 0; q < n; ++q) {
       const float kq = rkey[q];
       const int iq = rid[q];
       rank += (kq > mk || (kq == mk && iq < mi)) ? 1 : 0;
     }
   }
-  __syncthreads();
-  if (tid < n) {
+  __builtin_amdgcn_wave_barrier();
+  if (lane < n) {
     rkey[rank] = mk;
     rmass[rank] = mm;
   }
-  __syncthreads();
-  if (tid < n) {
-    // cumulative through the end of my tie group, in canonical order
-    double cum = c_excl;
-    const float me = rkey[tid];
+  __builtin_amdgcn_wave_barrier();
+  // cumulative through the end of my tie group, in canonical order
+  double cm = c_excl;
+  const float me = lane < n ? rkey[lane] : 0.0f;
+  if (lane < n)
     for (int q = 0; q < n; ++q)
-      if (rkey[q] >= me) cum += rmass[q];
-    sbc[3 + tid] = cum;   // sbc has room for R_CAP + 3
-  }
-  __syncthreads();
-  if (tid == 0) {
-    // largest key reaching TP; else the smallest key of the bin
-    int pick = n - 1;
-    for (int q = 0; q < n; ++q)
-      if (sbc[3 + q] >= TP) {
-        pick = q;
-        break;
-      }
-    // walk to the last entry of the picked tie group (same key)
-    si[5] = pick;
-  }
-  __syncthreads();
-  out.key = rkey[si[5]];
-  out.zk = sbc[3 + si[5]];
+      if (rkey[q] >= me) cm += rmass[q];
+  const uint64_t reach = __ballot(lane < n && cm >= TP);
+  const int pick = reach ? __builtin_ctzll(reach) : n - 1;
+  out.key = __shfl(me, pick);
+  out.zk = __shfl(cm, pick);
   return out;
 }
+
+// Per-wave partials to LDS and one barrier; every thread gets the result.
+// Each call site uses its own buffer (NT / WAVE entries).
+template <int NT>
+__device__ __forceinline__ float bar_max(float x, float* buf) {
+  x = wave_max(x);
+  if (threadIdx.x % WAVE == 0) buf[threadIdx.x / WAVE] = x;
+  __syncthreads();
+  float m = buf[0];
+#pragma unroll
+  for (int i = 1; i < NT / WAVE; ++i) m = fmaxf(m, buf[i]);
+  return m;
+}
+
+struct CutRes {
+  int ok, code;
+  float key, M;
+  double zk;
+};
 
 __device__ __forceinline__ void exact_push(const ExactList& ex, float key, int id, uint32_t raw) {
   const int ix = atomicAdd(ex.n, 1);
@@ -621,7 +644,7 @@ struct RowAcc {
 // normalizer, max, codes, histogram, exact entries.  Returns the two code
 // words (bytes: codes of elements 0..3 and 4..7).
 __device__ __forceinline__ uint2 row_vec(Vec8& v, int k, float rep, float c, float gc,
-                                         uint32_t t1, uint32_t hlane, uint32_t* hist,
+                                         uint32_t t1, uint32_t hlane2, uint32_t* hist,
                                          const ExactList& ex, RowAcc& acc) {
   const uint32_t t1x2 = t1 | (t1 << 16);
   uint32_t cc[4], hc[4], oo[4];
@@ -664,8 +687,7 @@ __device__ __forceinline__ uint2 row_vec(Vec8& v, int k, float rep, float c, flo
   acc.Z += (double)(((s[0] + s[1]) + (s[2] + s[3])) + ((s[4] + s[5]) + (s[6] + s[7])));
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
-    const uint32_t a2 = as_u32(as_u16x2(hc[e]) * (u16x2){NCOPY * 4, NCOPY * 4} +
-                               as_u16x2(hlane | (hlane << 16)));
+    const uint32_t a2 = as_u32(as_u16x2(hc[e]) * (u16x2){NCOPY * 4, NCOPY * 4} + as_u16x2(hlane2));
     atomicAdd(reinterpret_cast<uint32_t*>(reinterpret_cast<char*>(hist) + (a2 & 0xFFFFu)), 1u);
     atomicAdd(reinterpret_cast<uint32_t*>(reinterpret_cast<char*>(hist) + (a2 >> 16)), 1u);
   }
@@ -687,13 +709,17 @@ __device__ __forceinline__ RowAcc row_acc_init() {
   return r;
 }
 
-// Load g of the ring: target round g (g < NR) or draft round g - NR.
+// Load g of the ring: target round g (g < NR) or draft round g - NR.  The
+// load is unconditional, so the compiler's wait counts stay exact (a load
+// under a branch makes it wait for the whole ring): lanes past the row end,
+// and the draft rounds of a bonus unit, read vector 0 instead (one cache
+// line per wave) and their data is never used.
 __device__ __forceinline__ uint4 ring_load(const uint4* t4, const uint4* d4, int g, int tid, int nvec,
                                            bool bonus) {
   const bool drf = g >= NR;
   const int k = (drf ? g - NR : g) * NT_F + tid;
-  if (k >= nvec || (drf && bonus)) return make_uint4(0u, 0u, 0u, 0u);
-  return drf ? d4[k] : t4[k];
+  const bool use = k < nvec && !(drf && bonus);
+  return (drf ? d4 : t4)[use ? k : 0];
 }
 
 // Files the target-nucleus tokens of round l (code words cw0, cw1) in the
@@ -766,8 +792,14 @@ __global__ __launch_bounds__(NT_F) void k_pair_fast(Args a, UnitOut* uo) {
   __shared__ int si[NT / WAVE + 8];
   __shared__ int s_ne[2];
   __shared__ int s_acc;
+  __shared__ int s_rcnt;
+  __shared__ float red_f[4][NT / WAVE];    // per-wave partials, one row per reduction site
+  __shared__ double red_d[3][NT / WAVE];
+  __shared__ int red_i[2][NT / WAVE];
+  __shared__ CutRes s_cut[2];
 
   const int tid = threadIdx.x;
+  const int lane = tid % WAVE, wv = tid / WAVE;
   const Unit un = unit_of(a, blockIdx.x);
   const int r = un.r;
   const bool bonus = un.bonus;
@@ -786,6 +818,7 @@ __global__ __launch_bounds__(NT_F) void k_pair_fast(Args a, UnitOut* uo) {
   const uint4* t4 = reinterpret_cast<const uint4*>(trow);
   const uint4* d4 = reinterpret_cast<const uint4*>(drow);
   const uint32_t hlane = (uint32_t)(tid & (NCOPY - 1)) * 4u;
+  const uint32_t hlane2 = hlane | (hlane << 16);   // packed byte offset of this lane's copy
   ExactList exp_, exq;
   exp_.key = ekey[0];
   exp_.id = eid[0];
@@ -829,22 +862,27 @@ __global__ __launch_bounds__(NT_F) void k_pair_fast(Args a, UnitOut* uo) {
       m0 = fmaxf(m0, max8(v.z));
     }
   });
-  const float Gp = block_max<NT>(m0, sf);
+  const float Gp = bar_max<NT>(m0, red_f[0]);
   const bool anchor_ok = Gp > -1e30f && Gp < INFINITY;
   const uint32_t t1p = anchor_ok ? min(ord16f(Gp) + UP, 0xFFFEu) + 1u : 0xFFFFu;
   const float gcp = anchor_ok ? Gp * c : 0.0f;
 
   uint32_t code[NR][2];
   RowAcc ap = row_acc_init();
+  // The draft side computes its offsets from an opaque copy of tid, so the
+  // compiler does not keep the target's per-round offsets alive for reuse.
+  int tid_b = tid;
+  SDV_PIN(tid_b);
   static_for<NR>([&]<int l>() __attribute__((always_inline)) {
     const uint4 ld = stg[l % NSTG];
-    stg[l % NSTG] = ring_load(t4, d4, l + NSTG, tid, nvec, bonus);   // next target round, or a draft round
+    stg[l % NSTG] = ring_load(t4, d4, l + NSTG, l + NSTG < NR ? tid : tid_b, nvec, bonus);   // next target round, or a draft round
+    __builtin_amdgcn_sched_barrier(0);   // keep later rounds' loads in their rounds
     const int k = l * NT + tid;
     code[l][0] = code[l][1] = 0xFFFFFFFFu;
     if (k < nvec) {
       Vec8 v;
       vec8(ld, l, k, V, pen, bm, rep, v);
-      const uint2 cw = row_vec(v, k, rep, c, gcp, t1p, hlane, hist, exp_, ap);
+      const uint2 cw = row_vec(v, k, rep, c, gcp, t1p, hlane2, hist, exp_, ap);
       code[l][0] = cw.x;
       code[l][1] = cw.y;
     }
@@ -854,28 +892,50 @@ __global__ __launch_bounds__(NT_F) void k_pair_fast(Args a, UnitOut* uo) {
     SDV_PIN(code[l][0]);
     SDV_PIN(code[l][1]);
   });
-  const float Mp = block_max<NT>(row_max(ap), sf);
-  const double Zs = block_sum<NT>(ap.Z, sd);
-  const int nep = s_ne[0];
-  Cut cp;
-  cp.ok = 0;
-  if (!anchor_ok || !(Mp > -INFINITY) || !(Mp < INFINITY) || !(Zs > 0.0) || !(Zs < INFINITY) ||
-      nep > E_CAP) {
-    oflags = UO_FALLBACK;
-    goto write_out_flags;
-  }
   {
-  const double Zp = Zs * exp2((double)gcp - (double)Mp * (double)c);
-  cp = code_cut<NT>(hist, exp_, nep, t1p, Mp, c, tp * Zp, ecnt, emass, sd, si, sbc, rkey, rmass, rid);
+    const float wm = wave_max(row_max(ap));
+    const double wz = wave_sum(ap.Z);
+    if (lane == 0) {
+      red_f[1][wv] = wm;
+      red_d[0][wv] = wz;
+    }
+  }
+  __syncthreads();   // the target stream is done: histogram, exact list, partials
+  if (wv == 0) {
+    float M = red_f[1][0];
+    double Zs = 0.0;
+#pragma unroll
+    for (int i = 0; i < NT / WAVE; ++i) {
+      M = fmaxf(M, red_f[1][i]);
+      Zs += red_d[0][i];
+    }
+    const int ne = s_ne[0];
+    const bool good = anchor_ok && M > -INFINITY && M < INFINITY && Zs > 0.0 && Zs < INFINITY &&
+                      ne <= E_CAP;
+    Cut cc;
+    cc.ok = 0;
+    cc.code = 0;
+    cc.key = 0.0f;
+    cc.zk = 0.0;
+    if (good) {
+      const double Zp = Zs * exp2((double)gcp - (double)M * (double)c);
+      cc = wave_cut(hist, exp_, ne, t1p, M, c, tp * Zp, ecnt, emass, rkey, rmass, rid, &s_rcnt);
+    }
+    if (lane == 0) s_cut[0] = CutRes{good && cc.ok ? 1 : 0, cc.code, cc.key, M, cc.zk};
+  }
+  __syncthreads();
+  const CutRes cp = s_cut[0];
+  const float Mp = cp.M;
+  const int nep = s_ne[0];
   if (!cp.ok) {
     oflags = UO_FALLBACK;
     goto write_out_flags;
   }
+  {
   const float kp_cut = cp.key;
   const uint32_t cut_code = (uint32_t)cp.code;
   const double Zkp = cp.zk;
   const float ip = (float)(1.0 / Zkp);
-  __syncthreads();
   for (int i = tid; i < NBIN * NCOPY; i += NT) hist[i] = 0u;
 
   int nslot = 0;
@@ -900,7 +960,7 @@ __global__ __launch_bounds__(NT_F) void k_pair_fast(Args a, UnitOut* uo) {
   } else {
     float q0 = -INFINITY;
     static_for<NSAMP>([&]<int l>() __attribute__((always_inline)) {
-      const int k = l * NT + tid;
+      const int k = l * NT + tid_b;
       if (k < nvec) {
         Vec8 v;
         vec8(stg[(NR + l) % NSTG], l, k, V, pen, bm, rep, v);
@@ -912,21 +972,22 @@ __global__ __launch_bounds__(NT_F) void k_pair_fast(Args a, UnitOut* uo) {
         q0 = fmaxf(q0, max8(v.z));
       }
     });
-    const float Gq = block_max<NT>(q0, sf);   // also orders the hist clearing above
+    const float Gq = bar_max<NT>(q0, red_f[2]);   // also orders the hist clearing above
     const bool anchor_q = Gq > -1e30f && Gq < INFINITY;
     const uint32_t t1q = anchor_q ? min(ord16f(Gq) + UP, 0xFFFEu) + 1u : 0xFFFFu;
     const float gcq = anchor_q ? Gq * c : 0.0f;
     RowAcc aq = row_acc_init();
     static_for<NR>([&]<int l>() __attribute__((always_inline)) {
       const uint4 ld = stg[(NR + l) % NSTG];
-      if constexpr (l + NSTG < NR) stg[(NR + l) % NSTG] = ring_load(t4, d4, NR + l + NSTG, tid, nvec, bonus);
-      const int k = l * NT + tid;
+      if constexpr (l + NSTG < NR) stg[(NR + l) % NSTG] = ring_load(t4, d4, NR + l + NSTG, tid_b, nvec, bonus);
+      __builtin_amdgcn_sched_barrier(0);
+      const int k = l * NT + tid_b;
       if (k < nvec) {
         Vec8 v;
         vec8(ld, l, k, V, pen, bm, rep, v);
         const uint32_t bits = v.bits;
         const uint4 dv = make_uint4(v.w[0], v.w[1], v.w[2], v.w[3]);
-        (void)row_vec(v, k, rep, c, gcq, t1q, hlane, hist, exq, aq);
+        (void)row_vec(v, k, rep, c, gcq, t1q, hlane2, hist, exq, aq);
         file_round(l, k, code[l][0], code[l][1], dv, true, bits, cut_code, kp_cut, t1p, rep,
                      exp_, nep, slots, nslot);
       }
@@ -934,28 +995,63 @@ __global__ __launch_bounds__(NT_F) void k_pair_fast(Args a, UnitOut* uo) {
       SDV_PIN(aq.mpen);
       SDV_PIN(aq.Z);
     });
-    Mq = block_max<NT>(row_max(aq), sf);
-    const double Zqs = block_sum<NT>(aq.Z, sd);
-    const int neq = s_ne[1];
-    if (!anchor_q || !(Mq > -INFINITY) || !(Mq < INFINITY) || !(Zqs > 0.0) || !(Zqs < INFINITY) ||
-        neq > E_CAP) {
-      oflags = UO_FALLBACK;
-      goto write_out_flags;
+    {
+      const float wm = wave_max(row_max(aq));
+      const double wz = wave_sum(aq.Z);
+      const int wo = __any(nslot > CAPT) ? 1 : 0;
+      if (lane == 0) {
+        red_f[3][wv] = wm;
+        red_d[1][wv] = wz;
+        red_i[0][wv] = wo;
+      }
     }
-    const double Zqa = Zqs * exp2((double)gcq - (double)Mq * (double)c);
-    const Cut cq = code_cut<NT>(hist, exq, neq, t1q, Mq, c, tp * Zqa, ecnt, emass, sd, si, sbc,
-                                rkey, rmass, rid);
+    __syncthreads();   // the draft stream is done
+    if (wv == 0) {
+      float M = red_f[3][0];
+      double Zs = 0.0;
+      int over = 0;
+#pragma unroll
+      for (int i = 0; i < NT / WAVE; ++i) {
+        M = fmaxf(M, red_f[3][i]);
+        Zs += red_d[1][i];
+        over |= red_i[0][i];
+      }
+      const int ne = s_ne[1];
+      const bool good = anchor_q && M > -INFINITY && M < INFINITY && Zs > 0.0 && Zs < INFINITY &&
+                        ne <= E_CAP && !over;
+      Cut cc;
+      cc.ok = 0;
+      cc.code = 0;
+      cc.key = 0.0f;
+      cc.zk = 0.0;
+      if (good) {
+        const double Zqa = Zs * exp2((double)gcq - (double)M * (double)c);
+        cc = wave_cut(hist, exq, ne, t1q, M, c, tp * Zqa, ecnt, emass, rkey, rmass, rid, &s_rcnt);
+      }
+      if (lane == 0) s_cut[1] = CutRes{good && cc.ok ? 1 : 0, cc.code, cc.key, M, cc.zk};
+    }
+    __syncthreads();
+    const CutRes cq = s_cut[1];
     if (!cq.ok) {
       oflags = UO_FALLBACK;
       goto write_out_flags;
     }
+    Mq = cq.M;
     kq_cut = cq.key;
     Zkq = cq.zk;
     iq = (float)(1.0 / Zkq);
   }
-  if (block_or<NT>(nslot > CAPT, si)) {
-    oflags = UO_FALLBACK;
-    goto write_out_flags;
+  if (bonus) {
+    const int wo = __any(nslot > CAPT) ? 1 : 0;
+    if (lane == 0) red_i[1][wv] = wo;
+    __syncthreads();
+    int over = 0;
+#pragma unroll
+    for (int i = 0; i < NT / WAVE; ++i) over |= red_i[1][i];
+    if (over) {
+      oflags = UO_FALLBACK;
+      goto write_out_flags;
+    }
   }
 
   // Keys of slot s of this lane (penalty re-applied from the bitmap).
@@ -971,17 +1067,6 @@ __global__ __launch_bounds__(NT_F) void k_pair_fast(Args a, UnitOut* uo) {
   };
 
   // ---- TV, p(x), q(x), theta, pi, acceptance ----
-  double d = 0.0;
-  if (!bonus) {
-    double acc = 0.0;
-    for (int sl = 0; sl < nslot; ++sl) {
-      float zp, zq;
-      int id;
-      slot_keys(sl * NT + tid, zp, zq, id);
-      acc += (double)nucleus_w(zp, zq, 0, Mp, ip, kq_cut, Mq, iq, c);
-    }
-    d = fmin(block_sum<NT>(acc, sd), 1.0);
-  }
   UnitOut out;
   out.d = out.th = out.px = out.qx = out.pix = out.S = 0.0f;
   out.u = u_j;
@@ -991,7 +1076,21 @@ __global__ __launch_bounds__(NT_F) void k_pair_fast(Args a, UnitOut* uo) {
   out.flags = 0;
   out.pad = 0;
   if (!bonus) {
+    double acc = 0.0;
+    for (int sl = 0; sl < nslot; ++sl) {
+      float zp, zq;
+      int id;
+      slot_keys(sl * NT + tid, zp, zq, id);
+      acc += (double)nucleus_w(zp, zq, 0, Mp, ip, kq_cut, Mq, iq, c);
+    }
+    acc = wave_sum(acc);
+    if (lane == 0) red_d[2][wv] = acc;
+    __syncthreads();
     if (tid == 0) {
+      double d = 0.0;
+#pragma unroll
+      for (int i = 0; i < NT / WAVE; ++i) d += red_d[2][i];
+      d = fmin(d, 1.0);
       const int x = a.ids[(int64_t)r * a.K_max + j];
       float kxp = -INFINITY, kxq = -INFINITY;
       if (x >= 0 && x < V) {
@@ -1014,12 +1113,10 @@ __global__ __launch_bounds__(NT_F) void k_pair_fast(Args a, UnitOut* uo) {
       out.accept = dc.accept ? 1 : 0;
       if (dc.qx == 0.0) out.flags |= UO_QZERO;
       s_acc = out.accept;
+      if (dc.accept) uo[blockIdx.x] = out;
     }
     __syncthreads();
-    if (s_acc) {
-      if (tid == 0) uo[blockIdx.x] = out;
-      return;
-    }
+    if (s_acc) return;
   }
 
   // ---- correction (rejected position) or bonus draw from the nucleus ----
@@ -1126,9 +1223,9 @@ write_out_flags:
   }
 }
 
-// Exact multi-pass processing of the units k_pair_fast flagged for it
-// (re-reads their rows); other blocks exit at once.
-__global__ __launch_bounds__(NT_F) void k_pair_fallback(Args a, UnitOut* uo) {
+// Exact multi-pass processing of one unit k_pair_fast flagged (re-reads its
+// rows with the general-path routines).
+__device__ __forceinline__ void fallback_unit(const Args& a, UnitOut* uo, int u) {
   constexpr int NT = NT_F;
   __shared__ uint32_t bm[MAXV_FAST / 32];
   __shared__ uint64_t hmass[HBINS];
@@ -1140,7 +1237,7 @@ __global__ __launch_bounds__(NT_F) void k_pair_fallback(Args a, UnitOut* uo) {
   __shared__ int si[NT / WAVE + 4];
   __shared__ int s_acc;
   const int tid = threadIdx.x;
-  const Unit un = unit_of(a, blockIdx.x);
+  const Unit un = unit_of(a, u);
   const int r = un.r;
   const bool bonus = un.bonus;
   const int K = request_k(a, r);
@@ -1151,7 +1248,6 @@ __global__ __launch_bounds__(NT_F) void k_pair_fallback(Args a, UnitOut* uo) {
   if (!bonus && j >= K) return;
   const float T = request_t(a, r);
   if (!(T > 0.0f) || !(T < INFINITY)) return;
-  if (!(uo[blockIdx.x].flags & UO_FALLBACK)) return;
   const float c = 1.4426950408889634f / T;
   const char* trow = target_row(a, r, j);
   const char* drow = bonus ? trow : draft_row(a, r, j);
@@ -1164,7 +1260,7 @@ __global__ __launch_bounds__(NT_F) void k_pair_fallback(Args a, UnitOut* uo) {
   ex.sf = sf;
   ex.si = si;
   ex.ctot = ctot;
-  UnitOut out = uo[blockIdx.x];
+  UnitOut out = uo[u];
   out.flags = UO_SLOW;
   out.accept = 1;
   out.y = -1;
@@ -1172,7 +1268,7 @@ __global__ __launch_bounds__(NT_F) void k_pair_fallback(Args a, UnitOut* uo) {
   if (P.flags & NONFINITE) {
     if (tid == 0) {
       out.flags = UO_NONFINITE;
-      uo[blockIdx.x] = out;
+      uo[u] = out;
     }
     return;
   }
@@ -1181,7 +1277,7 @@ __global__ __launch_bounds__(NT_F) void k_pair_fallback(Args a, UnitOut* uo) {
     if (tid == 0) {
       out.y = dw.y;
       out.S = (float)dw.S;
-      uo[blockIdx.x] = out;
+      uo[u] = out;
     }
     return;
   }
@@ -1189,7 +1285,7 @@ __global__ __launch_bounds__(NT_F) void k_pair_fallback(Args a, UnitOut* uo) {
   if (Q.flags & NONFINITE) {
     if (tid == 0) {
       out.flags = UO_NONFINITE;
-      uo[blockIdx.x] = out;
+      uo[u] = out;
     }
     return;
   }
@@ -1224,7 +1320,25 @@ __global__ __launch_bounds__(NT_F) void k_pair_fallback(Args a, UnitOut* uo) {
       if (dw.resid_zero) out.flags |= UO_RESID_ZERO;
     }
   }
-  if (tid == 0) uo[blockIdx.x] = out;
+  if (tid == 0) uo[u] = out;
+}
+
+// Exact multi-pass processing of the units k_pair_fast flagged: a small
+// grid walks every unit and takes the flagged ones (each block holds one CU,
+// so the idle cost of this launch stays a few microseconds).
+__global__ __launch_bounds__(NT_F) void k_pair_fallback(Args a, UnitOut* uo, int nunits) {
+  for (int u = blockIdx.x; u < nunits; u += gridDim.x) {
+    const Unit un = unit_of(a, u);
+    const int K = request_k(a, un.r);
+    // Units k_pair_fast skipped (invalid request, position beyond K_r) hold
+    // no output of this call: never act on them.
+    if (K < 0 || K > a.K_max || (!un.bonus && un.j >= K)) continue;
+    const float T = request_t(a, un.r);
+    if (!(T > 0.0f) || !(T < INFINITY)) continue;
+    if (!(uo[u].flags & UO_FALLBACK)) continue;
+    fallback_unit(a, uo, u);
+    __syncthreads();   // the next unit reuses the shared arrays
+  }
 }
 
 __global__ __launch_bounds__(64) void k_fast_finalize(Args a, const UnitOut* uo, int32_t* out_acc,
@@ -1578,7 +1692,9 @@ int run_phase(const Args& a, const Layout& L, char* ws, int phase, int32_t* acc,
       return launch_status();
     }
     if (phase == 1) {
-      hipLaunchKernelGGL(k_pair_fallback, dim3(a.B * a.K_max + a.B), dim3(NT_F), 0, st, a, uo);
+      const int nunits = a.B * a.K_max + a.B;
+      hipLaunchKernelGGL(k_pair_fallback, dim3(nunits < FALLBACK_GRID ? nunits : FALLBACK_GRID),
+                         dim3(NT_F), 0, st, a, uo, nunits);
       return launch_status();
     }
     hipLaunchKernelGGL(k_fast_finalize, dim3(a.B), dim3(64), 0, st, a, uo, acc, tok, status, stats);
