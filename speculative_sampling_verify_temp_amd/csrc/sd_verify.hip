@@ -377,13 +377,14 @@ constexpr int NT_F = 1024;                   // threads per workgroup
 constexpr int NR = 19;                       // 16-byte loads per thread and row
 constexpr int MAXV_FAST = NR * NT_F * VEC;   // 155648 logits
 constexpr int NSAMP = 4;                     // rounds whose block max anchors a row's codes
-constexpr int NSTG = 6;                      // 16-byte loads in flight per thread
+constexpr int NSTG = 5;                      // 16-byte loads in flight per thread
 constexpr int UP = 32;                       // window bins above the sample max
 constexpr int NBIN = 256;                    // codes 0..255
 constexpr int NCOPY = 16;                    // histogram copies (bank spreading)
 constexpr int E_CAP = 512;                   // exact-key entries per row
 constexpr int R_CAP = 64;                    // exact entries in the crossing bin
 constexpr int CAPT = 20;                     // nucleus slots per lane
+constexpr int PV_CAP = 448;                  // penalized vectors per row stream
 constexpr int SHP = 40;                      // fixed-point shift of exact-entry masses
 constexpr int FALLBACK_GRID = 256;           // blocks of the exact fallback launch
 static_assert(NSTG >= NSAMP && NSTG < NR, "load ring");
@@ -584,12 +585,18 @@ __device__ __forceinline__ void exact_push(const ExactList& ex, float key, int i
   }
 }
 
-// Unprocessed bf16 bits of token id from an exact list (the entry exists).
+// Unprocessed bf16 bits of token id from an exact list, or 0xFFFFFFFF if
+// the list has no entry for it.
 __device__ __forceinline__ uint32_t exact_raw(const ExactList& ex, int ne, int id) {
-  uint32_t raw = 0u;
+  uint32_t raw = 0xFFFFFFFFu;
   for (int i = 0; i < ne; ++i)
     if (ex.id[i] == id) raw = ex.raw[i];
   return raw;
+}
+
+// Bit e of an 8-bit mask to bit 8(e & 3) + 4(e >> 2) (the candidate layout).
+__device__ __forceinline__ uint32_t spread8(uint32_t b) {
+  return (((b & 0xFu) * 0x204081u) & 0x01010101u) | (((((b >> 4) & 0xFu) * 0x204081u) & 0x01010101u) << 4);
 }
 
 // One 8-logit vector of a row: processed keys z, packed orderable keys o,
@@ -635,42 +642,45 @@ __device__ __forceinline__ float max8(const float (&z)[VEC]) {
 
 // Per-lane running state of one row's stream.
 struct RowAcc {
-  uint32_t mo;     // packed 16-bit orderable keys: max of the unpenalized logits
-  float mpen;      // max of the penalized keys
+  uint32_t mo;     // packed 16-bit orderable keys: max of the logits as read
+  float mpen;      // max of the penalized keys (after the stream)
   double Z;        // sum of exp2(key c - anchor c)
 };
 
-// Streaming work of one vector of a row against its window: penalty,
-// normalizer, max, codes, histogram, exact entries.  Returns the two code
-// words (bytes: codes of elements 0..3 and 4..7).
-__device__ __forceinline__ uint2 row_vec(Vec8& v, int k, float rep, float c, float gc,
-                                         uint32_t t1, uint32_t hlane2, uint32_t* hist,
-                                         const ExactList& ex, RowAcc& acc) {
+// Vectors holding penalized logits, captured during a stream (raw 16 bytes,
+// and k | bits << 24) and settled after it by pen_fix.
+struct PenList {
+  uint4* raw;
+  int* kb;
+  int* n;
+};
+
+__device__ __forceinline__ uint32_t pk_mad_u16(uint32_t a, uint32_t b, uint32_t c) {
+  uint32_t d;
+  asm("v_pk_mad_u16 %0, %1, %2, %3" : "=v"(d) : "v"(a), "s"(b), "v"(c));
+  return d;
+}
+
+// Streaming work of one vector of a row against its window: normalizer,
+// max, codes, histogram, exact entries for unpenalized keys above the
+// window.  Penalized logits are streamed as read and only their vector is
+// captured; pen_fix moves them to exact entries afterwards.  Returns the
+// two code words (bytes: codes of elements 0..3 and 4..7).
+__device__ __forceinline__ uint2 row_vec(Vec8& v, int k, float c, float gc, uint32_t t1,
+                                         uint32_t hlane2, uint32_t* hist, const ExactList& ex,
+                                         const PenList& pl, RowAcc& acc) {
   const uint32_t t1x2 = t1 | (t1 << 16);
-  uint32_t cc[4], hc[4], oo[4];
+  uint32_t cc[4];
 #pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    cc[e] = code_of(t1x2, v.o[e]);
-    hc[e] = cc[e];
-    oo[e] = v.o[e];
-  }
-  if (v.bits) {   // penalized logits: exact keys, kept out of the count bins and the packed max
-#pragma unroll
-    for (int e = 0; e < VEC; ++e) {
-      if ((v.bits >> e) & 1u) {
-        const float zp = penalize(v.z[e], rep);
-        v.z[e] = zp;
-        acc.mpen = fmaxf(acc.mpen, zp);
-        const uint32_t cd = code1(t1, zp);
-        const uint32_t sh = (e & 1) * 16;
-        cc[e >> 1] = (cc[e >> 1] & ~(0xFFFFu << sh)) | (cd << sh);
-        hc[e >> 1] &= ~(0xFFFFu << sh);   // bin 0: not counted
-        oo[e >> 1] &= ~(0xFFFFu << sh);   // below every key
-        if (cd < 255u) exact_push(ex, zp, k * VEC + e, (v.w[e >> 1] >> sh) & 0xFFFFu);
-      }
+  for (int e = 0; e < 4; ++e) cc[e] = code_of(t1x2, v.o[e]);
+  if (v.bits) {
+    const int ix = atomicAdd(pl.n, 1);
+    if (ix < PV_CAP) {
+      pl.raw[ix] = make_uint4(v.w[0], v.w[1], v.w[2], v.w[3]);
+      pl.kb[ix] = k | (int)(v.bits << 24);
     }
   }
-  const uint32_t vo = pk_max(pk_max(oo[0], oo[1]), pk_max(oo[2], oo[3]));
+  const uint32_t vo = pk_max(pk_max(v.o[0], v.o[1]), pk_max(v.o[2], v.o[3]));
   acc.mo = pk_max(acc.mo, vo);
   if (as_u32(__builtin_elementwise_sub_sat(as_u16x2(vo), as_u16x2(t1x2 - 0x00010001u))) != 0u) {
     // unpenalized keys above the window: exact entries
@@ -687,12 +697,41 @@ __device__ __forceinline__ uint2 row_vec(Vec8& v, int k, float rep, float c, flo
   acc.Z += (double)(((s[0] + s[1]) + (s[2] + s[3])) + ((s[4] + s[5]) + (s[6] + s[7])));
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
-    const uint32_t a2 = as_u32(as_u16x2(hc[e]) * (u16x2){NCOPY * 4, NCOPY * 4} + as_u16x2(hlane2));
+    const uint32_t a2 = pk_mad_u16(cc[e], (NCOPY * 4) * 0x00010001u, hlane2);
     atomicAdd(reinterpret_cast<uint32_t*>(reinterpret_cast<char*>(hist) + (a2 & 0xFFFFu)), 1u);
     atomicAdd(reinterpret_cast<uint32_t*>(reinterpret_cast<char*>(hist) + (a2 >> 16)), 1u);
   }
   return make_uint2(__builtin_amdgcn_perm(cc[1], cc[0], 0x06040200u),
                     __builtin_amdgcn_perm(cc[3], cc[2], 0x06040200u));
+}
+
+// After a stream: every penalized logit leaves its count bin (it was counted
+// under its raw key) and, if it reaches the window, becomes an exact entry
+// under its penalized key; the normalizer trades the raw term for the
+// penalized one.  Block-parallel over the captured vectors.
+__device__ __forceinline__ void pen_fix(const PenList& pl, int n, uint32_t t1, float rep, float c,
+                                        float gc, uint32_t* hist, const ExactList& ex,
+                                        RowAcc& acc) {
+  for (int i = threadIdx.x; i < n; i += NT_F) {
+    const uint4 w = pl.raw[i];
+    const int kb = pl.kb[i];
+    const int k = kb & 0xFFFFFF;
+    uint32_t bits = (uint32_t)kb >> 24;
+    while (bits) {
+      const int e = __builtin_ctz(bits);
+      bits &= bits - 1u;
+      const uint32_t word = (e >> 1) == 0 ? w.x : (e >> 1) == 1 ? w.y : (e >> 1) == 2 ? w.z : w.w;
+      const uint32_t raw = (word >> ((e & 1) * 16)) & 0xFFFFu;
+      const uint32_t o = raw ^ ((raw & 0x8000u) ? 0xFFFFu : 0x8000u);   // as ord16x2
+      const uint32_t cr = o >= t1 ? 0u : (t1 - o > 255u ? 255u : t1 - o);
+      if (cr >= 1u && cr <= 254u) atomicSub(&hist[cr * NCOPY], 1u);
+      const float z = __uint_as_float(raw << 16);
+      const float zp = penalize(z, rep);
+      if (code1(t1, zp) < 255u) exact_push(ex, zp, k * VEC + e, raw);
+      acc.Z += (double)fast_exp2(fmaf(zp, c, -gc)) - (double)fast_exp2(fmaf(z, c, -gc));
+      acc.mpen = fmaxf(acc.mpen, zp);
+    }
+  }
 }
 
 // Largest processed key of a lane's stream.
@@ -736,8 +775,12 @@ __device__ __forceinline__ void file_round(int l, int k, uint32_t cw0, uint32_t 
                                            const ExactList& ex, int nep, const Slots& sl,
                                            int& nslot) {
   const int tid = threadIdx.x;
-  // candidate logits: code <= cut code; bit 8b + 4h <-> logit 4h + b
+  // candidate logits: code <= cut code; bit 8b + 4h <-> logit 4h + b.  The
+  // codes are those of the logits as read; a penalty that lowers keys
+  // (r > 1) cannot make a non-candidate a member, one that raises them can,
+  // so then every penalized logit is a candidate.
   uint32_t m = (le_mask(cw0, cut_code) >> 7) | (le_mask(cw1, cut_code) >> 3);
+  if (rep < 1.0f) m |= spread8(bits);
   while (m) {
     const int p = __builtin_ctz(m);
     m &= m - 1u;
@@ -745,16 +788,20 @@ __device__ __forceinline__ void file_round(int l, int k, uint32_t cw0, uint32_t 
     const uint32_t cd = ((p & 4) ? cw1 : cw0) >> ((p >> 3) * 8) & 0xFFu;
     const bool pe = (bits >> e) & 1u;
     uint32_t praw;
-    bool keep = cd < cut_code;
-    if (cd == 0u || pe) {   // exact key from the row's exact list
+    bool keep;
+    if (cd == 0u || cd == 255u) {
+      // above the window (or, penalized, anywhere outside it): exact list.
+      // A penalized logit with no entry has its key below the window.
       praw = exact_raw(ex, nep, k * VEC + e);
+      if (praw == 0xFFFFFFFFu) continue;
       float kp = __uint_as_float(praw << 16);
       if (pe) kp = penalize(kp, rep);
       keep = kp >= kp_cut;
     } else {
       const uint32_t o = t1p - cd;
       praw = (o & 0x8000u) ? (o & 0x7FFFu) : (~o & 0xFFFFu);
-      if (!keep) keep = __uint_as_float(praw << 16) >= kp_cut;
+      if (pe) keep = penalize(__uint_as_float(praw << 16), rep) >= kp_cut;
+      else keep = cd < cut_code || __uint_as_float(praw << 16) >= kp_cut;
     }
     if (!keep) continue;
     if (nslot < CAPT) {
@@ -772,7 +819,7 @@ __global__ __launch_bounds__(NT_F) void k_pair_fast(Args a, UnitOut* uo) {
   constexpr int NT = NT_F;
   constexpr int NSLOT = CAPT * NT;
   __shared__ uint32_t bm[MAXV_FAST / 32];
-  __shared__ uint32_t hist[NBIN * NCOPY];
+  __shared__ __align__(16) uint32_t hist[NBIN * NCOPY];
   __shared__ float ekey[2][E_CAP];
   __shared__ int32_t eid[2][E_CAP];
   __shared__ uint16_t eraw[2][E_CAP];
@@ -787,7 +834,6 @@ __global__ __launch_bounds__(NT_F) void k_pair_fast(Args a, UnitOut* uo) {
   __shared__ double sd[NT / WAVE];
   __shared__ double sbc[R_CAP + 4];
   __shared__ double rt[NR + 1];
-  __shared__ double rtw[NR * (NT / WAVE)];
   __shared__ float sf[NT / WAVE];
   __shared__ int si[NT / WAVE + 8];
   __shared__ int s_ne[2];
@@ -797,6 +843,9 @@ __global__ __launch_bounds__(NT_F) void k_pair_fast(Args a, UnitOut* uo) {
   __shared__ double red_d[3][NT / WAVE];
   __shared__ int red_i[2][NT / WAVE];
   __shared__ CutRes s_cut[2];
+  __shared__ uint4 pv_raw[PV_CAP];
+  __shared__ int pv_kb[PV_CAP];
+  __shared__ int s_npv;
 
   const int tid = threadIdx.x;
   const int lane = tid % WAVE, wv = tid / WAVE;
@@ -828,6 +877,13 @@ __global__ __launch_bounds__(NT_F) void k_pair_fast(Args a, UnitOut* uo) {
   exq.id = eid[1];
   exq.raw = eraw[1];
   exq.n = &s_ne[1];
+  // per-round draw totals: the histogram is dead by the time of the draw
+  double* rtw = reinterpret_cast<double*>(hist);
+  static_assert(NR * (NT / WAVE) * sizeof(double) <= sizeof(hist), "rtw alias");
+  PenList pl;
+  pl.raw = pv_raw;
+  pl.kb = pv_kb;
+  pl.n = &s_npv;
 
   // One load ring over the target row (rounds 0..NR-1) and then the draft
   // row (rounds NR..2NR-1): NSTG loads in flight per thread throughout.
@@ -838,6 +894,7 @@ __global__ __launch_bounds__(NT_F) void k_pair_fast(Args a, UnitOut* uo) {
   if (tid == 0) {
     s_ne[0] = 0;
     s_ne[1] = 0;
+    s_npv = 0;
   }
   for (int i = tid; i < NBIN * NCOPY; i += NT) hist[i] = 0u;
   const bool pen = build_penalty_bitmap<NT>(a, r, j, 0, V, bm);   // synchronizes
@@ -853,13 +910,8 @@ __global__ __launch_bounds__(NT_F) void k_pair_fast(Args a, UnitOut* uo) {
     const int k = l * NT + tid;
     if (k < nvec) {
       Vec8 v;
-      vec8(stg[l], l, k, V, pen, bm, rep, v);
-      if (v.bits) {
-#pragma unroll
-        for (int e = 0; e < VEC; ++e)
-          if ((v.bits >> e) & 1u) v.z[e] = penalize(v.z[e], rep);
-      }
-      m0 = fmaxf(m0, max8(v.z));
+      vec8(stg[l], l, k, V, false, bm, rep, v);
+      m0 = fmaxf(m0, max8(v.z));   // logits as read: the anchor is only a reference
     }
   });
   const float Gp = bar_max<NT>(m0, red_f[0]);
@@ -882,7 +934,7 @@ __global__ __launch_bounds__(NT_F) void k_pair_fast(Args a, UnitOut* uo) {
     if (k < nvec) {
       Vec8 v;
       vec8(ld, l, k, V, pen, bm, rep, v);
-      const uint2 cw = row_vec(v, k, rep, c, gcp, t1p, hlane2, hist, exp_, ap);
+      const uint2 cw = row_vec(v, k, c, gcp, t1p, hlane2, hist, exp_, pl, ap);
       code[l][0] = cw.x;
       code[l][1] = cw.y;
     }
@@ -892,6 +944,9 @@ __global__ __launch_bounds__(NT_F) void k_pair_fast(Args a, UnitOut* uo) {
     SDV_PIN(code[l][0]);
     SDV_PIN(code[l][1]);
   });
+  __syncthreads();   // the target stream is done: histogram, captured vectors
+  const int npv_p = s_npv;
+  if (npv_p <= PV_CAP) pen_fix(pl, npv_p, t1p, rep, c, gcp, hist, exp_, ap);
   {
     const float wm = wave_max(row_max(ap));
     const double wz = wave_sum(ap.Z);
@@ -900,7 +955,7 @@ __global__ __launch_bounds__(NT_F) void k_pair_fast(Args a, UnitOut* uo) {
       red_d[0][wv] = wz;
     }
   }
-  __syncthreads();   // the target stream is done: histogram, exact list, partials
+  __syncthreads();   // penalized logits settled; partials
   if (wv == 0) {
     float M = red_f[1][0];
     double Zs = 0.0;
@@ -911,7 +966,7 @@ __global__ __launch_bounds__(NT_F) void k_pair_fast(Args a, UnitOut* uo) {
     }
     const int ne = s_ne[0];
     const bool good = anchor_ok && M > -INFINITY && M < INFINITY && Zs > 0.0 && Zs < INFINITY &&
-                      ne <= E_CAP;
+                      ne <= E_CAP && npv_p <= PV_CAP;
     Cut cc;
     cc.ok = 0;
     cc.code = 0;
@@ -921,7 +976,10 @@ __global__ __launch_bounds__(NT_F) void k_pair_fast(Args a, UnitOut* uo) {
       const double Zp = Zs * exp2((double)gcp - (double)M * (double)c);
       cc = wave_cut(hist, exp_, ne, t1p, M, c, tp * Zp, ecnt, emass, rkey, rmass, rid, &s_rcnt);
     }
-    if (lane == 0) s_cut[0] = CutRes{good && cc.ok ? 1 : 0, cc.code, cc.key, M, cc.zk};
+    if (lane == 0) {
+      s_cut[0] = CutRes{good && cc.ok ? 1 : 0, cc.code, cc.key, M, cc.zk};
+      s_npv = 0;   // the draft stream captures into the same list
+    }
   }
   __syncthreads();
   const CutRes cp = s_cut[0];
@@ -963,12 +1021,7 @@ __global__ __launch_bounds__(NT_F) void k_pair_fast(Args a, UnitOut* uo) {
       const int k = l * NT + tid_b;
       if (k < nvec) {
         Vec8 v;
-        vec8(stg[(NR + l) % NSTG], l, k, V, pen, bm, rep, v);
-        if (v.bits) {
-#pragma unroll
-          for (int e = 0; e < VEC; ++e)
-            if ((v.bits >> e) & 1u) v.z[e] = penalize(v.z[e], rep);
-        }
+        vec8(stg[(NR + l) % NSTG], l, k, V, false, bm, rep, v);
         q0 = fmaxf(q0, max8(v.z));
       }
     });
@@ -987,7 +1040,7 @@ __global__ __launch_bounds__(NT_F) void k_pair_fast(Args a, UnitOut* uo) {
         vec8(ld, l, k, V, pen, bm, rep, v);
         const uint32_t bits = v.bits;
         const uint4 dv = make_uint4(v.w[0], v.w[1], v.w[2], v.w[3]);
-        (void)row_vec(v, k, rep, c, gcq, t1q, hlane2, hist, exq, aq);
+        (void)row_vec(v, k, c, gcq, t1q, hlane2, hist, exq, pl, aq);
         file_round(l, k, code[l][0], code[l][1], dv, true, bits, cut_code, kp_cut, t1p, rep,
                      exp_, nep, slots, nslot);
       }
@@ -995,6 +1048,9 @@ __global__ __launch_bounds__(NT_F) void k_pair_fast(Args a, UnitOut* uo) {
       SDV_PIN(aq.mpen);
       SDV_PIN(aq.Z);
     });
+    __syncthreads();   // the draft stream is done: histogram, captured vectors
+    const int npv_q = s_npv;
+    if (npv_q <= PV_CAP) pen_fix(pl, npv_q, t1q, rep, c, gcq, hist, exq, aq);
     {
       const float wm = wave_max(row_max(aq));
       const double wz = wave_sum(aq.Z);
@@ -1005,7 +1061,7 @@ __global__ __launch_bounds__(NT_F) void k_pair_fast(Args a, UnitOut* uo) {
         red_i[0][wv] = wo;
       }
     }
-    __syncthreads();   // the draft stream is done
+    __syncthreads();   // penalized logits settled; partials
     if (wv == 0) {
       float M = red_f[3][0];
       double Zs = 0.0;
@@ -1018,7 +1074,7 @@ __global__ __launch_bounds__(NT_F) void k_pair_fast(Args a, UnitOut* uo) {
       }
       const int ne = s_ne[1];
       const bool good = anchor_q && M > -INFINITY && M < INFINITY && Zs > 0.0 && Zs < INFINITY &&
-                        ne <= E_CAP && !over;
+                        ne <= E_CAP && !over && npv_q <= PV_CAP;
       Cut cc;
       cc.ok = 0;
       cc.code = 0;
