@@ -769,16 +769,21 @@ struct Slots {
   uint8_t* pos;
 };
 
-__device__ __forceinline__ void file_round(int l, int k, uint32_t cw0, uint32_t cw1, uint4 dv,
+// Marker in a slot's target bits: the logit lies above the window; its
+// bits are in the row's exact list (an orderable key of 0, i.e. bf16
+// 0xFFFF, never arises from a window code).
+constexpr uint16_t SLOT_EXACT = 0xFFFFu;
+
+__device__ __forceinline__ void file_round(int l, uint32_t cw0, uint32_t cw1, uint4 dv,
                                            bool has_d, uint32_t bits, uint32_t cut_code,
-                                           float kp_cut, uint32_t t1p, float rep,
-                                           const ExactList& ex, int nep, const Slots& sl,
+                                           uint32_t t1p, float rep, const Slots& sl,
                                            int& nslot) {
   const int tid = threadIdx.x;
-  // candidate logits: code <= cut code; bit 8b + 4h <-> logit 4h + b.  The
-  // codes are those of the logits as read; a penalty that lowers keys
-  // (r > 1) cannot make a non-candidate a member, one that raises them can,
-  // so then every penalized logit is a candidate.
+  // Candidates: code <= cut code (bit 8b + 4h <-> logit 4h + b).  Whether a
+  // candidate is in the nucleus is settled when the slot is read.  The codes
+  // are those of the logits as read: a penalty that lowers keys (r > 1)
+  // cannot make a non-candidate a member, one that raises them can, so then
+  // every penalized logit is a candidate.
   uint32_t m = (le_mask(cw0, cut_code) >> 7) | (le_mask(cw1, cut_code) >> 3);
   if (rep < 1.0f) m |= spread8(bits);
   while (m) {
@@ -786,24 +791,9 @@ __device__ __forceinline__ void file_round(int l, int k, uint32_t cw0, uint32_t 
     m &= m - 1u;
     const int e = (p >> 3) | (p & 4);
     const uint32_t cd = ((p & 4) ? cw1 : cw0) >> ((p >> 3) * 8) & 0xFFu;
-    const bool pe = (bits >> e) & 1u;
-    uint32_t praw;
-    bool keep;
-    if (cd == 0u || cd == 255u) {
-      // above the window (or, penalized, anywhere outside it): exact list.
-      // A penalized logit with no entry has its key below the window.
-      praw = exact_raw(ex, nep, k * VEC + e);
-      if (praw == 0xFFFFFFFFu) continue;
-      float kp = __uint_as_float(praw << 16);
-      if (pe) kp = penalize(kp, rep);
-      keep = kp >= kp_cut;
-    } else {
-      const uint32_t o = t1p - cd;
-      praw = (o & 0x8000u) ? (o & 0x7FFFu) : (~o & 0xFFFFu);
-      if (pe) keep = penalize(__uint_as_float(praw << 16), rep) >= kp_cut;
-      else keep = cd < cut_code || __uint_as_float(praw << 16) >= kp_cut;
-    }
-    if (!keep) continue;
+    const uint32_t o = t1p - cd;
+    const uint32_t praw = (cd == 0u || cd == 255u) ? (uint32_t)SLOT_EXACT
+                          : (o & 0x8000u) ? (o & 0x7FFFu) : (~o & 0xFFFFu);
     if (nslot < CAPT) {
       const int sidx = nslot * NT_F + tid;
       const uint32_t dword = (e >> 1) == 0 ? dv.x : (e >> 1) == 1 ? dv.y : (e >> 1) == 2 ? dv.z : dv.w;
@@ -1011,8 +1001,8 @@ __global__ __launch_bounds__(NT_F) void k_pair_fast(Args a, UnitOut* uo) {
       if (k < nvec && ((code[l][0] & code[l][1]) != 0xFFFFFFFFu || cut_code >= 255u)) {
         uint32_t bits = 0u;
         if (pen) bits = (bm[(k * VEC) >> 5] >> ((k * VEC) & 31)) & 0xFFu;
-        file_round(l, k, code[l][0], code[l][1], make_uint4(0u, 0u, 0u, 0u), false, bits, cut_code,
-                   kp_cut, t1p, rep, exp_, nep, slots, nslot);
+        file_round(l, code[l][0], code[l][1], make_uint4(0u, 0u, 0u, 0u), false, bits, cut_code,
+                   t1p, rep, slots, nslot);
       }
     });
   } else {
@@ -1041,8 +1031,7 @@ __global__ __launch_bounds__(NT_F) void k_pair_fast(Args a, UnitOut* uo) {
         const uint32_t bits = v.bits;
         const uint4 dv = make_uint4(v.w[0], v.w[1], v.w[2], v.w[3]);
         (void)row_vec(v, k, c, gcq, t1q, hlane2, hist, exq, pl, aq);
-        file_round(l, k, code[l][0], code[l][1], dv, true, bits, cut_code, kp_cut, t1p, rep,
-                     exp_, nep, slots, nslot);
+        file_round(l, code[l][0], code[l][1], dv, true, bits, cut_code, t1p, rep, slots, nslot);
       }
       SDV_PIN(aq.mo);
       SDV_PIN(aq.mpen);
@@ -1110,16 +1099,20 @@ __global__ __launch_bounds__(NT_F) void k_pair_fast(Args a, UnitOut* uo) {
     }
   }
 
-  // Keys of slot s of this lane (penalty re-applied from the bitmap).
+  // Keys of slot s of this lane (penalty re-applied from the bitmap); a
+  // candidate outside the target nucleus gets zp = -inf (weight 0).
   auto slot_keys = [&](int sidx, float& zp, float& zq, int& id) {
     const int ps = pos_arr[sidx];
     id = ((ps >> 3) * NT + tid) * VEC + (ps & 7);
-    zp = __uint_as_float((uint32_t)kp_arr[sidx] << 16);
+    uint32_t praw = kp_arr[sidx];
+    if (praw == SLOT_EXACT) praw = exact_raw(exp_, nep, id);   // none: below the window
+    zp = praw == 0xFFFFFFFFu ? -INFINITY : __uint_as_float(praw << 16);
     zq = __uint_as_float((uint32_t)kq_arr[sidx] << 16);
     if (pen && ((bm[id >> 5] >> (id & 31)) & 1u)) {
       zp = penalize(zp, rep);
       zq = penalize(zq, rep);
     }
+    if (!(zp >= kp_cut)) zp = -INFINITY;
   };
 
   // ---- TV, p(x), q(x), theta, pi, acceptance ----
