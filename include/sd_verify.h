@@ -196,6 +196,19 @@ int sd_debug_run_phase(const sd_verify_args_t *args, void *workspace,
  * that phase launches nothing or the arguments are invalid. */
 const char *sd_debug_phase_kernel(const sd_verify_args_t *args, int phase);
 
+/* Test export: after phase 0 of the single-pass path (sd_debug_run_phase),
+ * the number of units (draft positions j < K_r and bonus rows of valid
+ * requests) that phase handed to the exact fallback, written to *out_count
+ * (host memory).  out_why (host, nullable): B * (K_max + 1) words, unit u =
+ * pair (r, j) at r * K_max + j, bonus row r at B * K_max + r; bit 1 a
+ * target-row stream state out of range, 2 a target cut the window did not
+ * settle, 4 and 8 the same for the draft row, 16 more nucleus candidates
+ * than slots; 0 for units not handed over.  Synchronizes `stream`.
+ * SD_EUNSUPPORTED when the arguments select the general path. */
+int sd_debug_fallback_units(const sd_verify_args_t *args, const void *workspace,
+                            size_t workspace_bytes, int32_t *out_count, uint32_t *out_why,
+                            void *stream);
+
 /* Test export: the Philox uniforms u, v for rows 0..B-1 and positions
  * 0..npos-1, written to out_u / out_v [B][npos] (fp32, exact). */
 int sd_debug_uniforms(uint64_t seed, uint64_t offset, int32_t B, int32_t npos,

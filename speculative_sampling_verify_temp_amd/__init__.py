@@ -82,6 +82,8 @@ def _load():
     lib.sd_debug_run_phase.restype = ctypes.c_int
     lib.sd_debug_phase_kernel.argtypes = [A, ctypes.c_int]
     lib.sd_debug_phase_kernel.restype = ctypes.c_char_p
+    lib.sd_debug_fallback_units.argtypes = [A, P, SZ, ctypes.POINTER(I32), P, P]
+    lib.sd_debug_fallback_units.restype = ctypes.c_int
     lib.sd_debug_uniforms.argtypes = [ctypes.c_uint64, ctypes.c_uint64, I32, I32, P, P, P]
     lib.sd_debug_uniforms.restype = ctypes.c_int
     return lib
@@ -248,6 +250,22 @@ def phase_kernel(args, phase):
     """Name of the kernel run_phase launches for `phase` (None: no launch)."""
     name = lib.sd_debug_phase_kernel(ctypes.byref(args), int(phase))
     return name.decode() if name is not None else None
+
+
+def fallback_units(args, workspace, stream=None, why=False):
+    """After run_phase(..., 0, ...) on the single-pass path: how many units
+    that phase handed to the exact fallback (and, with why=True, the reason
+    bits per unit as a numpy array)."""
+    import numpy as np
+    n = ctypes.c_int32(0)
+    nunits = args.B * (args.K_max + 1)
+    w = np.zeros(nunits, dtype=np.uint32)
+    rc = lib.sd_debug_fallback_units(ctypes.byref(args), _ptr(workspace), workspace.numel(),
+                                     ctypes.byref(n), w.ctypes.data if why else None,
+                                     _stream(stream))
+    if rc != SD_OK:
+        raise SdVerifyError(rc, "sd_debug_fallback_units")
+    return (int(n.value), w) if why else int(n.value)
 
 
 def debug_uniforms(seed, offset, B, npos, device="cuda", stream=None):

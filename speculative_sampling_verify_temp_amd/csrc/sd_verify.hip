@@ -27,7 +27,9 @@
 #include <limits.h>
 #include <math.h>
 #include <string.h>
+#include <stddef.h>
 #include <utility>
+#include <vector>
 
 #include "sd_verify.h"
 #include "sdv_device.h"
@@ -270,10 +272,14 @@ __global__ __launch_bounds__(NT_ROW) void k_finalize(Args a, const RowStat* rs, 
 struct UnitOut {
   float d, th, px, qx, pix, u, v, S;
   int32_t accept, y;
-  uint32_t flags, pad;
+  uint32_t flags, why;   // why: FB_* bits of a UO_FALLBACK unit (diagnostics)
 };
 static_assert(sizeof(UnitOut) == 48, "UnitOut layout");
 enum : uint32_t { UO_NONFINITE = 1, UO_QZERO = 2, UO_RESID_ZERO = 4, UO_SLOW = 8, UO_FALLBACK = 16 };
+// Why the single-pass kernel handed a unit to the fallback: a row's stream
+// state out of range (anchor, normalizer, list capacities), its cut not
+// settled by the window, or more nucleus candidates than slots.
+enum : uint32_t { FB_P_STATE = 1, FB_P_CUT = 2, FB_Q_STATE = 4, FB_Q_CUT = 8, FB_SLOTS = 16 };
 
 // Compile-time loop: f.template operator()<I>() for I = 0 .. N-1, so that
 // register arrays indexed by I stay in registers.
@@ -384,19 +390,40 @@ constexpr int NCOPY = 16;                    // histogram copies (bank spreading
 constexpr int E_CAP = 512;                   // exact-key entries per row
 constexpr int R_CAP = 64;                    // exact entries in the crossing bin
 constexpr int CAPT = 20;                     // nucleus slots per lane
-constexpr int PV_CAP = 448;                  // penalized vectors per row stream
+constexpr int PE_CAP = 256;                  // penalized exact entries per row
+constexpr int PL_CAP = 256;                  // distinct penalized ids per unit
 constexpr int SHP = 40;                      // fixed-point shift of exact-entry masses
 constexpr int FALLBACK_GRID = 256;           // blocks of the exact fallback launch
 static_assert(NSTG >= NSAMP && NSTG < NR, "load ring");
 
-// Exact-key list of one row: tokens whose key is not their bin's bf16 value
-// (penalized) or lies above the window.
+// Exact-key list of one row, in two regions.  The stream region holds the
+// logits found above the window while streaming, keyed as read; an entry
+// whose id is penalized is stale there.  The penalty region holds every
+// penalized logit whose penalized key reaches the window, under that key.
 struct ExactList {
   float* key;
   int32_t* id;
   uint16_t* raw;   // the unprocessed logit (bf16 bits)
   int* n;
+  float* pkey;     // penalty region
+  int32_t* pid;
+  uint16_t* praw;
+  int* np;
 };
+
+// Entry i of an exact list with ns stream entries (then the penalty
+// region); false for a stale stream entry.
+__device__ __forceinline__ bool ex_entry(const ExactList& ex, int ns, int i, const uint32_t* bm,
+                                         bool pen, float& k, int& id) {
+  if (i < ns) {
+    k = ex.key[i];
+    id = ex.id[i];
+    return !(pen && ((bm[id >> 5] >> (id & 31)) & 1u));
+  }
+  k = ex.pkey[i - ns];
+  id = ex.pid[i - ns];
+  return true;
+}
 
 struct Cut {
   int ok;         // 0: the window does not settle the cut
@@ -411,10 +438,11 @@ struct Cut {
 // reaches TP is the crossing bin.  A crossing bin that holds exact entries
 // is resolved key by key, ties kept together.  hist holds NCOPY
 // interleaved copies; lane L owns bins 4L .. 4L+3.
-__device__ __forceinline__ Cut wave_cut(const uint32_t* hist, const ExactList& ex, int ne,
-                                        uint32_t t1, float M, float c, double TP, uint32_t* ecnt,
-                                        uint64_t* emass, float* rkey, double* rmass, int* rid,
-                                        int* scnt) {
+__device__ __forceinline__ Cut wave_cut(const uint32_t* hist, const ExactList& ex, int ns, int np,
+                                        const uint32_t* bm, bool pen, uint32_t t1, float M, float c,
+                                        double TP, uint32_t* ecnt, uint64_t* emass, float* rkey,
+                                        double* rmass, int* rid, int* scnt) {
+  const int ne = ns + np;
   const int lane = threadIdx.x % WAVE;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -424,7 +452,9 @@ __device__ __forceinline__ Cut wave_cut(const uint32_t* hist, const ExactList& e
   if (lane == 0) *scnt = 0;
   __builtin_amdgcn_wave_barrier();
   for (int i = lane; i < ne; i += WAVE) {
-    const float k = ex.key[i];
+    float k;
+    int id;
+    if (!ex_entry(ex, ns, i, bm, pen, k, id)) continue;
     const uint32_t b = code1(t1, k);
     if (b < 255u) {
       atomicAdd(&ecnt[b], 1u);
@@ -506,11 +536,13 @@ __device__ __forceinline__ Cut wave_cut(const uint32_t* hist, const ExactList& e
     return out;
   }
   for (int i = lane; i < ne; i += WAVE) {
-    const float k = ex.key[i];
+    float k;
+    int id;
+    if (!ex_entry(ex, ns, i, bm, pen, k, id)) continue;
     if (code1(t1, k) == (uint32_t)b) {
       const int s = atomicAdd(scnt, 1);
       rkey[s] = k;
-      rid[s] = ex.id[i];
+      rid[s] = id;
       rmass[s] = (double)e_rel(k, M, c);
     }
   }
@@ -585,12 +617,23 @@ __device__ __forceinline__ void exact_push(const ExactList& ex, float key, int i
   }
 }
 
-// Unprocessed bf16 bits of token id from an exact list, or 0xFFFFFFFF if
-// the list has no entry for it.
-__device__ __forceinline__ uint32_t exact_raw(const ExactList& ex, int ne, int id) {
+__device__ __forceinline__ void pen_push(const ExactList& ex, float key, int id, uint32_t raw) {
+  const int ix = atomicAdd(ex.np, 1);
+  if (ix < PE_CAP) {
+    ex.pkey[ix] = key;
+    ex.pid[ix] = id;
+    ex.praw[ix] = (uint16_t)raw;
+  }
+}
+
+// Unprocessed bf16 bits of token id from an exact list (either region; both
+// store the bits as read), or 0xFFFFFFFF if the list has no entry for it.
+__device__ __forceinline__ uint32_t exact_raw(const ExactList& ex, int ns, int np, int id) {
   uint32_t raw = 0xFFFFFFFFu;
-  for (int i = 0; i < ne; ++i)
+  for (int i = 0; i < ns; ++i)
     if (ex.id[i] == id) raw = ex.raw[i];
+  for (int i = 0; i < np; ++i)
+    if (ex.pid[i] == id) raw = ex.praw[i];
   return raw;
 }
 
@@ -599,17 +642,15 @@ __device__ __forceinline__ uint32_t spread8(uint32_t b) {
   return (((b & 0xFu) * 0x204081u) & 0x01010101u) | (((((b >> 4) & 0xFu) * 0x204081u) & 0x01010101u) << 4);
 }
 
-// One 8-logit vector of a row: processed keys z, packed orderable keys o,
-// penalty bits.  Elements >= V read as -inf.
+// One 8-logit vector of a row: keys z as read, packed orderable keys o,
+// the raw words.  Elements >= V read as -inf.
 struct Vec8 {
   float z[VEC];
   uint32_t o[4];
   uint32_t w[4];
-  uint32_t bits;
 };
 
-__device__ __forceinline__ void vec8(const uint4& ld, int l, int k, int V, bool pen,
-                                     const uint32_t* bm, float rep, Vec8& v) {
+__device__ __forceinline__ void vec8(const uint4& ld, int l, int k, int V, Vec8& v) {
   v.w[0] = ld.x;
   v.w[1] = ld.y;
   v.w[2] = ld.z;
@@ -628,11 +669,12 @@ __device__ __forceinline__ void vec8(const uint4& ld, int l, int k, int V, bool 
     v.z[2 * e + 1] = __uint_as_float(v.w[e] & 0xFFFF0000u);
     v.o[e] = ord16x2(v.w[e]);
   }
-  v.bits = 0u;
-  if (pen) {
-    const int b = k * VEC;
-    v.bits = (bm[b >> 5] >> (b & 31)) & 0xFFu;
-  }
+}
+
+// Penalty bits of the 8 logits of vector k.
+__device__ __forceinline__ uint32_t pen_bits8(const uint32_t* bm, int k) {
+  const int b = k * VEC;
+  return (bm[b >> 5] >> (b & 31)) & 0xFFu;
 }
 
 __device__ __forceinline__ float max8(const float (&z)[VEC]) {
@@ -647,14 +689,6 @@ struct RowAcc {
   double Z;        // sum of exp2(key c - anchor c)
 };
 
-// Vectors holding penalized logits, captured during a stream (raw 16 bytes,
-// and k | bits << 24) and settled after it by pen_fix.
-struct PenList {
-  uint4* raw;
-  int* kb;
-  int* n;
-};
-
 __device__ __forceinline__ uint32_t pk_mad_u16(uint32_t a, uint32_t b, uint32_t c) {
   uint32_t d;
   asm("v_pk_mad_u16 %0, %1, %2, %3" : "=v"(d) : "v"(a), "s"(b), "v"(c));
@@ -662,32 +696,24 @@ __device__ __forceinline__ uint32_t pk_mad_u16(uint32_t a, uint32_t b, uint32_t 
 }
 
 // Streaming work of one vector of a row against its window: normalizer,
-// max, codes, histogram, exact entries for unpenalized keys above the
-// window.  Penalized logits are streamed as read and only their vector is
-// captured; pen_fix moves them to exact entries afterwards.  Returns the
-// two code words (bytes: codes of elements 0..3 and 4..7).
+// max, codes, histogram, exact entries for keys above the window.  Every
+// logit is streamed as read; pen_fix settles the penalized ones afterwards.
+// Returns the two code words (bytes: codes of elements 0..3 and 4..7).
 __device__ __forceinline__ uint2 row_vec(Vec8& v, int k, float c, float gc, uint32_t t1,
                                          uint32_t hlane2, uint32_t* hist, const ExactList& ex,
-                                         const PenList& pl, RowAcc& acc) {
+                                         RowAcc& acc) {
   const uint32_t t1x2 = t1 | (t1 << 16);
   uint32_t cc[4];
 #pragma unroll
   for (int e = 0; e < 4; ++e) cc[e] = code_of(t1x2, v.o[e]);
-  if (v.bits) {
-    const int ix = atomicAdd(pl.n, 1);
-    if (ix < PV_CAP) {
-      pl.raw[ix] = make_uint4(v.w[0], v.w[1], v.w[2], v.w[3]);
-      pl.kb[ix] = k | (int)(v.bits << 24);
-    }
-  }
   const uint32_t vo = pk_max(pk_max(v.o[0], v.o[1]), pk_max(v.o[2], v.o[3]));
   acc.mo = pk_max(acc.mo, vo);
   if (as_u32(__builtin_elementwise_sub_sat(as_u16x2(vo), as_u16x2(t1x2 - 0x00010001u))) != 0u) {
-    // unpenalized keys above the window: exact entries
+    // keys above the window: exact entries
 #pragma unroll
     for (int e = 0; e < VEC; ++e) {
       const uint32_t cd = (cc[e >> 1] >> ((e & 1) * 16)) & 0xFFFFu;
-      if (cd == 0u && !((v.bits >> e) & 1u))
+      if (cd == 0u)
         exact_push(ex, v.z[e], k * VEC + e, (v.w[e >> 1] >> ((e & 1) * 16)) & 0xFFFFu);
     }
   }
@@ -705,33 +731,21 @@ __device__ __forceinline__ uint2 row_vec(Vec8& v, int k, float c, float gc, uint
                     __builtin_amdgcn_perm(cc[3], cc[2], 0x06040200u));
 }
 
-// After a stream: every penalized logit leaves its count bin (it was counted
-// under its raw key) and, if it reaches the window, becomes an exact entry
-// under its penalized key; the normalizer trades the raw term for the
-// penalized one.  Block-parallel over the captured vectors.
-__device__ __forceinline__ void pen_fix(const PenList& pl, int n, uint32_t t1, float rep, float c,
+// After a stream, for one distinct penalized token (id, raw bits as read):
+// it leaves its count bin (it was counted under its raw key), and if its
+// penalized key reaches the window it becomes an entry of the penalty
+// region; the normalizer trades the raw term for the penalized one.
+__device__ __forceinline__ void pen_fix(uint32_t raw, int id, uint32_t t1, float rep, float c,
                                         float gc, uint32_t* hist, const ExactList& ex,
                                         RowAcc& acc) {
-  for (int i = threadIdx.x; i < n; i += NT_F) {
-    const uint4 w = pl.raw[i];
-    const int kb = pl.kb[i];
-    const int k = kb & 0xFFFFFF;
-    uint32_t bits = (uint32_t)kb >> 24;
-    while (bits) {
-      const int e = __builtin_ctz(bits);
-      bits &= bits - 1u;
-      const uint32_t word = (e >> 1) == 0 ? w.x : (e >> 1) == 1 ? w.y : (e >> 1) == 2 ? w.z : w.w;
-      const uint32_t raw = (word >> ((e & 1) * 16)) & 0xFFFFu;
-      const uint32_t o = raw ^ ((raw & 0x8000u) ? 0xFFFFu : 0x8000u);   // as ord16x2
-      const uint32_t cr = o >= t1 ? 0u : (t1 - o > 255u ? 255u : t1 - o);
-      if (cr >= 1u && cr <= 254u) atomicSub(&hist[cr * NCOPY], 1u);
-      const float z = __uint_as_float(raw << 16);
-      const float zp = penalize(z, rep);
-      if (code1(t1, zp) < 255u) exact_push(ex, zp, k * VEC + e, raw);
-      acc.Z += (double)fast_exp2(fmaf(zp, c, -gc)) - (double)fast_exp2(fmaf(z, c, -gc));
-      acc.mpen = fmaxf(acc.mpen, zp);
-    }
-  }
+  const uint32_t o = raw ^ ((raw & 0x8000u) ? 0xFFFFu : 0x8000u);   // as ord16x2
+  const uint32_t cr = o >= t1 ? 0u : (t1 - o > 255u ? 255u : t1 - o);
+  if (cr >= 1u && cr <= 254u) atomicSub(&hist[cr * NCOPY], 1u);
+  const float z = __uint_as_float(raw << 16);
+  const float zp = penalize(z, rep);
+  if (code1(t1, zp) < 255u) pen_push(ex, zp, id, raw);
+  acc.Z += (double)fast_exp2(fmaf(zp, c, -gc)) - (double)fast_exp2(fmaf(z, c, -gc));
+  acc.mpen = fmaxf(acc.mpen, zp);
 }
 
 // Largest processed key of a lane's stream.
@@ -748,17 +762,92 @@ __device__ __forceinline__ RowAcc row_acc_init() {
   return r;
 }
 
-// Load g of the ring: target round g (g < NR) or draft round g - NR.  The
-// load is unconditional, so the compiler's wait counts stay exact (a load
-// under a branch makes it wait for the whole ring): lanes past the row end,
-// and the draft rounds of a bonus unit, read vector 0 instead (one cache
-// line per wave) and their data is never used.
-__device__ __forceinline__ uint4 ring_load(const uint4* t4, const uint4* d4, int g, int tid, int nvec,
-                                           bool bonus) {
-  const bool drf = g >= NR;
-  const int k = (drf ? g - NR : g) * NT_F + tid;
-  const bool use = k < nvec && !(drf && bonus);
-  return (drf ? d4 : t4)[use ? k : 0];
+// A row as a buffer resource of `bytes` bytes: loads past the end return 0
+// and touch no memory.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t row_rsrc(const void* p, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, bytes, 0x00020000);
+}
+
+// Load G of the ring: target round G (G < NR) or draft round G - NR, at the
+// thread's byte offset voff.  Lanes past the row end, and every draft load
+// of a bonus unit (an empty resource), read zeros without a memory access.
+template <int G>
+__device__ __forceinline__ uint4 ring_load(__amdgpu_buffer_rsrc_t rt, __amdgpu_buffer_rsrc_t rd,
+                                           uint32_t voff) {
+  constexpr bool drf = G >= NR;
+  constexpr int round = drf ? G - NR : G;
+  const auto v = __builtin_amdgcn_raw_buffer_load_b128(drf ? rd : rt, voff, round * NT_F * 16, 0);
+  return make_uint4(v[0], v[1], v[2], v[3]);
+}
+
+// Penalty set of unit (r, j): the prior ids of request r, then the draft
+// ids x_0 .. x_{j-1} (entries; an id may repeat, the set is their union).
+struct PenSet {
+  int p0, nprior, npre;
+  bool on;
+};
+
+__device__ __forceinline__ PenSet pen_set(const Args& a, int r, int j) {
+  PenSet ps;
+  ps.p0 = 0;
+  ps.nprior = 0;
+  ps.npre = 0;
+  if (a.rep != 1.0f) {
+    if (a.prior && a.poff) {
+      ps.p0 = a.poff[r];
+      const int p1 = a.poff[r + 1];
+      ps.nprior = p1 > ps.p0 ? p1 - ps.p0 : 0;
+    }
+    ps.npre = (a.flags & SD_PENALTY_PRIOR_ONLY) ? 0 : j;
+  }
+  ps.on = ps.nprior + ps.npre > 0;
+  return ps;
+}
+
+// Entry `tid` of the penalty set, loaded in two parts by unconditional
+// buffer loads (an entry past either list reads nothing): the caller picks
+// with pen_pick once the loads are needed.
+struct PenFirst {
+  int prior, prefix;
+};
+
+__device__ __forceinline__ PenFirst pen_first(const Args& a, const PenSet& ps, int r, int tid) {
+  const __amdgpu_buffer_rsrc_t rp = row_rsrc(a.prior ? a.prior + ps.p0 : nullptr, ps.nprior * 4);
+  const __amdgpu_buffer_rsrc_t rx = row_rsrc(a.ids + (int64_t)r * a.K_max, ps.npre * 4);
+  PenFirst f;
+  f.prior = __builtin_amdgcn_raw_buffer_load_b32(rp, (uint32_t)tid * 4u, 0, 0);
+  f.prefix = __builtin_amdgcn_raw_buffer_load_b32(rx, (uint32_t)(tid - ps.nprior) * 4u, 0, 0);
+  return f;
+}
+
+__device__ __forceinline__ int pen_pick(const PenSet& ps, PenFirst f, int tid) {
+  return tid < ps.nprior ? f.prior : tid < ps.nprior + ps.npre ? f.prefix : -1;
+}
+
+// Marks the set's ids in the bitmap (cleared before a barrier) and lists
+// each distinct id once (plid; count *npl, more than PL_CAP overflow).
+// Returns the list index of id0 if this thread listed it, else -1; the
+// caller loads the logits of that id and stores them at plraw[index].  Ids
+// listed from later entries get plraw = 0xFFFFFFFF (logits not loaded).
+__device__ __forceinline__ int pen_claim(const Args& a, const PenSet& ps, int r, int V, int id0,
+                                         uint32_t* bm, int* plid, uint32_t* plraw, int* npl,
+                                         int tid) {
+  int x0 = -1;
+  auto claim = [&](int id, bool first) {
+    if (id < 0 || id >= V) return;
+    const uint32_t bit = 1u << (id & 31);
+    if (atomicOr(&bm[id >> 5], bit) & bit) return;
+    const int x = atomicAdd(npl, 1);
+    if (x >= PL_CAP) return;
+    plid[x] = id;
+    if (first) x0 = x;
+    else plraw[x] = 0xFFFFFFFFu;
+  };
+  claim(id0, true);
+  const int n = ps.nprior + ps.npre;
+  for (int e = tid + NT_F; e < n; e += NT_F)
+    claim(e < ps.nprior ? a.prior[ps.p0 + e] : a.ids[(int64_t)r * a.K_max + (e - ps.nprior)], false);
+  return x0;
 }
 
 // Files the target-nucleus tokens of round l (code words cw0, cw1) in the
@@ -833,9 +922,13 @@ __global__ __launch_bounds__(NT_F) void k_pair_fast(Args a, UnitOut* uo) {
   __shared__ double red_d[3][NT / WAVE];
   __shared__ int red_i[2][NT / WAVE];
   __shared__ CutRes s_cut[2];
-  __shared__ uint4 pv_raw[PV_CAP];
-  __shared__ int pv_kb[PV_CAP];
-  __shared__ int s_npv;
+  __shared__ float pkey_arr[2][PE_CAP];
+  __shared__ int32_t pid_arr[2][PE_CAP];
+  __shared__ uint16_t praw_arr[2][PE_CAP];
+  __shared__ int s_np[2];
+  __shared__ int plid[PL_CAP];         // distinct penalized ids
+  __shared__ uint32_t plraw[PL_CAP];    // their target | draft logits (bf16 bits)
+  __shared__ int s_npl;
 
   const int tid = threadIdx.x;
   const int lane = tid % WAVE, wv = tid / WAVE;
@@ -854,8 +947,9 @@ __global__ __launch_bounds__(NT_F) void k_pair_fast(Args a, UnitOut* uo) {
   const double tp = (double)a.top_p;
   const char* trow = target_row(a, r, j);
   const char* drow = bonus ? trow : draft_row(a, r, j);
-  const uint4* t4 = reinterpret_cast<const uint4*>(trow);
-  const uint4* d4 = reinterpret_cast<const uint4*>(drow);
+  const __amdgpu_buffer_rsrc_t rs_t = row_rsrc(trow, nvec * 16);
+  const __amdgpu_buffer_rsrc_t rs_d = row_rsrc(drow, bonus ? 0 : nvec * 16);
+  const uint32_t voff = (uint32_t)tid * 16u;
   const uint32_t hlane = (uint32_t)(tid & (NCOPY - 1)) * 4u;
   const uint32_t hlane2 = hlane | (hlane << 16);   // packed byte offset of this lane's copy
   ExactList exp_, exq;
@@ -863,34 +957,53 @@ __global__ __launch_bounds__(NT_F) void k_pair_fast(Args a, UnitOut* uo) {
   exp_.id = eid[0];
   exp_.raw = eraw[0];
   exp_.n = &s_ne[0];
+  exp_.pkey = pkey_arr[0];
+  exp_.pid = pid_arr[0];
+  exp_.praw = praw_arr[0];
+  exp_.np = &s_np[0];
   exq.key = ekey[1];
   exq.id = eid[1];
   exq.raw = eraw[1];
   exq.n = &s_ne[1];
+  exq.pkey = pkey_arr[1];
+  exq.pid = pid_arr[1];
+  exq.praw = praw_arr[1];
+  exq.np = &s_np[1];
   // per-round draw totals: the histogram is dead by the time of the draw
   double* rtw = reinterpret_cast<double*>(hist);
   static_assert(NR * (NT / WAVE) * sizeof(double) <= sizeof(hist), "rtw alias");
-  PenList pl;
-  pl.raw = pv_raw;
-  pl.kb = pv_kb;
-  pl.n = &s_npv;
-
-  // One load ring over the target row (rounds 0..NR-1) and then the draft
-  // row (rounds NR..2NR-1): NSTG loads in flight per thread throughout.
+  // One load ring over the target row (rounds 0..NR-1) and the draft row
+  // (rounds NR..2NR-1): NSTG loads in flight per thread throughout.  Then
+  // the penalty set's first entries.
   uint4 stg[NSTG];
   static_for<NSTG>([&]<int s>() __attribute__((always_inline)) {
-    stg[s] = ring_load(t4, d4, s, tid, nvec, bonus);
+    stg[s] = ring_load<s>(rs_t, rs_d, voff);
   });
+  const PenSet ps = pen_set(a, r, j);
+  const bool pen = ps.on;
+  const PenFirst pf = pen_first(a, ps, r, tid);
   if (tid == 0) {
     s_ne[0] = 0;
     s_ne[1] = 0;
-    s_npv = 0;
+    s_np[0] = 0;
+    s_np[1] = 0;
+    s_npl = 0;
   }
   for (int i = tid; i < NBIN * NCOPY; i += NT) hist[i] = 0u;
-  const bool pen = build_penalty_bitmap<NT>(a, r, j, 0, V, bm);   // synchronizes
+  if (pen)
+    for (int w = tid; w < (V + 31) / 32; w += NT) bm[w] = 0u;
+  __syncthreads();
+  // Each distinct penalized id is listed once; the thread that listed it
+  // loads its target and draft logits now (stored to the list during the
+  // target stream); they are settled after each stream.
+  const int id0 = pen_pick(ps, pf, tid);
+  const int x0 = pen ? pen_claim(a, ps, r, V, id0, bm, plid, plraw, &s_npl, tid) : -1;
+  const uint32_t goff = x0 >= 0 ? (uint32_t)id0 * 2u : 0x7FFFFFF0u;
+  const uint32_t gp = __builtin_amdgcn_raw_buffer_load_b16(rs_t, goff, 0, 0);
+  const uint32_t gq = __builtin_amdgcn_raw_buffer_load_b16(rs_d, goff, 0, 0);
   float u_j, v_j;
   uniforms(a.seed, a.offset, r, j, u_j, v_j);
-  uint32_t oflags = 0;
+  uint32_t oflags = 0, why = 0;
 
   // ---- phase A: the target row ----
   // Anchor: block max of the first NSAMP rounds; the window is the 254
@@ -900,7 +1013,7 @@ __global__ __launch_bounds__(NT_F) void k_pair_fast(Args a, UnitOut* uo) {
     const int k = l * NT + tid;
     if (k < nvec) {
       Vec8 v;
-      vec8(stg[l], l, k, V, false, bm, rep, v);
+      vec8(stg[l], l, k, V, v);
       m0 = fmaxf(m0, max8(v.z));   // logits as read: the anchor is only a reference
     }
   });
@@ -911,20 +1024,19 @@ __global__ __launch_bounds__(NT_F) void k_pair_fast(Args a, UnitOut* uo) {
 
   uint32_t code[NR][2];
   RowAcc ap = row_acc_init();
-  // The draft side computes its offsets from an opaque copy of tid, so the
-  // compiler does not keep the target's per-round offsets alive for reuse.
-  int tid_b = tid;
-  SDV_PIN(tid_b);
   static_for<NR>([&]<int l>() __attribute__((always_inline)) {
     const uint4 ld = stg[l % NSTG];
-    stg[l % NSTG] = ring_load(t4, d4, l + NSTG, l + NSTG < NR ? tid : tid_b, nvec, bonus);   // next target round, or a draft round
+    stg[l % NSTG] = ring_load<l + NSTG>(rs_t, rs_d, voff);   // next target round, or a draft round
     __builtin_amdgcn_sched_barrier(0);   // keep later rounds' loads in their rounds
+    if constexpr (l == NSTG - 1) {
+      if (x0 >= 0) plraw[x0] = (gp & 0xFFFFu) | (gq << 16);   // loaded rounds ago
+    }
     const int k = l * NT + tid;
     code[l][0] = code[l][1] = 0xFFFFFFFFu;
     if (k < nvec) {
       Vec8 v;
-      vec8(ld, l, k, V, pen, bm, rep, v);
-      const uint2 cw = row_vec(v, k, c, gcp, t1p, hlane2, hist, exp_, pl, ap);
+      vec8(ld, l, k, V, v);
+      const uint2 cw = row_vec(v, k, c, gcp, t1p, hlane2, hist, exp_, ap);
       code[l][0] = cw.x;
       code[l][1] = cw.y;
     }
@@ -934,9 +1046,15 @@ __global__ __launch_bounds__(NT_F) void k_pair_fast(Args a, UnitOut* uo) {
     SDV_PIN(code[l][0]);
     SDV_PIN(code[l][1]);
   });
-  __syncthreads();   // the target stream is done: histogram, captured vectors
-  const int npv_p = s_npv;
-  if (npv_p <= PV_CAP) pen_fix(pl, npv_p, t1p, rep, c, gcp, hist, exp_, ap);
+  __syncthreads();   // the target stream is done: histogram, stream entries, logit list
+  const int npl = s_npl;
+  if (npl <= PL_CAP)
+    for (int i = tid; i < npl; i += NT) {
+      const int id = plid[i];
+      const uint32_t g = plraw[i];
+      const uint32_t raw = g == 0xFFFFFFFFu ? reinterpret_cast<const uint16_t*>(trow)[id] : g & 0xFFFFu;
+      pen_fix(raw, id, t1p, rep, c, gcp, hist, exp_, ap);
+    }
   {
     const float wm = wave_max(row_max(ap));
     const double wz = wave_sum(ap.Z);
@@ -954,9 +1072,9 @@ __global__ __launch_bounds__(NT_F) void k_pair_fast(Args a, UnitOut* uo) {
       M = fmaxf(M, red_f[1][i]);
       Zs += red_d[0][i];
     }
-    const int ne = s_ne[0];
+    const int ne = s_ne[0], np = s_np[0];
     const bool good = anchor_ok && M > -INFINITY && M < INFINITY && Zs > 0.0 && Zs < INFINITY &&
-                      ne <= E_CAP && npv_p <= PV_CAP;
+                      ne <= E_CAP && np <= PE_CAP && npl <= PL_CAP;
     Cut cc;
     cc.ok = 0;
     cc.code = 0;
@@ -964,19 +1082,18 @@ __global__ __launch_bounds__(NT_F) void k_pair_fast(Args a, UnitOut* uo) {
     cc.zk = 0.0;
     if (good) {
       const double Zp = Zs * exp2((double)gcp - (double)M * (double)c);
-      cc = wave_cut(hist, exp_, ne, t1p, M, c, tp * Zp, ecnt, emass, rkey, rmass, rid, &s_rcnt);
+      cc = wave_cut(hist, exp_, ne, np, bm, pen, t1p, M, c, tp * Zp, ecnt, emass, rkey, rmass, rid,
+                    &s_rcnt);
     }
-    if (lane == 0) {
-      s_cut[0] = CutRes{good && cc.ok ? 1 : 0, cc.code, cc.key, M, cc.zk};
-      s_npv = 0;   // the draft stream captures into the same list
-    }
+    if (lane == 0) s_cut[0] = CutRes{good ? (cc.ok ? 1 : -1) : 0, cc.code, cc.key, M, cc.zk};
   }
   __syncthreads();
   const CutRes cp = s_cut[0];
   const float Mp = cp.M;
-  const int nep = s_ne[0];
-  if (!cp.ok) {
+  const int nep = s_ne[0], npp = s_np[0];
+  if (cp.ok != 1) {
     oflags = UO_FALLBACK;
+    why = cp.ok == 0 ? FB_P_STATE : FB_P_CUT;
     goto write_out_flags;
   }
   {
@@ -999,8 +1116,7 @@ __global__ __launch_bounds__(NT_F) void k_pair_fast(Args a, UnitOut* uo) {
     static_for<NR>([&]<int l>() __attribute__((always_inline)) {
       const int k = l * NT + tid;
       if (k < nvec && ((code[l][0] & code[l][1]) != 0xFFFFFFFFu || cut_code >= 255u)) {
-        uint32_t bits = 0u;
-        if (pen) bits = (bm[(k * VEC) >> 5] >> ((k * VEC) & 31)) & 0xFFu;
+        const uint32_t bits = (pen && rep < 1.0f) ? pen_bits8(bm, k) : 0u;
         file_round(l, code[l][0], code[l][1], make_uint4(0u, 0u, 0u, 0u), false, bits, cut_code,
                    t1p, rep, slots, nslot);
       }
@@ -1008,10 +1124,10 @@ __global__ __launch_bounds__(NT_F) void k_pair_fast(Args a, UnitOut* uo) {
   } else {
     float q0 = -INFINITY;
     static_for<NSAMP>([&]<int l>() __attribute__((always_inline)) {
-      const int k = l * NT + tid_b;
+      const int k = l * NT + tid;
       if (k < nvec) {
         Vec8 v;
-        vec8(stg[(NR + l) % NSTG], l, k, V, false, bm, rep, v);
+        vec8(stg[(NR + l) % NSTG], l, k, V, v);
         q0 = fmaxf(q0, max8(v.z));
       }
     });
@@ -1022,24 +1138,29 @@ __global__ __launch_bounds__(NT_F) void k_pair_fast(Args a, UnitOut* uo) {
     RowAcc aq = row_acc_init();
     static_for<NR>([&]<int l>() __attribute__((always_inline)) {
       const uint4 ld = stg[(NR + l) % NSTG];
-      if constexpr (l + NSTG < NR) stg[(NR + l) % NSTG] = ring_load(t4, d4, NR + l + NSTG, tid_b, nvec, bonus);
+      if constexpr (l + NSTG < NR) stg[(NR + l) % NSTG] = ring_load<NR + l + NSTG>(rs_t, rs_d, voff);
       __builtin_amdgcn_sched_barrier(0);
-      const int k = l * NT + tid_b;
+      const int k = l * NT + tid;
       if (k < nvec) {
         Vec8 v;
-        vec8(ld, l, k, V, pen, bm, rep, v);
-        const uint32_t bits = v.bits;
+        vec8(ld, l, k, V, v);
+        const uint32_t bits = (pen && rep < 1.0f) ? pen_bits8(bm, k) : 0u;
         const uint4 dv = make_uint4(v.w[0], v.w[1], v.w[2], v.w[3]);
-        (void)row_vec(v, k, c, gcq, t1q, hlane2, hist, exq, pl, aq);
+        (void)row_vec(v, k, c, gcq, t1q, hlane2, hist, exq, aq);
         file_round(l, code[l][0], code[l][1], dv, true, bits, cut_code, t1p, rep, slots, nslot);
       }
       SDV_PIN(aq.mo);
       SDV_PIN(aq.mpen);
       SDV_PIN(aq.Z);
     });
-    __syncthreads();   // the draft stream is done: histogram, captured vectors
-    const int npv_q = s_npv;
-    if (npv_q <= PV_CAP) pen_fix(pl, npv_q, t1q, rep, c, gcq, hist, exq, aq);
+    __syncthreads();   // the draft stream is done: histogram, stream entries
+    if (npl <= PL_CAP)
+      for (int i = tid; i < npl; i += NT) {
+        const int id = plid[i];
+        const uint32_t g = plraw[i];
+        const uint32_t raw = g == 0xFFFFFFFFu ? reinterpret_cast<const uint16_t*>(drow)[id] : g >> 16;
+        pen_fix(raw, id, t1q, rep, c, gcq, hist, exq, aq);
+      }
     {
       const float wm = wave_max(row_max(aq));
       const double wz = wave_sum(aq.Z);
@@ -1061,9 +1182,9 @@ __global__ __launch_bounds__(NT_F) void k_pair_fast(Args a, UnitOut* uo) {
         Zs += red_d[1][i];
         over |= red_i[0][i];
       }
-      const int ne = s_ne[1];
+      const int ne = s_ne[1], np = s_np[1];
       const bool good = anchor_q && M > -INFINITY && M < INFINITY && Zs > 0.0 && Zs < INFINITY &&
-                        ne <= E_CAP && !over && npv_q <= PV_CAP;
+                        ne <= E_CAP && np <= PE_CAP && !over;
       Cut cc;
       cc.ok = 0;
       cc.code = 0;
@@ -1071,14 +1192,17 @@ __global__ __launch_bounds__(NT_F) void k_pair_fast(Args a, UnitOut* uo) {
       cc.zk = 0.0;
       if (good) {
         const double Zqa = Zs * exp2((double)gcq - (double)M * (double)c);
-        cc = wave_cut(hist, exq, ne, t1q, M, c, tp * Zqa, ecnt, emass, rkey, rmass, rid, &s_rcnt);
+        cc = wave_cut(hist, exq, ne, np, bm, pen, t1q, M, c, tp * Zqa, ecnt, emass, rkey, rmass,
+                      rid, &s_rcnt);
       }
-      if (lane == 0) s_cut[1] = CutRes{good && cc.ok ? 1 : 0, cc.code, cc.key, M, cc.zk};
+      const int okv = over ? -2 : !good ? 0 : cc.ok ? 1 : -1;
+      if (lane == 0) s_cut[1] = CutRes{okv, cc.code, cc.key, M, cc.zk};
     }
     __syncthreads();
     const CutRes cq = s_cut[1];
-    if (!cq.ok) {
+    if (cq.ok != 1) {
       oflags = UO_FALLBACK;
+      why = cq.ok == -2 ? FB_SLOTS : cq.ok == 0 ? FB_Q_STATE : FB_Q_CUT;
       goto write_out_flags;
     }
     Mq = cq.M;
@@ -1095,6 +1219,7 @@ __global__ __launch_bounds__(NT_F) void k_pair_fast(Args a, UnitOut* uo) {
     for (int i = 0; i < NT / WAVE; ++i) over |= red_i[1][i];
     if (over) {
       oflags = UO_FALLBACK;
+      why = FB_SLOTS;
       goto write_out_flags;
     }
   }
@@ -1105,7 +1230,7 @@ __global__ __launch_bounds__(NT_F) void k_pair_fast(Args a, UnitOut* uo) {
     const int ps = pos_arr[sidx];
     id = ((ps >> 3) * NT + tid) * VEC + (ps & 7);
     uint32_t praw = kp_arr[sidx];
-    if (praw == SLOT_EXACT) praw = exact_raw(exp_, nep, id);   // none: below the window
+    if (praw == SLOT_EXACT) praw = exact_raw(exp_, nep, npp, id);   // none: below the window
     zp = praw == 0xFFFFFFFFu ? -INFINITY : __uint_as_float(praw << 16);
     zq = __uint_as_float((uint32_t)kq_arr[sidx] << 16);
     if (pen && ((bm[id >> 5] >> (id & 31)) & 1u)) {
@@ -1123,7 +1248,7 @@ __global__ __launch_bounds__(NT_F) void k_pair_fast(Args a, UnitOut* uo) {
   out.accept = 1;
   out.y = -1;
   out.flags = 0;
-  out.pad = 0;
+  out.why = 0;
   if (!bonus) {
     double acc = 0.0;
     for (int sl = 0; sl < nslot; ++sl) {
@@ -1267,7 +1392,7 @@ write_out_flags:
     o.accept = 0;
     o.y = -1;
     o.flags = oflags;
-    o.pad = 0;
+    o.why = why;
     uo[blockIdx.x] = o;
   }
 }
@@ -1892,6 +2017,51 @@ const char* sd_debug_phase_kernel(const sd_verify_args_t* args, int phase) {
   if (phase == 0) return "k_row_prepare";
   if (phase == 1) return (needs_tv(a, nullptr) && a.K_max > 0) ? "k_pair_tv" : nullptr;
   return "k_finalize";
+}
+
+int sd_debug_fallback_units(const sd_verify_args_t* args, const void* workspace,
+                            size_t workspace_bytes, int32_t* out_count, uint32_t* out_why,
+                            void* stream) {
+  int rc = check_common(args, true);
+  if (rc) return rc;
+  if (!out_count) return SD_EINVAL;
+  const Args a = make_args(args);
+  if (!(a.dtype == SD_BF16 && use_fast(a))) return SD_EUNSUPPORTED;
+  const Layout L = layout(args);
+  if (!workspace || workspace_bytes < L.total) return SD_EWORKSPACE;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  // The unit records' flags and the per-request K and T, copied to the host.
+  const int B = a.B, nunits = B * (a.K_max + 1);
+  std::vector<uint32_t> flags(2 * (size_t)nunits);   // flags, why per unit
+  std::vector<int32_t> ks(B, a.K_max);
+  std::vector<float> ts(B, 1.0f);
+  const char* uo = static_cast<const char*>(workspace) + L.uo;
+  static_assert(offsetof(UnitOut, why) == offsetof(UnitOut, flags) + 4, "UnitOut layout");
+  bool ok = hipMemcpy2DAsync(flags.data(), 2 * sizeof(uint32_t), uo + offsetof(UnitOut, flags),
+                             sizeof(UnitOut), 2 * sizeof(uint32_t), nunits, hipMemcpyDeviceToHost,
+                             st) == hipSuccess;
+  if (ok && a.kpr)
+    ok = hipMemcpyAsync(ks.data(), a.kpr, B * sizeof(int32_t), hipMemcpyDeviceToHost, st) == hipSuccess;
+  if (ok && a.temp)
+    ok = hipMemcpyAsync(ts.data(), a.temp, B * sizeof(float), hipMemcpyDeviceToHost, st) == hipSuccess;
+  if (!ok || hipStreamSynchronize(st) != hipSuccess) return SD_EHIP;
+  // Units the kernel skips (invalid request, position beyond K_r) hold no record.
+  int n = 0;
+  for (int u = 0; u < nunits; ++u) {
+    if (out_why) out_why[u] = 0u;
+    const bool bonus = u >= B * a.K_max;
+    const int r = bonus ? u - B * a.K_max : u / a.K_max;
+    const int j = bonus ? 0 : u % a.K_max;
+    const int K = ks[r];
+    const float T = ts[r];
+    if (K < 0 || K > a.K_max || (!bonus && j >= K) || !(T > 0.0f) || !(T < INFINITY)) continue;
+    if (flags[2 * u] & UO_FALLBACK) {
+      ++n;
+      if (out_why) out_why[u] = flags[2 * u + 1];
+    }
+  }
+  *out_count = n;
+  return SD_OK;
 }
 
 int sd_debug_uniforms(uint64_t seed, uint64_t offset, int32_t B, int32_t npos, float* out_u,

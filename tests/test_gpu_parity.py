@@ -297,6 +297,45 @@ def test_gpu_chi_square_law():
         assert ss.chisquare(np.bincount(a, minlength=3), exp_n).pvalue > 1e-4
 
 
+def _fast_fallbacks(w):
+    """Units of workload w that the single-pass kernel hands to its fallback."""
+    import torch
+    import speculative_sampling_verify_temp_amd as sdv
+    d = to_device(w)
+    args = sdv.make_args(d["target"], d["draft"], d["draft_ids"], d["k_per_row"],
+                         d["temperature"], w.top_p, w.rep_penalty, d["prior_ids"],
+                         d["prior_offsets"], w.tv_budget, w.seed, w.offset, w.flags)
+    assert sdv.phase_kernel(args, 0) == "k_pair_fast"
+    ws = sdv.alloc_workspace(args, d["target"].device)
+    B = w.target.shape[0]
+    acc = torch.empty(B, dtype=torch.int32, device=d["target"].device)
+    tok = torch.empty((B, w.target.shape[1]), dtype=torch.int32, device=d["target"].device)
+    sdv.run_phase(args, ws, 0, acc, tok)
+    return sdv.fallback_units(args, ws)
+
+
+@pytest.mark.parametrize("case", ["rep_below_one", "many_entries"])
+def test_single_pass_penalty_sets(case):
+    """Penalty sets settled after each stream, on the single-pass path: a
+    penalty below 1 (penalized keys rise and may enter the nucleus), and more
+    penalty entries than threads per block drawn from few distinct ids."""
+    if case == "rep_below_one":
+        kw = dict(B=4, K_max=3, V=20011, dtype="bf16", D=0.5, top_p=0.9, sigma=3.0,
+                  T_range=(0.5, 0.9), n_prior=60, rep_penalty=0.8)
+    else:
+        kw = dict(B=3, K_max=3, V=30000, dtype="bf16", D=0.5, top_p=0.9, sigma=3.0,
+                  T_range=(0.5, 0.9), n_prior=1500, prior_pool=150, rep_penalty=1.3)
+    tot = [0, 0]
+    for seed in range(3):
+        w = wl.random_case(500 + seed, **kw)
+        assert _fast_fallbacks(w) == 0
+        c, f = compare_sample(gpu_sample(w), oracle_sample(w), w)
+        tot[0] += c
+        tot[1] += f
+    print(f"{case}: checked {tot[0]} rows, near-tie rows {tot[1]}")
+    assert tot[0] >= 3
+
+
 def test_single_pass_fallback_routes():
     """bf16 + top-p cases that the single-pass kernel hands to its exact
     fallback: a flat distribution (nucleus larger than the per-lane slots), a

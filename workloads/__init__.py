@@ -129,8 +129,13 @@ def gumbel_proposal(rng, z, T, topk=None):
     return int(cand[np.argmax(z[cand] / T + g)])
 
 
-def _prior(rng, B, n, V):
-    ids = rng.integers(0, V, size=(B, n), dtype=np.int64).astype(np.int32)
+def _prior(rng, B, n, V, pool=None):
+    if pool is None:
+        ids = rng.integers(0, V, size=(B, n), dtype=np.int64).astype(np.int32)
+    else:
+        # n entries per row drawn from `pool` distinct ids (many repeats)
+        ids = np.stack([rng.choice(V, size=pool, replace=False)[rng.integers(0, pool, size=n)]
+                        for _ in range(B)]).astype(np.int32)
     offs = (np.arange(B + 1, dtype=np.int64) * n).astype(np.int32)
     return ids.reshape(-1), offs
 
@@ -265,7 +270,7 @@ def config5(seed=0, B=512, K_max=8, V=V_QWEN3, T=0.7, threshold=0.6,
 
 def random_case(seed, B=3, K_max=3, V=300, dtype="f32", sigma=2.0, corr=0.8,
                 T_range=(0.5, 1.5), top_p=1.0, rep_penalty=1.0, n_prior=0,
-                D=0.0, ragged=False, philox_seed=None, flags=0):
+                D=0.0, ragged=False, philox_seed=None, flags=0, prior_pool=None):
     """Small generic case for parity sweeps (rows span several tiles when V
     is a few thousand, with a ragged tail when V is not a tile multiple)."""
     rng = np.random.default_rng([9, seed])
@@ -281,7 +286,7 @@ def random_case(seed, B=3, K_max=3, V=300, dtype="f32", sigma=2.0, corr=0.8,
           else np.full(B, K_max)).astype(np.int32)
     pid = poff = None
     if n_prior:
-        pid, poff = _prior(rng, B, n_prior, V)
+        pid, poff = _prior(rng, B, n_prior, V, prior_pool)
     return Workload("random", dtype, tt, dd, ids, ks, T, top_p=top_p,
                     rep_penalty=rep_penalty, prior_ids=pid, prior_offsets=poff,
                     tv_budget=D, seed=seed if philox_seed is None else philox_seed,
