@@ -655,13 +655,19 @@ __device__ __forceinline__ void vec8(const uint4& ld, int l, int k, int V, Vec8&
   v.w[1] = ld.y;
   v.w[2] = ld.z;
   v.w[3] = ld.w;
-  if ((l + 1) * NT_F * VEC > V) {
-#pragma unroll
-    for (int e = 0; e < VEC; ++e)
-      if (k * VEC + e >= V) {
-        const uint32_t sh = (e & 1) * 16;
-        v.w[e >> 1] = (v.w[e >> 1] & ~(0xFFFFu << sh)) | (0xFF80u << sh);
-      }
+  // The vector that holds the row end, when V is not a multiple of 8: its
+  // elements from V on read as -inf (bf16 0xFF80).
+  if ((l + 1) * NT_F * VEC > V && (V & 7) && k == (V >> 3)) {
+    const int keep = (V & 7) * 16;   // bits of the 128 that stay
+    const uint64_t m0 = keep >= 64 ? ~0ull : (1ull << keep) - 1ull;
+    const uint64_t m1 = keep <= 64 ? 0ull : (1ull << (keep - 64)) - 1ull;
+    const uint64_t inf4 = 0xFF80FF80FF80FF80ull;
+    const uint64_t lo = (((uint64_t)v.w[1] << 32 | v.w[0]) & m0) | (inf4 & ~m0);
+    const uint64_t hi = (((uint64_t)v.w[3] << 32 | v.w[2]) & m1) | (inf4 & ~m1);
+    v.w[0] = (uint32_t)lo;
+    v.w[1] = (uint32_t)(lo >> 32);
+    v.w[2] = (uint32_t)hi;
+    v.w[3] = (uint32_t)(hi >> 32);
   }
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
@@ -709,12 +715,18 @@ __device__ __forceinline__ uint2 row_vec(Vec8& v, int k, float c, float gc, uint
   const uint32_t vo = pk_max(pk_max(v.o[0], v.o[1]), pk_max(v.o[2], v.o[3]));
   acc.mo = pk_max(acc.mo, vo);
   if (as_u32(__builtin_elementwise_sub_sat(as_u16x2(vo), as_u16x2(t1x2 - 0x00010001u))) != 0u) {
-    // keys above the window: exact entries
+    // Keys above the window (code 0) become exact entries.  Bit 2h + 16i of
+    // am is logit 2h + i (a zero 16-bit code half; codes are at most 255).
+    uint32_t am = 0u;
 #pragma unroll
-    for (int e = 0; e < VEC; ++e) {
-      const uint32_t cd = (cc[e >> 1] >> ((e & 1) * 16)) & 0xFFFFu;
-      if (cd == 0u)
-        exact_push(ex, v.z[e], k * VEC + e, (v.w[e >> 1] >> ((e & 1) * 16)) & 0xFFFFu);
+    for (int h = 0; h < 4; ++h) am |= ((~(cc[h] + 0x7FFF7FFFu) & 0x80008000u) >> 15) << (2 * h);
+    while (am) {
+      const int p = __builtin_ctz(am);
+      am &= am - 1u;
+      const int h = (p & 15) >> 1, i = p >> 4;
+      const uint32_t wd = h == 0 ? v.w[0] : h == 1 ? v.w[1] : h == 2 ? v.w[2] : v.w[3];
+      const uint32_t raw = (wd >> (16 * i)) & 0xFFFFu;
+      exact_push(ex, __uint_as_float(raw << 16), k * VEC + 2 * h + i, raw);
     }
   }
   float s[VEC];
