@@ -502,11 +502,11 @@ __device__ __forceinline__ Cut wave_cut(const uint32_t* hist, const ExactList& e
   out.zk = 0.0;
   if (!out.ok) return out;
   const int src = __builtin_ctzll(bal);
-  const int hb = __shfl(hit, src);
+  const int hb = lane_read(hit, src);
   const int b = 4 * src + hb;
-  const double c_incl = __shfl(cin, src), c_excl = __shfl(cex, src);
-  const int gcnt = __shfl((int)(hb == 0 ? cnt[0] : hb == 1 ? cnt[1] : hb == 2 ? cnt[2] : cnt[3]), src);
-  const int necb = __shfl((int)(hb == 0 ? ec[0] : hb == 1 ? ec[1] : hb == 2 ? ec[2] : ec[3]), src);
+  const double c_incl = lane_read(cin, src), c_excl = lane_read(cex, src);
+  const int gcnt = lane_read((int)(hb == 0 ? cnt[0] : hb == 1 ? cnt[1] : hb == 2 ? cnt[2] : cnt[3]), src);
+  const int necb = lane_read((int)(hb == 0 ? ec[0] : hb == 1 ? ec[1] : hb == 2 ? ec[2] : ec[3]), src);
   out.code = b;
   out.key = b > 0 ? key_of_ord16(t1 - b) : 0.0f;
   out.zk = c_incl;
@@ -514,10 +514,10 @@ __device__ __forceinline__ Cut wave_cut(const uint32_t* hist, const ExactList& e
     // A +0 crossing bin with a -0 bin just below: the two are one key.
     if (b < 254 && __float_as_uint(out.key) == 0u) {
       const int b1 = b + 1, l1 = b1 >> 2, i1 = b1 & 3;
-      const int n1 = __shfl((int)(i1 == 0 ? cnt[0] : i1 == 1 ? cnt[1] : i1 == 2 ? cnt[2] : cnt[3]), l1);
-      const int e1 = __shfl((int)(i1 == 0 ? ec[0] : i1 == 1 ? ec[1] : i1 == 2 ? ec[2] : ec[3]), l1);
+      const int n1 = lane_read((int)(i1 == 0 ? cnt[0] : i1 == 1 ? cnt[1] : i1 == 2 ? cnt[2] : cnt[3]), l1);
+      const int e1 = lane_read((int)(i1 == 0 ? ec[0] : i1 == 1 ? ec[1] : i1 == 2 ? ec[2] : ec[3]), l1);
       // cumulative through bin b + 1 = through bin b + its mass
-      const double m1 = __shfl(i1 == 0 ? mass[0] : i1 == 1 ? mass[1] : i1 == 2 ? mass[2] : mass[3], l1);
+      const double m1 = lane_read(i1 == 0 ? mass[0] : i1 == 1 ? mass[1] : i1 == 2 ? mass[2] : mass[3], l1);
       if (e1 > 0) out.ok = 0;
       else if (n1 > 0) {
         out.zk = c_incl + m1;
@@ -584,8 +584,8 @@ __device__ __forceinline__ Cut wave_cut(const uint32_t* hist, const ExactList& e
       if (rkey[q] >= me) cm += rmass[q];
   const uint64_t reach = __ballot(lane < n && cm >= TP);
   const int pick = reach ? __builtin_ctzll(reach) : n - 1;
-  out.key = __shfl(me, pick);
-  out.zk = __shfl(cm, pick);
+  out.key = lane_read(me, pick);
+  out.zk = lane_read(cm, pick);
   return out;
 }
 

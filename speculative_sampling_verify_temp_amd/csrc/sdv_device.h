@@ -166,12 +166,66 @@ __device__ __forceinline__ void uniforms(uint64_t seed, uint64_t off, int r, int
   v = (float)(b.y >> 8) * 0x1p-24f;
 }
 
-// ---- block reductions (deterministic: fixed shuffle + fixed LDS order) ----
+// ---- wave and block reductions (deterministic: fixed lane order) ----
+//
+// Cross-lane steps use DPP moves (quad permutes, row mirrors, row shifts and
+// broadcasts within the 64-lane wave), which run in the vector ALU with no
+// LDS round trip; the four 16-lane rows are combined through readlane.
+// Every lane of the wave must be active.
+
+enum : int {
+  DPP_XOR1 = 0xB1,          // quad_perm [1, 0, 3, 2]
+  DPP_XOR2 = 0x4E,          // quad_perm [2, 3, 0, 1]
+  DPP_ROW_SHR1 = 0x111,
+  DPP_ROW_SHR2 = 0x112,
+  DPP_ROW_SHR4 = 0x114,
+  DPP_ROW_SHR8 = 0x118,
+  DPP_ROW_MIRROR = 0x140,   // lane i of a row reads lane 15 - i
+  DPP_ROW_HALF_MIRROR = 0x141,   // lane i of a half row reads lane 7 - i
+  DPP_ROW_BCAST15 = 0x142,  // lane 15 of each row to the next row
+  DPP_ROW_BCAST31 = 0x143,  // lane 31 to rows 2 and 3
+};
+
+// x of the lane that DPP control CTRL names; 0 where the source lane is out
+// of its row or the destination row is masked off.
+template <int CTRL, int ROW_MASK = 0xF>
+__device__ __forceinline__ int dpp_i32(int x) {
+  return __builtin_amdgcn_update_dpp(0, x, CTRL, ROW_MASK, 0xF, true);
+}
+
+template <int CTRL, int ROW_MASK = 0xF>
+__device__ __forceinline__ float dpp_f32(float x) {
+  return __int_as_float(dpp_i32<CTRL, ROW_MASK>(__float_as_int(x)));
+}
+
+template <int CTRL, int ROW_MASK = 0xF>
+__device__ __forceinline__ double dpp_f64(double x) {
+  const uint64_t u = (uint64_t)__double_as_longlong(x);
+  const uint32_t lo = (uint32_t)dpp_i32<CTRL, ROW_MASK>((int)(uint32_t)u);
+  const uint32_t hi = (uint32_t)dpp_i32<CTRL, ROW_MASK>((int)(uint32_t)(u >> 32));
+  return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
+}
+
+// Value of x in lane `lane` (uniform across the wave).
+__device__ __forceinline__ int lane_read(int x, int lane) {
+  return __builtin_amdgcn_readlane(x, lane);
+}
+__device__ __forceinline__ float lane_read(float x, int lane) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), lane));
+}
+__device__ __forceinline__ double lane_read(double x, int lane) {
+  const uint64_t u = (uint64_t)__double_as_longlong(x);
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)u, lane);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(u >> 32), lane);
+  return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
+}
 
 __device__ __forceinline__ double wave_sum(double x) {
-#pragma unroll
-  for (int o = WAVE / 2; o > 0; o >>= 1) x += __shfl_xor(x, o);
-  return x;
+  x += dpp_f64<DPP_XOR1>(x);
+  x += dpp_f64<DPP_XOR2>(x);
+  x += dpp_f64<DPP_ROW_HALF_MIRROR>(x);
+  x += dpp_f64<DPP_ROW_MIRROR>(x);   // every lane: its row's total
+  return (lane_read(x, 0) + lane_read(x, 16)) + (lane_read(x, 32) + lane_read(x, 48));
 }
 
 __device__ __forceinline__ uint64_t wave_sum_u64(uint64_t x) {
@@ -181,9 +235,11 @@ __device__ __forceinline__ uint64_t wave_sum_u64(uint64_t x) {
 }
 
 __device__ __forceinline__ float wave_max(float x) {
-#pragma unroll
-  for (int o = WAVE / 2; o > 0; o >>= 1) x = fmaxf(x, __shfl_xor(x, o));
-  return x;
+  x = fmaxf(x, dpp_f32<DPP_XOR1>(x));
+  x = fmaxf(x, dpp_f32<DPP_XOR2>(x));
+  x = fmaxf(x, dpp_f32<DPP_ROW_HALF_MIRROR>(x));
+  x = fmaxf(x, dpp_f32<DPP_ROW_MIRROR>(x));
+  return fmaxf(fmaxf(lane_read(x, 0), lane_read(x, 16)), fmaxf(lane_read(x, 32), lane_read(x, 48)));
 }
 
 // Sum across the block; every thread gets the result.  scratch: >= NT/64 doubles.
@@ -239,24 +295,25 @@ __device__ __forceinline__ int block_or(int x, int* scratch) {
   return s;
 }
 
-// Wave-level inclusive scans (fixed shuffle order).
+// Wave-level inclusive scans: shifts within each 16-lane row, then the row
+// totals carried to the rows above (fixed order).
 __device__ __forceinline__ double wave_incl_scan(double x) {
-  const int l = threadIdx.x % WAVE;
-#pragma unroll
-  for (int o = 1; o < WAVE; o <<= 1) {
-    const double y = __shfl_up(x, o);
-    if (l >= o) x += y;
-  }
+  x += dpp_f64<DPP_ROW_SHR1>(x);
+  x += dpp_f64<DPP_ROW_SHR2>(x);
+  x += dpp_f64<DPP_ROW_SHR4>(x);
+  x += dpp_f64<DPP_ROW_SHR8>(x);
+  x += dpp_f64<DPP_ROW_BCAST15, 0xA>(x);
+  x += dpp_f64<DPP_ROW_BCAST31, 0xC>(x);
   return x;
 }
 
 __device__ __forceinline__ int wave_incl_scan_int(int x) {
-  const int l = threadIdx.x % WAVE;
-#pragma unroll
-  for (int o = 1; o < WAVE; o <<= 1) {
-    const int y = __shfl_up(x, o);
-    if (l >= o) x += y;
-  }
+  x += dpp_i32<DPP_ROW_SHR1>(x);
+  x += dpp_i32<DPP_ROW_SHR2>(x);
+  x += dpp_i32<DPP_ROW_SHR4>(x);
+  x += dpp_i32<DPP_ROW_SHR8>(x);
+  x += dpp_i32<DPP_ROW_BCAST15, 0xA>(x);
+  x += dpp_i32<DPP_ROW_BCAST31, 0xC>(x);
   return x;
 }
 
