@@ -436,19 +436,17 @@ struct Cut {
 // one wave (the caller's wave 0; no block barriers).  Window bins are
 // visited from the top; the first non-empty bin whose cumulative mass
 // reaches TP is the crossing bin.  A crossing bin that holds exact entries
-// is resolved key by key, ties kept together.  hist holds NCOPY
-// interleaved copies; lane L owns bins 4L .. 4L+3.
-__device__ __forceinline__ Cut wave_cut(const uint32_t* hist, const ExactList& ex, int ns, int np,
+// is resolved key by key, ties kept together.  A bin's count is
+// hsum - hneg (the folded histogram less the penalized logits that left
+// it); ecnt / emass (count and fixed-point mass of exact entries per bin)
+// start at zero.  Lane L owns bins 4L .. 4L+3.
+__device__ __forceinline__ Cut wave_cut(const uint32_t* hsum, const uint32_t* hneg, const ExactList& ex,
+                                        int ns, int np,
                                         const uint32_t* bm, bool pen, uint32_t t1, float M, float c,
                                         double TP, uint32_t* ecnt, uint64_t* emass, float* rkey,
                                         double* rmass, int* rid, int* scnt) {
   const int ne = ns + np;
   const int lane = threadIdx.x % WAVE;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    ecnt[4 * lane + i] = 0u;
-    emass[4 * lane + i] = 0ull;
-  }
   if (lane == 0) *scnt = 0;
   __builtin_amdgcn_wave_barrier();
   for (int i = lane; i < ne; i += WAVE) {
@@ -466,12 +464,13 @@ __device__ __forceinline__ Cut wave_cut(const uint32_t* hist, const ExactList& e
   uint32_t cnt[4], ec[4];
   double mass[4];
   double lsum = 0.0;
+  const uint4 hs = reinterpret_cast<const uint4*>(hsum)[lane];
+  const uint4 hn = reinterpret_cast<const uint4*>(hneg)[lane];
+  const uint32_t hc[4] = {hs.x - hn.x, hs.y - hn.y, hs.z - hn.z, hs.w - hn.w};
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int b = 4 * lane + i;
-    uint32_t n = 0u;
-#pragma unroll
-    for (int q = 0; q < NCOPY; ++q) n += hist[b * NCOPY + ((q + lane) & (NCOPY - 1))];
+    uint32_t n = hc[i];
     if (b == 0 || b == 255) n = 0u;   // not window bins
     cnt[i] = n;
     ec[i] = b < 255 ? ecnt[b] : 0u;
@@ -744,15 +743,16 @@ __device__ __forceinline__ uint2 row_vec(Vec8& v, int k, float c, float gc, uint
 }
 
 // After a stream, for one distinct penalized token (id, raw bits as read):
-// it leaves its count bin (it was counted under its raw key), and if its
+// it leaves its count bin (it was counted under its raw key: hneg counts
+// the departures), and if its
 // penalized key reaches the window it becomes an entry of the penalty
 // region; the normalizer trades the raw term for the penalized one.
 __device__ __forceinline__ void pen_fix(uint32_t raw, int id, uint32_t t1, float rep, float c,
-                                        float gc, uint32_t* hist, const ExactList& ex,
+                                        float gc, uint32_t* hneg, const ExactList& ex,
                                         RowAcc& acc) {
   const uint32_t o = raw ^ ((raw & 0x8000u) ? 0xFFFFu : 0x8000u);   // as ord16x2
   const uint32_t cr = o >= t1 ? 0u : (t1 - o > 255u ? 255u : t1 - o);
-  if (cr >= 1u && cr <= 254u) atomicSub(&hist[cr * NCOPY], 1u);
+  if (cr >= 1u && cr <= 254u) atomicAdd(&hneg[cr], 1u);
   const float z = __uint_as_float(raw << 16);
   const float zp = penalize(z, rep);
   if (code1(t1, zp) < 255u) pen_push(ex, zp, id, raw);
@@ -764,6 +764,17 @@ __device__ __forceinline__ void pen_fix(uint32_t raw, int id, uint32_t t1, float
 __device__ __forceinline__ float row_max(const RowAcc& acc) {
   const uint32_t o = max(acc.mo & 0xFFFFu, acc.mo >> 16);
   return fmaxf(key_of_ord16(o), acc.mpen);
+}
+
+// The NCOPY interleaved copies of the histogram summed into hsum, by the
+// whole block: four threads per bin, one 16-byte read each.
+__device__ __forceinline__ void hist_fold(const uint32_t* hist, uint32_t* hsum, int tid) {
+  static_assert(NT_F == 4 * NBIN && NCOPY == 16, "hist_fold geometry");
+  const uint4 v = reinterpret_cast<const uint4*>(hist)[tid];   // bin tid / 4, copies 4 (tid % 4) ..
+  int x = (int)(v.x + v.y + v.z + v.w);
+  x += dpp_i32<DPP_XOR1>(x);
+  x += dpp_i32<DPP_XOR2>(x);
+  if ((tid & 3) == 0) hsum[tid >> 2] = (uint32_t)x;
 }
 
 __device__ __forceinline__ RowAcc row_acc_init() {
@@ -916,6 +927,8 @@ __global__ __launch_bounds__(NT_F) void k_pair_fast(Args a, UnitOut* uo) {
   __shared__ uint16_t eraw[2][E_CAP];
   __shared__ uint32_t ecnt[NBIN];
   __shared__ uint64_t emass[NBIN];
+  __shared__ __align__(16) uint32_t hsum[NBIN];   // folded histogram
+  __shared__ __align__(16) uint32_t hneg[NBIN];   // penalized logits that left a bin
   __shared__ uint16_t kp_arr[NSLOT];   // slot (s, lane) at s * NT + lane
   __shared__ uint16_t kq_arr[NSLOT];
   __shared__ uint8_t pos_arr[NSLOT];   // 8 * round + logit within the lane's 16 bytes
@@ -941,6 +954,7 @@ __global__ __launch_bounds__(NT_F) void k_pair_fast(Args a, UnitOut* uo) {
   __shared__ int plid[PL_CAP];         // distinct penalized ids
   __shared__ uint32_t plraw[PL_CAP];    // their target | draft logits (bf16 bits)
   __shared__ int s_npl;
+  __shared__ uint32_t s_kx;             // target | draft logit of the draft token (bf16 bits)
 
   const int tid = threadIdx.x;
   const int lane = tid % WAVE, wv = tid / WAVE;
@@ -1002,6 +1016,11 @@ __global__ __launch_bounds__(NT_F) void k_pair_fast(Args a, UnitOut* uo) {
     s_npl = 0;
   }
   for (int i = tid; i < NBIN * NCOPY; i += NT) hist[i] = 0u;
+  if (tid < NBIN) {
+    hneg[tid] = 0u;
+    ecnt[tid] = 0u;
+    emass[tid] = 0ull;
+  }
   if (pen)
     for (int w = tid; w < (V + 31) / 32; w += NT) bm[w] = 0u;
   __syncthreads();
@@ -1013,6 +1032,11 @@ __global__ __launch_bounds__(NT_F) void k_pair_fast(Args a, UnitOut* uo) {
   const uint32_t goff = x0 >= 0 ? (uint32_t)id0 * 2u : 0x7FFFFFF0u;
   const uint32_t gp = __builtin_amdgcn_raw_buffer_load_b16(rs_t, goff, 0, 0);
   const uint32_t gq = __builtin_amdgcn_raw_buffer_load_b16(rs_d, goff, 0, 0);
+  // The logits of the draft token x_j, for the accept test (thread 0).
+  const int xtok = bonus ? -1 : a.ids[(int64_t)r * a.K_max + j];
+  const uint32_t xoff = (tid == 0 && xtok >= 0 && xtok < V) ? (uint32_t)xtok * 2u : 0x7FFFFFF0u;
+  const uint32_t gxp = __builtin_amdgcn_raw_buffer_load_b16(rs_t, xoff, 0, 0);
+  const uint32_t gxq = __builtin_amdgcn_raw_buffer_load_b16(rs_d, xoff, 0, 0);
   float u_j, v_j;
   uniforms(a.seed, a.offset, r, j, u_j, v_j);
   uint32_t oflags = 0, why = 0;
@@ -1040,8 +1064,9 @@ __global__ __launch_bounds__(NT_F) void k_pair_fast(Args a, UnitOut* uo) {
     const uint4 ld = stg[l % NSTG];
     stg[l % NSTG] = ring_load<l + NSTG>(rs_t, rs_d, voff);   // next target round, or a draft round
     __builtin_amdgcn_sched_barrier(0);   // keep later rounds' loads in their rounds
-    if constexpr (l == NSTG - 1) {
-      if (x0 >= 0) plraw[x0] = (gp & 0xFFFFu) | (gq << 16);   // loaded rounds ago
+    if constexpr (l == NSTG - 1) {   // loaded rounds ago
+      if (x0 >= 0) plraw[x0] = (gp & 0xFFFFu) | (gq << 16);
+      if (tid == 0) s_kx = (gxp & 0xFFFFu) | (gxq << 16);
     }
     const int k = l * NT + tid;
     code[l][0] = code[l][1] = 0xFFFFFFFFu;
@@ -1065,8 +1090,9 @@ __global__ __launch_bounds__(NT_F) void k_pair_fast(Args a, UnitOut* uo) {
       const int id = plid[i];
       const uint32_t g = plraw[i];
       const uint32_t raw = g == 0xFFFFFFFFu ? reinterpret_cast<const uint16_t*>(trow)[id] : g & 0xFFFFu;
-      pen_fix(raw, id, t1p, rep, c, gcp, hist, exp_, ap);
+      pen_fix(raw, id, t1p, rep, c, gcp, hneg, exp_, ap);
     }
+  hist_fold(hist, hsum, tid);
   {
     const float wm = wave_max(row_max(ap));
     const double wz = wave_sum(ap.Z);
@@ -1094,7 +1120,7 @@ __global__ __launch_bounds__(NT_F) void k_pair_fast(Args a, UnitOut* uo) {
     cc.zk = 0.0;
     if (good) {
       const double Zp = Zs * exp2((double)gcp - (double)M * (double)c);
-      cc = wave_cut(hist, exp_, ne, np, bm, pen, t1p, M, c, tp * Zp, ecnt, emass, rkey, rmass, rid,
+      cc = wave_cut(hsum, hneg, exp_, ne, np, bm, pen, t1p, M, c, tp * Zp, ecnt, emass, rkey, rmass, rid,
                     &s_rcnt);
     }
     if (lane == 0) s_cut[0] = CutRes{good ? (cc.ok ? 1 : -1) : 0, cc.code, cc.key, M, cc.zk};
@@ -1114,6 +1140,11 @@ __global__ __launch_bounds__(NT_F) void k_pair_fast(Args a, UnitOut* uo) {
   const double Zkp = cp.zk;
   const float ip = (float)(1.0 / Zkp);
   for (int i = tid; i < NBIN * NCOPY; i += NT) hist[i] = 0u;
+  if (tid < NBIN) {
+    hneg[tid] = 0u;
+    ecnt[tid] = 0u;
+    emass[tid] = 0ull;
+  }
 
   int nslot = 0;
   Slots slots;
@@ -1171,8 +1202,9 @@ __global__ __launch_bounds__(NT_F) void k_pair_fast(Args a, UnitOut* uo) {
         const int id = plid[i];
         const uint32_t g = plraw[i];
         const uint32_t raw = g == 0xFFFFFFFFu ? reinterpret_cast<const uint16_t*>(drow)[id] : g >> 16;
-        pen_fix(raw, id, t1q, rep, c, gcq, hist, exq, aq);
+        pen_fix(raw, id, t1q, rep, c, gcq, hneg, exq, aq);
       }
+    hist_fold(hist, hsum, tid);
     {
       const float wm = wave_max(row_max(aq));
       const double wz = wave_sum(aq.Z);
@@ -1204,7 +1236,7 @@ __global__ __launch_bounds__(NT_F) void k_pair_fast(Args a, UnitOut* uo) {
       cc.zk = 0.0;
       if (good) {
         const double Zqa = Zs * exp2((double)gcq - (double)M * (double)c);
-        cc = wave_cut(hist, exq, ne, np, bm, pen, t1q, M, c, tp * Zqa, ecnt, emass, rkey, rmass,
+        cc = wave_cut(hsum, hneg, exq, ne, np, bm, pen, t1q, M, c, tp * Zqa, ecnt, emass, rkey, rmass,
                       rid, &s_rcnt);
       }
       const int okv = over ? -2 : !good ? 0 : cc.ok ? 1 : -1;
@@ -1277,11 +1309,11 @@ __global__ __launch_bounds__(NT_F) void k_pair_fast(Args a, UnitOut* uo) {
 #pragma unroll
       for (int i = 0; i < NT / WAVE; ++i) d += red_d[2][i];
       d = fmin(d, 1.0);
-      const int x = a.ids[(int64_t)r * a.K_max + j];
+      const int x = xtok;
       float kxp = -INFINITY, kxq = -INFINITY;
       if (x >= 0 && x < V) {
-        kxp = load1<SD_BF16>(trow, x);
-        kxq = load1<SD_BF16>(drow, x);
+        kxp = __uint_as_float(s_kx << 16);
+        kxq = __uint_as_float(s_kx & 0xFFFF0000u);
         if (pen && ((bm[x >> 5] >> (x & 31)) & 1u)) {
           kxp = penalize(kxp, rep);
           kxq = penalize(kxq, rep);
