@@ -873,23 +873,13 @@ __device__ __forceinline__ int pen_claim(const Args& a, const PenSet& ps, int r,
   return x0;
 }
 
-// Files the target-nucleus tokens of round l (code words cw0, cw1) in the
-// lane's slots with their draft logits (dv; none for a bonus row).
-struct Slots {
-  uint16_t* kp;
-  uint16_t* kq;
-  uint8_t* pos;
-};
-
-// Marker in a slot's target bits: the logit lies above the window; its
-// bits are in the row's exact list (an orderable key of 0, i.e. bf16
-// 0xFFFF, never arises from a window code).
-constexpr uint16_t SLOT_EXACT = 0xFFFFu;
-
+// Files the target-nucleus candidates of round l (code words cw0, cw1) in
+// the lane's slots, one word each: draft logit bits (dv; 0 for a bonus row)
+// in bits 0-15, the target code in bits 16-23, 8 l + logit in bits 24-31.
+// Slot (s, lane) is word s * NT_F + lane.
 __device__ __forceinline__ void file_round(int l, uint32_t cw0, uint32_t cw1, uint4 dv,
                                            bool has_d, uint32_t bits, uint32_t cut_code,
-                                           uint32_t t1p, float rep, const Slots& sl,
-                                           int& nslot) {
+                                           float rep, uint32_t* slots, int& nslot) {
   const int tid = threadIdx.x;
   // Candidates: code <= cut code (bit 8b + 4h <-> logit 4h + b).  Whether a
   // candidate is in the nucleus is settled when the slot is read.  The codes
@@ -898,23 +888,29 @@ __device__ __forceinline__ void file_round(int l, uint32_t cw0, uint32_t cw1, ui
   // every penalized logit is a candidate.
   uint32_t m = (le_mask(cw0, cut_code) >> 7) | (le_mask(cw1, cut_code) >> 3);
   if (rep < 1.0f) m |= spread8(bits);
+  if (!has_d) dv = make_uint4(0u, 0u, 0u, 0u);
   while (m) {
     const int p = __builtin_ctz(m);
     m &= m - 1u;
-    const int e = (p >> 3) | (p & 4);
-    const uint32_t cd = ((p & 4) ? cw1 : cw0) >> ((p >> 3) * 8) & 0xFFu;
-    const uint32_t o = t1p - cd;
-    const uint32_t praw = (cd == 0u || cd == 255u) ? (uint32_t)SLOT_EXACT
-                          : (o & 0x8000u) ? (o & 0x7FFFu) : (~o & 0xFFFFu);
-    if (nslot < CAPT) {
-      const int sidx = nslot * NT_F + tid;
-      const uint32_t dword = (e >> 1) == 0 ? dv.x : (e >> 1) == 1 ? dv.y : (e >> 1) == 2 ? dv.z : dv.w;
-      sl.kp[sidx] = (uint16_t)praw;
-      sl.kq[sidx] = has_d ? (uint16_t)((dword >> ((e & 1) * 16)) & 0xFFFFu) : (uint16_t)0;
-      sl.pos[sidx] = (uint8_t)(l * VEC + e);
-    }
+    const int h = (p >> 2) & 1, b = p >> 3;   // logit 4h + b
+    const uint32_t cd = __builtin_amdgcn_ubfe(h ? cw1 : cw0, (uint32_t)(p & 24), 8u);
+    const uint32_t lo = h ? dv.z : dv.x, hi = h ? dv.w : dv.y;
+    const uint32_t q = __builtin_amdgcn_ubfe((b & 2) ? hi : lo, (uint32_t)((b & 1) * 16), 16u);
+    if (nslot < CAPT)
+      slots[nslot * NT_F + tid] = q | (cd << 16) | ((uint32_t)(l * VEC + 4 * h + b) << 24);
     ++nslot;
   }
+}
+
+// Marker for a slot whose target logit lies above or below the window (code
+// 0 or 255): its bits are looked up in the row's exact list.
+constexpr uint32_t SLOT_EXACT = 0xFFFFu;
+
+// Target bf16 bits of window code cd (1..254) against anchor t1, or
+// SLOT_EXACT for codes 0 and 255.
+__device__ __forceinline__ uint32_t slot_praw(uint32_t cd, uint32_t t1) {
+  const uint32_t o = t1 - cd;
+  return (cd == 0u || cd == 255u) ? SLOT_EXACT : (o & 0x8000u) ? (o & 0x7FFFu) : (~o & 0xFFFFu);
 }
 
 __global__ __launch_bounds__(NT_F) void k_pair_fast(Args a, UnitOut* uo) {
@@ -929,9 +925,7 @@ __global__ __launch_bounds__(NT_F) void k_pair_fast(Args a, UnitOut* uo) {
   __shared__ uint64_t emass[NBIN];
   __shared__ __align__(16) uint32_t hsum[NBIN];   // folded histogram
   __shared__ __align__(16) uint32_t hneg[NBIN];   // penalized logits that left a bin
-  __shared__ uint16_t kp_arr[NSLOT];   // slot (s, lane) at s * NT + lane
-  __shared__ uint16_t kq_arr[NSLOT];
-  __shared__ uint8_t pos_arr[NSLOT];   // 8 * round + logit within the lane's 16 bytes
+  __shared__ uint32_t slot_arr[NSLOT];   // slot (s, lane) at s * NT + lane (file_round)
   __shared__ float rkey[R_CAP];
   __shared__ double rmass[R_CAP];
   __shared__ int rid[R_CAP];
@@ -1147,10 +1141,6 @@ __global__ __launch_bounds__(NT_F) void k_pair_fast(Args a, UnitOut* uo) {
   }
 
   int nslot = 0;
-  Slots slots;
-  slots.kp = kp_arr;
-  slots.kq = kq_arr;
-  slots.pos = pos_arr;
 
   // ---- phase B: the draft row (pairs) or the nucleus from the codes (bonus) ----
   float Mq = 0.0f, kq_cut = 0.0f, iq = 0.0f;
@@ -1161,7 +1151,7 @@ __global__ __launch_bounds__(NT_F) void k_pair_fast(Args a, UnitOut* uo) {
       if (k < nvec && ((code[l][0] & code[l][1]) != 0xFFFFFFFFu || cut_code >= 255u)) {
         const uint32_t bits = (pen && rep < 1.0f) ? pen_bits8(bm, k) : 0u;
         file_round(l, code[l][0], code[l][1], make_uint4(0u, 0u, 0u, 0u), false, bits, cut_code,
-                   t1p, rep, slots, nslot);
+                   rep, slot_arr, nslot);
       }
     });
   } else {
@@ -1190,7 +1180,7 @@ __global__ __launch_bounds__(NT_F) void k_pair_fast(Args a, UnitOut* uo) {
         const uint32_t bits = (pen && rep < 1.0f) ? pen_bits8(bm, k) : 0u;
         const uint4 dv = make_uint4(v.w[0], v.w[1], v.w[2], v.w[3]);
         (void)row_vec(v, k, c, gcq, t1q, hlane2, hist, exq, aq);
-        file_round(l, code[l][0], code[l][1], dv, true, bits, cut_code, t1p, rep, slots, nslot);
+        file_round(l, code[l][0], code[l][1], dv, true, bits, cut_code, rep, slot_arr, nslot);
       }
       SDV_PIN(aq.mo);
       SDV_PIN(aq.mpen);
@@ -1271,12 +1261,13 @@ __global__ __launch_bounds__(NT_F) void k_pair_fast(Args a, UnitOut* uo) {
   // Keys of slot s of this lane (penalty re-applied from the bitmap); a
   // candidate outside the target nucleus gets zp = -inf (weight 0).
   auto slot_keys = [&](int sidx, float& zp, float& zq, int& id) {
-    const int ps = pos_arr[sidx];
-    id = ((ps >> 3) * NT + tid) * VEC + (ps & 7);
-    uint32_t praw = kp_arr[sidx];
+    const uint32_t w = slot_arr[sidx];
+    const uint32_t ps = w >> 24;
+    id = ((int)(ps >> 3) * NT + tid) * VEC + (int)(ps & 7);
+    uint32_t praw = slot_praw((w >> 16) & 0xFFu, t1p);
     if (praw == SLOT_EXACT) praw = exact_raw(exp_, nep, npp, id);   // none: below the window
     zp = praw == 0xFFFFFFFFu ? -INFINITY : __uint_as_float(praw << 16);
-    zq = __uint_as_float((uint32_t)kq_arr[sidx] << 16);
+    zq = __uint_as_float(w << 16);
     if (pen && ((bm[id >> 5] >> (id & 31)) & 1u)) {
       zp = penalize(zp, rep);
       zq = penalize(zq, rep);
@@ -1347,7 +1338,7 @@ __global__ __launch_bounds__(NT_F) void k_pair_fast(Args a, UnitOut* uo) {
     int sl = 0;
     for (int l = 0; l < NR; ++l) {
       double s = 0.0;
-      while (sl < nslot && (pos_arr[sl * NT + tid] >> 3) == l) {
+      while (sl < nslot && (int)(slot_arr[sl * NT + tid] >> 27) == l) {
         float zp, zq;
         int id;
         slot_keys(sl * NT + tid, zp, zq, id);
@@ -1389,7 +1380,7 @@ __global__ __launch_bounds__(NT_F) void k_pair_fast(Args a, UnitOut* uo) {
     double s = 0.0;
     int first = -1, cnt = 0;
     for (int sl = 0; sl < nslot; ++sl) {
-      if ((pos_arr[sl * NT + tid] >> 3) != lstar) continue;
+      if ((int)(slot_arr[sl * NT + tid] >> 27) != lstar) continue;
       if (first < 0) first = sl;
       ++cnt;
       float zp, zq;
