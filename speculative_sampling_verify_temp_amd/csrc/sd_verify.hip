@@ -394,6 +394,7 @@ constexpr int PE_CAP = 256;                  // penalized exact entries per row
 constexpr int PL_CAP = 256;                  // distinct penalized ids per unit
 constexpr int SHP = 40;                      // fixed-point shift of exact-entry masses
 constexpr int FALLBACK_GRID = 256;           // blocks of the exact fallback launch
+constexpr int NT_FB = 512;                   // threads per fallback block
 static_assert(NSTG >= NSAMP && NSTG < NR, "load ring");
 
 // Exact-key list of one row, in two regions.  The stream region holds the
@@ -1435,7 +1436,7 @@ write_out_flags:
 // Exact multi-pass processing of one unit k_pair_fast flagged (re-reads its
 // rows with the general-path routines).
 __device__ __forceinline__ void fallback_unit(const Args& a, UnitOut* uo, int u) {
-  constexpr int NT = NT_F;
+  constexpr int NT = NT_FB;
   __shared__ uint32_t bm[MAXV_FAST / 32];
   __shared__ uint64_t hmass[HBINS];
   __shared__ uint32_t hcnt[HBINS];
@@ -1535,18 +1536,61 @@ __device__ __forceinline__ void fallback_unit(const Args& a, UnitOut* uo, int u)
 // Exact multi-pass processing of the units k_pair_fast flagged: a small
 // grid walks every unit and takes the flagged ones (each block holds one CU,
 // so the idle cost of this launch stays a few microseconds).
-__global__ __launch_bounds__(NT_F) void k_pair_fallback(Args a, UnitOut* uo, int nunits) {
-  for (int u = blockIdx.x; u < nunits; u += gridDim.x) {
-    const Unit un = unit_of(a, u);
-    const int K = request_k(a, un.r);
-    // Units k_pair_fast skipped (invalid request, position beyond K_r) hold
-    // no output of this call: never act on them.
-    if (K < 0 || K > a.K_max || (!un.bonus && un.j >= K)) continue;
-    const float T = request_t(a, un.r);
-    if (!(T > 0.0f) || !(T < INFINITY)) continue;
-    if (!(uo[u].flags & UO_FALLBACK)) continue;
-    fallback_unit(a, uo, u);
-    __syncthreads();   // the next unit reuses the shared arrays
+// The flagged units of this call (UO_FALLBACK records of units k_pair_fast
+// processed; units it skipped, an invalid request or a position beyond
+// K_r, hold no output of this call) are enumerated the same way by every
+// block and dealt out round robin: the k-th goes to block k % gridDim.x
+// (gridDim.x = min(nunits, FALLBACK_GRID)).  Each thread tests UPT units at
+// once, so a call with nothing flagged costs one memory round trip per
+// NT_FB * UPT units.
+__global__ __launch_bounds__(NT_FB) void k_pair_fallback(Args a, UnitOut* uo, int nunits) {
+  constexpr int NT = NT_FB;
+  constexpr int UPT = 8;
+  constexpr int MINE = (NT * UPT + FALLBACK_GRID - 1) / FALLBACK_GRID;   // per block per pass
+  __shared__ int wtot[NT / WAVE];
+  __shared__ int mine[MINE];
+  __shared__ int s_n;
+  const int tid = threadIdx.x;
+  const int npairs = a.B * a.K_max;
+  int base = 0;
+  for (int c = 0; c < nunits; c += NT * UPT) {
+    uint32_t fl = 0u;   // bit i: unit c + i NT + tid is flagged
+    uint32_t fw[UPT];
+    int kr[UPT];
+    float tr[UPT];
+    static_for<UPT>([&]<int i>() __attribute__((always_inline)) {
+      const int u = min(c + i * NT + tid, nunits - 1);   // loads stay unconditional
+      const int r = u < npairs ? u / a.K_max : u - npairs;
+      fw[i] = uo[u].flags;
+      kr[i] = request_k(a, r);
+      tr[i] = request_t(a, r);
+    });
+    static_for<UPT>([&]<int i>() __attribute__((always_inline)) {
+      const int u = c + i * NT + tid;
+      const bool bonus = u >= npairs;
+      const int j = bonus ? 0 : u % a.K_max;
+      const bool valid = u < nunits && kr[i] >= 0 && kr[i] <= a.K_max && (bonus || j < kr[i]) &&
+                         tr[i] > 0.0f && tr[i] < INFINITY;
+      if (valid && (fw[i] & UO_FALLBACK)) fl |= 1u << i;
+    });
+    int total;
+    const int first = base + block_excl_scan_int<NT>(__builtin_popcount(fl), wtot, &total);
+    if (tid == 0) s_n = 0;
+    __syncthreads();
+    int rank = first;
+    while (fl) {
+      const int i = __builtin_ctz(fl);
+      fl &= fl - 1u;
+      if (rank % (int)gridDim.x == (int)blockIdx.x) mine[atomicAdd(&s_n, 1)] = c + i * NT + tid;
+      ++rank;
+    }
+    __syncthreads();
+    const int n = s_n;
+    for (int q = 0; q < n; ++q) {
+      fallback_unit(a, uo, mine[q]);
+      __syncthreads();   // the next unit reuses the shared arrays
+    }
+    base += total;
   }
 }
 
@@ -1903,7 +1947,7 @@ int run_phase(const Args& a, const Layout& L, char* ws, int phase, int32_t* acc,
     if (phase == 1) {
       const int nunits = a.B * a.K_max + a.B;
       hipLaunchKernelGGL(k_pair_fallback, dim3(nunits < FALLBACK_GRID ? nunits : FALLBACK_GRID),
-                         dim3(NT_F), 0, st, a, uo, nunits);
+                         dim3(NT_FB), 0, st, a, uo, nunits);
       return launch_status();
     }
     hipLaunchKernelGGL(k_fast_finalize, dim3(a.B), dim3(64), 0, st, a, uo, acc, tok, status, stats);

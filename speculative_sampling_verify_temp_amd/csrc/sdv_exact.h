@@ -97,7 +97,7 @@ __device__ void find_crossing(const uint64_t* hm, const uint32_t* hc, int nbins,
 // thread, fp64 totals); with top-p, three histogram passes over 12 + 12 + 8
 // bits of the orderable key with fixed-point masses find the cut key.
 template <int DT, int NT>
-__device__ RowStat row_stats_dev(const Args& a, const char* row, float c, bool pen,
+__device__ __forceinline__ RowStat row_stats_dev(const Args& a, const char* row, float c, bool pen,
                                  const uint32_t* bm, const ExactLds& L) {
   const int V = a.V, nvec = (V + VEC - 1) / VEC;
   float m = -INFINITY;
@@ -227,7 +227,7 @@ __device__ RowStat row_stats_dev(const Args& a, const char* row, float c, bool p
 
 // d = TV(p, q) = 1/2 sum |p - q| over the processed, truncated rows.
 template <int DT, int NT>
-__device__ double pair_tv_dev(const Args& a, const char* trow, const char* drow,
+__device__ __forceinline__ double pair_tv_dev(const Args& a, const char* trow, const char* drow,
                               const RowStat& P, const RowStat& Q, bool pen,
                               const uint32_t* bm, const ExactLds& L) {
   const int V = a.V, nvec = (V + VEC - 1) / VEC;
@@ -265,7 +265,7 @@ struct Drawn {
 // mass), mode 1 from p.  Two streaming passes give the chunk totals, then
 // the chunk holding t = v * S is read once more and scanned.
 template <int DT, int NT>
-__device__ Drawn draw_dev(const Args& a, const char* trow, const char* drow, const RowStat& P,
+__device__ __forceinline__ Drawn draw_dev(const Args& a, const char* trow, const char* drow, const RowStat& P,
                           const RowStat& Q, int mode, float v, bool pen, const uint32_t* bm,
                           const ExactLds& L) {
   const int V = a.V, nvec = (V + VEC - 1) / VEC;
