@@ -650,6 +650,11 @@ struct Vec8 {
   uint32_t w[4];
 };
 
+// POS: every key of the row's window is positive.  Then the orderable key
+// of a positive logit is its bits with the sign flipped, and a negative
+// logit only needs some key below the window, which the same flip gives;
+// one operation per word instead of two.
+template <bool POS = false>
 __device__ __forceinline__ void vec8(const uint4& ld, int l, int k, int V, Vec8& v) {
   v.w[0] = ld.x;
   v.w[1] = ld.y;
@@ -673,7 +678,7 @@ __device__ __forceinline__ void vec8(const uint4& ld, int l, int k, int V, Vec8&
   for (int e = 0; e < 4; ++e) {
     v.z[2 * e] = __uint_as_float(v.w[e] << 16);
     v.z[2 * e + 1] = __uint_as_float(v.w[e] & 0xFFFF0000u);
-    v.o[e] = ord16x2(v.w[e]);
+    v.o[e] = POS ? (v.w[e] ^ 0x80008000u) : ord16x2(v.w[e]);
   }
 }
 
@@ -1055,6 +1060,7 @@ __global__ __launch_bounds__(NT_F) void k_pair_fast(Args a, UnitOut* uo) {
 
   uint32_t code[NR][2];
   RowAcc ap = row_acc_init();
+  auto stream_a = [&]<bool POS>() __attribute__((always_inline)) {
   static_for<NR>([&]<int l>() __attribute__((always_inline)) {
     const uint4 ld = stg[l % NSTG];
     stg[l % NSTG] = ring_load<l + NSTG>(rs_t, rs_d, voff);   // next target round, or a draft round
@@ -1067,7 +1073,7 @@ __global__ __launch_bounds__(NT_F) void k_pair_fast(Args a, UnitOut* uo) {
     code[l][0] = code[l][1] = 0xFFFFFFFFu;
     if (k < nvec) {
       Vec8 v;
-      vec8(ld, l, k, V, v);
+      vec8<POS>(ld, l, k, V, v);
       const uint2 cw = row_vec(v, k, c, gcp, t1p, hlane2, hist, exp_, ap);
       code[l][0] = cw.x;
       code[l][1] = cw.y;
@@ -1078,6 +1084,9 @@ __global__ __launch_bounds__(NT_F) void k_pair_fast(Args a, UnitOut* uo) {
     SDV_PIN(code[l][0]);
     SDV_PIN(code[l][1]);
   });
+  };
+  if (t1p >= 0x8000u + 254u) stream_a.template operator()<true>();
+  else stream_a.template operator()<false>();
   __syncthreads();   // the target stream is done: histogram, stream entries, logit list
   const int npl = s_npl;
   if (npl <= PL_CAP)
@@ -1170,6 +1179,7 @@ __global__ __launch_bounds__(NT_F) void k_pair_fast(Args a, UnitOut* uo) {
     const uint32_t t1q = anchor_q ? min(ord16f(Gq) + UP, 0xFFFEu) + 1u : 0xFFFFu;
     const float gcq = anchor_q ? Gq * c : 0.0f;
     RowAcc aq = row_acc_init();
+    auto stream_b = [&]<bool POS>() __attribute__((always_inline)) {
     static_for<NR>([&]<int l>() __attribute__((always_inline)) {
       const uint4 ld = stg[(NR + l) % NSTG];
       if constexpr (l + NSTG < NR) stg[(NR + l) % NSTG] = ring_load<NR + l + NSTG>(rs_t, rs_d, voff);
@@ -1177,7 +1187,7 @@ __global__ __launch_bounds__(NT_F) void k_pair_fast(Args a, UnitOut* uo) {
       const int k = l * NT + tid;
       if (k < nvec) {
         Vec8 v;
-        vec8(ld, l, k, V, v);
+        vec8<POS>(ld, l, k, V, v);
         const uint32_t bits = (pen && rep < 1.0f) ? pen_bits8(bm, k) : 0u;
         const uint4 dv = make_uint4(v.w[0], v.w[1], v.w[2], v.w[3]);
         (void)row_vec(v, k, c, gcq, t1q, hlane2, hist, exq, aq);
@@ -1187,6 +1197,9 @@ __global__ __launch_bounds__(NT_F) void k_pair_fast(Args a, UnitOut* uo) {
       SDV_PIN(aq.mpen);
       SDV_PIN(aq.Z);
     });
+    };
+    if (t1q >= 0x8000u + 254u) stream_b.template operator()<true>();
+    else stream_b.template operator()<false>();
     __syncthreads();   // the draft stream is done: histogram, stream entries
     if (npl <= PL_CAP)
       for (int i = tid; i < npl; i += NT) {

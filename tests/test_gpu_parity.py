@@ -336,6 +336,30 @@ def test_single_pass_penalty_sets(case):
     assert tot[0] >= 3
 
 
+@pytest.mark.parametrize("case", ["negative", "mixed_signs"])
+def test_single_pass_window_signs(case):
+    """A window of negative keys (codes from the full orderable key), and a
+    positive window over rows that are mostly negative (negative logits must
+    code below the window)."""
+    tot = [0, 0]
+    for seed in range(3):
+        w = wl.random_case(610 + seed, B=3, K_max=3, V=20011, dtype="bf16", D=0.5, top_p=0.9,
+                           sigma=3.0, T_range=(0.5, 0.9))
+        if case == "negative":   # every logit negative
+            w.target[:] = wl.f32_to_bf16_bits(w.target_f32() - 20.0)
+            w.draft[:] = wl.f32_to_bf16_bits(w.draft_f32() - 20.0)
+        else:   # negative logits moved further down; the window stays positive
+            t, d = w.target_f32(), w.draft_f32()
+            w.target[:] = wl.f32_to_bf16_bits(np.where(t < 0, t - 10.0, t))
+            w.draft[:] = wl.f32_to_bf16_bits(np.where(d < 0, d - 10.0, d))
+        assert _fast_fallbacks(w) == 0
+        c, f = compare_sample(gpu_sample(w), oracle_sample(w), w)
+        tot[0] += c
+        tot[1] += f
+    print(f"{case}: checked {tot[0]} rows, near-tie rows {tot[1]}")
+    assert tot[0] >= 3
+
+
 def test_single_pass_fallback_routes():
     """bf16 + top-p cases that the single-pass kernel hands to its exact
     fallback: a flat distribution (nucleus larger than the per-lane slots), a
