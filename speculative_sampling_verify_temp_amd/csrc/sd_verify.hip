@@ -800,12 +800,13 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t row_rsrc(const void* p, int by
 // Load G of the ring: target round G (G < NR) or draft round G - NR, at the
 // thread's byte offset voff.  Lanes past the row end, and every draft load
 // of a bonus unit (an empty resource), read zeros without a memory access.
+// The rows are read once: the loads are marked non-temporal.
 template <int G>
 __device__ __forceinline__ uint4 ring_load(__amdgpu_buffer_rsrc_t rt, __amdgpu_buffer_rsrc_t rd,
                                            uint32_t voff) {
   constexpr bool drf = G >= NR;
   constexpr int round = drf ? G - NR : G;
-  const auto v = __builtin_amdgcn_raw_buffer_load_b128(drf ? rd : rt, voff, round * NT_F * 16, 0);
+  const auto v = __builtin_amdgcn_raw_buffer_load_b128(drf ? rd : rt, voff, round * NT_F * 16, 2);
   return make_uint4(v[0], v[1], v[2], v[3]);
 }
 
