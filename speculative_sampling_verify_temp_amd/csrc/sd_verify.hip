@@ -962,14 +962,12 @@ __global__ __launch_bounds__(NT_F) void k_pair_fast(Args a, UnitOut* uo) {
   const Unit un = unit_of(a, blockIdx.x);
   const int r = un.r;
   const bool bonus = un.bonus;
-  const int K = request_k(a, r);
-  if (K < 0 || K > a.K_max) return;
-  const int j = bonus ? K : un.j;
-  if (!bonus && j >= K) return;
-  const float T = request_t(a, r);
-  if (!(T > 0.0f) || !(T < INFINITY)) return;
+  // A pair's rows are known without any load, so its first loads go out
+  // before the request checks (a unit that then turns out invalid exits
+  // with them in flight; they read inside the rows either way).
+  int j = un.j;
+  if (bonus) j = min(max(request_k(a, r), 0), a.K_max);
   const int V = a.V, nvec = (V + VEC - 1) / VEC;
-  const float c = 1.4426950408889634f / T;
   const float rep = a.rep;
   const double tp = (double)a.top_p;
   const char* trow = target_row(a, r, j);
@@ -1009,6 +1007,19 @@ __global__ __launch_bounds__(NT_F) void k_pair_fast(Args a, UnitOut* uo) {
   const PenSet ps = pen_set(a, r, j);
   const bool pen = ps.on;
   const PenFirst pf = pen_first(a, ps, r, tid);
+  // The logits of the draft token x_j, for the accept test (thread 0).
+  const int xtok = bonus ? -1 : a.ids[(int64_t)r * a.K_max + j];
+  const uint32_t xoff = (tid == 0 && xtok >= 0 && xtok < V) ? (uint32_t)xtok * 2u : 0x7FFFFFF0u;
+  // (gathers load the aligned dword that holds the logit and pick it out
+  // where it is used, so that no earlier instruction waits for them)
+  const uint32_t gxp = __builtin_amdgcn_raw_buffer_load_b32(rs_t, xoff & ~3u, 0, 0);
+  const uint32_t gxq = __builtin_amdgcn_raw_buffer_load_b32(rs_d, xoff & ~3u, 0, 0);
+  const int K = request_k(a, r);
+  if (K < 0 || K > a.K_max) return;
+  if (bonus ? j != K : j >= K) return;
+  const float T = request_t(a, r);
+  if (!(T > 0.0f) || !(T < INFINITY)) return;
+  const float c = 1.4426950408889634f / T;
   if (tid == 0) {
     s_ne[0] = 0;
     s_ne[1] = 0;
@@ -1024,20 +1035,8 @@ __global__ __launch_bounds__(NT_F) void k_pair_fast(Args a, UnitOut* uo) {
   }
   if (pen)
     for (int w = tid; w < (V + 31) / 32; w += NT) bm[w] = 0u;
-  __syncthreads();
-  // Each distinct penalized id is listed once; the thread that listed it
-  // loads its target and draft logits now (stored to the list during the
-  // target stream); they are settled after each stream.
-  const int id0 = pen_pick(ps, pf, tid);
-  const int x0 = pen ? pen_claim(a, ps, r, V, id0, bm, plid, plraw, &s_npl, tid) : -1;
-  const uint32_t goff = x0 >= 0 ? (uint32_t)id0 * 2u : 0x7FFFFFF0u;
-  const uint32_t gp = __builtin_amdgcn_raw_buffer_load_b16(rs_t, goff, 0, 0);
-  const uint32_t gq = __builtin_amdgcn_raw_buffer_load_b16(rs_d, goff, 0, 0);
-  // The logits of the draft token x_j, for the accept test (thread 0).
-  const int xtok = bonus ? -1 : a.ids[(int64_t)r * a.K_max + j];
-  const uint32_t xoff = (tid == 0 && xtok >= 0 && xtok < V) ? (uint32_t)xtok * 2u : 0x7FFFFFF0u;
-  const uint32_t gxp = __builtin_amdgcn_raw_buffer_load_b16(rs_t, xoff, 0, 0);
-  const uint32_t gxq = __builtin_amdgcn_raw_buffer_load_b16(rs_d, xoff, 0, 0);
+  // (the anchor's block max below is the barrier that orders these clears
+  // before the penalty claim in the stream's first round)
   float u_j, v_j;
   uniforms(a.seed, a.offset, r, j, u_j, v_j);
   uint32_t oflags = 0, why = 0;
@@ -1061,14 +1060,30 @@ __global__ __launch_bounds__(NT_F) void k_pair_fast(Args a, UnitOut* uo) {
 
   uint32_t code[NR][2];
   RowAcc ap = row_acc_init();
+  int x0 = -1;          // this thread's penalty-list index (set in round 1)
+  uint32_t gp = 0u, gq = 0u, goff = 0u;
   auto stream_a = [&]<bool POS>() __attribute__((always_inline)) {
   static_for<NR>([&]<int l>() __attribute__((always_inline)) {
     const uint4 ld = stg[l % NSTG];
     stg[l % NSTG] = ring_load<l + NSTG>(rs_t, rs_d, voff);   // next target round, or a draft round
     __builtin_amdgcn_sched_barrier(0);   // keep later rounds' loads in their rounds
+    if constexpr (l == 1) {
+      // Each distinct penalized id is listed once; the thread that listed it
+      // loads its target and draft logits now (stored to the list a few
+      // rounds later); they are settled after each stream.
+      const int id0 = pen_pick(ps, pf, tid);
+      x0 = pen ? pen_claim(a, ps, r, V, id0, bm, plid, plraw, &s_npl, tid) : -1;
+      goff = x0 >= 0 ? (uint32_t)id0 * 2u : 0x7FFFFFF0u;
+      gp = __builtin_amdgcn_raw_buffer_load_b32(rs_t, goff & ~3u, 0, 0);
+      gq = __builtin_amdgcn_raw_buffer_load_b32(rs_d, goff & ~3u, 0, 0);
+    }
     if constexpr (l == NSTG - 1) {   // loaded rounds ago
-      if (x0 >= 0) plraw[x0] = (gp & 0xFFFFu) | (gq << 16);
-      if (tid == 0) s_kx = (gxp & 0xFFFFu) | (gxq << 16);
+      const uint32_t sh = (xoff & 2u) * 8u;
+      if (tid == 0) s_kx = __builtin_amdgcn_ubfe(gxp, sh, 16u) | (__builtin_amdgcn_ubfe(gxq, sh, 16u) << 16);
+    }
+    if constexpr (l == 8) {
+      const uint32_t sh = (goff & 2u) * 8u;
+      if (x0 >= 0) plraw[x0] = __builtin_amdgcn_ubfe(gp, sh, 16u) | (__builtin_amdgcn_ubfe(gq, sh, 16u) << 16);
     }
     const int k = l * NT + tid;
     code[l][0] = code[l][1] = 0xFFFFFFFFu;
