@@ -884,9 +884,10 @@ __device__ __forceinline__ int pen_claim(const Args& a, const PenSet& ps, int r,
 // the lane's slots, one word each: draft logit bits (dv; 0 for a bonus row)
 // in bits 0-15, the target code in bits 16-23, 8 l + logit in bits 24-31.
 // Slot (s, lane) is word s * NT_F + lane.
+// raise: a penalty is active and below 1 (it raises penalized keys).
 __device__ __forceinline__ void file_round(int l, uint32_t cw0, uint32_t cw1, uint4 dv,
                                            bool has_d, uint32_t bits, uint32_t cut_code,
-                                           float rep, uint32_t* slots, int& nslot) {
+                                           bool raise, uint32_t* slots, int& nslot) {
   const int tid = threadIdx.x;
   // Candidates: code <= cut code (bit 8b + 4h <-> logit 4h + b).  Whether a
   // candidate is in the nucleus is settled when the slot is read.  The codes
@@ -894,7 +895,7 @@ __device__ __forceinline__ void file_round(int l, uint32_t cw0, uint32_t cw1, ui
   // cannot make a non-candidate a member, one that raises them can, so then
   // every penalized logit is a candidate.
   uint32_t m = (le_mask(cw0, cut_code) >> 7) | (le_mask(cw1, cut_code) >> 3);
-  if (rep < 1.0f) m |= spread8(bits);
+  if (raise) m |= spread8(bits);
   if (!has_d) dv = make_uint4(0u, 0u, 0u, 0u);
   while (m) {
     const int p = __builtin_ctz(m);
@@ -924,7 +925,7 @@ __global__ __launch_bounds__(NT_F) void k_pair_fast(Args a, UnitOut* uo) {
   constexpr int NT = NT_F;
   constexpr int NSLOT = CAPT * NT;
   __shared__ uint32_t bm[MAXV_FAST / 32];
-  __shared__ __align__(16) uint32_t hist[NBIN * NCOPY];
+  __shared__ __align__(16) uint32_t hist2[2][NBIN * NCOPY];   // target row, draft row
   __shared__ float ekey[2][E_CAP];
   __shared__ int32_t eid[2][E_CAP];
   __shared__ uint16_t eraw[2][E_CAP];
@@ -995,8 +996,10 @@ __global__ __launch_bounds__(NT_F) void k_pair_fast(Args a, UnitOut* uo) {
   exq.praw = praw_arr[1];
   exq.np = &s_np[1];
   // per-round draw totals: the histogram is dead by the time of the draw
+  uint32_t* hist = hist2[0];
+  uint32_t* histq = hist2[1];
   double* rtw = reinterpret_cast<double*>(hist);
-  static_assert(NR * (NT / WAVE) * sizeof(double) <= sizeof(hist), "rtw alias");
+  static_assert(NR * (NT / WAVE) * sizeof(double) <= sizeof(hist2[0]), "rtw alias");
   // One load ring over the target row (rounds 0..NR-1) and the draft row
   // (rounds NR..2NR-1): NSTG loads in flight per thread throughout.  Then
   // the penalty set's first entries.
@@ -1027,7 +1030,7 @@ __global__ __launch_bounds__(NT_F) void k_pair_fast(Args a, UnitOut* uo) {
     s_np[1] = 0;
     s_npl = 0;
   }
-  for (int i = tid; i < NBIN * NCOPY; i += NT) hist[i] = 0u;
+  for (int i = tid; i < 2 * NBIN * NCOPY; i += NT) hist[i] = 0u;   // both rows' histograms
   if (tid < NBIN) {
     hneg[tid] = 0u;
     ecnt[tid] = 0u;
@@ -1114,10 +1117,25 @@ __global__ __launch_bounds__(NT_F) void k_pair_fast(Args a, UnitOut* uo) {
     }
   hist_fold(hist, hsum, tid);
   {
+    // The draft's anchor rides along: the block max of its first NSAMP
+    // rounds, which the ring already holds.
+    float q0 = -INFINITY;
+    if (!bonus) {
+      static_for<NSAMP>([&]<int l>() __attribute__((always_inline)) {
+        const int k = l * NT + tid;
+        if (k < nvec) {
+          Vec8 v;
+          vec8(stg[(NR + l) % NSTG], l, k, V, v);
+          q0 = fmaxf(q0, max8(v.z));
+        }
+      });
+    }
     const float wm = wave_max(row_max(ap));
+    const float wq = wave_max(q0);
     const double wz = wave_sum(ap.Z);
     if (lane == 0) {
       red_f[1][wv] = wm;
+      red_f[2][wv] = wq;
       red_d[0][wv] = wz;
     }
   }
@@ -1159,14 +1177,14 @@ __global__ __launch_bounds__(NT_F) void k_pair_fast(Args a, UnitOut* uo) {
   const uint32_t cut_code = (uint32_t)cp.code;
   const double Zkp = cp.zk;
   const float ip = (float)(1.0 / Zkp);
-  for (int i = tid; i < NBIN * NCOPY; i += NT) hist[i] = 0u;
-  if (tid < NBIN) {
+  if (tid < NBIN) {   // first touched after the draft stream's closing barrier
     hneg[tid] = 0u;
     ecnt[tid] = 0u;
     emass[tid] = 0ull;
   }
 
   int nslot = 0;
+  const bool raise = pen && rep < 1.0f;   // penalized keys rise: all are candidates
 
   // ---- phase B: the draft row (pairs) or the nucleus from the codes (bonus) ----
   float Mq = 0.0f, kq_cut = 0.0f, iq = 0.0f;
@@ -1175,22 +1193,15 @@ __global__ __launch_bounds__(NT_F) void k_pair_fast(Args a, UnitOut* uo) {
     static_for<NR>([&]<int l>() __attribute__((always_inline)) {
       const int k = l * NT + tid;
       if (k < nvec && ((code[l][0] & code[l][1]) != 0xFFFFFFFFu || cut_code >= 255u)) {
-        const uint32_t bits = (pen && rep < 1.0f) ? pen_bits8(bm, k) : 0u;
+        const uint32_t bits = raise ? pen_bits8(bm, k) : 0u;
         file_round(l, code[l][0], code[l][1], make_uint4(0u, 0u, 0u, 0u), false, bits, cut_code,
-                   rep, slot_arr, nslot);
+                   raise, slot_arr, nslot);
       }
     });
   } else {
-    float q0 = -INFINITY;
-    static_for<NSAMP>([&]<int l>() __attribute__((always_inline)) {
-      const int k = l * NT + tid;
-      if (k < nvec) {
-        Vec8 v;
-        vec8(stg[(NR + l) % NSTG], l, k, V, v);
-        q0 = fmaxf(q0, max8(v.z));
-      }
-    });
-    const float Gq = bar_max<NT>(q0, red_f[2]);   // also orders the hist clearing above
+    float Gq = red_f[2][0];
+#pragma unroll
+    for (int i = 1; i < NT / WAVE; ++i) Gq = fmaxf(Gq, red_f[2][i]);
     const bool anchor_q = Gq > -1e30f && Gq < INFINITY;
     const uint32_t t1q = anchor_q ? min(ord16f(Gq) + UP, 0xFFFEu) + 1u : 0xFFFFu;
     const float gcq = anchor_q ? Gq * c : 0.0f;
@@ -1204,10 +1215,10 @@ __global__ __launch_bounds__(NT_F) void k_pair_fast(Args a, UnitOut* uo) {
       if (k < nvec) {
         Vec8 v;
         vec8<POS>(ld, l, k, V, v);
-        const uint32_t bits = (pen && rep < 1.0f) ? pen_bits8(bm, k) : 0u;
+        const uint32_t bits = raise ? pen_bits8(bm, k) : 0u;
         const uint4 dv = make_uint4(v.w[0], v.w[1], v.w[2], v.w[3]);
-        (void)row_vec(v, k, c, gcq, t1q, hlane2, hist, exq, aq);
-        file_round(l, code[l][0], code[l][1], dv, true, bits, cut_code, rep, slot_arr, nslot);
+        (void)row_vec(v, k, c, gcq, t1q, hlane2, histq, exq, aq);
+        file_round(l, code[l][0], code[l][1], dv, true, bits, cut_code, raise, slot_arr, nslot);
       }
       SDV_PIN(aq.mo);
       SDV_PIN(aq.mpen);
@@ -1224,7 +1235,7 @@ __global__ __launch_bounds__(NT_F) void k_pair_fast(Args a, UnitOut* uo) {
         const uint32_t raw = g == 0xFFFFFFFFu ? reinterpret_cast<const uint16_t*>(drow)[id] : g >> 16;
         pen_fix(raw, id, t1q, rep, c, gcq, hneg, exq, aq);
       }
-    hist_fold(hist, hsum, tid);
+    hist_fold(histq, hsum, tid);
     {
       const float wm = wave_max(row_max(aq));
       const double wz = wave_sum(aq.Z);
