@@ -393,6 +393,7 @@ constexpr int CAPT = 20;                     // nucleus slots per lane
 constexpr int PE_CAP = 256;                  // penalized exact entries per row
 constexpr int PL_CAP = 256;                  // distinct penalized ids per unit
 constexpr int SHP = 40;                      // fixed-point shift of exact-entry masses
+constexpr int SHD = 40;                      // fixed-point shift of draw weights (each <= 1)
 constexpr int FALLBACK_GRID = 256;           // blocks of the exact fallback launch
 constexpr int NT_FB = 512;                   // threads per fallback block
 static_assert(NSTG >= NSAMP && NSTG < NR, "load ring");
@@ -939,7 +940,7 @@ __global__ __launch_bounds__(NT_F) void k_pair_fast(Args a, UnitOut* uo) {
   __shared__ int rid[R_CAP];
   __shared__ double sd[NT / WAVE];
   __shared__ double sbc[R_CAP + 4];
-  __shared__ double rt[NR + 1];
+  __shared__ unsigned long long rtf[NR + 1];   // draw: per-round weight totals (fixed point)
   __shared__ float sf[NT / WAVE];
   __shared__ int si[NT / WAVE + 8];
   __shared__ int s_ne[2];
@@ -995,11 +996,8 @@ __global__ __launch_bounds__(NT_F) void k_pair_fast(Args a, UnitOut* uo) {
   exq.pid = pid_arr[1];
   exq.praw = praw_arr[1];
   exq.np = &s_np[1];
-  // per-round draw totals: the histogram is dead by the time of the draw
   uint32_t* hist = hist2[0];
   uint32_t* histq = hist2[1];
-  double* rtw = reinterpret_cast<double*>(hist);
-  static_assert(NR * (NT / WAVE) * sizeof(double) <= sizeof(hist2[0]), "rtw alias");
   // One load ring over the target row (rounds 0..NR-1) and the draft row
   // (rounds NR..2NR-1): NSTG loads in flight per thread throughout.  Then
   // the penalty set's first entries.
@@ -1372,44 +1370,40 @@ __global__ __launch_bounds__(NT_F) void k_pair_fast(Args a, UnitOut* uo) {
   // ---- correction (rejected position) or bonus draw from the nucleus ----
   // Ascending token ids run over rounds l (ids [8192 l, 8192 l + 8192)), then
   // lanes, then the 8 logits of a lane; a lane's slots are in round order.
+  // Weights are summed in 64-bit fixed point (SHD fractional bits): the
+  // round totals by LDS atomics in any order, the crossing round by an exact
+  // scan, so every comparison with t = v S is exact and order-free.
   int mode = bonus ? 1 : 0;
-  double S = 0.0, t = 0.0, R = 0.0;
+  uint64_t Sf = 0, tf = 0, Rf = 0;
   int lstar = -1;
+  const uint64_t vk = (uint64_t)(v_j * 0x1p24f);   // v = vk 2^-24 exactly
   for (int pass = 0; pass < 2; ++pass) {
-    int sl = 0;
-    for (int l = 0; l < NR; ++l) {
-      double s = 0.0;
-      while (sl < nslot && (int)(slot_arr[sl * NT + tid] >> 27) == l) {
-        float zp, zq;
-        int id;
-        slot_keys(sl * NT + tid, zp, zq, id);
-        s += (double)nucleus_w(zp, zq, mode, Mp, ip, kq_cut, Mq, iq, c);
-        ++sl;
-      }
-      s = wave_sum(s);
-      if (tid % WAVE == 0) rtw[l * (NT / WAVE) + tid / WAVE] = s;
+    if (tid <= NR) rtf[tid] = 0ull;
+    __syncthreads();
+    for (int sl = 0; sl < nslot; ++sl) {
+      float zp, zq;
+      int id;
+      slot_keys(sl * NT + tid, zp, zq, id);
+      const float w = nucleus_w(zp, zq, mode, Mp, ip, kq_cut, Mq, iq, c);
+      if (w > 0.0f)
+        atomicAdd(&rtf[slot_arr[sl * NT + tid] >> 27], (unsigned long long)e_fixed(w, SHD));
     }
     __syncthreads();
-    if (tid < NR) {
-      double Rl = 0.0;
-      for (int w = 0; w < NT / WAVE; ++w) Rl += rtw[tid * (NT / WAVE) + w];
-      rt[tid] = Rl;
-    }
-    __syncthreads();
-    S = 0.0;
-    for (int l = 0; l < NR; ++l) S += rt[l];
-    t = (double)v_j * S;
-    double accr = 0.0, alast = 0.0;
+    Sf = 0;
+    for (int l = 0; l < NR; ++l) Sf += rtf[l];
+    tf = (__umul64hi(vk, Sf) << 40) | ((vk * Sf) >> 24);   // floor(v S), exact
+    uint64_t accr = 0, alast = 0;
     int last = -1;
     lstar = -1;
     for (int l = 0; l < NR; ++l) {
-      if (rt[l] > 0.0) { last = l; alast = accr; }
-      if (lstar < 0 && accr + rt[l] > t) { lstar = l; R = accr; }
-      accr += rt[l];
+      const uint64_t rl = rtf[l];
+      if (rl > 0) { last = l; alast = accr; }
+      if (lstar < 0 && accr + rl > tf) { lstar = l; Rf = accr; }
+      accr += rl;
     }
-    if (lstar < 0) { lstar = last; R = alast; }
-    __syncthreads();
-    if (!(S > 0.0) && mode == 0) {
+    if (lstar < 0) { lstar = last; Rf = alast; }
+    __syncthreads();   // the totals are read before a second pass clears them
+    if (Sf == 0 && mode == 0) {
       mode = 1;
       oflags |= UO_RESID_ZERO;
       continue;
@@ -1417,8 +1411,9 @@ __global__ __launch_bounds__(NT_F) void k_pair_fast(Args a, UnitOut* uo) {
     break;
   }
   {
-    // round lstar: lane totals, block scan, then the crossing lane's logits
-    double s = 0.0;
+    // round lstar: lane totals, block scan (integers below 2^53 held exactly
+    // in doubles), then the crossing lane's logits
+    uint64_t sf = 0;
     int first = -1, cnt = 0;
     for (int sl = 0; sl < nslot; ++sl) {
       if ((int)(slot_arr[sl * NT + tid] >> 27) != lstar) continue;
@@ -1427,31 +1422,31 @@ __global__ __launch_bounds__(NT_F) void k_pair_fast(Args a, UnitOut* uo) {
       float zp, zq;
       int id;
       slot_keys(sl * NT + tid, zp, zq, id);
-      s += (double)nucleus_w(zp, zq, mode, Mp, ip, kq_cut, Mq, iq, c);
+      sf += e_fixed(nucleus_w(zp, zq, mode, Mp, ip, kq_cut, Mq, iq, c), SHD);
     }
-    const double incl = block_incl_scan_fast<NT>(s, sd);
+    const uint64_t incl = (uint64_t)block_incl_scan_fast<NT>((double)sf, sd);
     if (tid == 0) { si[0] = INT_MAX; si[1] = -1; }
     __syncthreads();
-    if (lstar >= 0 && R + incl > t) atomicMin(&si[0], tid);
+    if (lstar >= 0 && Rf + incl > tf) atomicMin(&si[0], tid);
     __syncthreads();
     if (tid == si[0]) {
-      double C = R + incl - s;
+      uint64_t C = Rf + incl - sf;
       int yy = -1, lastpos = -1;
       for (int q = 0; q < cnt && yy < 0; ++q) {
         float zp, zq;
         int id;
         slot_keys((first + q) * NT + tid, zp, zq, id);
-        const float wv = nucleus_w(zp, zq, mode, Mp, ip, kq_cut, Mq, iq, c);
-        if (wv > 0.0f) lastpos = id;
-        C += (double)wv;
-        if (C > t) yy = id;
+        const uint64_t wf = e_fixed(nucleus_w(zp, zq, mode, Mp, ip, kq_cut, Mq, iq, c), SHD);
+        if (wf > 0) lastpos = id;
+        C += wf;
+        if (C > tf) yy = id;
       }
       si[1] = yy >= 0 ? yy : lastpos;
     }
     __syncthreads();
     if (tid == 0) {
       out.y = si[1];
-      out.S = (float)S;
+      out.S = (float)((double)Sf * 0x1p-40);
       out.flags |= oflags;
       uo[blockIdx.x] = out;
     }
