@@ -334,9 +334,11 @@ __device__ __forceinline__ uint32_t code1(uint32_t t1, float z) {
 }
 
 // Bytes of x that are <= t (t <= 254): the top bit of each such byte,
-// exact per byte (no borrow crosses a byte).
+// exact per byte (no borrow crosses a byte).  LOW: t < 127, when known at
+// compile time (-1: decided at run time).
+template <int LOW = -1>
 __device__ __forceinline__ uint32_t le_mask(uint32_t x, uint32_t t) {
-  if (t < 127u) {
+  if (LOW == 1 || (LOW < 0 && t < 127u)) {
     const uint32_t r = (x | 0x80808080u) - (t + 1u) * 0x01010101u;
     return ~(r | x) & 0x80808080u;
   }
@@ -886,6 +888,8 @@ __device__ __forceinline__ int pen_claim(const Args& a, const PenSet& ps, int r,
 // in bits 0-15, the target code in bits 16-23, 8 l + logit in bits 24-31.
 // Slot (s, lane) is word s * NT_F + lane.
 // raise: a penalty is active and below 1 (it raises penalized keys).
+// LOW: cut_code < 127 when known at compile time (-1: at run time).
+template <int LOW = -1>
 __device__ __forceinline__ void file_round(int l, uint32_t cw0, uint32_t cw1, uint4 dv,
                                            bool has_d, uint32_t bits, uint32_t cut_code,
                                            bool raise, uint32_t* slots, int& nslot) {
@@ -895,7 +899,7 @@ __device__ __forceinline__ void file_round(int l, uint32_t cw0, uint32_t cw1, ui
   // are those of the logits as read: a penalty that lowers keys (r > 1)
   // cannot make a non-candidate a member, one that raises them can, so then
   // every penalized logit is a candidate.
-  uint32_t m = (le_mask(cw0, cut_code) >> 7) | (le_mask(cw1, cut_code) >> 3);
+  uint32_t m = (le_mask<LOW>(cw0, cut_code) >> 7) | (le_mask<LOW>(cw1, cut_code) >> 3);
   if (raise) m |= spread8(bits);
   if (!has_d) dv = make_uint4(0u, 0u, 0u, 0u);
   while (m) {
@@ -1204,7 +1208,7 @@ __global__ __launch_bounds__(NT_F) void k_pair_fast(Args a, UnitOut* uo) {
     const uint32_t t1q = anchor_q ? min(ord16f(Gq) + UP, 0xFFFEu) + 1u : 0xFFFFu;
     const float gcq = anchor_q ? Gq * c : 0.0f;
     RowAcc aq = row_acc_init();
-    auto stream_b = [&]<bool POS>() __attribute__((always_inline)) {
+    auto stream_b = [&]<bool POS, int LOW>() __attribute__((always_inline)) {
     static_for<NR>([&]<int l>() __attribute__((always_inline)) {
       const uint4 ld = stg[(NR + l) % NSTG];
       if constexpr (l + NSTG < NR) stg[(NR + l) % NSTG] = ring_load<NR + l + NSTG>(rs_t, rs_d, voff);
@@ -1216,15 +1220,22 @@ __global__ __launch_bounds__(NT_F) void k_pair_fast(Args a, UnitOut* uo) {
         const uint32_t bits = raise ? pen_bits8(bm, k) : 0u;
         const uint4 dv = make_uint4(v.w[0], v.w[1], v.w[2], v.w[3]);
         (void)row_vec(v, k, c, gcq, t1q, hlane2, histq, exq, aq);
-        file_round(l, code[l][0], code[l][1], dv, true, bits, cut_code, raise, slot_arr, nslot);
+        file_round<LOW>(l, code[l][0], code[l][1], dv, true, bits, cut_code, raise, slot_arr, nslot);
       }
       SDV_PIN(aq.mo);
       SDV_PIN(aq.mpen);
       SDV_PIN(aq.Z);
     });
     };
-    if (t1q >= 0x8000u + 254u) stream_b.template operator()<true>();
-    else stream_b.template operator()<false>();
+    // (instances by window sign and by the target cut's half of the code range)
+    const bool posq = t1q >= 0x8000u + 254u, low = cut_code < 127u;
+    if (posq) {
+      if (low) stream_b.template operator()<true, 1>();
+      else stream_b.template operator()<true, 0>();
+    } else {
+      if (low) stream_b.template operator()<false, 1>();
+      else stream_b.template operator()<false, 0>();
+    }
     __syncthreads();   // the draft stream is done: histogram, stream entries
     if (npl <= PL_CAP)
       for (int i = tid; i < npl; i += NT) {
