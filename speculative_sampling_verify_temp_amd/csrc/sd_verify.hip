@@ -1072,6 +1072,7 @@ __global__ __launch_bounds__(NT_F) void k_pair_fast(Args a, UnitOut* uo) {
     const uint4 ld = stg[l % NSTG];
     stg[l % NSTG] = ring_load<l + NSTG>(rs_t, rs_d, voff);   // next target round, or a draft round
     __builtin_amdgcn_sched_barrier(0);   // keep later rounds' loads in their rounds
+    if constexpr (l % 5 == 0) __builtin_amdgcn_s_setprio(3 - l / 5);   // lagging waves first
     if constexpr (l == 1) {
       // Each distinct penalized id is listed once; the thread that listed it
       // loads its target and draft logits now (stored to the list a few
@@ -1213,6 +1214,7 @@ __global__ __launch_bounds__(NT_F) void k_pair_fast(Args a, UnitOut* uo) {
       const uint4 ld = stg[(NR + l) % NSTG];
       if constexpr (l + NSTG < NR) stg[(NR + l) % NSTG] = ring_load<NR + l + NSTG>(rs_t, rs_d, voff);
       __builtin_amdgcn_sched_barrier(0);
+      if constexpr (l % 5 == 0) __builtin_amdgcn_s_setprio(3 - l / 5);
       const int k = l * NT + tid;
       if (k < nvec) {
         Vec8 v;
