@@ -926,6 +926,32 @@ __device__ __forceinline__ uint32_t slot_praw(uint32_t cd, uint32_t t1) {
   return (cd == 0u || cd == 255u) ? SLOT_EXACT : (o & 0x8000u) ? (o & 0x7FFFu) : (~o & 0xFFFFu);
 }
 
+// Two zero words that stand in for an absent per-request array, so that a
+// block can issue all of its request loads at once.
+__device__ int32_t g_zero_words[2];
+
+struct ReqWords {
+  uint64_t off;        // two words: the request's prior-id list bounds
+  uint32_t k, t, x;    // K, T (bits), the draft token
+};
+
+// The four scalar loads issued back to back and awaited once (the compiler
+// would otherwise wait for each before issuing the next).  Every pointer
+// must address readable words.
+__device__ __forceinline__ ReqWords request_words(const int32_t* po, const int32_t* pk,
+                                                  const int32_t* pt, const int32_t* px) {
+  ReqWords w;
+  asm volatile(
+      "s_load_dwordx2 %0, %4, 0x0\n\t"
+      "s_load_dword %1, %5, 0x0\n\t"
+      "s_load_dword %2, %6, 0x0\n\t"
+      "s_load_dword %3, %7, 0x0\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&s"(w.off), "=&s"(w.k), "=&s"(w.t), "=&s"(w.x)
+      : "s"(po), "s"(pk), "s"(pt), "s"(px));
+  return w;
+}
+
 __global__ __launch_bounds__(NT_F) void k_pair_fast(Args a, UnitOut* uo) {
   constexpr int NT = NT_F;
   constexpr int NSLOT = CAPT * NT;
@@ -962,6 +988,7 @@ __global__ __launch_bounds__(NT_F) void k_pair_fast(Args a, UnitOut* uo) {
   __shared__ uint32_t plraw[PL_CAP];    // their target | draft logits (bf16 bits)
   __shared__ int s_npl;
   __shared__ uint32_t s_kx;             // target | draft logit of the draft token (bf16 bits)
+  __shared__ double s_xe[2];            // draft token: p(x_j); exp part of q(x_j)
 
   const int tid = threadIdx.x;
   const int lane = tid % WAVE, wv = tid / WAVE;
@@ -1009,22 +1036,7 @@ __global__ __launch_bounds__(NT_F) void k_pair_fast(Args a, UnitOut* uo) {
   static_for<NSTG>([&]<int s>() __attribute__((always_inline)) {
     stg[s] = ring_load<s>(rs_t, rs_d, voff);
   });
-  const PenSet ps = pen_set(a, r, j);
-  const bool pen = ps.on;
-  const PenFirst pf = pen_first(a, ps, r, tid);
-  // The logits of the draft token x_j, for the accept test (thread 0).
-  const int xtok = bonus ? -1 : a.ids[(int64_t)r * a.K_max + j];
-  const uint32_t xoff = (tid == 0 && xtok >= 0 && xtok < V) ? (uint32_t)xtok * 2u : 0x7FFFFFF0u;
-  // (gathers load the aligned dword that holds the logit and pick it out
-  // where it is used, so that no earlier instruction waits for them)
-  const uint32_t gxp = __builtin_amdgcn_raw_buffer_load_b32(rs_t, xoff & ~3u, 0, 0);
-  const uint32_t gxq = __builtin_amdgcn_raw_buffer_load_b32(rs_d, xoff & ~3u, 0, 0);
-  const int K = request_k(a, r);
-  if (K < 0 || K > a.K_max) return;
-  if (bonus ? j != K : j >= K) return;
-  const float T = request_t(a, r);
-  if (!(T > 0.0f) || !(T < INFINITY)) return;
-  const float c = 1.4426950408889634f / T;
+  __builtin_amdgcn_sched_barrier(0);   // the ring's loads go out first
   if (tid == 0) {
     s_ne[0] = 0;
     s_ne[1] = 0;
@@ -1038,12 +1050,39 @@ __global__ __launch_bounds__(NT_F) void k_pair_fast(Args a, UnitOut* uo) {
     ecnt[tid] = 0u;
     emass[tid] = 0ull;
   }
+  float u_j, v_j;
+  uniforms(a.seed, a.offset, r, j, u_j, v_j);
+  // The request's words in one round trip: the prior-id list bounds, the
+  // draft token x_j, K and T (an absent array, and the draft token of a
+  // bonus unit, read a zero word instead, which is then not used).
+  const bool pen_prior = a.rep != 1.0f && a.prior && a.poff;
+  const ReqWords rw = request_words(pen_prior ? a.poff + r : g_zero_words,
+                                    a.kpr ? a.kpr + r : g_zero_words,
+                                    a.temp ? reinterpret_cast<const int32_t*>(a.temp + r) : g_zero_words,
+                                    bonus ? g_zero_words : a.ids + (int64_t)r * a.K_max + j);
+  const int K = a.kpr ? (int)rw.k : a.K_max;
+  const float T = a.temp ? __uint_as_float(rw.t) : 1.0f;
+  if (K < 0 || K > a.K_max || (bonus ? j != K : j >= K) || !(T > 0.0f) || !(T < INFINITY)) return;
+  const float c = 1.4426950408889634f / T;
+  const int po0 = (int)(uint32_t)rw.off, po1 = (int)(uint32_t)(rw.off >> 32);
+  PenSet ps;
+  ps.p0 = pen_prior ? po0 : 0;
+  ps.nprior = pen_prior && po1 > po0 ? po1 - po0 : 0;
+  ps.npre = a.rep != 1.0f && !(a.flags & SD_PENALTY_PRIOR_ONLY) ? j : 0;
+  ps.on = ps.nprior + ps.npre > 0;
+  const bool pen = ps.on;
+  const PenFirst pf = pen_first(a, ps, r, tid);
+  // The logits of the draft token x_j, for the accept test (thread 0).
+  const int xtok = bonus ? -1 : (int)rw.x;
+  const uint32_t xoff = (tid == 0 && xtok >= 0 && xtok < V) ? (uint32_t)xtok * 2u : 0x7FFFFFF0u;
+  // (gathers load the aligned dword that holds the logit and pick it out
+  // where it is used, so that no earlier instruction waits for them)
+  const uint32_t gxp = __builtin_amdgcn_raw_buffer_load_b32(rs_t, xoff & ~3u, 0, 0);
+  const uint32_t gxq = __builtin_amdgcn_raw_buffer_load_b32(rs_d, xoff & ~3u, 0, 0);
   if (pen)
     for (int w = tid; w < (V + 31) / 32; w += NT) bm[w] = 0u;
   // (the anchor's block max below is the barrier that orders these clears
   // before the penalty claim in the stream's first round)
-  float u_j, v_j;
-  uniforms(a.seed, a.offset, r, j, u_j, v_j);
   uint32_t oflags = 0, why = 0;
 
   // ---- phase A: the target row ----
@@ -1188,6 +1227,18 @@ __global__ __launch_bounds__(NT_F) void k_pair_fast(Args a, UnitOut* uo) {
 
   int nslot = 0;
   const bool raise = pen && rep < 1.0f;   // penalized keys rise: all are candidates
+  // Processed keys of the draft token x_j in the target and draft rows.
+  auto draft_keys = [&](float& kxp, float& kxq) {
+    kxp = kxq = -INFINITY;
+    if (xtok >= 0 && xtok < V) {
+      kxp = __uint_as_float(s_kx << 16);
+      kxq = __uint_as_float(s_kx & 0xFFFF0000u);
+      if (pen && ((bm[xtok >> 5] >> (xtok & 31)) & 1u)) {
+        kxp = penalize(kxp, rep);
+        kxq = penalize(kxq, rep);
+      }
+    }
+  };
 
   // ---- phase B: the draft row (pairs) or the nucleus from the codes (bonus) ----
   float Mq = 0.0f, kq_cut = 0.0f, iq = 0.0f;
@@ -1283,6 +1334,23 @@ __global__ __launch_bounds__(NT_F) void k_pair_fast(Args a, UnitOut* uo) {
       }
       const int okv = over ? -2 : !good ? 0 : cc.ok ? 1 : -1;
       if (lane == 0) s_cut[1] = CutRes{okv, cc.code, cc.key, M, cc.zk};
+    } else if (wv == 1 && lane < 2) {
+      // Meanwhile the draft token's fp64 exponentials: lane 0 p(x_j) (the
+      // target cut is known), lane 1 the draft's, which its normalizer and
+      // cut complete later.
+      float M = Mp;
+      if (lane == 1) {
+        M = red_f[3][0];
+#pragma unroll
+        for (int i = 1; i < NT / WAVE; ++i) M = fmaxf(M, red_f[3][i]);
+      }
+      float kxp, kxq;
+      draft_keys(kxp, kxq);
+      const float kx = lane == 0 ? kxp : kxq;
+      const double e = exp(((double)kx - (double)M) / (double)T);
+      RowStat P;
+      P.kord = ord_key(kp_cut);
+      s_xe[lane] = lane == 1 ? e : kept(P, ord_key(kx)) ? e / Zkp : 0.0;
     }
     __syncthreads();
     const CutRes cq = s_cut[1];
@@ -1352,20 +1420,12 @@ __global__ __launch_bounds__(NT_F) void k_pair_fast(Args a, UnitOut* uo) {
 #pragma unroll
       for (int i = 0; i < NT / WAVE; ++i) d += red_d[2][i];
       d = fmin(d, 1.0);
-      const int x = xtok;
-      float kxp = -INFINITY, kxq = -INFINITY;
-      if (x >= 0 && x < V) {
-        kxp = __uint_as_float(s_kx << 16);
-        kxq = __uint_as_float(s_kx & 0xFFFF0000u);
-        if (pen && ((bm[x >> 5] >> (x & 31)) & 1u)) {
-          kxp = penalize(kxp, rep);
-          kxq = penalize(kxq, rep);
-        }
-      }
-      RowStat P, Q;
-      P.M = Mp; P.c = c; P.Zk = Zkp; P.kord = ord_key(kp_cut);
-      Q.M = Mq; Q.c = c; Q.Zk = Zkq; Q.kord = ord_key(kq_cut);
-      const Decision dc = decide(P, Q, kxp, kxq, (double)T, (double)a.D, true, d, u_j);
+      float kxp, kxq;
+      draft_keys(kxp, kxq);
+      RowStat Q;
+      Q.kord = ord_key(kq_cut);
+      const double qx = kept(Q, ord_key(kxq)) ? s_xe[1] / Zkq : 0.0;   // as prob_at
+      const Decision dc = decide_from(s_xe[0], qx, (double)a.D, true, d, u_j);
       out.d = (float)d;
       out.th = (float)dc.th;
       out.px = (float)dc.px;

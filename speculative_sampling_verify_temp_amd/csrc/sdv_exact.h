@@ -369,17 +369,23 @@ struct Decision {
   bool accept;
 };
 
-__device__ __forceinline__ Decision decide(const RowStat& P, const RowStat& Q, float kxp,
-                                           float kxq, double T, double D, bool tv_valid,
-                                           double d, float u) {
+// The decision from p(x) and q(x) already computed.
+__device__ __forceinline__ Decision decide_from(double px, double qx, double D, bool tv_valid,
+                                                double d, float u) {
   Decision o;
-  o.px = prob_at(P, kxp, T);
-  o.qx = prob_at(Q, kxq, T);
+  o.px = px;
+  o.qx = qx;
   if (tv_valid) o.th = (d <= D) ? 1.0 : D / d;
   else o.th = (D >= 1.0) ? 1.0 : 0.0;   // D = 0: theta only matters when p = q
   o.pix = (1.0 - o.th) * o.px + o.th * o.qx;
   o.accept = (double)u * o.qx < o.pix;
   return o;
+}
+
+__device__ __forceinline__ Decision decide(const RowStat& P, const RowStat& Q, float kxp,
+                                           float kxq, double T, double D, bool tv_valid,
+                                           double d, float u) {
+  return decide_from(prob_at(P, kxp, T), prob_at(Q, kxq, T), D, tv_valid, d, u);
 }
 
 }  // namespace sdv
