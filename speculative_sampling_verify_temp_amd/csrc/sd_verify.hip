@@ -640,9 +640,12 @@ __device__ __forceinline__ uint32_t exact_raw(const ExactList& ex, int ns, int n
   return raw;
 }
 
-// Bit e of an 8-bit mask to bit 8(e & 3) + 4(e >> 2) (the candidate layout).
+// Bit e of an 8-bit mask to bit 4e (the candidate layout).
 __device__ __forceinline__ uint32_t spread8(uint32_t b) {
-  return (((b & 0xFu) * 0x204081u) & 0x01010101u) | (((((b >> 4) & 0xFu) * 0x204081u) & 0x01010101u) << 4);
+  uint32_t x = b & 0xFFu;
+  x = (x | (x << 12)) & 0x000F000Fu;   // elements 4..7 to bits 16..19
+  x = (x | (x << 6)) & 0x03030303u;    // two elements per byte
+  return (x | (x << 3)) & 0x11111111u;   // one per nibble
 }
 
 // One 8-logit vector of a row: keys z as read, packed orderable keys o,
@@ -712,7 +715,8 @@ __device__ __forceinline__ uint32_t pk_mad_u16(uint32_t a, uint32_t b, uint32_t 
 // Streaming work of one vector of a row against its window: normalizer,
 // max, codes, histogram, exact entries for keys above the window.  Every
 // logit is streamed as read; pen_fix settles the penalized ones afterwards.
-// Returns the two code words (bytes: codes of elements 0..3 and 4..7).
+// Returns the two code words: the codes of the even elements 0, 2, 4, 6
+// and of the odd ones 1, 3, 5, 7 (one byte each, in that order).
 __device__ __forceinline__ uint2 row_vec(Vec8& v, int k, float c, float gc, uint32_t t1,
                                          uint32_t hlane2, uint32_t* hist, const ExactList& ex,
                                          RowAcc& acc) {
@@ -747,8 +751,10 @@ __device__ __forceinline__ uint2 row_vec(Vec8& v, int k, float c, float gc, uint
     atomicAdd(reinterpret_cast<uint32_t*>(reinterpret_cast<char*>(hist) + (a2 & 0xFFFFu)), 1u);
     atomicAdd(reinterpret_cast<uint32_t*>(reinterpret_cast<char*>(hist) + (a2 >> 16)), 1u);
   }
-  return make_uint2(__builtin_amdgcn_perm(cc[1], cc[0], 0x06040200u),
-                    __builtin_amdgcn_perm(cc[3], cc[2], 0x06040200u));
+  const uint32_t t01 = (cc[1] << 8) | cc[0];   // bytes: codes 0 2 1 3
+  const uint32_t t23 = (cc[3] << 8) | cc[2];   // bytes: codes 4 6 5 7
+  return make_uint2(__builtin_amdgcn_perm(t23, t01, 0x05040100u),
+                    __builtin_amdgcn_perm(t23, t01, 0x07060302u));
 }
 
 // After a stream, for one distinct penalized token (id, raw bits as read):
@@ -883,10 +889,12 @@ __device__ __forceinline__ int pen_claim(const Args& a, const PenSet& ps, int r,
   return x0;
 }
 
-// Files the target-nucleus candidates of round l (code words cw0, cw1) in
-// the lane's slots, one word each: draft logit bits (dv; 0 for a bonus row)
-// in bits 0-15, the target code in bits 16-23, 8 l + logit in bits 24-31.
-// Slot (s, lane) is word s * NT_F + lane.
+// Files the target-nucleus candidates of round l (code words cw0, cw1 of
+// the even and odd logits) in the lane's slots, in ascending logit order,
+// one word each: draft logit bits (dv; 0 for a bonus row) in bits 0-15,
+// the target code in bits 16-23, 8 l + logit in bits 24-31.  Slot (s, lane)
+// is word s * NT_F + lane; past CAPT candidates the last slot is reused
+// (the unit is then flagged: nslot > CAPT).
 // raise: a penalty is active and below 1 (it raises penalized keys).
 // LOW: cut_code < 127 when known at compile time (-1: at run time).
 template <int LOW = -1>
@@ -894,7 +902,7 @@ __device__ __forceinline__ void file_round(int l, uint32_t cw0, uint32_t cw1, ui
                                            bool has_d, uint32_t bits, uint32_t cut_code,
                                            bool raise, uint32_t* slots, int& nslot) {
   const int tid = threadIdx.x;
-  // Candidates: code <= cut code (bit 8b + 4h <-> logit 4h + b).  Whether a
+  // Candidates: code <= cut code (bit 4e <-> logit e).  Whether a
   // candidate is in the nucleus is settled when the slot is read.  The codes
   // are those of the logits as read: a penalty that lowers keys (r > 1)
   // cannot make a non-candidate a member, one that raises them can, so then
@@ -902,15 +910,13 @@ __device__ __forceinline__ void file_round(int l, uint32_t cw0, uint32_t cw1, ui
   uint32_t m = (le_mask<LOW>(cw0, cut_code) >> 7) | (le_mask<LOW>(cw1, cut_code) >> 3);
   if (raise) m |= spread8(bits);
   if (!has_d) dv = make_uint4(0u, 0u, 0u, 0u);
+  const uint64_t dlo = (uint64_t)dv.y << 32 | dv.x, dhi = (uint64_t)dv.w << 32 | dv.z;
   while (m) {
-    const int p = __builtin_ctz(m);
+    const int p = __builtin_ctz(m);   // 4e: code byte e >> 1 of cw0 or cw1, draft half e of dv
     m &= m - 1u;
-    const int h = (p >> 2) & 1, b = p >> 3;   // logit 4h + b
-    const uint32_t cd = __builtin_amdgcn_ubfe(h ? cw1 : cw0, (uint32_t)(p & 24), 8u);
-    const uint32_t lo = h ? dv.z : dv.x, hi = h ? dv.w : dv.y;
-    const uint32_t q = __builtin_amdgcn_ubfe((b & 2) ? hi : lo, (uint32_t)((b & 1) * 16), 16u);
-    if (nslot < CAPT)
-      slots[nslot * NT_F + tid] = q | (cd << 16) | ((uint32_t)(l * VEC + 4 * h + b) << 24);
+    const uint32_t cd = __builtin_amdgcn_ubfe((p & 4) ? cw1 : cw0, (uint32_t)(p & 24), 8u);
+    const uint32_t q = (uint32_t)(((p & 16) ? dhi : dlo) >> ((p & 12) << 2)) & 0xFFFFu;
+    slots[min(nslot, CAPT - 1) * NT_F + tid] = q | (cd << 16) | ((uint32_t)(l * VEC + (p >> 2)) << 24);
     ++nslot;
   }
 }

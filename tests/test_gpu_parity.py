@@ -360,6 +360,25 @@ def test_single_pass_window_signs(case):
     assert tot[0] >= 3
 
 
+def test_single_pass_draw_order():
+    """Corrections drawn on the single-pass path over large nuclei: a lane
+    then holds several weighted candidates in one 8-logit vector, and the
+    inverse CDF must walk them in ascending token id."""
+    tot = [0, 0]
+    rejected = 0
+    for seed in range(4):
+        w = wl.random_case(700 + seed, B=64, K_max=2, V=20011, dtype="bf16", D=0.0, top_p=0.9,
+                           sigma=3.0, corr=0.3, T_range=(0.9, 1.0))
+        assert _fast_fallbacks(w) == 0
+        g = gpu_sample(w)
+        rejected += int((g["accepted"] < w.k_per_row).sum())
+        c, f = compare_sample(g, oracle_sample(w), w)
+        tot[0] += c
+        tot[1] += f
+    print(f"draw order: checked {tot[0]} rows, near-tie rows {tot[1]}, rejected rows {rejected}")
+    assert tot[0] >= 128 and rejected >= 64
+
+
 def test_single_pass_fallback_routes():
     """bf16 + top-p cases that the single-pass kernel hands to its exact
     fallback: a flat distribution (nucleus larger than the per-lane slots), a
