@@ -706,9 +706,23 @@ struct RowAcc {
   double Z;        // sum of exp2(key c - anchor c)
 };
 
-__device__ __forceinline__ uint32_t pk_mad_u16(uint32_t a, uint32_t b, uint32_t c) {
+typedef __attribute__((address_space(3))) uint32_t lds_u32;
+
+// LDS byte address of a shared array.
+__device__ __forceinline__ uint32_t lds_addr(const uint32_t* p) {
+  return (uint32_t)(size_t)(const lds_u32*)p;
+}
+
+// c + 64 * (16-bit half of a): the LDS address of a logit's histogram word
+// from its code (64 bytes per bin: NCOPY copies) and the lane's copy.
+__device__ __forceinline__ uint32_t bin_addr_lo(uint32_t a, uint32_t c) {
   uint32_t d;
-  asm("v_pk_mad_u16 %0, %1, %2, %3" : "=v"(d) : "v"(a), "s"(b), "v"(c));
+  asm("v_mad_u32_u16 %0, %1, 64, %2" : "=v"(d) : "v"(a), "v"(c));
+  return d;
+}
+__device__ __forceinline__ uint32_t bin_addr_hi(uint32_t a, uint32_t c) {
+  uint32_t d;
+  asm("v_mad_u32_u16 %0, %1, 64, %2 op_sel:[1,0,0,0]" : "=v"(d) : "v"(a), "v"(c));
   return d;
 }
 
@@ -718,8 +732,7 @@ __device__ __forceinline__ uint32_t pk_mad_u16(uint32_t a, uint32_t b, uint32_t 
 // Returns the two code words: the codes of the even elements 0, 2, 4, 6
 // and of the odd ones 1, 3, 5, 7 (one byte each, in that order).
 __device__ __forceinline__ uint2 row_vec(Vec8& v, int k, float c, float gc, uint32_t t1,
-                                         uint32_t hlane2, uint32_t* hist, const ExactList& ex,
-                                         RowAcc& acc) {
+                                         uint32_t hbase, const ExactList& ex, RowAcc& acc) {
   const uint32_t t1x2 = t1 | (t1 << 16);
   uint32_t cc[4];
 #pragma unroll
@@ -745,11 +758,13 @@ __device__ __forceinline__ uint2 row_vec(Vec8& v, int k, float c, float gc, uint
 #pragma unroll
   for (int e = 0; e < VEC; ++e) s[e] = fast_exp2(fmaf(v.z[e], c, -gc));
   acc.Z += (double)(((s[0] + s[1]) + (s[2] + s[3])) + ((s[4] + s[5]) + (s[6] + s[7])));
+  static_assert(NCOPY * 4 == 64, "bin_addr stride");
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
-    const uint32_t a2 = pk_mad_u16(cc[e], (NCOPY * 4) * 0x00010001u, hlane2);
-    atomicAdd(reinterpret_cast<uint32_t*>(reinterpret_cast<char*>(hist) + (a2 & 0xFFFFu)), 1u);
-    atomicAdd(reinterpret_cast<uint32_t*>(reinterpret_cast<char*>(hist) + (a2 >> 16)), 1u);
+    __hip_atomic_fetch_add((lds_u32*)(size_t)bin_addr_lo(cc[e], hbase), 1u, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_WORKGROUP);
+    __hip_atomic_fetch_add((lds_u32*)(size_t)bin_addr_hi(cc[e], hbase), 1u, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_WORKGROUP);
   }
   const uint32_t t01 = (cc[1] << 8) | cc[0];   // bytes: codes 0 2 1 3
   const uint32_t t23 = (cc[3] << 8) | cc[2];   // bytes: codes 4 6 5 7
@@ -1015,7 +1030,6 @@ __global__ __launch_bounds__(NT_F) void k_pair_fast(Args a, UnitOut* uo) {
   const __amdgpu_buffer_rsrc_t rs_d = row_rsrc(drow, bonus ? 0 : nvec * 16);
   const uint32_t voff = (uint32_t)tid * 16u;
   const uint32_t hlane = (uint32_t)(tid & (NCOPY - 1)) * 4u;
-  const uint32_t hlane2 = hlane | (hlane << 16);   // packed byte offset of this lane's copy
   ExactList exp_, exq;
   exp_.key = ekey[0];
   exp_.id = eid[0];
@@ -1141,7 +1155,7 @@ __global__ __launch_bounds__(NT_F) void k_pair_fast(Args a, UnitOut* uo) {
     if (k < nvec) {
       Vec8 v;
       vec8<POS>(ld, l, k, V, v);
-      const uint2 cw = row_vec(v, k, c, gcp, t1p, hlane2, hist, exp_, ap);
+      const uint2 cw = row_vec(v, k, c, gcp, t1p, lds_addr(hist) + hlane, exp_, ap);
       code[l][0] = cw.x;
       code[l][1] = cw.y;
     }
@@ -1278,7 +1292,7 @@ __global__ __launch_bounds__(NT_F) void k_pair_fast(Args a, UnitOut* uo) {
         vec8<POS>(ld, l, k, V, v);
         const uint32_t bits = raise ? pen_bits8(bm, k) : 0u;
         const uint4 dv = make_uint4(v.w[0], v.w[1], v.w[2], v.w[3]);
-        (void)row_vec(v, k, c, gcq, t1q, hlane2, histq, exq, aq);
+        (void)row_vec(v, k, c, gcq, t1q, lds_addr(histq) + hlane, exq, aq);
         file_round<LOW>(l, code[l][0], code[l][1], dv, true, bits, cut_code, raise, slot_arr, nslot);
       }
       SDV_PIN(aq.mo);
