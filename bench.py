@@ -11,8 +11,13 @@ One step = one sd_verify_sample call over the whole batch, issued as its
 phases on torch's current stream so the dominant kernel can be bracketed by
 HIP events inside the timed region.  Prints one JSON line.
 
-    python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--no-cpu-baseline]
+    python bench.py [--gpus 1] [--steps 100] [--warmup 60] [--no-cpu-baseline]
                     [--copy-probe BYTES]
+
+The default warmup is long on purpose: after an idle spell the first ~40
+back-to-back calls run through a clock transient (the dominant kernel takes
+up to ~1.25x its sustained time), and the timed steps should see the
+sustained rate.
 
 `roofline.traffic` is the dominant kernel's HBM bytes per launch from two
 rocprofv3 counter runs (FETCH_SIZE, then WRITE_SIZE) of this script with
@@ -169,8 +174,8 @@ def cpu_baseline(w, budget_s=12.0):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=60)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", type=int, default=0,
                     help="bytes of one plain device copy run before the warmup")
