@@ -1151,7 +1151,8 @@ __global__ __launch_bounds__(NT_F) void k_pair_fast(Args a, UnitOut* uo) {
       if (x0 >= 0) plraw[x0] = __builtin_amdgcn_ubfe(gp, sh, 16u) | (__builtin_amdgcn_ubfe(gq, sh, 16u) << 16);
     }
     const int k = l * NT + tid;
-    code[l][0] = code[l][1] = 0xFFFFFFFFu;
+    // (codes of vectors past the row end are never read: every reader
+    // checks k < nvec)
     if (k < nvec) {
       Vec8 v;
       vec8<POS>(ld, l, k, V, v);
