@@ -704,6 +704,7 @@ struct RowAcc {
   uint32_t mo;     // packed 16-bit orderable keys: max of the logits as read
   float mpen;      // max of the penalized keys (after the stream)
   double Z;        // sum of exp2(key c - anchor c)
+  float zf;        // the part of it not yet added to Z (at most two rounds)
 };
 
 typedef __attribute__((address_space(3))) uint32_t lds_u32;
@@ -757,7 +758,7 @@ __device__ __forceinline__ uint2 row_vec(Vec8& v, int k, float c, float gc, uint
   float s[VEC];
 #pragma unroll
   for (int e = 0; e < VEC; ++e) s[e] = fast_exp2(fmaf(v.z[e], c, -gc));
-  acc.Z += (double)(((s[0] + s[1]) + (s[2] + s[3])) + ((s[4] + s[5]) + (s[6] + s[7])));
+  acc.zf += ((s[0] + s[1]) + (s[2] + s[3])) + ((s[4] + s[5]) + (s[6] + s[7]));
   static_assert(NCOPY * 4 == 64, "bin_addr stride");
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
@@ -812,6 +813,7 @@ __device__ __forceinline__ RowAcc row_acc_init() {
   r.mo = 0x007F007Fu;   // orderable key of -inf
   r.mpen = -INFINITY;
   r.Z = 0.0;
+  r.zf = 0.0f;
   return r;
 }
 
@@ -1160,9 +1162,14 @@ __global__ __launch_bounds__(NT_F) void k_pair_fast(Args a, UnitOut* uo) {
       code[l][0] = cw.x;
       code[l][1] = cw.y;
     }
+    if constexpr (l % 2 == 1 || l == NR - 1) {   // fp32 sums of two rounds, then fp64
+      ap.Z += (double)ap.zf;
+      ap.zf = 0.0f;
+    }
     SDV_PIN(ap.mo);
     SDV_PIN(ap.mpen);
     SDV_PIN(ap.Z);
+    SDV_PIN(ap.zf);
     SDV_PIN(code[l][0]);
     SDV_PIN(code[l][1]);
   });
@@ -1296,9 +1303,14 @@ __global__ __launch_bounds__(NT_F) void k_pair_fast(Args a, UnitOut* uo) {
         (void)row_vec(v, k, c, gcq, t1q, lds_addr(histq) + hlane, exq, aq);
         file_round<LOW>(l, code[l][0], code[l][1], dv, true, bits, cut_code, raise, slot_arr, nslot);
       }
+      if constexpr (l % 2 == 1 || l == NR - 1) {
+        aq.Z += (double)aq.zf;
+        aq.zf = 0.0f;
+      }
       SDV_PIN(aq.mo);
       SDV_PIN(aq.mpen);
       SDV_PIN(aq.Z);
+      SDV_PIN(aq.zf);
     });
     };
     // (instances by window sign and by the target cut's half of the code range)
