@@ -1288,7 +1288,7 @@ __global__ __launch_bounds__(NT_F) void k_pair_fast(Args a, UnitOut* uo) {
     const uint32_t t1q = anchor_q ? min(ord16f(Gq) + UP, 0xFFFEu) + 1u : 0xFFFFu;
     const float gcq = anchor_q ? Gq * c : 0.0f;
     RowAcc aq = row_acc_init();
-    auto stream_b = [&]<bool POS, int LOW>() __attribute__((always_inline)) {
+    auto stream_b = [&]<bool POS, int LOW, bool RAISE>() __attribute__((always_inline)) {
     static_for<NR>([&]<int l>() __attribute__((always_inline)) {
       const uint4 ld = stg[(NR + l) % NSTG];
       if constexpr (l + NSTG < NR) stg[(NR + l) % NSTG] = ring_load<NR + l + NSTG>(rs_t, rs_d, voff);
@@ -1298,10 +1298,10 @@ __global__ __launch_bounds__(NT_F) void k_pair_fast(Args a, UnitOut* uo) {
       if (k < nvec) {
         Vec8 v;
         vec8<POS>(ld, l, k, V, v);
-        const uint32_t bits = raise ? pen_bits8(bm, k) : 0u;
+        const uint32_t bits = RAISE ? pen_bits8(bm, k) : 0u;
         const uint4 dv = make_uint4(v.w[0], v.w[1], v.w[2], v.w[3]);
         (void)row_vec(v, k, c, gcq, t1q, lds_addr(histq) + hlane, exq, aq);
-        file_round<LOW>(l, code[l][0], code[l][1], dv, true, bits, cut_code, raise, slot_arr, nslot);
+        file_round<LOW>(l, code[l][0], code[l][1], dv, true, bits, cut_code, RAISE, slot_arr, nslot);
       }
       if constexpr (l % 2 == 1 || l == NR - 1) {
         aq.Z += (double)aq.zf;
@@ -1315,12 +1315,16 @@ __global__ __launch_bounds__(NT_F) void k_pair_fast(Args a, UnitOut* uo) {
     };
     // (instances by window sign and by the target cut's half of the code range)
     const bool posq = t1q >= 0x8000u + 254u, low = cut_code < 127u;
-    if (posq) {
-      if (low) stream_b.template operator()<true, 1>();
-      else stream_b.template operator()<true, 0>();
+    // (and by whether penalized keys rise)
+    if (raise) {
+      if (posq) stream_b.template operator()<true, -1, true>();
+      else stream_b.template operator()<false, -1, true>();
+    } else if (posq) {
+      if (low) stream_b.template operator()<true, 1, false>();
+      else stream_b.template operator()<true, 0, false>();
     } else {
-      if (low) stream_b.template operator()<false, 1>();
-      else stream_b.template operator()<false, 0>();
+      if (low) stream_b.template operator()<false, 1, false>();
+      else stream_b.template operator()<false, 0, false>();
     }
     __syncthreads();   // the draft stream is done: histogram, stream entries
     if (npl <= PL_CAP)
