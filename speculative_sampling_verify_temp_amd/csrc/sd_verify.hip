@@ -732,15 +732,20 @@ __device__ __forceinline__ uint32_t bin_addr_hi(uint32_t a, uint32_t c) {
 // logit is streamed as read; pen_fix settles the penalized ones afterwards.
 // Returns the two code words: the codes of the even elements 0, 2, 4, 6
 // and of the odd ones 1, 3, 5, 7 (one byte each, in that order).
+// SAMPLED: the vector is in one of the rounds whose block max set the
+// anchor, so no key of it is above the window or above the max that the
+// caller started acc.mo from (non-finite logits show in the normalizer).
+template <bool SAMPLED = false>
 __device__ __forceinline__ uint2 row_vec(Vec8& v, int k, float c, float gc, uint32_t t1,
                                          uint32_t hbase, const ExactList& ex, RowAcc& acc) {
   const uint32_t t1x2 = t1 | (t1 << 16);
   uint32_t cc[4];
 #pragma unroll
   for (int e = 0; e < 4; ++e) cc[e] = code_of(t1x2, v.o[e]);
-  const uint32_t vo = pk_max(pk_max(v.o[0], v.o[1]), pk_max(v.o[2], v.o[3]));
-  acc.mo = pk_max(acc.mo, vo);
-  if (as_u32(__builtin_elementwise_sub_sat(as_u16x2(vo), as_u16x2(t1x2 - 0x00010001u))) != 0u) {
+  const uint32_t vo = SAMPLED ? 0u : pk_max(pk_max(v.o[0], v.o[1]), pk_max(v.o[2], v.o[3]));
+  if (!SAMPLED) acc.mo = pk_max(acc.mo, vo);
+  if (!SAMPLED &&
+      as_u32(__builtin_elementwise_sub_sat(as_u16x2(vo), as_u16x2(t1x2 - 0x00010001u))) != 0u) {
     // Keys above the window (code 0) become exact entries.  Bit 2h + 16i of
     // am is logit 2h + i (a zero 16-bit code half; codes are at most 255).
     uint32_t am = 0u;
@@ -1126,6 +1131,7 @@ __global__ __launch_bounds__(NT_F) void k_pair_fast(Args a, UnitOut* uo) {
 
   uint32_t code[NR][2];
   RowAcc ap = row_acc_init();
+  if (anchor_ok) ap.mo = ord16f(Gp) * 0x00010001u;   // the max of the sampled rounds
   int x0 = -1;          // this thread's penalty-list index (set in round 1)
   uint32_t gp = 0u, gq = 0u, goff = 0u;
   auto stream_a = [&]<bool POS>() __attribute__((always_inline)) {
@@ -1158,7 +1164,7 @@ __global__ __launch_bounds__(NT_F) void k_pair_fast(Args a, UnitOut* uo) {
     if (k < nvec) {
       Vec8 v;
       vec8<POS>(ld, l, k, V, v);
-      const uint2 cw = row_vec(v, k, c, gcp, t1p, lds_addr(hist) + hlane, exp_, ap);
+      const uint2 cw = row_vec<(l < NSAMP)>(v, k, c, gcp, t1p, lds_addr(hist) + hlane, exp_, ap);
       code[l][0] = cw.x;
       code[l][1] = cw.y;
     }
@@ -1288,6 +1294,7 @@ __global__ __launch_bounds__(NT_F) void k_pair_fast(Args a, UnitOut* uo) {
     const uint32_t t1q = anchor_q ? min(ord16f(Gq) + UP, 0xFFFEu) + 1u : 0xFFFFu;
     const float gcq = anchor_q ? Gq * c : 0.0f;
     RowAcc aq = row_acc_init();
+    if (anchor_q) aq.mo = ord16f(Gq) * 0x00010001u;
     auto stream_b = [&]<bool POS, int LOW, bool RAISE>() __attribute__((always_inline)) {
     static_for<NR>([&]<int l>() __attribute__((always_inline)) {
       const uint4 ld = stg[(NR + l) % NSTG];
@@ -1300,7 +1307,7 @@ __global__ __launch_bounds__(NT_F) void k_pair_fast(Args a, UnitOut* uo) {
         vec8<POS>(ld, l, k, V, v);
         const uint32_t bits = RAISE ? pen_bits8(bm, k) : 0u;
         const uint4 dv = make_uint4(v.w[0], v.w[1], v.w[2], v.w[3]);
-        (void)row_vec(v, k, c, gcq, t1q, lds_addr(histq) + hlane, exq, aq);
+        (void)row_vec<(l < NSAMP)>(v, k, c, gcq, t1q, lds_addr(histq) + hlane, exq, aq);
         file_round<LOW>(l, code[l][0], code[l][1], dv, true, bits, cut_code, RAISE, slot_arr, nslot);
       }
       if constexpr (l % 2 == 1 || l == NR - 1) {
