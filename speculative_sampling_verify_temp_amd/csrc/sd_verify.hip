@@ -660,7 +660,8 @@ struct Vec8 {
 // of a positive logit is its bits with the sign flipped, and a negative
 // logit only needs some key below the window, which the same flip gives;
 // one operation per word instead of two.
-template <bool POS = false>
+// TAIL false: V is a multiple of 8, so no vector needs masking.
+template <bool POS = false, bool TAIL = true>
 __device__ __forceinline__ void vec8(const uint4& ld, int l, int k, int V, Vec8& v) {
   v.w[0] = ld.x;
   v.w[1] = ld.y;
@@ -668,7 +669,7 @@ __device__ __forceinline__ void vec8(const uint4& ld, int l, int k, int V, Vec8&
   v.w[3] = ld.w;
   // The vector that holds the row end, when V is not a multiple of 8: its
   // elements from V on read as -inf (bf16 0xFF80).
-  if ((l + 1) * NT_F * VEC > V && (V & 7) && k == (V >> 3)) {
+  if (TAIL && (l + 1) * NT_F * VEC > V && (V & 7) && k == (V >> 3)) {
     const int keep = (V & 7) * 16;   // bits of the 128 that stay
     const uint64_t m0 = keep >= 64 ? ~0ull : (1ull << keep) - 1ull;
     const uint64_t m1 = keep <= 64 ? 0ull : (1ull << (keep - 64)) - 1ull;
@@ -1134,11 +1135,9 @@ __global__ __launch_bounds__(NT_F) void k_pair_fast(Args a, UnitOut* uo) {
   if (anchor_ok) ap.mo = ord16f(Gp) * 0x00010001u;   // the max of the sampled rounds
   int x0 = -1;          // this thread's penalty-list index (set in round 1)
   uint32_t gp = 0u, gq = 0u, goff = 0u;
-  auto stream_a = [&]<bool POS>() __attribute__((always_inline)) {
+  auto stream_a = [&]<bool POS, bool TAIL>() __attribute__((always_inline)) {
   static_for<NR>([&]<int l>() __attribute__((always_inline)) {
     const uint4 ld = stg[l % NSTG];
-    stg[l % NSTG] = ring_load<l + NSTG>(rs_t, rs_d, voff);   // next target round, or a draft round
-    __builtin_amdgcn_sched_barrier(0);   // keep later rounds' loads in their rounds
     if constexpr (l % 5 == 0) __builtin_amdgcn_s_setprio(3 - l / 5);   // lagging waves first
     if constexpr (l == 1) {
       // Each distinct penalized id is listed once; the thread that listed it
@@ -1163,7 +1162,7 @@ __global__ __launch_bounds__(NT_F) void k_pair_fast(Args a, UnitOut* uo) {
     // checks k < nvec)
     if (k < nvec) {
       Vec8 v;
-      vec8<POS>(ld, l, k, V, v);
+      vec8<POS, TAIL>(ld, l, k, V, v);
       const uint2 cw = row_vec<(l < NSAMP)>(v, k, c, gcp, t1p, lds_addr(hist) + hlane, exp_, ap);
       code[l][0] = cw.x;
       code[l][1] = cw.y;
@@ -1178,10 +1177,22 @@ __global__ __launch_bounds__(NT_F) void k_pair_fast(Args a, UnitOut* uo) {
     SDV_PIN(ap.zf);
     SDV_PIN(code[l][0]);
     SDV_PIN(code[l][1]);
+    // The slot's next load (next target round, or a draft round) goes out
+    // once this round's words are used, into the same registers.
+    __builtin_amdgcn_sched_barrier(0);
+    stg[l % NSTG] = ring_load<l + NSTG>(rs_t, rs_d, voff);
+    __builtin_amdgcn_sched_barrier(0);   // keep later rounds' loads in their rounds
   });
   };
-  if (t1p >= 0x8000u + 254u) stream_a.template operator()<true>();
-  else stream_a.template operator()<false>();
+  // (instances by window sign and by whether a vector needs masking)
+  const bool tail = (V & 7) != 0;
+  if (t1p >= 0x8000u + 254u) {
+    if (tail) stream_a.template operator()<true, true>();
+    else stream_a.template operator()<true, false>();
+  } else {
+    if (tail) stream_a.template operator()<false, true>();
+    else stream_a.template operator()<false, false>();
+  }
   __syncthreads();   // the target stream is done: histogram, stream entries, logit list
   const int npl = s_npl;
   if (npl <= PL_CAP)
@@ -1295,16 +1306,14 @@ __global__ __launch_bounds__(NT_F) void k_pair_fast(Args a, UnitOut* uo) {
     const float gcq = anchor_q ? Gq * c : 0.0f;
     RowAcc aq = row_acc_init();
     if (anchor_q) aq.mo = ord16f(Gq) * 0x00010001u;
-    auto stream_b = [&]<bool POS, int LOW, bool RAISE>() __attribute__((always_inline)) {
+    auto stream_b = [&]<bool POS, int LOW, bool RAISE, bool TAIL>() __attribute__((always_inline)) {
     static_for<NR>([&]<int l>() __attribute__((always_inline)) {
       const uint4 ld = stg[(NR + l) % NSTG];
-      if constexpr (l + NSTG < NR) stg[(NR + l) % NSTG] = ring_load<NR + l + NSTG>(rs_t, rs_d, voff);
-      __builtin_amdgcn_sched_barrier(0);
       if constexpr (l % 5 == 0) __builtin_amdgcn_s_setprio(3 - l / 5);
       const int k = l * NT + tid;
       if (k < nvec) {
         Vec8 v;
-        vec8<POS>(ld, l, k, V, v);
+        vec8<POS, TAIL>(ld, l, k, V, v);
         const uint32_t bits = RAISE ? pen_bits8(bm, k) : 0u;
         const uint4 dv = make_uint4(v.w[0], v.w[1], v.w[2], v.w[3]);
         (void)row_vec<(l < NSAMP)>(v, k, c, gcq, t1q, lds_addr(histq) + hlane, exq, aq);
@@ -1318,20 +1327,23 @@ __global__ __launch_bounds__(NT_F) void k_pair_fast(Args a, UnitOut* uo) {
       SDV_PIN(aq.mpen);
       SDV_PIN(aq.Z);
       SDV_PIN(aq.zf);
+      __builtin_amdgcn_sched_barrier(0);
+      if constexpr (l + NSTG < NR) stg[(NR + l) % NSTG] = ring_load<NR + l + NSTG>(rs_t, rs_d, voff);
+      __builtin_amdgcn_sched_barrier(0);
     });
     };
     // (instances by window sign and by the target cut's half of the code range)
     const bool posq = t1q >= 0x8000u + 254u, low = cut_code < 127u;
     // (and by whether penalized keys rise)
-    if (raise) {
-      if (posq) stream_b.template operator()<true, -1, true>();
-      else stream_b.template operator()<false, -1, true>();
+    if (raise || tail) {
+      if (posq) stream_b.template operator()<true, -1, true, true>();
+      else stream_b.template operator()<false, -1, true, true>();
     } else if (posq) {
-      if (low) stream_b.template operator()<true, 1, false>();
-      else stream_b.template operator()<true, 0, false>();
+      if (low) stream_b.template operator()<true, 1, false, false>();
+      else stream_b.template operator()<true, 0, false, false>();
     } else {
-      if (low) stream_b.template operator()<false, 1, false>();
-      else stream_b.template operator()<false, 0, false>();
+      if (low) stream_b.template operator()<false, 1, false, false>();
+      else stream_b.template operator()<false, 0, false, false>();
     }
     __syncthreads();   // the draft stream is done: histogram, stream entries
     if (npl <= PL_CAP)
