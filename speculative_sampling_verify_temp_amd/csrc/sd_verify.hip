@@ -738,7 +738,8 @@ __device__ __forceinline__ uint32_t bin_addr_hi(uint32_t a, uint32_t c) {
 // caller started acc.mo from (non-finite logits show in the normalizer).
 template <bool SAMPLED = false>
 __device__ __forceinline__ uint2 row_vec(Vec8& v, int k, float c, float gc, uint32_t t1,
-                                         uint32_t hbase, const ExactList& ex, RowAcc& acc) {
+                                         uint32_t* hist, uint32_t hlane, const ExactList& ex,
+                                         RowAcc& acc) {
   const uint32_t t1x2 = t1 | (t1 << 16);
   uint32_t cc[4];
 #pragma unroll
@@ -766,11 +767,13 @@ __device__ __forceinline__ uint2 row_vec(Vec8& v, int k, float c, float gc, uint
   for (int e = 0; e < VEC; ++e) s[e] = fast_exp2(fmaf(v.z[e], c, -gc));
   acc.zf += ((s[0] + s[1]) + (s[2] + s[3])) + ((s[4] + s[5]) + (s[6] + s[7]));
   static_assert(NCOPY * 4 == 64, "bin_addr stride");
+  typedef __attribute__((address_space(3))) char lds_char;
+  lds_char* const hb = (lds_char*)(lds_u32*)hist;
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
-    __hip_atomic_fetch_add((lds_u32*)(size_t)bin_addr_lo(cc[e], hbase), 1u, __ATOMIC_RELAXED,
+    __hip_atomic_fetch_add((lds_u32*)(hb + bin_addr_lo(cc[e], hlane)), 1u, __ATOMIC_RELAXED,
                            __HIP_MEMORY_SCOPE_WORKGROUP);
-    __hip_atomic_fetch_add((lds_u32*)(size_t)bin_addr_hi(cc[e], hbase), 1u, __ATOMIC_RELAXED,
+    __hip_atomic_fetch_add((lds_u32*)(hb + bin_addr_hi(cc[e], hlane)), 1u, __ATOMIC_RELAXED,
                            __HIP_MEMORY_SCOPE_WORKGROUP);
   }
   const uint32_t t01 = (cc[1] << 8) | cc[0];   // bytes: codes 0 2 1 3
@@ -983,9 +986,18 @@ __device__ __forceinline__ ReqWords request_words(const int32_t* po, const int32
 
 __global__ __launch_bounds__(NT_F) void k_pair_fast(Args a, UnitOut* uo) {
   constexpr int NT = NT_F;
-  constexpr int NSLOT = CAPT * NT;
   __shared__ uint32_t bm[MAXV_FAST / 32];
-  __shared__ __align__(16) uint32_t hist2[2][NBIN * NCOPY];   // target row, draft row
+  // The two histograms (target row, draft row) and the nucleus slots, in
+  // one block so that the histograms sit at LDS address 0: a bin's address
+  // is then the lane's copy plus 64 bytes per code, with the draft row's
+  // base in the instruction's offset field.
+  struct HistSlots {
+    uint32_t hist2[2][NBIN * NCOPY];
+    uint32_t slot_arr[CAPT * NT];   // slot (s, lane) at s * NT + lane (file_round)
+  };
+  __shared__ __align__(16) HistSlots hsl;
+  auto& hist2 = hsl.hist2;
+  auto& slot_arr = hsl.slot_arr;
   __shared__ float ekey[2][E_CAP];
   __shared__ int32_t eid[2][E_CAP];
   __shared__ uint16_t eraw[2][E_CAP];
@@ -993,7 +1005,6 @@ __global__ __launch_bounds__(NT_F) void k_pair_fast(Args a, UnitOut* uo) {
   __shared__ uint64_t emass[NBIN];
   __shared__ __align__(16) uint32_t hsum[NBIN];   // folded histogram
   __shared__ __align__(16) uint32_t hneg[NBIN];   // penalized logits that left a bin
-  __shared__ uint32_t slot_arr[NSLOT];   // slot (s, lane) at s * NT + lane (file_round)
   __shared__ float rkey[R_CAP];
   __shared__ double rmass[R_CAP];
   __shared__ int rid[R_CAP];
@@ -1163,7 +1174,7 @@ __global__ __launch_bounds__(NT_F) void k_pair_fast(Args a, UnitOut* uo) {
     if (k < nvec) {
       Vec8 v;
       vec8<POS, TAIL>(ld, l, k, V, v);
-      const uint2 cw = row_vec<(l < NSAMP)>(v, k, c, gcp, t1p, lds_addr(hist) + hlane, exp_, ap);
+      const uint2 cw = row_vec<(l < NSAMP)>(v, k, c, gcp, t1p, hist, hlane, exp_, ap);
       code[l][0] = cw.x;
       code[l][1] = cw.y;
     }
@@ -1316,7 +1327,7 @@ __global__ __launch_bounds__(NT_F) void k_pair_fast(Args a, UnitOut* uo) {
         vec8<POS, TAIL>(ld, l, k, V, v);
         const uint32_t bits = RAISE ? pen_bits8(bm, k) : 0u;
         const uint4 dv = make_uint4(v.w[0], v.w[1], v.w[2], v.w[3]);
-        (void)row_vec<(l < NSAMP)>(v, k, c, gcq, t1q, lds_addr(histq) + hlane, exq, aq);
+        (void)row_vec<(l < NSAMP)>(v, k, c, gcq, t1q, histq, hlane, exq, aq);
         file_round<LOW>(l, code[l][0], code[l][1], dv, true, bits, cut_code, RAISE, slot_arr, nslot);
       }
       if constexpr (l % 2 == 1 || l == NR - 1) {
