@@ -1149,7 +1149,8 @@ __global__ __launch_bounds__(NT_F) void k_pair_fast(Args a, UnitOut* uo) {
   auto stream_a = [&]<bool POS, bool TAIL>() __attribute__((always_inline)) {
   static_for<NR>([&]<int l>() __attribute__((always_inline)) {
     const uint4 ld = stg[l % NSTG];
-    if constexpr (l % 5 == 0) __builtin_amdgcn_s_setprio(3 - l / 5);   // lagging waves first
+    if constexpr (l == 0 || l == 6 || l == 12 || l == 17)   // lagging waves first
+      __builtin_amdgcn_s_setprio(l == 0 ? 3 : l == 6 ? 2 : l == 12 ? 1 : 0);
     if constexpr (l == 1) {
       // Each distinct penalized id is listed once; the thread that listed it
       // loads its target and draft logits now (stored to the list a few
@@ -1320,7 +1321,8 @@ __global__ __launch_bounds__(NT_F) void k_pair_fast(Args a, UnitOut* uo) {
     auto stream_b = [&]<bool POS, int LOW, bool RAISE, bool TAIL>() __attribute__((always_inline)) {
     static_for<NR>([&]<int l>() __attribute__((always_inline)) {
       const uint4 ld = stg[(NR + l) % NSTG];
-      if constexpr (l % 5 == 0) __builtin_amdgcn_s_setprio(3 - l / 5);
+      if constexpr (l == 0 || l == 6 || l == 12 || l == 17)
+        __builtin_amdgcn_s_setprio(l == 0 ? 3 : l == 6 ? 2 : l == 12 ? 1 : 0);
       const int k = l * NT + tid;
       if (k < nvec) {
         Vec8 v;
