@@ -379,6 +379,25 @@ def test_single_pass_draw_order():
     assert tot[0] >= 128 and rejected >= 64
 
 
+@pytest.mark.parametrize("case", ["penalty_ragged", "raise_tail", "whole_vectors"])
+def test_single_pass_unit_loop(case):
+    """More units than the device has compute units: the single-pass
+    workgroups run in several waves per CU, with units past K_r (skipped),
+    accepted and rejected positions, bonus rows and penalties mixed among
+    them, at a modest V that the oracle covers row by row."""
+    kw = {"penalty_ragged": dict(seed=810, V=12007, rep_penalty=1.2, n_prior=24, D=0.0),
+          "raise_tail": dict(seed=811, V=12007, rep_penalty=0.9, n_prior=8, D=0.5),
+          "whole_vectors": dict(seed=812, V=12008, rep_penalty=1.0, n_prior=0, D=0.0)}[case]
+    seed = kw.pop("seed")
+    w = wl.random_case(seed, B=160, K_max=4, dtype="bf16", top_p=0.9, sigma=3.0, corr=0.8,
+                       T_range=(0.7, 1.2), ragged=True, **kw)
+    assert w.B * (w.K_max + 1) > 512   # at least two units per CU on 256 CUs
+    g = gpu_sample(w)
+    c, f = compare_sample(g, oracle_sample(w), w)
+    print(f"unit loop {case}: checked {c} rows, near-tie rows {f}")
+    assert c >= 120
+
+
 def test_single_pass_fallback_routes():
     """bf16 + top-p cases that the single-pass kernel hands to its exact
     fallback: a flat distribution (nucleus larger than the per-lane slots), a
