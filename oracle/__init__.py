@@ -13,6 +13,8 @@ philox   Philox4x32-10 counter-based generator, written from its published
 verify   The verify step itself: logit processing, top-p, TV distance, the
          mentored-decoding mixture, acceptance, first-rejection scan,
          correction/bonus draw, and greedy verify.
+confidence  The draft-side confidence step before it: each draft row's top-1
+         probability and the draft length an early-stop threshold implies.
 
 Parity status of each function is stated in its docstring.  Two readings are
 "parity unpinned" by the pages (the repetition-penalty formula and the top-p
@@ -28,5 +30,6 @@ from .verify import (
     process_dist, tv_distance, mentored_theta, inverse_cdf, verify_sample_ref,
     verify_greedy_ref, SampleResult, GreedyResult,
 )
+from .confidence import top1_prob, draft_lengths, draft_confidence_ref
 
 __all__ = [n for n in dir() if not n.startswith("_")]
