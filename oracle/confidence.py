@@ -18,8 +18,10 @@ Readings where the section is silent (each is listed in the design doc):
   * "below" is strict: row j stops the proposal when top1_j < threshold;
   * a request proposes K_r = j + 1 tokens when j is its first row below the
     threshold, and K_max when no row is;
-  * a row holding a non-finite logit, or a request with T not in (0, inf),
-    has no defined top-1 probability: NaN, which never stops a proposal.
+  * a logit of -inf is a masked token (probability 0); a row holding a NaN
+    or +inf logit, a row with no finite logit, or a request with T not in
+    (0, inf) has no defined top-1 probability: NaN, which never stops a
+    proposal.
 
 Parity: pinned by closed forms (uniform rows, two-level rows), the
 temperature scaling identity, and brute force over scipy-free explicit sums
@@ -36,9 +38,11 @@ def top1_prob(z, T):
     z: one row of logits (any float dtype); T: temperature > 0."""
     z = np.asarray(z, dtype=np.float64)
     T = float(T)
-    if z.size == 0 or not (T > 0.0 and math.isfinite(T)) or not np.all(np.isfinite(z)):
+    if z.size == 0 or not (T > 0.0 and math.isfinite(T)) or np.any(np.isnan(z)) or np.any(z == np.inf):
         return float("nan")
     m = z.max()
+    if m == -np.inf:
+        return float("nan")
     return float(1.0 / np.exp((z - m) / T).sum())
 
 

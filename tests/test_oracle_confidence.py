@@ -60,6 +60,13 @@ def test_undefined_rows_give_nan():
     assert math.isnan(top1_prob([1.0, float("inf")], 1.0))
     assert math.isnan(top1_prob([1.0, 2.0], 0.0))
     assert math.isnan(top1_prob([1.0, 2.0], float("inf")))
+    assert math.isnan(top1_prob([-np.inf, -np.inf], 1.0))
+
+
+def test_masked_tokens_have_zero_mass():
+    # -inf logits drop out: the row behaves as the row of its finite logits
+    assert top1_prob([2.0, -np.inf, 0.0, -np.inf], 1.0) == pytest.approx(1.0 / (1.0 + math.exp(-2.0)),
+                                                                          rel=1e-12)
 
 
 def test_draft_lengths_rule():
