@@ -164,6 +164,31 @@ int sd_verify_greedy(const sd_verify_args_t *args, void *workspace,
                      int32_t *out_argmax, void *stream);
 
 /* Human-readable text for a return code (static storage). */
+/* Draft-side confidence ("What I Gave Up to Make Speculative Decoding
+ * Faster", section "Confidence-guided early stop": after each draft token
+ * the probability of its most likely token is taken from the logits already
+ * produced; below a threshold the draft proposes nothing more, and that last
+ * token is still verified).
+ * draft_logits: device, B x K_max rows of V elements in the draft layout
+ *   above (row (r, j) at draft_logits + ((int64)r * K_max + j) * ld_draft),
+ *   dtype SD_F32 or SD_BF16, rows 16-byte aligned; read once, not written.
+ * temperature: device [B] fp32, or NULL for T = 1.
+ * out_top1: device [B][K_max] fp32 (required): max_i softmax(z / T)_i of
+ *   each row = 1 / sum_i exp((z_i - max z) / T).  -inf logits count as
+ *   masked tokens; a row with a NaN or +inf logit, a row with no finite
+ *   logit, or a request with T outside (0, inf) gets NaN.
+ * out_k: device [B] int32, or NULL: K_r = j + 1 for the first row j with
+ *   top1 < threshold (NaN never stops), else K_max.  It can feed the
+ *   k_per_row of sd_verify_sample.
+ * No workspace; two launches on `stream`.  Returns SD_OK; SD_EINVAL for a
+ * NULL or misaligned pointer, B, K_max or V < 1, ld_draft < V or not a
+ * 16-byte multiple, or a NaN threshold; SD_EUNSUPPORTED when B * K_max
+ * exceeds 2^31 - 1; SD_EHIP when a launch fails. */
+int sd_draft_confidence(const void *draft_logits, int32_t dtype, int32_t B,
+                        int32_t K_max, int32_t V, int64_t ld_draft,
+                        const float *temperature, float threshold,
+                        float *out_top1, int32_t *out_k, void *stream);
+
 const char *sd_strerror(int code);
 
 /* Test export: the processed, truncated, renormalized distributions of the

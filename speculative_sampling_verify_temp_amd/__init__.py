@@ -86,6 +86,8 @@ def _load():
     lib.sd_debug_fallback_units.restype = ctypes.c_int
     lib.sd_debug_uniforms.argtypes = [ctypes.c_uint64, ctypes.c_uint64, I32, I32, P, P, P]
     lib.sd_debug_uniforms.restype = ctypes.c_int
+    lib.sd_draft_confidence.argtypes = [P, I32, I32, I32, I32, ctypes.c_int64, P, ctypes.c_float, P, P, P]
+    lib.sd_draft_confidence.restype = ctypes.c_int
     return lib
 
 
@@ -277,3 +279,22 @@ def debug_uniforms(seed, offset, B, npos, device="cuda", stream=None):
     if rc != SD_OK:
         raise SdVerifyError(rc, "sd_debug_uniforms")
     return u, v
+
+
+def draft_confidence(draft, temperature=None, threshold=0.6, stream=None):
+    """Top-1 probability of each draft row and the early-stop draft length.
+
+    draft: [B][K_max][V] float32 or bfloat16 device tensor (rows back to
+    back); temperature: [B] float32 device tensor or None (T = 1).  Returns
+    (top1 [B][K_max] float32, K [B] int32) from sd_draft_confidence."""
+    import torch
+    B, K, V = draft.shape
+    ld = _rows_ld(draft, "draft")
+    top1 = torch.empty((B, K), dtype=torch.float32, device=draft.device)
+    kout = torch.empty(B, dtype=torch.int32, device=draft.device)
+    rc = lib.sd_draft_confidence(_ptr(draft), _dtype_code(draft), B, K, V, ld,
+                                 _ptr(temperature), float(threshold), _ptr(top1), _ptr(kout),
+                                 _stream(stream))
+    if rc != 0:
+        raise SdVerifyError(rc, "sd_draft_confidence")
+    return top1, kout

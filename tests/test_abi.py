@@ -113,3 +113,29 @@ def test_phase_kernel_names_follow_the_path_choice():
     assert sdv.phase_kernel(a, 3) is None
     a.B = 0
     assert sdv.phase_kernel(a, 0) is None
+
+
+def test_draft_confidence_rejects_bad_arguments_on_host():
+    """Every call here fails a host-side check, so nothing is launched (the
+    pointers are never dereferenced)."""
+    import speculative_sampling_verify_temp_amd as sdv
+    lib = ctypes.CDLL(sdv.LIB_PATH)
+    f = lib.sd_draft_confidence
+    P, I32 = ctypes.c_void_p, ctypes.c_int32
+    f.argtypes = [P, I32, I32, I32, I32, ctypes.c_int64, P, ctypes.c_float, P, P, P]
+    f.restype = ctypes.c_int
+    good, out = P(1 << 20), P(1 << 21)
+    cases = [
+        (None, sdv.SD_BF16, 2, 3, 64, 64, None, 0.6, out),          # no logits
+        (good, sdv.SD_BF16, 2, 3, 64, 64, None, 0.6, None),         # no top-1 output
+        (P((1 << 20) + 8), sdv.SD_BF16, 2, 3, 64, 64, None, 0.6, out),   # misaligned rows
+        (good, sdv.SD_BF16, 2, 3, 64, 60, None, 0.6, out),          # ld < V
+        (good, sdv.SD_BF16, 2, 3, 60, 60, None, 0.6, out),          # ld * 2 not a 16-byte multiple
+        (good, 7, 2, 3, 64, 64, None, 0.6, out),                    # unknown dtype
+        (good, sdv.SD_F32, 0, 3, 64, 64, None, 0.6, out),           # B < 1
+        (good, sdv.SD_F32, 2, 0, 64, 64, None, 0.6, out),           # K_max < 1
+        (good, sdv.SD_F32, 2, 3, 0, 64, None, 0.6, out),            # V < 1
+        (good, sdv.SD_F32, 2, 3, 64, 64, None, float("nan"), out),  # NaN threshold
+    ]
+    for c in cases:
+        assert f(*c, None, None) == -1, c   # SD_EINVAL
