@@ -48,13 +48,17 @@ WORKLOAD = ("256 requests x K=8, V=152064, bf16 logits, T~U[0.5,1], top-p 0.9, "
             "penalty 1.1 (128 prior ids + draft prefix), TV budget 0.75")
 
 
+# The sources k_pair_fast is built from (the confidence kernel's file is not
+# one of them).
+VERIFY_SOURCES = ("sd_verify.hip", "sdv_device.h", "sdv_exact.h")
+
+
 def source_hash():
-    """sha256 over the kernel sources, in name order."""
+    """sha256 over the verify kernels' sources, in name order."""
     h = hashlib.sha256()
-    for n in sorted(os.listdir(CSRC)):
-        if n.endswith((".hip", ".h")):
-            h.update(n.encode())
-            h.update(open(os.path.join(CSRC, n), "rb").read())
+    for n in sorted(VERIFY_SOURCES):
+        h.update(n.encode())
+        h.update(open(os.path.join(CSRC, n), "rb").read())
     return h.hexdigest()
 
 
@@ -180,6 +184,8 @@ def main():
     ap.add_argument("--copy-probe", type=int, default=0,
                     help="bytes of one plain device copy run before the warmup")
     ap.add_argument("--digest-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"))
+    ap.add_argument("--confidence", action="store_true",
+                    help="time the draft-side confidence step (sd_draft_confidence) instead")
     a = ap.parse_args()
     if a.digest_pmc:
         if a.copy_probe <= 0:
@@ -191,6 +197,10 @@ def main():
               "data-parallel over requests and this build has no multi-GPU path; "
               "run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
+
+    if a.confidence:
+        confidence_bench(a)
+        return
 
     import numpy as np
     import torch
@@ -284,6 +294,75 @@ def main():
     if not a.no_cpu_baseline:
         print("[bench] timing the CPU oracle on a sample", file=sys.stderr, flush=True)
         line["cpu_baseline"] = cpu_baseline(w)
+    print(json.dumps(line), flush=True)
+
+
+def confidence_bench(a):
+    """The draft-side confidence step on the verify workload's draft rows
+    (256 requests x 8 rows x V = 152064, bf16): one sd_draft_confidence call
+    per step, every draft logit read once."""
+    import numpy as np
+    import torch
+    import speculative_sampling_verify_temp_amd as sdv
+    import workloads as wl
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    w = wl.config4()
+    d = device_inputs(w, torch, dev)
+    draft, temp = d["draft"], d["temperature"]
+    thr = 0.6   # the threshold of the page's run
+    stream = torch.cuda.current_stream()
+    for _ in range(a.warmup):
+        sdv.draft_confidence(draft, temp, thr, stream)
+    torch.cuda.synchronize()
+    E = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
+    start, end = E(), E()
+    start.record(stream)
+    for _ in range(a.steps):
+        top1, kout = sdv.draft_confidence(draft, temp, thr, stream)
+    end.record(stream)
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / a.steps
+    # the row kernel alone (no draft-length launch), for its roofline
+    k0, k1 = E(), E()
+    k0.record(stream)
+    for _ in range(a.steps):
+        sdv.draft_confidence(draft, temp, thr, stream, lengths=False)
+    k1.record(stream)
+    torch.cuda.synchronize()
+    ms_k = k0.elapsed_time(k1) / a.steps
+    rows = w.B * w.K_max
+    nbytes = rows * w.V * 2
+    achieved = nbytes / (ms_k * 1e-3) / 1e9
+    line = {
+        "metric": "draft rows scored/sec (top-1 probability), V=152064 bf16",
+        "value": rows / (ms * 1e-3),
+        "unit": "rows/s",
+        "n_gpus": 1, "steps": a.steps, "warmup": a.warmup, "ms_per_step": ms,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "f32", "data": "synthetic",
+        "config": {"workload": "draft confidence: 256 requests x 8 draft rows, V=152064, bf16 logits, "
+                               "T~U[0.5,1], threshold 0.6",
+                   "B": w.B, "K": w.K_max, "V": w.V, "input_dtype": "bf16"},
+        "roofline": {"kernel": "k_draft_confidence", "bound": "hbm", "achieved": achieved,
+                     "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": achieved / PEAK_HBM_GBPS,
+                     "traffic": None, "algorithmic_bytes": nbytes},
+        "kernel_ms": ms_k,
+        "mean_k": float(kout.float().mean().item()),
+    }
+    if not a.no_cpu_baseline:
+        import oracle
+        df = w.draft_f32()
+        t0, n = time.perf_counter(), 0
+        while n < rows and (n < 2 or time.perf_counter() - t0 < 10.0):
+            r, j = divmod(n, w.K_max)
+            oracle.top1_prob(df[r, j], float(w.temperature[r]))
+            n += 1
+        dt = time.perf_counter() - t0
+        line["cpu_baseline"] = {"value": n / dt, "unit": "rows/s", "cores": 1, "kind": "oracle",
+                                "sample": f"the first {n} draft rows of the same workload in {dt:.1f} s, "
+                                          "numpy fp64 on one thread"}
     print(json.dumps(line), flush=True)
 
 

@@ -281,17 +281,18 @@ def debug_uniforms(seed, offset, B, npos, device="cuda", stream=None):
     return u, v
 
 
-def draft_confidence(draft, temperature=None, threshold=0.6, stream=None):
+def draft_confidence(draft, temperature=None, threshold=0.6, stream=None, lengths=True):
     """Top-1 probability of each draft row and the early-stop draft length.
 
     draft: [B][K_max][V] float32 or bfloat16 device tensor (rows back to
     back); temperature: [B] float32 device tensor or None (T = 1).  Returns
-    (top1 [B][K_max] float32, K [B] int32) from sd_draft_confidence."""
+    (top1 [B][K_max] float32, K [B] int32) from sd_draft_confidence; with
+    lengths=False, K is None and only the row kernel runs."""
     import torch
     B, K, V = draft.shape
     ld = _rows_ld(draft, "draft")
     top1 = torch.empty((B, K), dtype=torch.float32, device=draft.device)
-    kout = torch.empty(B, dtype=torch.int32, device=draft.device)
+    kout = torch.empty(B, dtype=torch.int32, device=draft.device) if lengths else None
     rc = lib.sd_draft_confidence(_ptr(draft), _dtype_code(draft), B, K, V, ld,
                                  _ptr(temperature), float(threshold), _ptr(top1), _ptr(kout),
                                  _stream(stream))
