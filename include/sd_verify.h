@@ -84,7 +84,9 @@ extern "C" {
                                          the draft could not have drawn)       */
 #define SD_ST_RESID_ZERO   (1u << 6)  /* the correction residual had zero mass;
                                          drew from p instead                    */
-#define SD_ST_INVALID_MASK 0xFu
+#define SD_ST_BAD_PARAM    (1u << 7)  /* top_p_per_row[r] outside (0, 1] or
+                                         tv_budget_per_row[r] < 0 or NaN invalid */
+#define SD_ST_INVALID_MASK 0x8Fu
 
 /* Largest supported K_max (draft positions per request). */
 #define SD_MAX_K 32
@@ -126,6 +128,12 @@ typedef struct sd_verify_args {
   uint64_t       seed;           /* Philox4x32-10 key (lo, hi words)           */
   uint64_t       offset;         /* Philox counter words 2-3                   */
   uint32_t       flags;          /* SD_NO_BONUS | SD_PENALTY_PRIOR_ONLY        */
+  /* Per-request sampling parameters (device [B] fp32, or NULL for the
+   * scalars above, which are then checked on the host).  When given, they
+   * replace top_p and tv_budget request by request; a request whose value
+   * is out of range gets SD_ST_BAD_PARAM.  Greedy ignores both. */
+  const float   *top_p_per_row;
+  const float   *tv_budget_per_row;
 } sd_verify_args_t;
 
 /* Bytes of device workspace sd_verify_sample / sd_verify_greedy need for

@@ -25,7 +25,7 @@ by brute force against a full sort, see tests/test_oracle_*.py.
 from .philox import philox4x32_10, uniforms_for
 from .verify import (
     ST_BAD_K, ST_BAD_TEMP, ST_BAD_DRAFT_ID, ST_NONFINITE, ST_BAD_PRIOR,
-    ST_Q_ZERO, ST_RESID_ZERO, ST_INVALID_MASK, FLAG_NO_BONUS,
+    ST_Q_ZERO, ST_RESID_ZERO, ST_BAD_PARAM, ST_INVALID_MASK, FLAG_NO_BONUS,
     FLAG_PENALTY_PRIOR_ONLY, penalty_keys, softmax64, top_p_filter,
     process_dist, tv_distance, mentored_theta, inverse_cdf, verify_sample_ref,
     verify_greedy_ref, SampleResult, GreedyResult,

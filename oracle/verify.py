@@ -61,7 +61,9 @@ ST_NONFINITE = 1 << 3      # NaN/+Inf logit, or a row of only -Inf  (invalid)
 ST_BAD_PRIOR = 1 << 4      # a prior id outside [0, V) was ignored  (info)
 ST_Q_ZERO = 1 << 5         # q(x_j) = 0 at a position j < K_r       (info)
 ST_RESID_ZERO = 1 << 6     # residual mass was 0; drew from p       (info)
-ST_INVALID_MASK = ST_BAD_K | ST_BAD_TEMP | ST_BAD_DRAFT_ID | ST_NONFINITE
+ST_BAD_PARAM = 1 << 7      # per-request top-p outside (0, 1] or TV
+                           # budget < 0 or NaN                      (invalid)
+ST_INVALID_MASK = ST_BAD_K | ST_BAD_TEMP | ST_BAD_DRAFT_ID | ST_NONFINITE | ST_BAD_PARAM
 
 FLAG_NO_BONUS = 1 << 0
 FLAG_PENALTY_PRIOR_ONLY = 1 << 1
@@ -319,6 +321,10 @@ def verify_sample_ref(target, draft, draft_ids, k_per_row=None,
     target: fp32 [B][K_max+1][V]; draft: fp32 [B][K_max][V];
     draft_ids: int [B][K_max]; k_per_row: int [B] or None (= K_max);
     temperature: fp32 [B] or None (= 1); prior CSR or None.
+    top_p, tv_budget: a scalar for every request, or an array [B] of
+    per-request values (fp32); a per-request value out of range (top-p
+    outside (0, 1], budget negative or NaN) makes that request invalid
+    (ST_BAD_PARAM), as the library does.
     rows: optional subset of rows to evaluate (others stay at -1 / 0).
     """
     B, K1, V = target.shape
@@ -335,6 +341,11 @@ def verify_sample_ref(target, draft, draft_ids, k_per_row=None,
         T = 1.0 if temperature is None else float(np.float32(temperature[r]))
         if st == 0 and not (np.isfinite(T) and T > 0.0):
             st = ST_BAD_TEMP
+        tp_r = float(np.float32(top_p[r])) if np.ndim(top_p) else float(top_p)
+        D_r = float(np.float32(tv_budget[r])) if np.ndim(tv_budget) else float(tv_budget)
+        if np.ndim(top_p) or np.ndim(tv_budget):
+            if not (tp_r > 0.0 and tp_r <= 1.0) or not (D_r >= 0.0):
+                st |= ST_BAD_PARAM
         prior, st_prior = _row_prior(prior_ids, prior_offsets, r, V)
         if st:
             status[r] = st | st_prior
@@ -344,7 +355,7 @@ def verify_sample_ref(target, draft, draft_ids, k_per_row=None,
         rr = verify_sample_row(
             np.asarray(target[r, :K + 1], dtype=np.float32),
             np.asarray(draft[r, :K], dtype=np.float32), x[:K], K, prior, T,
-            top_p, rep_penalty, tv_budget, u, v, V, flags)
+            tp_r, rep_penalty, D_r, u, v, V, flags)
         rr.status |= st_prior
         status[r] = rr.status
         out_rows[r] = rr

@@ -23,7 +23,8 @@ SD_F32, SD_BF16 = 0, 1
 SD_NO_BONUS, SD_PENALTY_PRIOR_ONLY = 1, 2
 SD_ST_BAD_K, SD_ST_BAD_TEMP, SD_ST_BAD_DRAFT_ID, SD_ST_NONFINITE = 1, 2, 4, 8
 SD_ST_BAD_PRIOR, SD_ST_Q_ZERO, SD_ST_RESID_ZERO = 16, 32, 64
-SD_ST_INVALID_MASK = 0xF
+SD_ST_BAD_PARAM = 1 << 7
+SD_ST_INVALID_MASK = 0x8F
 SD_NSTAT = 8
 SD_MAX_K = 32
 STAT_NAMES = ("d", "theta", "p_x", "q_x", "pi_x", "u", "v", "S")
@@ -50,6 +51,8 @@ class SdVerifyArgs(ctypes.Structure):
         ("seed", ctypes.c_uint64),
         ("offset", ctypes.c_uint64),
         ("flags", ctypes.c_uint32),
+        ("top_p_per_row", ctypes.c_void_p),
+        ("tv_budget_per_row", ctypes.c_void_p),
     ]
 
 
@@ -145,7 +148,17 @@ def make_args(target, draft, draft_ids, k_per_row=None, temperature=None, top_p=
     a.draft_ids = draft_ids.data_ptr() if draft_ids is not None and draft_ids.numel() else None
     a.k_per_row = None if k_per_row is None else k_per_row.data_ptr()
     a.temperature = None if temperature is None else temperature.data_ptr()
-    a.top_p, a.rep_penalty, a.tv_budget = float(top_p), float(rep_penalty), float(tv_budget)
+    # top_p and tv_budget: a float, or a [B] float32 device tensor of
+    # per-request values (the scalar field is then unused)
+    if hasattr(top_p, "data_ptr"):
+        a.top_p, a.top_p_per_row = 1.0, top_p.data_ptr()
+    else:
+        a.top_p, a.top_p_per_row = float(top_p), None
+    if hasattr(tv_budget, "data_ptr"):
+        a.tv_budget, a.tv_budget_per_row = 0.0, tv_budget.data_ptr()
+    else:
+        a.tv_budget, a.tv_budget_per_row = float(tv_budget), None
+    a.rep_penalty = float(rep_penalty)
     a.prior_ids = None if prior_ids is None else prior_ids.data_ptr()
     a.prior_offsets = None if prior_offsets is None else prior_offsets.data_ptr()
     a.seed = int(seed) & (2**64 - 1)

@@ -95,7 +95,7 @@ __global__ __launch_bounds__(NT_ROW) void k_row_prepare(Args a, RowStat* rs, int
   const char* row = is_t ? target_row(a, r, j) : draft_row(a, r, j);
   const float c = 1.4426950408889634f / T;
   const bool pen = build_penalty_bitmap<NT>(a, r, j, 0, a.V, bm);
-  RowStat out = row_stats_dev<DT, NT>(a, row, c, pen, bm, L);
+  RowStat out = row_stats_dev<DT, NT>(a, row, c, pen, bm, L, request_top_p(a, r));
   if (threadIdx.x == 0) {
     if (j < K) {
       const int x = a.ids[(int64_t)r * a.K_max + j];
@@ -144,6 +144,7 @@ __device__ uint32_t request_status(const Args& a, int r, int K, float T, bool ch
   uint32_t st = 0;
   if (K < 0 || K > a.K_max) st |= SD_ST_BAD_K;
   if (check_temp && (!(T > 0.0f) || !(T < INFINITY))) st |= SD_ST_BAD_TEMP;
+  if (check_temp && !params_ok(request_top_p(a, r), request_D(a, r))) st |= SD_ST_BAD_PARAM;
   int badid = 0, badprior = 0;
   if (!(st & SD_ST_BAD_K))
     for (int t = threadIdx.x; t < K; t += NT) {
@@ -214,7 +215,7 @@ __global__ __launch_bounds__(NT_ROW) void k_finalize(Args a, const RowStat* rs, 
       if (jj == K) break;
       const RowStat P = rs[row_index(a, r, true, jj)], Q = rs[row_index(a, r, false, jj)];
       const double d = tv_valid ? dtv[(int64_t)r * a.K_max + jj] : 0.0;
-      const Decision dc = decide(P, Q, P.kx, Q.kx, (double)T, (double)a.D, tv_valid != 0, d, u);
+      const Decision dc = decide(P, Q, P.kx, Q.kx, (double)T, (double)request_D(a, r), tv_valid != 0, d, u);
       if (dc.qx == 0.0) st |= SD_ST_Q_ZERO;
       sv[SD_STAT_D] = (float)d;
       sv[SD_STAT_THETA] = (float)dc.th;
@@ -965,25 +966,46 @@ __device__ int32_t g_zero_words[2];
 struct ReqWords {
   uint64_t off;        // two words: the request's prior-id list bounds
   uint32_t k, t, x;    // K, T (bits), the draft token
+  uint32_t tp, d;      // the request's top-p and TV budget (bits)
 };
 
-// The four scalar loads issued back to back and awaited once (the compiler
-// would otherwise wait for each before issuing the next).  Every pointer
-// must address readable words.
+// The scalar loads issued back to back and awaited once (the compiler
+// would otherwise wait for each before issuing the next): four, and the two
+// per-request parameter words when PR.  Every pointer must address
+// readable words.
+template <bool PR>
 __device__ __forceinline__ ReqWords request_words(const int32_t* po, const int32_t* pk,
-                                                  const int32_t* pt, const int32_t* px) {
+                                                  const int32_t* pt, const int32_t* px,
+                                                  const int32_t* ptp, const int32_t* pd) {
   ReqWords w;
+  w.tp = w.d = 0u;
+  if constexpr (!PR) {
+    asm volatile(
+        "s_load_dwordx2 %0, %4, 0x0\n\t"
+        "s_load_dword %1, %5, 0x0\n\t"
+        "s_load_dword %2, %6, 0x0\n\t"
+        "s_load_dword %3, %7, 0x0\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&s"(w.off), "=&s"(w.k), "=&s"(w.t), "=&s"(w.x)
+        : "s"(po), "s"(pk), "s"(pt), "s"(px));
+    return w;
+  }
   asm volatile(
-      "s_load_dwordx2 %0, %4, 0x0\n\t"
-      "s_load_dword %1, %5, 0x0\n\t"
-      "s_load_dword %2, %6, 0x0\n\t"
-      "s_load_dword %3, %7, 0x0\n\t"
+      "s_load_dwordx2 %0, %6, 0x0\n\t"
+      "s_load_dword %1, %7, 0x0\n\t"
+      "s_load_dword %2, %8, 0x0\n\t"
+      "s_load_dword %3, %9, 0x0\n\t"
+      "s_load_dword %4, %10, 0x0\n\t"
+      "s_load_dword %5, %11, 0x0\n\t"
       "s_waitcnt lgkmcnt(0)"
-      : "=&s"(w.off), "=&s"(w.k), "=&s"(w.t), "=&s"(w.x)
-      : "s"(po), "s"(pk), "s"(pt), "s"(px));
+      : "=&s"(w.off), "=&s"(w.k), "=&s"(w.t), "=&s"(w.x), "=&s"(w.tp), "=&s"(w.d)
+      : "s"(po), "s"(pk), "s"(pt), "s"(px), "s"(ptp), "s"(pd));
   return w;
 }
 
+// PR: per-request top-p / TV budget arrays are given (else the host-checked
+// scalars apply to every request).
+template <bool PR>
 __global__ __launch_bounds__(NT_F) void k_pair_fast(Args a, UnitOut* uo) {
   constexpr int NT = NT_F;
   __shared__ uint32_t bm[MAXV_FAST / 32];
@@ -1042,7 +1064,6 @@ __global__ __launch_bounds__(NT_F) void k_pair_fast(Args a, UnitOut* uo) {
   if (bonus) j = min(max(request_k(a, r), 0), a.K_max);
   const int V = a.V, nvec = (V + VEC - 1) / VEC;
   const float rep = a.rep;
-  const double tp = (double)a.top_p;
   const char* trow = target_row(a, r, j);
   const char* drow = bonus ? trow : draft_row(a, r, j);
   const __amdgpu_buffer_rsrc_t rs_t = row_rsrc(trow, nvec * 16);
@@ -1092,16 +1113,24 @@ __global__ __launch_bounds__(NT_F) void k_pair_fast(Args a, UnitOut* uo) {
   float u_j, v_j;
   uniforms(a.seed, a.offset, r, j, u_j, v_j);
   // The request's words in one round trip: the prior-id list bounds, the
-  // draft token x_j, K and T (an absent array, and the draft token of a
-  // bonus unit, read a zero word instead, which is then not used).
+  // draft token x_j, K, T, top-p and the TV budget (an absent array, and
+  // the draft token of a bonus unit, read a zero word instead, which is then
+  // not used).
   const bool pen_prior = a.rep != 1.0f && a.prior && a.poff;
-  const ReqWords rw = request_words(pen_prior ? a.poff + r : g_zero_words,
+  const ReqWords rw = request_words<PR>(pen_prior ? a.poff + r : g_zero_words,
                                     a.kpr ? a.kpr + r : g_zero_words,
                                     a.temp ? reinterpret_cast<const int32_t*>(a.temp + r) : g_zero_words,
-                                    bonus ? g_zero_words : a.ids + (int64_t)r * a.K_max + j);
+                                    bonus ? g_zero_words : a.ids + (int64_t)r * a.K_max + j,
+                                    PR && a.tpr ? reinterpret_cast<const int32_t*>(a.tpr + r) : g_zero_words,
+                                    PR && a.dpr ? reinterpret_cast<const int32_t*>(a.dpr + r) : g_zero_words);
   const int K = a.kpr ? (int)rw.k : a.K_max;
   const float T = a.temp ? __uint_as_float(rw.t) : 1.0f;
-  if (K < 0 || K > a.K_max || (bonus ? j != K : j >= K) || !(T > 0.0f) || !(T < INFINITY)) return;
+  const float top_p = PR && a.tpr ? __uint_as_float(rw.tp) : a.top_p;
+  const float Dr = PR && a.dpr ? __uint_as_float(rw.d) : a.D;
+  if (K < 0 || K > a.K_max || (bonus ? j != K : j >= K) || !(T > 0.0f) || !(T < INFINITY) ||
+      (PR && !params_ok(top_p, Dr)))
+    return;
+  const double tp = (double)top_p;
   const float c = 1.4426950408889634f / T;
   const int po0 = (int)(uint32_t)rw.off, po1 = (int)(uint32_t)(rw.off >> 32);
   PenSet ps;
@@ -1494,7 +1523,7 @@ __global__ __launch_bounds__(NT_F) void k_pair_fast(Args a, UnitOut* uo) {
       RowStat Q;
       Q.kord = ord_key(kq_cut);
       const double qx = kept(Q, ord_key(kxq)) ? s_xe[1] / Zkq : 0.0;   // as prob_at
-      const Decision dc = decide_from(s_xe[0], qx, (double)a.D, true, d, u_j);
+      const Decision dc = decide_from(s_xe[0], qx, (double)Dr, true, d, u_j);
       out.d = (float)d;
       out.th = (float)dc.th;
       out.px = (float)dc.px;
@@ -1651,7 +1680,7 @@ __device__ __forceinline__ void fallback_unit(const Args& a, UnitOut* uo, int u)
   out.flags = UO_SLOW;
   out.accept = 1;
   out.y = -1;
-  const RowStat P = row_stats_dev<SD_BF16, NT>(a, trow, c, pen, bm, ex);
+  const RowStat P = row_stats_dev<SD_BF16, NT>(a, trow, c, pen, bm, ex, request_top_p(a, r));
   if (P.flags & NONFINITE) {
     if (tid == 0) {
       out.flags = UO_NONFINITE;
@@ -1668,7 +1697,7 @@ __device__ __forceinline__ void fallback_unit(const Args& a, UnitOut* uo, int u)
     }
     return;
   }
-  const RowStat Q = row_stats_dev<SD_BF16, NT>(a, drow, c, pen, bm, ex);
+  const RowStat Q = row_stats_dev<SD_BF16, NT>(a, drow, c, pen, bm, ex, request_top_p(a, r));
   if (Q.flags & NONFINITE) {
     if (tid == 0) {
       out.flags = UO_NONFINITE;
@@ -1688,7 +1717,7 @@ __device__ __forceinline__ void fallback_unit(const Args& a, UnitOut* uo, int u)
         kxq = penalize(kxq, a.rep);
       }
     }
-    const Decision dc = decide(P, Q, kxp, kxq, (double)T, (double)a.D, true, d, out.u);
+    const Decision dc = decide(P, Q, kxp, kxq, (double)T, (double)request_D(a, r), true, d, out.u);
     out.d = (float)d;
     out.th = (float)dc.th;
     out.px = (float)dc.px;
@@ -1735,19 +1764,21 @@ __global__ __launch_bounds__(NT_FB) void k_pair_fallback(Args a, UnitOut* uo, in
     uint32_t fw[UPT];
     int kr[UPT];
     float tr[UPT];
+    bool pok[UPT];
     static_for<UPT>([&]<int i>() __attribute__((always_inline)) {
       const int u = min(c + i * NT + tid, nunits - 1);   // loads stay unconditional
       const int r = u < npairs ? u / a.K_max : u - npairs;
       fw[i] = uo[u].flags;
       kr[i] = request_k(a, r);
       tr[i] = request_t(a, r);
+      pok[i] = params_ok(request_top_p(a, r), request_D(a, r));
     });
     static_for<UPT>([&]<int i>() __attribute__((always_inline)) {
       const int u = c + i * NT + tid;
       const bool bonus = u >= npairs;
       const int j = bonus ? 0 : u % a.K_max;
       const bool valid = u < nunits && kr[i] >= 0 && kr[i] <= a.K_max && (bonus || j < kr[i]) &&
-                         tr[i] > 0.0f && tr[i] < INFINITY;
+                         tr[i] > 0.0f && tr[i] < INFINITY && pok[i];
       if (valid && (fw[i] & UO_FALLBACK)) fl |= 1u << i;
     });
     int total;
@@ -2045,8 +2076,8 @@ int check_common(const sd_verify_args_t* a, bool sample) {
     return SD_EINVAL;
   if (!(a->rep_penalty > 0.0f) || !(a->rep_penalty < INFINITY)) return SD_EINVAL;
   if (sample) {
-    if (!(a->top_p > 0.0f) || !(a->top_p <= 1.0f)) return SD_EINVAL;
-    if (!(a->tv_budget >= 0.0f)) return SD_EINVAL;
+    if (!a->top_p_per_row && (!(a->top_p > 0.0f) || !(a->top_p <= 1.0f))) return SD_EINVAL;
+    if (!a->tv_budget_per_row && !(a->tv_budget >= 0.0f)) return SD_EINVAL;
   }
   if ((a->prior_ids == nullptr) != (a->prior_offsets == nullptr)) return SD_EINVAL;
   if (a->flags & ~(SD_NO_BONUS | SD_PENALTY_PRIOR_ONLY)) return SD_EINVAL;
@@ -2069,6 +2100,8 @@ Args make_args(const sd_verify_args_t* s) {
   a.top_p = s->top_p;
   a.rep = s->rep_penalty;
   a.D = s->tv_budget;
+  a.tpr = s->top_p_per_row;
+  a.dpr = s->tv_budget_per_row;
   a.prior = s->prior_ids;
   a.poff = s->prior_offsets;
   a.seed = s->seed;
@@ -2094,7 +2127,7 @@ int launch_status() {
 
 // The single-pass kernel covers bf16 rows with top-p on and V <= 155648.
 bool use_fast(const Args& a) {
-  return a.dtype == SD_BF16 && a.top_p < 1.0f && a.V <= MAXV_FAST;
+  return a.dtype == SD_BF16 && (a.tpr || a.top_p < 1.0f) && a.V <= MAXV_FAST;
 }
 
 template <int DT>
@@ -2106,7 +2139,7 @@ int run_prepare(const Args& a, const Layout& L, char* ws, hipStream_t st) {
 }
 
 bool needs_tv(const Args& a, const float* stats) {
-  return stats != nullptr || (a.D > 0.0f && a.D < 1.0f);
+  return stats != nullptr || a.dpr != nullptr || (a.D > 0.0f && a.D < 1.0f);
 }
 
 // One phase of the sampling path.  Single-pass path: 0 = k_pair_fast,
@@ -2118,7 +2151,10 @@ int run_phase(const Args& a, const Layout& L, char* ws, int phase, int32_t* acc,
   if (DT == SD_BF16 && use_fast(a)) {
     UnitOut* uo = reinterpret_cast<UnitOut*>(ws + L.uo);
     if (phase == 0) {
-      hipLaunchKernelGGL(k_pair_fast, dim3(a.B * a.K_max + a.B), dim3(NT_F), 0, st, a, uo);
+      if (a.tpr || a.dpr)
+        hipLaunchKernelGGL(k_pair_fast<true>, dim3(a.B * a.K_max + a.B), dim3(NT_F), 0, st, a, uo);
+      else
+        hipLaunchKernelGGL(k_pair_fast<false>, dim3(a.B * a.K_max + a.B), dim3(NT_F), 0, st, a, uo);
       return launch_status();
     }
     if (phase == 1) {

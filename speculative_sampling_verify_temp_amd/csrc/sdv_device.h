@@ -31,6 +31,8 @@ struct Args {
   uint64_t seed, offset;
   uint32_t flags;
   int fp_shift;       // fixed-point scale exponent of masses (see e_fixed)
+  const float* tpr;   // per-request top-p, or null (top_p)
+  const float* dpr;   // per-request TV budget, or null (D)
 };
 
 // Per processed row (target j or draft j of request r).
@@ -47,6 +49,19 @@ static_assert(sizeof(RowStat) == 32, "RowStat layout");
 
 __device__ __forceinline__ int request_k(const Args& a, int r) {
   return a.kpr ? a.kpr[r] : a.K_max;
+}
+
+__device__ __forceinline__ float request_top_p(const Args& a, int r) {
+  return a.tpr ? a.tpr[r] : a.top_p;
+}
+
+__device__ __forceinline__ float request_D(const Args& a, int r) {
+  return a.dpr ? a.dpr[r] : a.D;
+}
+
+// A request's top-p and TV budget are usable: top-p in (0, 1], D >= 0.
+__device__ __forceinline__ bool params_ok(float tp, float D) {
+  return tp > 0.0f && tp <= 1.0f && D >= 0.0f;
 }
 
 __device__ __forceinline__ float request_t(const Args& a, int r) {

@@ -98,7 +98,7 @@ __device__ void find_crossing(const uint64_t* hm, const uint32_t* hc, int nbins,
 // bits of the orderable key with fixed-point masses find the cut key.
 template <int DT, int NT>
 __device__ __forceinline__ RowStat row_stats_dev(const Args& a, const char* row, float c, bool pen,
-                                 const uint32_t* bm, const ExactLds& L) {
+                                 const uint32_t* bm, const ExactLds& L, float top_p) {
   const int V = a.V, nvec = (V + VEC - 1) / VEC;
   float m = -INFINITY;
   double Z = 0.0;
@@ -138,10 +138,10 @@ __device__ __forceinline__ RowStat row_stats_dev(const Args& a, const char* row,
   out.idcut = INT_MAX;
   out.flags = bad ? NONFINITE : 0;
   out.kx = 0.0f;
-  if (bad || !(a.top_p < 1.0f) || V <= 1) return out;
+  if (bad || !(top_p < 1.0f) || V <= 1) return out;
 
   const int sh = a.fp_shift;
-  const double tp = (double)a.top_p;
+  const double tp = (double)top_p;
   // Tokens whose key is below L hold at most (1 - top_p)/2 of the mass
   // together, so the cut lies at or above L; level-1 bins below L's bin are
   // not histogrammed (they are either fully in or fully out).

@@ -50,10 +50,16 @@ def gpu_sample(w, stats=True, dev=None):
     import torch
     import speculative_sampling_verify_temp_amd as sdv
     d = dev or to_device(w)
+
+    def per_request(x):   # a [B] array of per-request values goes to the device
+        if np.ndim(x) == 0:
+            return x
+        return torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(d["target"].device)
+
     acc, tok, st, sts = sdv.verify_sample(
         d["target"], d["draft"], d["draft_ids"], d["k_per_row"], d["temperature"],
-        w.top_p, w.rep_penalty, d["prior_ids"], d["prior_offsets"], w.tv_budget,
-        w.seed, w.offset, w.flags, stats=stats)
+        per_request(w.top_p), w.rep_penalty, d["prior_ids"], d["prior_offsets"],
+        per_request(w.tv_budget), w.seed, w.offset, w.flags, stats=stats)
     torch.cuda.synchronize()
     return dict(accepted=acc.cpu().numpy(), tokens=tok.cpu().numpy(),
                 status=st.cpu().numpy().astype(np.uint32),

@@ -139,3 +139,14 @@ def test_draft_confidence_rejects_bad_arguments_on_host():
     ]
     for c in cases:
         assert f(*c, None, None) == -1, c   # SD_EINVAL
+
+
+def test_args_struct_matches_the_header():
+    """The ctypes mirror ends with the two per-request parameter pointers,
+    at the offsets the C struct gives them (no field skipped or reordered)."""
+    import speculative_sampling_verify_temp_amd as sdv
+    A = sdv.SdVerifyArgs
+    names = [f[0] for f in A._fields_]
+    assert names[-2:] == ["top_p_per_row", "tv_budget_per_row"]
+    assert A.tv_budget_per_row.offset == A.top_p_per_row.offset + 8
+    assert ctypes.sizeof(A) == A.tv_budget_per_row.offset + 8

@@ -398,6 +398,28 @@ def test_single_pass_unit_loop(case):
     assert c >= 120
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_per_request_top_p_and_budget(dtype):
+    """Per-request top-p and TV budget arrays (device [B]): every request
+    runs with its own values, on the single-pass path (bf16) and the general
+    path (fp32); top-p = 1 rows go to the exact routines; out-of-range
+    values invalidate just their request."""
+    w = wl.random_case(960, B=48, K_max=4, V=20011 if dtype == "bf16" else 3001, dtype=dtype,
+                       D=0.0, top_p=0.9, sigma=3.0, corr=0.8, T_range=(0.7, 1.2), ragged=True,
+                       rep_penalty=1.1, n_prior=16)
+    rng = np.random.default_rng(5)
+    w.top_p = rng.choice([0.5, 0.8, 0.9, 0.95, 1.0], size=w.B).astype(np.float32)
+    w.tv_budget = rng.choice([0.0, 0.2, 0.5, 1.0, 2.0], size=w.B).astype(np.float32)
+    w.top_p[3], w.top_p[7] = 0.0, 1.5
+    w.tv_budget[11], w.tv_budget[13] = -0.1, np.nan
+    g = gpu_sample(w)
+    c, f = compare_sample(g, oracle_sample(w), w)
+    print(f"per-request parameters ({dtype}): checked {c} rows, near-tie rows {f}")
+    assert c >= 30
+    for r in (3, 7, 11, 13):
+        assert g["status"][r] & (1 << 7) and g["accepted"][r] == -1
+
+
 def test_single_pass_fallback_routes():
     """bf16 + top-p cases that the single-pass kernel hands to its exact
     fallback: a flat distribution (nucleus larger than the per-lane slots), a

@@ -383,3 +383,25 @@ def test_vocab_of_one():
     ids = np.zeros((2, 2), np.int32)
     s = ov.verify_sample_ref(t, d, ids, None, None, 0.5, 1.1, None, None, 0.4, 3, 9)
     assert s.accepted.tolist() == [2, 2] and s.tokens.tolist() == [[0, 0, 0]] * 2
+
+
+def test_per_request_top_p_and_budget():
+    """Per-request top-p and TV budget arrays act request by request exactly
+    as the scalars would, and an out-of-range value invalidates only its
+    request (status bit 7)."""
+    import workloads as wl
+    from oracle.verify import verify_sample_ref, ST_BAD_PARAM, ST_INVALID_MASK
+    w = wl.random_case(41, B=6, K_max=3, V=300, dtype="f32", top_p=0.9, sigma=2.0)
+    tps = np.array([0.5, 0.9, 1.0, 0.0, 1.5, 0.8], dtype=np.float32)
+    Ds = np.array([0.0, 0.3, 1.0, 0.2, 0.2, np.nan], dtype=np.float32)
+    args = (w.target_f32(), w.draft_f32(), w.draft_ids, w.k_per_row, w.temperature)
+    got = verify_sample_ref(*args, top_p=tps, rep_penalty=1.0, tv_budget=Ds, seed=7, offset=3)
+    for r in range(3):
+        one = verify_sample_ref(*args, top_p=float(tps[r]), rep_penalty=1.0, tv_budget=float(Ds[r]),
+                                seed=7, offset=3, rows=[r])
+        assert got.accepted[r] == one.accepted[r] and got.status[r] == one.status[r]
+        assert np.array_equal(got.tokens[r], one.tokens[r])
+        assert np.array_equal(got.stats[r], one.stats[r])
+    for r in (3, 4, 5):
+        assert got.status[r] & ST_BAD_PARAM and got.status[r] & ST_INVALID_MASK
+        assert got.accepted[r] == -1 and (got.tokens[r] == -1).all()
