@@ -95,8 +95,8 @@ def digest_pmc(fetch_csv, write_csv, copy_bytes, out_path):
     import numpy as np
     med = lambda path, ctr, k: float(np.median(read_counters(path, ctr, k)))  # noqa: E731
     cf, cw = med(fetch_csv, "FETCH_SIZE", COPY_KERNEL), med(write_csv, "WRITE_SIZE", COPY_KERNEL)
-    kf = med(fetch_csv, "FETCH_SIZE", "k_pair_fast(")
-    kw = med(write_csv, "WRITE_SIZE", "k_pair_fast(")
+    kf = med(fetch_csv, "FETCH_SIZE", "k_pair_fast")
+    kw = med(write_csv, "WRITE_SIZE", "k_pair_fast")
     sf, sw = copy_bytes / (cf * 1024.0), copy_bytes / (cw * 1024.0)
     rec = {
         "kernel": "k_pair_fast", "workload": WORKLOAD, "source_sha256": source_hash(),
