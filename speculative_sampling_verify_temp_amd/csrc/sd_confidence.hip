@@ -71,7 +71,7 @@ __global__ __launch_bounds__(NT_C) void k_draft_confidence(const char* __restric
   const __amdgpu_buffer_rsrc_t rs =
       __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(p), (short)0, nvec * 16, 0x00020000);
   float m = -INFINITY, s = 0.0f;
-  int bad = 0;
+  int nan_seen = 0;   // NaNs in groups with no other value above -inf
   for (int k0 = 0; k0 < nvec; k0 += NT_C * UC) {
     uint4 w[UC];
 #pragma unroll
@@ -86,12 +86,13 @@ __global__ __launch_bounds__(NT_C) void k_draft_confidence(const char* __restric
     for (int u = 0; u < UC; ++u) {
       Lane16<DT>::unpack(w[u], z[u]);
       const int i0 = (k0 + u * NT_C + tid) * N;
+      if (i0 + N > V) {   // the vector that holds the row end, or one past it
 #pragma unroll
-      for (int e = 0; e < N; ++e) {
-        if (i0 + e >= V) z[u][e] = -INFINITY;   // past the row (or a lane past it)
-        bad |= (z[u][e] != z[u][e]) | (z[u][e] == INFINITY);
-        gm = fmaxf(gm, z[u][e]);
+        for (int e = 0; e < N; ++e)
+          if (i0 + e >= V) z[u][e] = -INFINITY;
       }
+#pragma unroll
+      for (int e = 0; e < N; ++e) gm = fmaxf(gm, z[u][e]);
     }
     if (gm > -INFINITY) {
       const float mn = fmaxf(m, gm);
@@ -104,10 +105,19 @@ __global__ __launch_bounds__(NT_C) void k_draft_confidence(const char* __restric
         for (int e = 0; e < N; ++e) t += fast_exp2(fmaf(z[u][e], c, -g));
       s += t;
       m = mn;
+    } else {
+      // (fmaxf passes over NaN, so a group of -inf and NaN lands here)
+#pragma unroll
+      for (int u = 0; u < UC; ++u)
+#pragma unroll
+        for (int e = 0; e < N; ++e) nan_seen |= z[u][e] != z[u][e];
     }
   }
+  // A NaN logit makes the running sum NaN, a +inf one the max +inf (and its
+  // own term NaN): no per-logit test is needed.
+  const int bad = (m == INFINITY) || (s != s) || nan_seen;
   const float M = block_max<NT_C>(m, sf);
-  const double part = m > -INFINITY ? (double)s * (double)fast_exp2((m - M) * c) : 0.0;
+  const double part = (m > -INFINITY && !bad) ? (double)s * (double)fast_exp2((m - M) * c) : 0.0;
   const double Z = block_sum<NT_C>(part, sd);
   const int any_bad = block_or<NT_C>(bad, si);
   if (tid == 0) top1[row] = (any_bad || !t_ok || !(Z > 0.0)) ? __builtin_nanf("") : (float)(1.0 / Z);

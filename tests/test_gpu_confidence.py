@@ -66,6 +66,8 @@ def test_confidence_edge_rows():
     x[0, 1, 5] = np.inf
     x[1, 0, :500] = -np.inf
     x[1, 1, :] = -np.inf
+    x[1, 2, :] = -np.inf           # a NaN among masked tokens only
+    x[1, 2, 999] = np.nan
     w.draft[...] = x
     w.temperature[2] = 0.0
     w.temperature[3] = np.inf
@@ -73,7 +75,7 @@ def test_confidence_edge_rows():
     top1, K = sdv.draft_confidence(d["draft"], d["temperature"], 0.5)
     t = top1.cpu().numpy()
     assert math.isnan(t[0, 0]) and math.isnan(t[0, 1]) and not math.isnan(t[0, 2])
-    assert not math.isnan(t[1, 0]) and math.isnan(t[1, 1])
+    assert not math.isnan(t[1, 0]) and math.isnan(t[1, 1]) and math.isnan(t[1, 2])
     assert np.isnan(t[2]).all() and np.isnan(t[3]).all()
     _check(w, t, K.cpu().numpy(), 0.5)
     # no temperature: T = 1
