@@ -259,7 +259,11 @@ def verify_sample_row(tgt, drf, x, K, prior, T, top_p, r_pen, D, u, v, V,
         res.stats[j, :7] = (d, th, px, qx, pix, u[j], v[j])
         if qx == 0.0:
             res.status |= ST_Q_ZERO
-            res.accept_margin[j] = abs(pix)
+            # u * 0 < pi(x) holds iff pi(x) = (1 - theta) p(x) > 0: decided
+            # by p(x) > 0 (nucleus membership, which has its own margin) and
+            # by theta < 1, i.e. d > D.  D >= 1 always gives theta = 1 (d is
+            # at most 1), and p(x) = 0 gives pi(x) = 0 whatever theta is.
+            res.accept_margin[j] = abs(d - D) if (px > 0.0 and D < 1.0) else np.inf
         else:
             res.accept_margin[j] = abs(u[j] - pix / qx)
         if n == K and not (u[j] * qx < pix):

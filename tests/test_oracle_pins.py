@@ -405,3 +405,38 @@ def test_per_request_top_p_and_budget():
     for r in (3, 4, 5):
         assert got.status[r] & ST_BAD_PARAM and got.status[r] & ST_INVALID_MASK
         assert got.accepted[r] == -1 and (got.tokens[r] == -1).all()
+
+
+def test_q_zero_acceptance_rule_and_margin():
+    """A proposal outside the draft's nucleus (q(x) = 0): the test u q(x) <
+    pi(x) accepts iff pi(x) = (1 - theta) p(x) > 0 ("What I Gave Up...",
+    section "A knob for accepting more draft tokens").  Hand-worked: target
+    p = [.5, .3, .2] and draft q = [.1, .2, .7] as log-probabilities, T = 1,
+    top-p 0.7 keep {0, 1} (p~ = [.625, .375, 0]) and {2} (q~ = [0, 0, 1]), so
+    d = 1.  x = 0: D = 0.5 gives theta = 0.5, pi(0) = 0.3125 and acceptance
+    whatever u, with the margin |d - D| = 0.5 (the decision flips only where
+    theta reaches 1); D = 1 gives theta = 1, pi(0) = 0 and a rejection that no
+    rounding can change (margin inf).  x = 1 with p~(1) = .375 > 0 likewise;
+    for an x outside both nuclei pi(x) = 0 whatever theta (margin inf)."""
+    from oracle.verify import verify_sample_row, ST_Q_ZERO
+    lp = np.log(np.array([0.5, 0.3, 0.2])).astype(np.float32)
+    lq = np.log(np.array([0.1, 0.2, 0.7])).astype(np.float32)
+    tgt = np.stack([lp, lp])
+    for x, D, acc, margin in ((0, 0.5, 1, 0.5), (0, 1.0, 0, np.inf), (1, 0.25, 1, 0.75)):
+        for u in (0.0, 0.5, 0.999):
+            rr = verify_sample_row(tgt, lq[None], np.array([x]), 1, [], 1.0, 0.7, 1.0, D,
+                                   np.array([u, 0.3]), np.array([0.1, 0.6]), 3)
+            assert rr.status & ST_Q_ZERO
+            # (the logits are fp32 roundings of log-probabilities: 1e-7)
+            assert rr.stats[0, 0] == pytest.approx(1.0, abs=1e-7)
+            assert rr.stats[0, 2] == pytest.approx([0.625, 0.375][x], abs=1e-7)
+            assert rr.stats[0, 3] == 0.0
+            assert rr.accepted == acc
+            assert rr.accept_margin[0] == pytest.approx(margin, abs=1e-7)
+    # outside both nuclei: x = 2 has p~ = 0 and, with a draft nucleus of {1},
+    # q~ = 0 as well
+    lq2 = np.log(np.array([0.1, 0.8, 0.1])).astype(np.float32)
+    rr = verify_sample_row(tgt, lq2[None], np.array([2]), 1, [], 1.0, 0.7, 1.0, 0.5,
+                           np.array([0.0, 0.3]), np.array([0.1, 0.6]), 3)
+    assert rr.accepted == 0 and rr.stats[0, 2] == 0.0 and rr.stats[0, 3] == 0.0
+    assert rr.accept_margin[0] == np.inf
