@@ -29,7 +29,11 @@
  *    synchronously by the return code and nothing is enqueued.
  *  - Data-dependent problems are reported per request in out_status[r]
  *    (SD_ST_* bits).  A request with an SD_ST_INVALID_MASK bit set gets
- *    out_accepted[r] = -1 and every out_tokens[r][*] = -1.
+ *    out_accepted[r] = -1 and every out_tokens[r][*] = -1.  One invalidating
+ *    defect is reported per request, the first found in the order K_r, draft
+ *    ids, temperature; SD_ST_BAD_PARAM is reported beside it, SD_ST_BAD_PRIOR
+ *    always; the logits of an invalid request are not examined, so
+ *    SD_ST_NONFINITE only appears on a request that passed the other checks.
  *  - Calls that share a workspace must not overlap in time.
  *
  * Logit layout
@@ -90,8 +94,6 @@ extern "C" {
 
 /* Largest supported K_max (draft positions per request). */
 #define SD_MAX_K 32
-/* Largest supported number of prior ids per request. */
-#define SD_MAX_PRIOR 4096
 
 /* Per-position statistics written when out_stats != NULL:
  * out_stats[(r * (K_max + 1) + j) * SD_NSTAT + s] for s =                  */
@@ -123,8 +125,9 @@ typedef struct sd_verify_args {
   float          rep_penalty;    /* > 0, finite; 1 = no penalty                */
   float          tv_budget;      /* D >= 0 (greedy ignores)                    */
   const int32_t *prior_ids;      /* CSR values of prior-context ids; NULL = none */
-  const int32_t *prior_offsets;  /* [B+1] CSR offsets (row r: [off[r], off[r+1]),
-                                    at most SD_MAX_PRIOR per row)              */
+  const int32_t *prior_offsets;  /* [B+1] CSR offsets (row r: [off[r], off[r+1]));
+                                    any count per row, repeats allowed (the
+                                    set is their union)                       */
   uint64_t       seed;           /* Philox4x32-10 key (lo, hi words)           */
   uint64_t       offset;         /* Philox counter words 2-3                   */
   uint32_t       flags;          /* SD_NO_BONUS | SD_PENALTY_PRIOR_ONLY        */
@@ -171,7 +174,6 @@ int sd_verify_greedy(const sd_verify_args_t *args, void *workspace,
                      int32_t *out_tokens, uint32_t *out_status,
                      int32_t *out_argmax, void *stream);
 
-/* Human-readable text for a return code (static storage). */
 /* Draft-side confidence ("What I Gave Up to Make Speculative Decoding
  * Faster", section "Confidence-guided early stop": after each draft token
  * the probability of its most likely token is taken from the logits already
@@ -197,6 +199,7 @@ int sd_draft_confidence(const void *draft_logits, int32_t dtype, int32_t B,
                         const float *temperature, float threshold,
                         float *out_top1, int32_t *out_k, void *stream);
 
+/* Human-readable text for a return code (static storage). */
 const char *sd_strerror(int code);
 
 /* Test export: the processed, truncated, renormalized distributions of the

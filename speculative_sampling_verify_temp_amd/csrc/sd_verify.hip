@@ -138,15 +138,18 @@ __global__ __launch_bounds__(NT_ROW) void k_pair_tv(Args a, const RowStat* rs, d
 }
 
 // Request-level checks shared by the finalize kernels.  Returns status bits.
+// One invalidating defect is reported per request, the first found in this
+// order: K_r out of range, a draft id out of range, a bad temperature; a bad
+// per-request parameter is reported beside any of them, and a bad prior id
+// (which is only ignored) always.  The logits of a request with an
+// invalidating bit are never scanned, so SD_ST_NONFINITE appears only on a
+// request that passed every other check.
 template <int NT>
 __device__ uint32_t request_status(const Args& a, int r, int K, float T, bool check_temp,
                                    int* si) {
-  uint32_t st = 0;
-  if (K < 0 || K > a.K_max) st |= SD_ST_BAD_K;
-  if (check_temp && (!(T > 0.0f) || !(T < INFINITY))) st |= SD_ST_BAD_TEMP;
-  if (check_temp && !params_ok(request_top_p(a, r), request_D(a, r))) st |= SD_ST_BAD_PARAM;
+  const bool kbad = K < 0 || K > a.K_max;
   int badid = 0, badprior = 0;
-  if (!(st & SD_ST_BAD_K))
+  if (!kbad)
     for (int t = threadIdx.x; t < K; t += NT) {
       const int x = a.ids[(int64_t)r * a.K_max + t];
       badid |= (x < 0 || x >= a.V);
@@ -158,8 +161,12 @@ __device__ uint32_t request_status(const Args& a, int r, int K, float T, bool ch
       badprior |= (id < 0 || id >= a.V);
     }
   }
-  if (block_or<NT>(badid, si)) st |= SD_ST_BAD_DRAFT_ID;
-  if (block_or<NT>(badprior, si)) st |= SD_ST_BAD_PRIOR;
+  const bool idbad = block_or<NT>(badid, si) != 0;
+  const bool priorbad = block_or<NT>(badprior, si) != 0;
+  uint32_t st = kbad ? SD_ST_BAD_K : idbad ? SD_ST_BAD_DRAFT_ID : 0u;
+  if (check_temp && st == 0u && (!(T > 0.0f) || !(T < INFINITY))) st |= SD_ST_BAD_TEMP;
+  if (check_temp && !params_ok(request_top_p(a, r), request_D(a, r))) st |= SD_ST_BAD_PARAM;
+  if (priorbad) st |= SD_ST_BAD_PRIOR;
   return st;
 }
 
@@ -185,7 +192,7 @@ __global__ __launch_bounds__(NT_ROW) void k_finalize(Args a, const RowStat* rs, 
   const float T = request_t(a, r);
   uint32_t st = request_status<NT>(a, r, K, T, true, si);
   int nonfin = 0;
-  if (!(st & (SD_ST_BAD_K | SD_ST_BAD_TEMP)))
+  if (!(st & SD_ST_INVALID_MASK))
     for (int t = threadIdx.x; t < 2 * K + 1; t += NT) {
       const bool tg = t <= K;
       nonfin |= (rs[row_index(a, r, tg, tg ? t : t - K - 1)].flags & NONFINITE) ? 1 : 0;
@@ -1814,7 +1821,9 @@ __global__ __launch_bounds__(64) void k_fast_finalize(Args a, const UnitOut* uo,
   uint32_t st = request_status<NT>(a, r, K, T, true, si);
   const int64_t bonus_idx = (int64_t)a.B * a.K_max + r;
   int nonfin = 0;
-  if (!(st & (SD_ST_BAD_K | SD_ST_BAD_TEMP))) {
+  // (units of a request with an invalidating bit may hold no record of this
+  // call: k_pair_fast skips requests with a bad K, temperature or parameter)
+  if (!(st & SD_ST_INVALID_MASK)) {
     for (int t = threadIdx.x; t < K; t += NT)
       nonfin |= (uo[(int64_t)r * a.K_max + t].flags & UO_NONFINITE) ? 1 : 0;
     if (threadIdx.x == 0) nonfin |= (uo[bonus_idx].flags & UO_NONFINITE) ? 1 : 0;
@@ -1995,7 +2004,7 @@ __global__ __launch_bounds__(64) void k_greedy_final(Args a, const GPart* parts,
   const int K = request_k(a, r);
   uint32_t st = request_status<NT>(a, r, K, 1.0f, false, si);
   int nan = 0;
-  if (!(st & SD_ST_BAD_K) && (int)threadIdx.x <= K) {
+  if (!(st & SD_ST_INVALID_MASK) && (int)threadIdx.x <= K) {
     const int jj = threadIdx.x;
     uint32_t bo = 0;
     int bi = INT_MAX;
@@ -2327,6 +2336,7 @@ int sd_debug_fallback_units(const sd_verify_args_t* args, const void* workspace,
   std::vector<uint32_t> flags(2 * (size_t)nunits);   // flags, why per unit
   std::vector<int32_t> ks(B, a.K_max);
   std::vector<float> ts(B, 1.0f);
+  std::vector<float> tps(B, a.top_p), ds(B, a.D);
   const char* uo = static_cast<const char*>(workspace) + L.uo;
   static_assert(offsetof(UnitOut, why) == offsetof(UnitOut, flags) + 4, "UnitOut layout");
   bool ok = hipMemcpy2DAsync(flags.data(), 2 * sizeof(uint32_t), uo + offsetof(UnitOut, flags),
@@ -2336,6 +2346,10 @@ int sd_debug_fallback_units(const sd_verify_args_t* args, const void* workspace,
     ok = hipMemcpyAsync(ks.data(), a.kpr, B * sizeof(int32_t), hipMemcpyDeviceToHost, st) == hipSuccess;
   if (ok && a.temp)
     ok = hipMemcpyAsync(ts.data(), a.temp, B * sizeof(float), hipMemcpyDeviceToHost, st) == hipSuccess;
+  if (ok && a.tpr)
+    ok = hipMemcpyAsync(tps.data(), a.tpr, B * sizeof(float), hipMemcpyDeviceToHost, st) == hipSuccess;
+  if (ok && a.dpr)
+    ok = hipMemcpyAsync(ds.data(), a.dpr, B * sizeof(float), hipMemcpyDeviceToHost, st) == hipSuccess;
   if (!ok || hipStreamSynchronize(st) != hipSuccess) return SD_EHIP;
   // Units the kernel skips (invalid request, position beyond K_r) hold no record.
   int n = 0;
@@ -2347,6 +2361,7 @@ int sd_debug_fallback_units(const sd_verify_args_t* args, const void* workspace,
     const int K = ks[r];
     const float T = ts[r];
     if (K < 0 || K > a.K_max || (!bonus && j >= K) || !(T > 0.0f) || !(T < INFINITY)) continue;
+    if (!(tps[r] > 0.0f && tps[r] <= 1.0f) || !(ds[r] >= 0.0f)) continue;   // as params_ok
     if (flags[2 * u] & UO_FALLBACK) {
       ++n;
       if (out_why) out_why[u] = flags[2 * u + 1];

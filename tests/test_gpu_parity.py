@@ -170,9 +170,9 @@ def test_sample_sweep(i):
         tot_c += c
         tot_f += f
     print(f"sweep {i}: checked {tot_c} rows, near-tie rows {tot_f}")
-    # A deep top-p cut (0.99 over a flat tail) puts cumulative masses within
-    # 1e-6 of top_p in most rows: those rows are counted, not compared.
-    assert tot_c >= 1
+    # near-ties that can change a row's output are rare (the oracle flags at
+    # most 1 of 12..18 rows per case here): nearly every row is compared
+    assert tot_c >= 0.9 * (tot_c + tot_f)
 
 
 def test_sample_edge_cases():
@@ -215,7 +215,7 @@ def test_config2_calls():
             tot[0] += c
             tot[1] += f
     print(f"config2: checked {tot[0]}, near-tie {tot[1]}")
-    assert tot[0] > 0
+    assert tot[0] >= 0.9 * (tot[0] + tot[1])
 
 
 @pytest.fixture(scope="module")
@@ -223,32 +223,92 @@ def cfg4():
     return wl.config4()
 
 
-def test_config4_full_size_sampled_rows(cfg4):
-    w = cfg4
-    g = gpu_sample(w)
-    rows = [0, 1, 2, 37, 64, 100, 128, 171, 200, 229, 254, 255]
-    o = oracle_sample(w, rows=rows)
-    c, f = compare_sample(g, o, w, rows=rows)
-    print(f"config4: checked {c}, near-tie {f}; mean accepted {g['accepted'].mean():.3f}")
-    assert c >= len(rows) // 2
-    # properties that hold for every row
-    assert (g["status"] & 0xF).sum() == 0
-    assert ((g["accepted"] >= 0) & (g["accepted"] <= 8)).all()
+@pytest.fixture(scope="module")
+def cfg4_odd():
+    return wl.config4(odd_share=0.15)
+
+
+def _full_size_properties(g, w):
+    """Properties every valid row of a full-size call must have."""
+    assert ((g["accepted"] >= 0) & (g["accepted"] <= w.k_per_row)).all()
     for r in range(w.B):
         n = g["accepted"][r]
         assert np.array_equal(g["tokens"][r, :n], w.draft_ids[r, :n])
         assert 0 <= g["tokens"][r, n] < w.V
 
 
-@pytest.mark.parametrize("forced", [False, True])
-def test_config5_full_size_sampled_rows(forced):
-    w = wl.config5(forced_ragged=forced)
+def test_config4_full_size_sampled_rows(cfg4):
+    """The measured workload at full size: every row the GPU rejects among the
+    first 96 plus every 8th row, compared with the oracle."""
+    w = cfg4
     g = gpu_sample(w)
-    rows = list(range(0, w.B, 16))
+    rej = [r for r in range(96) if g["accepted"][r] < w.k_per_row[r]]
+    rows = sorted(set(rej) | set(range(0, w.B, 8)))
     o = oracle_sample(w, rows=rows)
     c, f = compare_sample(g, o, w, rows=rows)
-    print(f"config5 forced={forced}: K hist {np.bincount(w.k_per_row)}, checked {c}, near-tie {f}")
-    assert c >= len(rows) // 2
+    print(f"config4: compared {len(rows)} rows ({len(rej)} rejecting), checked {c}, "
+          f"near-tie {f}; mean accepted {g['accepted'].mean():.3f}")
+    assert len(rows) >= 64 and c >= 0.9 * len(rows)
+    assert (g["status"] & 0x8F).sum() == 0
+    _full_size_properties(g, w)
+
+
+@pytest.mark.parametrize("D", [0.75, 0.0])
+def test_config4_full_size_odd_proposals(cfg4_odd, D):
+    """Full-size single-pass calls whose proposals include ids drawn uniformly
+    from [0, V) and from the prior ids (15% of positions): q(x) = 0, p(x) = 0
+    and penalized proposals, and at D = 0 (lossless) a rejection in nearly
+    every row, so the full-vocabulary correction draw is compared row by row."""
+    w = cfg4_odd.with_(tv_budget=D)
+    g = gpu_sample(w)
+    rows = list(range(80))
+    o = oracle_sample(w, rows=rows)
+    c, f = compare_sample(g, o, w, rows=rows)
+    rej = sum(int(o.accepted[r] < w.k_per_row[r]) for r in rows)
+    # decided positions (j <= n) whose proposal falls in each branch
+    qz = pz = pen = 0
+    for r in rows:
+        n = int(o.accepted[r])
+        prior = set(w.prior_ids[w.prior_offsets[r]:w.prior_offsets[r + 1]].tolist())
+        for j in range(min(n + 1, w.K_max)):
+            x = int(w.draft_ids[r, j])
+            qz += o.stats[r, j, 3] == 0.0
+            pz += o.stats[r, j, 2] == 0.0
+            pen += x in prior or x in set(w.draft_ids[r, :j].tolist())
+    print(f"config4 odd D={D}: checked {c}, near-tie {f}, rejecting rows {rej}; decided "
+          f"positions with q(x)=0 {qz}, p(x)=0 {pz}, penalized x {pen}")
+    assert c >= 0.9 * len(rows)
+    assert rej >= (64 if D == 0.0 else 40)
+    assert qz >= 10 and pz >= 10 and pen >= 3
+    assert (g["status"] & 0x8F).sum() == 0
+    _full_size_properties(g, w)
+
+
+@pytest.mark.parametrize("forced", [False, True])
+def test_config5_full_size_sampled_rows(forced):
+    """Config 5 at full size.  Under its statistics (N(0, 3^2) logits, T = 0.7)
+    the draft's top-1 probability is already below 0.6 at the first position
+    in most rows, so the early-stop rule gives K_r = 1 to 474 of the 512 rows
+    (the oracle's own rule reproduces the workload's K exactly); the forced
+    variant (K_r ~ U{1..8}) carries the ragged coverage."""
+    from oracle import draft_confidence_ref
+    w = wl.config5(forced_ragged=forced)
+    hist = np.bincount(w.k_per_row, minlength=9)
+    if not forced:
+        _, k_rule = draft_confidence_ref(w.draft_f32(), w.temperature, 0.6)
+        assert np.array_equal(w.k_per_row, k_rule)
+        assert hist[1] == 474 and hist[1:].sum() == w.B
+    else:
+        assert (hist[1:] > 0).all()
+    g = gpu_sample(w)
+    rows = list(range(0, w.B, 4))
+    o = oracle_sample(w, rows=rows)
+    c, f = compare_sample(g, o, w, rows=rows)
+    rej = sum(int(o.accepted[r] < w.k_per_row[r]) for r in rows)
+    print(f"config5 forced={forced}: K hist {hist.tolist()}, compared {len(rows)}, checked {c}, "
+          f"near-tie {f}, rejecting {rej}")
+    assert c >= 0.9 * len(rows)
+    _full_size_properties(g, w)
 
 
 def test_repeat_runs_identical():

@@ -32,9 +32,12 @@ through Qwen models, which are not available; logits are synthetic):
 sigma as the target.  N(0, s) means standard deviation s.
 
 Draft ids are proposals from the draft model's sampler: Gumbel-max over the
-raw draft logits divided by T (an exact sample of softmax(z/T)); when top-p is
-on the proposal is restricted to the row's 4 largest raw logits so that it
-lands inside the nucleus.
+whole raw draft row divided by T (an exact sample of softmax(z/T)).  Nothing
+restricts them to the nucleus: with top-p on, some land outside the draft's
+(q(x) = 0) or the target's (p(x) = 0) nucleus.  Workloads built for parity
+also replace a seeded share of the proposals (`odd_share`) by an id drawn
+uniformly from [0, V) or from the request's prior ids (a penalized token), so
+that those branches of the step are exercised on purpose.
 """
 
 from dataclasses import dataclass, replace
@@ -117,16 +120,28 @@ def _load(x, dtype):
     return x if dtype == "f32" else bf16_bits_to_f32(x)
 
 
-def gumbel_proposal(rng, z, T, topk=None):
-    """Draft proposal: Gumbel-max over z/T (an exact sample of softmax(z/T)),
-    optionally restricted to the topk largest raw logits."""
+def gumbel_proposal(rng, z, T):
+    """Draft proposal: Gumbel-max over the whole row z/T (an exact sample of
+    softmax(z/T))."""
     z = np.asarray(z, dtype=np.float64)
-    if topk is None:
-        g = rng.gumbel(size=z.size)
-        return int(np.argmax(z / T + g))
-    cand = np.argpartition(-z, topk - 1)[:topk]
-    g = rng.gumbel(size=cand.size)
-    return int(cand[np.argmax(z[cand] / T + g)])
+    g = rng.gumbel(size=z.size)
+    return int(np.argmax(z / T + g))
+
+
+def propose(rng, z, T, odd_share=0.0, prior=None):
+    """One draft id: with probability odd_share an odd proposal (half of them
+    uniform over [0, V), half a uniformly chosen prior id when the request has
+    prior ids), else gumbel_proposal.  The draws come from rng in a fixed
+    order, so a workload is a function of its seed."""
+    V = np.asarray(z).size
+    a, b = rng.random(), rng.random()
+    x = gumbel_proposal(rng, z, T)
+    if a < odd_share:
+        if b < 0.5 and prior is not None and len(prior):
+            x = int(prior[rng.integers(0, len(prior))])
+        else:
+            x = int(rng.integers(0, V))
+    return x
 
 
 def _prior(rng, B, n, V, pool=None):
@@ -198,7 +213,7 @@ def config3(K=8, call=0, B=1, V=V_QWEN3):
                     np.full(B, K, dtype=np.int32), np.ones(B, np.float32))
 
 
-def config4_row(seed, r, K=8, V=V_QWEN25, n_prior=128):
+def config4_row(seed, r, K=8, V=V_QWEN25, n_prior=128, odd_share=0.0):
     """One request row of config 4, from its own generator stream."""
     rng = np.random.default_rng([4, seed, r])
     T = np.float32(rng.uniform(0.5, 1.0))
@@ -206,21 +221,23 @@ def config4_row(seed, r, K=8, V=V_QWEN25, n_prior=128):
     dr = _corr_rows(rng, t[:K], 0.9, 3.0).astype(np.float32)
     tb, db = f32_to_bf16_bits(t), f32_to_bf16_bits(dr)
     dl = bf16_bits_to_f32(db)
-    ids = np.array([gumbel_proposal(rng, dl[j], T, topk=4) for j in range(K)],
-                   dtype=np.int32)
     prior = rng.integers(0, V, size=n_prior).astype(np.int32)
+    ids = np.array([propose(rng, dl[j], T, odd_share, prior) for j in range(K)],
+                   dtype=np.int32)
     return tb, db, ids, T, prior
 
 
 def config4(seed=0, B=256, K=8, V=V_QWEN25, n_prior=128, D=0.75,
-            philox_seed=0, top_p=0.9, rep_penalty=1.1):
+            philox_seed=0, top_p=0.9, rep_penalty=1.1, odd_share=0.0):
+    """The batched workload.  Proposals come from the draft's own sampler
+    (odd_share = 0, the measured workload); parity runs add odd proposals."""
     tb = np.empty((B, K + 1, V), dtype=np.uint16)
     db = np.empty((B, K, V), dtype=np.uint16)
     ids = np.empty((B, K), dtype=np.int32)
     T = np.empty(B, dtype=np.float32)
     prior = np.empty((B, n_prior), dtype=np.int32)
     for r in range(B):
-        tb[r], db[r], ids[r], T[r], prior[r] = config4_row(seed, r, K, V, n_prior)
+        tb[r], db[r], ids[r], T[r], prior[r] = config4_row(seed, r, K, V, n_prior, odd_share)
     offs = (np.arange(B + 1, dtype=np.int64) * n_prior).astype(np.int32)
     return Workload("config4", "bf16", tb, db, ids,
                     np.full(B, K, dtype=np.int32), T, top_p=top_p,
@@ -228,9 +245,12 @@ def config4(seed=0, B=256, K=8, V=V_QWEN25, n_prior=128, D=0.75,
                     prior_offsets=offs, tv_budget=D, seed=philox_seed)
 
 
-def top1_prob(z, T):
-    """Draft-side confidence of one row: the largest probability of
-    softmax(z/T) (early-stop rule input, computed by the draft sampler)."""
+def _draft_confidence(z, T):
+    """The draft sampler's own confidence in a row (the largest probability
+    of softmax(z/T)), used only to pick config 5's K_r as the early-stop rule
+    would.  Nothing compares against it: the verify step never computes it,
+    and the draft-side confidence kernel is checked against the oracle's
+    own routine, not this one."""
     a = np.asarray(z, dtype=np.float64) / T
     return 1.0 / np.exp(a - a.max()).sum()
 
@@ -258,7 +278,7 @@ def config5(seed=0, B=512, K_max=8, V=V_QWEN3, T=0.7, threshold=0.6,
         else:
             k = K_max
             for j in range(K_max):
-                if top1_prob(dl[j], T) < threshold:
+                if _draft_confidence(dl[j], T) < threshold:
                     k = j + 1
                     break
         ks[r] = k
@@ -270,7 +290,8 @@ def config5(seed=0, B=512, K_max=8, V=V_QWEN3, T=0.7, threshold=0.6,
 
 def random_case(seed, B=3, K_max=3, V=300, dtype="f32", sigma=2.0, corr=0.8,
                 T_range=(0.5, 1.5), top_p=1.0, rep_penalty=1.0, n_prior=0,
-                D=0.0, ragged=False, philox_seed=None, flags=0, prior_pool=None):
+                D=0.0, ragged=False, philox_seed=None, flags=0, prior_pool=None,
+                odd_share=0.1):
     """Small generic case for parity sweeps (rows span several tiles when V
     is a few thousand, with a ragged tail when V is not a tile multiple)."""
     rng = np.random.default_rng([9, seed])
@@ -279,14 +300,14 @@ def random_case(seed, B=3, K_max=3, V=300, dtype="f32", sigma=2.0, corr=0.8,
     tt, dd = _store(t, dtype), _store(dr, dtype)
     dl = _load(dd, dtype)
     T = rng.uniform(*T_range, size=B).astype(np.float32)
-    topk = 4 if top_p < 1.0 else None
-    ids = np.array([[gumbel_proposal(rng, dl[r, j], T[r], topk)
-                     for j in range(K_max)] for r in range(B)], dtype=np.int32)
-    ks = (rng.integers(0, K_max + 1, size=B) if ragged
-          else np.full(B, K_max)).astype(np.int32)
     pid = poff = None
     if n_prior:
         pid, poff = _prior(rng, B, n_prior, V, prior_pool)
+    ids = np.array([[propose(rng, dl[r, j], T[r], odd_share,
+                             None if pid is None else pid[poff[r]:poff[r + 1]])
+                     for j in range(K_max)] for r in range(B)], dtype=np.int32)
+    ks = (rng.integers(0, K_max + 1, size=B) if ragged
+          else np.full(B, K_max)).astype(np.int32)
     return Workload("random", dtype, tt, dd, ids, ks, T, top_p=top_p,
                     rep_penalty=rep_penalty, prior_ids=pid, prior_offsets=poff,
                     tv_budget=D, seed=seed if philox_seed is None else philox_seed,
