@@ -62,6 +62,8 @@ extern "C" {
 #define SD_EWORKSPACE   (-2)  /* workspace NULL or smaller than required      */
 #define SD_EHIP         (-3)  /* a HIP runtime call failed (launch, query)    */
 #define SD_EUNSUPPORTED (-4)  /* valid request outside this build's limits    */
+#define SD_ESCRATCH     (-5)  /* sd_verify_sample_noalloc: the call needs more
+                                 workspace than SD_NOALLOC_MAX_WORKSPACE       */
 
 /* Element types of the logit rows. */
 #define SD_F32  0
@@ -161,6 +163,23 @@ int sd_verify_sample(const sd_verify_args_t *args, void *workspace,
                      size_t workspace_bytes, int32_t *out_accepted,
                      int32_t *out_tokens, uint32_t *out_status,
                      float *out_stats, void *stream);
+
+/* Sampling verify that allocates nothing and takes no workspace, for callers
+ * that cannot allocate device memory (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc).  Same arguments, outputs,
+ * errors and results as sd_verify_sample; the workspace is instead a
+ * built-in array of SD_NOALLOC_MAX_WORKSPACE bytes in the library's device
+ * code, one per GPU, held until the process ends (its address is looked up
+ * on the first call on each device, with that device current).  Calls whose
+ * sd_verify_workspace_bytes exceeds that size return SD_ESCRATCH and enqueue
+ * nothing (8 MiB covers e.g. B = 2048 requests at K_max = 8 and V = 152064).
+ * Every call on one GPU shares that GPU's array: calls that overlap in time
+ * on one GPU (two streams, two host threads) race and must be serialized by
+ * the caller.  No part of the array needs clearing between calls. */
+#define SD_NOALLOC_MAX_WORKSPACE (8u << 20)
+int sd_verify_sample_noalloc(const sd_verify_args_t *args, int32_t *out_accepted,
+                             int32_t *out_tokens, uint32_t *out_status,
+                             float *out_stats, void *stream);
 
 /* Greedy verify (Adaptive-SpecDecode-Lab README, implementation section):
  * g_j = argmax of the penalized target row j (lowest id among equal maxima;

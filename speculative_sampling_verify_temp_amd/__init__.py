@@ -7,6 +7,8 @@ is no fallback: if the library is missing, importing this package raises.
 
 Functions mirror the C entry points:
     verify_sample(...)   -> sd_verify_sample
+    verify_sample_noalloc(...) -> sd_verify_sample_noalloc (outputs preallocated
+                            by the caller, no workspace)
     verify_greedy(...)   -> sd_verify_greedy
     workspace_bytes(...) -> sd_verify_workspace_bytes
     strerror(code)       -> sd_strerror
@@ -18,7 +20,8 @@ import os
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libsdverify.so")
 
-SD_OK, SD_EINVAL, SD_EWORKSPACE, SD_EHIP, SD_EUNSUPPORTED = 0, -1, -2, -3, -4
+SD_OK, SD_EINVAL, SD_EWORKSPACE, SD_EHIP, SD_EUNSUPPORTED, SD_ESCRATCH = 0, -1, -2, -3, -4, -5
+SD_NOALLOC_MAX_WORKSPACE = 8 << 20
 SD_F32, SD_BF16 = 0, 1
 SD_NO_BONUS, SD_PENALTY_PRIOR_ONLY = 1, 2
 SD_ST_BAD_K, SD_ST_BAD_TEMP, SD_ST_BAD_DRAFT_ID, SD_ST_NONFINITE = 1, 2, 4, 8
@@ -75,6 +78,8 @@ def _load():
     lib.sd_verify_workspace_bytes.restype = ctypes.c_int
     lib.sd_verify_sample.argtypes = [A, P, SZ, P, P, P, P, P]
     lib.sd_verify_sample.restype = ctypes.c_int
+    lib.sd_verify_sample_noalloc.argtypes = [A, P, P, P, P, P]
+    lib.sd_verify_sample_noalloc.restype = ctypes.c_int
     lib.sd_verify_greedy.argtypes = [A, P, SZ, P, P, P, P, P]
     lib.sd_verify_greedy.restype = ctypes.c_int
     lib.sd_strerror.argtypes = [ctypes.c_int]
@@ -207,6 +212,16 @@ def verify_sample(target, draft, draft_ids, k_per_row=None, temperature=None, to
     if rc != SD_OK:
         raise SdVerifyError(rc, "sd_verify_sample")
     return acc, tok, st, sts
+
+
+def verify_sample_noalloc(args, accepted, tokens, status=None, stats=None, stream=None):
+    """sd_verify_sample_noalloc on a filled argument struct (make_args) and
+    caller-allocated outputs: nothing is allocated, by this function or the
+    library."""
+    rc = lib.sd_verify_sample_noalloc(ctypes.byref(args), _ptr(accepted), _ptr(tokens),
+                                      _ptr(status), _ptr(stats), _stream(stream))
+    if rc != SD_OK:
+        raise SdVerifyError(rc, "sd_verify_sample_noalloc")
 
 
 def verify_greedy(target, draft_ids, k_per_row=None, rep_penalty=1.0, prior_ids=None,

@@ -28,6 +28,7 @@
 #include <math.h>
 #include <string.h>
 #include <stddef.h>
+#include <mutex>
 #include <utility>
 #include <vector>
 
@@ -2217,6 +2218,33 @@ int run_greedy(const Args& a, const Layout& L, char* ws, int32_t* acc, int32_t* 
 
 }  // namespace
 
+// Built-in workspace of sd_verify_sample_noalloc: one array per GPU, held
+// until the process ends.  In host code `scratch` names a host-side stand-in,
+// not device memory: its device address comes from hipGetSymbolAddress, once
+// per device with that device current, and only that address is used.
+static __device__ __align__(256) unsigned char scratch[SD_NOALLOC_MAX_WORKSPACE];
+
+namespace {
+constexpr int MAX_DEVICES = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[MAX_DEVICES];   // device address of `scratch`, per device
+
+// Device address of the current device's scratch array (looked up on the
+// first call on that device).
+int scratch_address(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= MAX_DEVICES) return SD_EHIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return SD_EHIP;
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return SD_OK;
+}
+}  // namespace
+
 extern "C" {
 
 int sd_verify_workspace_bytes(const sd_verify_args_t* args, size_t* bytes) {
@@ -2257,6 +2285,22 @@ int sd_verify_greedy(const sd_verify_args_t* args, void* workspace, size_t works
                             : run_greedy<SD_F32>(a, L, ws, out_accepted, out_tokens, out_status, out_argmax, st);
 }
 
+int sd_verify_sample_noalloc(const sd_verify_args_t* args, int32_t* out_accepted,
+                             int32_t* out_tokens, uint32_t* out_status, float* out_stats,
+                             void* stream) {
+  int rc = check_common(args, true);
+  if (rc) return rc;
+  if (!out_accepted || !out_tokens) return SD_EINVAL;
+  if (layout(args).total > SD_NOALLOC_MAX_WORKSPACE) return SD_ESCRATCH;
+  void* ws = nullptr;
+  rc = scratch_address(&ws);
+  if (rc) return rc;
+  // Nothing in the workspace needs to start at zero: every record a kernel
+  // reads is written earlier in the same call.
+  return sd_verify_sample(args, ws, SD_NOALLOC_MAX_WORKSPACE, out_accepted, out_tokens,
+                          out_status, out_stats, stream);
+}
+
 const char* sd_strerror(int code) {
   switch (code) {
     case SD_OK: return "ok";
@@ -2264,6 +2308,7 @@ const char* sd_strerror(int code) {
     case SD_EWORKSPACE: return "workspace missing or too small";
     case SD_EHIP: return "HIP runtime error";
     case SD_EUNSUPPORTED: return "unsupported size (K_max or V beyond this build's limits)";
+    case SD_ESCRATCH: return "call needs more workspace than the built-in scratch array holds";
     default: return "unknown error code";
   }
 }

@@ -150,3 +150,21 @@ def test_args_struct_matches_the_header():
     assert names[-2:] == ["top_p_per_row", "tv_budget_per_row"]
     assert A.tv_budget_per_row.offset == A.top_p_per_row.offset + 8
     assert ctypes.sizeof(A) == A.tv_budget_per_row.offset + 8
+
+
+def test_noalloc_rejects_on_host_before_touching_the_device():
+    """sd_verify_sample_noalloc checks its arguments, then whether the call
+    fits the built-in scratch array (SD_ESCRATCH), before it looks up the
+    array or enqueues anything."""
+    import speculative_sampling_verify_temp_amd as sdv
+    f = sdv.lib.sd_verify_sample_noalloc
+    out = ctypes.c_void_p(0x400000)
+    a = _good_args(sdv)
+    a.B = 0
+    assert f(ctypes.byref(a), out, out, None, None, None) == sdv.SD_EINVAL
+    a = _good_args(sdv)
+    assert f(ctypes.byref(a), None, out, None, None, None) == sdv.SD_EINVAL
+    a.B = 100000   # about 40 MiB of workspace
+    assert sdv.workspace_bytes(a) > sdv.SD_NOALLOC_MAX_WORKSPACE
+    assert f(ctypes.byref(a), out, out, None, None, None) == sdv.SD_ESCRATCH
+    assert "scratch" in sdv.strerror(sdv.SD_ESCRATCH)
