@@ -27,7 +27,7 @@ from .verify import (
     ST_BAD_K, ST_BAD_TEMP, ST_BAD_DRAFT_ID, ST_NONFINITE, ST_BAD_PRIOR,
     ST_Q_ZERO, ST_RESID_ZERO, ST_BAD_PARAM, ST_INVALID_MASK, FLAG_NO_BONUS,
     FLAG_PENALTY_PRIOR_ONLY, penalty_keys, softmax64, top_p_filter,
-    process_dist, tv_distance, mentored_theta, inverse_cdf, verify_sample_ref,
+    process_dist, draft_row_over_target, tv_distance, mentored_theta, inverse_cdf, verify_sample_ref,
     verify_greedy_ref, SampleResult, GreedyResult,
 )
 from .confidence import top1_prob, draft_lengths, draft_confidence_ref

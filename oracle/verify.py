@@ -157,6 +157,25 @@ def process_dist(z, pen_ids, r, temperature, top_p):
     return Dist(keys, pt, margin)
 
 
+def draft_row_over_target(z, V):
+    """A draft logit row over the target's vocabulary.
+
+    [ASL] implementation section: the draft and target tokenizers are fully
+    mapped, while the two models' logit rows need not have the same length
+    (the pages' Qwen2.5 7B / 0.5B pair pads its vocabularies to 152064 and
+    151936).  Reading: the draft's row covers token ids 0..V_d-1 and every id
+    from V_d to V-1 is a token the draft cannot propose, logit -inf, q = 0.
+    Returns the row padded to V entries (a copy only when V_d < V).
+    """
+    z = np.asarray(z, dtype=np.float32)
+    if z.shape[-1] == V:
+        return z
+    if z.shape[-1] > V:
+        raise ValueError("a draft row longer than the target's vocabulary")
+    pad = np.full(z.shape[:-1] + (V - z.shape[-1],), -np.inf, dtype=np.float32)
+    return np.concatenate([z, pad], axis=-1)
+
+
 def tv_distance(p, q):
     """d = TV(p, q) = 1/2 sum_x |p(x) - q(x)|  ([WGU] "A knob...", eq. for d).
 
@@ -227,6 +246,7 @@ def verify_sample_row(tgt, drf, x, K, prior, T, top_p, r_pen, D, u, v, V,
       n = K: bonus from p_K with v_K (unless NO_BONUS).
     """
     res = RowResult()
+    drf = draft_row_over_target(drf, V)   # a shorter draft vocabulary: q = 0 beyond it
     res.stats = np.zeros((K + 1, NSTAT))
     res.accept_margin = np.full(K, np.inf)
     res.topp_margin_p = np.full(K + 1, np.inf)
@@ -322,7 +342,8 @@ def verify_sample_ref(target, draft, draft_ids, k_per_row=None,
                       seed=0, offset=0, flags=0, rows=None):
     """Batched sampling verify, row by row.
 
-    target: fp32 [B][K_max+1][V]; draft: fp32 [B][K_max][V];
+    target: fp32 [B][K_max+1][V]; draft: fp32 [B][K_max][V_d] with V_d <= V
+    (tokens V_d..V-1 have q = 0, see draft_row_over_target);
     draft_ids: int [B][K_max]; k_per_row: int [B] or None (= K_max);
     temperature: fp32 [B] or None (= 1); prior CSR or None.
     top_p, tv_budget: a scalar for every request, or an array [B] of

@@ -9,7 +9,7 @@ arithmetic.
 """
 import numpy as np
 
-from oracle.verify import verify_sample_row, process_dist
+from oracle.verify import verify_sample_row, process_dist, draft_row_over_target
 
 GRID = 1 << 24
 
@@ -27,7 +27,8 @@ def _first_true(pred, lo=0, hi=GRID):
 
 
 class RowModel:
-    """A one-row problem: target rows [K+1][V], draft rows [K][V] (fp32)."""
+    """A one-row problem: target rows [K+1][V], draft rows [K][V_d] (fp32,
+    V_d <= V: the draft's tail tokens have q = 0)."""
 
     def __init__(self, tgt, drf, prior=(), T=1.0, top_p=1.0, r_pen=1.0, D=0.0,
                  flags=0):
@@ -47,7 +48,8 @@ class RowModel:
         """The proposal law at position j given the accepted prefix: the
         oracle's processed draft distribution."""
         pen = list(self.prior) if (self.flags & 2) else list(self.prior) + list(prefix)
-        return process_dist(self.drf[j], pen, self.r_pen, self.T, self.top_p).p
+        return process_dist(draft_row_over_target(self.drf[j], self.V), pen, self.r_pen,
+                            self.T, self.top_p).p
 
     def law(self):
         """dict: tuple(emitted tokens) -> probability, with x_j ~ q_j."""

@@ -440,3 +440,63 @@ def test_q_zero_acceptance_rule_and_margin():
                            np.array([0.0, 0.3]), np.array([0.1, 0.6]), 3)
     assert rr.accepted == 0 and rr.stats[0, 2] == 0.0 and rr.stats[0, 3] == 0.0
     assert rr.accept_margin[0] == np.inf
+
+
+# --- a draft vocabulary shorter than the target's (Adaptive-SpecDecode-Lab
+#     README, implementation section: fully mapped tokenizers; the draft's
+#     logit row covers ids 0..V_d-1 only)
+
+def _softmax_T(z, T):
+    e = np.exp((np.asarray(z, np.float64) - np.max(z)) / T)
+    return e / e.sum()
+
+
+@pytest.mark.parametrize("D", [0.0, 0.2, 1.0])
+def test_short_draft_vocabulary_law(D):
+    """V = 5 target tokens, V_d = 3 draft tokens.  The enumerated law of the
+    first emitted token is pi = (1 - theta) p + theta q with q extended by
+    zeros over ids 3 and 4 (p and q by textbook softmax here, d = TV(p, q)):
+    the tail tokens are only ever emitted as corrections, with mass
+    (1 - theta) p(i), and P(reject) = (1 - theta) d."""
+    tgt = np.array([[0.5, 1.0, -0.5, 1.5, 0.25], [0.0, 0.3, 1.2, -1.0, 0.6]], np.float32)
+    drf = np.array([[1.0, 0.75, 0.1]], np.float32)
+    T = 0.9
+    p = _softmax_T(tgt[0], T)
+    q = np.concatenate([_softmax_T(drf[0], T), [0.0, 0.0]])
+    d = 0.5 * np.abs(p - q).sum()
+    th = 1.0 if d <= D else D / d
+    pi = (1 - th) * p + th * q
+    law = RowModel(tgt, drf, T=T, D=D).law()
+    first, _ = marginal(law, 0)
+    np.testing.assert_allclose([first.get(i, 0) for i in range(5)], pi, atol=2e-6)
+    p_rej = sum(pr for s, pr in law.items() if len(s) == 1)
+    assert abs(p_rej - (1 - th) * d) < 2e-6
+    if D < 1.0:
+        assert first.get(3, 0) > 0.05 and first.get(4, 0) > 0.02
+
+
+def test_short_draft_vocabulary_rows_and_proposals():
+    """The oracle's processed draft row over the target's ids has q = 0 past
+    V_d, with and without top-p and a penalty on a tail id; a proposal in the
+    tail is a q(x) = 0 proposal (status bit, accepted iff pi(x) > 0), while an
+    id beyond V is a bad draft id."""
+    z = np.array([2.0, 0.5, 1.0, -1.0], np.float32)
+    full = ov.draft_row_over_target(z, 7)
+    assert full.shape == (7,) and np.isneginf(full[4:]).all() and np.array_equal(full[:4], z)
+    for top_p in (1.0, 0.8):
+        dq = ov.process_dist(full, [5, 1], 1.3, 0.7, top_p)
+        assert (dq.p[4:] == 0).all() and abs(dq.p.sum() - 1.0) < 1e-12
+        ref = _softmax_T(ov.penalty_keys(z, [1], 1.3), float(np.float32(0.7)))   # T as fp32
+        if top_p == 1.0:
+            np.testing.assert_allclose(dq.p[:4], ref, rtol=1e-12)
+    tgt = np.array([[0.1, 0.2, 0.3, 0.4, 0.5, 2.5, 0.0]] * 2, np.float32)
+    for D, acc in ((0.0, 1), (1.0, 0)):
+        rr = ov.verify_sample_row(tgt, z[None], np.array([5]), 1, [], 1.0, 1.0, 1.0, D,
+                                  np.array([0.99, 0.5]), np.array([0.5, 0.5]), 7)
+        assert rr.status & ov.ST_Q_ZERO and rr.stats[0, 3] == 0.0 and rr.stats[0, 2] > 0
+        assert rr.accepted == acc
+    w = random_case(5, B=2, K_max=2, V=9)
+    res = ov.verify_sample_ref(w.target_f32(), w.draft_f32()[:, :, :6],
+                               np.array([[8, 1], [9, 0]], np.int32), tv_budget=0.3)
+    assert res.status[0] & ov.ST_Q_ZERO and not res.status[0] & ov.ST_BAD_DRAFT_ID
+    assert res.status[1] == ov.ST_BAD_DRAFT_ID
