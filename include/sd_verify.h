@@ -40,7 +40,7 @@
  * ------------
  *  target row (r, j), 0 <= j <= K_max: element i at
  *      target_logits + ((int64)r * (K_max + 1) + j) * ld_target + i
- *  draft row (r, j), 0 <= j < K_max: element i at
+ *  draft row (r, j), 0 <= j < K_max: element i (i < V_draft) at
  *      draft_logits + ((int64)r * K_max + j) * ld_draft + i
  *  Element type is fp32 (SD_F32) or bf16 (SD_BF16, raw 16-bit patterns).
  *  Rows must be 16-byte aligned (ld * element size a multiple of 16 and the
@@ -139,6 +139,14 @@ typedef struct sd_verify_args {
    * is out of range gets SD_ST_BAD_PARAM.  Greedy ignores both. */
   const float   *top_p_per_row;
   const float   *tv_budget_per_row;
+  /* Draft vocabulary (Adaptive-SpecDecode-Lab README, implementation
+   * section: the two tokenizers are fully mapped, but the models' logit rows
+   * may differ in length, e.g. 152064 and 151936 for the pages' Qwen2.5
+   * 7B / 0.5B pair).  Draft rows hold the logits of ids 0..V_draft-1 only;
+   * ids V_draft..V-1 have q = 0 (the draft cannot propose them, a proposal
+   * there is a q(x) = 0 proposal).  0 means V; otherwise 1 <= V_draft <= V,
+   * and ld_draft >= V_draft.  Greedy ignores it. */
+  int32_t        V_draft;
 } sd_verify_args_t;
 
 /* Bytes of device workspace sd_verify_sample / sd_verify_greedy need for

@@ -56,6 +56,7 @@ class SdVerifyArgs(ctypes.Structure):
         ("flags", ctypes.c_uint32),
         ("top_p_per_row", ctypes.c_void_p),
         ("tv_budget_per_row", ctypes.c_void_p),
+        ("V_draft", ctypes.c_int32),
     ]
 
 
@@ -146,6 +147,9 @@ def make_args(target, draft, draft_ids, k_per_row=None, temperature=None, top_p=
             raise TypeError("target and draft logits must share a dtype")
         a.draft_logits = draft.data_ptr()
         a.ld_draft = _rows_ld(draft, "draft")
+        if draft.shape[2] > V:
+            raise ValueError("draft rows longer than the target's vocabulary")
+        a.V_draft = draft.shape[2]   # a shorter draft vocabulary: q = 0 past it
     else:
         a.draft_logits = None
         a.ld_draft = a.ld_target

@@ -96,12 +96,12 @@ __global__ __launch_bounds__(NT_ROW) void k_row_prepare(Args a, RowStat* rs, int
   const char* row = is_t ? target_row(a, r, j) : draft_row(a, r, j);
   const float c = 1.4426950408889634f / T;
   const bool pen = build_penalty_bitmap<NT>(a, r, j, 0, a.V, bm);
-  RowStat out = row_stats_dev<DT, NT>(a, row, c, pen, bm, L, request_top_p(a, r));
+  RowStat out = row_stats_dev<DT, NT>(a, row, is_t ? a.V : a.Vd, c, pen, bm, L, request_top_p(a, r));
   if (threadIdx.x == 0) {
     if (j < K) {
       const int x = a.ids[(int64_t)r * a.K_max + j];
       if (x >= 0 && x < a.V) {
-        float z = load1<DT>(row, x);
+        float z = (is_t || x < a.Vd) ? load1<DT>(row, x) : -INFINITY;
         if (pen && ((bm[x >> 5] >> (x & 31)) & 1u)) z = penalize(z, a.rep);
         out.kx = z;
       }
@@ -669,17 +669,20 @@ struct Vec8 {
 // of a positive logit is its bits with the sign flipped, and a negative
 // logit only needs some key below the window, which the same flip gives;
 // one operation per word instead of two.
-// TAIL false: V is a multiple of 8, so no vector needs masking.
+// TAIL false: the row holds a multiple of 8 logits and every vector streamed
+// lies inside it, so no vector needs masking.  V: logits the row holds (a
+// draft row may hold fewer than the vocabulary).
 template <bool POS = false, bool TAIL = true>
 __device__ __forceinline__ void vec8(const uint4& ld, int l, int k, int V, Vec8& v) {
   v.w[0] = ld.x;
   v.w[1] = ld.y;
   v.w[2] = ld.z;
   v.w[3] = ld.w;
-  // The vector that holds the row end, when V is not a multiple of 8: its
-  // elements from V on read as -inf (bf16 0xFF80).
-  if (TAIL && (l + 1) * NT_F * VEC > V && (V & 7) && k == (V >> 3)) {
-    const int keep = (V & 7) * 16;   // bits of the 128 that stay
+  // A vector that reaches past the row's V logits (the row-end vector when V
+  // is not a multiple of 8, and every vector of a draft row past a shorter
+  // draft vocabulary): its elements from V on read as -inf (bf16 0xFF80).
+  if (TAIL && (l + 1) * NT_F * VEC > V && k * VEC + VEC > V) {
+    const int keep = max(V - k * VEC, 0) * 16;   // bits of the 128 that stay
     const uint64_t m0 = keep >= 64 ? ~0ull : (1ull << keep) - 1ull;
     const uint64_t m1 = keep <= 64 ? 0ull : (1ull << (keep - 64)) - 1ull;
     const uint64_t inf4 = 0xFF80FF80FF80FF80ull;
@@ -1071,11 +1074,12 @@ __global__ __launch_bounds__(NT_F) void k_pair_fast(Args a, UnitOut* uo) {
   int j = un.j;
   if (bonus) j = min(max(request_k(a, r), 0), a.K_max);
   const int V = a.V, nvec = (V + VEC - 1) / VEC;
+  const int Vd = a.Vd;   // the draft row's logits (ids Vd..V-1 have q = 0)
   const float rep = a.rep;
   const char* trow = target_row(a, r, j);
   const char* drow = bonus ? trow : draft_row(a, r, j);
   const __amdgpu_buffer_rsrc_t rs_t = row_rsrc(trow, nvec * 16);
-  const __amdgpu_buffer_rsrc_t rs_d = row_rsrc(drow, bonus ? 0 : nvec * 16);
+  const __amdgpu_buffer_rsrc_t rs_d = row_rsrc(drow, bonus ? 0 : (Vd + VEC - 1) / VEC * 16);
   const uint32_t voff = (uint32_t)tid * 16u;
   const uint32_t hlane = (uint32_t)(tid & (NCOPY - 1)) * 4u;
   ExactList exp_, exq;
@@ -1261,7 +1265,7 @@ __global__ __launch_bounds__(NT_F) void k_pair_fast(Args a, UnitOut* uo) {
         const int k = l * NT + tid;
         if (k < nvec) {
           Vec8 v;
-          vec8(stg[(NR + l) % NSTG], l, k, V, v);
+          vec8(stg[(NR + l) % NSTG], l, k, Vd, v);
           q0 = fmaxf(q0, max8(v.z));
         }
       });
@@ -1326,7 +1330,7 @@ __global__ __launch_bounds__(NT_F) void k_pair_fast(Args a, UnitOut* uo) {
     kxp = kxq = -INFINITY;
     if (xtok >= 0 && xtok < V) {
       kxp = __uint_as_float(s_kx << 16);
-      kxq = __uint_as_float(s_kx & 0xFFFF0000u);
+      kxq = xtok < Vd ? __uint_as_float(s_kx & 0xFFFF0000u) : -INFINITY;
       if (pen && ((bm[xtok >> 5] >> (xtok & 31)) & 1u)) {
         kxp = penalize(kxp, rep);
         kxq = penalize(kxq, rep);
@@ -1363,7 +1367,7 @@ __global__ __launch_bounds__(NT_F) void k_pair_fast(Args a, UnitOut* uo) {
       const int k = l * NT + tid;
       if (k < nvec) {
         Vec8 v;
-        vec8<POS, TAIL>(ld, l, k, V, v);
+        vec8<POS, TAIL>(ld, l, k, Vd, v);
         const uint32_t bits = RAISE ? pen_bits8(bm, k) : 0u;
         const uint4 dv = make_uint4(v.w[0], v.w[1], v.w[2], v.w[3]);
         (void)row_vec<(l < NSAMP)>(v, k, c, gcq, t1q, histq, hlane, exq, aq);
@@ -1384,8 +1388,9 @@ __global__ __launch_bounds__(NT_F) void k_pair_fast(Args a, UnitOut* uo) {
     };
     // (instances by window sign and by the target cut's half of the code range)
     const bool posq = t1q >= 0x8000u + 254u, low = cut_code < 127u;
-    // (and by whether penalized keys rise)
-    if (raise || tail) {
+    // (and by whether penalized keys rise or a vector needs masking)
+    const bool tail_d = (Vd & 7) != 0 || Vd < V;
+    if (raise || tail_d) {
       if (posq) stream_b.template operator()<true, -1, true, true>();
       else stream_b.template operator()<false, -1, true, true>();
     } else if (posq) {
@@ -1400,7 +1405,8 @@ __global__ __launch_bounds__(NT_F) void k_pair_fast(Args a, UnitOut* uo) {
       for (int i = tid; i < npl; i += NT) {
         const int id = plid[i];
         const uint32_t g = plraw[i];
-        const uint32_t raw = g == 0xFFFFFFFFu ? reinterpret_cast<const uint16_t*>(drow)[id] : g >> 16;
+        const uint32_t raw = id >= Vd ? 0xFF80u   // past a shorter draft row: -inf
+                             : g == 0xFFFFFFFFu ? reinterpret_cast<const uint16_t*>(drow)[id] : g >> 16;
         pen_fix(raw, id, t1q, rep, c, gcq, hneg, exq, aq);
       }
     hist_fold(histq, hsum, tid);
@@ -1688,7 +1694,7 @@ __device__ __forceinline__ void fallback_unit(const Args& a, UnitOut* uo, int u)
   out.flags = UO_SLOW;
   out.accept = 1;
   out.y = -1;
-  const RowStat P = row_stats_dev<SD_BF16, NT>(a, trow, c, pen, bm, ex, request_top_p(a, r));
+  const RowStat P = row_stats_dev<SD_BF16, NT>(a, trow, a.V, c, pen, bm, ex, request_top_p(a, r));
   if (P.flags & NONFINITE) {
     if (tid == 0) {
       out.flags = UO_NONFINITE;
@@ -1705,7 +1711,7 @@ __device__ __forceinline__ void fallback_unit(const Args& a, UnitOut* uo, int u)
     }
     return;
   }
-  const RowStat Q = row_stats_dev<SD_BF16, NT>(a, drow, c, pen, bm, ex, request_top_p(a, r));
+  const RowStat Q = row_stats_dev<SD_BF16, NT>(a, drow, a.Vd, c, pen, bm, ex, request_top_p(a, r));
   if (Q.flags & NONFINITE) {
     if (tid == 0) {
       out.flags = UO_NONFINITE;
@@ -1719,7 +1725,7 @@ __device__ __forceinline__ void fallback_unit(const Args& a, UnitOut* uo, int u)
     float kxp = -INFINITY, kxq = -INFINITY;
     if (x >= 0 && x < a.V) {
       kxp = load1<SD_BF16>(trow, x);
-      kxq = load1<SD_BF16>(drow, x);
+      kxq = x < a.Vd ? load1<SD_BF16>(drow, x) : -INFINITY;
       if (pen && ((bm[x >> 5] >> (x & 31)) & 1u)) {
         kxp = penalize(kxp, a.rep);
         kxq = penalize(kxq, a.rep);
@@ -1909,7 +1915,7 @@ __global__ __launch_bounds__(NT_ROW) void k_debug_rows(Args a, const RowStat* rs
   const float ip = (float)(1.0 / S.Zk);
   for (int k = threadIdx.x; k < nvec; k += NT) {
     float z[VEC];
-    load8<DT>(row, k, V, z);
+    load8_row<DT>(row, k, is_t ? V : a.Vd, z);
     if (pen) apply_penalty8(bm, k, 0, a.rep, z);
 #pragma unroll
     for (int e = 0; e < VEC; ++e) {
@@ -2080,8 +2086,10 @@ int check_common(const sd_verify_args_t* a, bool sample) {
       (reinterpret_cast<uintptr_t>(a->target_logits) & 15u))
     return SD_EINVAL;
   if (a->K_max > 0 && !a->draft_ids) return SD_EINVAL;
+  if (sample && (a->V_draft < 0 || a->V_draft > a->V)) return SD_EINVAL;
+  const int64_t vd = a->V_draft > 0 ? a->V_draft : a->V;
   if (sample && a->K_max > 0 &&
-      (!a->draft_logits || a->ld_draft < a->V || (a->ld_draft * es) % 16 != 0 ||
+      (!a->draft_logits || a->ld_draft < vd || (a->ld_draft * es) % 16 != 0 ||
        (reinterpret_cast<uintptr_t>(a->draft_logits) & 15u)))
     return SD_EINVAL;
   if (!(a->rep_penalty > 0.0f) || !(a->rep_penalty < INFINITY)) return SD_EINVAL;
@@ -2118,6 +2126,7 @@ Args make_args(const sd_verify_args_t* s) {
   a.offset = s->offset;
   a.flags = s->flags;
   a.fp_shift = 62 - ceil_log2(s->V);
+  a.Vd = s->V_draft > 0 ? s->V_draft : s->V;
   return a;
 }
 

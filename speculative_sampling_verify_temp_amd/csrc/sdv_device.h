@@ -33,6 +33,7 @@ struct Args {
   int fp_shift;       // fixed-point scale exponent of masses (see e_fixed)
   const float* tpr;   // per-request top-p, or null (top_p)
   const float* dpr;   // per-request TV budget, or null (D)
+  int Vd;             // draft rows hold ids 0..Vd-1 (Vd <= V); ids Vd..V-1 have q = 0
 };
 
 // Per processed row (target j or draft j of request r).
@@ -108,6 +109,18 @@ __device__ __forceinline__ void load8(const char* row, int k, int V, float (&z)[
 #pragma unroll
     for (int e = 0; e < VEC; ++e)
       if (i0 + e >= V) z[e] = -INFINITY;
+  }
+}
+
+// load8 over a row that holds only Vr logits, inside a vocabulary of V >= Vr
+// ids: vectors past the row read as -inf without a memory access.
+template <int DT>
+__device__ __forceinline__ void load8_row(const char* row, int k, int Vr, float (&z)[VEC]) {
+  if (k * VEC < Vr) {
+    load8<DT>(row, k, Vr, z);
+  } else {
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) z[e] = -INFINITY;
   }
 }
 

@@ -95,11 +95,13 @@ __device__ void find_crossing(const uint64_t* hm, const uint32_t* hc, int nbins,
 // Statistics and top-p cut of one processed row, streaming it from global
 // memory: pass 0 gives the max M and Z = sum exp2((key - M) c) (online per
 // thread, fp64 totals); with top-p, three histogram passes over 12 + 12 + 8
-// bits of the orderable key with fixed-point masses find the cut key.
+// bits of the orderable key with fixed-point masses find the cut key.  The
+// row holds V logits (a.V for a target row, a.Vd for a draft row: ids past
+// a draft row have q = 0 and take no part).
 template <int DT, int NT>
-__device__ __forceinline__ RowStat row_stats_dev(const Args& a, const char* row, float c, bool pen,
-                                 const uint32_t* bm, const ExactLds& L, float top_p) {
-  const int V = a.V, nvec = (V + VEC - 1) / VEC;
+__device__ __forceinline__ RowStat row_stats_dev(const Args& a, const char* row, int V, float c,
+                                 bool pen, const uint32_t* bm, const ExactLds& L, float top_p) {
+  const int nvec = (V + VEC - 1) / VEC;
   float m = -INFINITY;
   double Z = 0.0;
   int bad = 0;
@@ -236,7 +238,7 @@ __device__ __forceinline__ double pair_tv_dev(const Args& a, const char* trow, c
   for (int k = threadIdx.x; k < nvec; k += NT) {
     float zp[VEC], zq[VEC];
     load8<DT>(trow, k, V, zp);
-    load8<DT>(drow, k, V, zq);
+    load8_row<DT>(drow, k, a.Vd, zq);
     if (pen) {
       apply_penalty8(bm, k, 0, a.rep, zp);
       apply_penalty8(bm, k, 0, a.rep, zq);
@@ -246,7 +248,7 @@ __device__ __forceinline__ double pair_tv_dev(const Args& a, const char* trow, c
     for (int e = 0; e < VEC; ++e) {
       const int id = k * VEC + e;
       const float p = (id < V && kept(P, ord_key(zp[e]))) ? e_rel(zp[e], P.M, P.c) * ip : 0.0f;
-      const float q = (id < V && kept(Q, ord_key(zq[e]))) ? e_rel(zq[e], Q.M, Q.c) * iq : 0.0f;
+      const float q = (id < a.Vd && kept(Q, ord_key(zq[e]))) ? e_rel(zq[e], Q.M, Q.c) * iq : 0.0f;
       s += fabsf(p - q);
     }
     acc += (double)s;
@@ -281,7 +283,7 @@ __device__ __forceinline__ Drawn draw_dev(const Args& a, const char* trow, const
       load8<DT>(trow, k, V, zp);
       if (pen) apply_penalty8(bm, k, 0, a.rep, zp);
       if (md == 0) {
-        load8<DT>(drow, k, V, zq);
+        load8_row<DT>(drow, k, a.Vd, zq);
         if (pen) apply_penalty8(bm, k, 0, a.rep, zq);
       }
 #pragma unroll
@@ -289,7 +291,7 @@ __device__ __forceinline__ Drawn draw_dev(const Args& a, const char* trow, const
         const int id = k * VEC + e;
         float p = (id < V && kept(P, ord_key(zp[e]))) ? e_rel(zp[e], P.M, P.c) * ip : 0.0f;
         if (md == 0) {
-          const float q = (id < V && kept(Q, ord_key(zq[e]))) ? e_rel(zq[e], Q.M, Q.c) * iq : 0.0f;
+          const float q = (id < a.Vd && kept(Q, ord_key(zq[e]))) ? e_rel(zq[e], Q.M, Q.c) * iq : 0.0f;
           p = fmaxf(p - q, 0.0f);
         }
         w[e] = p;

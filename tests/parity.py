@@ -18,16 +18,17 @@ TOL = 1e-5
 
 
 def to_device(w, device="cuda"):
-    """Workload arrays -> device tensors (bf16 rows padded to a multiple of 8
-    elements when V is not one, so every row is 16-byte aligned)."""
+    """Workload arrays -> device tensors (each row padded to a multiple of 16
+    bytes when its length is not one, so every row is 16-byte aligned; draft
+    rows of a shorter draft vocabulary get their own, shorter stride)."""
     import torch
     es_mult = 8 if w.dtype == "bf16" else 4
-    ld = -(-w.V // es_mult) * es_mult
 
     def rows(x):
         if x is None or x.size == 0:
             return None
         B, R, V = x.shape
+        ld = -(-V // es_mult) * es_mult
         if w.dtype == "bf16":
             buf = np.zeros((B, R, ld), dtype=np.uint16)
             buf[..., :V] = x

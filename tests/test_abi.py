@@ -142,14 +142,44 @@ def test_draft_confidence_rejects_bad_arguments_on_host():
 
 
 def test_args_struct_matches_the_header():
-    """The ctypes mirror ends with the two per-request parameter pointers,
-    at the offsets the C struct gives them (no field skipped or reordered)."""
+    """The ctypes mirror has every field of the C struct at the offset a C
+    compiler gives it, and the same size (the header compiled here by gcc)."""
+    import shutil
+    import subprocess
+    import tempfile
     import speculative_sampling_verify_temp_amd as sdv
     A = sdv.SdVerifyArgs
     names = [f[0] for f in A._fields_]
-    assert names[-2:] == ["top_p_per_row", "tv_budget_per_row"]
-    assert A.tv_budget_per_row.offset == A.top_p_per_row.offset + 8
-    assert ctypes.sizeof(A) == A.tv_budget_per_row.offset + 8
+    assert names[-3:] == ["top_p_per_row", "tv_budget_per_row", "V_draft"]
+    gcc = shutil.which("gcc") or shutil.which("cc")
+    if gcc is None:
+        pytest.skip("no C compiler")
+    src = "#include <stdio.h>\n#include <stddef.h>\n#include \"sd_verify.h\"\nint main(void){" + \
+        "printf(\"%zu\", sizeof(sd_verify_args_t));" + "".join(
+            f'printf(" %zu", offsetof(sd_verify_args_t, {n}));' for n in names) + "return 0;}\n"
+    with tempfile.TemporaryDirectory() as d:
+        c, exe = os.path.join(d, "t.c"), os.path.join(d, "t")
+        open(c, "w").write(src)
+        subprocess.run([gcc, "-I", os.path.dirname(HEADER), c, "-o", exe], check=True)
+        got = [int(v) for v in subprocess.run([exe], capture_output=True, text=True,
+                                               check=True).stdout.split()]
+    assert got[0] == ctypes.sizeof(A)
+    assert got[1:] == [getattr(A, n).offset for n in names]
+
+
+def test_draft_vocabulary_checked_on_host():
+    """V_draft in [0, V] (0 = V) and ld_draft >= V_draft pass the host checks
+    (the call then stops at the too-small workspace, SD_EWORKSPACE); other
+    values fail them (SD_EINVAL).  Nothing is launched either way."""
+    import speculative_sampling_verify_temp_amd as sdv
+    out = ctypes.c_void_p(0x400000)
+    for vd, ld, code in ((0, 1024, -2), (999, 1000, -2), (600, 600, -2), (1000, 1000, -2),
+                         (1001, 1024, -1), (-1, 1024, -1), (600, 592, -1), (0, 992, -1)):
+        a = _good_args(sdv)
+        a.V_draft, a.ld_draft = vd, ld
+        rc = sdv.lib.sd_verify_sample(ctypes.byref(a), ctypes.c_void_p(0x500000), 16,
+                                      out, out, None, None, None)
+        assert rc == code, (vd, ld)
 
 
 def test_noalloc_rejects_on_host_before_touching_the_device():

@@ -101,12 +101,16 @@ class Workload:
         """Verified draft positions in one call: sum of K_r."""
         return int(np.sum(self.k_per_row))
 
+    @property
+    def V_draft(self):
+        return self.draft.shape[2]
+
     def logit_bytes(self):
-        """Bytes of logits the sampling verify must read once:
-        (2 K_r + 1) rows of V per request row."""
+        """Bytes of logits the sampling verify must read once: K_r + 1
+        target rows of V and K_r draft rows of V_draft per request row."""
         es = 4 if self.dtype == "f32" else 2
         k = self.k_per_row.astype(np.int64)
-        return int(np.sum(2 * k + 1)) * self.V * es
+        return int(np.sum(k + 1) * self.V + np.sum(k) * self.V_draft) * es
 
     def with_(self, **kw):
         return replace(self, **kw)
@@ -128,12 +132,13 @@ def gumbel_proposal(rng, z, T):
     return int(np.argmax(z / T + g))
 
 
-def propose(rng, z, T, odd_share=0.0, prior=None):
+def propose(rng, z, T, odd_share=0.0, prior=None, V=None):
     """One draft id: with probability odd_share an odd proposal (half of them
-    uniform over [0, V), half a uniformly chosen prior id when the request has
-    prior ids), else gumbel_proposal.  The draws come from rng in a fixed
-    order, so a workload is a function of its seed."""
-    V = np.asarray(z).size
+    uniform over [0, V), V the target's vocabulary, by default the draft
+    row's length; half a uniformly chosen prior id when the request has prior
+    ids), else gumbel_proposal over the draft row.  The draws come from rng in
+    a fixed order, so a workload is a function of its seed."""
+    V = np.asarray(z).size if V is None else V
     a, b = rng.random(), rng.random()
     x = gumbel_proposal(rng, z, T)
     if a < odd_share:
@@ -213,31 +218,37 @@ def config3(K=8, call=0, B=1, V=V_QWEN3):
                     np.full(B, K, dtype=np.int32), np.ones(B, np.float32))
 
 
-def config4_row(seed, r, K=8, V=V_QWEN25, n_prior=128, odd_share=0.0):
+def config4_row(seed, r, K=8, V=V_QWEN25, n_prior=128, odd_share=0.0, V_draft=None):
     """One request row of config 4, from its own generator stream."""
     rng = np.random.default_rng([4, seed, r])
     T = np.float32(rng.uniform(0.5, 1.0))
     t = rng.normal(0.0, 3.0, size=(K + 1, V)).astype(np.float32)
     dr = _corr_rows(rng, t[:K], 0.9, 3.0).astype(np.float32)
+    if V_draft is not None:
+        dr = dr[:, :V_draft]
     tb, db = f32_to_bf16_bits(t), f32_to_bf16_bits(dr)
     dl = bf16_bits_to_f32(db)
     prior = rng.integers(0, V, size=n_prior).astype(np.int32)
-    ids = np.array([propose(rng, dl[j], T, odd_share, prior) for j in range(K)],
+    ids = np.array([propose(rng, dl[j], T, odd_share, prior, V) for j in range(K)],
                    dtype=np.int32)
     return tb, db, ids, T, prior
 
 
 def config4(seed=0, B=256, K=8, V=V_QWEN25, n_prior=128, D=0.75,
-            philox_seed=0, top_p=0.9, rep_penalty=1.1, odd_share=0.0):
+            philox_seed=0, top_p=0.9, rep_penalty=1.1, odd_share=0.0, V_draft=None):
     """The batched workload.  Proposals come from the draft's own sampler
-    (odd_share = 0, the measured workload); parity runs add odd proposals."""
+    (odd_share = 0, the measured workload); parity runs add odd proposals.
+    V_draft: a draft model with a shorter vocabulary (the pages' Qwen2.5
+    0.5B draft has 151936 logits against the 7B target's 152064)."""
+    Vd = V if V_draft is None else V_draft
     tb = np.empty((B, K + 1, V), dtype=np.uint16)
-    db = np.empty((B, K, V), dtype=np.uint16)
+    db = np.empty((B, K, Vd), dtype=np.uint16)
     ids = np.empty((B, K), dtype=np.int32)
     T = np.empty(B, dtype=np.float32)
     prior = np.empty((B, n_prior), dtype=np.int32)
     for r in range(B):
-        tb[r], db[r], ids[r], T[r], prior[r] = config4_row(seed, r, K, V, n_prior, odd_share)
+        tb[r], db[r], ids[r], T[r], prior[r] = config4_row(seed, r, K, V, n_prior, odd_share,
+                                                           V_draft)
     offs = (np.arange(B + 1, dtype=np.int64) * n_prior).astype(np.int32)
     return Workload("config4", "bf16", tb, db, ids,
                     np.full(B, K, dtype=np.int32), T, top_p=top_p,
@@ -291,12 +302,16 @@ def config5(seed=0, B=512, K_max=8, V=V_QWEN3, T=0.7, threshold=0.6,
 def random_case(seed, B=3, K_max=3, V=300, dtype="f32", sigma=2.0, corr=0.8,
                 T_range=(0.5, 1.5), top_p=1.0, rep_penalty=1.0, n_prior=0,
                 D=0.0, ragged=False, philox_seed=None, flags=0, prior_pool=None,
-                odd_share=0.1):
+                odd_share=0.1, V_draft=None):
     """Small generic case for parity sweeps (rows span several tiles when V
-    is a few thousand, with a ragged tail when V is not a tile multiple)."""
+    is a few thousand, with a ragged tail when V is not a tile multiple).
+    V_draft < V: the draft rows hold the first V_draft logits only (a draft
+    model with a shorter vocabulary)."""
     rng = np.random.default_rng([9, seed])
     t = rng.normal(0.0, sigma, size=(B, K_max + 1, V)).astype(np.float32)
     dr = _corr_rows(rng, t[:, :K_max], corr, sigma).astype(np.float32)
+    if V_draft is not None:
+        dr = np.ascontiguousarray(dr[..., :V_draft])
     tt, dd = _store(t, dtype), _store(dr, dtype)
     dl = _load(dd, dtype)
     T = rng.uniform(*T_range, size=B).astype(np.float32)
@@ -304,7 +319,7 @@ def random_case(seed, B=3, K_max=3, V=300, dtype="f32", sigma=2.0, corr=0.8,
     if n_prior:
         pid, poff = _prior(rng, B, n_prior, V, prior_pool)
     ids = np.array([[propose(rng, dl[r, j], T[r], odd_share,
-                             None if pid is None else pid[poff[r]:poff[r + 1]])
+                             None if pid is None else pid[poff[r]:poff[r + 1]], V)
                      for j in range(K_max)] for r in range(B)], dtype=np.int32)
     ks = (rng.integers(0, K_max + 1, size=B) if ragged
           else np.full(B, K_max)).astype(np.int32)
