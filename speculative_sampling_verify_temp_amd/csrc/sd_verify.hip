@@ -1042,7 +1042,7 @@ __global__ __launch_bounds__(NT_F) void k_pair_fast(Args a, UnitOut* uo) {
   __shared__ double rmass[R_CAP];
   __shared__ int rid[R_CAP];
   __shared__ double sd[NT / WAVE];
-  __shared__ double sbc[R_CAP + 4];
+  __shared__ double scanw[NT / WAVE];   // draw: per-wave scan totals
   __shared__ unsigned long long rtf[NR + 1];   // draw: per-round weight totals (fixed point)
   __shared__ float sf[NT / WAVE];
   __shared__ int si[NT / WAVE + 8];
@@ -1609,10 +1609,17 @@ __global__ __launch_bounds__(NT_F) void k_pair_fast(Args a, UnitOut* uo) {
       slot_keys(sl * NT + tid, zp, zq, id);
       sf += e_fixed(nucleus_w(zp, zq, mode, Mp, ip, kq_cut, Mq, iq, c), SHD);
     }
-    const uint64_t incl = (uint64_t)block_incl_scan_fast<NT>((double)sf, sd);
+    // block scan with one barrier (the per-wave totals have a buffer of
+    // their own); the one thread whose inclusive total first exceeds t (its
+    // exclusive total, the previous thread's inclusive, does not) claims
+    // the crossing with a plain store
     if (tid == 0) { si[0] = INT_MAX; si[1] = -1; }
+    double xs = wave_incl_scan((double)sf);
+    if (lane == WAVE - 1) scanw[wv] = xs;
     __syncthreads();
-    if (lstar >= 0 && Rf + incl > tf) atomicMin(&si[0], tid);
+    for (int i = 0; i < wv; ++i) xs += scanw[i];
+    const uint64_t incl = (uint64_t)xs;
+    if (lstar >= 0 && Rf + incl > tf && Rf + incl - sf <= tf) si[0] = tid;
     __syncthreads();
     if (tid == si[0]) {
       uint64_t C = Rf + incl - sf;
