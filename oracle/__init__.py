@@ -15,6 +15,8 @@ verify   The verify step itself: logit processing, top-p, TV distance, the
          correction/bonus draw, and greedy verify.
 confidence  The draft-side confidence step before it: each draft row's top-1
          probability and the draft length an early-stop threshold implies.
+lmhead   The step fed from hidden states through the LM heads: logits as the
+         fp64 product of hidden states and head weights, then verify.
 
 Parity status of each function is stated in its docstring.  Two readings are
 "parity unpinned" by the pages (the repetition-penalty formula and the top-p
@@ -31,5 +33,6 @@ from .verify import (
     verify_greedy_ref, SampleResult, GreedyResult,
 )
 from .confidence import top1_prob, draft_lengths, draft_confidence_ref
+from .lmhead import lmhead_logits, lmhead_verify_sample_ref, lmhead_verify_greedy_ref
 
 __all__ = [n for n in dir() if not n.startswith("_")]

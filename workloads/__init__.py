@@ -327,3 +327,116 @@ def random_case(seed, B=3, K_max=3, V=300, dtype="f32", sigma=2.0, corr=0.8,
                     rep_penalty=rep_penalty, prior_ids=pid, prior_offsets=poff,
                     tv_budget=D, seed=seed if philox_seed is None else philox_seed,
                     flags=flags)
+
+
+# ---------------------------------------------------------------------------
+# Hidden states and LM heads for the fused LM-head + verify path.
+# ---------------------------------------------------------------------------
+
+QWEN25_7B_HIDDEN = 3584    # the pages' target model's hidden size
+QWEN25_05B_HIDDEN = 896    # the pages' draft model's hidden size
+
+
+@dataclass
+class LmHeadWorkload:
+    name: str
+    target_hidden: np.ndarray   # uint16 bf16 bits [B][K_max+1][H_t]
+    draft_hidden: np.ndarray    # uint16 bf16 bits [B][K_max][H_d]
+    target_weight: np.ndarray   # uint16 bf16 bits [V][H_t]
+    draft_weight: np.ndarray    # uint16 bf16 bits [V_draft][H_d]
+    draft_ids: np.ndarray       # int32 [B][K_max]
+    k_per_row: np.ndarray       # int32 [B]
+    temperature: np.ndarray     # float32 [B]
+    tv_budget: float = 0.0
+    seed: int = 0
+    offset: int = 0
+    flags: int = 0
+
+    @property
+    def B(self):
+        return self.target_hidden.shape[0]
+
+    @property
+    def K_max(self):
+        return self.target_hidden.shape[1] - 1
+
+    @property
+    def V(self):
+        return self.target_weight.shape[0]
+
+    @property
+    def V_draft(self):
+        return self.draft_weight.shape[0]
+
+    def f32(self, name):
+        return bf16_bits_to_f32(getattr(self, name))
+
+    def positions(self):
+        return int(np.sum(self.k_per_row))
+
+    def with_(self, **kw):
+        return replace(self, **kw)
+
+
+def _dyadic_bf16(rng, shape, scale_steps, lo_hi=None):
+    """Values m * 2^-8 with integer m ~ round(N(0, scale_steps)), |m| <= 255
+    (exact in bf16), or small integers in [lo, hi] when lo_hi is given."""
+    if lo_hi is not None:
+        x = rng.integers(lo_hi[0], lo_hi[1] + 1, size=shape).astype(np.float32)
+    else:
+        m = np.clip(np.rint(rng.normal(0.0, scale_steps, size=shape)), -255, 255)
+        x = (m * 2.0 ** -8).astype(np.float32)
+    b = f32_to_bf16_bits(x)
+    assert np.array_equal(bf16_bits_to_f32(b), x)
+    return b
+
+
+def lmhead_case(seed, B=4, K_max=3, V=4096, V_draft=None, H_t=256, H_d=64, sigma=3.0,
+                T_range=(0.6, 1.0), D=0.0, ragged=False, exact=True, flags=0,
+                proposals=True):
+    """Hidden states and LM-head weights whose logits have standard deviation
+    about sigma; the draft's hidden state is the first H_d components of the
+    target's (a smaller model that sees part of the same state) and its head
+    is the target's first H_d columns scaled by sqrt(H_t / H_d), so draft
+    logits correlate with the target's at about sqrt(H_d / H_t).
+
+    exact=True: hidden components are integers in [-2, 2] and weights are
+    multiples of 2^-8 below 1 in magnitude, so every product and every partial
+    sum of a logit is exact in fp32 (|sum| < 2^13 for H <= 4096: 21 bits);
+    the logits are then exactly the fp64 oracle's whatever the summation
+    order.  exact=False: N(0, 1) hidden states and N(0, sigma^2 / H) weights
+    rounded to bf16 (the measured workload).
+
+    Draft ids come from the draft model's own sampler: Gumbel-max over its
+    logits / T (the draft forward a plain fp64 matmul here), when proposals is
+    set; else uniform ids."""
+    rng = np.random.default_rng([11, seed])
+    Vd = V if V_draft is None else V_draft
+    if exact:
+        th = _dyadic_bf16(rng, (B, K_max + 1, H_t), None, (-2, 2))
+        wt = _dyadic_bf16(rng, (V, H_t), 256.0 * sigma / np.sqrt(2.0 * H_t))
+    else:
+        th = f32_to_bf16_bits(rng.standard_normal((B, K_max + 1, H_t), dtype=np.float32))
+        wt = np.empty((V, H_t), dtype=np.uint16)
+        for i0 in range(0, V, 8192):   # in chunks: full-size heads are large
+            i1 = min(V, i0 + 8192)
+            wt[i0:i1] = f32_to_bf16_bits(
+                rng.standard_normal((i1 - i0, H_t), dtype=np.float32) * np.float32(sigma / np.sqrt(H_t)))
+    dh = np.ascontiguousarray(th[:, :K_max, :H_d])
+    wd_f = bf16_bits_to_f32(wt[:Vd, :H_d]) * np.float32(np.sqrt(H_t / H_d))
+    if exact:   # back onto the 2^-8 grid, |m| <= 255
+        wd_f = (np.clip(np.rint(wd_f * 256.0), -255, 255) / 256.0).astype(np.float32)
+    wd = f32_to_bf16_bits(wd_f)
+    T = rng.uniform(*T_range, size=B).astype(np.float32)
+    ids = np.empty((B, K_max), dtype=np.int32)
+    if proposals and K_max > 0:
+        dhf, wdf = bf16_bits_to_f32(dh).astype(np.float64), bf16_bits_to_f32(wd).astype(np.float64)
+        for r in range(B):
+            z = dhf[r] @ wdf.T
+            for j in range(K_max):
+                ids[r, j] = gumbel_proposal(rng, z[j], T[r])
+    else:
+        ids[:] = rng.integers(0, V, size=ids.shape)
+    ks = (rng.integers(0, K_max + 1, size=B) if ragged else np.full(B, K_max)).astype(np.int32)
+    return LmHeadWorkload("lmhead", th, dh, wt, wd, ids, ks, T, tv_budget=D, seed=seed,
+                          flags=flags)
