@@ -226,6 +226,75 @@ int sd_draft_confidence(const void *draft_logits, int32_t dtype, int32_t B,
                         const float *temperature, float threshold,
                         float *out_top1, int32_t *out_k, void *stream);
 
+/* ------------------------------------------------------------------------
+ * Verify fed from hidden states through the LM heads ("What I Gave Up to
+ * Make Speculative Decoding Faster", section "Finding the break-even point":
+ * the engine scores the verify rows with its LM head; Adaptive-SpecDecode-
+ * Lab README, implementation section: one target forward keeps the logits of
+ * the rows being verified).  The logits z = h . W^T are computed by a bf16
+ * MFMA GEMM with fp32 accumulation and consumed tile by tile: no V-wide
+ * logit row is written to memory.  The results are those of sd_verify_sample
+ * / sd_verify_greedy on these logits with top_p = 1 and rep_penalty = 1
+ * (neither is supported here).
+ *
+ * target_hidden: device bf16 [B][K_max+1][H_target] (position j of request r
+ *   at ((int64)r * (K_max + 1) + j) * H_target); draft_hidden: device bf16
+ *   [B][K_max][H_draft].  target_weight: device bf16 [V][H_target], row i
+ *   the output vector of token i; draft_weight: [V_draft][H_draft].
+ *   H_target and H_draft are multiples of 64; every pointer is 16-byte
+ *   aligned; nothing is written to them.
+ * V_draft (0 = V) and the draft ids, K, temperature, budget, seed, offset
+ * and SD_NO_BONUS mean what they mean in sd_verify_args_t.  Greedy ignores
+ * the draft fields and the temperature.
+ * ------------------------------------------------------------------------ */
+typedef struct sd_lmhead_args {
+  const void    *target_hidden;
+  const void    *draft_hidden;
+  const void    *target_weight;
+  const void    *draft_weight;
+  int32_t        H_target;
+  int32_t        H_draft;
+  int32_t        B;
+  int32_t        K_max;
+  int32_t        V;
+  int32_t        V_draft;
+  const int32_t *draft_ids;      /* [B][K_max]                                  */
+  const int32_t *k_per_row;      /* [B] or NULL (all K_max)                     */
+  const float   *temperature;    /* [B] or NULL (all 1)                         */
+  float          tv_budget;      /* D >= 0                                      */
+  uint32_t       flags;          /* SD_NO_BONUS                                 */
+  uint64_t       seed;
+  uint64_t       offset;
+} sd_lmhead_args_t;
+
+/* Workspace bytes of the two calls below (depends on B, K_max, V, V_draft):
+ * per (row, 128-token tile) partials, about 8 B * (2 K_max + 1) * B * V / 128
+ * plus per-row statistics; no V-wide row.  SD_OK or SD_EINVAL. */
+int sd_lmhead_workspace_bytes(const sd_lmhead_args_t *args, size_t *bytes);
+
+/* Sampling verify on LM-head logits.  Outputs, statistics, status bits and
+ * the return codes as for sd_verify_sample (statistics include d; d is
+ * computed, at the cost of a second pass over both heads, when
+ * 0 < tv_budget < 1 or out_stats is given).  Asynchronous on `stream`. */
+int sd_lmhead_verify_sample(const sd_lmhead_args_t *args, void *workspace,
+                            size_t workspace_bytes, int32_t *out_accepted,
+                            int32_t *out_tokens, uint32_t *out_status,
+                            float *out_stats, void *stream);
+
+/* Greedy verify on LM-head logits (target head only), as sd_verify_greedy. */
+int sd_lmhead_verify_greedy(const sd_lmhead_args_t *args, void *workspace,
+                            size_t workspace_bytes, int32_t *out_accepted,
+                            int32_t *out_tokens, uint32_t *out_status,
+                            int32_t *out_argmax, void *stream);
+
+/* Test export: the LM-head logits of the rows the sampling verify (out_draft
+ * non-NULL) or the greedy verify (out_draft NULL) uses, as fp32 into
+ * out_target [B][K_max+1][V] and out_draft [B][K_max][V_draft] (rows it
+ * does not use are left untouched), from the same tile engine. */
+int sd_debug_lmhead_logits(const sd_lmhead_args_t *args, void *workspace,
+                           size_t workspace_bytes, float *out_target,
+                           float *out_draft, void *stream);
+
 /* Human-readable text for a return code (static storage). */
 const char *sd_strerror(int code);
 

@@ -60,6 +60,28 @@ class SdVerifyArgs(ctypes.Structure):
     ]
 
 
+class SdLmHeadArgs(ctypes.Structure):
+    _fields_ = [
+        ("target_hidden", ctypes.c_void_p),
+        ("draft_hidden", ctypes.c_void_p),
+        ("target_weight", ctypes.c_void_p),
+        ("draft_weight", ctypes.c_void_p),
+        ("H_target", ctypes.c_int32),
+        ("H_draft", ctypes.c_int32),
+        ("B", ctypes.c_int32),
+        ("K_max", ctypes.c_int32),
+        ("V", ctypes.c_int32),
+        ("V_draft", ctypes.c_int32),
+        ("draft_ids", ctypes.c_void_p),
+        ("k_per_row", ctypes.c_void_p),
+        ("temperature", ctypes.c_void_p),
+        ("tv_budget", ctypes.c_float),
+        ("flags", ctypes.c_uint32),
+        ("seed", ctypes.c_uint64),
+        ("offset", ctypes.c_uint64),
+    ]
+
+
 class SdVerifyError(RuntimeError):
     def __init__(self, code, what):
         super().__init__(f"{what}: {strerror(code)} ({code})")
@@ -97,6 +119,15 @@ def _load():
     lib.sd_debug_uniforms.restype = ctypes.c_int
     lib.sd_draft_confidence.argtypes = [P, I32, I32, I32, I32, ctypes.c_int64, P, ctypes.c_float, P, P, P]
     lib.sd_draft_confidence.restype = ctypes.c_int
+    L = ctypes.POINTER(SdLmHeadArgs)
+    lib.sd_lmhead_workspace_bytes.argtypes = [L, ctypes.POINTER(SZ)]
+    lib.sd_lmhead_workspace_bytes.restype = ctypes.c_int
+    lib.sd_lmhead_verify_sample.argtypes = [L, P, SZ, P, P, P, P, P]
+    lib.sd_lmhead_verify_sample.restype = ctypes.c_int
+    lib.sd_lmhead_verify_greedy.argtypes = [L, P, SZ, P, P, P, P, P]
+    lib.sd_lmhead_verify_greedy.restype = ctypes.c_int
+    lib.sd_debug_lmhead_logits.argtypes = [L, P, SZ, P, P, P]
+    lib.sd_debug_lmhead_logits.restype = ctypes.c_int
     return lib
 
 
@@ -331,3 +362,70 @@ def draft_confidence(draft, temperature=None, threshold=0.6, stream=None, length
     if rc != 0:
         raise SdVerifyError(rc, "sd_draft_confidence")
     return top1, kout
+
+
+# ---------------------------------------------------------------------------
+# Verify fed from hidden states through the LM heads (sd_lmhead_*).
+# ---------------------------------------------------------------------------
+
+def make_lmhead_args(target_hidden, target_weight, draft_ids, draft_hidden=None, draft_weight=None,
+                     k_per_row=None, temperature=None, tv_budget=0.0, seed=0, offset=0, flags=0):
+    """Fill sd_lmhead_args_t from bf16 device tensors: target_hidden
+    [B][K_max+1][H_t], target_weight [V][H_t], draft_hidden [B][K_max][H_d],
+    draft_weight [V_draft][H_d] (all contiguous)."""
+    for t in (target_hidden, target_weight, draft_hidden, draft_weight):
+        if t is not None and not t.is_contiguous():
+            raise ValueError("LM-head tensors must be contiguous")
+    a = SdLmHeadArgs()
+    B, K1, Ht = target_hidden.shape
+    a.target_hidden, a.target_weight = target_hidden.data_ptr(), target_weight.data_ptr()
+    a.H_target, a.B, a.K_max, a.V = Ht, B, K1 - 1, target_weight.shape[0]
+    if draft_hidden is not None:
+        a.draft_hidden, a.draft_weight = draft_hidden.data_ptr(), draft_weight.data_ptr()
+        a.H_draft, a.V_draft = draft_hidden.shape[2], draft_weight.shape[0]
+    a.draft_ids = draft_ids.data_ptr() if draft_ids is not None and draft_ids.numel() else None
+    a.k_per_row = None if k_per_row is None else k_per_row.data_ptr()
+    a.temperature = None if temperature is None else temperature.data_ptr()
+    a.tv_budget = float(tv_budget)
+    a.flags = int(flags)
+    a.seed = int(seed) & (2**64 - 1)
+    a.offset = int(offset) & (2**64 - 1)
+    return a
+
+
+def lmhead_workspace(args, device):
+    import torch
+    n = ctypes.c_size_t()
+    rc = lib.sd_lmhead_workspace_bytes(ctypes.byref(args), ctypes.byref(n))
+    if rc != SD_OK:
+        raise SdVerifyError(rc, "sd_lmhead_workspace_bytes")
+    return torch.empty(max(1, n.value), dtype=torch.uint8, device=device)
+
+
+def lmhead_verify_sample(args, accepted, tokens, status=None, stats=None, workspace=None,
+                         stream=None):
+    """sd_lmhead_verify_sample into caller-allocated outputs."""
+    ws = lmhead_workspace(args, accepted.device) if workspace is None else workspace
+    rc = lib.sd_lmhead_verify_sample(ctypes.byref(args), _ptr(ws), ws.numel(), _ptr(accepted),
+                                     _ptr(tokens), _ptr(status), _ptr(stats), _stream(stream))
+    if rc != SD_OK:
+        raise SdVerifyError(rc, "sd_lmhead_verify_sample")
+
+
+def lmhead_verify_greedy(args, accepted, tokens, status=None, argmax=None, workspace=None,
+                         stream=None):
+    """sd_lmhead_verify_greedy into caller-allocated outputs."""
+    ws = lmhead_workspace(args, accepted.device) if workspace is None else workspace
+    rc = lib.sd_lmhead_verify_greedy(ctypes.byref(args), _ptr(ws), ws.numel(), _ptr(accepted),
+                                     _ptr(tokens), _ptr(status), _ptr(argmax), _stream(stream))
+    if rc != SD_OK:
+        raise SdVerifyError(rc, "sd_lmhead_verify_greedy")
+
+
+def debug_lmhead_logits(args, out_target, out_draft=None, workspace=None, stream=None):
+    """The LM-head logits of the used rows (test export)."""
+    ws = lmhead_workspace(args, out_target.device) if workspace is None else workspace
+    rc = lib.sd_debug_lmhead_logits(ctypes.byref(args), _ptr(ws), ws.numel(), _ptr(out_target),
+                                    _ptr(out_draft), _stream(stream))
+    if rc != SD_OK:
+        raise SdVerifyError(rc, "sd_debug_lmhead_logits")

@@ -15,7 +15,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libsdverify.so")
-SOURCES = ["sd_verify.hip", "sd_confidence.hip"]
+SOURCES = ["sd_verify.hip", "sd_confidence.hip", "sd_lmhead.hip"]
 ARCH = os.environ.get("SDV_OFFLOAD_ARCH", "gfx950")
 
 HIPCC_FLAGS = [

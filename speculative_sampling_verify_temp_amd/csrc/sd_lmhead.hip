@@ -1,0 +1,1039 @@
+// Verify step fed from hidden states through the LM heads on gfx950, with no
+// V-wide logit row written to memory ("What I Gave Up to Make Speculative
+// Decoding Faster", section "Finding the break-even point": the engine scores
+// the verify rows with its LM head; Adaptive-SpecDecode-Lab README,
+// implementation section: one target forward keeps the logits of the rows
+// being verified).
+//
+// Logits come out of a bf16 MFMA tile engine (v_mfma_f32_32x32x16_bf16, fp32
+// accumulation): a workgroup of 256 threads computes a 64-row x 128-token
+// tile, hidden states (rows) times head rows (tokens), both K-contiguous,
+// through LDS in K chunks of 64.  Every kernel consumes its tiles in an
+// epilogue:
+//   k_lm_stats      per (row, token tile): max and sum of exp2 of l = z c,
+//                   and the logit of the row's draft token when the tile
+//                   holds it
+//   k_lm_rowstat    per row: M = max l, Z = sum 2^(l - M)
+//   k_lm_tv         per (pair, tile): sum |p - q| (target and draft tiles
+//                   of the same pair in one workgroup), only when a budget
+//                   strictly between 0 and 1 needs d
+//   k_lm_decide     per request: theta, pi(x), acceptance, first rejection
+//   k_lm_draw_tiles per (request, tile): fixed-point totals of the draw
+//                   weights (the residual max(p - q, 0) and p)
+//   k_lm_draw_pick  per request: the crossing tile, recomputed, scanned
+// Greedy: k_lm_greedy_part (per row and tile: max and lowest argmax) and
+// k_lm_greedy_final.  A tile engine call recomputes the same logits bit for
+// bit wherever it runs (same K order), so the draw's pick agrees with its
+// tile totals.  Rows are taken from compacted lists of the rows each request
+// uses, so a ragged K costs no work on unused rows.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <limits.h>
+#include <math.h>
+#include <stddef.h>
+
+#include "sd_verify.h"
+#include "sdv_device.h"
+
+using namespace sdv;
+
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+constexpr int TM = 64;            // rows per tile
+constexpr int TN = 128;           // tokens per tile
+constexpr int BK = 64;            // K chunk
+constexpr int LDK = BK + 8;       // LDS row stride of the A/B chunks (bf16): 144 B
+constexpr int NT_L = 256;         // threads of a tile workgroup (4 waves)
+constexpr int LDC = TN;           // LDS row stride of a stashed fp32 tile
+constexpr int NXCD = 8;           // dies of the device (tile order is per die)
+constexpr int SHL = 40;           // fixed-point shift of the draw weights (each <= 1)
+
+struct LmArgs {
+  const uint16_t* th;   // target hidden [B][K_max+1][Ht]
+  const uint16_t* dh;   // draft hidden  [B][K_max][Hd]
+  const uint16_t* wt;   // target head [V][Ht]
+  const uint16_t* wd;   // draft head  [Vd][Hd]
+  int Ht, Hd, B, K_max, V, Vd;
+  const int32_t* ids;
+  const int32_t* kpr;
+  const float* temp;
+  float D;
+  uint64_t seed, offset;
+  uint32_t flags;
+};
+
+struct RowSL {       // statistics of one listed row
+  float M;           // max of l = z c (log2 units)
+  float c;           // log2(e) / T
+  double Z;          // sum of 2^(l - M)
+  float zx;          // logit of the row's draft token (or -inf)
+  uint32_t flags;    // 1: a non-finite logit
+  int32_t pad0, pad1;
+};
+static_assert(sizeof(RowSL) == 32, "RowSL layout");
+
+// Workspace carve-up.
+struct LmLayout {
+  size_t cnt, toff, doff, tlist, dlist, tpart, dpart, trs, drs, tvp, dvec, drw, wpart, gpart, total;
+  int ntt, ntd;   // token tiles of the target and draft heads
+};
+
+__host__ __device__ inline size_t al256(size_t x) { return (x + 255) / 256 * 256; }
+
+LmLayout lm_layout(int B, int K, int V, int Vd) {
+  LmLayout L;
+  L.ntt = (V + TN - 1) / TN;
+  L.ntd = (Vd + TN - 1) / TN;
+  const size_t nt = (size_t)B * (K + 1), nd = (size_t)B * K;
+  size_t o = 0;
+  L.cnt = o;   o = al256(o + 4 * sizeof(int));
+  L.toff = o;  o = al256(o + (size_t)B * sizeof(int));
+  L.doff = o;  o = al256(o + (size_t)B * sizeof(int));
+  L.tlist = o; o = al256(o + nt * sizeof(int));
+  L.dlist = o; o = al256(o + (nd ? nd : 1) * sizeof(int));
+  L.tpart = o; o = al256(o + nt * L.ntt * sizeof(float2));
+  L.dpart = o; o = al256(o + (nd ? nd : 1) * L.ntd * sizeof(float2));
+  L.trs = o;   o = al256(o + nt * sizeof(RowSL));
+  L.drs = o;   o = al256(o + (nd ? nd : 1) * sizeof(RowSL));
+  L.tvp = o;   o = al256(o + (nd ? nd : 1) * L.ntt * sizeof(float));
+  L.dvec = o;  o = al256(o + (nd ? nd : 1) * sizeof(double));
+  L.drw = o;   o = al256(o + (size_t)B * sizeof(int2));
+  L.wpart = o; o = al256(o + (size_t)B * L.ntt * 2 * sizeof(uint64_t));
+  L.gpart = o; o = al256(o + nt * L.ntt * sizeof(uint2));
+  L.total = o;
+  return L;
+}
+
+struct LmWs {
+  int* cnt;      // [0] target rows listed, [1] draft rows listed
+  int* toff;     // per request: its first target row in the list (-1: none)
+  int* doff;     // per request: its first draft row in the list
+  int* tlist;    // listed target rows: r (K_max + 1) + j
+  int* dlist;    // listed draft rows: r K_max + j
+  float2* tpart; // [listed target row][token tile] (max l, sum 2^(l - max))
+  float2* dpart;
+  RowSL* trs;
+  RowSL* drs;
+  float* tvp;    // [pair = listed draft row][target token tile] sum |p - q|
+  double* dvec;  // [pair] d
+  int2* drw;     // per request: (mode, n); mode 0 residual, 1 p, -1 none
+  uint64_t* wpart;   // [request][tile][2] fixed-point totals: residual, p
+  uint2* gpart;  // [listed target row][tile] (orderable key, id) of the max
+};
+
+LmWs carve(char* ws, const LmLayout& L) {
+  LmWs w;
+  w.cnt = reinterpret_cast<int*>(ws + L.cnt);
+  w.toff = reinterpret_cast<int*>(ws + L.toff);
+  w.doff = reinterpret_cast<int*>(ws + L.doff);
+  w.tlist = reinterpret_cast<int*>(ws + L.tlist);
+  w.dlist = reinterpret_cast<int*>(ws + L.dlist);
+  w.tpart = reinterpret_cast<float2*>(ws + L.tpart);
+  w.dpart = reinterpret_cast<float2*>(ws + L.dpart);
+  w.trs = reinterpret_cast<RowSL*>(ws + L.trs);
+  w.drs = reinterpret_cast<RowSL*>(ws + L.drs);
+  w.tvp = reinterpret_cast<float*>(ws + L.tvp);
+  w.dvec = reinterpret_cast<double*>(ws + L.dvec);
+  w.drw = reinterpret_cast<int2*>(ws + L.drw);
+  w.wpart = reinterpret_cast<uint64_t*>(ws + L.wpart);
+  w.gpart = reinterpret_cast<uint2*>(ws + L.gpart);
+  return w;
+}
+
+__device__ __forceinline__ int req_k(const LmArgs& a, int r) { return a.kpr ? a.kpr[r] : a.K_max; }
+__device__ __forceinline__ float req_t(const LmArgs& a, int r) { return a.temp ? a.temp[r] : 1.0f; }
+
+// Status of request r before any logit is seen (sampling: with the
+// temperature; greedy: without).  One invalidating defect, in the order K,
+// draft ids, temperature.
+__device__ uint32_t lm_status(const LmArgs& a, int r, bool sample) {
+  const int K = req_k(a, r);
+  if (K < 0 || K > a.K_max) return SD_ST_BAD_K;
+  for (int j = 0; j < K; ++j) {
+    const int x = a.ids[(int64_t)r * a.K_max + j];
+    if (x < 0 || x >= a.V) return SD_ST_BAD_DRAFT_ID;
+  }
+  if (sample) {
+    const float T = req_t(a, r);
+    if (!(T > 0.0f) || !(T < INFINITY)) return SD_ST_BAD_TEMP;
+  }
+  return 0u;
+}
+
+// ---------------------------------------------------------------------------
+// Row lists: one workgroup; valid requests list rows j = 0..K_r (target) and
+// j = 0..K_r - 1 (draft) in request order.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(1024) void k_lm_lists(LmArgs a, LmWs w, int sample) {
+  constexpr int NT = 1024;
+  __shared__ int wt_t[NT / WAVE], wt_d[NT / WAVE];
+  __shared__ int base_t, base_d;
+  if (threadIdx.x == 0) { base_t = 0; base_d = 0; }
+  __syncthreads();
+  for (int r0 = 0; r0 < a.B; r0 += NT) {
+    const int r = r0 + threadIdx.x;
+    int nt = 0, nd = 0;
+    if (r < a.B && lm_status(a, r, sample != 0) == 0u) {
+      const int K = req_k(a, r);
+      nt = K + 1;
+      nd = sample ? K : 0;
+    }
+    int tot_t, tot_d;
+    const int et = block_excl_scan_int<NT>(nt, wt_t, &tot_t);
+    const int ed = block_excl_scan_int<NT>(nd, wt_d, &tot_d);
+    const int bt = base_t, bd = base_d;
+    if (r < a.B) {
+      w.toff[r] = nt ? bt + et : -1;
+      w.doff[r] = nd ? bd + ed : -1;
+      for (int j = 0; j < nt; ++j) w.tlist[bt + et + j] = r * (a.K_max + 1) + j;
+      for (int j = 0; j < nd; ++j) w.dlist[bd + ed + j] = r * a.K_max + j;
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) { base_t += tot_t; base_d += tot_d; }
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) { w.cnt[0] = base_t; w.cnt[1] = base_d; }
+}
+
+// ---------------------------------------------------------------------------
+// The tile engine.
+// ---------------------------------------------------------------------------
+struct TileLds {
+  uint16_t* a;   // [TM][LDK]
+  uint16_t* b;   // [TN][LDK]
+};
+
+// acc[nb] = rows (TM) x tokens (TN) of hidden x head^T.  arow[i]: this
+// thread's two A rows (i = 0, 1: tile rows t / 8 and t / 8 + 32), null for
+// a row past the list; weight rows n0 .. n0 + TN - 1 past nrows_w read 0.
+// Wave (wr, wc) = (wave / 2, wave % 2) holds rows 32 wr + m and tokens
+// 64 wc + 32 b + n (b = 0, 1) in the MFMA 32x32 output layout: lane l, value
+// v: n = l % 32, m = 8 (v / 4) + 4 (l / 32) + v % 4.
+__device__ __forceinline__ void tile_gemm(const uint16_t* const (&arow)[2], const uint16_t* w,
+                                          int n0, int nrows_w, int H, const TileLds& s,
+                                          f32x16 (&acc)[2]) {
+  const int t = threadIdx.x;
+  const int lane = t % WAVE, wv = t / WAVE;
+  const int wr = wv >> 1, wc = wv & 1;
+  const int kc = (t & 7) * 8;     // this thread's 8-element chunk of a K chunk
+  const int rr = t >> 3;          // its row within a 32-row slab
+  const uint16_t* brow[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int n = n0 + rr + 32 * i;
+    brow[i] = n < nrows_w ? w + (int64_t)n * H : nullptr;
+  }
+#pragma unroll
+  for (int b = 0; b < 2; ++b)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) acc[b][v] = 0.0f;
+  uint4 ra[2], rb[4];
+  auto load = [&](int k0) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+      ra[i] = arow[i] ? *reinterpret_cast<const uint4*>(arow[i] + k0 + kc) : make_uint4(0, 0, 0, 0);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      rb[i] = brow[i] ? *reinterpret_cast<const uint4*>(brow[i] + k0 + kc) : make_uint4(0, 0, 0, 0);
+  };
+  load(0);
+  const int am = 32 * wr + (lane & 31), ko = 8 * (lane >> 5);
+  for (int k0 = 0; k0 < H; k0 += BK) {
+    __syncthreads();   // the previous chunk's fragments are read
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+      *reinterpret_cast<uint4*>(s.a + (rr + 32 * i) * LDK + kc) = ra[i];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      *reinterpret_cast<uint4*>(s.b + (rr + 32 * i) * LDK + kc) = rb[i];
+    __syncthreads();
+    if (k0 + BK < H) load(k0 + BK);   // the next chunk's loads overlap this chunk's MFMAs
+#pragma unroll
+    for (int st = 0; st < BK / 16; ++st) {
+      const bf16x8 af = *reinterpret_cast<const bf16x8*>(s.a + am * LDK + 16 * st + ko);
+#pragma unroll
+      for (int b = 0; b < 2; ++b) {
+        const int bn = 64 * wc + 32 * b + (lane & 31);
+        const bf16x8 bfr = *reinterpret_cast<const bf16x8*>(s.b + bn * LDK + 16 * st + ko);
+        acc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, bfr, acc[b], 0, 0, 0);
+      }
+    }
+  }
+}
+
+// The accumulators into an fp32 LDS tile C[TM][LDC].
+__device__ __forceinline__ void stash(const f32x16 (&acc)[2], float* C) {
+  const int lane = threadIdx.x % WAVE, wv = threadIdx.x / WAVE;
+  const int wr = wv >> 1, wc = wv & 1;
+#pragma unroll
+  for (int b = 0; b < 2; ++b)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int m = 32 * wr + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+      const int n = 64 * wc + 32 * b + (lane & 31);
+      C[m * LDC + n] = acc[b][v];
+    }
+}
+
+// Tile order: the blocks of one die take consecutive tiles, row blocks
+// fastest, so a head tile is fetched into that die's L2 once for all its row
+// blocks.  Returns false for padding blocks.
+__device__ __forceinline__ bool tile_of(int nm, int nn, int& m, int& n) {
+  const int per = (int)gridDim.x / NXCD;
+  const int g = ((int)blockIdx.x % NXCD) * per + (int)blockIdx.x / NXCD;
+  if (g >= nm * nn) return false;
+  m = g % nm;
+  n = g / nm;
+  return true;
+}
+
+// Hidden-state row pointer of listed row `li` (target or draft list).
+__device__ __forceinline__ const uint16_t* hidden_row(const LmArgs& a, bool target, int enc) {
+  return target ? a.th + (int64_t)enc * a.Ht : a.dh + (int64_t)enc * a.Hd;
+}
+
+// ---------------------------------------------------------------------------
+// Pass 1: per (listed row, token tile) max and exp2 sum; the draft token's logit.
+// ---------------------------------------------------------------------------
+template <bool TGT>
+__global__ __launch_bounds__(NT_L) void k_lm_stats(LmArgs a, LmWs w, int nm, int nn) {
+  __shared__ __align__(16) uint16_t sa[TM * LDK];
+  __shared__ __align__(16) uint16_t sb[TN * LDK];
+  __shared__ __align__(16) float C[TM * LDC];
+  int mb, nb;
+  if (!tile_of(nm, nn, mb, nb)) return;
+  const int nrows = w.cnt[TGT ? 0 : 1];
+  const int m0 = mb * TM, n0 = nb * TN;
+  if (m0 >= nrows) return;
+  const int* list = TGT ? w.tlist : w.dlist;
+  const int rr = threadIdx.x >> 3;
+  const uint16_t* arow[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int li = m0 + rr + 32 * i;
+    arow[i] = li < nrows ? hidden_row(a, TGT, list[li]) : nullptr;
+  }
+  const int Vs = TGT ? a.V : a.Vd;
+  f32x16 acc[2];
+  tile_gemm(arow, TGT ? a.wt : a.wd, n0, Vs, TGT ? a.Ht : a.Hd, TileLds{sa, sb}, acc);
+  __syncthreads();
+  stash(acc, C);
+  __syncthreads();
+  // four threads per row, 32 tokens each
+  const int row = threadIdx.x >> 2, q4 = threadIdx.x & 3;
+  const int li = m0 + row;
+  const bool live = li < nrows;
+  int r = 0, j = 0;
+  float c = 1.0f;
+  int x = -1;
+  if (live) {
+    const int enc = list[li];
+    r = TGT ? enc / (a.K_max + 1) : enc / a.K_max;
+    j = TGT ? enc % (a.K_max + 1) : enc % a.K_max;
+    c = 1.4426950408889634f / req_t(a, r);
+    if (j < req_k(a, r)) x = a.ids[(int64_t)r * a.K_max + j];
+  }
+  float m = -INFINITY;
+  int bad = 0;
+  const int nv = min(TN, Vs - n0);
+  for (int e = 0; e < 32; ++e) {
+    const int n = q4 * 32 + e;
+    if (n < nv) {
+      const float z = C[row * LDC + n];
+      bad |= nonfinite(z);
+      m = fmaxf(m, z * c);
+    }
+    if (live && n0 + n == x && n < nv) {
+      RowSL* rs = (TGT ? w.trs : w.drs) + li;
+      rs->zx = C[row * LDC + n];
+    }
+  }
+  m = fmaxf(m, __shfl_xor(m, 1));
+  m = fmaxf(m, __shfl_xor(m, 2));
+  float s = 0.0f;
+  if (m > -INFINITY)
+    for (int e = 0; e < 32; ++e) {
+      const int n = q4 * 32 + e;
+      if (n < nv) s += fast_exp2(C[row * LDC + n] * c - m);
+    }
+  s += __shfl_xor(s, 1);
+  s += __shfl_xor(s, 2);
+  bad |= __shfl_xor(bad, 1);
+  bad |= __shfl_xor(bad, 2);
+  if (live && q4 == 0) {
+    float2* part = (TGT ? w.tpart : w.dpart) + (int64_t)li * nn + nb;
+    *part = make_float2(bad ? NAN : m, s);
+  }
+}
+
+// Per listed row: M, Z from the tile partials (fp64 combine in tile order).
+template <bool TGT>
+__global__ __launch_bounds__(256) void k_lm_rowstat(LmArgs a, LmWs w, int nn) {
+  __shared__ float sf[256 / WAVE];
+  __shared__ double sd[256 / WAVE];
+  __shared__ int si[256 / WAVE + 4];
+  const int li = blockIdx.x;
+  if (li >= w.cnt[TGT ? 0 : 1]) return;
+  const float2* part = (TGT ? w.tpart : w.dpart) + (int64_t)li * nn;
+  float m = -INFINITY;
+  int bad = 0;
+  for (int t = threadIdx.x; t < nn; t += 256) {
+    const float2 p = part[t];
+    bad |= (p.x != p.x);
+    m = fmaxf(m, p.x);
+  }
+  const float M = block_max<256>(m, sf);
+  bad = block_or<256>(bad, si);
+  double z = 0.0;
+  for (int t = threadIdx.x; t < nn; t += 256) {
+    const float2 p = part[t];
+    if (p.x > -INFINITY) z += (double)p.y * exp2((double)p.x - (double)M);
+  }
+  const double Z = block_sum<256>(z, sd);
+  if (threadIdx.x == 0) {
+    RowSL* rs = (TGT ? w.trs : w.drs) + li;
+    const int enc = (TGT ? w.tlist : w.dlist)[li];
+    const int r = TGT ? enc / (a.K_max + 1) : enc / a.K_max;
+    rs->M = M;
+    rs->c = 1.4426950408889634f / req_t(a, r);
+    rs->Z = Z;
+    rs->flags = (bad || !(M > -INFINITY) || !(M < INFINITY)) ? 1u : 0u;
+  }
+}
+
+// Clears the draft-token logits before pass 1 writes the ones it finds (a
+// token past a short draft head is never found: -inf).
+__global__ void k_lm_clear_zx(LmWs w, int nt_max, int nd_max) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < nt_max) w.trs[i].zx = -INFINITY;
+  if (i < nd_max) w.drs[i].zx = -INFINITY;
+}
+
+// ---------------------------------------------------------------------------
+// The pair kernels: a tile of 64 pairs (or requests) x 128 tokens, the
+// target tile stashed in LDS, the draft tile in registers.
+// ---------------------------------------------------------------------------
+struct PairRows {
+  int tli, dli;   // listed target / draft row (-1: none)
+};
+
+// TV partials: pair p = listed draft row (r, j); its target row is listed at
+// toff[r] + j.
+__global__ __launch_bounds__(NT_L) void k_lm_tv(LmArgs a, LmWs w, int nm, int nn) {
+  __shared__ __align__(16) float Ct[TM * LDC];
+  __shared__ __align__(16) float U[TM * LDC];   // A/B chunks, then the draft tile
+  __shared__ int s_tli[TM];
+  int mb, nb;
+  if (!tile_of(nm, nn, mb, nb)) return;
+  const int npairs = w.cnt[1];
+  const int m0 = mb * TM, n0 = nb * TN;
+  if (m0 >= npairs) return;
+  if (threadIdx.x < TM) {
+    const int p = m0 + threadIdx.x;
+    int tli = -1;
+    if (p < npairs) {
+      const int enc = w.dlist[p];
+      const int r = enc / a.K_max, j = enc % a.K_max;
+      tli = w.toff[r] + j;
+    }
+    s_tli[threadIdx.x] = tli;
+  }
+  __syncthreads();
+  const int rr = threadIdx.x >> 3;
+  TileLds s{reinterpret_cast<uint16_t*>(U), reinterpret_cast<uint16_t*>(U) + TM * LDK};
+  f32x16 acc[2];
+  {
+    const uint16_t* arow[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int tli = s_tli[rr + 32 * i];
+      arow[i] = tli >= 0 ? hidden_row(a, true, w.tlist[tli]) : nullptr;
+    }
+    tile_gemm(arow, a.wt, n0, a.V, a.Ht, s, acc);
+    stash(acc, Ct);
+  }
+  {
+    const uint16_t* arow[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int p = m0 + rr + 32 * i;
+      arow[i] = p < npairs ? hidden_row(a, false, w.dlist[p]) : nullptr;
+    }
+    tile_gemm(arow, a.wd, n0, a.Vd, a.Hd, s, acc);
+  }
+  __syncthreads();
+  stash(acc, U);
+  __syncthreads();
+  const int row = threadIdx.x >> 2, q4 = threadIdx.x & 3;
+  const int p = m0 + row;
+  float sum = 0.0f;
+  if (p < npairs) {
+    const RowSL P = w.trs[s_tli[row]], Q = w.drs[p];
+    const float ip = (float)(1.0 / P.Z), iq = (float)(1.0 / Q.Z);
+    const int nv = min(TN, a.V - n0);
+    for (int e = 0; e < 32; ++e) {
+      const int n = q4 * 32 + e;
+      if (n >= nv) continue;
+      const float pp = fast_exp2(Ct[row * LDC + n] * P.c - P.M) * ip;
+      const float qq = (n0 + n < a.Vd) ? fast_exp2(U[row * LDC + n] * Q.c - Q.M) * iq : 0.0f;
+      sum += fabsf(pp - qq);
+    }
+  }
+  sum += __shfl_xor(sum, 1);
+  sum += __shfl_xor(sum, 2);
+  if (p < npairs && q4 == 0) w.tvp[(int64_t)p * nn + nb] = sum;
+}
+
+__global__ __launch_bounds__(256) void k_lm_tv_reduce(LmWs w, int nn) {
+  __shared__ double sd[256 / WAVE];
+  const int p = blockIdx.x;
+  if (p >= w.cnt[1]) return;
+  double s = 0.0;
+  for (int t = threadIdx.x; t < nn; t += 256) s += (double)w.tvp[(int64_t)p * nn + t];
+  s = block_sum<256>(s, sd);
+  if (threadIdx.x == 0) w.dvec[p] = fmin(0.5 * s, 1.0);
+}
+
+// p(x) or q(x) of a listed row in fp64.
+__device__ __forceinline__ double prob_x(const RowSL& s) {
+  if (!(s.zx > -INFINITY)) return 0.0;
+  return exp2((double)s.zx * (double)s.c - (double)s.M) / s.Z;
+}
+
+// Decisions of one request: one thread per request.
+__global__ __launch_bounds__(64) void k_lm_decide(LmArgs a, LmWs w, int tv_valid, int32_t* out_acc,
+                                                  int32_t* out_tok, uint32_t* out_status,
+                                                  float* out_stats) {
+  const int r = blockIdx.x * 64 + threadIdx.x;
+  if (r >= a.B) return;
+  const int K1 = a.K_max + 1;
+  const int64_t base = (int64_t)r * K1;
+  uint32_t st = lm_status(a, r, true);
+  const int K = st ? 0 : req_k(a, r);
+  int n = K;
+  if (!st) {
+    const int t0 = w.toff[r], d0 = w.doff[r];
+    for (int jj = 0; jj <= K; ++jj)
+      if (w.trs[t0 + jj].flags) st |= SD_ST_NONFINITE;
+    for (int jj = 0; jj < K; ++jj)
+      if (w.drs[d0 + jj].flags) st |= SD_ST_NONFINITE;
+  }
+  if (st & SD_ST_INVALID_MASK) {
+    for (int t = 0; t < K1; ++t) out_tok[base + t] = -1;
+    if (out_stats)
+      for (int t = 0; t < K1 * SD_NSTAT; ++t) out_stats[base * SD_NSTAT + t] = 0.0f;
+    out_acc[r] = -1;
+    if (out_status) out_status[r] = st;
+    w.drw[r] = make_int2(-1, 0);
+    return;
+  }
+  const int t0 = w.toff[r], d0 = w.doff[r];
+  for (int jj = 0; jj <= K; ++jj) {
+    float u, v;
+    uniforms(a.seed, a.offset, r, jj, u, v);
+    float sv[SD_NSTAT] = {0, 0, 0, 0, 0, u, v, 0};
+    if (jj < K) {
+      const double px = prob_x(w.trs[t0 + jj]);
+      const double qx = prob_x(w.drs[d0 + jj]);
+      const double d = tv_valid ? w.dvec[d0 + jj] : 0.0;
+      double th;
+      if (tv_valid) th = (d <= (double)a.D) ? 1.0 : (double)a.D / d;
+      else th = (a.D >= 1.0f) ? 1.0 : 0.0;   // D = 0: theta matters only where p = q
+      const double pix = (1.0 - th) * px + th * qx;
+      const bool acc = (double)u * qx < pix;
+      if (qx == 0.0) st |= SD_ST_Q_ZERO;
+      sv[SD_STAT_D] = (float)d;
+      sv[SD_STAT_THETA] = (float)th;
+      sv[SD_STAT_PX] = (float)px;
+      sv[SD_STAT_QX] = (float)qx;
+      sv[SD_STAT_PIX] = (float)pix;
+      if (n == K && !acc) n = jj;
+    }
+    if (out_stats)
+      for (int s2 = 0; s2 < SD_NSTAT; ++s2) out_stats[(base + jj) * SD_NSTAT + s2] = sv[s2];
+  }
+  if (out_stats)
+    for (int t = K + 1; t < K1; ++t)
+      for (int s2 = 0; s2 < SD_NSTAT; ++s2) out_stats[(base + t) * SD_NSTAT + s2] = 0.0f;
+  const bool emit = !(n == K && (a.flags & SD_NO_BONUS));
+  for (int t = 0; t < K1; ++t) out_tok[base + t] = t < n ? a.ids[(int64_t)r * a.K_max + t] : -1;
+  out_acc[r] = n;
+  if (out_status) out_status[r] = st;
+  w.drw[r] = make_int2(emit ? (n < K ? 0 : 1) : -1, n);
+}
+
+// Draw weights of one token: residual max(p - q, 0) (mode 0) and p.
+__device__ __forceinline__ void draw_w(float zt, float zd, bool has_q, const RowSL& P,
+                                       const RowSL& Q, float ip, float iq, float& wres,
+                                       float& wp) {
+  const float pp = fast_exp2(zt * P.c - P.M) * ip;
+  const float qq = has_q ? fast_exp2(zd * Q.c - Q.M) * iq : 0.0f;
+  wp = pp;
+  wres = fmaxf(pp - qq, 0.0f);
+}
+
+// The tiles of a draw: requests r with a draw, 64 per block, the target row
+// (r, n) and (mode 0) the draft row (r, n).
+__device__ __forceinline__ void draw_tiles_gemm(const LmArgs& a, const LmWs& w, const int* reqs,
+                                                int n0, float* Ct, float* U, f32x16 (&acc)[2]) {
+  const int rr = threadIdx.x >> 3;
+  TileLds s{reinterpret_cast<uint16_t*>(U), reinterpret_cast<uint16_t*>(U) + TM * LDK};
+  {
+    const uint16_t* arow[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int r = reqs[rr + 32 * i];
+      arow[i] = nullptr;
+      if (r >= 0) {
+        const int2 dr = w.drw[r];
+        arow[i] = hidden_row(a, true, w.tlist[w.toff[r] + dr.y]);
+      }
+    }
+    tile_gemm(arow, a.wt, n0, a.V, a.Ht, s, acc);
+    stash(acc, Ct);
+  }
+  {
+    const uint16_t* arow[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int r = reqs[rr + 32 * i];
+      arow[i] = nullptr;
+      if (r >= 0) {
+        const int2 dr = w.drw[r];
+        if (dr.x == 0) arow[i] = hidden_row(a, false, w.dlist[w.doff[r] + dr.y]);
+      }
+    }
+    tile_gemm(arow, a.wd, n0, a.Vd, a.Hd, s, acc);
+  }
+  __syncthreads();
+  stash(acc, U);
+  __syncthreads();
+}
+
+__global__ __launch_bounds__(NT_L) void k_lm_draw_tiles(LmArgs a, LmWs w, int nm, int nn) {
+  __shared__ __align__(16) float Ct[TM * LDC];
+  __shared__ __align__(16) float U[TM * LDC];
+  __shared__ int reqs[TM];
+  int mb, nb;
+  if (!tile_of(nm, nn, mb, nb)) return;
+  const int m0 = mb * TM, n0 = nb * TN;
+  if (threadIdx.x < TM) {
+    const int r = m0 + threadIdx.x;
+    reqs[threadIdx.x] = (r < a.B && w.drw[r].x >= 0) ? r : -1;
+  }
+  __syncthreads();
+  int any = 0;
+  for (int i = 0; i < TM; ++i) any |= reqs[i] >= 0;
+  if (!any) return;
+  f32x16 acc[2];
+  draw_tiles_gemm(a, w, reqs, n0, Ct, U, acc);
+  const int row = threadIdx.x >> 2, q4 = threadIdx.x & 3;
+  const int r = reqs[row];
+  uint64_t sres = 0, sp = 0;
+  if (r >= 0) {
+    const int2 dr = w.drw[r];
+    const RowSL P = w.trs[w.toff[r] + dr.y];
+    RowSL Q = P;
+    if (dr.x == 0) Q = w.drs[w.doff[r] + dr.y];
+    const float ip = (float)(1.0 / P.Z), iq = (float)(1.0 / Q.Z);
+    const int nv = min(TN, a.V - n0);
+    for (int e = 0; e < 32; ++e) {
+      const int n = q4 * 32 + e;
+      if (n >= nv) continue;
+      float wres, wp;
+      draw_w(Ct[row * LDC + n], U[row * LDC + n], dr.x == 0 && n0 + n < a.Vd, P, Q, ip, iq, wres, wp);
+      sres += e_fixed(wres, SHL);
+      sp += e_fixed(wp, SHL);
+    }
+  }
+  sres += __shfl_xor(sres, 1);
+  sres += __shfl_xor(sres, 2);
+  sp += __shfl_xor(sp, 1);
+  sp += __shfl_xor(sp, 2);
+  if (r >= 0 && q4 == 0) {
+    w.wpart[((int64_t)r * nn + nb) * 2 + 0] = sres;
+    w.wpart[((int64_t)r * nn + nb) * 2 + 1] = sp;
+  }
+}
+
+// One request per block: the crossing tile from the tile totals (ascending
+// token id), that tile recomputed, the crossing token.  A residual of zero
+// mass falls back to p (status bit).
+__global__ __launch_bounds__(NT_L) void k_lm_draw_pick(LmArgs a, LmWs w, int nn, int32_t* out_tok,
+                                                       uint32_t* out_status, float* out_stats) {
+  __shared__ __align__(16) float Ct[TM * LDC];
+  __shared__ __align__(16) float U[TM * LDC];
+  __shared__ int reqs[TM];
+  __shared__ uint64_t su[NT_L];
+  __shared__ int s_tile, s_y;
+  __shared__ uint64_t s_R, s_tf, s_S;
+  __shared__ int s_mode;
+  const int r = blockIdx.x;
+  const int2 dr = w.drw[r];
+  if (dr.x < 0) return;
+  const int K1 = a.K_max + 1;
+  float u, v;
+  uniforms(a.seed, a.offset, r, dr.y, u, v);
+  if (threadIdx.x == 0) {
+    // totals in tile order (one thread: nn is about a thousand)
+    int mode = dr.x;
+    uint64_t S = 0;
+    for (int t = 0; t < nn; ++t) S += w.wpart[((int64_t)r * nn + t) * 2 + mode];
+    if (S == 0 && mode == 0) {
+      mode = 1;
+      S = 0;
+      for (int t = 0; t < nn; ++t) S += w.wpart[((int64_t)r * nn + t) * 2 + 1];
+      if (out_status) out_status[r] |= SD_ST_RESID_ZERO;
+    }
+    const uint64_t vk = (uint64_t)(v * 0x1p24f);
+    const uint64_t tf = (__umul64hi(vk, S) << 40) | ((vk * S) >> 24);   // floor(v S)
+    uint64_t acc = 0, alast = 0;
+    int tile = -1, last = -1;
+    uint64_t R = 0;
+    for (int t = 0; t < nn; ++t) {
+      const uint64_t x = w.wpart[((int64_t)r * nn + t) * 2 + mode];
+      if (x > 0) { last = t; alast = acc; }
+      if (tile < 0 && acc + x > tf) { tile = t; R = acc; }
+      acc += x;
+    }
+    if (tile < 0) { tile = last; R = alast; }
+    s_tile = tile;
+    s_R = R;
+    s_tf = tf;
+    s_S = S;
+    s_mode = mode;
+    s_y = -1;
+  }
+  if (threadIdx.x < TM) reqs[threadIdx.x] = threadIdx.x == 0 ? r : -1;
+  __syncthreads();
+  const int tile = s_tile;
+  if (tile < 0) {
+    if (threadIdx.x == 0) {
+      out_tok[(int64_t)r * K1 + dr.y] = -1;
+      if (out_stats) out_stats[((int64_t)r * K1 + dr.y) * SD_NSTAT + SD_STAT_S] = 0.0f;
+    }
+    return;
+  }
+  const int n0 = tile * TN;
+  f32x16 acc[2];
+  draw_tiles_gemm(a, w, reqs, n0, Ct, U, acc);
+  // row 0 of the tile: per-token fixed weights, two per thread in id order
+  const RowSL P = w.trs[w.toff[r] + dr.y];
+  RowSL Q = P;
+  if (dr.x == 0) Q = w.drs[w.doff[r] + dr.y];
+  const float ip = (float)(1.0 / P.Z), iq = (float)(1.0 / Q.Z);
+  const int mode = s_mode;
+  const int nv = min(TN, a.V - n0);
+  uint64_t wf = 0;
+  const int n = threadIdx.x;   // token n0 + n (threads >= TN hold nothing)
+  if (n < nv) {
+    float wres, wp;
+    draw_w(Ct[n], U[n], dr.x == 0 && n0 + n < a.Vd, P, Q, ip, iq, wres, wp);
+    wf = e_fixed(mode == 0 ? wres : wp, SHL);
+  }
+  su[threadIdx.x] = wf;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint64_t C = s_R;
+    int y = -1, lastpos = -1;
+    for (int i = 0; i < nv; ++i) {
+      if (su[i] > 0) lastpos = n0 + i;
+      C += su[i];
+      if (C > s_tf) { y = n0 + i; break; }
+    }
+    if (y < 0) y = lastpos;
+    out_tok[(int64_t)r * K1 + dr.y] = y;
+    if (out_stats) out_stats[((int64_t)r * K1 + dr.y) * SD_NSTAT + SD_STAT_S] = (float)((double)s_S * 0x1p-40);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Greedy: per (listed target row, tile) the largest logit and its lowest id.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(NT_L) void k_lm_greedy_part(LmArgs a, LmWs w, int nm, int nn) {
+  __shared__ __align__(16) uint16_t sa[TM * LDK];
+  __shared__ __align__(16) uint16_t sb[TN * LDK];
+  __shared__ __align__(16) float C[TM * LDC];
+  int mb, nb;
+  if (!tile_of(nm, nn, mb, nb)) return;
+  const int nrows = w.cnt[0];
+  const int m0 = mb * TM, n0 = nb * TN;
+  if (m0 >= nrows) return;
+  const int rr = threadIdx.x >> 3;
+  const uint16_t* arow[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int li = m0 + rr + 32 * i;
+    arow[i] = li < nrows ? hidden_row(a, true, w.tlist[li]) : nullptr;
+  }
+  f32x16 acc[2];
+  tile_gemm(arow, a.wt, n0, a.V, a.Ht, TileLds{sa, sb}, acc);
+  __syncthreads();
+  stash(acc, C);
+  __syncthreads();
+  const int row = threadIdx.x >> 2, q4 = threadIdx.x & 3;
+  const int li = m0 + row;
+  uint32_t bo = 0u;
+  int bi = INT_MAX;
+  int nan = 0;
+  const int nv = min(TN, a.V - n0);
+  for (int e = 0; e < 32; ++e) {
+    const int n = q4 * 32 + e;
+    if (n >= nv) continue;
+    const float z = C[row * LDC + n];
+    if (z != z) { nan = 1; continue; }
+    const uint32_t o = ord_key(z);
+    if (o > bo || (o == bo && n0 + n < bi)) { bo = o; bi = n0 + n; }
+  }
+#pragma unroll
+  for (int off = 1; off < 4; off <<= 1) {
+    const uint32_t o2 = __shfl_xor(bo, off);
+    const int i2 = __shfl_xor(bi, off);
+    if (o2 > bo || (o2 == bo && i2 < bi)) { bo = o2; bi = i2; }
+    nan |= __shfl_xor(nan, off);
+  }
+  if (li < nrows && q4 == 0) w.gpart[(int64_t)li * nn + nb] = make_uint2(nan ? 0xFFFFFFFFu : bo, (uint32_t)bi);
+}
+
+__global__ __launch_bounds__(64) void k_lm_greedy_final(LmArgs a, LmWs w, int nn, int32_t* out_acc,
+                                                        int32_t* out_tok, uint32_t* out_status,
+                                                        int32_t* out_argmax) {
+  const int r = blockIdx.x * 64 + threadIdx.x;
+  if (r >= a.B) return;
+  const int K1 = a.K_max + 1;
+  const int64_t base = (int64_t)r * K1;
+  uint32_t st = lm_status(a, r, false);
+  const int K = st ? 0 : req_k(a, r);
+  int g[SD_MAX_K + 1];
+  if (!st) {
+    const int t0 = w.toff[r];
+    for (int jj = 0; jj <= K; ++jj) {
+      uint32_t bo = 0u;
+      int bi = INT_MAX;
+      for (int t = 0; t < nn; ++t) {
+        const uint2 p = w.gpart[(int64_t)(t0 + jj) * nn + t];
+        if (p.x == 0xFFFFFFFFu) { st |= SD_ST_NONFINITE; continue; }
+        if (p.x > bo || (p.x == bo && (int)p.y < bi)) { bo = p.x; bi = (int)p.y; }
+      }
+      g[jj] = bi;
+    }
+  }
+  if (st & SD_ST_INVALID_MASK) {
+    for (int t = 0; t < K1; ++t) {
+      out_tok[base + t] = -1;
+      if (out_argmax) out_argmax[base + t] = -1;
+    }
+    out_acc[r] = -1;
+    if (out_status) out_status[r] = st;
+    return;
+  }
+  int n = K;
+  for (int jj = 0; jj < K; ++jj)
+    if (a.ids[(int64_t)r * a.K_max + jj] != g[jj]) { n = jj; break; }
+  for (int t = 0; t < K1; ++t) {
+    int v = -1;
+    if (t < n) v = a.ids[(int64_t)r * a.K_max + t];
+    else if (t == n && !(n == K && (a.flags & SD_NO_BONUS))) v = g[n];
+    out_tok[base + t] = v;
+    if (out_argmax) out_argmax[base + t] = t <= K ? g[t] : -1;
+  }
+  out_acc[r] = n;
+  if (out_status) out_status[r] = st;
+}
+
+// Test export: the logits of every listed row, written densely.
+template <bool TGT>
+__global__ __launch_bounds__(NT_L) void k_lm_dump(LmArgs a, LmWs w, int nm, int nn, float* out) {
+  __shared__ __align__(16) uint16_t sa[TM * LDK];
+  __shared__ __align__(16) uint16_t sb[TN * LDK];
+  __shared__ __align__(16) float C[TM * LDC];
+  int mb, nb;
+  if (!tile_of(nm, nn, mb, nb)) return;
+  const int nrows = w.cnt[TGT ? 0 : 1];
+  const int m0 = mb * TM, n0 = nb * TN;
+  if (m0 >= nrows) return;
+  const int* list = TGT ? w.tlist : w.dlist;
+  const int rr = threadIdx.x >> 3;
+  const uint16_t* arow[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int li = m0 + rr + 32 * i;
+    arow[i] = li < nrows ? hidden_row(a, TGT, list[li]) : nullptr;
+  }
+  const int Vs = TGT ? a.V : a.Vd;
+  f32x16 acc[2];
+  tile_gemm(arow, TGT ? a.wt : a.wd, n0, Vs, TGT ? a.Ht : a.Hd, TileLds{sa, sb}, acc);
+  __syncthreads();
+  stash(acc, C);
+  __syncthreads();
+  for (int i = threadIdx.x; i < TM * TN; i += NT_L) {
+    const int row = i / TN, n = i % TN;
+    if (m0 + row < nrows && n0 + n < Vs) out[(int64_t)list[m0 + row] * Vs + n0 + n] = C[row * LDC + n];
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Host side.
+// ---------------------------------------------------------------------------
+int lm_check(const sd_lmhead_args_t* s, bool sample) {
+  if (!s) return SD_EINVAL;
+  if (s->B < 1 || s->K_max < 0 || s->V < 1) return SD_EINVAL;
+  if (s->K_max > SD_MAX_K) return SD_EUNSUPPORTED;
+  if (!s->target_hidden || !s->target_weight) return SD_EINVAL;
+  if (s->H_target < BK || s->H_target % BK) return SD_EINVAL;
+  if ((reinterpret_cast<uintptr_t>(s->target_hidden) | reinterpret_cast<uintptr_t>(s->target_weight)) & 15u)
+    return SD_EINVAL;
+  if (s->K_max > 0 && !s->draft_ids) return SD_EINVAL;
+  if ((int64_t)s->B * (s->K_max + 1) > INT_MAX / 4) return SD_EUNSUPPORTED;
+  if ((s->flags & ~(uint32_t)SD_NO_BONUS)) return SD_EINVAL;
+  if (sample) {
+    if (s->V_draft < 0 || s->V_draft > s->V) return SD_EINVAL;
+    if (!(s->tv_budget >= 0.0f)) return SD_EINVAL;
+    if (s->K_max > 0) {
+      if (!s->draft_hidden || !s->draft_weight) return SD_EINVAL;
+      if (s->H_draft < BK || s->H_draft % BK) return SD_EINVAL;
+      if ((reinterpret_cast<uintptr_t>(s->draft_hidden) | reinterpret_cast<uintptr_t>(s->draft_weight)) & 15u)
+        return SD_EINVAL;
+    }
+  }
+  return SD_OK;
+}
+
+LmArgs lm_args(const sd_lmhead_args_t* s) {
+  LmArgs a;
+  a.th = static_cast<const uint16_t*>(s->target_hidden);
+  a.dh = static_cast<const uint16_t*>(s->draft_hidden);
+  a.wt = static_cast<const uint16_t*>(s->target_weight);
+  a.wd = static_cast<const uint16_t*>(s->draft_weight);
+  a.Ht = s->H_target;
+  a.Hd = s->H_draft > 0 ? s->H_draft : BK;
+  a.B = s->B;
+  a.K_max = s->K_max;
+  a.V = s->V;
+  a.Vd = s->V_draft > 0 ? s->V_draft : s->V;
+  a.ids = s->draft_ids;
+  a.kpr = s->k_per_row;
+  a.temp = s->temperature;
+  a.D = s->tv_budget;
+  a.seed = s->seed;
+  a.offset = s->offset;
+  a.flags = s->flags;
+  return a;
+}
+
+int lm_launch_status() { return hipGetLastError() == hipSuccess ? SD_OK : SD_EHIP; }
+
+// A 1-D grid of tile blocks, a multiple of the die count.
+unsigned tile_grid(int nm, int nn) {
+  const long long n = (long long)nm * nn;
+  return (unsigned)((n + NXCD - 1) / NXCD * NXCD);
+}
+
+int lm_prepare(const LmArgs& a, const LmLayout& L, const LmWs& w, bool sample, hipStream_t st) {
+  const int nt_max = a.B * (a.K_max + 1), nd_max = sample ? a.B * a.K_max : 0;
+  hipLaunchKernelGGL(k_lm_lists, dim3(1), dim3(1024), 0, st, a, w, sample ? 1 : 0);
+  if (sample) {
+    const int nmx = nt_max > nd_max ? nt_max : nd_max;
+    hipLaunchKernelGGL(k_lm_clear_zx, dim3((nmx + 255) / 256), dim3(256), 0, st, w, nt_max, nd_max);
+  }
+  (void)L;
+  return lm_launch_status();
+}
+
+}  // namespace
+
+extern "C" {
+
+int sd_lmhead_workspace_bytes(const sd_lmhead_args_t* args, size_t* bytes) {
+  if (!args || !bytes) return SD_EINVAL;
+  if (args->B < 1 || args->K_max < 0 || args->V < 1 || args->V_draft < 0 || args->V_draft > args->V)
+    return SD_EINVAL;
+  if (args->K_max > SD_MAX_K) return SD_EUNSUPPORTED;
+  *bytes = lm_layout(args->B, args->K_max, args->V, args->V_draft > 0 ? args->V_draft : args->V).total;
+  return SD_OK;
+}
+
+int sd_lmhead_verify_sample(const sd_lmhead_args_t* args, void* workspace, size_t workspace_bytes,
+                            int32_t* out_accepted, int32_t* out_tokens, uint32_t* out_status,
+                            float* out_stats, void* stream) {
+  int rc = lm_check(args, true);
+  if (rc) return rc;
+  if (!out_accepted || !out_tokens) return SD_EINVAL;
+  const LmArgs a = lm_args(args);
+  const LmLayout L = lm_layout(a.B, a.K_max, a.V, a.Vd);
+  if (!workspace || workspace_bytes < L.total) return SD_EWORKSPACE;
+  const LmWs w = carve(static_cast<char*>(workspace), L);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  rc = lm_prepare(a, L, w, true, st);
+  if (rc) return rc;
+  const int nt_max = a.B * (a.K_max + 1), nd_max = a.B * a.K_max;
+  const int nmt = (nt_max + TM - 1) / TM, nmd = (nd_max + TM - 1) / TM;
+  hipLaunchKernelGGL(k_lm_stats<true>, dim3(tile_grid(nmt, L.ntt)), dim3(NT_L), 0, st, a, w, nmt, L.ntt);
+  if (nd_max > 0)
+    hipLaunchKernelGGL(k_lm_stats<false>, dim3(tile_grid(nmd, L.ntd)), dim3(NT_L), 0, st, a, w, nmd, L.ntd);
+  hipLaunchKernelGGL(k_lm_rowstat<true>, dim3(nt_max), dim3(256), 0, st, a, w, L.ntt);
+  if (nd_max > 0)
+    hipLaunchKernelGGL(k_lm_rowstat<false>, dim3(nd_max), dim3(256), 0, st, a, w, L.ntd);
+  // d is needed where theta depends on it (0 < D < 1) or when statistics are asked for
+  const bool tv = nd_max > 0 && ((a.D > 0.0f && a.D < 1.0f) || out_stats);
+  if (tv) {
+    hipLaunchKernelGGL(k_lm_tv, dim3(tile_grid(nmd, L.ntt)), dim3(NT_L), 0, st, a, w, nmd, L.ntt);
+    hipLaunchKernelGGL(k_lm_tv_reduce, dim3(nd_max), dim3(256), 0, st, w, L.ntt);
+  }
+  hipLaunchKernelGGL(k_lm_decide, dim3((a.B + 63) / 64), dim3(64), 0, st, a, w, tv ? 1 : 0,
+                     out_accepted, out_tokens, out_status, out_stats);
+  const int nmr = (a.B + TM - 1) / TM;
+  hipLaunchKernelGGL(k_lm_draw_tiles, dim3(tile_grid(nmr, L.ntt)), dim3(NT_L), 0, st, a, w, nmr, L.ntt);
+  hipLaunchKernelGGL(k_lm_draw_pick, dim3(a.B), dim3(NT_L), 0, st, a, w, L.ntt, out_tokens,
+                     out_status, out_stats);
+  return lm_launch_status();
+}
+
+int sd_lmhead_verify_greedy(const sd_lmhead_args_t* args, void* workspace, size_t workspace_bytes,
+                            int32_t* out_accepted, int32_t* out_tokens, uint32_t* out_status,
+                            int32_t* out_argmax, void* stream) {
+  int rc = lm_check(args, false);
+  if (rc) return rc;
+  if (!out_accepted || !out_tokens) return SD_EINVAL;
+  const LmArgs a = lm_args(args);
+  const LmLayout L = lm_layout(a.B, a.K_max, a.V, a.Vd);
+  if (!workspace || workspace_bytes < L.total) return SD_EWORKSPACE;
+  const LmWs w = carve(static_cast<char*>(workspace), L);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  rc = lm_prepare(a, L, w, false, st);
+  if (rc) return rc;
+  const int nmt = (a.B * (a.K_max + 1) + TM - 1) / TM;
+  hipLaunchKernelGGL(k_lm_greedy_part, dim3(tile_grid(nmt, L.ntt)), dim3(NT_L), 0, st, a, w, nmt, L.ntt);
+  hipLaunchKernelGGL(k_lm_greedy_final, dim3((a.B + 63) / 64), dim3(64), 0, st, a, w, L.ntt,
+                     out_accepted, out_tokens, out_status, out_argmax);
+  return lm_launch_status();
+}
+
+int sd_debug_lmhead_logits(const sd_lmhead_args_t* args, void* workspace, size_t workspace_bytes,
+                           float* out_target, float* out_draft, void* stream) {
+  const bool sample = out_draft != nullptr;
+  int rc = lm_check(args, sample);
+  if (rc) return rc;
+  if (!out_target) return SD_EINVAL;
+  const LmArgs a = lm_args(args);
+  const LmLayout L = lm_layout(a.B, a.K_max, a.V, a.Vd);
+  if (!workspace || workspace_bytes < L.total) return SD_EWORKSPACE;
+  const LmWs w = carve(static_cast<char*>(workspace), L);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  rc = lm_prepare(a, L, w, sample, st);
+  if (rc) return rc;
+  const int nmt = (a.B * (a.K_max + 1) + TM - 1) / TM;
+  hipLaunchKernelGGL(k_lm_dump<true>, dim3(tile_grid(nmt, L.ntt)), dim3(NT_L), 0, st, a, w, nmt, L.ntt,
+                     out_target);
+  if (sample && a.K_max > 0) {
+    const int nmd = (a.B * a.K_max + TM - 1) / TM;
+    hipLaunchKernelGGL(k_lm_dump<false>, dim3(tile_grid(nmd, L.ntd)), dim3(NT_L), 0, st, a, w, nmd,
+                       L.ntd, out_draft);
+  }
+  return lm_launch_status();
+}
+
+}  // extern "C"
