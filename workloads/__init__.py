@@ -218,10 +218,11 @@ def config3(K=8, call=0, B=1, V=V_QWEN3):
                     np.full(B, K, dtype=np.int32), np.ones(B, np.float32))
 
 
-def config4_row(seed, r, K=8, V=V_QWEN25, n_prior=128, odd_share=0.0, V_draft=None):
+def config4_row(seed, r, K=8, V=V_QWEN25, n_prior=128, odd_share=0.0, V_draft=None,
+                T_range=(0.5, 1.0)):
     """One request row of config 4, from its own generator stream."""
     rng = np.random.default_rng([4, seed, r])
-    T = np.float32(rng.uniform(0.5, 1.0))
+    T = np.float32(rng.uniform(*T_range))
     t = rng.normal(0.0, 3.0, size=(K + 1, V)).astype(np.float32)
     dr = _corr_rows(rng, t[:K], 0.9, 3.0).astype(np.float32)
     if V_draft is not None:
@@ -235,7 +236,8 @@ def config4_row(seed, r, K=8, V=V_QWEN25, n_prior=128, odd_share=0.0, V_draft=No
 
 
 def config4(seed=0, B=256, K=8, V=V_QWEN25, n_prior=128, D=0.75,
-            philox_seed=0, top_p=0.9, rep_penalty=1.1, odd_share=0.0, V_draft=None):
+            philox_seed=0, top_p=0.9, rep_penalty=1.1, odd_share=0.0, V_draft=None,
+            T_range=(0.5, 1.0)):
     """The batched workload.  Proposals come from the draft's own sampler
     (odd_share = 0, the measured workload); parity runs add odd proposals.
     V_draft: a draft model with a shorter vocabulary (the pages' Qwen2.5
@@ -248,7 +250,7 @@ def config4(seed=0, B=256, K=8, V=V_QWEN25, n_prior=128, D=0.75,
     prior = np.empty((B, n_prior), dtype=np.int32)
     for r in range(B):
         tb[r], db[r], ids[r], T[r], prior[r] = config4_row(seed, r, K, V, n_prior, odd_share,
-                                                           V_draft)
+                                                           V_draft, T_range)
     offs = (np.arange(B + 1, dtype=np.int64) * n_prior).astype(np.int32)
     return Workload("config4", "bf16", tb, db, ids,
                     np.full(B, K, dtype=np.int32), T, top_p=top_p,
