@@ -1669,7 +1669,7 @@ __device__ __forceinline__ void fallback_unit(const Args& a, UnitOut* uo, int u)
   __shared__ uint32_t hcnt[HBINS];
   __shared__ uint64_t su[NT];
   __shared__ double sd[NT];
-  __shared__ double ctot[64];
+  __shared__ double ctot[(MAXV_FAST / VEC + WAVE - 1) / WAVE + 1];   // the draw's chunk totals
   __shared__ float sf[NT / WAVE];
   __shared__ int si[NT / WAVE + 4];
   __shared__ int s_acc;
@@ -2142,8 +2142,8 @@ int bitmap_words(int V) { return (V + 31) / 32; }
 size_t row_lds(int V) { return align_up((size_t)bitmap_words(V) * 4, 16) + exact_lds(V, NT_ROW); }
 
 size_t fin_lds(int V) {
-  const int nch = ((V + VEC - 1) / VEC + NT_ROW - 1) / NT_ROW;
-  return align_up((size_t)bitmap_words(V) * 4, 16) + (size_t)nch * 8;
+  const int nch = ((V + VEC - 1) / VEC + WAVE - 1) / WAVE;   // the draw's 64-vector chunks
+  return align_up((size_t)bitmap_words(V) * 4, 16) + (size_t)(nch + 1) * 8;
 }
 
 int launch_status() {

@@ -92,6 +92,25 @@ __device__ void find_crossing(const uint64_t* hm, const uint32_t* hc, int nbins,
   __syncthreads();
 }
 
+// Loads in flight per thread in the row passes below: each thread issues
+// the loads of RU strided vectors before it uses any of them.
+constexpr int RU = 4;
+
+// One pass over vectors k = threadIdx.x + i NT (i = 0, 1, ...) of a row of V
+// logits (nvec vectors of the pass; vectors past the row read as -inf):
+// f(k, z) for each, RU vectors loaded at a time, in ascending i per thread.
+template <int DT, int NT, class F>
+__device__ __forceinline__ void row_pass(const char* row, int V, int nvec, F&& f) {
+  for (int k0 = threadIdx.x; k0 < nvec; k0 += RU * NT) {
+    float z[RU][VEC];
+#pragma unroll
+    for (int u = 0; u < RU; ++u) load8_row<DT>(row, k0 + u * NT, k0 + u * NT < nvec ? V : 0, z[u]);
+#pragma unroll
+    for (int u = 0; u < RU; ++u)
+      if (k0 + u * NT < nvec) f(k0 + u * NT, z[u]);
+  }
+}
+
 // Statistics and top-p cut of one processed row, streaming it from global
 // memory: pass 0 gives the max M and Z = sum exp2((key - M) c) (online per
 // thread, fp64 totals); with top-p, three histogram passes over 12 + 12 + 8
@@ -105,25 +124,36 @@ __device__ __forceinline__ RowStat row_stats_dev(const Args& a, const char* row,
   float m = -INFINITY;
   double Z = 0.0;
   int bad = 0;
-  for (int k = threadIdx.x; k < nvec; k += NT) {
-    float z[VEC];
-    load8<DT>(row, k, V, z);
-    if (pen) apply_penalty8(bm, k, 0, a.rep, z);
+  // RU vectors per step: their loads in flight together, one max update
+  // (and fp64 rescale of Z) per step, the step's terms summed in fp32
+  for (int k0 = threadIdx.x; k0 < nvec; k0 += RU * NT) {
+    float z[RU][VEC];
+#pragma unroll
+    for (int u = 0; u < RU; ++u) load8_row<DT>(row, k0 + u * NT, k0 + u * NT < nvec ? V : 0, z[u]);
     float vm = -INFINITY;
 #pragma unroll
-    for (int e = 0; e < VEC; ++e) {
-      bad |= nonfinite(z[e]);
-      vm = fmaxf(vm, z[e]);
+    for (int u = 0; u < RU; ++u) {
+      if (pen && k0 + u * NT < nvec) apply_penalty8(bm, k0 + u * NT, 0, a.rep, z[u]);
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) {
+        bad |= nonfinite(z[u][e]);
+        vm = fmaxf(vm, z[u][e]);
+      }
     }
     if (vm > m) {
       if (m > -INFINITY) Z *= exp2(((double)m - (double)vm) * (double)c);
       m = vm;
     }
     if (m > -INFINITY) {
-      float s[VEC];
+      float su = 0.0f;
 #pragma unroll
-      for (int e = 0; e < VEC; ++e) s[e] = e_rel(z[e], m, c);
-      Z += (double)(((s[0] + s[1]) + (s[2] + s[3])) + ((s[4] + s[5]) + (s[6] + s[7])));
+      for (int u = 0; u < RU; ++u) {
+        float s[VEC];
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) s[e] = e_rel(z[u][e], m, c);
+        su += ((s[0] + s[1]) + (s[2] + s[3])) + ((s[4] + s[5]) + (s[6] + s[7]));
+      }
+      Z += (double)su;
     }
   }
   const float M = block_max<NT>(m, L.sf);
@@ -155,9 +185,7 @@ __device__ __forceinline__ RowStat row_stats_dev(const Args& a, const char* row,
   for (int b = threadIdx.x; b < HBINS; b += NT) { L.hmass[b] = 0; L.hcnt[b] = 0; }
   __syncthreads();
   uint64_t zfp = 0;
-  for (int k = threadIdx.x; k < nvec; k += NT) {
-    float z[VEC];
-    load8<DT>(row, k, V, z);
+  row_pass<DT, NT>(row, V, nvec, [&](int k, float (&z)[VEC]) {
     if (pen) apply_penalty8(bm, k, 0, a.rep, z);
 #pragma unroll
     for (int e = 0; e < VEC; ++e) {
@@ -170,7 +198,7 @@ __device__ __forceinline__ RowStat row_stats_dev(const Args& a, const char* row,
         if (ef) atomicAdd(reinterpret_cast<unsigned long long*>(&L.hmass[b]), (unsigned long long)ef);
       }
     }
-  }
+  });
   const uint64_t Zfp = block_sum_u64<NT>(zfp, L.su);
   const double TP = tp * (double)Zfp;
   int b1;
@@ -180,9 +208,7 @@ __device__ __forceinline__ RowStat row_stats_dev(const Args& a, const char* row,
   // Level 2: ord bits [19:8] among tokens of bin b1.
   for (int b = threadIdx.x; b < HBINS; b += NT) { L.hmass[b] = 0; L.hcnt[b] = 0; }
   __syncthreads();
-  for (int k = threadIdx.x; k < nvec; k += NT) {
-    float z[VEC];
-    load8<DT>(row, k, V, z);
+  row_pass<DT, NT>(row, V, nvec, [&](int k, float (&z)[VEC]) {
     if (pen) apply_penalty8(bm, k, 0, a.rep, z);
 #pragma unroll
     for (int e = 0; e < VEC; ++e) {
@@ -194,18 +220,24 @@ __device__ __forceinline__ RowStat row_stats_dev(const Args& a, const char* row,
       const uint64_t ef = e_fixed(e_rel(z[e], M, c), sh);
       if (ef) atomicAdd(reinterpret_cast<unsigned long long*>(&L.hmass[b]), (unsigned long long)ef);
     }
-  }
+  });
   __syncthreads();
   int b2;
   find_crossing<NT>(L.hmass, L.hcnt, HBINS, above, TP, b2, above, L.su, L.si);
   const uint32_t pre24 = ((uint32_t)b1 << 12) | (uint32_t)b2;
+  if (DT == SD_BF16 && !pen) {
+    // bf16 keys have zero low 16 bits: the 24-bit prefix is the whole key
+    // (a penalized key is an fp32 quotient or product, so not with a penalty)
+    out.kord = pre24 << 8;
+    out.Zk = (double)(above + L.hmass[b2]) * exp2(-(double)sh);
+    __syncthreads();
+    return out;
+  }
 
   // Level 3: ord bits [7:0] among tokens with the 24-bit prefix.
   for (int b = threadIdx.x; b < 256; b += NT) { L.hmass[b] = 0; L.hcnt[b] = 0; }
   __syncthreads();
-  for (int k = threadIdx.x; k < nvec; k += NT) {
-    float z[VEC];
-    load8<DT>(row, k, V, z);
+  row_pass<DT, NT>(row, V, nvec, [&](int k, float (&z)[VEC]) {
     if (pen) apply_penalty8(bm, k, 0, a.rep, z);
 #pragma unroll
     for (int e = 0; e < VEC; ++e) {
@@ -216,7 +248,7 @@ __device__ __forceinline__ RowStat row_stats_dev(const Args& a, const char* row,
       const uint64_t ef = e_fixed(e_rel(z[e], M, c), sh);
       if (ef) atomicAdd(reinterpret_cast<unsigned long long*>(&L.hmass[o & 0xFFu]), (unsigned long long)ef);
     }
-  }
+  });
   __syncthreads();
   int b3;
   find_crossing<NT>(L.hmass, L.hcnt, 256, above, TP, b3, above, L.su, L.si);
@@ -235,21 +267,30 @@ __device__ __forceinline__ double pair_tv_dev(const Args& a, const char* trow, c
   const int V = a.V, nvec = (V + VEC - 1) / VEC;
   const float ip = (float)(1.0 / P.Zk), iq = (float)(1.0 / Q.Zk);
   double acc = 0.0;
-  for (int k = threadIdx.x; k < nvec; k += NT) {
-    float zp[VEC], zq[VEC];
-    load8<DT>(trow, k, V, zp);
-    load8_row<DT>(drow, k, a.Vd, zq);
-    if (pen) {
-      apply_penalty8(bm, k, 0, a.rep, zp);
-      apply_penalty8(bm, k, 0, a.rep, zq);
+  for (int k0 = threadIdx.x; k0 < nvec; k0 += RU * NT) {
+    float zp[RU][VEC], zq[RU][VEC];
+#pragma unroll
+    for (int u = 0; u < RU; ++u) {
+      const int k = k0 + u * NT;
+      load8_row<DT>(trow, k, k < nvec ? V : 0, zp[u]);
+      load8_row<DT>(drow, k, k < nvec ? a.Vd : 0, zq[u]);
     }
     float s = 0.0f;
 #pragma unroll
-    for (int e = 0; e < VEC; ++e) {
-      const int id = k * VEC + e;
-      const float p = (id < V && kept(P, ord_key(zp[e]))) ? e_rel(zp[e], P.M, P.c) * ip : 0.0f;
-      const float q = (id < a.Vd && kept(Q, ord_key(zq[e]))) ? e_rel(zq[e], Q.M, Q.c) * iq : 0.0f;
-      s += fabsf(p - q);
+    for (int u = 0; u < RU; ++u) {
+      const int k = k0 + u * NT;
+      if (k >= nvec) continue;
+      if (pen) {
+        apply_penalty8(bm, k, 0, a.rep, zp[u]);
+        apply_penalty8(bm, k, 0, a.rep, zq[u]);
+      }
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) {
+        const int id = k * VEC + e;
+        const float p = (id < V && kept(P, ord_key(zp[u][e]))) ? e_rel(zp[u][e], P.M, P.c) * ip : 0.0f;
+        const float q = (id < a.Vd && kept(Q, ord_key(zq[u][e]))) ? e_rel(zq[u][e], Q.M, Q.c) * iq : 0.0f;
+        s += fabsf(p - q);
+      }
     }
     acc += (double)s;
   }
@@ -262,106 +303,133 @@ struct Drawn {
   int resid_zero;
 };
 
-// Inverse-CDF draw over ascending token ids with fp64 block prefix sums:
-// mode 0 draws from max(p - q, 0) (falling back to p when that has no
-// mass), mode 1 from p.  Two streaming passes give the chunk totals, then
-// the chunk holding t = v * S is read once more and scanned.
+// Inverse-CDF draw over ascending token ids with fp64 prefix sums: mode 0
+// draws from max(p - q, 0) (falling back to p when that has no mass), mode
+// 1 from p.  One coalesced pass (RU vectors in flight per thread) writes the
+// total of every chunk of 64 consecutive vectors (a wave's share of one
+// step) to L.ctot (nch + 1 doubles: the last holds the mass before the
+// crossing chunk); a block scan over the chunk totals finds the chunk that
+// holds t = v S; wave 0 reads that chunk again and scans it lane by lane;
+// the crossing lane walks its 8 tokens.  Every sum is fp64 in a fixed order.
 template <int DT, int NT>
 __device__ __forceinline__ Drawn draw_dev(const Args& a, const char* trow, const char* drow, const RowStat& P,
                           const RowStat& Q, int mode, float v, bool pen, const uint32_t* bm,
                           const ExactLds& L) {
   const int V = a.V, nvec = (V + VEC - 1) / VEC;
-  const int nch = (nvec + NT - 1) / NT;
+  const int nch = (nvec + WAVE - 1) / WAVE;
+  const int lane = threadIdx.x % WAVE, wv = threadIdx.x / WAVE;
   const float ip = (float)(1.0 / P.Zk), iq = (float)(1.0 / Q.Zk);
   Drawn out;
   out.resid_zero = 0;
 
-  auto own_sum = [&](int k, int md, float (&w)[VEC]) -> double {
+  // fp64 total of the draw weights of vector k (0 past the row)
+  auto vec_sum = [&](int k, int md, float (&zp)[VEC], float (&zq)[VEC], float (&w)[VEC]) -> double {
     double s = 0.0;
-    if (k < nvec) {
-      float zp[VEC], zq[VEC];
-      load8<DT>(trow, k, V, zp);
-      if (pen) apply_penalty8(bm, k, 0, a.rep, zp);
-      if (md == 0) {
-        load8_row<DT>(drow, k, a.Vd, zq);
-        if (pen) apply_penalty8(bm, k, 0, a.rep, zq);
-      }
-#pragma unroll
-      for (int e = 0; e < VEC; ++e) {
-        const int id = k * VEC + e;
-        float p = (id < V && kept(P, ord_key(zp[e]))) ? e_rel(zp[e], P.M, P.c) * ip : 0.0f;
-        if (md == 0) {
-          const float q = (id < a.Vd && kept(Q, ord_key(zq[e]))) ? e_rel(zq[e], Q.M, Q.c) * iq : 0.0f;
-          p = fmaxf(p - q, 0.0f);
-        }
-        w[e] = p;
-        s += (double)p;
-      }
-    } else {
+    if (k >= nvec) {
 #pragma unroll
       for (int e = 0; e < VEC; ++e) w[e] = 0.0f;
+      return s;
+    }
+    if (pen) apply_penalty8(bm, k, 0, a.rep, zp);
+    if (md == 0 && pen) apply_penalty8(bm, k, 0, a.rep, zq);
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) {
+      const int id = k * VEC + e;
+      float p = (id < V && kept(P, ord_key(zp[e]))) ? e_rel(zp[e], P.M, P.c) * ip : 0.0f;
+      if (md == 0) {
+        const float q = (id < a.Vd && kept(Q, ord_key(zq[e]))) ? e_rel(zq[e], Q.M, Q.c) * iq : 0.0f;
+        p = fmaxf(p - q, 0.0f);
+      }
+      w[e] = p;
+      s += (double)p;
     }
     return s;
   };
+  auto load2 = [&](int k, int md, float (&zp)[VEC], float (&zq)[VEC]) {
+    load8_row<DT>(trow, k, k < nvec ? V : 0, zp);
+    if (md == 0) load8_row<DT>(drow, k, k < nvec ? a.Vd : 0, zq);
+  };
 
-  double S = 0.0, t = 0.0, R = 0.0;
-  int chs = -1;
+  double S = 0.0, t = 0.0;
   for (int pass = 0; pass < 2; ++pass) {
-    for (int ch = 0; ch < nch; ++ch) {
-      float w[VEC];
-      const double own = own_sum(ch * NT + threadIdx.x, mode, w);
-      const double incl = block_incl_scan<NT>(own, L.sd);
-      if (threadIdx.x == NT - 1) L.ctot[ch] = incl;
+    // chunk totals: every wave runs every step (the wave sums need all lanes)
+    for (int base = 0; base < nvec; base += RU * NT) {
+      float zp[RU][VEC], zq[RU][VEC];
+#pragma unroll
+      for (int u = 0; u < RU; ++u) load2(base + u * NT + (int)threadIdx.x, mode, zp[u], zq[u]);
+#pragma unroll
+      for (int u = 0; u < RU; ++u) {
+        float w[VEC];
+        const double ls = vec_sum(base + u * NT + (int)threadIdx.x, mode, zp[u], zq[u], w);
+        const double cs = wave_sum(ls);
+        const int ch = (base + u * NT) / WAVE + wv;
+        if (lane == 0 && ch < nch) L.ctot[ch] = cs;
+      }
     }
     __syncthreads();
-    // every thread reads the same totals in the same order
-    S = 0.0;
-    for (int ch = 0; ch < nch; ++ch) S += L.ctot[ch];
+    // block scan over the chunk totals (thread t owns chunks t per ..)
+    const int per = (nch + NT - 1) / NT;
+    const int c0 = min((int)threadIdx.x * per, nch), c1 = min(c0 + per, nch);
+    double own = 0.0;
+    for (int ch = c0; ch < c1; ++ch) own += L.ctot[ch];
+    const double incl = block_incl_scan_fast<NT>(own, L.sd);
+    __syncthreads();   // the scan's reads of its wave totals are done
+    L.sd[threadIdx.x] = incl;
+    if (threadIdx.x == 0) { L.si[0] = -1; L.si[1] = -1; }
+    __syncthreads();
+    // the previous thread's inclusive total is this thread's exclusive one,
+    // exactly: the crossing thread below is unique and exists when S > 0
+    const double excl = threadIdx.x ? L.sd[threadIdx.x - 1] : 0.0;
+    S = L.sd[NT - 1];
     t = (double)v * S;
-    double Racc = 0.0, Rlast = 0.0;
-    int lastpos = -1;
-    chs = -1;
-    for (int ch = 0; ch < nch; ++ch) {
-      if (L.ctot[ch] > 0.0) { lastpos = ch; Rlast = Racc; }
-      if (chs < 0 && Racc + L.ctot[ch] > t) { chs = ch; R = Racc; }
-      Racc += L.ctot[ch];
-    }
-    if (chs < 0) { chs = lastpos; R = Rlast; }
-    __syncthreads();
     if (!(S > 0.0) && mode == 0) {   // zero residual: draw from p
+      __syncthreads();
       mode = 1;
       out.resid_zero = 1;
       continue;
     }
+    // the crossing chunk and the mass before it (one thread)
+    if (S > 0.0 && incl > t && excl <= t) {
+      double R = excl;
+      int cs = c1 - 1;
+      for (int ch = c0; ch < c1; ++ch) {
+        if (R + L.ctot[ch] > t) { cs = ch; break; }
+        R += L.ctot[ch];
+      }
+      L.si[0] = cs;
+      L.ctot[nch] = R;
+    }
+    __syncthreads();
     break;
   }
   out.S = S;
-  out.y = -1;
-  if (chs >= 0) {
-    float w[VEC];
-    const int k = chs * NT + threadIdx.x;
-    const double own = own_sum(k, mode, w);
-    const double incl = block_incl_scan<NT>(own, L.sd);
-    const double prev = threadIdx.x ? L.sd[threadIdx.x - 1] : 0.0;
-    __syncthreads();
-    if (threadIdx.x == 0) { L.si[0] = INT_MAX; L.si[1] = -1; }
-    __syncthreads();
-    if (R + incl > t) atomicMin(&L.si[0], (int)threadIdx.x);
-    __syncthreads();
-    if ((int)threadIdx.x == L.si[0]) {
-      double C = R + prev;
+  const int cs = L.si[0];
+  if (wv == 0 && cs >= 0) {
+    const int k = cs * WAVE + lane;
+    float zp[VEC], zq[VEC], w[VEC];
+    load2(k, mode, zp, zq);
+    const double ls = vec_sum(k, mode, zp, zq, w);
+    const double li = wave_incl_scan(ls);
+    const double R = L.ctot[nch];
+    const uint64_t hit = __ballot(R + li > t);
+    // the first lane whose inclusive total exceeds t, else (rounding) the
+    // last lane that carries weight
+    const uint64_t pos = __ballot(ls > 0.0);
+    const int src = hit ? __builtin_ctzll(hit) : (pos ? 63 - __builtin_clzll(pos) : -1);
+    if (lane == src) {
+      double C = R + li - ls;
       int y = -1, lastpos = -1;
       for (int e = 0; e < VEC; ++e) {
         if (w[e] > 0.0f) lastpos = k * VEC + e;
         C += (double)w[e];
-        if (C > t) { y = k * VEC + e; break; }
+        if (C > t && hit) { y = k * VEC + e; break; }
       }
       L.si[1] = (y >= 0) ? y : lastpos;
     }
-    __syncthreads();
-    out.y = L.si[1];
-    __syncthreads();
   }
+  __syncthreads();
+  out.y = L.si[1];
+  __syncthreads();
   return out;
 }
 
