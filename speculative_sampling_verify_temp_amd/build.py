@@ -37,16 +37,36 @@ def hipcc():
 
 
 def build(verbose=False):
-    """Compile every HIP source into libsdverify.so (always rebuilds)."""
+    """Compile every HIP source (side by side) and link them into
+    libsdverify.so (always rebuilds)."""
+    tmpdir = LIB + ".objs"
+    os.makedirs(tmpdir, exist_ok=True)
+    objs, procs = [], []
+    for src in SOURCES:
+        obj = os.path.join(tmpdir, os.path.splitext(src)[0] + ".o")
+        cmd = [hipcc(), *[f for f in HIPCC_FLAGS if f != "-shared"], "-c", f"-I{INCLUDE}",
+               f"-I{CSRC}", os.path.join(CSRC, src), "-o", obj]
+        if verbose:
+            print(" ".join(cmd))
+        procs.append((src, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT,
+                                            text=True)))
+        objs.append(obj)
+    failed = []
+    for src, pr in procs:
+        out, _ = pr.communicate()
+        if pr.returncode != 0:
+            failed.append(f"hipcc failed on {src}:\n{out}")
+    if failed:
+        raise RuntimeError("\n".join(failed))
     tmp = LIB + ".tmp"
-    cmd = [hipcc(), *HIPCC_FLAGS, f"-I{INCLUDE}", f"-I{CSRC}",
-           *[os.path.join(CSRC, s) for s in SOURCES], "-o", tmp]
+    cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
     if verbose:
         print(" ".join(cmd))
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
-        raise RuntimeError("hipcc failed:\n" + res.stdout + res.stderr)
+        raise RuntimeError("link failed:\n" + res.stdout + res.stderr)
     os.replace(tmp, LIB)
+    shutil.rmtree(tmpdir, ignore_errors=True)
     return LIB
 
 

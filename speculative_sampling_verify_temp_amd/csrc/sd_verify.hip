@@ -2156,11 +2156,21 @@ bool use_fast(const Args& a) {
   return a.dtype == SD_BF16 && (a.tpr || a.top_p < 1.0f) && a.V <= MAXV_FAST;
 }
 
+// LDS of the general row pass: the penalty bitmap only with a penalty, the
+// radix-select histograms only when some request truncates (top-p < 1).
+size_t prepare_lds(const Args& a) {
+  const bool topp = a.tpr || a.top_p < 1.0f;
+  const size_t bm = align_up((size_t)bitmap_words(a.V) * 4, 16);
+  if (topp) return bm + exact_lds(a.V, NT_ROW);
+  return a.rep != 1.0f ? bm : 0;
+}
+
 template <int DT>
 int run_prepare(const Args& a, const Layout& L, char* ws, hipStream_t st) {
   const int grid = a.B * (2 * a.K_max + 1);
-  hipLaunchKernelGGL(k_row_prepare<DT>, dim3(grid), dim3(NT_ROW), row_lds(a.V), st, a,
-                     reinterpret_cast<RowStat*>(ws + L.rs), bitmap_words(a.V));
+  const int bmw = (a.rep != 1.0f || a.tpr || a.top_p < 1.0f) ? bitmap_words(a.V) : 0;
+  hipLaunchKernelGGL(k_row_prepare<DT>, dim3(grid), dim3(NT_ROW), prepare_lds(a), st, a,
+                     reinterpret_cast<RowStat*>(ws + L.rs), bmw);
   return launch_status();
 }
 
@@ -2197,7 +2207,7 @@ int run_phase(const Args& a, const Layout& L, char* ws, int phase, int32_t* acc,
   if (phase == 1) {
     if (!need_tv || a.K_max == 0) return SD_OK;
     hipLaunchKernelGGL(k_pair_tv<DT>, dim3(a.B * a.K_max), dim3(NT_ROW),
-                       align_up((size_t)bitmap_words(a.V) * 4, 16), st, a,
+                       a.rep != 1.0f ? align_up((size_t)bitmap_words(a.V) * 4, 16) : 0, st, a,
                        reinterpret_cast<const RowStat*>(ws + L.rs),
                        reinterpret_cast<double*>(ws + L.dtv));
     return launch_status();

@@ -135,15 +135,16 @@ __device__ __forceinline__ RowStat row_stats_dev(const Args& a, const char* row,
     for (int u = 0; u < RU; ++u) {
       if (pen && k0 + u * NT < nvec) apply_penalty8(bm, k0 + u * NT, 0, a.rep, z[u]);
 #pragma unroll
-      for (int e = 0; e < VEC; ++e) {
-        bad |= nonfinite(z[u][e]);
-        vm = fmaxf(vm, z[u][e]);
-      }
+      for (int e = 0; e < VEC; ++e) vm = fmaxf(vm, z[u][e]);
     }
     if (vm > m) {
       if (m > -INFINITY) Z *= exp2(((double)m - (double)vm) * (double)c);
       m = vm;
     }
+    // Non-finite logits need no test per element: +inf becomes the max
+    // (caught below), and a NaN turns its term, hence Z, into NaN once the
+    // running max is finite; only a NaN met while every logit so far is
+    // -inf is looked for explicitly.
     if (m > -INFINITY) {
       float su = 0.0f;
 #pragma unroll
@@ -154,13 +155,18 @@ __device__ __forceinline__ RowStat row_stats_dev(const Args& a, const char* row,
         su += ((s[0] + s[1]) + (s[2] + s[3])) + ((s[4] + s[5]) + (s[6] + s[7]));
       }
       Z += (double)su;
+    } else {
+#pragma unroll
+      for (int u = 0; u < RU; ++u)
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) bad |= z[u][e] != z[u][e];
     }
   }
   const float M = block_max<NT>(m, L.sf);
   Z = (m > -INFINITY) ? Z * exp2(((double)m - (double)M) * (double)c) : 0.0;
   const double Zall = block_sum<NT>(Z, L.sd);
   bad = block_or<NT>(bad, L.si);
-  if (!(M > -INFINITY)) bad = 1;
+  if (!(M > -INFINITY) || !(M < INFINITY) || Zall != Zall) bad = 1;
 
   RowStat out;
   out.M = M;
