@@ -397,7 +397,10 @@ constexpr int NSAMP = 4;                     // rounds whose block max anchors a
 constexpr int NSTG = 5;                      // 16-byte loads in flight per thread
 constexpr int UP = 32;                       // window bins above the sample max
 constexpr int NBIN = 256;                    // codes 0..255
-constexpr int NCOPY = 16;                    // histogram copies (bank spreading)
+constexpr int NBINW = 8192;                  // bins of a row's key histogram
+constexpr int RUP = 4096;                    // exact bins from the window's top key down
+constexpr int RNEG = 4094;                   // exact bins below the lumped band
+static_assert(RUP + RNEG + 2 <= NBINW && RUP > NBIN, "histogram geometry");
 constexpr int E_CAP = 512;                   // exact-key entries per row
 constexpr int R_CAP = 64;                    // exact entries in the crossing bin
 constexpr int CAPT = 20;                     // nucleus slots per lane
@@ -450,10 +453,11 @@ struct Cut {
 // visited from the top; the first non-empty bin whose cumulative mass
 // reaches TP is the crossing bin.  A crossing bin that holds exact entries
 // is resolved key by key, ties kept together.  A bin's count is
-// hsum - hneg (the folded histogram less the penalized logits that left
-// it); ecnt / emass (count and fixed-point mass of exact entries per bin)
-// start at zero.  Lane L owns bins 4L .. 4L+3.
-__device__ __forceinline__ Cut wave_cut(const uint32_t* hsum, const uint32_t* hneg, const ExactList& ex,
+// hist - hneg (the row's key histogram, whose bins 1..254 are the window,
+// less the penalized logits that left it); ecnt / emass (count and
+// fixed-point mass of exact entries per bin) start at zero.  Lane L owns
+// bins 4L .. 4L+3.
+__device__ __forceinline__ Cut wave_cut(const uint32_t* hist, const uint32_t* hneg, const ExactList& ex,
                                         int ns, int np,
                                         const uint32_t* bm, bool pen, uint32_t t1, float M, float c,
                                         double TP, uint32_t* ecnt, uint64_t* emass, float* rkey,
@@ -477,7 +481,7 @@ __device__ __forceinline__ Cut wave_cut(const uint32_t* hsum, const uint32_t* hn
   uint32_t cnt[4], ec[4];
   double mass[4];
   double lsum = 0.0;
-  const uint4 hs = reinterpret_cast<const uint4*>(hsum)[lane];
+  const uint4 hs = reinterpret_cast<const uint4*>(hist)[lane];
   const uint4 hn = reinterpret_cast<const uint4*>(hneg)[lane];
   const uint32_t hc[4] = {hs.x - hn.x, hs.y - hn.y, hs.z - hn.z, hs.w - hn.w};
 #pragma unroll
@@ -665,14 +669,10 @@ struct Vec8 {
   uint32_t w[4];
 };
 
-// POS: every key of the row's window is positive.  Then the orderable key
-// of a positive logit is its bits with the sign flipped, and a negative
-// logit only needs some key below the window, which the same flip gives;
-// one operation per word instead of two.
 // TAIL false: the row holds a multiple of 8 logits and every vector streamed
 // lies inside it, so no vector needs masking.  V: logits the row holds (a
 // draft row may hold fewer than the vocabulary).
-template <bool POS = false, bool TAIL = true>
+template <bool TAIL = true>
 __device__ __forceinline__ void vec8(const uint4& ld, int l, int k, int V, Vec8& v) {
   v.w[0] = ld.x;
   v.w[1] = ld.y;
@@ -697,7 +697,7 @@ __device__ __forceinline__ void vec8(const uint4& ld, int l, int k, int V, Vec8&
   for (int e = 0; e < 4; ++e) {
     v.z[2 * e] = __uint_as_float(v.w[e] << 16);
     v.z[2 * e + 1] = __uint_as_float(v.w[e] & 0xFFFF0000u);
-    v.o[e] = POS ? (v.w[e] ^ 0x80008000u) : ord16x2(v.w[e]);
+    v.o[e] = ord16x2(v.w[e]);
   }
 }
 
@@ -715,9 +715,9 @@ __device__ __forceinline__ float max8(const float (&z)[VEC]) {
 // Per-lane running state of one row's stream.
 struct RowAcc {
   uint32_t mo;     // packed 16-bit orderable keys: max of the logits as read
+  uint32_t lo;     // and their min (a key below that of -inf is a NaN)
   float mpen;      // max of the penalized keys (after the stream)
-  double Z;        // sum of exp2(key c - anchor c)
-  float zf;        // the part of it not yet added to Z (at most two rounds)
+  double Z;        // the penalty's changes to the normalizer (sum of exp2(key c - anchor c))
 };
 
 typedef __attribute__((address_space(3))) uint32_t lds_u32;
@@ -727,37 +727,94 @@ __device__ __forceinline__ uint32_t lds_addr(const uint32_t* p) {
   return (uint32_t)(size_t)(const lds_u32*)p;
 }
 
-// c + 64 * (16-bit half of a): the LDS address of a logit's histogram word
-// from its code (64 bytes per bin: NCOPY copies) and the lane's copy.
-__device__ __forceinline__ uint32_t bin_addr_lo(uint32_t a, uint32_t c) {
+// 4 * (16-bit half of a): the byte offset of a histogram word from its bin.
+__device__ __forceinline__ uint32_t bin_addr_lo(uint32_t a) {
   uint32_t d;
-  asm("v_mad_u32_u16 %0, %1, 64, %2" : "=v"(d) : "v"(a), "v"(c));
+  asm("v_mad_u32_u16 %0, %1, 4, 0" : "=v"(d) : "v"(a));
   return d;
 }
-__device__ __forceinline__ uint32_t bin_addr_hi(uint32_t a, uint32_t c) {
+__device__ __forceinline__ uint32_t bin_addr_hi(uint32_t a) {
   uint32_t d;
-  asm("v_mad_u32_u16 %0, %1, 64, %2 op_sel:[1,0,0,0]" : "=v"(d) : "v"(a), "v"(c));
+  asm("v_mad_u32_u16 %0, %1, 4, 0 op_sel:[1,0,0,0]" : "=v"(d) : "v"(a));
   return d;
 }
 
-// Streaming work of one vector of a row against its window: normalizer,
-// max, codes, histogram, exact entries for keys above the window.  Every
-// logit is streamed as read; pen_fix settles the penalized ones afterwards.
+// The key histogram of a row.  A logit's distance below the window's top,
+// d = t1 - (its 16-bit orderable key), picks its bin: d < RUP, bin d (one
+// bf16 key each: bins 1..254 are the window's codes, bin 0 the keys above
+// it, whose counts are not used); then one lumped bin for the band of keys
+// of magnitude below 2^-20 that the upper range does not reach (d in
+// [RUP, R2)); then RNEG bins of one key each (d in [R2, R3)); then one
+// bin for everything below (d >= R3, -inf included).  The row's normalizer
+// is the sum over bins of count x the bin's term, so the stream takes no
+// exponential per logit; the two lumped bins carry an error bound that the
+// cut checks.
+struct Bins {
+  uint32_t r3x2, wx2;   // packed R3 and R2 - RUP - 1 (the band's width less one)
+  int r2, r3;
+};
+
+__device__ __forceinline__ Bins row_bins(uint32_t t1) {
+  Bins b;
+  const int dneg = (int)t1 - (int)ord16f(-0x1p-20f);   // d of the key -2^-20
+  b.r2 = max(RUP + 1, dneg + 1);
+  b.r3 = min(b.r2 + RNEG, 0xFFFF);
+  b.r3x2 = (uint32_t)b.r3 * 0x00010001u;
+  b.wx2 = (uint32_t)(b.r2 - RUP - 1) * 0x00010001u;
+  return b;
+}
+
+// Bins of two logits from their packed distances d.
+__device__ __forceinline__ uint32_t bins_of(uint32_t d, const Bins& b) {
+  const u16x2 dv = as_u16x2(d);
+  const u16x2 m1 = __builtin_elementwise_min(dv, as_u16x2(b.r3x2));
+  const u16x2 m2 = __builtin_elementwise_min(
+      __builtin_elementwise_sub_sat(dv, (u16x2){(uint16_t)RUP, (uint16_t)RUP}), as_u16x2(b.wx2));
+  return as_u32(m1 - m2);
+}
+
+// Distance below the window's top (t1 - key) of bin i, or -1 for the two
+// lumped bins and unused bins.
+__device__ __forceinline__ int bin_dist(int i, const Bins& b) {
+  if (i < RUP) return i;
+  if (i == RUP) return -1;
+  const int d = b.r2 + (i - RUP - 1);
+  return d < b.r3 ? d : -1;
+}
+
+// Streaming work of one vector of a row against its window: max, codes,
+// key histogram, exact entries for keys above the window.  Every logit is
+// streamed as read; pen_fix settles the penalized ones afterwards.
 // Returns the two code words: the codes of the even elements 0, 2, 4, 6
 // and of the odd ones 1, 3, 5, 7 (one byte each, in that order).
 // SAMPLED: the vector is in one of the rounds whose block max set the
-// anchor, so no key of it is above the window or above the max that the
-// caller started acc.mo from (non-finite logits show in the normalizer).
+// anchor, so no finite key of it is above the window.
 template <bool SAMPLED = false>
-__device__ __forceinline__ uint2 row_vec(Vec8& v, int k, float c, float gc, uint32_t t1,
-                                         uint32_t* hist, uint32_t hlane, const ExactList& ex,
-                                         RowAcc& acc) {
+__device__ __forceinline__ uint2 row_vec(Vec8& v, int k, uint32_t t1, const Bins& bn,
+                                         uint32_t* hist, const ExactList& ex, RowAcc& acc) {
   const uint32_t t1x2 = t1 | (t1 << 16);
+  typedef __attribute__((address_space(3))) char lds_char;
+  lds_char* const hb = (lds_char*)(lds_u32*)hist;
   uint32_t cc[4];
 #pragma unroll
-  for (int e = 0; e < 4; ++e) cc[e] = code_of(t1x2, v.o[e]);
-  const uint32_t vo = SAMPLED ? 0u : pk_max(pk_max(v.o[0], v.o[1]), pk_max(v.o[2], v.o[3]));
-  if (!SAMPLED) acc.mo = pk_max(acc.mo, vo);
+  for (int e = 0; e < 4; ++e) {
+    // distance, code and bin of the pair, its two counts out at once (each
+    // pair's temporaries die before the next pair's are made)
+    const uint32_t dd = as_u32(__builtin_elementwise_sub_sat(as_u16x2(t1x2), as_u16x2(v.o[e])));
+    cc[e] = as_u32(__builtin_elementwise_min(as_u16x2(dd), (u16x2){255, 255}));
+    const uint32_t bb = bins_of(dd, bn);
+    __hip_atomic_fetch_add((lds_u32*)(hb + bin_addr_lo(bb)), 1u, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_WORKGROUP);
+    __hip_atomic_fetch_add((lds_u32*)(hb + bin_addr_hi(bb)), 1u, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_WORKGROUP);
+    SDV_PIN(cc[e]);
+  }
+  acc.lo = as_u32(__builtin_elementwise_min(
+      as_u16x2(acc.lo),
+      __builtin_elementwise_min(__builtin_elementwise_min(as_u16x2(v.o[0]), as_u16x2(v.o[1])),
+                                __builtin_elementwise_min(as_u16x2(v.o[2]), as_u16x2(v.o[3])))));
+  const uint32_t vo = pk_max(pk_max(v.o[0], v.o[1]), pk_max(v.o[2], v.o[3]));
+  acc.mo = pk_max(acc.mo, vo);
   if (!SAMPLED &&
       as_u32(__builtin_elementwise_sub_sat(as_u16x2(vo), as_u16x2(t1x2 - 0x00010001u))) != 0u) {
     // Keys above the window (code 0) become exact entries.  Bit 2h + 16i of
@@ -773,20 +830,6 @@ __device__ __forceinline__ uint2 row_vec(Vec8& v, int k, float c, float gc, uint
       const uint32_t raw = (wd >> (16 * i)) & 0xFFFFu;
       exact_push(ex, __uint_as_float(raw << 16), k * VEC + 2 * h + i, raw);
     }
-  }
-  float s[VEC];
-#pragma unroll
-  for (int e = 0; e < VEC; ++e) s[e] = fast_exp2(fmaf(v.z[e], c, -gc));
-  acc.zf += ((s[0] + s[1]) + (s[2] + s[3])) + ((s[4] + s[5]) + (s[6] + s[7]));
-  static_assert(NCOPY * 4 == 64, "bin_addr stride");
-  typedef __attribute__((address_space(3))) char lds_char;
-  lds_char* const hb = (lds_char*)(lds_u32*)hist;
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    __hip_atomic_fetch_add((lds_u32*)(hb + bin_addr_lo(cc[e], hlane)), 1u, __ATOMIC_RELAXED,
-                           __HIP_MEMORY_SCOPE_WORKGROUP);
-    __hip_atomic_fetch_add((lds_u32*)(hb + bin_addr_hi(cc[e], hlane)), 1u, __ATOMIC_RELAXED,
-                           __HIP_MEMORY_SCOPE_WORKGROUP);
   }
   const uint32_t t01 = (cc[1] << 8) | cc[0];   // bytes: codes 0 2 1 3
   const uint32_t t23 = (cc[3] << 8) | cc[2];   // bytes: codes 4 6 5 7
@@ -812,30 +855,77 @@ __device__ __forceinline__ void pen_fix(uint32_t raw, int id, uint32_t t1, float
   acc.mpen = fmaxf(acc.mpen, zp);
 }
 
-// Largest processed key of a lane's stream.
+// Largest processed key of a lane's stream (+inf when the lane read a NaN
+// of either sign, whose orderable keys lie beyond those of +-inf: the
+// normalizer check then fails).
 __device__ __forceinline__ float row_max(const RowAcc& acc) {
   const uint32_t o = max(acc.mo & 0xFFFFu, acc.mo >> 16);
-  return fmaxf(key_of_ord16(o), acc.mpen);
-}
-
-// The NCOPY interleaved copies of the histogram summed into hsum, by the
-// whole block: four threads per bin, one 16-byte read each.
-__device__ __forceinline__ void hist_fold(const uint32_t* hist, uint32_t* hsum, int tid) {
-  static_assert(NT_F == 4 * NBIN && NCOPY == 16, "hist_fold geometry");
-  const uint4 v = reinterpret_cast<const uint4*>(hist)[tid];   // bin tid / 4, copies 4 (tid % 4) ..
-  int x = (int)(v.x + v.y + v.z + v.w);
-  x += dpp_i32<DPP_XOR1>(x);
-  x += dpp_i32<DPP_XOR2>(x);
-  if ((tid & 3) == 0) hsum[tid >> 2] = (uint32_t)x;
+  const uint32_t lo = min(acc.lo & 0xFFFFu, acc.lo >> 16);
+  return (lo < 0x007Fu || o > 0xFF80u) ? INFINITY : fmaxf(key_of_ord16(o), acc.mpen);
 }
 
 __device__ __forceinline__ RowAcc row_acc_init() {
   RowAcc r;
   r.mo = 0x007F007Fu;   // orderable key of -inf
+  r.lo = 0xFFFFFFFFu;
   r.mpen = -INFINITY;
   r.Z = 0.0;
-  r.zf = 0.0f;
   return r;
+}
+
+// Term of a key: exp2(key c - anchor c) as the stream's normalizer takes it.
+__device__ __forceinline__ float key_term(float key, float c, float gc) {
+  return fast_exp2(fmaf(key, c, -gc));
+}
+
+// This thread's share of a row's normalizer from its key histogram (bins
+// 4 tid .. 4 tid + 3 and the same NT_F * 4 further on, the lumped ones
+// excepted) and from the stream's exact entries (keys above the window;
+// bin 0's count is not used).
+__device__ __forceinline__ double hist_z(const uint32_t* hist, const Bins& bn, uint32_t t1, float c,
+                                         float gc, const ExactList& ex, int ns, int tid) {
+  static_assert(NBINW == 8 * NT_F, "hist_z geometry");
+  // (fp32 within a thread: eight terms, each count x term with a relative
+  // error of a few ulp, as the stream's own per-round sums were)
+  float z = 0.0f;
+  // (a loop, not unrolled: the stream's codes and the draft ring are live here)
+#pragma unroll 1
+  for (int half = 0; half < 2; ++half) {
+    const int i0 = 4 * (tid + half * NT_F);
+    const uint4 h4 = reinterpret_cast<const uint4*>(hist)[tid + half * NT_F];
+    const uint32_t hv[4] = {h4.x, h4.y, h4.z, h4.w};
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int d = bin_dist(i0 + q, bn);
+      if (hv[q] != 0u && d > 0 && d <= (int)t1)   // (a wave whose bins are all empty skips)
+        z = fmaf((float)hv[q], key_term(key_of_ord16(t1 - (uint32_t)d), c, gc), z);
+    }
+  }
+  double zd = (double)z;
+  for (int i = tid; i < min(ns, E_CAP); i += NT_F) zd += (double)key_term(ex.key[i], c, gc);
+  return zd;
+}
+
+// The lumped bins' share of the normalizer: each at the middle of its range
+// of terms; *err bounds the error (half that range times the count).
+__device__ __forceinline__ double lumped_z(const uint32_t* hist, const Bins& bn, uint32_t t1, float c,
+                                           float gc, double* err) {
+  const int bottom = RUP + 1 + (bn.r3 - bn.r2);
+  const double nb = (double)hist[RUP], nbot = (double)hist[bottom];
+  double z = 0.0, e = 0.0;
+  if (nb > 0.0) {
+    const double th = (double)key_term(key_of_ord16(t1 - (uint32_t)RUP), c, gc);
+    const double tl = (double)key_term(key_of_ord16(t1 - (uint32_t)min(bn.r2 - 1, (int)t1)), c, gc);
+    z += nb * 0.5 * (th + tl);
+    e += nb * 0.5 * fabs(th - tl);
+  }
+  if (nbot > 0.0) {
+    const double tb = bn.r3 <= (int)t1 ? (double)key_term(key_of_ord16(t1 - (uint32_t)bn.r3), c, gc) : 0.0;
+    z += nbot * 0.5 * tb;
+    e += nbot * 0.5 * tb;
+  }
+  *err = e;
+  return z;
 }
 
 // A row as a buffer resource of `bytes` bytes: loads past the end return 0
@@ -1020,23 +1110,21 @@ template <bool PR>
 __global__ __launch_bounds__(NT_F) void k_pair_fast(Args a, UnitOut* uo) {
   constexpr int NT = NT_F;
   __shared__ uint32_t bm[MAXV_FAST / 32];
-  // The two histograms (target row, draft row) and the nucleus slots, in
-  // one block so that the histograms sit at LDS address 0: a bin's address
-  // is then the lane's copy plus 64 bytes per code, with the draft row's
-  // base in the instruction's offset field.
+  // The draft row's key histogram and the nucleus slots.  The target row's
+  // histogram lives in the slots' space: it is read for the last time by the
+  // target cut, and the slots are filed after it.
   struct HistSlots {
-    uint32_t hist2[2][NBIN * NCOPY];
+    uint32_t histq[NBINW];
     uint32_t slot_arr[CAPT * NT];   // slot (s, lane) at s * NT + lane (file_round)
   };
+  static_assert(CAPT * NT >= NBINW, "the target histogram shares the slots' space");
   __shared__ __align__(16) HistSlots hsl;
-  auto& hist2 = hsl.hist2;
   auto& slot_arr = hsl.slot_arr;
   __shared__ float ekey[2][E_CAP];
   __shared__ int32_t eid[2][E_CAP];
   __shared__ uint16_t eraw[2][E_CAP];
   __shared__ uint32_t ecnt[NBIN];
   __shared__ uint64_t emass[NBIN];
-  __shared__ __align__(16) uint32_t hsum[NBIN];   // folded histogram
   __shared__ __align__(16) uint32_t hneg[NBIN];   // penalized logits that left a bin
   __shared__ float rkey[R_CAP];
   __shared__ double rmass[R_CAP];
@@ -1081,7 +1169,6 @@ __global__ __launch_bounds__(NT_F) void k_pair_fast(Args a, UnitOut* uo) {
   const __amdgpu_buffer_rsrc_t rs_t = row_rsrc(trow, nvec * 16);
   const __amdgpu_buffer_rsrc_t rs_d = row_rsrc(drow, bonus ? 0 : (Vd + VEC - 1) / VEC * 16);
   const uint32_t voff = (uint32_t)tid * 16u;
-  const uint32_t hlane = (uint32_t)(tid & (NCOPY - 1)) * 4u;
   ExactList exp_, exq;
   exp_.key = ekey[0];
   exp_.id = eid[0];
@@ -1099,8 +1186,8 @@ __global__ __launch_bounds__(NT_F) void k_pair_fast(Args a, UnitOut* uo) {
   exq.pid = pid_arr[1];
   exq.praw = praw_arr[1];
   exq.np = &s_np[1];
-  uint32_t* hist = hist2[0];
-  uint32_t* histq = hist2[1];
+  uint32_t* hist = hsl.slot_arr;
+  uint32_t* histq = hsl.histq;
   // One load ring over the target row (rounds 0..NR-1) and the draft row
   // (rounds NR..2NR-1): NSTG loads in flight per thread throughout.  Then
   // the penalty set's first entries.
@@ -1116,7 +1203,10 @@ __global__ __launch_bounds__(NT_F) void k_pair_fast(Args a, UnitOut* uo) {
     s_np[1] = 0;
     s_npl = 0;
   }
-  for (int i = tid; i < 2 * NBIN * NCOPY; i += NT) hist[i] = 0u;   // both rows' histograms
+  for (int i = tid; i < NBINW; i += NT) {   // both rows' histograms
+    hist[i] = 0u;
+    histq[i] = 0u;
+  }
   if (tid < NBIN) {
     hneg[tid] = 0u;
     ecnt[tid] = 0u;
@@ -1177,17 +1267,19 @@ __global__ __launch_bounds__(NT_F) void k_pair_fast(Args a, UnitOut* uo) {
       m0 = fmaxf(m0, max8(v.z));   // logits as read: the anchor is only a reference
     }
   });
-  const float Gp = bar_max<NT>(m0, red_f[0]);
+  // (block-uniform values read from LDS: moved to scalar registers)
+  const float Gp = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(bar_max<NT>(m0, red_f[0]))));
   const bool anchor_ok = Gp > -1e30f && Gp < INFINITY;
   const uint32_t t1p = anchor_ok ? min(ord16f(Gp) + UP, 0xFFFEu) + 1u : 0xFFFFu;
   const float gcp = anchor_ok ? Gp * c : 0.0f;
+  const Bins binp = row_bins(t1p);
 
   uint32_t code[NR][2];
   RowAcc ap = row_acc_init();
   if (anchor_ok) ap.mo = ord16f(Gp) * 0x00010001u;   // the max of the sampled rounds
   int x0 = -1;          // this thread's penalty-list index (set in round 1)
   uint32_t gp = 0u, gq = 0u, goff = 0u;
-  auto stream_a = [&]<bool POS, bool TAIL>() __attribute__((always_inline)) {
+  auto stream_a = [&]<bool TAIL>() __attribute__((always_inline)) {
   static_for<NR>([&]<int l>() __attribute__((always_inline)) {
     const uint4 ld = stg[l % NSTG];
     if constexpr (l == 0 || l == 6 || l == 12 || l == 17)   // lagging waves first
@@ -1213,21 +1305,15 @@ __global__ __launch_bounds__(NT_F) void k_pair_fast(Args a, UnitOut* uo) {
     const int k = l * NT + tid;
     // (codes of vectors past the row end are never read: every reader
     // checks k < nvec)
-    if (k < nvec) {
+    if ((!TAIL && l < NR - 1) || k < nvec) {
       Vec8 v;
-      vec8<POS, TAIL>(ld, l, k, V, v);
-      const uint2 cw = row_vec<(l < NSAMP)>(v, k, c, gcp, t1p, hist, hlane, exp_, ap);
+      vec8<TAIL>(ld, l, k, V, v);
+      const uint2 cw = row_vec<(l < NSAMP)>(v, k, t1p, binp, hist, exp_, ap);
       code[l][0] = cw.x;
       code[l][1] = cw.y;
     }
-    if constexpr (l % 2 == 1 || l == NR - 1) {   // fp32 sums of two rounds, then fp64
-      ap.Z += (double)ap.zf;
-      ap.zf = 0.0f;
-    }
     SDV_PIN(ap.mo);
-    SDV_PIN(ap.mpen);
-    SDV_PIN(ap.Z);
-    SDV_PIN(ap.zf);
+    SDV_PIN(ap.lo);
     SDV_PIN(code[l][0]);
     SDV_PIN(code[l][1]);
     // The slot's next load (next target round, or a draft round) goes out
@@ -1237,15 +1323,10 @@ __global__ __launch_bounds__(NT_F) void k_pair_fast(Args a, UnitOut* uo) {
     __builtin_amdgcn_sched_barrier(0);   // keep later rounds' loads in their rounds
   });
   };
-  // (instances by window sign and by whether a vector needs masking)
-  const bool tail = (V & 7) != 0;
-  if (t1p >= 0x8000u + 254u) {
-    if (tail) stream_a.template operator()<true, true>();
-    else stream_a.template operator()<true, false>();
-  } else {
-    if (tail) stream_a.template operator()<false, true>();
-    else stream_a.template operator()<false, false>();
-  }
+  // (instances by whether a vector needs masking)
+  const bool tail = (V & 7) != 0 || V <= (NR - 1) * NT_F * VEC;
+  if (tail) stream_a.template operator()<true>();
+  else stream_a.template operator()<false>();
   __syncthreads();   // the target stream is done: histogram, stream entries, logit list
   const int npl = s_npl;
   if (npl <= PL_CAP)
@@ -1255,7 +1336,7 @@ __global__ __launch_bounds__(NT_F) void k_pair_fast(Args a, UnitOut* uo) {
       const uint32_t raw = g == 0xFFFFFFFFu ? reinterpret_cast<const uint16_t*>(trow)[id] : g & 0xFFFFu;
       pen_fix(raw, id, t1p, rep, c, gcp, hneg, exp_, ap);
     }
-  hist_fold(hist, hsum, tid);
+  ap.Z += hist_z(hist, binp, t1p, c, gcp, exp_, s_ne[0], tid);
   {
     // The draft's anchor rides along: the block max of its first NSAMP
     // rounds, which the ring already holds.
@@ -1288,9 +1369,12 @@ __global__ __launch_bounds__(NT_F) void k_pair_fast(Args a, UnitOut* uo) {
       M = fmaxf(M, red_f[1][i]);
       Zs += red_d[0][i];
     }
+    double zerr;
+    Zs += lumped_z(hist, binp, t1p, c, gcp, &zerr);
     const int ne = s_ne[0], np = s_np[0];
+    // (the lumped bins may move the normalizer by at most 2^-24 of itself)
     const bool good = anchor_ok && M > -INFINITY && M < INFINITY && Zs > 0.0 && Zs < INFINITY &&
-                      ne <= E_CAP && np <= PE_CAP && npl <= PL_CAP;
+                      zerr <= 0x1p-24 * Zs && ne <= E_CAP && np <= PE_CAP && npl <= PL_CAP;
     Cut cc;
     cc.ok = 0;
     cc.code = 0;
@@ -1298,7 +1382,7 @@ __global__ __launch_bounds__(NT_F) void k_pair_fast(Args a, UnitOut* uo) {
     cc.zk = 0.0;
     if (good) {
       const double Zp = Zs * exp2((double)gcp - (double)M * (double)c);
-      cc = wave_cut(hsum, hneg, exp_, ne, np, bm, pen, t1p, M, c, tp * Zp, ecnt, emass, rkey, rmass, rid,
+      cc = wave_cut(hist, hneg, exp_, ne, np, bm, pen, t1p, M, c, tp * Zp, ecnt, emass, rkey, rmass, rid,
                     &s_rcnt);
     }
     if (lane == 0) s_cut[0] = CutRes{good ? (cc.ok ? 1 : -1) : 0, cc.code, cc.key, M, cc.zk};
@@ -1354,52 +1438,41 @@ __global__ __launch_bounds__(NT_F) void k_pair_fast(Args a, UnitOut* uo) {
     float Gq = red_f[2][0];
 #pragma unroll
     for (int i = 1; i < NT / WAVE; ++i) Gq = fmaxf(Gq, red_f[2][i]);
+    Gq = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(Gq)));
     const bool anchor_q = Gq > -1e30f && Gq < INFINITY;
     const uint32_t t1q = anchor_q ? min(ord16f(Gq) + UP, 0xFFFEu) + 1u : 0xFFFFu;
     const float gcq = anchor_q ? Gq * c : 0.0f;
+    const Bins binq = row_bins(t1q);
     RowAcc aq = row_acc_init();
     if (anchor_q) aq.mo = ord16f(Gq) * 0x00010001u;
-    auto stream_b = [&]<bool POS, int LOW, bool RAISE, bool TAIL>() __attribute__((always_inline)) {
+    auto stream_b = [&]<int LOW, bool RAISE, bool TAIL>() __attribute__((always_inline)) {
     static_for<NR>([&]<int l>() __attribute__((always_inline)) {
       const uint4 ld = stg[(NR + l) % NSTG];
       if constexpr (l == 0 || l == 6 || l == 12 || l == 17)
         __builtin_amdgcn_s_setprio(l == 0 ? 3 : l == 6 ? 2 : l == 12 ? 1 : 0);
       const int k = l * NT + tid;
-      if (k < nvec) {
+      if ((!TAIL && l < NR - 1) || k < nvec) {
         Vec8 v;
-        vec8<POS, TAIL>(ld, l, k, Vd, v);
+        vec8<TAIL>(ld, l, k, Vd, v);
         const uint32_t bits = RAISE ? pen_bits8(bm, k) : 0u;
         const uint4 dv = make_uint4(v.w[0], v.w[1], v.w[2], v.w[3]);
-        (void)row_vec<(l < NSAMP)>(v, k, c, gcq, t1q, histq, hlane, exq, aq);
+        (void)row_vec<(l < NSAMP)>(v, k, t1q, binq, histq, exq, aq);
         file_round<LOW>(l, code[l][0], code[l][1], dv, true, bits, cut_code, RAISE, slot_arr, nslot);
       }
-      if constexpr (l % 2 == 1 || l == NR - 1) {
-        aq.Z += (double)aq.zf;
-        aq.zf = 0.0f;
-      }
       SDV_PIN(aq.mo);
-      SDV_PIN(aq.mpen);
-      SDV_PIN(aq.Z);
-      SDV_PIN(aq.zf);
+      SDV_PIN(aq.lo);
       __builtin_amdgcn_sched_barrier(0);
       if constexpr (l + NSTG < NR) stg[(NR + l) % NSTG] = ring_load<NR + l + NSTG>(rs_t, rs_d, voff);
       __builtin_amdgcn_sched_barrier(0);
     });
     };
-    // (instances by window sign and by the target cut's half of the code range)
-    const bool posq = t1q >= 0x8000u + 254u, low = cut_code < 127u;
-    // (and by whether penalized keys rise or a vector needs masking)
-    const bool tail_d = (Vd & 7) != 0 || Vd < V;
-    if (raise || tail_d) {
-      if (posq) stream_b.template operator()<true, -1, true, true>();
-      else stream_b.template operator()<false, -1, true, true>();
-    } else if (posq) {
-      if (low) stream_b.template operator()<true, 1, false, false>();
-      else stream_b.template operator()<true, 0, false, false>();
-    } else {
-      if (low) stream_b.template operator()<false, 1, false, false>();
-      else stream_b.template operator()<false, 0, false, false>();
-    }
+    // (instances by the target cut's half of the code range, and by whether
+    // penalized keys rise or a vector needs masking)
+    const bool low = cut_code < 127u;
+    const bool tail_d = (Vd & 7) != 0 || Vd < V || Vd <= (NR - 1) * NT_F * VEC;
+    if (raise || tail_d) stream_b.template operator()<-1, true, true>();
+    else if (low) stream_b.template operator()<1, false, false>();
+    else stream_b.template operator()<0, false, false>();
     __syncthreads();   // the draft stream is done: histogram, stream entries
     if (npl <= PL_CAP)
       for (int i = tid; i < npl; i += NT) {
@@ -1409,7 +1482,7 @@ __global__ __launch_bounds__(NT_F) void k_pair_fast(Args a, UnitOut* uo) {
                              : g == 0xFFFFFFFFu ? reinterpret_cast<const uint16_t*>(drow)[id] : g >> 16;
         pen_fix(raw, id, t1q, rep, c, gcq, hneg, exq, aq);
       }
-    hist_fold(histq, hsum, tid);
+    aq.Z += hist_z(histq, binq, t1q, c, gcq, exq, s_ne[1], tid);
     {
       const float wm = wave_max(row_max(aq));
       const double wz = wave_sum(aq.Z);
@@ -1431,9 +1504,11 @@ __global__ __launch_bounds__(NT_F) void k_pair_fast(Args a, UnitOut* uo) {
         Zs += red_d[1][i];
         over |= red_i[0][i];
       }
+      double zerr;
+      Zs += lumped_z(histq, binq, t1q, c, gcq, &zerr);
       const int ne = s_ne[1], np = s_np[1];
       const bool good = anchor_q && M > -INFINITY && M < INFINITY && Zs > 0.0 && Zs < INFINITY &&
-                        ne <= E_CAP && np <= PE_CAP && !over;
+                        zerr <= 0x1p-24 * Zs && ne <= E_CAP && np <= PE_CAP && !over;
       Cut cc;
       cc.ok = 0;
       cc.code = 0;
@@ -1441,7 +1516,7 @@ __global__ __launch_bounds__(NT_F) void k_pair_fast(Args a, UnitOut* uo) {
       cc.zk = 0.0;
       if (good) {
         const double Zqa = Zs * exp2((double)gcq - (double)M * (double)c);
-        cc = wave_cut(hsum, hneg, exq, ne, np, bm, pen, t1q, M, c, tp * Zqa, ecnt, emass, rkey, rmass,
+        cc = wave_cut(histq, hneg, exq, ne, np, bm, pen, t1q, M, c, tp * Zqa, ecnt, emass, rkey, rmass,
                       rid, &s_rcnt);
       }
       const int okv = over ? -2 : !good ? 0 : cc.ok ? 1 : -1;
@@ -1698,13 +1773,17 @@ __device__ __forceinline__ void fallback_unit(const Args& a, UnitOut* uo, int u)
   ex.si = si;
   ex.ctot = ctot;
   UnitOut out = uo[u];
-  out.flags = UO_SLOW;
+  // (the fallback bit stays set: every block of this launch enumerates the
+  // flagged units of a pass from these records, and a block that has
+  // finished its share of a pass must not change what a slower block, still
+  // enumerating that pass, reads)
+  out.flags = UO_SLOW | UO_FALLBACK;
   out.accept = 1;
   out.y = -1;
   const RowStat P = row_stats_dev<SD_BF16, NT>(a, trow, a.V, c, pen, bm, ex, request_top_p(a, r));
   if (P.flags & NONFINITE) {
     if (tid == 0) {
-      out.flags = UO_NONFINITE;
+      out.flags = UO_NONFINITE | UO_FALLBACK;
       uo[u] = out;
     }
     return;
@@ -1721,7 +1800,7 @@ __device__ __forceinline__ void fallback_unit(const Args& a, UnitOut* uo, int u)
   const RowStat Q = row_stats_dev<SD_BF16, NT>(a, drow, a.Vd, c, pen, bm, ex, request_top_p(a, r));
   if (Q.flags & NONFINITE) {
     if (tid == 0) {
-      out.flags = UO_NONFINITE;
+      out.flags = UO_NONFINITE | UO_FALLBACK;
       uo[u] = out;
     }
     return;

@@ -148,6 +148,50 @@ def test_single_pass_law_bf16_top_p():
         assert p1 > 1e-4 and p2 > 1e-4
 
 
+def test_fallback_over_several_passes():
+    """Every unit of a batch above 4096 units handed to the exact fallback:
+    its blocks deal the flagged units of each pass among themselves from the
+    unit records, which must read the same to every block for the whole
+    pass (a block that has finished its share may not change them).  Rows
+    whose maximum is small and whose mass sits largely on keys within 2^-20
+    of zero (here exact zeros) go to the fallback by construction; the
+    results must equal the general path's on the same values (fp32 input),
+    which runs the same exact routines."""
+    import torch
+    sdv = _sdv()
+    rng = np.random.default_rng(31)
+    B, K, V = 2200, 1, 64
+    base = np.zeros((K + 1, V), np.float32)
+    base[:, : V // 2] = rng.integers(-8, 9, size=(K + 1, V // 2)) / 16.0   # exact in bf16
+    dbase = np.zeros((K, V), np.float32)
+    dbase[:, : V // 2] = rng.integers(-8, 9, size=(K, V // 2)) / 16.0
+    tb, db = wl.f32_to_bf16_bits(base), wl.f32_to_bf16_bits(dbase)
+    assert np.array_equal(wl.bf16_bits_to_f32(tb), base)
+    dev = "cuda"
+    tt = torch.from_numpy(np.ascontiguousarray(np.broadcast_to(tb.view(np.int16), (B, K + 1, V)))).to(dev)
+    tt = tt.view(torch.bfloat16)
+    dd = torch.from_numpy(np.ascontiguousarray(np.broadcast_to(db.view(np.int16), (B, K, V)))).to(dev)
+    dd = dd.view(torch.bfloat16)
+    tf = torch.from_numpy(np.ascontiguousarray(np.broadcast_to(base, (B, K + 1, V)))).to(dev)
+    df = torch.from_numpy(np.ascontiguousarray(np.broadcast_to(dbase, (B, K, V)))).to(dev)
+    ids = torch.from_numpy(rng.integers(0, V, size=(B, K)).astype(np.int32)).to(dev)
+    temp = torch.from_numpy(rng.uniform(0.7, 1.2, size=B).astype(np.float32)).to(dev)
+    for D in (0.0, 0.4):
+        args = sdv.make_args(tt, dd, ids, None, temp, 0.9, 1.0, None, None, D, 41, 0)
+        assert sdv.phase_kernel(args, 0) == "k_pair_fast"
+        ws = sdv.alloc_workspace(args, dev)
+        acc = torch.empty(B, dtype=torch.int32, device=dev)
+        tok = torch.empty((B, K + 1), dtype=torch.int32, device=dev)
+        sdv.run_phase(args, ws, 0, acc, tok)
+        assert sdv.fallback_units(args, ws) == B * (K + 1)
+        g = sdv.verify_sample(tt, dd, ids, None, temp, 0.9, 1.0, None, None, D, 41, 0, stats=True)
+        r = sdv.verify_sample(tf, df, ids, None, temp, 0.9, 1.0, None, None, D, 41, 0, stats=True)
+        torch.cuda.synchronize()
+        for x, y, name in zip(g, r, ("accepted", "tokens", "status", "stats")):
+            np.testing.assert_array_equal(x.cpu().numpy(), y.cpu().numpy(), err_msg=f"D={D} {name}")
+        assert (g[1][:, 0].cpu().numpy() >= 0).all()
+
+
 @pytest.mark.parametrize("path", ["single_pass", "general"])
 def test_status_precedence_and_workspace_reuse(path):
     """One invalidating defect per request, the first in the order K, draft
