@@ -62,18 +62,29 @@ def source_hash():
     return h.hexdigest()
 
 
-def algorithmic_bytes(kernel, w):
+def algorithmic_bytes(kernel, w, flagged=None, accepted=None):
     """Bytes the kernel must move per launch by definition of its work.
 
     The single-pass kernel and the general row pass read every logit row of
     the call once; the general TV pass reads the 2K draft-position rows of
-    each request; the fallback re-read, finalize and draw kernels read no
-    logit row unconditionally.
+    each request.  The exact fallback must read the rows of the units handed
+    to it (flagged: a per-unit bool array, pairs first: target and draft
+    row; then one bonus row per request); the general draw reads, per
+    request, the target and draft row of the first rejected position, or the
+    bonus row (accepted: the accepted lengths).  Otherwise 0.
     """
+    import numpy as np
+    es = 2 if w.dtype == "bf16" else 4
     if kernel in ("k_pair_fast", "k_row_prepare"):
         return w.logit_bytes()
     if kernel == "k_pair_tv":
-        return 2 * w.K_max * w.V * 2 * w.B
+        return 2 * w.K_max * w.V * es * w.B
+    if kernel == "k_pair_fallback" and flagged is not None:
+        npairs = w.B * w.K_max
+        return int(2 * flagged[:npairs].sum() + flagged[npairs:].sum()) * w.V * es
+    if kernel == "k_finalize" and accepted is not None:
+        rows = np.where(accepted < w.k_per_row, 2, 1)
+        return int(rows.sum()) * w.V * es
     return 0
 
 
@@ -352,7 +363,13 @@ def main():
     positions = w.positions()
     logit_bytes = w.logit_bytes()
     dom = max(phase_ms, key=phase_ms.get)
-    achieved = algorithmic_bytes(dom, w) / (phase_ms[dom] * 1e-3) / 1e9
+    flagged = None
+    if "k_pair_fallback" in phase_ms:
+        sdv.run_phase(args, ws, 0, acc, tok, st, None, stream)
+        nfb, why = sdv.fallback_units(args, ws, stream, why=True)
+        flagged = why != 0
+    nbytes = algorithmic_bytes(dom, w, flagged=flagged)
+    achieved = nbytes / (phase_ms[dom] * 1e-3) / 1e9
     line = {
         "metric": METRIC,
         "value": positions / (ms_step * 1e-3),
@@ -374,14 +391,13 @@ def main():
         "roofline": {"kernel": dom, "bound": "hbm", "achieved": achieved,
                      "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": achieved / PEAK_HBM_GBPS,
                      "traffic": measured_traffic(dom),
-                     "algorithmic_bytes": algorithmic_bytes(dom, w)},
+                     "algorithmic_bytes": nbytes},
         "mean_accepted": float(acc.float().mean().item()),
     }
     if a.config == "4fb":
         line["config"]["workload"] = WORKLOAD.replace("T~U[0.5,1]", "T~U[1,1.5]")
-        if "k_pair_fallback" in phase_ms:
-            sdv.run_phase(args, ws, 0, acc, tok, st, None, stream)
-            line["fallback_units"] = sdv.fallback_units(args, ws, stream)
+        if flagged is not None:
+            line["fallback_units"] = int(flagged.sum())
             line["units"] = w.B * (w.K_max + 1)
     if cpu is not None:
         line["cpu_baseline"] = cpu
@@ -655,9 +671,12 @@ def bench_config5(a):
            "B": w.B, "K_max": w.K_max, "V": w.V, "input_dtype": "bf16",
            "positions": w.positions(), "k_hist": np.bincount(w.k_per_row, minlength=9).tolist(),
            "logit_bytes_per_call": w.logit_bytes()}
+    acc_np = outs[0].cpu().numpy()
     line = _line(METRIC, w.positions() / (ms * 1e-3), "positions/s", a, ms, cfg,
-                 _hbm_roof(dom, w.logit_bytes() if dom == "k_row_prepare" else 0, per[dom]),
-                 {"phases_ms": per, "call_hbm_gbps": w.logit_bytes() / (ms * 1e-3) / 1e9})
+                 _hbm_roof(dom, algorithmic_bytes(dom, w, accepted=acc_np), per[dom]),
+                 {"phases_ms": per, "call_hbm_gbps": w.logit_bytes() / (ms * 1e-3) / 1e9,
+                  "row_pass_roofline": _hbm_roof("k_row_prepare", w.logit_bytes(),
+                                                 per["k_row_prepare"])})
     if cpu is not None:
         line["cpu_baseline"] = cpu
     print(json.dumps(line), flush=True)
