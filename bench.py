@@ -62,16 +62,16 @@ def source_hash():
     return h.hexdigest()
 
 
-def algorithmic_bytes(kernel, w, flagged=None, accepted=None):
+def algorithmic_bytes(kernel, w, accepted=None):
     """Bytes the kernel must move per launch by definition of its work.
 
     The single-pass kernel and the general row pass read every logit row of
-    the call once; the general TV pass reads the 2K draft-position rows of
-    each request.  The exact fallback must read the rows of the units handed
-    to it (flagged: a per-unit bool array, pairs first: target and draft
-    row; then one bonus row per request); the general draw reads, per
-    request, the target and draft row of the first rejected position, or the
-    bonus row (accepted: the accepted lengths).  Otherwise 0.
+    the call once (the single pass's exact route re-reads the rows of units
+    it could not settle: that is extra traffic, not algorithmic bytes); the
+    general TV pass reads the 2K draft-position rows of each request; the
+    general draw reads, per request, the target and draft row of the first
+    rejected position, or the bonus row (accepted: the accepted lengths).
+    Otherwise 0.
     """
     import numpy as np
     es = 2 if w.dtype == "bf16" else 4
@@ -79,9 +79,6 @@ def algorithmic_bytes(kernel, w, flagged=None, accepted=None):
         return w.logit_bytes()
     if kernel == "k_pair_tv":
         return 2 * w.K_max * w.V * es * w.B
-    if kernel == "k_pair_fallback" and flagged is not None:
-        npairs = w.B * w.K_max
-        return int(2 * flagged[:npairs].sum() + flagged[npairs:].sum()) * w.V * es
     if kernel == "k_finalize" and accepted is not None:
         rows = np.where(accepted < w.k_per_row, 2, 1)
         return int(rows.sum()) * w.V * es
@@ -269,7 +266,7 @@ def main():
                     help="time the draft-side confidence step (sd_draft_confidence) instead")
     ap.add_argument("--config", default="4", choices=["4", "4fb", "2", "3", "5", "5b", "lmhead"],
                     help="workload: 4 (default, the measured one), 4fb (T in [1, 1.5]: wide "
-                         "nuclei, units the single-pass kernel hands to its exact fallback), "
+                         "nuclei, units the single-pass kernel settles by its exact route), "
                          "2, 3 (greedy), 5, 5b, lmhead (the fused LM-head path)")
     ap.add_argument("--cpu-cores", choices=["all", "one"], default="all",
                     help="cpu_baseline over a pool of worker processes (all) or one thread")
@@ -364,11 +361,11 @@ def main():
     logit_bytes = w.logit_bytes()
     dom = max(phase_ms, key=phase_ms.get)
     flagged = None
-    if "k_pair_fallback" in phase_ms:
-        sdv.run_phase(args, ws, 0, acc, tok, st, None, stream)
+    if names[0] == "k_pair_fast":
+        # units the single pass handed to its exact route (records of the last step)
         nfb, why = sdv.fallback_units(args, ws, stream, why=True)
         flagged = why != 0
-    nbytes = algorithmic_bytes(dom, w, flagged=flagged)
+    nbytes = algorithmic_bytes(dom, w)
     achieved = nbytes / (phase_ms[dom] * 1e-3) / 1e9
     line = {
         "metric": METRIC,
@@ -396,9 +393,9 @@ def main():
     }
     if a.config == "4fb":
         line["config"]["workload"] = WORKLOAD.replace("T~U[0.5,1]", "T~U[1,1.5]")
-        if flagged is not None:
-            line["fallback_units"] = int(flagged.sum())
-            line["units"] = w.B * (w.K_max + 1)
+    if flagged is not None:
+        line["fallback_units"] = int(flagged.sum())
+        line["units"] = w.B * (w.K_max + 1)
     if cpu is not None:
         line["cpu_baseline"] = cpu
     print(json.dumps(line), flush=True)

@@ -313,9 +313,10 @@ int sd_debug_process_rows(const sd_verify_args_t *args, void *workspace,
  * depends on the arguments (sd_debug_phase_kernel names them):
  *   single-pass path (bf16, top_p < 1, V <= 155648):
  *     0 = one pass over every (row, position) pair and bonus row: top-p
- *         cut, TV, accept test and draw; 1 = exact multi-pass recompute of
- *         the units phase 0 flagged (every other unit exits at once);
- *     2 = longest accepted prefix, output tokens and statistics;
+ *         cut, TV, accept test and draw (a unit the pass cannot settle is
+ *         recomputed by the same workgroup's exact multi-pass route);
+ *     1 = no launch; 2 = longest accepted prefix, output tokens and
+ *         statistics;
  *   general path: 0 = per-row statistics and top-p cut, 1 = per-position
  *     TV distance (no launch when not needed), 2 = decisions and draws. */
 int sd_debug_run_phase(const sd_verify_args_t *args, void *workspace,
@@ -330,12 +331,12 @@ const char *sd_debug_phase_kernel(const sd_verify_args_t *args, int phase);
 
 /* Test export: after phase 0 of the single-pass path (sd_debug_run_phase),
  * the number of units (draft positions j < K_r and bonus rows of valid
- * requests) that phase handed to the exact fallback, written to *out_count
+ * requests) that phase settled by its exact route, written to *out_count
  * (host memory).  out_why (host, nullable): B * (K_max + 1) words, unit u =
  * pair (r, j) at r * K_max + j, bonus row r at B * K_max + r; bit 1 a
  * target-row stream state out of range, 2 a target cut the window did not
  * settle, 4 and 8 the same for the draft row, 16 more nucleus candidates
- * than slots; 0 for units not handed over.  Synchronizes `stream`.
+ * than slots; 0 for units the single pass settled.  Synchronizes `stream`.
  * SD_EUNSUPPORTED when the arguments select the general path. */
 int sd_debug_fallback_units(const sd_verify_args_t *args, const void *workspace,
                             size_t workspace_bytes, int32_t *out_count, uint32_t *out_why,

@@ -319,7 +319,7 @@ def phase_kernel(args, phase):
 
 def fallback_units(args, workspace, stream=None, why=False):
     """After run_phase(..., 0, ...) on the single-pass path: how many units
-    that phase handed to the exact fallback (and, with why=True, the reason
+    that phase settled by its exact route (and, with why=True, the reason
     bits per unit as a numpy array)."""
     import numpy as np
     n = ctypes.c_int32(0)

@@ -285,7 +285,7 @@ struct UnitOut {
 };
 static_assert(sizeof(UnitOut) == 48, "UnitOut layout");
 enum : uint32_t { UO_NONFINITE = 1, UO_QZERO = 2, UO_RESID_ZERO = 4, UO_SLOW = 8, UO_FALLBACK = 16 };
-// Why the single-pass kernel handed a unit to the fallback: a row's stream
+// Why the single pass handed a unit to its exact route: a row's stream
 // state out of range (anchor, normalizer, list capacities), its cut not
 // settled by the window, or more nucleus candidates than slots.
 enum : uint32_t { FB_P_STATE = 1, FB_P_CUT = 2, FB_Q_STATE = 4, FB_Q_CUT = 8, FB_SLOTS = 16 };
@@ -408,8 +408,6 @@ constexpr int PE_CAP = 256;                  // penalized exact entries per row
 constexpr int PL_CAP = 256;                  // distinct penalized ids per unit
 constexpr int SHP = 40;                      // fixed-point shift of exact-entry masses
 constexpr int SHD = 40;                      // fixed-point shift of draw weights (each <= 1)
-constexpr int FALLBACK_GRID = 256;           // blocks of the exact fallback launch
-constexpr int NT_FB = 512;                   // threads per fallback block
 static_assert(NSTG >= NSAMP && NSTG < NR, "load ring");
 
 // Exact-key list of one row, in two regions.  The stream region holds the
@@ -1104,6 +1102,103 @@ __device__ __forceinline__ ReqWords request_words(const int32_t* po, const int32
   return w;
 }
 
+// Exact multi-pass processing of a unit that the single pass could not settle
+// (its cut lies outside the window, its nucleus overflows the slots, or a
+// row is not finite), by the same workgroup right away: it re-reads the
+// unit's rows with the general-path routines (row statistics with the
+// radix-select cut, TV, decision, draw).  bm holds the unit's penalty
+// bitmap when pen; ex is carved from the single pass's histogram and slot
+// space, which is free by then.  Writes the unit's record with UO_SLOW |
+// UO_FALLBACK and the reasons why.
+template <int NT>
+__device__ __forceinline__ void exact_unit(const Args& a, UnitOut* uo, int u, const uint32_t* bm,
+                                        const ExactLds& ex, uint32_t why) {
+  const int tid = threadIdx.x;
+  __shared__ int s_acc;
+  // (the unit's request values are derived again here, so that none of
+  // them is held through the single pass for this route's sake)
+  const Unit un = unit_of(a, u);
+  const int r = un.r;
+  const bool bonus = un.bonus;
+  const int j = bonus ? request_k(a, r) : un.j;
+  const float T = request_t(a, r);
+  const PenSet ps = pen_set(a, r, j);
+  const bool pen = ps.on;
+  float u_j, v_j;
+  uniforms(a.seed, a.offset, r, j, u_j, v_j);
+  const float c = 1.4426950408889634f / T;
+  const char* trow = target_row(a, r, j);
+  const char* drow = bonus ? trow : draft_row(a, r, j);
+  UnitOut out;
+  out.d = out.th = out.px = out.qx = out.pix = out.S = 0.0f;
+  out.u = u_j;
+  out.v = v_j;
+  out.accept = 1;
+  out.y = -1;
+  out.flags = UO_SLOW | UO_FALLBACK;
+  out.why = why;
+  const float tpr = request_top_p(a, r);
+  const RowStat P = row_stats_dev<SD_BF16, NT>(a, trow, a.V, c, pen, bm, ex, tpr);
+  if (P.flags & NONFINITE) {
+    if (tid == 0) {
+      out.flags = UO_NONFINITE | UO_FALLBACK;
+      out.accept = 0;
+      uo[u] = out;
+    }
+    return;
+  }
+  if (bonus) {
+    const Drawn dw = draw_dev<SD_BF16, NT>(a, trow, trow, P, P, 1, v_j, pen, bm, ex);
+    if (tid == 0) {
+      out.y = dw.y;
+      out.S = (float)dw.S;
+      uo[u] = out;
+    }
+    return;
+  }
+  const RowStat Q = row_stats_dev<SD_BF16, NT>(a, drow, a.Vd, c, pen, bm, ex, tpr);
+  if (Q.flags & NONFINITE) {
+    if (tid == 0) {
+      out.flags = UO_NONFINITE | UO_FALLBACK;
+      out.accept = 0;
+      uo[u] = out;
+    }
+    return;
+  }
+  const double d = pair_tv_dev<SD_BF16, NT>(a, trow, drow, P, Q, pen, bm, ex);
+  if (tid == 0) {
+    const int x = a.ids[(int64_t)r * a.K_max + j];
+    float kxp = -INFINITY, kxq = -INFINITY;
+    if (x >= 0 && x < a.V) {
+      kxp = load1<SD_BF16>(trow, x);
+      kxq = x < a.Vd ? load1<SD_BF16>(drow, x) : -INFINITY;
+      if (pen && ((bm[x >> 5] >> (x & 31)) & 1u)) {
+        kxp = penalize(kxp, a.rep);
+        kxq = penalize(kxq, a.rep);
+      }
+    }
+    const Decision dc = decide(P, Q, kxp, kxq, (double)T, (double)request_D(a, r), true, d, u_j);
+    out.d = (float)d;
+    out.th = (float)dc.th;
+    out.px = (float)dc.px;
+    out.qx = (float)dc.qx;
+    out.pix = (float)dc.pix;
+    out.accept = dc.accept ? 1 : 0;
+    if (dc.qx == 0.0) out.flags |= UO_QZERO;
+    s_acc = out.accept;
+  }
+  __syncthreads();
+  if (!s_acc) {
+    const Drawn dw = draw_dev<SD_BF16, NT>(a, trow, drow, P, Q, 0, v_j, pen, bm, ex);
+    if (tid == 0) {
+      out.y = dw.y;
+      out.S = (float)dw.S;
+      if (dw.resid_zero) out.flags |= UO_RESID_ZERO;
+    }
+  }
+  if (tid == 0) uo[u] = out;
+}
+
 // PR: per-request top-p / TV budget arrays are given (else the host-checked
 // scalars apply to every request).
 template <bool PR>
@@ -1722,183 +1817,33 @@ __global__ __launch_bounds__(NT_F) void k_pair_fast(Args a, UnitOut* uo) {
   }
 
 write_out_flags:
-  if (tid == 0) {
-    UnitOut o;
-    o.d = o.th = o.px = o.qx = o.pix = o.S = 0.0f;
-    o.u = u_j;
-    o.v = v_j;
-    o.accept = 0;
-    o.y = -1;
-    o.flags = oflags;
-    o.why = why;
-    uo[blockIdx.x] = o;
-  }
-}
-
-// Exact multi-pass processing of one unit k_pair_fast flagged (re-reads its
-// rows with the general-path routines).
-__device__ __forceinline__ void fallback_unit(const Args& a, UnitOut* uo, int u) {
-  constexpr int NT = NT_FB;
-  __shared__ uint32_t bm[MAXV_FAST / 32];
-  __shared__ uint64_t hmass[HBINS];
-  __shared__ uint32_t hcnt[HBINS];
-  __shared__ uint64_t su[NT];
-  __shared__ double sd[NT];
-  __shared__ double ctot[(MAXV_FAST / VEC + WAVE - 1) / WAVE + 1];   // the draw's chunk totals
-  __shared__ float sf[NT / WAVE];
-  __shared__ int si[NT / WAVE + 4];
-  __shared__ int s_acc;
-  const int tid = threadIdx.x;
-  const Unit un = unit_of(a, u);
-  const int r = un.r;
-  const bool bonus = un.bonus;
-  const int K = request_k(a, r);
-  // Units k_pair_fast skipped (invalid request, position beyond K_r) hold
-  // no output of this call: never act on them.
-  if (K < 0 || K > a.K_max) return;
-  const int j = bonus ? K : un.j;
-  if (!bonus && j >= K) return;
-  const float T = request_t(a, r);
-  if (!(T > 0.0f) || !(T < INFINITY)) return;
-  const float c = 1.4426950408889634f / T;
-  const char* trow = target_row(a, r, j);
-  const char* drow = bonus ? trow : draft_row(a, r, j);
-  const bool pen = build_penalty_bitmap<NT>(a, r, j, 0, a.V, bm);
-  ExactLds ex;
-  ex.hmass = hmass;
-  ex.hcnt = hcnt;
-  ex.su = su;
-  ex.sd = sd;
-  ex.sf = sf;
-  ex.si = si;
-  ex.ctot = ctot;
-  UnitOut out = uo[u];
-  // (the fallback bit stays set: every block of this launch enumerates the
-  // flagged units of a pass from these records, and a block that has
-  // finished its share of a pass must not change what a slower block, still
-  // enumerating that pass, reads)
-  out.flags = UO_SLOW | UO_FALLBACK;
-  out.accept = 1;
-  out.y = -1;
-  const RowStat P = row_stats_dev<SD_BF16, NT>(a, trow, a.V, c, pen, bm, ex, request_top_p(a, r));
-  if (P.flags & NONFINITE) {
-    if (tid == 0) {
-      out.flags = UO_NONFINITE | UO_FALLBACK;
-      uo[u] = out;
-    }
-    return;
-  }
-  if (bonus) {
-    const Drawn dw = draw_dev<SD_BF16, NT>(a, trow, trow, P, P, 1, out.v, pen, bm, ex);
-    if (tid == 0) {
-      out.y = dw.y;
-      out.S = (float)dw.S;
-      uo[u] = out;
-    }
-    return;
-  }
-  const RowStat Q = row_stats_dev<SD_BF16, NT>(a, drow, a.Vd, c, pen, bm, ex, request_top_p(a, r));
-  if (Q.flags & NONFINITE) {
-    if (tid == 0) {
-      out.flags = UO_NONFINITE | UO_FALLBACK;
-      uo[u] = out;
-    }
-    return;
-  }
-  const double d = pair_tv_dev<SD_BF16, NT>(a, trow, drow, P, Q, pen, bm, ex);
-  if (tid == 0) {
-    const int x = a.ids[(int64_t)r * a.K_max + j];
-    float kxp = -INFINITY, kxq = -INFINITY;
-    if (x >= 0 && x < a.V) {
-      kxp = load1<SD_BF16>(trow, x);
-      kxq = x < a.Vd ? load1<SD_BF16>(drow, x) : -INFINITY;
-      if (pen && ((bm[x >> 5] >> (x & 31)) & 1u)) {
-        kxp = penalize(kxp, a.rep);
-        kxq = penalize(kxq, a.rep);
-      }
-    }
-    const Decision dc = decide(P, Q, kxp, kxq, (double)T, (double)request_D(a, r), true, d, out.u);
-    out.d = (float)d;
-    out.th = (float)dc.th;
-    out.px = (float)dc.px;
-    out.qx = (float)dc.qx;
-    out.pix = (float)dc.pix;
-    out.accept = dc.accept ? 1 : 0;
-    if (dc.qx == 0.0) out.flags |= UO_QZERO;
-    s_acc = out.accept;
-  }
-  __syncthreads();
-  if (!s_acc) {
-    const Drawn dw = draw_dev<SD_BF16, NT>(a, trow, drow, P, Q, 0, out.v, pen, bm, ex);
-    if (tid == 0) {
-      out.y = dw.y;
-      out.S = (float)dw.S;
-      if (dw.resid_zero) out.flags |= UO_RESID_ZERO;
-    }
-  }
-  if (tid == 0) uo[u] = out;
-}
-
-// Exact multi-pass processing of the units k_pair_fast flagged: a small
-// grid walks every unit and takes the flagged ones (each block holds one CU,
-// so the idle cost of this launch stays a few microseconds).
-// The flagged units of this call (UO_FALLBACK records of units k_pair_fast
-// processed; units it skipped, an invalid request or a position beyond
-// K_r, hold no output of this call) are enumerated the same way by every
-// block and dealt out round robin: the k-th goes to block k % gridDim.x
-// (gridDim.x = min(nunits, FALLBACK_GRID)).  Each thread tests UPT units at
-// once, so a call with nothing flagged costs one memory round trip per
-// NT_FB * UPT units.
-__global__ __launch_bounds__(NT_FB) void k_pair_fallback(Args a, UnitOut* uo, int nunits) {
-  constexpr int NT = NT_FB;
-  constexpr int UPT = 8;
-  constexpr int MINE = (NT * UPT + FALLBACK_GRID - 1) / FALLBACK_GRID;   // per block per pass
-  __shared__ int wtot[NT / WAVE];
-  __shared__ int mine[MINE];
-  __shared__ int s_n;
-  const int tid = threadIdx.x;
-  const int npairs = a.B * a.K_max;
-  int base = 0;
-  for (int c = 0; c < nunits; c += NT * UPT) {
-    uint32_t fl = 0u;   // bit i: unit c + i NT + tid is flagged
-    uint32_t fw[UPT];
-    int kr[UPT];
-    float tr[UPT];
-    bool pok[UPT];
-    static_for<UPT>([&]<int i>() __attribute__((always_inline)) {
-      const int u = min(c + i * NT + tid, nunits - 1);   // loads stay unconditional
-      const int r = u < npairs ? u / a.K_max : u - npairs;
-      fw[i] = uo[u].flags;
-      kr[i] = request_k(a, r);
-      tr[i] = request_t(a, r);
-      pok[i] = params_ok(request_top_p(a, r), request_D(a, r));
-    });
-    static_for<UPT>([&]<int i>() __attribute__((always_inline)) {
-      const int u = c + i * NT + tid;
-      const bool bonus = u >= npairs;
-      const int j = bonus ? 0 : u % a.K_max;
-      const bool valid = u < nunits && kr[i] >= 0 && kr[i] <= a.K_max && (bonus || j < kr[i]) &&
-                         tr[i] > 0.0f && tr[i] < INFINITY && pok[i];
-      if (valid && (fw[i] & UO_FALLBACK)) fl |= 1u << i;
-    });
-    int total;
-    const int first = base + block_excl_scan_int<NT>(__builtin_popcount(fl), wtot, &total);
-    if (tid == 0) s_n = 0;
-    __syncthreads();
-    int rank = first;
-    while (fl) {
-      const int i = __builtin_ctz(fl);
-      fl &= fl - 1u;
-      if (rank % (int)gridDim.x == (int)blockIdx.x) mine[atomicAdd(&s_n, 1)] = c + i * NT + tid;
-      ++rank;
-    }
-    __syncthreads();
-    const int n = s_n;
-    for (int q = 0; q < n; ++q) {
-      fallback_unit(a, uo, mine[q]);
-      __syncthreads();   // the next unit reuses the shared arrays
-    }
-    base += total;
+  // The unit leaves the single pass (oflags holds UO_FALLBACK): the exact
+  // route, in the histogram and slot space.
+  {
+    unsigned char* const fb = reinterpret_cast<unsigned char*>(&hsl);
+    ExactLds ex;
+    ex.hmass = reinterpret_cast<uint64_t*>(fb);
+    ex.hcnt = reinterpret_cast<uint32_t*>(fb + HBINS * 8);
+    ex.su = reinterpret_cast<uint64_t*>(fb + HBINS * 12);
+    ex.sd = reinterpret_cast<double*>(fb + HBINS * 12 + NT * 8);
+    ex.ctot = reinterpret_cast<double*>(fb + HBINS * 12 + NT * 16);
+    ex.sf = sf;
+    ex.si = si;
+    static_assert(HBINS * 12 + NT_F * 16 + (MAXV_FAST / VEC / WAVE + 1) * 8 <= sizeof(HistSlots),
+                  "exact route LDS");
+    (void)oflags;
+    // (the arguments are read again from the kernel's argument segment, where
+    // the first parameter starts: held in registers from the kernel's start,
+    // the fields only this route uses would crowd the streams)
+#if __HIP_DEVICE_COMPILE__
+    auto kseg = __builtin_amdgcn_kernarg_segment_ptr();
+    asm volatile("" : "+s"(kseg));
+    typedef __attribute__((address_space(4))) const Args KArgs;
+    const Args ax = *(KArgs*)kseg;
+#else
+    const Args ax = a;   // (the host pass only parses device code)
+#endif
+    exact_unit<NT>(ax, uo, blockIdx.x, bm, ex, why);
   }
 }
 
@@ -2257,9 +2202,10 @@ bool needs_tv(const Args& a, const float* stats) {
   return stats != nullptr || a.dpr != nullptr || (a.D > 0.0f && a.D < 1.0f);
 }
 
-// One phase of the sampling path.  Single-pass path: 0 = k_pair_fast,
-// 1 = k_pair_fallback (exact re-read of flagged units), 2 = k_fast_finalize.  General path: 0 = k_row_prepare,
-// 1 = k_pair_tv (when needed), 2 = k_finalize.
+// One phase of the sampling path.  Single-pass path: 0 = k_pair_fast (with
+// the exact route of the units it cannot settle), 1 = no launch,
+// 2 = k_fast_finalize.  General path: 0 = k_row_prepare, 1 = k_pair_tv (when
+// needed), 2 = k_finalize.
 template <int DT>
 int run_phase(const Args& a, const Layout& L, char* ws, int phase, int32_t* acc, int32_t* tok,
               uint32_t* status, float* stats, hipStream_t st) {
@@ -2272,12 +2218,7 @@ int run_phase(const Args& a, const Layout& L, char* ws, int phase, int32_t* acc,
         hipLaunchKernelGGL(k_pair_fast<false>, dim3(a.B * a.K_max + a.B), dim3(NT_F), 0, st, a, uo);
       return launch_status();
     }
-    if (phase == 1) {
-      const int nunits = a.B * a.K_max + a.B;
-      hipLaunchKernelGGL(k_pair_fallback, dim3(nunits < FALLBACK_GRID ? nunits : FALLBACK_GRID),
-                         dim3(NT_FB), 0, st, a, uo, nunits);
-      return launch_status();
-    }
+    if (phase == 1) return SD_OK;   // (flagged units take the exact route inside k_pair_fast)
     hipLaunchKernelGGL(k_fast_finalize, dim3(a.B), dim3(64), 0, st, a, uo, acc, tok, status, stats);
     return launch_status();
   }
@@ -2462,7 +2403,7 @@ const char* sd_debug_phase_kernel(const sd_verify_args_t* args, int phase) {
   if (check_common(args, true) != SD_OK || phase < 0 || phase > 2) return nullptr;
   const Args a = make_args(args);
   if (a.dtype == SD_BF16 && use_fast(a)) {
-    static const char* const fast[3] = {"k_pair_fast", "k_pair_fallback", "k_fast_finalize"};
+    static const char* const fast[3] = {"k_pair_fast", nullptr, "k_fast_finalize"};
     return fast[phase];
   }
   if (phase == 0) return "k_row_prepare";

@@ -1,7 +1,7 @@
 // Exact row-level building blocks of the verify step, written for one
 // workgroup of NT threads that streams rows from global memory.  They serve
 // the general multi-pass path (any dtype, any V up to 2^19, top-p on or off)
-// and the in-kernel fallback of the single-pass kernel.  Every result is
+// and the exact route of the single-pass kernel.  Every result is
 // returned to all threads of the block.  Included by sd_verify.hip only.
 #pragma once
 #include "sdv_device.h"

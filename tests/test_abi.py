@@ -102,7 +102,7 @@ def test_phase_kernel_names_follow_the_path_choice():
     import speculative_sampling_verify_temp_amd as sdv
     a = _good_args(sdv)
     assert [sdv.phase_kernel(a, p) for p in range(3)] == \
-        ["k_pair_fast", "k_pair_fallback", "k_fast_finalize"]
+        ["k_pair_fast", None, "k_fast_finalize"]   # (flagged units: exact route inside k_pair_fast)
     a.top_p = 1.0   # no truncation: general path; TV needed for 0 < D < 1
     assert [sdv.phase_kernel(a, p) for p in range(3)] == \
         ["k_row_prepare", "k_pair_tv", "k_finalize"]

@@ -148,15 +148,13 @@ def test_single_pass_law_bf16_top_p():
         assert p1 > 1e-4 and p2 > 1e-4
 
 
-def test_fallback_over_several_passes():
-    """Every unit of a batch above 4096 units handed to the exact fallback:
-    its blocks deal the flagged units of each pass among themselves from the
-    unit records, which must read the same to every block for the whole
-    pass (a block that has finished its share may not change them).  Rows
-    whose maximum is small and whose mass sits largely on keys within 2^-20
-    of zero (here exact zeros) go to the fallback by construction; the
-    results must equal the general path's on the same values (fp32 input),
-    which runs the same exact routines."""
+def test_exact_route_for_every_unit():
+    """Every unit of a batch of 4400 units leaves the single pass for its
+    exact route (each workgroup settles its own flagged units at once, with
+    the general-path routines).  Rows whose maximum is small and whose mass
+    sits largely on keys within 2^-20 of zero (here exact zeros) leave it by
+    construction; the results must equal the general path's on the same
+    values (fp32 input), which runs the same exact routines."""
     import torch
     sdv = _sdv()
     rng = np.random.default_rng(31)
