@@ -48,6 +48,8 @@ constexpr int BK = 64;            // K chunk
 constexpr int LDK = BK + 8;       // LDS row stride of the A/B chunks (bf16): 144 B
 constexpr int NT_L = 256;         // threads of a tile workgroup (4 waves)
 constexpr int LDC = TN;           // LDS row stride of a stashed fp32 tile
+// LDS words of the A/B chunks or, after the product, the stashed fp32 tile
+constexpr int TILE_LDS_WORDS = (TM + TN) * LDK / 2 > TM * LDC ? (TM + TN) * LDK / 2 : TM * LDC;
 constexpr int NXCD = 8;           // dies of the device (tile order is per die)
 constexpr int SHL = 40;           // fixed-point shift of the draw weights (each <= 1)
 
@@ -300,9 +302,12 @@ __device__ __forceinline__ const uint16_t* hidden_row(const LmArgs& a, bool targ
 // ---------------------------------------------------------------------------
 template <bool TGT>
 __global__ __launch_bounds__(NT_L) void k_lm_stats(LmArgs a, LmWs w, int nm, int nn) {
-  __shared__ __align__(16) uint16_t sa[TM * LDK];
-  __shared__ __align__(16) uint16_t sb[TN * LDK];
-  __shared__ __align__(16) float C[TM * LDC];
+  // (the fp32 tile is stashed over the A/B chunks once the product is done:
+  // 32 KB of LDS instead of 60, so more workgroups share a CU)
+  __shared__ __align__(16) float lds_ab_c[TILE_LDS_WORDS];
+  uint16_t* const sa = reinterpret_cast<uint16_t*>(lds_ab_c);
+  uint16_t* const sb = sa + TM * LDK;
+  float* const C = lds_ab_c;
   int mb, nb;
   if (!tile_of(nm, nn, mb, nb)) return;
   const int nrows = w.cnt[TGT ? 0 : 1];
@@ -677,35 +682,60 @@ __global__ __launch_bounds__(NT_L) void k_lm_draw_pick(LmArgs a, LmWs w, int nn,
   const int K1 = a.K_max + 1;
   float u, v;
   uniforms(a.seed, a.offset, r, dr.y, u, v);
-  if (threadIdx.x == 0) {
-    // totals in tile order (one thread: nn is about a thousand)
-    int mode = dr.x;
-    uint64_t S = 0;
-    for (int t = 0; t < nn; ++t) S += w.wpart[((int64_t)r * nn + t) * 2 + mode];
-    if (S == 0 && mode == 0) {
-      mode = 1;
-      S = 0;
-      for (int t = 0; t < nn; ++t) S += w.wpart[((int64_t)r * nn + t) * 2 + 1];
-      if (out_status) out_status[r] |= SD_ST_RESID_ZERO;
+  // Totals in tile order, spread over the block: thread t sums tiles
+  // [t CH, t CH + CH); a block scan of those sums finds the thread whose
+  // range holds the crossing, and that thread walks its tiles.  (All sums
+  // are exact integers, so the order of the additions does not matter.)
+  {
+    const int t = threadIdx.x;
+    const int CH = (nn + NT_L - 1) / NT_L;
+    const int t0 = min(t * CH, nn), t1 = min(t0 + CH, nn);
+    uint64_t own0 = 0, own1 = 0;
+    for (int q = t0; q < t1; ++q) {
+      own0 += w.wpart[((int64_t)r * nn + q) * 2 + 0];
+      own1 += w.wpart[((int64_t)r * nn + q) * 2 + 1];
     }
+    const uint64_t S0 = block_sum_u64<NT_L>(own0, su);
+    const uint64_t S1 = block_sum_u64<NT_L>(own1, su);
+    int mode = dr.x;
+    if (mode == 0 && S0 == 0) mode = 1;
+    const uint64_t S = mode == 0 ? S0 : S1;
+    const uint64_t own = mode == 0 ? own0 : own1;
     const uint64_t vk = (uint64_t)(v * 0x1p24f);
     const uint64_t tf = (__umul64hi(vk, S) << 40) | ((vk * S) >> 24);   // floor(v S)
-    uint64_t acc = 0, alast = 0;
-    int tile = -1, last = -1;
-    uint64_t R = 0;
-    for (int t = 0; t < nn; ++t) {
-      const uint64_t x = w.wpart[((int64_t)r * nn + t) * 2 + mode];
-      if (x > 0) { last = t; alast = acc; }
-      if (tile < 0 && acc + x > tf) { tile = t; R = acc; }
-      acc += x;
+    // inclusive scan of the per-thread sums (Hillis-Steele in LDS)
+    __syncthreads();
+    su[t] = own;
+    __syncthreads();
+    for (int o = 1; o < NT_L; o <<= 1) {
+      const uint64_t y = t >= o ? su[t - o] : 0ull;
+      __syncthreads();
+      su[t] += y;
+      __syncthreads();
     }
-    if (tile < 0) { tile = last; R = alast; }
-    s_tile = tile;
-    s_R = R;
-    s_tf = tf;
-    s_S = S;
-    s_mode = mode;
-    s_y = -1;
+    const uint64_t incl = su[t], excl = incl - own;
+    if (t == 0) {
+      s_tile = -1;
+      s_tf = tf;
+      s_S = S;
+      s_mode = mode;
+      s_y = -1;
+      if (mode != dr.x && out_status) out_status[r] |= SD_ST_RESID_ZERO;
+    }
+    __syncthreads();
+    if (excl <= tf && incl > tf) {   // the one thread whose range crosses t
+      uint64_t acc = excl;
+      for (int q = t0; q < t1; ++q) {
+        const uint64_t x = w.wpart[((int64_t)r * nn + q) * 2 + mode];
+        if (acc + x > tf) {
+          s_tile = q;
+          s_R = acc;
+          break;
+        }
+        acc += x;
+      }
+    }
+    __syncthreads();
   }
   if (threadIdx.x < TM) reqs[threadIdx.x] = threadIdx.x == 0 ? r : -1;
   __syncthreads();
@@ -754,9 +784,12 @@ __global__ __launch_bounds__(NT_L) void k_lm_draw_pick(LmArgs a, LmWs w, int nn,
 // Greedy: per (listed target row, tile) the largest logit and its lowest id.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(NT_L) void k_lm_greedy_part(LmArgs a, LmWs w, int nm, int nn) {
-  __shared__ __align__(16) uint16_t sa[TM * LDK];
-  __shared__ __align__(16) uint16_t sb[TN * LDK];
-  __shared__ __align__(16) float C[TM * LDC];
+  // (the fp32 tile is stashed over the A/B chunks once the product is done:
+  // 32 KB of LDS instead of 60, so more workgroups share a CU)
+  __shared__ __align__(16) float lds_ab_c[TILE_LDS_WORDS];
+  uint16_t* const sa = reinterpret_cast<uint16_t*>(lds_ab_c);
+  uint16_t* const sb = sa + TM * LDK;
+  float* const C = lds_ab_c;
   int mb, nb;
   if (!tile_of(nm, nn, mb, nb)) return;
   const int nrows = w.cnt[0];
@@ -847,9 +880,12 @@ __global__ __launch_bounds__(64) void k_lm_greedy_final(LmArgs a, LmWs w, int nn
 // Test export: the logits of every listed row, written densely.
 template <bool TGT>
 __global__ __launch_bounds__(NT_L) void k_lm_dump(LmArgs a, LmWs w, int nm, int nn, float* out) {
-  __shared__ __align__(16) uint16_t sa[TM * LDK];
-  __shared__ __align__(16) uint16_t sb[TN * LDK];
-  __shared__ __align__(16) float C[TM * LDC];
+  // (the fp32 tile is stashed over the A/B chunks once the product is done:
+  // 32 KB of LDS instead of 60, so more workgroups share a CU)
+  __shared__ __align__(16) float lds_ab_c[TILE_LDS_WORDS];
+  uint16_t* const sa = reinterpret_cast<uint16_t*>(lds_ab_c);
+  uint16_t* const sb = sa + TM * LDK;
+  float* const C = lds_ab_c;
   int mb, nb;
   if (!tile_of(nm, nn, mb, nb)) return;
   const int nrows = w.cnt[TGT ? 0 : 1];
