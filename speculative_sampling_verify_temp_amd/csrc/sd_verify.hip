@@ -146,7 +146,7 @@ __global__ __launch_bounds__(NT_ROW) void k_pair_tv(Args a, const RowStat* rs, d
 // invalidating bit are never scanned, so SD_ST_NONFINITE appears only on a
 // request that passed every other check.
 template <int NT>
-__device__ uint32_t request_status(const Args& a, int r, int K, float T, bool check_temp,
+__device__ __forceinline__ uint32_t request_status(const Args& a, int r, int K, float T, bool check_temp,
                                    int* si) {
   const bool kbad = K < 0 || K > a.K_max;
   int badid = 0, badprior = 0;

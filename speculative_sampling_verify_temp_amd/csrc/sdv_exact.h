@@ -53,7 +53,7 @@ __device__ uint64_t block_incl_scan_u64(uint64_t x, uint64_t* buf) {
 // last non-empty bin if the masses never reach TP.  above_out = above0 +
 // mass of all bins above beta.  nbins is a multiple of NT or <= NT.
 template <int NT>
-__device__ void find_crossing(const uint64_t* hm, const uint32_t* hc, int nbins,
+__device__ __forceinline__ void find_crossing(const uint64_t* hm, const uint32_t* hc, int nbins,
                               uint64_t above0, double TP, int& beta_out,
                               uint64_t& above_out, uint64_t* sbuf, int* sint) {
   const int per = nbins >= NT ? nbins / NT : 1;
@@ -309,28 +309,34 @@ struct Drawn {
   int resid_zero;
 };
 
-// Inverse-CDF draw over ascending token ids with fp64 prefix sums: mode 0
-// draws from max(p - q, 0) (falling back to p when that has no mass), mode
-// 1 from p.  One coalesced pass (RU vectors in flight per thread) writes the
-// total of every chunk of 64 consecutive vectors (a wave's share of one
-// step) to L.ctot (nch + 1 doubles: the last holds the mass before the
-// crossing chunk); a block scan over the chunk totals finds the chunk that
-// holds t = v S; wave 0 reads that chunk again and scans it lane by lane;
-// the crossing lane walks its 8 tokens.  Every sum is fp64 in a fixed order.
+// Inverse-CDF draw over ascending token ids: mode 0 draws from
+// max(p - q, 0) (falling back to p when that has no mass), mode 1 from p.
+// One coalesced pass (RU vectors in flight per thread) writes the total of
+// every chunk to L.ctot (nch + 1 doubles: the last holds the mass before
+// the crossing chunk).  A chunk is one wave's share of one step, RU blocks
+// of 64 consecutive vectors in ascending order (256 consecutive vectors for
+// RU = 4), so a step takes one wave reduction, not one per vector.  A block
+// scan over the chunk totals finds the chunk that holds t = v S; wave 0
+// reads that chunk again and scans it block by block, lane by lane; the
+// crossing lane walks its 8 tokens.  A vector's weights are summed in fp32
+// in token order, the same running sum the walk compares, and every sum
+// above that is fp64 in a fixed order.
 template <int DT, int NT>
 __device__ __forceinline__ Drawn draw_dev(const Args& a, const char* trow, const char* drow, const RowStat& P,
                           const RowStat& Q, int mode, float v, bool pen, const uint32_t* bm,
                           const ExactLds& L) {
+  constexpr int CHV = RU * WAVE;   // vectors per chunk
   const int V = a.V, nvec = (V + VEC - 1) / VEC;
-  const int nch = (nvec + WAVE - 1) / WAVE;
+  const int nch = (nvec + CHV - 1) / CHV;
   const int lane = threadIdx.x % WAVE, wv = threadIdx.x / WAVE;
   const float ip = (float)(1.0 / P.Zk), iq = (float)(1.0 / Q.Zk);
   Drawn out;
   out.resid_zero = 0;
 
-  // fp64 total of the draw weights of vector k (0 past the row)
-  auto vec_sum = [&](int k, int md, float (&zp)[VEC], float (&zq)[VEC], float (&w)[VEC]) -> double {
-    double s = 0.0;
+  // draw weights of vector k (0 past the row) and their fp32 sum in token order
+  auto vec_w = [&](int k, int md, float (&zp)[VEC], float (&zq)[VEC], float (&w)[VEC])
+                   __attribute__((always_inline)) -> float {
+    float s = 0.0f;
     if (k >= nvec) {
 #pragma unroll
       for (int e = 0; e < VEC; ++e) w[e] = 0.0f;
@@ -347,11 +353,11 @@ __device__ __forceinline__ Drawn draw_dev(const Args& a, const char* trow, const
         p = fmaxf(p - q, 0.0f);
       }
       w[e] = p;
-      s += (double)p;
+      s += p;
     }
     return s;
   };
-  auto load2 = [&](int k, int md, float (&zp)[VEC], float (&zq)[VEC]) {
+  auto load2 = [&](int k, int md, float (&zp)[VEC], float (&zq)[VEC]) __attribute__((always_inline)) {
     load8_row<DT>(trow, k, k < nvec ? V : 0, zp);
     if (md == 0) load8_row<DT>(drow, k, k < nvec ? a.Vd : 0, zq);
   };
@@ -360,17 +366,19 @@ __device__ __forceinline__ Drawn draw_dev(const Args& a, const char* trow, const
   for (int pass = 0; pass < 2; ++pass) {
     // chunk totals: every wave runs every step (the wave sums need all lanes)
     for (int base = 0; base < nvec; base += RU * NT) {
+      const int k0 = base + wv * CHV;   // this wave's chunk
       float zp[RU][VEC], zq[RU][VEC];
 #pragma unroll
-      for (int u = 0; u < RU; ++u) load2(base + u * NT + (int)threadIdx.x, mode, zp[u], zq[u]);
+      for (int u = 0; u < RU; ++u) load2(k0 + u * WAVE + lane, mode, zp[u], zq[u]);
+      double ls = 0.0;
 #pragma unroll
       for (int u = 0; u < RU; ++u) {
         float w[VEC];
-        const double ls = vec_sum(base + u * NT + (int)threadIdx.x, mode, zp[u], zq[u], w);
-        const double cs = wave_sum(ls);
-        const int ch = (base + u * NT) / WAVE + wv;
-        if (lane == 0 && ch < nch) L.ctot[ch] = cs;
+        ls += (double)vec_w(k0 + u * WAVE + lane, mode, zp[u], zq[u], w);
       }
+      const double cs = wave_sum(ls);
+      const int ch = k0 / CHV;
+      if (lane == 0 && ch < nch) L.ctot[ch] = cs;
     }
     __syncthreads();
     // block scan over the chunk totals (thread t owns chunks t per ..)
@@ -411,27 +419,51 @@ __device__ __forceinline__ Drawn draw_dev(const Args& a, const char* trow, const
   out.S = S;
   const int cs = L.si[0];
   if (wv == 0 && cs >= 0) {
-    const int k = cs * WAVE + lane;
-    float zp[VEC], zq[VEC], w[VEC];
-    load2(k, mode, zp, zq);
-    const double ls = vec_sum(k, mode, zp, zq, w);
-    const double li = wave_incl_scan(ls);
-    const double R = L.ctot[nch];
-    const uint64_t hit = __ballot(R + li > t);
-    // the first lane whose inclusive total exceeds t, else (rounding) the
-    // last lane that carries weight
-    const uint64_t pos = __ballot(ls > 0.0);
-    const int src = hit ? __builtin_ctzll(hit) : (pos ? 63 - __builtin_clzll(pos) : -1);
-    if (lane == src) {
-      double C = R + li - ls;
-      int y = -1, lastpos = -1;
-      for (int e = 0; e < VEC; ++e) {
-        if (w[e] > 0.0f) lastpos = k * VEC + e;
-        C += (double)w[e];
-        if (C > t && hit) { y = k * VEC + e; break; }
+    // the crossing chunk's RU blocks of 64 vectors, in ascending order
+    float zp[RU][VEC], zq[RU][VEC];
+#pragma unroll
+    for (int u = 0; u < RU; ++u) load2(cs * CHV + u * WAVE + lane, mode, zp[u], zq[u]);
+    double R = L.ctot[nch];
+    int found = 0, y = -1, lastpos = -1;
+#pragma unroll
+    for (int u = 0; u < RU; ++u) {
+      const int k = cs * CHV + u * WAVE + lane;
+      float w[VEC];
+      const double ls = (double)vec_w(k, mode, zp[u], zq[u], w);
+      const double li = wave_incl_scan(ls);
+      // the last token with weight so far (rounding fallback)
+      const uint64_t pos = __ballot(ls > 0.0);
+      if (pos) {
+        const int lp = 63 - __builtin_clzll(pos);
+        int e_last = -1;
+#pragma unroll
+        for (int e = 0; e < VEC; ++e)
+          if (w[e] > 0.0f) e_last = e;
+        const int cand = __shfl(k * VEC + e_last, lp);
+        lastpos = cand;
       }
-      L.si[1] = (y >= 0) ? y : lastpos;
+      if (!found) {
+        // the first lane whose inclusive total exceeds t walks its tokens
+        const uint64_t hit = __ballot(R + li > t);
+        if (hit) {
+          const int src = __builtin_ctzll(hit);
+          int yy = -1;
+          if (lane == src) {
+            const double C0 = R + li - ls;
+            float c = 0.0f;
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) {
+              c += w[e];
+              if (yy < 0 && C0 + (double)c > t) yy = k * VEC + e;
+            }
+          }
+          y = __shfl(yy, src);
+          found = 1;
+        }
+        R += __shfl(li, WAVE - 1);
+      }
     }
+    if (lane == 0) L.si[1] = (found && y >= 0) ? y : lastpos;
   }
   __syncthreads();
   out.y = L.si[1];
