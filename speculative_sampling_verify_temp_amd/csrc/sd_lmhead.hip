@@ -50,6 +50,12 @@ constexpr int NT_L = 256;         // threads of a tile workgroup (4 waves)
 constexpr int LDC = TN;           // LDS row stride of a stashed fp32 tile
 // LDS words of the A/B chunks or, after the product, the stashed fp32 tile
 constexpr int TILE_LDS_WORDS = (TM + TN) * LDK / 2 > TM * LDC ? (TM + TN) * LDK / 2 : TM * LDC;
+// The row-statistics and greedy passes take taller tiles, MBS 64-row parts
+// (each head tile is then read once per 192 rows instead of per 64), and
+// stash their result one 64-row part at a time over the chunk buffers.
+constexpr int MBS = 3;
+constexpr int TMS = 64 * MBS;
+constexpr int TALL_LDS_WORDS = (TMS + TN) * LDK / 2 > TM * LDC ? (TMS + TN) * LDK / 2 : TM * LDC;
 constexpr int NXCD = 8;           // dies of the device (tile order is per die)
 constexpr int SHL = 40;           // fixed-point shift of the draw weights (each <= 1)
 
@@ -208,15 +214,18 @@ struct TileLds {
   uint16_t* b;   // [TN][LDK]
 };
 
-// acc[nb] = rows (TM) x tokens (TN) of hidden x head^T.  arow[i]: this
-// thread's two A rows (i = 0, 1: tile rows t / 8 and t / 8 + 32), null for
-// a row past the list; weight rows n0 .. n0 + TN - 1 past nrows_w read 0.
-// Wave (wr, wc) = (wave / 2, wave % 2) holds rows 32 wr + m and tokens
+// acc[mb][nb] = rows (64 MB) x tokens (TN) of hidden x head^T.  arow[i]:
+// this thread's A rows (tile rows t / 8 + 32 i, i < 2 MB), null for a row
+// past the list; weight rows n0 .. n0 + TN - 1 past nrows_w read 0.  Wave
+// (wr, wc) = (wave / 2, wave % 2) holds rows 32 (MB wr + mb) + m and tokens
 // 64 wc + 32 b + n (b = 0, 1) in the MFMA 32x32 output layout: lane l, value
-// v: n = l % 32, m = 8 (v / 4) + 4 (l / 32) + v % 4.
-__device__ __forceinline__ void tile_gemm(const uint16_t* const (&arow)[2], const uint16_t* w,
+// v: n = l % 32, m = 8 (v / 4) + 4 (l / 32) + v % 4.  Every logit is the
+// same K-ordered chain of MFMA steps whatever MB is, so tiles of any height
+// give the same logits bit for bit.
+template <int MB>
+__device__ __forceinline__ void tile_gemm(const uint16_t* const (&arow)[2 * MB], const uint16_t* w,
                                           int n0, int nrows_w, int H, const TileLds& s,
-                                          f32x16 (&acc)[2]) {
+                                          f32x16 (&acc)[MB][2]) {
   const int t = threadIdx.x;
   const int lane = t % WAVE, wv = t / WAVE;
   const int wr = wv >> 1, wc = wv & 1;
@@ -229,24 +238,26 @@ __device__ __forceinline__ void tile_gemm(const uint16_t* const (&arow)[2], cons
     brow[i] = n < nrows_w ? w + (int64_t)n * H : nullptr;
   }
 #pragma unroll
-  for (int b = 0; b < 2; ++b)
+  for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-    for (int v = 0; v < 16; ++v) acc[b][v] = 0.0f;
-  uint4 ra[2], rb[4];
-  auto load = [&](int k0) {
+    for (int b = 0; b < 2; ++b)
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+      for (int v = 0; v < 16; ++v) acc[mb][b][v] = 0.0f;
+  uint4 ra[2 * MB], rb[4];
+  auto load = [&](int k0) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < 2 * MB; ++i)
       ra[i] = arow[i] ? *reinterpret_cast<const uint4*>(arow[i] + k0 + kc) : make_uint4(0, 0, 0, 0);
 #pragma unroll
     for (int i = 0; i < 4; ++i)
       rb[i] = brow[i] ? *reinterpret_cast<const uint4*>(brow[i] + k0 + kc) : make_uint4(0, 0, 0, 0);
   };
   load(0);
-  const int am = 32 * wr + (lane & 31), ko = 8 * (lane >> 5);
+  const int ko = 8 * (lane >> 5);
   for (int k0 = 0; k0 < H; k0 += BK) {
     __syncthreads();   // the previous chunk's fragments are read
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < 2 * MB; ++i)
       *reinterpret_cast<uint4*>(s.a + (rr + 32 * i) * LDK + kc) = ra[i];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
@@ -255,14 +266,40 @@ __device__ __forceinline__ void tile_gemm(const uint16_t* const (&arow)[2], cons
     if (k0 + BK < H) load(k0 + BK);   // the next chunk's loads overlap this chunk's MFMAs
 #pragma unroll
     for (int st = 0; st < BK / 16; ++st) {
-      const bf16x8 af = *reinterpret_cast<const bf16x8*>(s.a + am * LDK + 16 * st + ko);
+      bf16x8 af[MB];
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb)
+        af[mb] = *reinterpret_cast<const bf16x8*>(s.a + (32 * (MB * wr + mb) + (lane & 31)) * LDK + 16 * st + ko);
 #pragma unroll
       for (int b = 0; b < 2; ++b) {
         const int bn = 64 * wc + 32 * b + (lane & 31);
         const bf16x8 bfr = *reinterpret_cast<const bf16x8*>(s.b + bn * LDK + 16 * st + ko);
-        acc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, bfr, acc[b], 0, 0, 0);
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+          acc[mb][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[mb], bfr, acc[mb][b], 0, 0, 0);
       }
     }
+  }
+}
+
+// Rows 64 p .. 64 p + 63 of a tile of 64 MB rows into an fp32 LDS tile
+// C[64][LDC] (the waves holding other rows write nothing).
+template <int MB>
+__device__ __forceinline__ void stash_part(const f32x16 (&acc)[MB][2], float* C, int p) {
+  const int lane = threadIdx.x % WAVE, wv = threadIdx.x / WAVE;
+  const int wr = wv >> 1, wc = wv & 1;
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb) {
+    const int row0 = 32 * (MB * wr + mb) - 64 * p;
+    if (row0 < 0 || row0 >= 64) continue;
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int m = row0 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+        const int n = 64 * wc + 32 * b + (lane & 31);
+        C[m * LDC + n] = acc[mb][b][v];
+      }
   }
 }
 
@@ -302,75 +339,79 @@ __device__ __forceinline__ const uint16_t* hidden_row(const LmArgs& a, bool targ
 // ---------------------------------------------------------------------------
 template <bool TGT>
 __global__ __launch_bounds__(NT_L) void k_lm_stats(LmArgs a, LmWs w, int nm, int nn) {
-  // (the fp32 tile is stashed over the A/B chunks once the product is done:
-  // 32 KB of LDS instead of 60, so more workgroups share a CU)
-  __shared__ __align__(16) float lds_ab_c[TILE_LDS_WORDS];
+  // (each fp32 part is stashed over the A/B chunks once the product is done)
+  __shared__ __align__(16) float lds_ab_c[TALL_LDS_WORDS];
   uint16_t* const sa = reinterpret_cast<uint16_t*>(lds_ab_c);
-  uint16_t* const sb = sa + TM * LDK;
+  uint16_t* const sb = sa + TMS * LDK;
   float* const C = lds_ab_c;
   int mb, nb;
   if (!tile_of(nm, nn, mb, nb)) return;
   const int nrows = w.cnt[TGT ? 0 : 1];
-  const int m0 = mb * TM, n0 = nb * TN;
+  const int m0 = mb * TMS, n0 = nb * TN;
   if (m0 >= nrows) return;
   const int* list = TGT ? w.tlist : w.dlist;
   const int rr = threadIdx.x >> 3;
-  const uint16_t* arow[2];
+  const uint16_t* arow[2 * MBS];
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
+  for (int i = 0; i < 2 * MBS; ++i) {
     const int li = m0 + rr + 32 * i;
     arow[i] = li < nrows ? hidden_row(a, TGT, list[li]) : nullptr;
   }
   const int Vs = TGT ? a.V : a.Vd;
-  f32x16 acc[2];
-  tile_gemm(arow, TGT ? a.wt : a.wd, n0, Vs, TGT ? a.Ht : a.Hd, TileLds{sa, sb}, acc);
-  __syncthreads();
-  stash(acc, C);
-  __syncthreads();
-  // four threads per row, 32 tokens each
-  const int row = threadIdx.x >> 2, q4 = threadIdx.x & 3;
-  const int li = m0 + row;
-  const bool live = li < nrows;
-  int r = 0, j = 0;
-  float c = 1.0f;
-  int x = -1;
-  if (live) {
-    const int enc = list[li];
-    r = TGT ? enc / (a.K_max + 1) : enc / a.K_max;
-    j = TGT ? enc % (a.K_max + 1) : enc % a.K_max;
-    c = 1.4426950408889634f / req_t(a, r);
-    if (j < req_k(a, r)) x = a.ids[(int64_t)r * a.K_max + j];
-  }
-  float m = -INFINITY;
-  int bad = 0;
+  f32x16 acc[MBS][2];
+  tile_gemm<MBS>(arow, TGT ? a.wt : a.wd, n0, Vs, TGT ? a.Ht : a.Hd, TileLds{sa, sb}, acc);
   const int nv = min(TN, Vs - n0);
-  for (int e = 0; e < 32; ++e) {
-    const int n = q4 * 32 + e;
-    if (n < nv) {
-      const float z = C[row * LDC + n];
-      bad |= nonfinite(z);
-      m = fmaxf(m, z * c);
+  // (unrolled: each part reads its own accumulators where it stashes them)
+#pragma unroll
+  for (int part = 0; part < MBS; ++part) {
+    if (m0 + 64 * part >= nrows) continue;
+    __syncthreads();   // the chunk buffers, or the previous part, are read
+    stash_part<MBS>(acc, C, part);
+    __syncthreads();
+    // four threads per row, 32 tokens each
+    const int row = threadIdx.x >> 2, q4 = threadIdx.x & 3;
+    const int li = m0 + 64 * part + row;
+    const bool live = li < nrows;
+    int r = 0, j = 0;
+    float c = 1.0f;
+    int x = -1;
+    if (live) {
+      const int enc = list[li];
+      r = TGT ? enc / (a.K_max + 1) : enc / a.K_max;
+      j = TGT ? enc % (a.K_max + 1) : enc % a.K_max;
+      c = 1.4426950408889634f / req_t(a, r);
+      if (j < req_k(a, r)) x = a.ids[(int64_t)r * a.K_max + j];
     }
-    if (live && n0 + n == x && n < nv) {
-      RowSL* rs = (TGT ? w.trs : w.drs) + li;
-      rs->zx = C[row * LDC + n];
-    }
-  }
-  m = fmaxf(m, __shfl_xor(m, 1));
-  m = fmaxf(m, __shfl_xor(m, 2));
-  float s = 0.0f;
-  if (m > -INFINITY)
+    float m = -INFINITY;
+    int bad = 0;
     for (int e = 0; e < 32; ++e) {
       const int n = q4 * 32 + e;
-      if (n < nv) s += fast_exp2(C[row * LDC + n] * c - m);
+      if (n < nv) {
+        const float z = C[row * LDC + n];
+        bad |= nonfinite(z);
+        m = fmaxf(m, z * c);
+      }
+      if (live && n0 + n == x && n < nv) {
+        RowSL* rs = (TGT ? w.trs : w.drs) + li;
+        rs->zx = C[row * LDC + n];
+      }
     }
-  s += __shfl_xor(s, 1);
-  s += __shfl_xor(s, 2);
-  bad |= __shfl_xor(bad, 1);
-  bad |= __shfl_xor(bad, 2);
-  if (live && q4 == 0) {
-    float2* part = (TGT ? w.tpart : w.dpart) + (int64_t)li * nn + nb;
-    *part = make_float2(bad ? NAN : m, s);
+    m = fmaxf(m, __shfl_xor(m, 1));
+    m = fmaxf(m, __shfl_xor(m, 2));
+    float s = 0.0f;
+    if (m > -INFINITY)
+      for (int e = 0; e < 32; ++e) {
+        const int n = q4 * 32 + e;
+        if (n < nv) s += fast_exp2(C[row * LDC + n] * c - m);
+      }
+    s += __shfl_xor(s, 1);
+    s += __shfl_xor(s, 2);
+    bad |= __shfl_xor(bad, 1);
+    bad |= __shfl_xor(bad, 2);
+    if (live && q4 == 0) {
+      float2* part_out = (TGT ? w.tpart : w.dpart) + (int64_t)li * nn + nb;
+      *part_out = make_float2(bad ? NAN : m, s);
+    }
   }
 }
 
@@ -449,7 +490,7 @@ __global__ __launch_bounds__(NT_L) void k_lm_tv(LmArgs a, LmWs w, int nm, int nn
   __syncthreads();
   const int rr = threadIdx.x >> 3;
   TileLds s{reinterpret_cast<uint16_t*>(U), reinterpret_cast<uint16_t*>(U) + TM * LDK};
-  f32x16 acc[2];
+  f32x16 acc[1][2];
   {
     const uint16_t* arow[2];
 #pragma unroll
@@ -457,8 +498,8 @@ __global__ __launch_bounds__(NT_L) void k_lm_tv(LmArgs a, LmWs w, int nm, int nn
       const int tli = s_tli[rr + 32 * i];
       arow[i] = tli >= 0 ? hidden_row(a, true, w.tlist[tli]) : nullptr;
     }
-    tile_gemm(arow, a.wt, n0, a.V, a.Ht, s, acc);
-    stash(acc, Ct);
+    tile_gemm<1>(arow, a.wt, n0, a.V, a.Ht, s, acc);
+    stash(acc[0], Ct);
   }
   {
     const uint16_t* arow[2];
@@ -467,10 +508,10 @@ __global__ __launch_bounds__(NT_L) void k_lm_tv(LmArgs a, LmWs w, int nm, int nn
       const int p = m0 + rr + 32 * i;
       arow[i] = p < npairs ? hidden_row(a, false, w.dlist[p]) : nullptr;
     }
-    tile_gemm(arow, a.wd, n0, a.Vd, a.Hd, s, acc);
+    tile_gemm<1>(arow, a.wd, n0, a.Vd, a.Hd, s, acc);
   }
   __syncthreads();
-  stash(acc, U);
+  stash(acc[0], U);
   __syncthreads();
   const int row = threadIdx.x >> 2, q4 = threadIdx.x & 3;
   const int p = m0 + row;
@@ -583,7 +624,7 @@ __device__ __forceinline__ void draw_w(float zt, float zd, bool has_q, const Row
 // The tiles of a draw: requests r with a draw, 64 per block, the target row
 // (r, n) and (mode 0) the draft row (r, n).
 __device__ __forceinline__ void draw_tiles_gemm(const LmArgs& a, const LmWs& w, const int* reqs,
-                                                int n0, float* Ct, float* U, f32x16 (&acc)[2]) {
+                                                int n0, float* Ct, float* U, f32x16 (&acc)[1][2]) {
   const int rr = threadIdx.x >> 3;
   TileLds s{reinterpret_cast<uint16_t*>(U), reinterpret_cast<uint16_t*>(U) + TM * LDK};
   {
@@ -597,8 +638,8 @@ __device__ __forceinline__ void draw_tiles_gemm(const LmArgs& a, const LmWs& w, 
         arow[i] = hidden_row(a, true, w.tlist[w.toff[r] + dr.y]);
       }
     }
-    tile_gemm(arow, a.wt, n0, a.V, a.Ht, s, acc);
-    stash(acc, Ct);
+    tile_gemm<1>(arow, a.wt, n0, a.V, a.Ht, s, acc);
+    stash(acc[0], Ct);
   }
   {
     const uint16_t* arow[2];
@@ -611,10 +652,10 @@ __device__ __forceinline__ void draw_tiles_gemm(const LmArgs& a, const LmWs& w, 
         if (dr.x == 0) arow[i] = hidden_row(a, false, w.dlist[w.doff[r] + dr.y]);
       }
     }
-    tile_gemm(arow, a.wd, n0, a.Vd, a.Hd, s, acc);
+    tile_gemm<1>(arow, a.wd, n0, a.Vd, a.Hd, s, acc);
   }
   __syncthreads();
-  stash(acc, U);
+  stash(acc[0], U);
   __syncthreads();
 }
 
@@ -633,7 +674,7 @@ __global__ __launch_bounds__(NT_L) void k_lm_draw_tiles(LmArgs a, LmWs w, int nm
   int any = 0;
   for (int i = 0; i < TM; ++i) any |= reqs[i] >= 0;
   if (!any) return;
-  f32x16 acc[2];
+  f32x16 acc[1][2];
   draw_tiles_gemm(a, w, reqs, n0, Ct, U, acc);
   const int row = threadIdx.x >> 2, q4 = threadIdx.x & 3;
   const int r = reqs[row];
@@ -748,7 +789,7 @@ __global__ __launch_bounds__(NT_L) void k_lm_draw_pick(LmArgs a, LmWs w, int nn,
     return;
   }
   const int n0 = tile * TN;
-  f32x16 acc[2];
+  f32x16 acc[1][2];
   draw_tiles_gemm(a, w, reqs, n0, Ct, U, acc);
   // row 0 of the tile: per-token fixed weights, two per thread in id order
   const RowSL P = w.trs[w.toff[r] + dr.y];
@@ -784,51 +825,55 @@ __global__ __launch_bounds__(NT_L) void k_lm_draw_pick(LmArgs a, LmWs w, int nn,
 // Greedy: per (listed target row, tile) the largest logit and its lowest id.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(NT_L) void k_lm_greedy_part(LmArgs a, LmWs w, int nm, int nn) {
-  // (the fp32 tile is stashed over the A/B chunks once the product is done:
-  // 32 KB of LDS instead of 60, so more workgroups share a CU)
-  __shared__ __align__(16) float lds_ab_c[TILE_LDS_WORDS];
+  // (each fp32 part is stashed over the A/B chunks once the product is done)
+  __shared__ __align__(16) float lds_ab_c[TALL_LDS_WORDS];
   uint16_t* const sa = reinterpret_cast<uint16_t*>(lds_ab_c);
-  uint16_t* const sb = sa + TM * LDK;
+  uint16_t* const sb = sa + TMS * LDK;
   float* const C = lds_ab_c;
   int mb, nb;
   if (!tile_of(nm, nn, mb, nb)) return;
   const int nrows = w.cnt[0];
-  const int m0 = mb * TM, n0 = nb * TN;
+  const int m0 = mb * TMS, n0 = nb * TN;
   if (m0 >= nrows) return;
   const int rr = threadIdx.x >> 3;
-  const uint16_t* arow[2];
+  const uint16_t* arow[2 * MBS];
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
+  for (int i = 0; i < 2 * MBS; ++i) {
     const int li = m0 + rr + 32 * i;
     arow[i] = li < nrows ? hidden_row(a, true, w.tlist[li]) : nullptr;
   }
-  f32x16 acc[2];
-  tile_gemm(arow, a.wt, n0, a.V, a.Ht, TileLds{sa, sb}, acc);
-  __syncthreads();
-  stash(acc, C);
-  __syncthreads();
-  const int row = threadIdx.x >> 2, q4 = threadIdx.x & 3;
-  const int li = m0 + row;
-  uint32_t bo = 0u;
-  int bi = INT_MAX;
-  int nan = 0;
+  f32x16 acc[MBS][2];
+  tile_gemm<MBS>(arow, a.wt, n0, a.V, a.Ht, TileLds{sa, sb}, acc);
   const int nv = min(TN, a.V - n0);
-  for (int e = 0; e < 32; ++e) {
-    const int n = q4 * 32 + e;
-    if (n >= nv) continue;
-    const float z = C[row * LDC + n];
-    if (z != z) { nan = 1; continue; }
-    const uint32_t o = ord_key(z);
-    if (o > bo || (o == bo && n0 + n < bi)) { bo = o; bi = n0 + n; }
-  }
+  // (unrolled: each part reads its own accumulators where it stashes them)
 #pragma unroll
-  for (int off = 1; off < 4; off <<= 1) {
-    const uint32_t o2 = __shfl_xor(bo, off);
-    const int i2 = __shfl_xor(bi, off);
-    if (o2 > bo || (o2 == bo && i2 < bi)) { bo = o2; bi = i2; }
-    nan |= __shfl_xor(nan, off);
+  for (int part = 0; part < MBS; ++part) {
+    if (m0 + 64 * part >= nrows) continue;
+    __syncthreads();   // the chunk buffers, or the previous part, are read
+    stash_part<MBS>(acc, C, part);
+    __syncthreads();
+    const int row = threadIdx.x >> 2, q4 = threadIdx.x & 3;
+    const int li = m0 + 64 * part + row;
+    uint32_t bo = 0u;
+    int bi = INT_MAX;
+    int nan = 0;
+    for (int e = 0; e < 32; ++e) {
+      const int n = q4 * 32 + e;
+      if (n >= nv) continue;
+      const float z = C[row * LDC + n];
+      if (z != z) { nan = 1; continue; }
+      const uint32_t o = ord_key(z);
+      if (o > bo || (o == bo && n0 + n < bi)) { bo = o; bi = n0 + n; }
+    }
+#pragma unroll
+    for (int off = 1; off < 4; off <<= 1) {
+      const uint32_t o2 = __shfl_xor(bo, off);
+      const int i2 = __shfl_xor(bi, off);
+      if (o2 > bo || (o2 == bo && i2 < bi)) { bo = o2; bi = i2; }
+      nan |= __shfl_xor(nan, off);
+    }
+    if (li < nrows && q4 == 0) w.gpart[(int64_t)li * nn + nb] = make_uint2(nan ? 0xFFFFFFFFu : bo, (uint32_t)bi);
   }
-  if (li < nrows && q4 == 0) w.gpart[(int64_t)li * nn + nb] = make_uint2(nan ? 0xFFFFFFFFu : bo, (uint32_t)bi);
 }
 
 __global__ __launch_bounds__(64) void k_lm_greedy_final(LmArgs a, LmWs w, int nn, int32_t* out_acc,
@@ -900,10 +945,10 @@ __global__ __launch_bounds__(NT_L) void k_lm_dump(LmArgs a, LmWs w, int nm, int 
     arow[i] = li < nrows ? hidden_row(a, TGT, list[li]) : nullptr;
   }
   const int Vs = TGT ? a.V : a.Vd;
-  f32x16 acc[2];
-  tile_gemm(arow, TGT ? a.wt : a.wd, n0, Vs, TGT ? a.Ht : a.Hd, TileLds{sa, sb}, acc);
+  f32x16 acc[1][2];
+  tile_gemm<1>(arow, TGT ? a.wt : a.wd, n0, Vs, TGT ? a.Ht : a.Hd, TileLds{sa, sb}, acc);
   __syncthreads();
-  stash(acc, C);
+  stash(acc[0], C);
   __syncthreads();
   for (int i = threadIdx.x; i < TM * TN; i += NT_L) {
     const int row = i / TN, n = i % TN;
@@ -1006,10 +1051,11 @@ int sd_lmhead_verify_sample(const sd_lmhead_args_t* args, void* workspace, size_
   rc = lm_prepare(a, L, w, true, st);
   if (rc) return rc;
   const int nt_max = a.B * (a.K_max + 1), nd_max = a.B * a.K_max;
-  const int nmt = (nt_max + TM - 1) / TM, nmd = (nd_max + TM - 1) / TM;
-  hipLaunchKernelGGL(k_lm_stats<true>, dim3(tile_grid(nmt, L.ntt)), dim3(NT_L), 0, st, a, w, nmt, L.ntt);
+  const int nmd = (nd_max + TM - 1) / TM;   // 64-row tiles of the pair kernels
+  const int nst = (nt_max + TMS - 1) / TMS, nsd = (nd_max + TMS - 1) / TMS;   // tall tiles
+  hipLaunchKernelGGL(k_lm_stats<true>, dim3(tile_grid(nst, L.ntt)), dim3(NT_L), 0, st, a, w, nst, L.ntt);
   if (nd_max > 0)
-    hipLaunchKernelGGL(k_lm_stats<false>, dim3(tile_grid(nmd, L.ntd)), dim3(NT_L), 0, st, a, w, nmd, L.ntd);
+    hipLaunchKernelGGL(k_lm_stats<false>, dim3(tile_grid(nsd, L.ntd)), dim3(NT_L), 0, st, a, w, nsd, L.ntd);
   hipLaunchKernelGGL(k_lm_rowstat<true>, dim3(nt_max), dim3(256), 0, st, a, w, L.ntt);
   if (nd_max > 0)
     hipLaunchKernelGGL(k_lm_rowstat<false>, dim3(nd_max), dim3(256), 0, st, a, w, L.ntd);
@@ -1041,7 +1087,7 @@ int sd_lmhead_verify_greedy(const sd_lmhead_args_t* args, void* workspace, size_
   hipStream_t st = static_cast<hipStream_t>(stream);
   rc = lm_prepare(a, L, w, false, st);
   if (rc) return rc;
-  const int nmt = (a.B * (a.K_max + 1) + TM - 1) / TM;
+  const int nmt = (a.B * (a.K_max + 1) + TMS - 1) / TMS;
   hipLaunchKernelGGL(k_lm_greedy_part, dim3(tile_grid(nmt, L.ntt)), dim3(NT_L), 0, st, a, w, nmt, L.ntt);
   hipLaunchKernelGGL(k_lm_greedy_final, dim3((a.B + 63) / 64), dim3(64), 0, st, a, w, L.ntt,
                      out_accepted, out_tokens, out_status, out_argmax);
