@@ -124,6 +124,53 @@ __device__ __forceinline__ void load8_row(const char* row, int k, int Vr, float 
   }
 }
 
+// Raw words of one 8-logit vector: one 16-byte word (bf16) or two (fp32).
+template <int DT>
+struct RawVec {
+  uint4 w[DT == SD_BF16 ? 1 : 2];
+};
+
+// Issues the loads of vector k of a row of Vr logits and returns their
+// destination registers without waiting; a vector past the row end reads
+// nothing (zero words, which unpack turns into -inf).
+template <int DT>
+__device__ __forceinline__ RawVec<DT> load_raw(const char* row, int k, int Vr) {
+  RawVec<DT> r;
+  const uint4* p = reinterpret_cast<const uint4*>(row);
+  const bool in = k * VEC < Vr;
+  if constexpr (DT == SD_BF16) {
+    r.w[0] = in ? p[k] : make_uint4(0, 0, 0, 0);
+  } else {
+    r.w[0] = in ? p[2 * k] : make_uint4(0, 0, 0, 0);
+    r.w[1] = (in && k * VEC + 4 < Vr) ? p[2 * k + 1] : make_uint4(0, 0, 0, 0);
+  }
+  return r;
+}
+
+// The logits of a loaded vector k of a row of Vr logits (-inf past its end).
+template <int DT>
+__device__ __forceinline__ void unpack(const RawVec<DT>& r, int k, int Vr, float (&z)[VEC]) {
+  if constexpr (DT == SD_BF16) {
+    const uint32_t u[4] = {r.w[0].x, r.w[0].y, r.w[0].z, r.w[0].w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      z[2 * e] = __uint_as_float(u[e] << 16);
+      z[2 * e + 1] = __uint_as_float(u[e] & 0xFFFF0000u);
+    }
+  } else {
+    z[0] = __uint_as_float(r.w[0].x); z[1] = __uint_as_float(r.w[0].y);
+    z[2] = __uint_as_float(r.w[0].z); z[3] = __uint_as_float(r.w[0].w);
+    z[4] = __uint_as_float(r.w[1].x); z[5] = __uint_as_float(r.w[1].y);
+    z[6] = __uint_as_float(r.w[1].z); z[7] = __uint_as_float(r.w[1].w);
+  }
+  const int i0 = k * VEC;
+  if (i0 + VEC > Vr) {
+#pragma unroll
+    for (int e = 0; e < VEC; ++e)
+      if (i0 + e >= Vr) z[e] = -INFINITY;
+  }
+}
+
 template <int DT>
 __device__ __forceinline__ float load1(const char* row, int i) {
   if constexpr (DT == SD_BF16) {

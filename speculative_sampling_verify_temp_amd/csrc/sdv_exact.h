@@ -92,23 +92,67 @@ __device__ __forceinline__ void find_crossing(const uint64_t* hm, const uint32_t
   __syncthreads();
 }
 
-// Loads in flight per thread in the row passes below: each thread issues
-// the loads of RU strided vectors before it uses any of them.
+// Vectors per thread and step of the row passes below: RU over one row, RU2
+// over two rows side by side.  A step's loads go out while the step before
+// it computes (two register sets), so 2 RU (or 2 x 2 RU2) loads per thread
+// are in flight.
 constexpr int RU = 4;
+constexpr int RU2 = 2;
+
+// Streams one row (TWO: two rows, r2 beside r1) in steps of RUX vectors per
+// thread: kv(base, u) is the vector a thread takes as the u-th of the step
+// at base (steps at base = 0, RUX NT, ... while base < nvec; every thread
+// runs every step); step(base, z1, z2) gets the step's logits unpacked
+// (-inf past a row's end, which holds V1 or V2 logits; vectors k >= nvec
+// read nothing).  The next step's loads are in flight while a step runs.
+template <int DT, int NT, int RUX, bool TWO, class KV, class STEP>
+__device__ __forceinline__ void stream_steps(const char* r1, int V1, const char* r2, int V2, int nvec,
+                                             KV&& kv, STEP&& step) {
+  RawVec<DT> a1[RUX], a2[RUX], b1[RUX], b2[RUX];
+  auto issue = [&](int base, RawVec<DT> (&x1)[RUX], RawVec<DT> (&x2)[RUX]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int u = 0; u < RUX; ++u) {
+      const int k = kv(base, u);
+      const bool in = base < nvec && k < nvec;
+      x1[u] = load_raw<DT>(r1, k, in ? V1 : 0);
+      if constexpr (TWO) x2[u] = load_raw<DT>(r2, k, in ? V2 : 0);
+    }
+  };
+  auto run = [&](int base, const RawVec<DT> (&x1)[RUX], const RawVec<DT> (&x2)[RUX]) __attribute__((always_inline)) {
+    float z1[RUX][VEC], z2[RUX][VEC];
+#pragma unroll
+    for (int u = 0; u < RUX; ++u) {
+      const int k = kv(base, u);
+      unpack<DT>(x1[u], k, k < nvec ? V1 : 0, z1[u]);
+      if constexpr (TWO) unpack<DT>(x2[u], k, k < nvec ? V2 : 0, z2[u]);
+    }
+    step(base, z1, z2);
+  };
+  constexpr int SV = RUX * NT;
+  issue(0, a1, a2);
+  for (int base = 0; base < nvec; base += 2 * SV) {
+    issue(base + SV, b1, b2);
+    run(base, a1, a2);
+    if (base + SV >= nvec) break;
+    issue(base + 2 * SV, a1, a2);
+    run(base + SV, b1, b2);
+  }
+}
 
 // One pass over vectors k = threadIdx.x + i NT (i = 0, 1, ...) of a row of V
 // logits (nvec vectors of the pass; vectors past the row read as -inf):
-// f(k, z) for each, RU vectors loaded at a time, in ascending i per thread.
+// f(k, z) for each, in ascending i per thread.
 template <int DT, int NT, class F>
 __device__ __forceinline__ void row_pass(const char* row, int V, int nvec, F&& f) {
-  for (int k0 = threadIdx.x; k0 < nvec; k0 += RU * NT) {
-    float z[RU][VEC];
+  const int tid = threadIdx.x;
+  stream_steps<DT, NT, RU, false>(
+      row, V, row, V, nvec,
+      [&](int base, int u) __attribute__((always_inline)) { return base + u * NT + tid; },
+      [&](int base, float (&z)[RU][VEC], float (&)[RU][VEC]) __attribute__((always_inline)) {
 #pragma unroll
-    for (int u = 0; u < RU; ++u) load8_row<DT>(row, k0 + u * NT, k0 + u * NT < nvec ? V : 0, z[u]);
-#pragma unroll
-    for (int u = 0; u < RU; ++u)
-      if (k0 + u * NT < nvec) f(k0 + u * NT, z[u]);
-  }
+        for (int u = 0; u < RU; ++u)
+          if (base + u * NT + tid < nvec) f(base + u * NT + tid, z[u]);
+      });
 }
 
 // Statistics and top-p cut of one processed row, streaming it from global
@@ -124,44 +168,45 @@ __device__ __forceinline__ RowStat row_stats_dev(const Args& a, const char* row,
   float m = -INFINITY;
   double Z = 0.0;
   int bad = 0;
-  // RU vectors per step: their loads in flight together, one max update
+  // RU vectors per step (the next step's loads in flight), one max update
   // (and fp64 rescale of Z) per step, the step's terms summed in fp32
-  for (int k0 = threadIdx.x; k0 < nvec; k0 += RU * NT) {
-    float z[RU][VEC];
+  const int tid = threadIdx.x;
+  stream_steps<DT, NT, RU, false>(
+      row, V, row, V, nvec,
+      [&](int base, int u) __attribute__((always_inline)) { return base + u * NT + tid; },
+      [&](int base, float (&z)[RU][VEC], float (&)[RU][VEC]) __attribute__((always_inline)) {
+        float vm = -INFINITY;
 #pragma unroll
-    for (int u = 0; u < RU; ++u) load8_row<DT>(row, k0 + u * NT, k0 + u * NT < nvec ? V : 0, z[u]);
-    float vm = -INFINITY;
+        for (int u = 0; u < RU; ++u) {
+          if (pen && base + u * NT + tid < nvec) apply_penalty8(bm, base + u * NT + tid, 0, a.rep, z[u]);
 #pragma unroll
-    for (int u = 0; u < RU; ++u) {
-      if (pen && k0 + u * NT < nvec) apply_penalty8(bm, k0 + u * NT, 0, a.rep, z[u]);
+          for (int e = 0; e < VEC; ++e) vm = fmaxf(vm, z[u][e]);
+        }
+        if (vm > m) {
+          if (m > -INFINITY) Z *= exp2(((double)m - (double)vm) * (double)c);
+          m = vm;
+        }
+        // Non-finite logits need no test per element: +inf becomes the max
+        // (caught below), and a NaN turns its term, hence Z, into NaN once the
+        // running max is finite; only a NaN met while every logit so far is
+        // -inf is looked for explicitly.
+        if (m > -INFINITY) {
+          float su = 0.0f;
 #pragma unroll
-      for (int e = 0; e < VEC; ++e) vm = fmaxf(vm, z[u][e]);
-    }
-    if (vm > m) {
-      if (m > -INFINITY) Z *= exp2(((double)m - (double)vm) * (double)c);
-      m = vm;
-    }
-    // Non-finite logits need no test per element: +inf becomes the max
-    // (caught below), and a NaN turns its term, hence Z, into NaN once the
-    // running max is finite; only a NaN met while every logit so far is
-    // -inf is looked for explicitly.
-    if (m > -INFINITY) {
-      float su = 0.0f;
+          for (int u = 0; u < RU; ++u) {
+            float sv[VEC];
 #pragma unroll
-      for (int u = 0; u < RU; ++u) {
-        float s[VEC];
+            for (int e = 0; e < VEC; ++e) sv[e] = e_rel(z[u][e], m, c);
+            su += ((sv[0] + sv[1]) + (sv[2] + sv[3])) + ((sv[4] + sv[5]) + (sv[6] + sv[7]));
+          }
+          Z += (double)su;
+        } else {
 #pragma unroll
-        for (int e = 0; e < VEC; ++e) s[e] = e_rel(z[u][e], m, c);
-        su += ((s[0] + s[1]) + (s[2] + s[3])) + ((s[4] + s[5]) + (s[6] + s[7]));
-      }
-      Z += (double)su;
-    } else {
+          for (int u = 0; u < RU; ++u)
 #pragma unroll
-      for (int u = 0; u < RU; ++u)
-#pragma unroll
-        for (int e = 0; e < VEC; ++e) bad |= z[u][e] != z[u][e];
-    }
-  }
+            for (int e = 0; e < VEC; ++e) bad |= z[u][e] != z[u][e];
+        }
+      });
   const float M = block_max<NT>(m, L.sf);
   Z = (m > -INFINITY) ? Z * exp2(((double)m - (double)M) * (double)c) : 0.0;
   const double Zall = block_sum<NT>(Z, L.sd);
@@ -273,33 +318,30 @@ __device__ __forceinline__ double pair_tv_dev(const Args& a, const char* trow, c
   const int V = a.V, nvec = (V + VEC - 1) / VEC;
   const float ip = (float)(1.0 / P.Zk), iq = (float)(1.0 / Q.Zk);
   double acc = 0.0;
-  for (int k0 = threadIdx.x; k0 < nvec; k0 += RU * NT) {
-    float zp[RU][VEC], zq[RU][VEC];
+  const int tid = threadIdx.x;
+  stream_steps<DT, NT, RU2, true>(
+      trow, V, drow, a.Vd, nvec,
+      [&](int base, int u) __attribute__((always_inline)) { return base + u * NT + tid; },
+      [&](int base, float (&zp)[RU2][VEC], float (&zq)[RU2][VEC]) __attribute__((always_inline)) {
+        float s = 0.0f;
 #pragma unroll
-    for (int u = 0; u < RU; ++u) {
-      const int k = k0 + u * NT;
-      load8_row<DT>(trow, k, k < nvec ? V : 0, zp[u]);
-      load8_row<DT>(drow, k, k < nvec ? a.Vd : 0, zq[u]);
-    }
-    float s = 0.0f;
+        for (int u = 0; u < RU2; ++u) {
+          const int k = base + u * NT + tid;
+          if (k >= nvec) continue;
+          if (pen) {
+            apply_penalty8(bm, k, 0, a.rep, zp[u]);
+            apply_penalty8(bm, k, 0, a.rep, zq[u]);
+          }
 #pragma unroll
-    for (int u = 0; u < RU; ++u) {
-      const int k = k0 + u * NT;
-      if (k >= nvec) continue;
-      if (pen) {
-        apply_penalty8(bm, k, 0, a.rep, zp[u]);
-        apply_penalty8(bm, k, 0, a.rep, zq[u]);
-      }
-#pragma unroll
-      for (int e = 0; e < VEC; ++e) {
-        const int id = k * VEC + e;
-        const float p = (id < V && kept(P, ord_key(zp[u][e]))) ? e_rel(zp[u][e], P.M, P.c) * ip : 0.0f;
-        const float q = (id < a.Vd && kept(Q, ord_key(zq[u][e]))) ? e_rel(zq[u][e], Q.M, Q.c) * iq : 0.0f;
-        s += fabsf(p - q);
-      }
-    }
-    acc += (double)s;
-  }
+          for (int e = 0; e < VEC; ++e) {
+            const int id = k * VEC + e;
+            const float p = (id < V && kept(P, ord_key(zp[u][e]))) ? e_rel(zp[u][e], P.M, P.c) * ip : 0.0f;
+            const float q = (id < a.Vd && kept(Q, ord_key(zq[u][e]))) ? e_rel(zq[u][e], Q.M, Q.c) * iq : 0.0f;
+            s += fabsf(p - q);
+          }
+        }
+        acc += (double)s;
+      });
   return fmin(0.5 * block_sum<NT>(acc, L.sd), 1.0);
 }
 
@@ -311,11 +353,11 @@ struct Drawn {
 
 // Inverse-CDF draw over ascending token ids: mode 0 draws from
 // max(p - q, 0) (falling back to p when that has no mass), mode 1 from p.
-// One coalesced pass (RU vectors in flight per thread) writes the total of
-// every chunk to L.ctot (nch + 1 doubles: the last holds the mass before
-// the crossing chunk).  A chunk is one wave's share of one step, RU blocks
-// of 64 consecutive vectors in ascending order (256 consecutive vectors for
-// RU = 4), so a step takes one wave reduction, not one per vector.  A block
+// One coalesced pass over the row (mode 0: both rows, side by side) writes
+// the total of every chunk to L.ctot (nch + 1 doubles: the last holds the
+// mass before the crossing chunk).  A chunk is one wave's share of one step,
+// RU2 blocks of 64 consecutive vectors in ascending order (128 consecutive
+// vectors), so a step takes one wave reduction, not one per vector.  A block
 // scan over the chunk totals finds the chunk that holds t = v S; wave 0
 // reads that chunk again and scans it block by block, lane by lane; the
 // crossing lane walks its 8 tokens.  A vector's weights are summed in fp32
@@ -325,7 +367,7 @@ template <int DT, int NT>
 __device__ __forceinline__ Drawn draw_dev(const Args& a, const char* trow, const char* drow, const RowStat& P,
                           const RowStat& Q, int mode, float v, bool pen, const uint32_t* bm,
                           const ExactLds& L) {
-  constexpr int CHV = RU * WAVE;   // vectors per chunk
+  constexpr int CHV = RU2 * WAVE;   // vectors per chunk
   const int V = a.V, nvec = (V + VEC - 1) / VEC;
   const int nch = (nvec + CHV - 1) / CHV;
   const int lane = threadIdx.x % WAVE, wv = threadIdx.x / WAVE;
@@ -365,21 +407,22 @@ __device__ __forceinline__ Drawn draw_dev(const Args& a, const char* trow, const
   double S = 0.0, t = 0.0;
   for (int pass = 0; pass < 2; ++pass) {
     // chunk totals: every wave runs every step (the wave sums need all lanes)
-    for (int base = 0; base < nvec; base += RU * NT) {
-      const int k0 = base + wv * CHV;   // this wave's chunk
-      float zp[RU][VEC], zq[RU][VEC];
+    const int md = mode;
+    stream_steps<DT, NT, RU2, true>(
+        trow, V, drow, md == 0 ? a.Vd : 0, nvec,
+        [&](int base, int u) __attribute__((always_inline)) { return base + wv * CHV + u * WAVE + lane; },
+        [&](int base, float (&zp)[RU2][VEC], float (&zq)[RU2][VEC]) __attribute__((always_inline)) {
+          const int k0 = base + wv * CHV;   // this wave's chunk
+          double ls = 0.0;
 #pragma unroll
-      for (int u = 0; u < RU; ++u) load2(k0 + u * WAVE + lane, mode, zp[u], zq[u]);
-      double ls = 0.0;
-#pragma unroll
-      for (int u = 0; u < RU; ++u) {
-        float w[VEC];
-        ls += (double)vec_w(k0 + u * WAVE + lane, mode, zp[u], zq[u], w);
-      }
-      const double cs = wave_sum(ls);
-      const int ch = k0 / CHV;
-      if (lane == 0 && ch < nch) L.ctot[ch] = cs;
-    }
+          for (int u = 0; u < RU2; ++u) {
+            float w[VEC];
+            ls += (double)vec_w(k0 + u * WAVE + lane, md, zp[u], zq[u], w);
+          }
+          const double cs = wave_sum(ls);
+          const int ch = k0 / CHV;
+          if (lane == 0 && ch < nch) L.ctot[ch] = cs;
+        });
     __syncthreads();
     // block scan over the chunk totals (thread t owns chunks t per ..)
     const int per = (nch + NT - 1) / NT;
@@ -419,14 +462,14 @@ __device__ __forceinline__ Drawn draw_dev(const Args& a, const char* trow, const
   out.S = S;
   const int cs = L.si[0];
   if (wv == 0 && cs >= 0) {
-    // the crossing chunk's RU blocks of 64 vectors, in ascending order
-    float zp[RU][VEC], zq[RU][VEC];
+    // the crossing chunk's RU2 blocks of 64 vectors, in ascending order
+    float zp[RU2][VEC], zq[RU2][VEC];
 #pragma unroll
-    for (int u = 0; u < RU; ++u) load2(cs * CHV + u * WAVE + lane, mode, zp[u], zq[u]);
+    for (int u = 0; u < RU2; ++u) load2(cs * CHV + u * WAVE + lane, mode, zp[u], zq[u]);
     double R = L.ctot[nch];
     int found = 0, y = -1, lastpos = -1;
 #pragma unroll
-    for (int u = 0; u < RU; ++u) {
+    for (int u = 0; u < RU2; ++u) {
       const int k = cs * CHV + u * WAVE + lane;
       float w[VEC];
       const double ls = (double)vec_w(k, mode, zp[u], zq[u], w);
