@@ -1110,9 +1110,12 @@ __device__ __forceinline__ ReqWords request_words(const int32_t* po, const int32
 // bitmap when pen; ex is carved from the single pass's histogram and slot
 // space, which is free by then.  Writes the unit's record with UO_SLOW |
 // UO_FALLBACK and the reasons why.
+// cpk / cqk: the single pass's settled cuts of the target / draft row (null:
+// recompute), which a unit handed over for a slot overflow carries.
 template <int NT>
 __device__ __forceinline__ void exact_unit(const Args& a, UnitOut* uo, int u, const uint32_t* bm,
-                                        const ExactLds& ex, uint32_t why) {
+                                        const ExactLds& ex, uint32_t why, const CutRes* cpk,
+                                        const CutRes* cqk) {
   const int tid = threadIdx.x;
   __shared__ int s_acc;
   // (the unit's request values are derived again here, so that none of
@@ -1138,7 +1141,18 @@ __device__ __forceinline__ void exact_unit(const Args& a, UnitOut* uo, int u, co
   out.flags = UO_SLOW | UO_FALLBACK;
   out.why = why;
   const float tpr = request_top_p(a, r);
-  const RowStat P = row_stats_dev<SD_BF16, NT>(a, trow, a.V, c, pen, bm, ex, tpr);
+  auto from_cut = [&](const CutRes& k) {
+    RowStat s;
+    s.M = k.M;
+    s.c = c;
+    s.Zk = k.zk;
+    s.kord = ord_key(k.key);
+    s.idcut = INT_MAX;
+    s.flags = 0;
+    s.kx = 0.0f;
+    return s;
+  };
+  const RowStat P = cpk ? from_cut(*cpk) : row_stats_dev<SD_BF16, NT>(a, trow, a.V, c, pen, bm, ex, tpr);
   if (P.flags & NONFINITE) {
     if (tid == 0) {
       out.flags = UO_NONFINITE | UO_FALLBACK;
@@ -1156,7 +1170,7 @@ __device__ __forceinline__ void exact_unit(const Args& a, UnitOut* uo, int u, co
     }
     return;
   }
-  const RowStat Q = row_stats_dev<SD_BF16, NT>(a, drow, a.Vd, c, pen, bm, ex, tpr);
+  const RowStat Q = cqk ? from_cut(*cqk) : row_stats_dev<SD_BF16, NT>(a, drow, a.Vd, c, pen, bm, ex, tpr);
   if (Q.flags & NONFINITE) {
     if (tid == 0) {
       out.flags = UO_NONFINITE | UO_FALLBACK;
@@ -1603,7 +1617,7 @@ __global__ __launch_bounds__(NT_F) void k_pair_fast(Args a, UnitOut* uo) {
       Zs += lumped_z(histq, binq, t1q, c, gcq, &zerr);
       const int ne = s_ne[1], np = s_np[1];
       const bool good = anchor_q && M > -INFINITY && M < INFINITY && Zs > 0.0 && Zs < INFINITY &&
-                        zerr <= 0x1p-24 * Zs && ne <= E_CAP && np <= PE_CAP && !over;
+                        zerr <= 0x1p-24 * Zs && ne <= E_CAP && np <= PE_CAP;
       Cut cc;
       cc.ok = 0;
       cc.code = 0;
@@ -1614,7 +1628,8 @@ __global__ __launch_bounds__(NT_F) void k_pair_fast(Args a, UnitOut* uo) {
         cc = wave_cut(histq, hneg, exq, ne, np, bm, pen, t1q, M, c, tp * Zqa, ecnt, emass, rkey, rmass,
                       rid, &s_rcnt);
       }
-      const int okv = over ? -2 : !good ? 0 : cc.ok ? 1 : -1;
+      // (a slot overflow with both cuts settled hands those cuts to the exact route)
+      const int okv = !good ? 0 : !cc.ok ? -1 : over ? -2 : 1;
       if (lane == 0) s_cut[1] = CutRes{okv, cc.code, cc.key, M, cc.zk};
     } else if (wv == 1 && lane < 2) {
       // Meanwhile the draft token's fp64 exponentials: lane 0 p(x_j) (the
@@ -1843,7 +1858,10 @@ write_out_flags:
 #else
     const Args ax = a;   // (the host pass only parses device code)
 #endif
-    exact_unit<NT>(ax, uo, blockIdx.x, bm, ex, why);
+    // a slot overflow comes with both cuts settled (for a bonus row, its one)
+    const bool cuts = why == FB_SLOTS;
+    exact_unit<NT>(ax, uo, blockIdx.x, bm, ex, why, cuts ? &s_cut[0] : nullptr,
+                   cuts && !bonus ? &s_cut[1] : nullptr);
   }
 }
 
