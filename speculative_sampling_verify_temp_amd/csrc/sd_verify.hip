@@ -288,7 +288,7 @@ enum : uint32_t { UO_NONFINITE = 1, UO_QZERO = 2, UO_RESID_ZERO = 4, UO_SLOW = 8
 // Why the single pass handed a unit to its exact route: a row's stream
 // state out of range (anchor, normalizer, list capacities), its cut not
 // settled by the window, or more nucleus candidates than slots.
-enum : uint32_t { FB_P_STATE = 1, FB_P_CUT = 2, FB_Q_STATE = 4, FB_Q_CUT = 8, FB_SLOTS = 16 };
+enum : uint32_t { FB_P_STATE = 1, FB_P_CUT = 2, FB_Q_STATE = 4, FB_Q_CUT = 8, FB_SLOTS = 16, FB_WIDE = 32 };
 
 // Compile-time loop: f.template operator()<I>() for I = 0 .. N-1, so that
 // register arrays indexed by I stay in registers.
@@ -524,23 +524,26 @@ __device__ __forceinline__ Cut wave_cut(const uint32_t* hist, const uint32_t* hn
   out.code = b;
   out.key = b > 0 ? key_of_ord16(t1 - b) : 0.0f;
   out.zk = c_incl;
-  if (necb == 0) {
-    // A +0 crossing bin with a -0 bin just below: the two are one key.
-    if (b < 254 && __float_as_uint(out.key) == 0u) {
-      const int b1 = b + 1, l1 = b1 >> 2, i1 = b1 & 3;
-      const int n1 = lane_read((int)(i1 == 0 ? cnt[0] : i1 == 1 ? cnt[1] : i1 == 2 ? cnt[2] : cnt[3]), l1);
-      const int e1 = lane_read((int)(i1 == 0 ? ec[0] : i1 == 1 ? ec[1] : i1 == 2 ? ec[2] : ec[3]), l1);
-      // cumulative through bin b + 1 = through bin b + its mass
-      const double m1 = lane_read(i1 == 0 ? mass[0] : i1 == 1 ? mass[1] : i1 == 2 ? mass[2] : mass[3], l1);
-      if (e1 > 0) out.ok = 0;
-      else if (n1 > 0) {
-        out.zk = c_incl + m1;
-        out.code = b1;
-        out.key = -0.0f;
+  if (b > 0 && b < 254 && __float_as_uint(out.key) == 0u) {
+    // A +0 crossing bin with a non-empty bin just below (-0, and negative
+    // keys above the largest negative bf16): the two share the key 0.
+    // Merged when both hold logits of one key each; else unsettled.
+    const int b1 = b + 1, l1 = b1 >> 2, i1 = b1 & 3;
+    const int n1 = lane_read((int)(i1 == 0 ? cnt[0] : i1 == 1 ? cnt[1] : i1 == 2 ? cnt[2] : cnt[3]), l1);
+    const int e1 = lane_read((int)(i1 == 0 ? ec[0] : i1 == 1 ? ec[1] : i1 == 2 ? ec[2] : ec[3]), l1);
+    // cumulative through bin b + 1 = through bin b + its mass
+    const double m1 = lane_read(i1 == 0 ? mass[0] : i1 == 1 ? mass[1] : i1 == 2 ? mass[2] : mass[3], l1);
+    if (n1 > 0 || e1 > 0) {
+      if (e1 > 0 || necb > 0) {
+        out.ok = 0;
+        return out;
       }
+      out.zk = c_incl + m1;
+      out.code = b1;
+      out.key = -0.0f;
     }
-    return out;
   }
+  if (necb == 0) return out;
   // Exact resolution inside the crossing bin: gather its entries (plus the
   // bin's unpenalized group), order them canonically (key descending, id
   // ascending); the cut is the largest key whose cumulative mass, ties
@@ -603,6 +606,7 @@ __device__ __forceinline__ Cut wave_cut(const uint32_t* hist, const uint32_t* hn
   return out;
 }
 
+
 // Per-wave partials to LDS and one barrier; every thread gets the result.
 // Each call site uses its own buffer (NT / WAVE entries).
 template <int NT>
@@ -621,6 +625,263 @@ struct CutRes {
   float key, M;
   double zk;
 };
+
+// A row's key histogram and lists, for wide_cut.
+struct WideLds {
+  const uint32_t* hist;   // the row's key histogram
+  uint32_t* dep;          // scratch: RUP words
+  uint32_t* ecnt4;        // scratch: RUP words
+  uint64_t* emass4;       // scratch: RUP words of 8 bytes
+  ExactList ex;           // its stream entries (the first ns)
+  int ns;
+  const int* plid;        // distinct penalized ids
+  const uint32_t* plraw;  // their logits (bf16 bits, the row's in the low half; all ones: not loaded)
+  int npl;
+  float* rkey;            // R_CAP entries each
+  double* rmass;
+  int* rid;
+  int* scnt;
+  double* wtot;           // NT_F / WAVE
+  double TP;              // mass threshold, relative to exp2(M c)
+  uint32_t t1;            // the row's anchor: key of bin d is t1 - d
+  CutRes* cut;            // the row's cut record (M read, result written)
+};
+
+// Exact top-p cut of a row over its whole exact key range (bins 0 .. RUP-1
+// of its key histogram; bin 0 holds only exact entries), for a row whose
+// crossing lies below the window: block-wide, the same rule as wave_cut.
+// Every penalized logit leaves the bin of its raw key (dep counts the
+// departures) and joins the exact entries under its penalized key, with
+// the stream entries of unpenalized ids.  ok = 0 when no bin above RUP - 1
+// reaches the threshold or the crossing bin holds more exact entries than
+// R_CAP.
+__device__ __forceinline__ Cut wide_cut(const WideLds& L, const char* trow, const uint32_t* bm, bool pen,
+                                        float rep, float M, float c) {
+  constexpr int NT = NT_F;
+  static_assert(RUP == 4 * NT && 2 * RUP <= NBINW && NBINW + 2 * RUP <= CAPT * NT,
+                "wide_cut geometry and scratch");
+  const int tid = threadIdx.x, lane = tid % WAVE;
+  const uint32_t* const hist = L.hist;
+  uint32_t* const dep = L.dep;
+  uint32_t* const ecnt4 = L.ecnt4;
+  uint64_t* const emass4 = L.emass4;
+  const ExactList& ex = L.ex;
+  const int ns = L.ns, npl = L.npl;
+  const int* const plid = L.plid;
+  const uint32_t* const plraw = L.plraw;
+  float* const rkey = L.rkey;
+  double* const rmass = L.rmass;
+  int* const rid = L.rid;
+  int* const scnt = L.scnt;
+  const uint32_t t1 = L.t1;
+  const double TP = L.TP;
+  __shared__ int s_b;   // the crossing bin
+  for (int i = tid; i < RUP; i += NT) {
+    dep[i] = 0u;
+    ecnt4[i] = 0u;
+    emass4[i] = 0ull;
+  }
+  if (tid == 0) {
+    *scnt = 0;
+    s_b = INT_MAX;
+  }
+  __syncthreads();
+  auto bin_of = [&](float k) __attribute__((always_inline)) {
+    const uint32_t o = ord16f(k);
+    return o >= t1 ? 0u : t1 - o;
+  };
+  for (int i = tid; i < npl; i += NT) {
+    const int id = plid[i];
+    const uint32_t g = plraw[i];
+    const uint32_t raw = g == 0xFFFFFFFFu ? reinterpret_cast<const uint16_t*>(trow)[id] : g & 0xFFFFu;
+    const uint32_t o = raw ^ ((raw & 0x8000u) ? 0xFFFFu : 0x8000u);
+    if (o < t1 && t1 - o < (uint32_t)RUP) atomicAdd(&dep[t1 - o], 1u);
+    const float zp = penalize(__uint_as_float(raw << 16), rep);
+    const uint32_t b = bin_of(zp);
+    if (b < (uint32_t)RUP) {
+      atomicAdd(&ecnt4[b], 1u);
+      atomicAdd(reinterpret_cast<unsigned long long*>(&emass4[b]),
+                (unsigned long long)e_fixed(e_rel(zp, M, c), SHP));
+    }
+  }
+  for (int i = tid; i < ns; i += NT) {
+    const int id = ex.id[i];
+    if (pen && ((bm[id >> 5] >> (id & 31)) & 1u)) continue;   // stale: listed above
+    const float k = ex.key[i];
+    const uint32_t b = bin_of(k);
+    if (b < (uint32_t)RUP) {
+      atomicAdd(&ecnt4[b], 1u);
+      atomicAdd(reinterpret_cast<unsigned long long*>(&emass4[b]),
+                (unsigned long long)e_fixed(e_rel(k, M, c), SHP));
+    }
+  }
+  __syncthreads();
+  // thread t: bins 4t .. 4t + 3, masses in fp64
+  uint32_t cnt[4], ec[4];
+  double mass[4];
+  double lsum = 0.0;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int b = 4 * tid + q;
+    const uint32_t n = (b == 0 || b > (int)t1) ? 0u : hist[b] - dep[b];
+    cnt[q] = n;
+    ec[q] = ecnt4[b];
+    double m = n ? (double)n * (double)e_rel(key_of_ord16(t1 - (uint32_t)b), M, c) : 0.0;
+    m += (double)emass4[b] * 0x1p-40;
+    mass[q] = m;
+    lsum += m;
+  }
+  const double incl_t = block_incl_scan_fast<NT>(lsum, L.wtot);
+  double cum = incl_t - lsum;
+  int hit = -1;
+  double cin = 0.0, cex = 0.0;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const double nx = cum + mass[q];
+    if (hit < 0 && (cnt[q] + ec[q]) > 0u && nx >= TP) {
+      hit = q;
+      cin = nx;
+      cex = cum;
+    }
+    cum = nx;
+  }
+  if (hit >= 0) atomicMin(&s_b, 4 * tid + hit);
+  __syncthreads();
+  const int bstar = s_b;
+  Cut out;
+  out.ok = 0;
+  out.code = 0;
+  out.key = 0.0f;
+  out.zk = 0.0;
+  if (bstar == INT_MAX || bstar >= RUP - 1) {
+    __syncthreads();
+    return out;
+  }
+  // the crossing thread publishes its bin's totals, and those of the bin
+  // below (for a +0 crossing bin over a -0 one)
+  __shared__ double s_w[3];
+  __shared__ int s_wi[4];
+  __shared__ float s_k;
+  if (hit >= 0 && 4 * tid + hit == bstar) {
+    auto pick4 = [&](const auto (&x)[4]) __attribute__((always_inline)) {
+      return hit == 0 ? x[0] : hit == 1 ? x[1] : hit == 2 ? x[2] : x[3];
+    };
+    s_w[0] = cin;
+    s_w[1] = cex;
+    s_wi[0] = (int)pick4(cnt);
+    s_wi[1] = (int)pick4(ec);
+    const int b1 = bstar + 1;
+    const uint32_t n1 = b1 > (int)t1 ? 0u : hist[b1] - dep[b1];
+    s_wi[2] = (int)n1;
+    s_wi[3] = (int)ecnt4[b1];
+    s_w[2] = (n1 ? (double)n1 * (double)e_rel(key_of_ord16(t1 - (uint32_t)b1), M, c) : 0.0) +
+             (double)emass4[b1] * 0x1p-40;
+  }
+  __syncthreads();
+  const double c_incl = s_w[0], c_excl = s_w[1];
+  const int gcnt = s_wi[0], necb = s_wi[1];
+  out.ok = 1;
+  out.code = bstar;
+  out.key = bstar > 0 ? key_of_ord16(t1 - (uint32_t)bstar) : 0.0f;
+  out.zk = c_incl;
+  // A +0 crossing bin with a non-empty bin just below (-0, and negative
+  // keys above the largest negative bf16): the two share the key 0.  Merged
+  // when both hold logits of one key each; the rest is left to the passes.
+  // (bin 0, the keys above the window, has no key of its own)
+  const bool zero_pair = bstar > 0 && __float_as_uint(out.key) == 0u && (s_wi[2] > 0 || s_wi[3] > 0);
+  if (necb == 0) {
+    if (zero_pair) {
+      if (s_wi[3] > 0) out.ok = 0;
+      else {
+        out.zk = c_incl + s_w[2];
+        out.code = bstar + 1;
+        out.key = -0.0f;
+      }
+    }
+    __syncthreads();
+    return out;
+  }
+  if (necb + 1 > R_CAP || zero_pair) {
+    out.ok = 0;
+    __syncthreads();
+    return out;
+  }
+  // Exact resolution inside the crossing bin: its entries plus the bin's
+  // unpenalized group, in canonical order (key descending, id ascending).
+  for (int i = tid; i < npl; i += NT) {
+    const int id = plid[i];
+    const uint32_t g = plraw[i];
+    const uint32_t raw = g == 0xFFFFFFFFu ? reinterpret_cast<const uint16_t*>(trow)[id] : g & 0xFFFFu;
+    const float zp = penalize(__uint_as_float(raw << 16), rep);
+    if (bin_of(zp) == (uint32_t)bstar) {
+      const int sidx = atomicAdd(scnt, 1);
+      rkey[sidx] = zp;
+      rid[sidx] = id;
+      rmass[sidx] = (double)e_rel(zp, M, c);
+    }
+  }
+  for (int i = tid; i < ns; i += NT) {
+    const int id = ex.id[i];
+    if (pen && ((bm[id >> 5] >> (id & 31)) & 1u)) continue;
+    const float k = ex.key[i];
+    if (bin_of(k) == (uint32_t)bstar) {
+      const int sidx = atomicAdd(scnt, 1);
+      rkey[sidx] = k;
+      rid[sidx] = id;
+      rmass[sidx] = (double)e_rel(k, M, c);
+    }
+  }
+  __syncthreads();
+  if (tid < WAVE) {
+    int n = necb;
+    if (gcnt > 0) {
+      if (lane == 0) {
+        rkey[n] = out.key;
+        rid[n] = -1;
+        rmass[n] = (double)gcnt * (double)e_rel(out.key, M, c);
+      }
+      ++n;
+    }
+    __builtin_amdgcn_wave_barrier();
+    float mk = 0.0f;
+    double mm = 0.0;
+    int rank = 0;
+    if (lane < n) {
+      mk = rkey[lane];
+      const int mi = rid[lane];
+      mm = rmass[lane];
+      for (int q = 0; q < n; ++q) {
+        const float kq = rkey[q];
+        const int iq = rid[q];
+        rank += (kq > mk || (kq == mk && iq < mi)) ? 1 : 0;
+      }
+    }
+    __builtin_amdgcn_wave_barrier();
+    if (lane < n) {
+      rkey[rank] = mk;
+      rmass[rank] = mm;
+    }
+    __builtin_amdgcn_wave_barrier();
+    double cm = c_excl;
+    const float me = lane < n ? rkey[lane] : 0.0f;
+    if (lane < n)
+      for (int q = 0; q < n; ++q)
+        if (rkey[q] >= me) cm += rmass[q];
+    const uint64_t reach = __ballot(lane < n && cm >= TP);
+    const int pick = reach ? __builtin_ctzll(reach) : n - 1;
+    const double zsel = lane_read(cm, pick);
+    const float ksel = lane_read(me, pick);
+    if (lane == 0) {
+      s_w[0] = zsel;
+      s_k = ksel;
+    }
+  }
+  __syncthreads();
+  out.zk = s_w[0];
+  out.key = s_k;
+  __syncthreads();
+  return out;
+}
 
 __device__ __forceinline__ void exact_push(const ExactList& ex, float key, int id, uint32_t raw) {
   const int ix = atomicAdd(ex.n, 1);
@@ -1115,7 +1376,7 @@ __device__ __forceinline__ ReqWords request_words(const int32_t* po, const int32
 template <int NT>
 __device__ __forceinline__ void exact_unit(const Args& a, UnitOut* uo, int u, const uint32_t* bm,
                                         const ExactLds& ex, uint32_t why, const CutRes* cpk,
-                                        const CutRes* cqk) {
+                                        const CutRes* cqk, const WideLds& wl, bool wide) {
   const int tid = threadIdx.x;
   __shared__ int s_acc;
   // (the unit's request values are derived again here, so that none of
@@ -1152,6 +1413,17 @@ __device__ __forceinline__ void exact_unit(const Args& a, UnitOut* uo, int u, co
     s.kx = 0.0f;
     return s;
   };
+  if (wide) {
+    // (the wide cut's scratch is in the space the exact passes use: it runs first)
+    const float M = wl.cut->M;
+    const Cut w = wide_cut(wl, trow, bm, pen, a.rep, M, c);
+    if (w.ok && tid == 0) *wl.cut = CutRes{1, w.code, w.key, M, w.zk};
+    __syncthreads();
+    if (w.ok) {
+      cpk = wl.cut;
+      out.why |= FB_WIDE;
+    }
+  }
   const RowStat P = cpk ? from_cut(*cpk) : row_stats_dev<SD_BF16, NT>(a, trow, a.V, c, pen, bm, ex, tpr);
   if (P.flags & NONFINITE) {
     if (tid == 0) {
@@ -1250,6 +1522,8 @@ __global__ __launch_bounds__(NT_F) void k_pair_fast(Args a, UnitOut* uo) {
   __shared__ double red_d[3][NT / WAVE];
   __shared__ int red_i[2][NT / WAVE];
   __shared__ CutRes s_cut[2];
+  __shared__ double s_tp;     // the target cut's mass threshold (for the wide cut)
+  __shared__ uint32_t s_t1;   // and the target row's anchor
   __shared__ float pkey_arr[2][PE_CAP];
   __shared__ int32_t pid_arr[2][PE_CAP];
   __shared__ uint16_t praw_arr[2][PE_CAP];
@@ -1489,12 +1763,17 @@ __global__ __launch_bounds__(NT_F) void k_pair_fast(Args a, UnitOut* uo) {
     cc.code = 0;
     cc.key = 0.0f;
     cc.zk = 0.0;
+    double TP = 0.0;
     if (good) {
       const double Zp = Zs * exp2((double)gcp - (double)M * (double)c);
-      cc = wave_cut(hist, hneg, exp_, ne, np, bm, pen, t1p, M, c, tp * Zp, ecnt, emass, rkey, rmass, rid,
-                    &s_rcnt);
+      TP = tp * Zp;
+      cc = wave_cut(hist, hneg, exp_, ne, np, bm, pen, t1p, M, c, TP, ecnt, emass, rkey, rmass, rid, &s_rcnt);
     }
-    if (lane == 0) s_cut[0] = CutRes{good ? (cc.ok ? 1 : -1) : 0, cc.code, cc.key, M, cc.zk};
+    if (lane == 0) {
+      s_cut[0] = CutRes{good ? (cc.ok ? 1 : -1) : 0, cc.code, cc.key, M, cc.zk};
+      s_tp = TP;
+      s_t1 = t1p;
+    }
   }
   __syncthreads();
   const CutRes cp = s_cut[0];
@@ -1858,10 +2137,31 @@ write_out_flags:
 #else
     const Args ax = a;   // (the host pass only parses device code)
 #endif
+    // A target row whose crossing lies below the window: its key histogram
+    // (in the slots' space; the draft stream has not begun) is exact for
+    // RUP keys below the window's top, which most such crossings reach.
+    WideLds wl;
+    wl.hist = hsl.slot_arr;
+    wl.dep = hsl.histq;
+    wl.ecnt4 = hsl.histq + RUP;
+    wl.emass4 = reinterpret_cast<uint64_t*>(hsl.slot_arr + NBINW);
+    wl.ex = exp_;
+    wl.ns = s_ne[0];
+    wl.plid = plid;
+    wl.plraw = plraw;
+    wl.npl = s_npl;
+    wl.rkey = rkey;
+    wl.rmass = rmass;
+    wl.rid = rid;
+    wl.scnt = &s_rcnt;
+    wl.wtot = sd;
+    wl.TP = s_tp;
+    wl.t1 = s_t1;
+    wl.cut = &s_cut[0];
     // a slot overflow comes with both cuts settled (for a bonus row, its one)
     const bool cuts = why == FB_SLOTS;
     exact_unit<NT>(ax, uo, blockIdx.x, bm, ex, why, cuts ? &s_cut[0] : nullptr,
-                   cuts && !bonus ? &s_cut[1] : nullptr);
+                   cuts && !bonus ? &s_cut[1] : nullptr, wl, why == FB_P_CUT);
   }
 }
 

@@ -498,3 +498,58 @@ def test_single_pass_fallback_routes():
         tot[1] += f
     print(f"fallback routes: checked {tot[0]}, near-tie {tot[1]}")
     assert tot[0] >= 4
+
+
+def test_single_pass_wide_target_cut():
+    """Temperatures in [1, 1.5] over V = 152064 (the batched workload's rows
+    otherwise): the target's top-p crossing often lies below the single
+    pass's 254-key window.  Such a unit takes the exact route, whose target
+    cut then comes from the row's key histogram (exact for 4096 keys below
+    the window's top) instead of the row's own passes; the outputs and
+    per-position statistics must match the oracle's."""
+    sdv = _sdv()
+    w = wl.config4(seed=9, B=24, K=8, T_range=(1.0, 1.5), odd_share=0.3)
+    d = to_device(w)
+    args = sdv.make_args(d["target"], d["draft"], d["draft_ids"], d["k_per_row"],
+                         d["temperature"], w.top_p, w.rep_penalty, d["prior_ids"],
+                         d["prior_offsets"], w.tv_budget, w.seed, w.offset, w.flags)
+    assert sdv.phase_kernel(args, 0) == "k_pair_fast"
+    import torch
+    ws = sdv.alloc_workspace(args, "cuda")
+    acc = torch.empty(w.B, dtype=torch.int32, device="cuda")
+    tok = torch.empty((w.B, w.K_max + 1), dtype=torch.int32, device="cuda")
+    sdv.run_phase(args, ws, 0, acc, tok)
+    n, why = sdv.fallback_units(args, ws, why=True)
+    wide = int(((why & 32) != 0).sum())
+    pcut = int(((why & 2) != 0).sum())
+    assert ((why & 32) == 0).all() or ((why[(why & 32) != 0] & 2) != 0).all()
+    g = gpu_sample(w, dev=d)
+    c, f = compare_sample(g, oracle_sample(w), w)
+    print(f"wide target cut: {n} of {len(why)} units flagged, {pcut} target cuts below the "
+          f"window, {wide} of them settled from the histogram; checked {c} rows, near-tie {f}")
+    assert wide >= 10 and c >= 0.9 * w.B
+
+
+def test_single_pass_crossing_above_window():
+    """A few logits far above the sampled rounds' maximum (ids past the
+    rounds that set the window's anchor) carry most of each row's mass: the
+    top-p crossing then lies among the exact entries above the window (bin
+    0), which the single pass settles itself, for target and draft rows."""
+    w = wl.random_case(1300, B=8, K_max=3, V=wl.V_QWEN25, dtype="bf16", sigma=3.0, corr=0.9,
+                       T_range=(0.5, 1.0), top_p=0.9, rep_penalty=1.1, n_prior=24, D=0.5,
+                       odd_share=0.3)
+    rng = np.random.default_rng(77)
+    t, d = w.target_f32(), w.draft_f32()
+    for r in range(w.B):
+        for j in range(w.K_max + 1):
+            ids = rng.choice(np.arange(40000, w.V), size=6, replace=False)
+            top = float(t[r, j].max()) + 8.0
+            t[r, j, ids] = top + 0.5 * np.arange(6)
+            if j < w.K_max:
+                d[r, j, ids] = top + 0.5 * rng.permutation(6)
+    w.target[:] = wl.f32_to_bf16_bits(t)
+    w.draft[:] = wl.f32_to_bf16_bits(d)
+    assert _fast_fallbacks(w) == 0
+    c, f = compare_sample(gpu_sample(w), oracle_sample(w), w)
+    print(f"crossing above the window: checked {c} rows, near-tie {f}")
+    assert c >= 6
