@@ -337,8 +337,8 @@ const char *sd_debug_phase_kernel(const sd_verify_args_t *args, int phase);
  * target-row stream state out of range, 2 a target cut the window did not
  * settle, 4 and 8 the same for the draft row, 16 more nucleus candidates
  * than slots, 32 (with 2) a target cut settled from the row's whole exact
- * key histogram instead of its own passes; 0 for units the single pass
- * settled.  Synchronizes `stream`.
+ * key histogram instead of its own passes, 64 (with 8) the same for the
+ * draft row; 0 for units the single pass settled.  Synchronizes `stream`.
  * SD_EUNSUPPORTED when the arguments select the general path. */
 int sd_debug_fallback_units(const sd_verify_args_t *args, const void *workspace,
                             size_t workspace_bytes, int32_t *out_count, uint32_t *out_why,

@@ -288,7 +288,11 @@ enum : uint32_t { UO_NONFINITE = 1, UO_QZERO = 2, UO_RESID_ZERO = 4, UO_SLOW = 8
 // Why the single pass handed a unit to its exact route: a row's stream
 // state out of range (anchor, normalizer, list capacities), its cut not
 // settled by the window, or more nucleus candidates than slots.
-enum : uint32_t { FB_P_STATE = 1, FB_P_CUT = 2, FB_Q_STATE = 4, FB_Q_CUT = 8, FB_SLOTS = 16, FB_WIDE = 32 };
+enum : uint32_t {
+  FB_P_STATE = 1, FB_P_CUT = 2, FB_Q_STATE = 4, FB_Q_CUT = 8, FB_SLOTS = 16,
+  FB_WIDE = 32,     // (with FB_P_CUT) the target cut came from its whole histogram
+  FB_WIDE_Q = 64    // (with FB_Q_CUT) the draft cut likewise
+};
 
 // Compile-time loop: f.template operator()<I>() for I = 0 .. N-1, so that
 // register arrays indexed by I stay in registers.
@@ -628,14 +632,13 @@ struct CutRes {
 
 // A row's key histogram and lists, for wide_cut.
 struct WideLds {
-  const uint32_t* hist;   // the row's key histogram
-  uint32_t* dep;          // scratch: RUP words
+  uint32_t* hist;         // the row's key histogram (its exact bins are consumed)
   uint32_t* ecnt4;        // scratch: RUP words
   uint64_t* emass4;       // scratch: RUP words of 8 bytes
   ExactList ex;           // its stream entries (the first ns)
   int ns;
   const int* plid;        // distinct penalized ids
-  const uint32_t* plraw;  // their logits (bf16 bits, the row's in the low half; all ones: not loaded)
+  const uint32_t* plraw;  // their target | draft logits (bf16 bits; all ones: not loaded)
   int npl;
   float* rkey;            // R_CAP entries each
   double* rmass;
@@ -644,25 +647,26 @@ struct WideLds {
   double* wtot;           // NT_F / WAVE
   double TP;              // mass threshold, relative to exp2(M c)
   uint32_t t1;            // the row's anchor: key of bin d is t1 - d
-  CutRes* cut;            // the row's cut record (M read, result written)
+  CutRes* cut;            // the row's cut record (M read; the result written by the caller)
 };
 
 // Exact top-p cut of a row over its whole exact key range (bins 0 .. RUP-1
 // of its key histogram; bin 0 holds only exact entries), for a row whose
 // crossing lies below the window: block-wide, the same rule as wave_cut.
-// Every penalized logit leaves the bin of its raw key (dep counts the
-// departures) and joins the exact entries under its penalized key, with
-// the stream entries of unpenalized ids.  ok = 0 when no bin above RUP - 1
-// reaches the threshold or the crossing bin holds more exact entries than
-// R_CAP.
-__device__ __forceinline__ Cut wide_cut(const WideLds& L, const char* trow, const uint32_t* bm, bool pen,
-                                        float rep, float M, float c) {
+// Every penalized logit leaves the bin of its raw key (taken off the
+// histogram in place) and joins the exact entries under its penalized key,
+// with the stream entries of unpenalized ids.  The row is the target's
+// (DRAFT false: plraw's low halves) or the draft's (high halves; ids from
+// Vrow on hold -inf).  ok = 0 when no bin above RUP - 1 reaches the
+// threshold, or the crossing bin holds more exact entries than R_CAP, or
+// it is the bin of +0 over a bin below it that is not one plain key.
+template <bool DRAFT>
+__device__ __forceinline__ Cut wide_cut(const WideLds& L, const char* row, int Vrow, const uint32_t* bm,
+                                        bool pen, float rep, float M, float c) {
   constexpr int NT = NT_F;
-  static_assert(RUP == 4 * NT && 2 * RUP <= NBINW && NBINW + 2 * RUP <= CAPT * NT,
-                "wide_cut geometry and scratch");
+  static_assert(RUP == 4 * NT && RUP <= NBINW, "wide_cut geometry");
   const int tid = threadIdx.x, lane = tid % WAVE;
-  const uint32_t* const hist = L.hist;
-  uint32_t* const dep = L.dep;
+  uint32_t* const hist = L.hist;
   uint32_t* const ecnt4 = L.ecnt4;
   uint64_t* const emass4 = L.emass4;
   const ExactList& ex = L.ex;
@@ -677,7 +681,6 @@ __device__ __forceinline__ Cut wide_cut(const WideLds& L, const char* trow, cons
   const double TP = L.TP;
   __shared__ int s_b;   // the crossing bin
   for (int i = tid; i < RUP; i += NT) {
-    dep[i] = 0u;
     ecnt4[i] = 0u;
     emass4[i] = 0ull;
   }
@@ -685,45 +688,49 @@ __device__ __forceinline__ Cut wide_cut(const WideLds& L, const char* trow, cons
     *scnt = 0;
     s_b = INT_MAX;
   }
-  __syncthreads();
+  // the row's logit of penalized id i, as read (bf16 bits)
+  auto pen_raw = [&](int i) __attribute__((always_inline)) {
+    const int id = plid[i];
+    const uint32_t g = plraw[i];
+    if (DRAFT && id >= Vrow) return 0xFF80u;
+    if (g == 0xFFFFFFFFu) return (uint32_t)reinterpret_cast<const uint16_t*>(row)[id];
+    return DRAFT ? g >> 16 : g & 0xFFFFu;
+  };
   auto bin_of = [&](float k) __attribute__((always_inline)) {
     const uint32_t o = ord16f(k);
     return o >= t1 ? 0u : t1 - o;
   };
-  for (int i = tid; i < npl; i += NT) {
-    const int id = plid[i];
-    const uint32_t g = plraw[i];
-    const uint32_t raw = g == 0xFFFFFFFFu ? reinterpret_cast<const uint16_t*>(trow)[id] : g & 0xFFFFu;
-    const uint32_t o = raw ^ ((raw & 0x8000u) ? 0xFFFFu : 0x8000u);
-    if (o < t1 && t1 - o < (uint32_t)RUP) atomicAdd(&dep[t1 - o], 1u);
-    const float zp = penalize(__uint_as_float(raw << 16), rep);
-    const uint32_t b = bin_of(zp);
-    if (b < (uint32_t)RUP) {
-      atomicAdd(&ecnt4[b], 1u);
-      atomicAdd(reinterpret_cast<unsigned long long*>(&emass4[b]),
-                (unsigned long long)e_fixed(e_rel(zp, M, c), SHP));
-    }
-  }
-  for (int i = tid; i < ns; i += NT) {
-    const int id = ex.id[i];
-    if (pen && ((bm[id >> 5] >> (id & 31)) & 1u)) continue;   // stale: listed above
-    const float k = ex.key[i];
+  auto add_exact = [&](float k) __attribute__((always_inline)) {
     const uint32_t b = bin_of(k);
     if (b < (uint32_t)RUP) {
       atomicAdd(&ecnt4[b], 1u);
       atomicAdd(reinterpret_cast<unsigned long long*>(&emass4[b]),
                 (unsigned long long)e_fixed(e_rel(k, M, c), SHP));
     }
+  };
+  __syncthreads();
+  for (int i = tid; i < npl; i += NT) {
+    const uint32_t raw = pen_raw(i);
+    const uint32_t o = raw ^ ((raw & 0x8000u) ? 0xFFFFu : 0x8000u);   // as the stream keyed it
+    if (o < t1 && t1 - o < (uint32_t)RUP) atomicSub(&hist[t1 - o], 1u);
+    add_exact(penalize(__uint_as_float(raw << 16), rep));
+  }
+  for (int i = tid; i < ns; i += NT) {
+    const int id = ex.id[i];
+    if (pen && ((bm[id >> 5] >> (id & 31)) & 1u)) continue;   // stale: listed above
+    add_exact(ex.key[i]);
   }
   __syncthreads();
-  // thread t: bins 4t .. 4t + 3, masses in fp64
+  // thread t: bins 4t .. 4t + 3
   uint32_t cnt[4], ec[4];
   double mass[4];
   double lsum = 0.0;
+  const uint4 h4 = reinterpret_cast<const uint4*>(hist)[tid];
+  const uint32_t hv[4] = {h4.x, h4.y, h4.z, h4.w};
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
     const int b = 4 * tid + q;
-    const uint32_t n = (b == 0 || b > (int)t1) ? 0u : hist[b] - dep[b];
+    const uint32_t n = (b == 0 || b > (int)t1) ? 0u : hv[q];
     cnt[q] = n;
     ec[q] = ecnt4[b];
     double m = n ? (double)n * (double)e_rel(key_of_ord16(t1 - (uint32_t)b), M, c) : 0.0;
@@ -771,7 +778,7 @@ __device__ __forceinline__ Cut wide_cut(const WideLds& L, const char* trow, cons
     s_wi[0] = (int)pick4(cnt);
     s_wi[1] = (int)pick4(ec);
     const int b1 = bstar + 1;
-    const uint32_t n1 = b1 > (int)t1 ? 0u : hist[b1] - dep[b1];
+    const uint32_t n1 = b1 > (int)t1 ? 0u : hist[b1];
     s_wi[2] = (int)n1;
     s_wi[3] = (int)ecnt4[b1];
     s_w[2] = (n1 ? (double)n1 * (double)e_rel(key_of_ord16(t1 - (uint32_t)b1), M, c) : 0.0) +
@@ -808,28 +815,19 @@ __device__ __forceinline__ Cut wide_cut(const WideLds& L, const char* trow, cons
   }
   // Exact resolution inside the crossing bin: its entries plus the bin's
   // unpenalized group, in canonical order (key descending, id ascending).
-  for (int i = tid; i < npl; i += NT) {
-    const int id = plid[i];
-    const uint32_t g = plraw[i];
-    const uint32_t raw = g == 0xFFFFFFFFu ? reinterpret_cast<const uint16_t*>(trow)[id] : g & 0xFFFFu;
-    const float zp = penalize(__uint_as_float(raw << 16), rep);
-    if (bin_of(zp) == (uint32_t)bstar) {
-      const int sidx = atomicAdd(scnt, 1);
-      rkey[sidx] = zp;
-      rid[sidx] = id;
-      rmass[sidx] = (double)e_rel(zp, M, c);
-    }
-  }
-  for (int i = tid; i < ns; i += NT) {
-    const int id = ex.id[i];
-    if (pen && ((bm[id >> 5] >> (id & 31)) & 1u)) continue;
-    const float k = ex.key[i];
+  auto take = [&](float k, int id) __attribute__((always_inline)) {
     if (bin_of(k) == (uint32_t)bstar) {
       const int sidx = atomicAdd(scnt, 1);
       rkey[sidx] = k;
       rid[sidx] = id;
       rmass[sidx] = (double)e_rel(k, M, c);
     }
+  };
+  for (int i = tid; i < npl; i += NT) take(penalize(__uint_as_float(pen_raw(i) << 16), rep), plid[i]);
+  for (int i = tid; i < ns; i += NT) {
+    const int id = ex.id[i];
+    if (pen && ((bm[id >> 5] >> (id & 31)) & 1u)) continue;
+    take(ex.key[i], id);
   }
   __syncthreads();
   if (tid < WAVE) {
@@ -1376,7 +1374,7 @@ __device__ __forceinline__ ReqWords request_words(const int32_t* po, const int32
 template <int NT>
 __device__ __forceinline__ void exact_unit(const Args& a, UnitOut* uo, int u, const uint32_t* bm,
                                         const ExactLds& ex, uint32_t why, const CutRes* cpk,
-                                        const CutRes* cqk, const WideLds& wl, bool wide) {
+                                        const CutRes* cqk, const WideLds& wlp, const WideLds& wlq) {
   const int tid = threadIdx.x;
   __shared__ int s_acc;
   // (the unit's request values are derived again here, so that none of
@@ -1413,15 +1411,26 @@ __device__ __forceinline__ void exact_unit(const Args& a, UnitOut* uo, int u, co
     s.kx = 0.0f;
     return s;
   };
-  if (wide) {
-    // (the wide cut's scratch is in the space the exact passes use: it runs first)
-    const float M = wl.cut->M;
-    const Cut w = wide_cut(wl, trow, bm, pen, a.rep, M, c);
-    if (w.ok && tid == 0) *wl.cut = CutRes{1, w.code, w.key, M, w.zk};
+  // Cuts over a row's whole key histogram (their scratch is in the space
+  // the exact passes use: they run first), the target's before the draft's.
+  if (why & FB_P_CUT) {
+    const float M = wlp.cut->M;
+    const Cut w = wide_cut<false>(wlp, trow, a.V, bm, pen, a.rep, M, c);
+    if (w.ok && tid == 0) *wlp.cut = CutRes{1, w.code, w.key, M, w.zk};
     __syncthreads();
     if (w.ok) {
-      cpk = wl.cut;
+      cpk = wlp.cut;
       out.why |= FB_WIDE;
+    }
+  }
+  if ((why & FB_Q_CUT) && !bonus) {
+    const float M = wlq.cut->M;
+    const Cut w = wide_cut<true>(wlq, drow, a.Vd, bm, pen, a.rep, M, c);
+    if (w.ok && tid == 0) *wlq.cut = CutRes{1, w.code, w.key, M, w.zk};
+    __syncthreads();
+    if (w.ok) {
+      cqk = wlq.cut;
+      out.why |= FB_WIDE_Q;
     }
   }
   const RowStat P = cpk ? from_cut(*cpk) : row_stats_dev<SD_BF16, NT>(a, trow, a.V, c, pen, bm, ex, tpr);
@@ -1522,8 +1531,8 @@ __global__ __launch_bounds__(NT_F) void k_pair_fast(Args a, UnitOut* uo) {
   __shared__ double red_d[3][NT / WAVE];
   __shared__ int red_i[2][NT / WAVE];
   __shared__ CutRes s_cut[2];
-  __shared__ double s_tp;     // the target cut's mass threshold (for the wide cut)
-  __shared__ uint32_t s_t1;   // and the target row's anchor
+  __shared__ double s_tp[2];     // each cut's mass threshold and row anchor (for a wide cut)
+  __shared__ uint32_t s_t1[2];
   __shared__ float pkey_arr[2][PE_CAP];
   __shared__ int32_t pid_arr[2][PE_CAP];
   __shared__ uint16_t praw_arr[2][PE_CAP];
@@ -1771,17 +1780,23 @@ __global__ __launch_bounds__(NT_F) void k_pair_fast(Args a, UnitOut* uo) {
     }
     if (lane == 0) {
       s_cut[0] = CutRes{good ? (cc.ok ? 1 : -1) : 0, cc.code, cc.key, M, cc.zk};
-      s_tp = TP;
-      s_t1 = t1p;
+      s_tp[0] = TP;
+      s_t1[0] = t1p;
     }
   }
   __syncthreads();
   const CutRes cp = s_cut[0];
   const float Mp = cp.M;
   const int nep = s_ne[0], npp = s_np[0];
-  if (cp.ok != 1) {
+  // A target crossing below the window: the row's key histogram (in the
+  // slots' space) is exact for RUP keys below the window's top, which most
+  // such crossings reach.  The unit streams its draft row without filing
+  // slots (the window's codes do not mark that nucleus), and the exact
+  // route cuts both rows from their histograms.
+  const bool pmiss = cp.ok == -1;
+  if (cp.ok == 0 || (pmiss && bonus)) {
     oflags = UO_FALLBACK;
-    why = cp.ok == 0 ? FB_P_STATE : FB_P_CUT;
+    why = pmiss ? FB_P_CUT : FB_P_STATE;
     goto write_out_flags;
   }
   {
@@ -1833,7 +1848,7 @@ __global__ __launch_bounds__(NT_F) void k_pair_fast(Args a, UnitOut* uo) {
     const Bins binq = row_bins(t1q);
     RowAcc aq = row_acc_init();
     if (anchor_q) aq.mo = ord16f(Gq) * 0x00010001u;
-    auto stream_b = [&]<int LOW, bool RAISE, bool TAIL>() __attribute__((always_inline)) {
+    auto stream_b = [&]<int LOW, bool RAISE, bool TAIL, bool FILE = true>() __attribute__((always_inline)) {
     static_for<NR>([&]<int l>() __attribute__((always_inline)) {
       const uint4 ld = stg[(NR + l) % NSTG];
       if constexpr (l == 0 || l == 6 || l == 12 || l == 17)
@@ -1845,7 +1860,8 @@ __global__ __launch_bounds__(NT_F) void k_pair_fast(Args a, UnitOut* uo) {
         const uint32_t bits = RAISE ? pen_bits8(bm, k) : 0u;
         const uint4 dv = make_uint4(v.w[0], v.w[1], v.w[2], v.w[3]);
         (void)row_vec<(l < NSAMP)>(v, k, t1q, binq, histq, exq, aq);
-        file_round<LOW>(l, code[l][0], code[l][1], dv, true, bits, cut_code, RAISE, slot_arr, nslot);
+        if constexpr (FILE)
+          file_round<LOW>(l, code[l][0], code[l][1], dv, true, bits, cut_code, RAISE, slot_arr, nslot);
       }
       SDV_PIN(aq.mo);
       SDV_PIN(aq.lo);
@@ -1858,7 +1874,8 @@ __global__ __launch_bounds__(NT_F) void k_pair_fast(Args a, UnitOut* uo) {
     // penalized keys rise or a vector needs masking)
     const bool low = cut_code < 127u;
     const bool tail_d = (Vd & 7) != 0 || Vd < V || Vd <= (NR - 1) * NT_F * VEC;
-    if (raise || tail_d) stream_b.template operator()<-1, true, true>();
+    if (pmiss) stream_b.template operator()<-1, false, true, false>();
+    else if (raise || tail_d) stream_b.template operator()<-1, true, true>();
     else if (low) stream_b.template operator()<1, false, false>();
     else stream_b.template operator()<0, false, false>();
     __syncthreads();   // the draft stream is done: histogram, stream entries
@@ -1902,14 +1919,20 @@ __global__ __launch_bounds__(NT_F) void k_pair_fast(Args a, UnitOut* uo) {
       cc.code = 0;
       cc.key = 0.0f;
       cc.zk = 0.0;
+      double TPq = 0.0;
       if (good) {
         const double Zqa = Zs * exp2((double)gcq - (double)M * (double)c);
-        cc = wave_cut(histq, hneg, exq, ne, np, bm, pen, t1q, M, c, tp * Zqa, ecnt, emass, rkey, rmass,
-                      rid, &s_rcnt);
+        TPq = tp * Zqa;
+        cc = wave_cut(histq, hneg, exq, ne, np, bm, pen, t1q, M, c, TPq, ecnt, emass, rkey, rmass, rid,
+                      &s_rcnt);
       }
       // (a slot overflow with both cuts settled hands those cuts to the exact route)
       const int okv = !good ? 0 : !cc.ok ? -1 : over ? -2 : 1;
-      if (lane == 0) s_cut[1] = CutRes{okv, cc.code, cc.key, M, cc.zk};
+      if (lane == 0) {
+        s_cut[1] = CutRes{okv, cc.code, cc.key, M, cc.zk};
+        s_tp[1] = TPq;
+        s_t1[1] = t1q;
+      }
     } else if (wv == 1 && lane < 2) {
       // Meanwhile the draft token's fp64 exponentials: lane 0 p(x_j) (the
       // target cut is known), lane 1 the draft's, which its normalizer and
@@ -1930,9 +1953,10 @@ __global__ __launch_bounds__(NT_F) void k_pair_fast(Args a, UnitOut* uo) {
     }
     __syncthreads();
     const CutRes cq = s_cut[1];
-    if (cq.ok != 1) {
+    if (cq.ok != 1 || pmiss) {
       oflags = UO_FALLBACK;
-      why = cq.ok == -2 ? FB_SLOTS : cq.ok == 0 ? FB_Q_STATE : FB_Q_CUT;
+      why = (pmiss ? FB_P_CUT : 0u) |
+            (cq.ok == 1 ? 0u : cq.ok == -2 ? FB_SLOTS : cq.ok == 0 ? FB_Q_STATE : FB_Q_CUT);
       goto write_out_flags;
     }
     Mq = cq.M;
@@ -2137,31 +2161,37 @@ write_out_flags:
 #else
     const Args ax = a;   // (the host pass only parses device code)
 #endif
-    // A target row whose crossing lies below the window: its key histogram
-    // (in the slots' space; the draft stream has not begun) is exact for
-    // RUP keys below the window's top, which most such crossings reach.
-    WideLds wl;
-    wl.hist = hsl.slot_arr;
-    wl.dep = hsl.histq;
-    wl.ecnt4 = hsl.histq + RUP;
-    wl.emass4 = reinterpret_cast<uint64_t*>(hsl.slot_arr + NBINW);
-    wl.ex = exp_;
-    wl.ns = s_ne[0];
-    wl.plid = plid;
-    wl.plraw = plraw;
-    wl.npl = s_npl;
-    wl.rkey = rkey;
-    wl.rmass = rmass;
-    wl.rid = rid;
-    wl.scnt = &s_rcnt;
-    wl.wtot = sd;
-    wl.TP = s_tp;
-    wl.t1 = s_t1;
-    wl.cut = &s_cut[0];
-    // a slot overflow comes with both cuts settled (for a bonus row, its one)
-    const bool cuts = why == FB_SLOTS;
-    exact_unit<NT>(ax, uo, blockIdx.x, bm, ex, why, cuts ? &s_cut[0] : nullptr,
-                   cuts && !bonus ? &s_cut[1] : nullptr, wl, why == FB_P_CUT);
+    // Rows whose crossing lies below the window are cut from their whole
+    // key histograms: the target's (in the slots' space, no slot filed),
+    // then the draft's (with the slots' space for scratch).
+    auto wide_lds = [&](bool is_t) __attribute__((always_inline)) {
+      WideLds w;
+      w.hist = is_t ? hsl.slot_arr : hsl.histq;
+      w.ecnt4 = is_t ? hsl.slot_arr + NBINW + 2 * RUP : hsl.slot_arr;
+      w.emass4 = reinterpret_cast<uint64_t*>(is_t ? hsl.slot_arr + NBINW : hsl.slot_arr + RUP);
+      w.ex = is_t ? exp_ : exq;
+      w.ns = s_ne[is_t ? 0 : 1];
+      w.plid = plid;
+      w.plraw = plraw;
+      w.npl = s_npl;
+      w.rkey = rkey;
+      w.rmass = rmass;
+      w.rid = rid;
+      w.scnt = &s_rcnt;
+      w.wtot = sd;
+      w.TP = s_tp[is_t ? 0 : 1];
+      w.t1 = s_t1[is_t ? 0 : 1];
+      w.cut = &s_cut[is_t ? 0 : 1];
+      return w;
+    };
+    static_assert(NBINW + 3 * RUP <= CAPT * NT, "wide-cut scratch");
+    // The cuts the single pass settled go along: the target's unless its
+    // state or cut failed, the draft's with a slot overflow or after a
+    // target cut below the window.
+    const bool p_set = !(why & (FB_P_STATE | FB_P_CUT));
+    const bool q_set = !bonus && (why == FB_SLOTS || why == FB_P_CUT);
+    exact_unit<NT>(ax, uo, blockIdx.x, bm, ex, why, p_set ? &s_cut[0] : nullptr, q_set ? &s_cut[1] : nullptr,
+                   wide_lds(true), wide_lds(false));
   }
 }
 
