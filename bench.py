@@ -17,7 +17,9 @@ HIP events inside the timed region.  Prints one JSON line.
 The default warmup is long on purpose: after an idle spell the first ~40
 back-to-back calls run through a clock transient (the dominant kernel takes
 up to ~1.25x its sustained time), and the timed steps should see the
-sustained rate.
+sustained rate.  With a shorter --warmup W the bench still runs untimed
+steps until SETTLE_STEPS have run in all (the line's settle_steps says how
+many it added).
 
 `roofline.traffic` is the dominant kernel's HBM bytes per launch from two
 rocprofv3 counter runs (FETCH_SIZE, then WRITE_SIZE) of this script with
@@ -50,6 +52,9 @@ WORKLOAD = ("256 requests x K=8, V=152064, bf16 logits, T~U[0.5,1], top-p 0.9, "
 
 # The sources k_pair_fast is built from (the confidence kernel's file is not
 # one of them).
+# Untimed steps before the timed region, at least (W included).
+SETTLE_STEPS = 40
+
 VERIFY_SOURCES = ("sd_verify.hip", "sdv_device.h", "sdv_exact.h")
 
 
@@ -337,10 +342,17 @@ def main():
             if evs is not None:
                 evs[ph][1].record(stream)
 
+    # W warmup steps, then more untimed steps while fewer than SETTLE_STEPS
+    # have run: the clocks' ramp after an idle spell spans ~40 calls, and the
+    # timed steps should see the sustained rate whatever W is (reported as
+    # settle_steps).
     for _ in range(a.warmup):
         step()
+    settle = max(0, SETTLE_STEPS - a.warmup)
+    for _ in range(settle):
+        step()
     torch.cuda.synchronize()
-    print(f"[bench] warmup done ({a.warmup} steps)", file=sys.stderr, flush=True)
+    print(f"[bench] warmup done ({a.warmup} steps + {settle} settle steps)", file=sys.stderr, flush=True)
 
     E = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
     evs = [[[E(), E()] for _ in range(3)] for _ in range(a.steps)]
@@ -374,6 +386,7 @@ def main():
         "n_gpus": 1,
         "steps": a.steps,
         "warmup": a.warmup,
+        "settle_steps": settle,
         "ms_per_step": ms_step,
         "higher_is_better": True,
         "scaling": "weak",

@@ -332,11 +332,21 @@ __device__ __forceinline__ double pair_tv_dev(const Args& a, const char* trow, c
             apply_penalty8(bm, k, 0, a.rep, zp[u]);
             apply_penalty8(bm, k, 0, a.rep, zq[u]);
           }
+          bool kp[VEC], kq[VEC];
+          bool any = false;
 #pragma unroll
           for (int e = 0; e < VEC; ++e) {
             const int id = k * VEC + e;
-            const float p = (id < V && kept(P, ord_key(zp[u][e]))) ? e_rel(zp[u][e], P.M, P.c) * ip : 0.0f;
-            const float q = (id < a.Vd && kept(Q, ord_key(zq[u][e]))) ? e_rel(zq[u][e], Q.M, Q.c) * iq : 0.0f;
+            kp[e] = id < V && kept(P, ord_key(zp[u][e]));
+            kq[e] = id < a.Vd && kept(Q, ord_key(zq[u][e]));
+            any |= kp[e] | kq[e];
+          }
+          // (vectors of the wave outside both nuclei add zeros: skipped)
+          if (!__any(any)) continue;
+#pragma unroll
+          for (int e = 0; e < VEC; ++e) {
+            const float p = kp[e] ? e_rel(zp[u][e], P.M, P.c) * ip : 0.0f;
+            const float q = kq[e] ? e_rel(zq[u][e], Q.M, Q.c) * iq : 0.0f;
             s += fabsf(p - q);
           }
         }
@@ -386,10 +396,24 @@ __device__ __forceinline__ Drawn draw_dev(const Args& a, const char* trow, const
     }
     if (pen) apply_penalty8(bm, k, 0, a.rep, zp);
     if (md == 0 && pen) apply_penalty8(bm, k, 0, a.rep, zq);
+    bool kp[VEC];
+    bool any = false;
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) {
+      kp[e] = k * VEC + e < V && kept(P, ord_key(zp[e]));
+      any |= kp[e];
+    }
+    // (a weight is zero outside p's nucleus: vectors of the wave with none
+    // of its tokens skip the exponentials)
+    if (!__any(any)) {
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) w[e] = 0.0f;
+      return s;
+    }
 #pragma unroll
     for (int e = 0; e < VEC; ++e) {
       const int id = k * VEC + e;
-      float p = (id < V && kept(P, ord_key(zp[e]))) ? e_rel(zp[e], P.M, P.c) * ip : 0.0f;
+      float p = kp[e] ? e_rel(zp[e], P.M, P.c) * ip : 0.0f;
       if (md == 0) {
         const float q = (id < a.Vd && kept(Q, ord_key(zq[e]))) ? e_rel(zq[e], Q.M, Q.c) * iq : 0.0f;
         p = fmaxf(p - q, 0.0f);
