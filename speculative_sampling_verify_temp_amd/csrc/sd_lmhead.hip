@@ -243,8 +243,11 @@ __device__ __forceinline__ void tile_gemm(const uint16_t* const (&arow)[2 * MB],
     for (int b = 0; b < 2; ++b)
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[mb][b][v] = 0.0f;
-  uint4 ra[2 * MB], rb[4];
-  auto load = [&](int k0) __attribute__((always_inline)) {
+  // Two register sets of chunk loads: chunk k + 2 is loaded while chunk k
+  // is multiplied, so two chunks' loads are in flight behind the matrix
+  // cores (one chunk's latency is several times its MFMA work).
+  uint4 ra0[2 * MB], rb0[4], ra1[2 * MB], rb1[4];
+  auto load = [&](int k0, uint4 (&ra)[2 * MB], uint4 (&rb)[4]) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < 2 * MB; ++i)
       ra[i] = arow[i] ? *reinterpret_cast<const uint4*>(arow[i] + k0 + kc) : make_uint4(0, 0, 0, 0);
@@ -252,9 +255,10 @@ __device__ __forceinline__ void tile_gemm(const uint16_t* const (&arow)[2 * MB],
     for (int i = 0; i < 4; ++i)
       rb[i] = brow[i] ? *reinterpret_cast<const uint4*>(brow[i] + k0 + kc) : make_uint4(0, 0, 0, 0);
   };
-  load(0);
   const int ko = 8 * (lane >> 5);
-  for (int k0 = 0; k0 < H; k0 += BK) {
+  // one K chunk: its loads to LDS, the load of the chunk two ahead into the
+  // same registers, then the products
+  auto chunk = [&](int k0, uint4 (&ra)[2 * MB], uint4 (&rb)[4]) __attribute__((always_inline)) {
     __syncthreads();   // the previous chunk's fragments are read
 #pragma unroll
     for (int i = 0; i < 2 * MB; ++i)
@@ -263,7 +267,7 @@ __device__ __forceinline__ void tile_gemm(const uint16_t* const (&arow)[2 * MB],
     for (int i = 0; i < 4; ++i)
       *reinterpret_cast<uint4*>(s.b + (rr + 32 * i) * LDK + kc) = rb[i];
     __syncthreads();
-    if (k0 + BK < H) load(k0 + BK);   // the next chunk's loads overlap this chunk's MFMAs
+    if (k0 + 2 * BK < H) load(k0 + 2 * BK, ra, rb);
 #pragma unroll
     for (int st = 0; st < BK / 16; ++st) {
       bf16x8 af[MB];
@@ -279,7 +283,15 @@ __device__ __forceinline__ void tile_gemm(const uint16_t* const (&arow)[2 * MB],
           acc[mb][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[mb], bfr, acc[mb][b], 0, 0, 0);
       }
     }
+  };
+  load(0, ra0, rb0);
+  if (BK < H) load(BK, ra1, rb1);
+  int k0 = 0;
+  for (; k0 + BK < H; k0 += 2 * BK) {
+    chunk(k0, ra0, rb0);
+    chunk(k0 + BK, ra1, rb1);
   }
+  if (k0 < H) chunk(k0, ra0, rb0);
 }
 
 // Rows 64 p .. 64 p + 63 of a tile of 64 MB rows into an fp32 LDS tile
@@ -338,7 +350,7 @@ __device__ __forceinline__ const uint16_t* hidden_row(const LmArgs& a, bool targ
 // Pass 1: per (listed row, token tile) max and exp2 sum; the draft token's logit.
 // ---------------------------------------------------------------------------
 template <bool TGT>
-__global__ __launch_bounds__(NT_L) void k_lm_stats(LmArgs a, LmWs w, int nm, int nn) {
+__global__ __launch_bounds__(NT_L, 2) void k_lm_stats(LmArgs a, LmWs w, int nm, int nn) {
   // (each fp32 part is stashed over the A/B chunks once the product is done)
   __shared__ __align__(16) float lds_ab_c[TALL_LDS_WORDS];
   uint16_t* const sa = reinterpret_cast<uint16_t*>(lds_ab_c);
@@ -824,7 +836,7 @@ __global__ __launch_bounds__(NT_L) void k_lm_draw_pick(LmArgs a, LmWs w, int nn,
 // ---------------------------------------------------------------------------
 // Greedy: per (listed target row, tile) the largest logit and its lowest id.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(NT_L) void k_lm_greedy_part(LmArgs a, LmWs w, int nm, int nn) {
+__global__ __launch_bounds__(NT_L, 2) void k_lm_greedy_part(LmArgs a, LmWs w, int nm, int nn) {
   // (each fp32 part is stashed over the A/B chunks once the product is done)
   __shared__ __align__(16) float lds_ab_c[TALL_LDS_WORDS];
   uint16_t* const sa = reinterpret_cast<uint16_t*>(lds_ab_c);
