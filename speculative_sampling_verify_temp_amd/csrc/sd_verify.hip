@@ -451,23 +451,24 @@ struct Cut {
 };
 
 // Exact top-p cut of a row from its window histogram and exact list, by
-// one wave (the caller's wave 0; no block barriers).  Window bins are
+// one wave (the caller's wave 0; no block barriers), in two parts so that
+// the first can run before the row's normalizer is summed.  Window bins are
 // visited from the top; the first non-empty bin whose cumulative mass
 // reaches TP is the crossing bin.  A crossing bin that holds exact entries
-// is resolved key by key, ties kept together.  A bin's count is
-// hist - hneg (the row's key histogram, whose bins 1..254 are the window,
-// less the penalized logits that left it); ecnt / emass (count and
-// fixed-point mass of exact entries per bin) start at zero.  Lane L owns
-// bins 4L .. 4L+3.
-__device__ __forceinline__ Cut wave_cut(const uint32_t* hist, const uint32_t* hneg, const ExactList& ex,
-                                        int ns, int np,
-                                        const uint32_t* bm, bool pen, uint32_t t1, float M, float c,
-                                        double TP, uint32_t* ecnt, uint64_t* emass, float* rkey,
-                                        double* rmass, int* rid, int* scnt) {
+// is resolved key by key, ties kept together.
+//
+// wave_cut_prep (needs the row max M): a bin's count is hist - hneg (the
+// row's key histogram, whose bins 1..254 are the window, less the
+// penalized logits that left it); ecnt / emass (count and fixed-point mass
+// of exact entries per bin) start at zero.  Lane L owns bins 4L .. 4L+3.
+// It leaves each bin's count in hneg, its exact-entry count in ecnt, its
+// mass (a double) in emass, and lane L's exclusive scan in cx[L].
+__device__ __forceinline__ void wave_cut_prep(const uint32_t* hist, uint32_t* hneg, const ExactList& ex,
+                                              int ns, int np, const uint32_t* bm, bool pen, uint32_t t1,
+                                              float M, float c, uint32_t* ecnt, uint64_t* emass,
+                                              double* cx) {
   const int ne = ns + np;
   const int lane = threadIdx.x % WAVE;
-  if (lane == 0) *scnt = 0;
-  __builtin_amdgcn_wave_barrier();
   for (int i = lane; i < ne; i += WAVE) {
     float k;
     int id;
@@ -499,6 +500,34 @@ __device__ __forceinline__ Cut wave_cut(const uint32_t* hist, const uint32_t* hn
     lsum += m;
   }
   const double excl = wave_incl_scan(lsum) - lsum;
+  __builtin_amdgcn_wave_barrier();
+  reinterpret_cast<uint4*>(hneg)[lane] = make_uint4(cnt[0], cnt[1], cnt[2], cnt[3]);
+  reinterpret_cast<uint4*>(ecnt)[lane] = make_uint4(ec[0], ec[1], ec[2], ec[3]);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) reinterpret_cast<double*>(emass)[4 * lane + i] = mass[i];
+  cx[lane] = excl;
+}
+
+// wave_cut_finish: the crossing and the cut from wave_cut_prep's bins and
+// the threshold TP (mass relative to exp2(M c)); the exact list, M and t1
+// as for the prep.
+__device__ __forceinline__ Cut wave_cut_finish(const uint32_t* hcnt, const uint32_t* ecnt,
+                                               const uint64_t* emass, const double* cx,
+                                               const ExactList& ex, int ns, int np, const uint32_t* bm,
+                                               bool pen, uint32_t t1, float M, float c, double TP,
+                                               float* rkey, double* rmass, int* rid, int* scnt) {
+  const int ne = ns + np;
+  const int lane = threadIdx.x % WAVE;
+  if (lane == 0) *scnt = 0;
+  const uint4 h4 = reinterpret_cast<const uint4*>(hcnt)[lane];
+  const uint4 e4 = reinterpret_cast<const uint4*>(ecnt)[lane];
+  const uint32_t cnt[4] = {h4.x, h4.y, h4.z, h4.w};
+  const uint32_t ec[4] = {e4.x, e4.y, e4.z, e4.w};
+  double mass[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) mass[i] = reinterpret_cast<const double*>(emass)[4 * lane + i];
+  const double excl = cx[lane];
+  __builtin_amdgcn_wave_barrier();
   // first crossing bin of this lane
   double cum = excl, cin = 0.0, cex = 0.0;
   int hit = -1;
@@ -1135,21 +1164,20 @@ __device__ __forceinline__ float key_term(float key, float c, float gc) {
   return fast_exp2(fmaf(key, c, -gc));
 }
 
-// This thread's share of a row's normalizer from its key histogram (bins
-// 4 tid .. 4 tid + 3 and the same NT_F * 4 further on, the lumped ones
-// excepted) and from the stream's exact entries (keys above the window;
-// bin 0's count is not used).
+// Worker wk's share (of nwk workers) of a row's normalizer from its key
+// histogram (bin groups 4g .. 4g + 3 for g = wk, wk + nwk, ..., the lumped
+// bins excepted) and from the stream's exact entries (keys above the
+// window; bin 0's count is not used).
 __device__ __forceinline__ double hist_z(const uint32_t* hist, const Bins& bn, uint32_t t1, float c,
-                                         float gc, const ExactList& ex, int ns, int tid) {
-  static_assert(NBINW == 8 * NT_F, "hist_z geometry");
-  // (fp32 within a thread: eight terms, each count x term with a relative
+                                         float gc, const ExactList& ex, int ns, int wk, int nwk) {
+  // (fp32 within a thread: a few terms, each count x term with a relative
   // error of a few ulp, as the stream's own per-round sums were)
   float z = 0.0f;
   // (a loop, not unrolled: the stream's codes and the draft ring are live here)
 #pragma unroll 1
-  for (int half = 0; half < 2; ++half) {
-    const int i0 = 4 * (tid + half * NT_F);
-    const uint4 h4 = reinterpret_cast<const uint4*>(hist)[tid + half * NT_F];
+  for (int g = wk; g < NBINW / 4; g += nwk) {
+    const int i0 = 4 * g;
+    const uint4 h4 = reinterpret_cast<const uint4*>(hist)[g];
     const uint32_t hv[4] = {h4.x, h4.y, h4.z, h4.w};
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
@@ -1159,7 +1187,7 @@ __device__ __forceinline__ double hist_z(const uint32_t* hist, const Bins& bn, u
     }
   }
   double zd = (double)z;
-  for (int i = tid; i < min(ns, E_CAP); i += NT_F) zd += (double)key_term(ex.key[i], c, gc);
+  for (int i = wk; i < min(ns, E_CAP); i += nwk) zd += (double)key_term(ex.key[i], c, gc);
   return zd;
 }
 
@@ -1516,6 +1544,7 @@ __global__ __launch_bounds__(NT_F) void k_pair_fast(Args a, UnitOut* uo) {
   __shared__ uint32_t ecnt[NBIN];
   __shared__ uint64_t emass[NBIN];
   __shared__ __align__(16) uint32_t hneg[NBIN];   // penalized logits that left a bin
+  __shared__ double cxs[WAVE];                   // the window cut's per-lane scan
   __shared__ float rkey[R_CAP];
   __shared__ double rmass[R_CAP];
   __shared__ int rid[R_CAP];
@@ -1728,7 +1757,29 @@ __global__ __launch_bounds__(NT_F) void k_pair_fast(Args a, UnitOut* uo) {
       const uint32_t raw = g == 0xFFFFFFFFu ? reinterpret_cast<const uint16_t*>(trow)[id] : g & 0xFFFFu;
       pen_fix(raw, id, t1p, rep, c, gcp, hneg, exp_, ap);
     }
-  ap.Z += hist_z(hist, binp, t1p, c, gcp, exp_, s_ne[0], tid);
+  {
+    const float wm = wave_max(row_max(ap));
+    if (lane == 0) red_f[1][wv] = wm;
+  }
+  __syncthreads();   // penalized logits settled; maxima
+  // Wave 0 prepares the window cut (it needs the row max, not the
+  // normalizer) while waves 1.. sum the normalizer from the histogram.
+  float M = 0.0f;
+  bool prep_ok = false;
+  const int ne0 = s_ne[0], np0 = s_np[0];
+  if (wv == 0) {
+    M = red_f[1][0];
+#pragma unroll
+    for (int i = 1; i < NT / WAVE; ++i) M = fmaxf(M, red_f[1][i]);
+    prep_ok = anchor_ok && M > -INFINITY && M < INFINITY && ne0 <= E_CAP && np0 <= PE_CAP && npl <= PL_CAP;
+    if (prep_ok) {
+      __builtin_amdgcn_s_setprio(3);
+      wave_cut_prep(hist, hneg, exp_, ne0, np0, bm, pen, t1p, M, c, ecnt, emass, cxs);
+      __builtin_amdgcn_s_setprio(0);
+    }
+  } else {
+    ap.Z += hist_z(hist, binp, t1p, c, gcp, exp_, s_ne[0], tid - WAVE, NT - WAVE);
+  }
   {
     // The draft's anchor rides along: the block max of its first NSAMP
     // rounds, which the ring already holds.
@@ -1743,30 +1794,22 @@ __global__ __launch_bounds__(NT_F) void k_pair_fast(Args a, UnitOut* uo) {
         }
       });
     }
-    const float wm = wave_max(row_max(ap));
     const float wq = wave_max(q0);
     const double wz = wave_sum(ap.Z);
     if (lane == 0) {
-      red_f[1][wv] = wm;
       red_f[2][wv] = wq;
       red_d[0][wv] = wz;
     }
   }
-  __syncthreads();   // penalized logits settled; partials
+  __syncthreads();   // partials
   if (wv == 0) {
-    float M = red_f[1][0];
     double Zs = 0.0;
 #pragma unroll
-    for (int i = 0; i < NT / WAVE; ++i) {
-      M = fmaxf(M, red_f[1][i]);
-      Zs += red_d[0][i];
-    }
+    for (int i = 0; i < NT / WAVE; ++i) Zs += red_d[0][i];
     double zerr;
     Zs += lumped_z(hist, binp, t1p, c, gcp, &zerr);
-    const int ne = s_ne[0], np = s_np[0];
     // (the lumped bins may move the normalizer by at most 2^-24 of itself)
-    const bool good = anchor_ok && M > -INFINITY && M < INFINITY && Zs > 0.0 && Zs < INFINITY &&
-                      zerr <= 0x1p-24 * Zs && ne <= E_CAP && np <= PE_CAP && npl <= PL_CAP;
+    const bool good = prep_ok && Zs > 0.0 && Zs < INFINITY && zerr <= 0x1p-24 * Zs;
     Cut cc;
     cc.ok = 0;
     cc.code = 0;
@@ -1776,7 +1819,8 @@ __global__ __launch_bounds__(NT_F) void k_pair_fast(Args a, UnitOut* uo) {
     if (good) {
       const double Zp = Zs * exp2((double)gcp - (double)M * (double)c);
       TP = tp * Zp;
-      cc = wave_cut(hist, hneg, exp_, ne, np, bm, pen, t1p, M, c, TP, ecnt, emass, rkey, rmass, rid, &s_rcnt);
+      cc = wave_cut_finish(hneg, ecnt, emass, cxs, exp_, ne0, np0, bm, pen, t1p, M, c, TP, rkey, rmass, rid,
+                           &s_rcnt);
     }
     if (lane == 0) {
       s_cut[0] = CutRes{good ? (cc.ok ? 1 : -1) : 0, cc.code, cc.key, M, cc.zk};
@@ -1887,33 +1931,49 @@ __global__ __launch_bounds__(NT_F) void k_pair_fast(Args a, UnitOut* uo) {
                              : g == 0xFFFFFFFFu ? reinterpret_cast<const uint16_t*>(drow)[id] : g >> 16;
         pen_fix(raw, id, t1q, rep, c, gcq, hneg, exq, aq);
       }
-    aq.Z += hist_z(histq, binq, t1q, c, gcq, exq, s_ne[1], tid);
     {
       const float wm = wave_max(row_max(aq));
-      const double wz = wave_sum(aq.Z);
       const int wo = __any(nslot > CAPT) ? 1 : 0;
       if (lane == 0) {
         red_f[3][wv] = wm;
-        red_d[1][wv] = wz;
         red_i[0][wv] = wo;
       }
     }
-    __syncthreads();   // penalized logits settled; partials
+    __syncthreads();   // penalized logits settled; maxima
+    // (as for the target row: wave 0 prepares the cut meanwhile)
+    float Mq0 = 0.0f;
+    bool prepq = false;
+    const int ne1 = s_ne[1], np1 = s_np[1];
     if (wv == 0) {
-      float M = red_f[3][0];
+      Mq0 = red_f[3][0];
+#pragma unroll
+      for (int i = 1; i < NT / WAVE; ++i) Mq0 = fmaxf(Mq0, red_f[3][i]);
+      prepq = anchor_q && Mq0 > -INFINITY && Mq0 < INFINITY && ne1 <= E_CAP && np1 <= PE_CAP;
+      if (prepq) {
+        __builtin_amdgcn_s_setprio(3);
+        wave_cut_prep(histq, hneg, exq, ne1, np1, bm, pen, t1q, Mq0, c, ecnt, emass, cxs);
+        __builtin_amdgcn_s_setprio(0);
+      }
+    } else {
+      aq.Z += hist_z(histq, binq, t1q, c, gcq, exq, s_ne[1], tid - WAVE, NT - WAVE);
+    }
+    {
+      const double wz = wave_sum(aq.Z);
+      if (lane == 0) red_d[1][wv] = wz;
+    }
+    __syncthreads();   // partials
+    if (wv == 0) {
+      const float M = Mq0;
       double Zs = 0.0;
       int over = 0;
 #pragma unroll
       for (int i = 0; i < NT / WAVE; ++i) {
-        M = fmaxf(M, red_f[3][i]);
         Zs += red_d[1][i];
         over |= red_i[0][i];
       }
       double zerr;
       Zs += lumped_z(histq, binq, t1q, c, gcq, &zerr);
-      const int ne = s_ne[1], np = s_np[1];
-      const bool good = anchor_q && M > -INFINITY && M < INFINITY && Zs > 0.0 && Zs < INFINITY &&
-                        zerr <= 0x1p-24 * Zs && ne <= E_CAP && np <= PE_CAP;
+      const bool good = prepq && Zs > 0.0 && Zs < INFINITY && zerr <= 0x1p-24 * Zs;
       Cut cc;
       cc.ok = 0;
       cc.code = 0;
@@ -1923,8 +1983,8 @@ __global__ __launch_bounds__(NT_F) void k_pair_fast(Args a, UnitOut* uo) {
       if (good) {
         const double Zqa = Zs * exp2((double)gcq - (double)M * (double)c);
         TPq = tp * Zqa;
-        cc = wave_cut(histq, hneg, exq, ne, np, bm, pen, t1q, M, c, TPq, ecnt, emass, rkey, rmass, rid,
-                      &s_rcnt);
+        cc = wave_cut_finish(hneg, ecnt, emass, cxs, exq, ne1, np1, bm, pen, t1q, M, c, TPq, rkey, rmass,
+                             rid, &s_rcnt);
       }
       // (a slot overflow with both cuts settled hands those cuts to the exact route)
       const int okv = !good ? 0 : !cc.ok ? -1 : over ? -2 : 1;
