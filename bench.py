@@ -512,14 +512,15 @@ def _gumbel_ids(torch, rows, T, g):
 
 
 def _phase_loop(torch, sdv, argsets, ws, outs, steps, warmup, stream):
-    """Run sd_verify_sample phase by phase over the argument sets in turn;
-    returns (ms per call, {kernel: ms per launch})."""
+    """Run sd_verify_sample phase by phase over the argument sets in turn
+    (each set with the phases it needs: a TV budget strictly between 0 and
+    1 adds the TV pass); returns (ms per call, {kernel: ms per launch})."""
     import numpy as np
     acc, tok, st = outs
-    names = [sdv.phase_kernel(argsets[0], ph) for ph in range(3)]
+    names = [[sdv.phase_kernel(a_, ph) for ph in range(3)] for a_ in argsets]
     for i in range(warmup):
         for ph in range(3):
-            if names[ph] is not None:
+            if names[i % len(argsets)][ph] is not None:
                 sdv.run_phase(argsets[i % len(argsets)], ws, ph, acc, tok, st, None, stream)
     torch.cuda.synchronize()
     E = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
@@ -528,7 +529,7 @@ def _phase_loop(torch, sdv, argsets, ws, outs, steps, warmup, stream):
     s0.record(stream)
     for i in range(steps):
         for ph in range(3):
-            if names[ph] is None:
+            if names[i % len(argsets)][ph] is None:
                 continue
             evs[i][ph][0].record(stream)
             sdv.run_phase(argsets[i % len(argsets)], ws, ph, acc, tok, st, None, stream)
@@ -536,8 +537,13 @@ def _phase_loop(torch, sdv, argsets, ws, outs, steps, warmup, stream):
     s1.record(stream)
     torch.cuda.synchronize()
     ms = s0.elapsed_time(s1) / steps
-    per = {names[ph]: float(np.mean([evs[i][ph][0].elapsed_time(evs[i][ph][1]) for i in range(steps)]))
-           for ph in range(3) if names[ph] is not None}
+    times = {}
+    for i in range(steps):
+        for ph in range(3):
+            nm = names[i % len(argsets)][ph]
+            if nm is not None:
+                times.setdefault(nm, []).append(evs[i][ph][0].elapsed_time(evs[i][ph][1]))
+    per = {nm: float(np.mean(v)) for nm, v in times.items()}
     return ms, per
 
 

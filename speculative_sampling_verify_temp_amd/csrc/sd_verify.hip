@@ -110,8 +110,145 @@ __global__ __launch_bounds__(NT_ROW) void k_row_prepare(Args a, RowStat* rs, int
   }
 }
 
+// Slices of the general path's TV and draw passes at small batch sizes:
+// each (pair) or (request) task is split over workgroups by vector ranges
+// so that a call fills the device's 256 compute units with one workgroup
+// each; from 128 tasks on a task keeps one workgroup.  Slices hold
+// TV_SLICE_MIN vectors, or DRAW_SLICE_CH draw chunks, at least.
+constexpr int SLICE_TASKS = 256;
+constexpr int TV_SLICE_MIN = 512;
+constexpr int DRAW_SLICE_CH = 2;
+
+__host__ __device__ inline int slices_for(int tasks, int smax) {
+  if (tasks <= 0 || 2 * tasks > SLICE_TASKS) return 1;
+  return max(1, min(smax, SLICE_TASKS / tasks));
+}
+
+__host__ __device__ inline int tv_slices(int B, int K, int V) {
+  return slices_for(B * K, max(1, (V + VEC - 1) / VEC / TV_SLICE_MIN));
+}
+
+__host__ __device__ inline int draw_chunks(int V) { return ((V + VEC - 1) / VEC + CHV - 1) / CHV; }
+
+__host__ __device__ inline int draw_slices(int B, int V) {
+  return slices_for(B, max(1, draw_chunks(V) / DRAW_SLICE_CH));
+}
+
+// |p - q| sums of the pairs' rows: workgroup b takes slice b % S of pair
+// b / S (vectors [s len, s len + len) with len = ceil(nvec / S)) and writes
+// its sum to dpart[b]; d = min(sum over the pair's slices / 2, 1).
+// Rows without top-p at small batch sizes: each row's max and normalizer
+// pass is split over workgroups by vector ranges (ROW_SLICE_MIN vectors at
+// least), and k_row_combine merges the slices.  (Rows with top-p keep one
+// workgroup: their cut's histogram passes need the whole row.)
+constexpr int ROW_SLICE_MIN = 512;
+
+__host__ __device__ inline int row_slices(int B, int K, int V, bool topp) {
+  if (topp) return 1;
+  return slices_for(B * (2 * K + 1), min(WAVE, max(1, (V + VEC - 1) / VEC / ROW_SLICE_MIN)));
+}
+
+struct RowPart {
+  float M;       // the slice's max (-inf: none)
+  int bad;       // a NaN met while the slice's logits so far were -inf
+  double Z;      // sum exp2((key - M) c) over the slice
+};
+static_assert(sizeof(RowPart) == 16, "RowPart layout");
+
+// The row's decode: row u = r (2 K_max + 1) + rho of the prepared rows, and
+// whether k_row_prepare would skip it (request or position not valid).
+__device__ __forceinline__ bool row_task(const Args& a, int u, int& r, bool& is_t, int& j, int& K, float& c) {
+  const int nrows = 2 * a.K_max + 1;
+  r = u / nrows;
+  const int rho = u % nrows;
+  K = request_k(a, r);
+  if (K < 0 || K > a.K_max) return false;
+  is_t = rho <= a.K_max;
+  j = is_t ? rho : rho - a.K_max - 1;
+  if (is_t ? (j > K) : (j >= K)) return false;
+  const float T = request_t(a, r);
+  if (!(T > 0.0f) || !(T < INFINITY)) return false;
+  c = 1.4426950408889634f / T;
+  return true;
+}
+
+// Slice b % S of prepared row b / S: vectors [s len, s len + len) with
+// len = ceil(nvec / S) of the row's own length.
 template <int DT>
-__global__ __launch_bounds__(NT_ROW) void k_pair_tv(Args a, const RowStat* rs, double* dout) {
+__global__ __launch_bounds__(NT_ROW) void k_row_part(Args a, RowPart* parts, int S) {
+  constexpr int NT = NT_ROW;
+  extern __shared__ __align__(16) unsigned char smem[];
+  uint32_t* bm = reinterpret_cast<uint32_t*>(smem);
+  __shared__ double sd[NT];
+  __shared__ float sf[NT / WAVE];
+  __shared__ int si[NT / WAVE + 4];
+  const int u = blockIdx.x / S, sl = blockIdx.x % S;
+  int r, j, K;
+  bool is_t;
+  float c;
+  if (!row_task(a, u, r, is_t, j, K, c)) return;
+  const int Vr = is_t ? a.V : a.Vd;
+  const int nvec = (Vr + VEC - 1) / VEC, len = (nvec + S - 1) / S;
+  const int k0 = min(nvec, sl * len), k1 = min(nvec, k0 + len);
+  const bool pen = build_penalty_bitmap<NT>(a, r, j, k0 * VEC, (k1 - k0) * VEC, bm);
+  ExactLds L{};
+  L.sd = sd;
+  L.sf = sf;
+  L.si = si;
+  RowPart o;
+  row_max_z<DT, NT>(a, is_t ? target_row(a, r, j) : draft_row(a, r, j), Vr, c, pen, bm, k0 * VEC, L, k0, k1,
+                    o.M, o.Z, o.bad);
+  if (threadIdx.x == 0) parts[blockIdx.x] = o;
+}
+
+// One wave per prepared row: the slices merged into the row's statistics
+// (no top-p: every token kept), with the draft token's key (penalized when
+// it is in the position's penalty set: prior ids and, unless
+// PENALTY_PRIOR_ONLY, the draft prefix).
+template <int DT>
+__global__ __launch_bounds__(WAVE) void k_row_combine(Args a, const RowPart* parts, RowStat* rs, int S) {
+  const int u = blockIdx.x, lane = threadIdx.x;
+  int r, j, K;
+  bool is_t;
+  float c;
+  if (!row_task(a, u, r, is_t, j, K, c)) return;
+  const RowPart* pp = parts + (int64_t)u * S;
+  // (S <= WAVE slices: one per lane)
+  const RowPart q = lane < S ? pp[lane] : RowPart{-INFINITY, 0, 0.0};
+  const float M = wave_max(q.M);
+  const int bad0 = __any(q.bad != 0) ? 1 : 0;
+  const double Z = wave_sum(q.M > -INFINITY ? q.Z * exp2(((double)q.M - (double)M) * (double)c) : 0.0);
+  int x = -1;
+  if (j < K) x = a.ids[(int64_t)r * a.K_max + j];
+  int hit = 0;
+  if (x >= 0 && x < a.V && a.rep != 1.0f) {
+    if (a.prior && a.poff)
+      for (int t = a.poff[r] + lane; t < a.poff[r + 1]; t += WAVE) hit |= a.prior[t] == x;
+    if (!(a.flags & SD_PENALTY_PRIOR_ONLY))
+      for (int t = lane; t < j; t += WAVE) hit |= a.ids[(int64_t)r * a.K_max + t] == x;
+  }
+  const bool pen_x = __any(hit);
+  if (lane == 0) {
+    const int bad = bad0 || !(M > -INFINITY) || !(M < INFINITY) || Z != Z;
+    RowStat out;
+    out.M = M;
+    out.c = c;
+    out.Zk = Z;
+    out.kord = KEEP_ALL;
+    out.idcut = INT_MAX;
+    out.flags = bad ? NONFINITE : 0;
+    out.kx = 0.0f;
+    if (x >= 0 && x < a.V) {
+      float z = (is_t || x < a.Vd) ? load1<DT>(is_t ? target_row(a, r, j) : draft_row(a, r, j), x) : -INFINITY;
+      if (pen_x) z = penalize(z, a.rep);
+      out.kx = z;
+    }
+    rs[u] = out;
+  }
+}
+
+template <int DT>
+__global__ __launch_bounds__(NT_ROW) void k_pair_tv(Args a, const RowStat* rs, double* dpart, int S) {
   constexpr int NT = NT_ROW;
   extern __shared__ __align__(16) unsigned char smem[];
   uint32_t* bm = reinterpret_cast<uint32_t*>(smem);
@@ -119,23 +256,27 @@ __global__ __launch_bounds__(NT_ROW) void k_pair_tv(Args a, const RowStat* rs, d
   __shared__ float sf[NT / WAVE];
   __shared__ int si[NT / WAVE + 4];
   if (a.K_max == 0) return;
-  const int r = blockIdx.x / a.K_max, j = blockIdx.x % a.K_max;
+  const int task = blockIdx.x / S, sl = blockIdx.x % S;
+  const int r = task / a.K_max, j = task % a.K_max;
   const int K = request_k(a, r);
   if (K < 0 || K > a.K_max || j >= K) return;
   const float T = request_t(a, r);
   if (!(T > 0.0f) || !(T < INFINITY)) return;
   const RowStat P = rs[row_index(a, r, true, j)], Q = rs[row_index(a, r, false, j)];
   if ((P.flags | Q.flags) & NONFINITE) {
-    if (threadIdx.x == 0) dout[(int64_t)r * a.K_max + j] = 0.0;
+    if (threadIdx.x == 0) dpart[blockIdx.x] = 0.0;
     return;
   }
-  const bool pen = build_penalty_bitmap<NT>(a, r, j, 0, a.V, bm);
+  const int nvec = (a.V + VEC - 1) / VEC, len = (nvec + S - 1) / S;
+  const int k0 = min(nvec, sl * len), k1 = min(nvec, k0 + len);
+  const bool pen = build_penalty_bitmap<NT>(a, r, j, k0 * VEC, (k1 - k0) * VEC, bm);
   ExactLds L{};
   L.sd = sd;
   L.sf = sf;
   L.si = si;
-  const double d = pair_tv_dev<DT, NT>(a, target_row(a, r, j), draft_row(a, r, j), P, Q, pen, bm, L);
-  if (threadIdx.x == 0) dout[(int64_t)r * a.K_max + j] = d;
+  const double part = pair_tv_range<DT, NT>(a, target_row(a, r, j), draft_row(a, r, j), P, Q, pen, bm,
+                                            k0 * VEC, L, k0, k1);
+  if (threadIdx.x == 0) dpart[blockIdx.x] = part;
 }
 
 // Request-level checks shared by the finalize kernels.  Returns status bits.
@@ -171,9 +312,12 @@ __device__ __forceinline__ uint32_t request_status(const Args& a, int r, int K, 
   return st;
 }
 
-template <int DT>
-__global__ __launch_bounds__(NT_ROW) void k_finalize(Args a, const RowStat* rs, const double* dtv,
-                                                    int tv_valid, int bm_words,
+// Decisions, first rejection and outputs of request r; without SPLIT also
+// the draw, else the draw's choice goes to drec[r] (n, mode; mode 2: no
+// draw) for k_draw_tot / k_draw_pick, which fill in the drawn token.
+template <int DT, bool SPLIT>
+__global__ __launch_bounds__(NT_ROW) void k_finalize(Args a, const RowStat* rs, const double* dpart,
+                                                    int tv_valid, int tvS, int bm_words, int2* drec,
                                                     int32_t* out_acc, int32_t* out_tok,
                                                     uint32_t* out_status, float* out_stats) {
   constexpr int NT = NT_ROW;
@@ -201,6 +345,7 @@ __global__ __launch_bounds__(NT_ROW) void k_finalize(Args a, const RowStat* rs, 
   if (block_or<NT>(nonfin, si)) st |= SD_ST_NONFINITE;
 
   if (st & SD_ST_INVALID_MASK) {
+    if (SPLIT && threadIdx.x == 0) drec[r] = make_int2(0, 2);
     for (int t = threadIdx.x; t < K1; t += NT) out_tok[(int64_t)r * K1 + t] = -1;
     if (out_stats)
       for (int t = threadIdx.x; t < K1 * SD_NSTAT; t += NT) out_stats[(int64_t)r * K1 * SD_NSTAT + t] = 0.0f;
@@ -211,26 +356,41 @@ __global__ __launch_bounds__(NT_ROW) void k_finalize(Args a, const RowStat* rs, 
     return;
   }
 
-  if (threadIdx.x == 0) {
-    int n = K;
-    for (int jj = 0; jj <= K; ++jj) {
-      float u, v;
-      uniforms(a.seed, a.offset, r, jj, u, v);
-      float* sv = &sh_stat[jj * SD_NSTAT];
-      for (int s = 0; s < SD_NSTAT; ++s) sv[s] = 0.0f;
-      sv[SD_STAT_U] = u;
-      sv[SD_STAT_V] = v;
-      if (jj == K) break;
+  // Every position at once (thread jj): its uniforms, statistics and
+  // decision; then thread 0 takes the first rejection.
+  __shared__ unsigned char sh_acc[SD_MAX_K + 1], sh_qz[SD_MAX_K + 1];
+  if ((int)threadIdx.x <= K) {
+    const int jj = threadIdx.x;
+    float u, v;
+    uniforms(a.seed, a.offset, r, jj, u, v);
+    float* sv = &sh_stat[jj * SD_NSTAT];
+    for (int s = 0; s < SD_NSTAT; ++s) sv[s] = 0.0f;
+    sv[SD_STAT_U] = u;
+    sv[SD_STAT_V] = v;
+    if (jj < K) {
       const RowStat P = rs[row_index(a, r, true, jj)], Q = rs[row_index(a, r, false, jj)];
-      const double d = tv_valid ? dtv[(int64_t)r * a.K_max + jj] : 0.0;
+      double d = 0.0;
+      if (tv_valid) {
+        const double* dp = dpart + ((int64_t)r * a.K_max + jj) * tvS;
+        for (int s = 0; s < tvS; ++s) d += dp[s];
+        d = fmin(0.5 * d, 1.0);
+      }
       const Decision dc = decide(P, Q, P.kx, Q.kx, (double)T, (double)request_D(a, r), tv_valid != 0, d, u);
-      if (dc.qx == 0.0) st |= SD_ST_Q_ZERO;
+      sh_qz[jj] = dc.qx == 0.0;
+      sh_acc[jj] = dc.accept;
       sv[SD_STAT_D] = (float)d;
       sv[SD_STAT_THETA] = (float)dc.th;
       sv[SD_STAT_PX] = (float)dc.px;
       sv[SD_STAT_QX] = (float)dc.qx;
       sv[SD_STAT_PIX] = (float)dc.pix;
-      if (n == K && !dc.accept) n = jj;
+    }
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int n = K;
+    for (int jj = 0; jj < K; ++jj) {
+      if (sh_qz[jj]) st |= SD_ST_Q_ZERO;
+      if (n == K && !sh_acc[jj]) n = jj;
     }
     sh_n = n;
     sh_mode = (n < K) ? 0 : ((a.flags & SD_NO_BONUS) ? 2 : 1);
@@ -239,7 +399,9 @@ __global__ __launch_bounds__(NT_ROW) void k_finalize(Args a, const RowStat* rs, 
   __syncthreads();
   const int n = sh_n, mode = sh_mode;
   int y = -1;
-  if (mode != 2) {
+  if (SPLIT) {
+    if (threadIdx.x == 0) drec[r] = make_int2(n, mode);
+  } else if (mode != 2) {
     const bool pen = build_penalty_bitmap<NT>(a, r, n, 0, a.V, bm);
     const RowStat P = rs[row_index(a, r, true, n)];
     const RowStat Q = (n < K) ? rs[row_index(a, r, false, n)] : P;
@@ -271,6 +433,80 @@ __global__ __launch_bounds__(NT_ROW) void k_finalize(Args a, const RowStat* rs, 
   if (threadIdx.x == 0) {
     out_acc[r] = n;
     if (out_status) out_status[r] = sh_st;
+  }
+}
+
+// The draw's chunk totals of request r, slice b % S of its chunks (both
+// modes' totals for a residual draw, whose mode 1 is the fallback when the
+// residual has no mass), to ctot[r][0 .. nch] and ctot[r][nch + 1 ..].
+template <int DT>
+__global__ __launch_bounds__(NT_ROW) void k_draw_tot(Args a, const RowStat* rs, const int2* drec,
+                                                     double* ctot, int S) {
+  constexpr int NT = NT_ROW;
+  extern __shared__ __align__(16) unsigned char smem[];
+  uint32_t* bm = reinterpret_cast<uint32_t*>(smem);
+  const int r = blockIdx.x / S, sl = blockIdx.x % S;
+  const int2 rec = drec[r];
+  const int n = rec.x, mode = rec.y;
+  if (mode == 2) return;
+  const int K = request_k(a, r);
+  const int nch = draw_chunks(a.V), len = (nch + S - 1) / S;
+  const int ch0 = min(nch, sl * len), ch1 = min(nch, ch0 + len);
+  if (ch0 >= ch1) return;
+  const bool pen = build_penalty_bitmap<NT>(a, r, n, ch0 * CHV * VEC, (ch1 - ch0) * CHV * VEC, bm);
+  const RowStat P = rs[row_index(a, r, true, n)];
+  const RowStat Q = (n < K) ? rs[row_index(a, r, false, n)] : P;
+  const char* trow = target_row(a, r, n);
+  const char* drow = (n < K) ? draft_row(a, r, n) : trow;
+  double* c0 = ctot + (int64_t)r * 2 * (nch + 1);
+  draw_totals<DT, NT, true>(a, trow, drow, P, Q, mode, pen, bm, ch0 * CHV * VEC, ch0, ch1, c0, c0 + nch + 1);
+}
+
+// The draw of request r from its chunk totals: the same scan and crossing
+// chunk walk as the one-workgroup draw, so the same token; writes it, S,
+// and the zero-residual bit into the outputs k_finalize<DT, true> wrote.
+template <int DT>
+__global__ __launch_bounds__(NT_ROW) void k_draw_pick(Args a, const RowStat* rs, const int2* drec,
+                                                      double* ctot, int32_t* out_tok, uint32_t* out_status,
+                                                      float* out_stats) {
+  constexpr int NT = NT_ROW;
+  __shared__ uint32_t bm[CHV * VEC / 32];
+  __shared__ double sd[NT];
+  __shared__ int si[NT / WAVE + 4];
+  const int r = blockIdx.x;
+  const int2 rec = drec[r];
+  const int n = rec.x;
+  int mode = rec.y;
+  if (mode == 2) return;
+  const int K = request_k(a, r);
+  const int nch = draw_chunks(a.V);
+  float u, v;
+  uniforms(a.seed, a.offset, r, n, u, v);
+  ExactLds L{};
+  L.sd = sd;
+  L.si = si;
+  double* c0 = ctot + (int64_t)r * 2 * (nch + 1);
+  double S = 0.0, t = 0.0;
+  int cs = draw_scan<NT>(c0, nch, v, L, S, t);
+  int resid_zero = 0;
+  if (!(S > 0.0) && mode == 0) {   // zero residual: draw from p
+    mode = 1;
+    resid_zero = 1;
+    c0 += nch + 1;
+    cs = draw_scan<NT>(c0, nch, v, L, S, t);
+  }
+  bool pen = false;
+  if (cs >= 0) pen = build_penalty_bitmap<NT>(a, r, n, cs * CHV * VEC, CHV * VEC, bm);
+  const RowStat P = rs[row_index(a, r, true, n)];
+  const RowStat Q = (n < K) ? rs[row_index(a, r, false, n)] : P;
+  const char* trow = target_row(a, r, n);
+  const char* drow = (n < K) ? draft_row(a, r, n) : trow;
+  const int y = draw_resolve<DT, NT>(a, trow, drow, P, Q, mode, pen, bm, cs * CHV * VEC, cs, t, c0[nch], L);
+  if (threadIdx.x == 0) {
+    const int K1 = a.K_max + 1;
+    out_tok[(int64_t)r * K1 + n] = y;
+    if (out_stats) out_stats[((int64_t)r * K1 + n) * SD_NSTAT + SD_STAT_S] = (float)S;
+    if (out_status && resid_zero) out_status[r] |= SD_ST_RESID_ZERO;
   }
 }
 
@@ -2491,8 +2727,9 @@ __global__ __launch_bounds__(64) void k_greedy_final(Args a, const GPart* parts,
 // Host side.
 // ---------------------------------------------------------------------------
 struct Layout {
-  size_t rs, dtv, gp, uo, total;
+  size_t rs, dtv, gp, uo, drec, ctot, rpart, total;
   int ns;
+  int tvS, drS, rowS;   // slices of the general path's TV, draw and row passes
 };
 
 Layout layout(const sd_verify_args_t* a) {
@@ -2500,8 +2737,14 @@ Layout layout(const sd_verify_args_t* a) {
   const size_t B = (size_t)a->B, K = (size_t)a->K_max;
   L.ns = (a->V + G_SLICE - 1) / G_SLICE;
   size_t off = 0;
+  L.tvS = tv_slices(a->B, a->K_max, a->V);
+  L.drS = draw_slices(a->B, a->V);
+  L.rowS = row_slices(a->B, a->K_max, a->V, a->top_p_per_row != nullptr || a->top_p < 1.0f);
   L.rs = off;  off = align_up(off + B * (2 * K + 1) * sizeof(RowStat), 256);
-  L.dtv = off; off = align_up(off + B * K * sizeof(double), 256);
+  L.dtv = off; off = align_up(off + B * K * (size_t)L.tvS * sizeof(double), 256);
+  L.drec = off; off = align_up(off + (L.drS > 1 ? B * sizeof(int2) : 0), 256);
+  L.ctot = off; off = align_up(off + (L.drS > 1 ? B * 2 * (size_t)(draw_chunks(a->V) + 1) * sizeof(double) : 0), 256);
+  L.rpart = off; off = align_up(off + (L.rowS > 1 ? B * (2 * K + 1) * L.rowS * sizeof(RowPart) : 0), 256);
   L.gp = off;  off = align_up(off + B * (K + 1) * (size_t)L.ns * sizeof(GPart), 256);
   L.uo = off;  off = align_up(off + B * (K + 1) * sizeof(UnitOut), 256);
   L.total = off;
@@ -2600,6 +2843,14 @@ size_t prepare_lds(const Args& a) {
 template <int DT>
 int run_prepare(const Args& a, const Layout& L, char* ws, hipStream_t st) {
   const int grid = a.B * (2 * a.K_max + 1);
+  if (L.rowS > 1) {
+    RowPart* parts = reinterpret_cast<RowPart*>(ws + L.rpart);
+    hipLaunchKernelGGL(k_row_part<DT>, dim3(grid * L.rowS), dim3(NT_ROW),
+                       a.rep != 1.0f ? align_up((size_t)bitmap_words(a.V) * 4, 16) : 0, st, a, parts, L.rowS);
+    hipLaunchKernelGGL(k_row_combine<DT>, dim3(grid), dim3(WAVE), 0, st, a, parts,
+                       reinterpret_cast<RowStat*>(ws + L.rs), L.rowS);
+    return launch_status();
+  }
   const int bmw = (a.rep != 1.0f || a.tpr || a.top_p < 1.0f) ? bitmap_words(a.V) : 0;
   hipLaunchKernelGGL(k_row_prepare<DT>, dim3(grid), dim3(NT_ROW), prepare_lds(a), st, a,
                      reinterpret_cast<RowStat*>(ws + L.rs), bmw);
@@ -2634,16 +2885,28 @@ int run_phase(const Args& a, const Layout& L, char* ws, int phase, int32_t* acc,
   if (phase == 0) return run_prepare<DT>(a, L, ws, st);
   if (phase == 1) {
     if (!need_tv || a.K_max == 0) return SD_OK;
-    hipLaunchKernelGGL(k_pair_tv<DT>, dim3(a.B * a.K_max), dim3(NT_ROW),
+    hipLaunchKernelGGL(k_pair_tv<DT>, dim3(a.B * a.K_max * L.tvS), dim3(NT_ROW),
                        a.rep != 1.0f ? align_up((size_t)bitmap_words(a.V) * 4, 16) : 0, st, a,
                        reinterpret_cast<const RowStat*>(ws + L.rs),
-                       reinterpret_cast<double*>(ws + L.dtv));
+                       reinterpret_cast<double*>(ws + L.dtv), L.tvS);
     return launch_status();
   }
-  hipLaunchKernelGGL(k_finalize<DT>, dim3(a.B), dim3(NT_ROW), fin_lds(a.V), st, a,
-                     reinterpret_cast<const RowStat*>(ws + L.rs),
-                     reinterpret_cast<const double*>(ws + L.dtv), need_tv ? 1 : 0,
-                     bitmap_words(a.V), acc, tok, status, stats);
+  const RowStat* rs = reinterpret_cast<const RowStat*>(ws + L.rs);
+  const double* dpart = reinterpret_cast<const double*>(ws + L.dtv);
+  if (L.drS <= 1) {
+    hipLaunchKernelGGL((k_finalize<DT, false>), dim3(a.B), dim3(NT_ROW), fin_lds(a.V), st, a, rs, dpart,
+                       need_tv ? 1 : 0, L.tvS, bitmap_words(a.V), nullptr, acc, tok, status, stats);
+    return launch_status();
+  }
+  // small batches: the draw split over workgroups by chunk ranges
+  int2* drec = reinterpret_cast<int2*>(ws + L.drec);
+  double* ctot = reinterpret_cast<double*>(ws + L.ctot);
+  hipLaunchKernelGGL((k_finalize<DT, true>), dim3(a.B), dim3(NT_ROW), 0, st, a, rs, dpart, need_tv ? 1 : 0,
+                     L.tvS, 0, drec, acc, tok, status, stats);
+  hipLaunchKernelGGL(k_draw_tot<DT>, dim3(a.B * L.drS), dim3(NT_ROW),
+                     a.rep != 1.0f ? align_up((size_t)bitmap_words(a.V) * 4, 16) : 0, st, a, rs, drec, ctot,
+                     L.drS);
+  hipLaunchKernelGGL(k_draw_pick<DT>, dim3(a.B), dim3(NT_ROW), 0, st, a, rs, drec, ctot, tok, status, stats);
   return launch_status();
 }
 
@@ -2816,7 +3079,7 @@ const char* sd_debug_phase_kernel(const sd_verify_args_t* args, int phase) {
   }
   if (phase == 0) return "k_row_prepare";
   if (phase == 1) return (needs_tv(a, nullptr) && a.K_max > 0) ? "k_pair_tv" : nullptr;
-  return "k_finalize";
+  return draw_slices(a.B, a.V) > 1 ? "k_finalize + k_draw_tot + k_draw_pick" : "k_finalize";
 }
 
 int sd_debug_fallback_units(const sd_verify_args_t* args, const void* workspace,

@@ -155,30 +155,36 @@ __device__ __forceinline__ void row_pass(const char* row, int V, int nvec, F&& f
       });
 }
 
-// Statistics and top-p cut of one processed row, streaming it from global
-// memory: pass 0 gives the max M and Z = sum exp2((key - M) c) (online per
-// thread, fp64 totals); with top-p, three histogram passes over 12 + 12 + 8
-// bits of the orderable key with fixed-point masses find the cut key.  The
-// row holds V logits (a.V for a target row, a.Vd for a draft row: ids past
-// a draft row have q = 0 and take no part).
+// A row's pointer advanced to vector k0 (the rows of a pass over vectors
+// [k0, ...))
+template <int DT>
+__device__ __forceinline__ const char* row_from(const char* row, int k0) {
+  return row + (size_t)k0 * VEC * (DT == SD_BF16 ? 2 : 4);
+}
+
+// Max and normalizer of vectors [k0, k1) of a processed row of V logits
+// (bm covers ids from bmlo): M the block max, Z = sum exp2((key - M) c)
+// (0 when M is -inf), bad whether a NaN was met while every logit before it
+// was -inf (otherwise a NaN makes Z NaN).  RU vectors per step (the next
+// step's loads in flight), one max update (and fp64 rescale of Z) per step,
+// the step's terms summed in fp32.
 template <int DT, int NT>
-__device__ __forceinline__ RowStat row_stats_dev(const Args& a, const char* row, int V, float c,
-                                 bool pen, const uint32_t* bm, const ExactLds& L, float top_p) {
-  const int nvec = (V + VEC - 1) / VEC;
+__device__ __forceinline__ void row_max_z(const Args& a, const char* row, int V, float c, bool pen,
+                                          const uint32_t* bm, int bmlo, const ExactLds& L, int k0, int k1,
+                                          float& Mout, double& Zout, int& badout) {
   float m = -INFINITY;
   double Z = 0.0;
   int bad = 0;
-  // RU vectors per step (the next step's loads in flight), one max update
-  // (and fp64 rescale of Z) per step, the step's terms summed in fp32
   const int tid = threadIdx.x;
+  const int nv = k1 - k0;
   stream_steps<DT, NT, RU, false>(
-      row, V, row, V, nvec,
+      row_from<DT>(row, k0), max(V - k0 * VEC, 0), row_from<DT>(row, k0), max(V - k0 * VEC, 0), nv,
       [&](int base, int u) __attribute__((always_inline)) { return base + u * NT + tid; },
       [&](int base, float (&z)[RU][VEC], float (&)[RU][VEC]) __attribute__((always_inline)) {
         float vm = -INFINITY;
 #pragma unroll
         for (int u = 0; u < RU; ++u) {
-          if (pen && base + u * NT + tid < nvec) apply_penalty8(bm, base + u * NT + tid, 0, a.rep, z[u]);
+          if (pen && base + u * NT + tid < nv) apply_penalty8(bm, k0 + base + u * NT + tid, bmlo, a.rep, z[u]);
 #pragma unroll
           for (int e = 0; e < VEC; ++e) vm = fmaxf(vm, z[u][e]);
         }
@@ -187,9 +193,9 @@ __device__ __forceinline__ RowStat row_stats_dev(const Args& a, const char* row,
           m = vm;
         }
         // Non-finite logits need no test per element: +inf becomes the max
-        // (caught below), and a NaN turns its term, hence Z, into NaN once the
-        // running max is finite; only a NaN met while every logit so far is
-        // -inf is looked for explicitly.
+        // (caught by the caller), and a NaN turns its term, hence Z, into
+        // NaN once the running max is finite; only a NaN met while every
+        // logit so far is -inf is looked for explicitly.
         if (m > -INFINITY) {
           float su = 0.0f;
 #pragma unroll
@@ -209,8 +215,25 @@ __device__ __forceinline__ RowStat row_stats_dev(const Args& a, const char* row,
       });
   const float M = block_max<NT>(m, L.sf);
   Z = (m > -INFINITY) ? Z * exp2(((double)m - (double)M) * (double)c) : 0.0;
-  const double Zall = block_sum<NT>(Z, L.sd);
-  bad = block_or<NT>(bad, L.si);
+  Zout = block_sum<NT>(Z, L.sd);
+  badout = block_or<NT>(bad, L.si);
+  Mout = M;
+}
+
+// Statistics and top-p cut of one processed row, streaming it from global
+// memory: pass 0 gives the max M and Z = sum exp2((key - M) c) (online per
+// thread, fp64 totals); with top-p, three histogram passes over 12 + 12 + 8
+// bits of the orderable key with fixed-point masses find the cut key.  The
+// row holds V logits (a.V for a target row, a.Vd for a draft row: ids past
+// a draft row have q = 0 and take no part).
+template <int DT, int NT>
+__device__ __forceinline__ RowStat row_stats_dev(const Args& a, const char* row, int V, float c,
+                                 bool pen, const uint32_t* bm, const ExactLds& L, float top_p) {
+  const int nvec = (V + VEC - 1) / VEC;
+  float M;
+  double Zall;
+  int bad;
+  row_max_z<DT, NT>(a, row, V, c, pen, bm, 0, L, 0, nvec, M, Zall, bad);
   if (!(M > -INFINITY) || !(M < INFINITY) || Zall != Zall) bad = 1;
 
   RowStat out;
@@ -310,27 +333,32 @@ __device__ __forceinline__ RowStat row_stats_dev(const Args& a, const char* row,
   return out;
 }
 
-// d = TV(p, q) = 1/2 sum |p - q| over the processed, truncated rows.
+// sum |p - q| over vectors [k0, k1) of the processed, truncated rows (the
+// block's total; bm covers ids from bmlo).  TV(p, q) is half the sum over
+// the whole row.
 template <int DT, int NT>
-__device__ __forceinline__ double pair_tv_dev(const Args& a, const char* trow, const char* drow,
-                              const RowStat& P, const RowStat& Q, bool pen,
-                              const uint32_t* bm, const ExactLds& L) {
-  const int V = a.V, nvec = (V + VEC - 1) / VEC;
+__device__ __forceinline__ double pair_tv_range(const Args& a, const char* trow, const char* drow,
+                                                const RowStat& P, const RowStat& Q, bool pen,
+                                                const uint32_t* bm, int bmlo, const ExactLds& L, int k0,
+                                                int k1) {
+  const int V = a.V;
   const float ip = (float)(1.0 / P.Zk), iq = (float)(1.0 / Q.Zk);
   double acc = 0.0;
   const int tid = threadIdx.x;
+  const int nv = k1 - k0;
   stream_steps<DT, NT, RU2, true>(
-      trow, V, drow, a.Vd, nvec,
+      row_from<DT>(trow, k0), max(V - k0 * VEC, 0), row_from<DT>(drow, k0), max(a.Vd - k0 * VEC, 0), nv,
       [&](int base, int u) __attribute__((always_inline)) { return base + u * NT + tid; },
       [&](int base, float (&zp)[RU2][VEC], float (&zq)[RU2][VEC]) __attribute__((always_inline)) {
         float s = 0.0f;
 #pragma unroll
         for (int u = 0; u < RU2; ++u) {
-          const int k = base + u * NT + tid;
-          if (k >= nvec) continue;
+          const int kr = base + u * NT + tid;
+          if (kr >= nv) continue;
+          const int k = k0 + kr;
           if (pen) {
-            apply_penalty8(bm, k, 0, a.rep, zp[u]);
-            apply_penalty8(bm, k, 0, a.rep, zq[u]);
+            apply_penalty8(bm, k, bmlo, a.rep, zp[u]);
+            apply_penalty8(bm, k, bmlo, a.rep, zq[u]);
           }
           bool kp[VEC], kq[VEC];
           bool any = false;
@@ -352,7 +380,16 @@ __device__ __forceinline__ double pair_tv_dev(const Args& a, const char* trow, c
         }
         acc += (double)s;
       });
-  return fmin(0.5 * block_sum<NT>(acc, L.sd), 1.0);
+  return block_sum<NT>(acc, L.sd);
+}
+
+// d = TV(p, q) = 1/2 sum |p - q| over the processed, truncated rows.
+template <int DT, int NT>
+__device__ __forceinline__ double pair_tv_dev(const Args& a, const char* trow, const char* drow,
+                              const RowStat& P, const RowStat& Q, bool pen,
+                              const uint32_t* bm, const ExactLds& L) {
+  const int nvec = (a.V + VEC - 1) / VEC;
+  return fmin(0.5 * pair_tv_range<DT, NT>(a, trow, drow, P, Q, pen, bm, 0, L, 0, nvec), 1.0);
 }
 
 struct Drawn {
@@ -363,140 +400,167 @@ struct Drawn {
 
 // Inverse-CDF draw over ascending token ids: mode 0 draws from
 // max(p - q, 0) (falling back to p when that has no mass), mode 1 from p.
-// One coalesced pass over the row (mode 0: both rows, side by side) writes
-// the total of every chunk to L.ctot (nch + 1 doubles: the last holds the
-// mass before the crossing chunk).  A chunk is one wave's share of one step,
-// RU2 blocks of 64 consecutive vectors in ascending order (128 consecutive
-// vectors), so a step takes one wave reduction, not one per vector.  A block
-// scan over the chunk totals finds the chunk that holds t = v S; wave 0
+// A chunk is one wave's share of one step of a pass over the rows (mode 0:
+// both rows, side by side): RU2 blocks of 64 consecutive vectors in
+// ascending order, CHV = 128 consecutive vectors, so a step takes one wave
+// reduction, not one per vector.  One pass writes every chunk's total; a
+// block scan over the totals finds the chunk that holds t = v S; wave 0
 // reads that chunk again and scans it block by block, lane by lane; the
 // crossing lane walks its 8 tokens.  A vector's weights are summed in fp32
 // in token order, the same running sum the walk compares, and every sum
-// above that is fp64 in a fixed order.
-template <int DT, int NT>
-__device__ __forceinline__ Drawn draw_dev(const Args& a, const char* trow, const char* drow, const RowStat& P,
-                          const RowStat& Q, int mode, float v, bool pen, const uint32_t* bm,
-                          const ExactLds& L) {
-  constexpr int CHV = RU2 * WAVE;   // vectors per chunk
+// above that is fp64 in a fixed order.  The pass may be split over
+// workgroups by chunk ranges (draw_totals) with the same totals.
+constexpr int CHV = RU2 * WAVE;   // vectors per chunk
+
+// Draw weights of vector k (0 past the row) and their fp32 sum in token
+// order; sp: the sum of p alone (mode 1's weights), in the same order.  bm
+// covers ids from bmlo.
+template <int DT>
+__device__ __forceinline__ float draw_vec_w(const Args& a, const RowStat& P, const RowStat& Q, float ip,
+                                            float iq, int k, int md, bool pen, const uint32_t* bm,
+                                            int bmlo, float (&zp)[VEC], float (&zq)[VEC], float (&w)[VEC],
+                                            float& sp) {
   const int V = a.V, nvec = (V + VEC - 1) / VEC;
-  const int nch = (nvec + CHV - 1) / CHV;
+  float s = 0.0f;
+  sp = 0.0f;
+  if (k >= nvec) {
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) w[e] = 0.0f;
+    return s;
+  }
+  if (pen) apply_penalty8(bm, k, bmlo, a.rep, zp);
+  if (md == 0 && pen) apply_penalty8(bm, k, bmlo, a.rep, zq);
+  bool kp[VEC];
+  bool any = false;
+#pragma unroll
+  for (int e = 0; e < VEC; ++e) {
+    kp[e] = k * VEC + e < V && kept(P, ord_key(zp[e]));
+    any |= kp[e];
+  }
+  // (a weight is zero outside p's nucleus: vectors of the wave with none
+  // of its tokens skip the exponentials)
+  if (!__any(any)) {
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) w[e] = 0.0f;
+    return s;
+  }
+#pragma unroll
+  for (int e = 0; e < VEC; ++e) {
+    const int id = k * VEC + e;
+    float p = kp[e] ? e_rel(zp[e], P.M, P.c) * ip : 0.0f;
+    sp += p;
+    if (md == 0) {
+      const float q = (id < a.Vd && kept(Q, ord_key(zq[e]))) ? e_rel(zq[e], Q.M, Q.c) * iq : 0.0f;
+      p = fmaxf(p - q, 0.0f);
+    }
+    w[e] = p;
+    s += p;
+  }
+  return s;
+}
+
+// Totals of chunks [ch0, ch1) to ctot[ch] (BOTH, with md 0: the totals of
+// mode 1's weights too, to ctot1[ch]).  Every thread takes part.
+template <int DT, int NT, bool BOTH>
+__device__ __forceinline__ void draw_totals(const Args& a, const char* trow, const char* drow,
+                                            const RowStat& P, const RowStat& Q, int md, bool pen,
+                                            const uint32_t* bm, int bmlo, int ch0, int ch1, double* ctot,
+                                            double* ctot1) {
+  const int V = a.V, nvec = (V + VEC - 1) / VEC;
   const int lane = threadIdx.x % WAVE, wv = threadIdx.x / WAVE;
   const float ip = (float)(1.0 / P.Zk), iq = (float)(1.0 / Q.Zk);
-  Drawn out;
-  out.resid_zero = 0;
+  const int k0 = ch0 * CHV;
+  const int nv = min(nvec, ch1 * CHV) - k0;
+  stream_steps<DT, NT, RU2, true>(
+      row_from<DT>(trow, k0), max(V - k0 * VEC, 0), row_from<DT>(drow, k0),
+      md == 0 ? max(a.Vd - k0 * VEC, 0) : 0, nv,
+      [&](int base, int u) __attribute__((always_inline)) { return base + wv * CHV + u * WAVE + lane; },
+      [&](int base, float (&zp)[RU2][VEC], float (&zq)[RU2][VEC]) __attribute__((always_inline)) {
+        const int kr0 = base + wv * CHV;   // this wave's chunk
+        double ls = 0.0, ls1 = 0.0;
+#pragma unroll
+        for (int u = 0; u < RU2; ++u) {
+          float w[VEC];
+          float sp;
+          ls += (double)draw_vec_w<DT>(a, P, Q, ip, iq, k0 + kr0 + u * WAVE + lane, md, pen, bm, bmlo, zp[u],
+                                       zq[u], w, sp);
+          if (BOTH) ls1 += (double)sp;
+        }
+        const double cs = wave_sum(ls);
+        const int ch = ch0 + kr0 / CHV;
+        if (lane == 0 && ch < ch1) ctot[ch] = cs;
+        if (BOTH) {
+          const double cs1 = wave_sum(ls1);
+          if (lane == 0 && ch < ch1) ctot1[ch] = cs1;
+        }
+      });
+}
 
-  // draw weights of vector k (0 past the row) and their fp32 sum in token order
-  auto vec_w = [&](int k, int md, float (&zp)[VEC], float (&zq)[VEC], float (&w)[VEC])
-                   __attribute__((always_inline)) -> float {
-    float s = 0.0f;
-    if (k >= nvec) {
-#pragma unroll
-      for (int e = 0; e < VEC; ++e) w[e] = 0.0f;
-      return s;
+// Block scan over the nch chunk totals: S, t = v S, and the crossing
+// chunk (returned; -1 when S is not positive), the mass before it in
+// ctot[nch].  Every thread takes part.
+template <int NT>
+__device__ __forceinline__ int draw_scan(double* ctot, int nch, float v, const ExactLds& L, double& S,
+                                         double& t) {
+  // (thread t owns chunks t per ..)
+  const int per = (nch + NT - 1) / NT;
+  const int c0 = min((int)threadIdx.x * per, nch), c1 = min(c0 + per, nch);
+  double own = 0.0;
+  for (int ch = c0; ch < c1; ++ch) own += ctot[ch];
+  const double incl = block_incl_scan_fast<NT>(own, L.sd);
+  __syncthreads();   // the scan's reads of its wave totals are done
+  L.sd[threadIdx.x] = incl;
+  if (threadIdx.x == 0) { L.si[0] = -1; L.si[1] = -1; }
+  __syncthreads();
+  // the previous thread's inclusive total is this thread's exclusive one,
+  // exactly: the crossing thread below is unique and exists when S > 0
+  const double excl = threadIdx.x ? L.sd[threadIdx.x - 1] : 0.0;
+  S = L.sd[NT - 1];
+  t = (double)v * S;
+  if (S > 0.0 && incl > t && excl <= t) {
+    double R = excl;
+    int cs = c1 - 1;
+    for (int ch = c0; ch < c1; ++ch) {
+      if (R + ctot[ch] > t) { cs = ch; break; }
+      R += ctot[ch];
     }
-    if (pen) apply_penalty8(bm, k, 0, a.rep, zp);
-    if (md == 0 && pen) apply_penalty8(bm, k, 0, a.rep, zq);
-    bool kp[VEC];
-    bool any = false;
-#pragma unroll
-    for (int e = 0; e < VEC; ++e) {
-      kp[e] = k * VEC + e < V && kept(P, ord_key(zp[e]));
-      any |= kp[e];
-    }
-    // (a weight is zero outside p's nucleus: vectors of the wave with none
-    // of its tokens skip the exponentials)
-    if (!__any(any)) {
-#pragma unroll
-      for (int e = 0; e < VEC; ++e) w[e] = 0.0f;
-      return s;
-    }
-#pragma unroll
-    for (int e = 0; e < VEC; ++e) {
-      const int id = k * VEC + e;
-      float p = kp[e] ? e_rel(zp[e], P.M, P.c) * ip : 0.0f;
-      if (md == 0) {
-        const float q = (id < a.Vd && kept(Q, ord_key(zq[e]))) ? e_rel(zq[e], Q.M, Q.c) * iq : 0.0f;
-        p = fmaxf(p - q, 0.0f);
-      }
-      w[e] = p;
-      s += p;
-    }
-    return s;
-  };
-  auto load2 = [&](int k, int md, float (&zp)[VEC], float (&zq)[VEC]) __attribute__((always_inline)) {
-    load8_row<DT>(trow, k, k < nvec ? V : 0, zp);
-    if (md == 0) load8_row<DT>(drow, k, k < nvec ? a.Vd : 0, zq);
-  };
-
-  double S = 0.0, t = 0.0;
-  for (int pass = 0; pass < 2; ++pass) {
-    // chunk totals: every wave runs every step (the wave sums need all lanes)
-    const int md = mode;
-    stream_steps<DT, NT, RU2, true>(
-        trow, V, drow, md == 0 ? a.Vd : 0, nvec,
-        [&](int base, int u) __attribute__((always_inline)) { return base + wv * CHV + u * WAVE + lane; },
-        [&](int base, float (&zp)[RU2][VEC], float (&zq)[RU2][VEC]) __attribute__((always_inline)) {
-          const int k0 = base + wv * CHV;   // this wave's chunk
-          double ls = 0.0;
-#pragma unroll
-          for (int u = 0; u < RU2; ++u) {
-            float w[VEC];
-            ls += (double)vec_w(k0 + u * WAVE + lane, md, zp[u], zq[u], w);
-          }
-          const double cs = wave_sum(ls);
-          const int ch = k0 / CHV;
-          if (lane == 0 && ch < nch) L.ctot[ch] = cs;
-        });
-    __syncthreads();
-    // block scan over the chunk totals (thread t owns chunks t per ..)
-    const int per = (nch + NT - 1) / NT;
-    const int c0 = min((int)threadIdx.x * per, nch), c1 = min(c0 + per, nch);
-    double own = 0.0;
-    for (int ch = c0; ch < c1; ++ch) own += L.ctot[ch];
-    const double incl = block_incl_scan_fast<NT>(own, L.sd);
-    __syncthreads();   // the scan's reads of its wave totals are done
-    L.sd[threadIdx.x] = incl;
-    if (threadIdx.x == 0) { L.si[0] = -1; L.si[1] = -1; }
-    __syncthreads();
-    // the previous thread's inclusive total is this thread's exclusive one,
-    // exactly: the crossing thread below is unique and exists when S > 0
-    const double excl = threadIdx.x ? L.sd[threadIdx.x - 1] : 0.0;
-    S = L.sd[NT - 1];
-    t = (double)v * S;
-    if (!(S > 0.0) && mode == 0) {   // zero residual: draw from p
-      __syncthreads();
-      mode = 1;
-      out.resid_zero = 1;
-      continue;
-    }
-    // the crossing chunk and the mass before it (one thread)
-    if (S > 0.0 && incl > t && excl <= t) {
-      double R = excl;
-      int cs = c1 - 1;
-      for (int ch = c0; ch < c1; ++ch) {
-        if (R + L.ctot[ch] > t) { cs = ch; break; }
-        R += L.ctot[ch];
-      }
-      L.si[0] = cs;
-      L.ctot[nch] = R;
-    }
-    __syncthreads();
-    break;
+    L.si[0] = cs;
+    ctot[nch] = R;
   }
-  out.S = S;
+  __syncthreads();
   const int cs = L.si[0];
+  __syncthreads();
+  return cs;
+}
+
+// The token of crossing chunk cs (t and the mass before the chunk, R): wave
+// 0 reads the chunk again and walks it; returned to every thread.  bm
+// covers the chunk's ids, from bmlo.
+template <int DT, int NT>
+__device__ __forceinline__ int draw_resolve(const Args& a, const char* trow, const char* drow,
+                                            const RowStat& P, const RowStat& Q, int mode, bool pen,
+                                            const uint32_t* bm, int bmlo, int cs, double t, double R0,
+                                            const ExactLds& L) {
+  const int V = a.V, nvec = (V + VEC - 1) / VEC;
+  const int lane = threadIdx.x % WAVE, wv = threadIdx.x / WAVE;
+  const float ip = (float)(1.0 / P.Zk), iq = (float)(1.0 / Q.Zk);
   if (wv == 0 && cs >= 0) {
     // the crossing chunk's RU2 blocks of 64 vectors, in ascending order
     float zp[RU2][VEC], zq[RU2][VEC];
 #pragma unroll
-    for (int u = 0; u < RU2; ++u) load2(cs * CHV + u * WAVE + lane, mode, zp[u], zq[u]);
-    double R = L.ctot[nch];
+    for (int u = 0; u < RU2; ++u) {
+      const int k = cs * CHV + u * WAVE + lane;
+      load8_row<DT>(trow, k, k < nvec ? V : 0, zp[u]);
+      if (mode == 0) load8_row<DT>(drow, k, k < nvec ? a.Vd : 0, zq[u]);
+    }
+    double R = R0;
     int found = 0, y = -1, lastpos = -1;
 #pragma unroll
     for (int u = 0; u < RU2; ++u) {
       const int k = cs * CHV + u * WAVE + lane;
       float w[VEC];
-      const double ls = (double)vec_w(k, mode, zp[u], zq[u], w);
+      float sp;
+      const double ls = (double)draw_vec_w<DT>(a, P, Q, ip, iq, k, mode, pen, bm, bmlo, zp[u], zq[u], w, sp);
       const double li = wave_incl_scan(ls);
       // the last token with weight so far (rounding fallback)
       const uint64_t pos = __ballot(ls > 0.0);
@@ -533,8 +597,35 @@ __device__ __forceinline__ Drawn draw_dev(const Args& a, const char* trow, const
     if (lane == 0) L.si[1] = (found && y >= 0) ? y : lastpos;
   }
   __syncthreads();
-  out.y = L.si[1];
+  const int y = L.si[1];
   __syncthreads();
+  return y;
+}
+
+// The whole draw in one workgroup (L.ctot holds nch + 1 doubles).
+template <int DT, int NT>
+__device__ __forceinline__ Drawn draw_dev(const Args& a, const char* trow, const char* drow, const RowStat& P,
+                          const RowStat& Q, int mode, float v, bool pen, const uint32_t* bm,
+                          const ExactLds& L) {
+  const int nvec = (a.V + VEC - 1) / VEC;
+  const int nch = (nvec + CHV - 1) / CHV;
+  Drawn out;
+  out.resid_zero = 0;
+  double S = 0.0, t = 0.0;
+  int cs = -1;
+  for (int pass = 0; pass < 2; ++pass) {
+    draw_totals<DT, NT, false>(a, trow, drow, P, Q, mode, pen, bm, 0, 0, nch, L.ctot, nullptr);
+    __syncthreads();
+    cs = draw_scan<NT>(L.ctot, nch, v, L, S, t);
+    if (!(S > 0.0) && mode == 0) {   // zero residual: draw from p
+      mode = 1;
+      out.resid_zero = 1;
+      continue;
+    }
+    break;
+  }
+  out.S = S;
+  out.y = draw_resolve<DT, NT>(a, trow, drow, P, Q, mode, pen, bm, 0, cs, t, L.ctot[nch], L);
   return out;
 }
 

@@ -554,3 +554,55 @@ def test_single_pass_crossing_above_window():
     c, f = compare_sample(gpu_sample(w), oracle_sample(w), w)
     print(f"crossing above the window: checked {c} rows, near-tie {f}")
     assert c >= 6
+
+
+def test_general_path_split_draw_matches_one_workgroup():
+    """Small batches split the general path's draw over workgroups by chunk
+    ranges (and its TV pass by vector ranges); the draw takes the same chunk
+    totals, scan and walk as the one-workgroup draw of a large batch, so
+    each request's emitted tokens must be identical whether it runs in a
+    batch of 512 (one workgroup per request) or of 8 (split)."""
+    import torch
+    sdv = _sdv()
+    B, K, V, dev = 512, 2, 40000, "cuda"
+    g = torch.Generator(device=dev).manual_seed(123)
+    tgt = torch.randn((B, K + 1, V), generator=g, device=dev) * 3.0
+    drf = 0.8 * tgt[:, :K] + 1.8 * torch.randn((B, K, V), generator=g, device=dev)
+    u = torch.rand((B, K, V), generator=g, device=dev).clamp_(1e-20, 1.0)
+    ids = torch.argmax(drf / 0.8 - torch.log(-torch.log(u)), dim=-1).to(torch.int32)
+    ids[::5, 0] = torch.randint(0, V, (ids[::5, 0].numel(),), generator=g, device=dev, dtype=torch.int32)
+    prior = torch.randint(0, V, (B * 16,), generator=g, device=dev, dtype=torch.int32)
+    offs = torch.arange(0, B * 16 + 1, 16, dtype=torch.int32, device=dev)
+    temp = torch.full((B,), 0.8, device=dev)
+    for top_p in (0.9, 1.0):
+        full = sdv.verify_sample(tgt, drf, ids, None, temp, top_p, 1.1, prior, offs, 0.0, 77, 0)
+        args = sdv.make_args(tgt[:8], drf[:8], ids[:8], None, temp[:8], top_p, 1.1, prior[:8 * 16 + 0],
+                             offs[:9], 0.0, 77, 0)
+        assert "k_draw_pick" in sdv.phase_kernel(args, 2)
+        part = sdv.verify_sample(tgt[:8], drf[:8], ids[:8], None, temp[:8], top_p, 1.1, prior[:8 * 16],
+                                 offs[:9], 0.0, 77, 0)
+        torch.cuda.synchronize()
+        for x, y, name in zip(full[:3], part[:3], ("accepted", "tokens", "status")):
+            np.testing.assert_array_equal(x[:8].cpu().numpy(), y.cpu().numpy(), err_msg=f"top_p={top_p} {name}")
+        rejected = int((part[0].cpu().numpy() < K).sum())
+        print(f"split draw, top_p={top_p}: 8 requests identical ({rejected} corrections, "
+              f"{8 - rejected} bonus draws)")
+
+
+def test_general_path_zero_residual():
+    """A draft row equal to its target row and a proposal outside both
+    nuclei: the proposal is rejected and the residual max(p - q, 0) has no
+    mass, so the correction is drawn from p (status bit RESID_ZERO), on the
+    general path split over workgroups."""
+    w = wl.random_case(1400, B=3, K_max=2, V=20011, dtype="f32", sigma=3.0, corr=0.9,
+                       T_range=(0.7, 0.9), top_p=0.9, D=0.0, odd_share=0.0)
+    w.draft[:] = w.target[:, :w.K_max]
+    from oracle import verify as ov
+    tf = w.target_f32()
+    for r in range(w.B):
+        p = ov.process_dist(tf[r, 0], [], w.rep_penalty, float(w.temperature[r]), w.top_p).p
+        w.draft_ids[r, 0] = int(np.flatnonzero(p == 0)[r])
+    g, o = gpu_sample(w), oracle_sample(w)
+    c, f = compare_sample(g, o, w)
+    assert c == w.B and (o.status & (1 << 6)).all() and (g["status"] & (1 << 6)).all()
+    print(f"zero residual: {c} requests checked, RESID_ZERO on all")
