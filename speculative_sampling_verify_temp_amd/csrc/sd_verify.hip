@@ -1635,6 +1635,74 @@ __device__ __forceinline__ ReqWords request_words(const int32_t* po, const int32
 // UO_FALLBACK and the reasons why.
 // cpk / cqk: the single pass's settled cuts of the target / draft row (null:
 // recompute), which a unit handed over for a slot overflow carries.
+// TV of a bf16 pair from per-key tables (the exact route).  Every logit of
+// the pair is a bf16 value, and p (or q) depends on the value alone unless
+// the token is penalized, so p is tabulated for the TBL keys from the row
+// max down (p_tbl[i] for the key of 16-bit order t1 - i, t1 the order of
+// the row max), when the row's cut lies inside that range (every key below
+// it is then cut, p = 0).  A penalized token's p is computed directly.
+// The table entries are the direct values, so the sum is the direct pass's.
+constexpr int TBL = 4096;
+
+__device__ __forceinline__ bool tbl_fits(const RowStat& s) {
+  return s.kord != KEEP_ALL && (int)(s.kord >> 16) > (int)ord16f(s.M) - (TBL - 2);
+}
+
+template <int NT>
+__device__ __forceinline__ void build_tbl(const RowStat& s, float* tbl) {
+  const uint32_t t1 = ord16f(s.M);
+  const float is = (float)(1.0 / s.Zk);
+  for (int i = threadIdx.x; i < TBL; i += NT) {
+    const int o = (int)t1 - i;
+    float v = 0.0f;
+    if (o >= 0x0080 && i < TBL - 1) {   // (orders below -inf's hold no logit; the last entry stays 0)
+      const float k = key_of_ord16((uint32_t)o);
+      v = kept(s, ord_key(k)) ? e_rel(k, s.M, s.c) * is : 0.0f;
+    }
+    tbl[i] = v;
+  }
+}
+
+template <int NT>
+__device__ __forceinline__ double pair_tv_tbl(const Args& a, const char* trow, const char* drow,
+                                              const RowStat& P, const RowStat& Q, bool pen,
+                                              const uint32_t* bm, const ExactLds& L, const float* tp,
+                                              const float* tq) {
+  const int V = a.V, nvec = (V + VEC - 1) / VEC;
+  const float ip = (float)(1.0 / P.Zk), iq = (float)(1.0 / Q.Zk);
+  const int t1p = (int)ord16f(P.M), t1q = (int)ord16f(Q.M);
+  double acc = 0.0;
+  const int tid = threadIdx.x;
+  stream_steps<SD_BF16, NT, RU2, true>(
+      trow, V, drow, a.Vd, nvec,
+      [&](int base, int u) __attribute__((always_inline)) { return base + u * NT + tid; },
+      [&](int base, float (&zp)[RU2][VEC], float (&zq)[RU2][VEC]) __attribute__((always_inline)) {
+        float s = 0.0f;
+#pragma unroll
+        for (int u = 0; u < RU2; ++u) {
+          const int k = base + u * NT + tid;
+          if (k >= nvec) continue;
+          const uint32_t bits = pen ? (bm[(k * VEC) >> 5] >> ((k * VEC) & 31)) & 0xFFu : 0u;
+#pragma unroll
+          for (int e = 0; e < VEC; ++e) {
+            const int id = k * VEC + e;
+            float p, q;
+            if (bits & (1u << e)) {   // penalized: direct
+              const float kp = penalize(zp[u][e], a.rep), kq = penalize(zq[u][e], a.rep);
+              p = id < V && kept(P, ord_key(kp)) ? e_rel(kp, P.M, P.c) * ip : 0.0f;
+              q = id < a.Vd && kept(Q, ord_key(kq)) ? e_rel(kq, Q.M, Q.c) * iq : 0.0f;
+            } else {
+              p = tp[min(max(t1p - (int)ord16f(zp[u][e]), 0), TBL - 1)];
+              q = tq[min(max(t1q - (int)ord16f(zq[u][e]), 0), TBL - 1)];
+            }
+            s += fabsf(p - q);
+          }
+        }
+        acc += (double)s;
+      });
+  return fmin(0.5 * block_sum<NT>(acc, L.sd), 1.0);
+}
+
 template <int NT>
 __device__ __forceinline__ void exact_unit(const Args& a, UnitOut* uo, int u, const uint32_t* bm,
                                         const ExactLds& ex, uint32_t why, const CutRes* cpk,
@@ -1724,7 +1792,17 @@ __device__ __forceinline__ void exact_unit(const Args& a, UnitOut* uo, int u, co
     }
     return;
   }
-  const double d = pair_tv_dev<SD_BF16, NT>(a, trow, drow, P, Q, pen, bm, ex);
+  double d;
+  if (tbl_fits(P) && tbl_fits(Q)) {
+    // (the tables take the radix passes' histogram space, free by now)
+    float* tp = reinterpret_cast<float*>(ex.hmass);
+    build_tbl<NT>(P, tp);
+    build_tbl<NT>(Q, tp + TBL);
+    __syncthreads();
+    d = pair_tv_tbl<NT>(a, trow, drow, P, Q, pen, bm, ex, tp, tp + TBL);
+  } else {
+    d = pair_tv_dev<SD_BF16, NT>(a, trow, drow, P, Q, pen, bm, ex);
+  }
   if (tid == 0) {
     const int x = a.ids[(int64_t)r * a.K_max + j];
     float kxp = -INFINITY, kxq = -INFINITY;
