@@ -500,15 +500,18 @@ def test_single_pass_fallback_routes():
     assert tot[0] >= 4
 
 
-def test_single_pass_wide_target_cut():
+@pytest.mark.parametrize("rep", [1.1, 0.8])
+def test_single_pass_wide_target_cut(rep):
     """Temperatures in [1, 1.5] over V = 152064 (the batched workload's rows
     otherwise): the target's top-p crossing often lies below the single
-    pass's 254-key window.  Such a unit takes the exact route, whose target
-    cut then comes from the row's key histogram (exact for 4096 keys below
-    the window's top) instead of the row's own passes; the outputs and
-    per-position statistics must match the oracle's."""
+    pass's 254-key window.  Such a unit takes the exact route, whose cuts
+    then come from the rows' key histograms (exact for 4096 keys below each
+    window's top) instead of the rows' own passes; the outputs and
+    per-position statistics must match the oracle's.  A penalty below 1
+    raises the penalized keys (some above the window)."""
     sdv = _sdv()
-    w = wl.config4(seed=9, B=24, K=8, T_range=(1.0, 1.5), odd_share=0.3)
+    w = wl.config4(seed=9 if rep > 1 else 10, B=24, K=8, T_range=(1.0, 1.5), odd_share=0.3,
+                   rep_penalty=rep)
     d = to_device(w)
     args = sdv.make_args(d["target"], d["draft"], d["draft_ids"], d["k_per_row"],
                          d["temperature"], w.top_p, w.rep_penalty, d["prior_ids"],
@@ -606,3 +609,31 @@ def test_general_path_zero_residual():
     c, f = compare_sample(g, o, w)
     assert c == w.B and (o.status & (1 << 6)).all() and (g["status"] & (1 << 6)).all()
     print(f"zero residual: {c} requests checked, RESID_ZERO on all")
+
+
+def test_single_pass_cut_beyond_histogram():
+    """Temperatures in [2, 3]: the nucleus reaches deep into the negative
+    logits, below the 4096 exact keys under each window's top, so the cuts
+    from the key histograms do not settle and the exact route runs the
+    rows' own radix-select passes; outputs must still match the oracle.
+    (Such flat rows put many tokens within 1e-6 of the top-p threshold, so
+    near-tie rows are common; the checked rows are compared bit for bit.)"""
+    import torch
+    sdv = _sdv()
+    w = wl.config4(seed=12, B=24, K=4, T_range=(2.0, 3.0), odd_share=0.3)
+    d = to_device(w)
+    args = sdv.make_args(d["target"], d["draft"], d["draft_ids"], d["k_per_row"],
+                         d["temperature"], w.top_p, w.rep_penalty, d["prior_ids"],
+                         d["prior_offsets"], w.tv_budget, w.seed, w.offset, w.flags)
+    assert sdv.phase_kernel(args, 0) == "k_pair_fast"
+    ws = sdv.alloc_workspace(args, "cuda")
+    acc = torch.empty(w.B, dtype=torch.int32, device="cuda")
+    tok = torch.empty((w.B, w.K_max + 1), dtype=torch.int32, device="cuda")
+    sdv.run_phase(args, ws, 0, acc, tok)
+    n, why = sdv.fallback_units(args, ws, why=True)
+    deep = int((((why & 2) != 0) & ((why & 32) == 0)).sum())
+    g = gpu_sample(w, dev=d)
+    c, f = compare_sample(g, oracle_sample(w), w)
+    print(f"cuts beyond the histogram: {n} of {len(why)} units flagged, {deep} target cuts left to "
+          f"the radix passes; checked {c} rows, near-tie {f}")
+    assert deep >= 5 and c >= 8
