@@ -48,6 +48,16 @@ constexpr int BK = 64;            // K chunk
 constexpr int LDK = BK + 8;       // LDS row stride of the A/B chunks (bf16): 144 B
 constexpr int NT_L = 256;         // threads of a tile workgroup (4 waves)
 constexpr int LDC = TN;           // LDS row stride of a stashed fp32 tile
+
+// Word of element (m, n) of a stashed fp32 tile.  Within each 32-column
+// group of a row the column is XORed with (m mod 8, group) so that the
+// epilogues' pattern (thread 4 row + q takes columns 32 q + e of its row,
+// at the same e across the wave) touches 32 different banks per half-wave,
+// and the stash's (32 consecutive columns of one row per half-wave) stays
+// a permutation of one group.
+__device__ __forceinline__ int cidx(int m, int n) {
+  return m * LDC + (n ^ (((m & 7) << 2) | ((n >> 5) & 3)));
+}
 // LDS words of the A/B chunks or, after the product, the stashed fp32 tile
 constexpr int TILE_LDS_WORDS = (TM + TN) * LDK / 2 > TM * LDC ? (TM + TN) * LDK / 2 : TM * LDC;
 // The row-statistics and greedy passes take taller tiles, MBS 64-row parts
@@ -310,7 +320,7 @@ __device__ __forceinline__ void stash_part(const f32x16 (&acc)[MB][2], float* C,
       for (int v = 0; v < 16; ++v) {
         const int m = row0 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
         const int n = 64 * wc + 32 * b + (lane & 31);
-        C[m * LDC + n] = acc[mb][b][v];
+        C[cidx(m, n)] = acc[mb][b][v];
       }
   }
 }
@@ -325,7 +335,7 @@ __device__ __forceinline__ void stash(const f32x16 (&acc)[2], float* C) {
     for (int v = 0; v < 16; ++v) {
       const int m = 32 * wr + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
       const int n = 64 * wc + 32 * b + (lane & 31);
-      C[m * LDC + n] = acc[b][v];
+      C[cidx(m, n)] = acc[b][v];
     }
 }
 
@@ -399,13 +409,13 @@ __global__ __launch_bounds__(NT_L, 2) void k_lm_stats(LmArgs a, LmWs w, int nm, 
     for (int e = 0; e < 32; ++e) {
       const int n = q4 * 32 + e;
       if (n < nv) {
-        const float z = C[row * LDC + n];
+        const float z = C[cidx(row, n)];
         bad |= nonfinite(z);
         m = fmaxf(m, z * c);
       }
       if (live && n0 + n == x && n < nv) {
         RowSL* rs = (TGT ? w.trs : w.drs) + li;
-        rs->zx = C[row * LDC + n];
+        rs->zx = C[cidx(row, n)];
       }
     }
     m = fmaxf(m, __shfl_xor(m, 1));
@@ -414,7 +424,7 @@ __global__ __launch_bounds__(NT_L, 2) void k_lm_stats(LmArgs a, LmWs w, int nm, 
     if (m > -INFINITY)
       for (int e = 0; e < 32; ++e) {
         const int n = q4 * 32 + e;
-        if (n < nv) s += fast_exp2(C[row * LDC + n] * c - m);
+        if (n < nv) s += fast_exp2(C[cidx(row, n)] * c - m);
       }
     s += __shfl_xor(s, 1);
     s += __shfl_xor(s, 2);
@@ -535,8 +545,8 @@ __global__ __launch_bounds__(NT_L) void k_lm_tv(LmArgs a, LmWs w, int nm, int nn
     for (int e = 0; e < 32; ++e) {
       const int n = q4 * 32 + e;
       if (n >= nv) continue;
-      const float pp = fast_exp2(Ct[row * LDC + n] * P.c - P.M) * ip;
-      const float qq = (n0 + n < a.Vd) ? fast_exp2(U[row * LDC + n] * Q.c - Q.M) * iq : 0.0f;
+      const float pp = fast_exp2(Ct[cidx(row, n)] * P.c - P.M) * ip;
+      const float qq = (n0 + n < a.Vd) ? fast_exp2(U[cidx(row, n)] * Q.c - Q.M) * iq : 0.0f;
       sum += fabsf(pp - qq);
     }
   }
@@ -702,7 +712,7 @@ __global__ __launch_bounds__(NT_L) void k_lm_draw_tiles(LmArgs a, LmWs w, int nm
       const int n = q4 * 32 + e;
       if (n >= nv) continue;
       float wres, wp;
-      draw_w(Ct[row * LDC + n], U[row * LDC + n], dr.x == 0 && n0 + n < a.Vd, P, Q, ip, iq, wres, wp);
+      draw_w(Ct[cidx(row, n)], U[cidx(row, n)], dr.x == 0 && n0 + n < a.Vd, P, Q, ip, iq, wres, wp);
       sres += e_fixed(wres, SHL);
       sp += e_fixed(wp, SHL);
     }
@@ -814,7 +824,7 @@ __global__ __launch_bounds__(NT_L) void k_lm_draw_pick(LmArgs a, LmWs w, int nn,
   const int n = threadIdx.x;   // token n0 + n (threads >= TN hold nothing)
   if (n < nv) {
     float wres, wp;
-    draw_w(Ct[n], U[n], dr.x == 0 && n0 + n < a.Vd, P, Q, ip, iq, wres, wp);
+    draw_w(Ct[cidx(0, n)], U[cidx(0, n)], dr.x == 0 && n0 + n < a.Vd, P, Q, ip, iq, wres, wp);
     wf = e_fixed(mode == 0 ? wres : wp, SHL);
   }
   su[threadIdx.x] = wf;
@@ -872,7 +882,7 @@ __global__ __launch_bounds__(NT_L, 2) void k_lm_greedy_part(LmArgs a, LmWs w, in
     for (int e = 0; e < 32; ++e) {
       const int n = q4 * 32 + e;
       if (n >= nv) continue;
-      const float z = C[row * LDC + n];
+      const float z = C[cidx(row, n)];
       if (z != z) { nan = 1; continue; }
       const uint32_t o = ord_key(z);
       if (o > bo || (o == bo && n0 + n < bi)) { bo = o; bi = n0 + n; }
@@ -964,7 +974,7 @@ __global__ __launch_bounds__(NT_L) void k_lm_dump(LmArgs a, LmWs w, int nm, int 
   __syncthreads();
   for (int i = threadIdx.x; i < TM * TN; i += NT_L) {
     const int row = i / TN, n = i % TN;
-    if (m0 + row < nrows && n0 + n < Vs) out[(int64_t)list[m0 + row] * Vs + n0 + n] = C[row * LDC + n];
+    if (m0 + row < nrows && n0 + n < Vs) out[(int64_t)list[m0 + row] * Vs + n0 + n] = C[cidx(row, n)];
   }
 }
 
