@@ -412,8 +412,11 @@ __global__ __launch_bounds__(NT_ROW) void k_finalize(Args a, const RowStat* rs, 
     L.sf = sf;
     L.si = si;
     L.ctot = ctot;
-    const Drawn dw = draw_dev<DT, NT>(a, trow, drow, P, Q, mode, sh_stat[n * SD_NSTAT + SD_STAT_V],
-                                      pen, bm, L);
+    // (rows without top-p compare no key with a cut)
+    const float v = sh_stat[n * SD_NSTAT + SD_STAT_V];
+    const Drawn dw = P.kord == KEEP_ALL && Q.kord == KEEP_ALL
+                         ? draw_dev<DT, NT, true>(a, trow, drow, P, Q, mode, v, pen, bm, L)
+                         : draw_dev<DT, NT>(a, trow, drow, P, Q, mode, v, pen, bm, L);
     y = dw.y;
     if (threadIdx.x == 0) {
       sh_stat[n * SD_NSTAT + SD_STAT_S] = (float)dw.S;
@@ -459,7 +462,11 @@ __global__ __launch_bounds__(NT_ROW) void k_draw_tot(Args a, const RowStat* rs, 
   const char* trow = target_row(a, r, n);
   const char* drow = (n < K) ? draft_row(a, r, n) : trow;
   double* c0 = ctot + (int64_t)r * 2 * (nch + 1);
-  draw_totals<DT, NT, true>(a, trow, drow, P, Q, mode, pen, bm, ch0 * CHV * VEC, ch0, ch1, c0, c0 + nch + 1);
+  if (P.kord == KEEP_ALL && Q.kord == KEEP_ALL)   // (rows without top-p compare no key with a cut)
+    draw_totals<DT, NT, true, true>(a, trow, drow, P, Q, mode, pen, bm, ch0 * CHV * VEC, ch0, ch1, c0,
+                                    c0 + nch + 1);
+  else
+    draw_totals<DT, NT, true>(a, trow, drow, P, Q, mode, pen, bm, ch0 * CHV * VEC, ch0, ch1, c0, c0 + nch + 1);
 }
 
 // The draw of request r from its chunk totals: the same scan and crossing

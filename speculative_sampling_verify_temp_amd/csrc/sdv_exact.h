@@ -414,8 +414,9 @@ constexpr int CHV = RU2 * WAVE;   // vectors per chunk
 
 // Draw weights of vector k (0 past the row) and their fp32 sum in token
 // order; sp: the sum of p alone (mode 1's weights), in the same order.  bm
-// covers ids from bmlo.
-template <int DT>
+// covers ids from bmlo.  ALLK: neither row is truncated (top-p off), so no
+// key is compared with a cut.
+template <int DT, bool ALLK = false>
 __device__ __forceinline__ float draw_vec_w(const Args& a, const RowStat& P, const RowStat& Q, float ip,
                                             float iq, int k, int md, bool pen, const uint32_t* bm,
                                             int bmlo, float (&zp)[VEC], float (&zq)[VEC], float (&w)[VEC],
@@ -434,7 +435,7 @@ __device__ __forceinline__ float draw_vec_w(const Args& a, const RowStat& P, con
   bool any = false;
 #pragma unroll
   for (int e = 0; e < VEC; ++e) {
-    kp[e] = k * VEC + e < V && kept(P, ord_key(zp[e]));
+    kp[e] = k * VEC + e < V && (ALLK || kept(P, ord_key(zp[e])));
     any |= kp[e];
   }
   // (a weight is zero outside p's nucleus: vectors of the wave with none
@@ -450,7 +451,7 @@ __device__ __forceinline__ float draw_vec_w(const Args& a, const RowStat& P, con
     float p = kp[e] ? e_rel(zp[e], P.M, P.c) * ip : 0.0f;
     sp += p;
     if (md == 0) {
-      const float q = (id < a.Vd && kept(Q, ord_key(zq[e]))) ? e_rel(zq[e], Q.M, Q.c) * iq : 0.0f;
+      const float q = (id < a.Vd && (ALLK || kept(Q, ord_key(zq[e])))) ? e_rel(zq[e], Q.M, Q.c) * iq : 0.0f;
       p = fmaxf(p - q, 0.0f);
     }
     w[e] = p;
@@ -461,7 +462,7 @@ __device__ __forceinline__ float draw_vec_w(const Args& a, const RowStat& P, con
 
 // Totals of chunks [ch0, ch1) to ctot[ch] (BOTH, with md 0: the totals of
 // mode 1's weights too, to ctot1[ch]).  Every thread takes part.
-template <int DT, int NT, bool BOTH>
+template <int DT, int NT, bool BOTH, bool ALLK = false>
 __device__ __forceinline__ void draw_totals(const Args& a, const char* trow, const char* drow,
                                             const RowStat& P, const RowStat& Q, int md, bool pen,
                                             const uint32_t* bm, int bmlo, int ch0, int ch1, double* ctot,
@@ -482,8 +483,8 @@ __device__ __forceinline__ void draw_totals(const Args& a, const char* trow, con
         for (int u = 0; u < RU2; ++u) {
           float w[VEC];
           float sp;
-          ls += (double)draw_vec_w<DT>(a, P, Q, ip, iq, k0 + kr0 + u * WAVE + lane, md, pen, bm, bmlo, zp[u],
-                                       zq[u], w, sp);
+          ls += (double)draw_vec_w<DT, ALLK>(a, P, Q, ip, iq, k0 + kr0 + u * WAVE + lane, md, pen, bm, bmlo,
+                                             zp[u], zq[u], w, sp);
           if (BOTH) ls1 += (double)sp;
         }
         const double cs = wave_sum(ls);
@@ -536,7 +537,7 @@ __device__ __forceinline__ int draw_scan(double* ctot, int nch, float v, const E
 // The token of crossing chunk cs (t and the mass before the chunk, R): wave
 // 0 reads the chunk again and walks it; returned to every thread.  bm
 // covers the chunk's ids, from bmlo.
-template <int DT, int NT>
+template <int DT, int NT, bool ALLK = false>
 __device__ __forceinline__ int draw_resolve(const Args& a, const char* trow, const char* drow,
                                             const RowStat& P, const RowStat& Q, int mode, bool pen,
                                             const uint32_t* bm, int bmlo, int cs, double t, double R0,
@@ -560,7 +561,7 @@ __device__ __forceinline__ int draw_resolve(const Args& a, const char* trow, con
       const int k = cs * CHV + u * WAVE + lane;
       float w[VEC];
       float sp;
-      const double ls = (double)draw_vec_w<DT>(a, P, Q, ip, iq, k, mode, pen, bm, bmlo, zp[u], zq[u], w, sp);
+      const double ls = (double)draw_vec_w<DT, ALLK>(a, P, Q, ip, iq, k, mode, pen, bm, bmlo, zp[u], zq[u], w, sp);
       const double li = wave_incl_scan(ls);
       // the last token with weight so far (rounding fallback)
       const uint64_t pos = __ballot(ls > 0.0);
@@ -603,7 +604,7 @@ __device__ __forceinline__ int draw_resolve(const Args& a, const char* trow, con
 }
 
 // The whole draw in one workgroup (L.ctot holds nch + 1 doubles).
-template <int DT, int NT>
+template <int DT, int NT, bool ALLK = false>
 __device__ __forceinline__ Drawn draw_dev(const Args& a, const char* trow, const char* drow, const RowStat& P,
                           const RowStat& Q, int mode, float v, bool pen, const uint32_t* bm,
                           const ExactLds& L) {
@@ -614,7 +615,7 @@ __device__ __forceinline__ Drawn draw_dev(const Args& a, const char* trow, const
   double S = 0.0, t = 0.0;
   int cs = -1;
   for (int pass = 0; pass < 2; ++pass) {
-    draw_totals<DT, NT, false>(a, trow, drow, P, Q, mode, pen, bm, 0, 0, nch, L.ctot, nullptr);
+    draw_totals<DT, NT, false, ALLK>(a, trow, drow, P, Q, mode, pen, bm, 0, 0, nch, L.ctot, nullptr);
     __syncthreads();
     cs = draw_scan<NT>(L.ctot, nch, v, L, S, t);
     if (!(S > 0.0) && mode == 0) {   // zero residual: draw from p
@@ -625,7 +626,7 @@ __device__ __forceinline__ Drawn draw_dev(const Args& a, const char* trow, const
     break;
   }
   out.S = S;
-  out.y = draw_resolve<DT, NT>(a, trow, drow, P, Q, mode, pen, bm, 0, cs, t, L.ctot[nch], L);
+  out.y = draw_resolve<DT, NT, ALLK>(a, trow, drow, P, Q, mode, pen, bm, 0, cs, t, L.ctot[nch], L);
   return out;
 }
 
