@@ -274,8 +274,12 @@ __global__ __launch_bounds__(NT_ROW) void k_pair_tv(Args a, const RowStat* rs, d
   L.sd = sd;
   L.sf = sf;
   L.si = si;
-  const double part = pair_tv_range<DT, NT>(a, target_row(a, r, j), draft_row(a, r, j), P, Q, pen, bm,
-                                            k0 * VEC, L, k0, k1);
+  // (rows without top-p compare no key with a cut)
+  const double part =
+      P.kord == KEEP_ALL && Q.kord == KEEP_ALL
+          ? pair_tv_range<DT, NT, true>(a, target_row(a, r, j), draft_row(a, r, j), P, Q, pen, bm, k0 * VEC, L, k0,
+                                        k1)
+          : pair_tv_range<DT, NT>(a, target_row(a, r, j), draft_row(a, r, j), P, Q, pen, bm, k0 * VEC, L, k0, k1);
   if (threadIdx.x == 0) dpart[blockIdx.x] = part;
 }
 

@@ -335,8 +335,8 @@ __device__ __forceinline__ RowStat row_stats_dev(const Args& a, const char* row,
 
 // sum |p - q| over vectors [k0, k1) of the processed, truncated rows (the
 // block's total; bm covers ids from bmlo).  TV(p, q) is half the sum over
-// the whole row.
-template <int DT, int NT>
+// the whole row.  ALLK: neither row is truncated (no cut comparison).
+template <int DT, int NT, bool ALLK = false>
 __device__ __forceinline__ double pair_tv_range(const Args& a, const char* trow, const char* drow,
                                                 const RowStat& P, const RowStat& Q, bool pen,
                                                 const uint32_t* bm, int bmlo, const ExactLds& L, int k0,
@@ -365,8 +365,8 @@ __device__ __forceinline__ double pair_tv_range(const Args& a, const char* trow,
 #pragma unroll
           for (int e = 0; e < VEC; ++e) {
             const int id = k * VEC + e;
-            kp[e] = id < V && kept(P, ord_key(zp[u][e]));
-            kq[e] = id < a.Vd && kept(Q, ord_key(zq[u][e]));
+            kp[e] = id < V && (ALLK || kept(P, ord_key(zp[u][e])));
+            kq[e] = id < a.Vd && (ALLK || kept(Q, ord_key(zq[u][e])));
             any |= kp[e] | kq[e];
           }
           // (vectors of the wave outside both nuclei add zeros: skipped)
