@@ -242,7 +242,8 @@ int sd_draft_confidence(const void *draft_logits, int32_t dtype, int32_t B,
  *   [B][K_max][H_draft].  target_weight: device bf16 [V][H_target], row i
  *   the output vector of token i; draft_weight: [V_draft][H_draft].
  *   H_target and H_draft are multiples of 64; every pointer is 16-byte
- *   aligned; nothing is written to them.
+ *   aligned; nothing is written to them.  Each hidden-state array is below
+ *   2 GiB (else SD_EUNSUPPORTED).
  * V_draft (0 = V) and the draft ids, K, temperature, budget, seed, offset
  * and SD_NO_BONUS mean what they mean in sd_verify_args_t.  Greedy ignores
  * the draft fields and the temperature.

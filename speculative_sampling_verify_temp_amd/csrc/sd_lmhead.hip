@@ -224,29 +224,49 @@ struct TileLds {
   uint16_t* b;   // [TN][LDK]
 };
 
-// acc[mb][nb] = rows (64 MB) x tokens (TN) of hidden x head^T.  arow[i]:
-// this thread's A rows (tile rows t / 8 + 32 i, i < 2 MB), null for a row
-// past the list; weight rows n0 .. n0 + TN - 1 past nrows_w read 0.  Wave
+// Hidden-state rows of a tile engine call: A slot i of this thread holds
+// tile row t / 8 + 32 i (i < 2 MB); row[i] is its row of the hidden-state
+// array at base (rows of H elements, bytes in all, below 2^31), or -1 for
+// a row past the list, which reads 0.
+template <int MB>
+struct ARows {
+  const uint16_t* base;
+  uint32_t bytes;
+  int row[2 * MB];
+};
+
+// acc[mb][nb] = rows (64 MB) x tokens (TN) of hidden x head^T; weight rows
+// n0 .. n0 + TN - 1 past nrows_w read 0.  The chunk loads are buffer loads:
+// a row past the list or the head reads zeros without a memory access, and
+// every load is issued unconditionally, so the wait before a chunk's LDS
+// writes counts only that chunk's loads and the other set's stay in flight.
+// Wave
 // (wr, wc) = (wave / 2, wave % 2) holds rows 32 (MB wr + mb) + m and tokens
 // 64 wc + 32 b + n (b = 0, 1) in the MFMA 32x32 output layout: lane l, value
 // v: n = l % 32, m = 8 (v / 4) + 4 (l / 32) + v % 4.  Every logit is the
 // same K-ordered chain of MFMA steps whatever MB is, so tiles of any height
 // give the same logits bit for bit.
 template <int MB>
-__device__ __forceinline__ void tile_gemm(const uint16_t* const (&arow)[2 * MB], const uint16_t* w,
-                                          int n0, int nrows_w, int H, const TileLds& s,
-                                          f32x16 (&acc)[MB][2]) {
+__device__ __forceinline__ void tile_gemm(const ARows<MB>& ar, const uint16_t* w, int n0, int nrows_w,
+                                          int H, const TileLds& s, f32x16 (&acc)[MB][2]) {
   const int t = threadIdx.x;
   const int lane = t % WAVE, wv = t / WAVE;
   const int wr = wv >> 1, wc = wv & 1;
   const int kc = (t & 7) * 8;     // this thread's 8-element chunk of a K chunk
   const int rr = t >> 3;          // its row within a 32-row slab
-  const uint16_t* brow[4];
+  // byte offsets of the slots' rows at k = kc (a row past the end: at 2^31,
+  // beyond either resource)
+  const __amdgpu_buffer_rsrc_t rsa =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(ar.base), (short)0, (int)ar.bytes, 0x00020000);
+  const int64_t wbytes = (int64_t)max(nrows_w - n0, 0) * H * 2;
+  const __amdgpu_buffer_rsrc_t rsb = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(w + (int64_t)n0 * H), (short)0, (int)min(wbytes, (int64_t)0x7FFFFFFF), 0x00020000);
+  uint32_t aoff[2 * MB], boff[4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int n = n0 + rr + 32 * i;
-    brow[i] = n < nrows_w ? w + (int64_t)n * H : nullptr;
-  }
+  for (int i = 0; i < 2 * MB; ++i)
+    aoff[i] = ar.row[i] >= 0 ? (uint32_t)ar.row[i] * (uint32_t)H * 2u + (uint32_t)kc * 2u : 0x80000000u;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) boff[i] = (uint32_t)(rr + 32 * i) * (uint32_t)H * 2u + (uint32_t)kc * 2u;
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
@@ -258,12 +278,17 @@ __device__ __forceinline__ void tile_gemm(const uint16_t* const (&arow)[2 * MB],
   // cores (one chunk's latency is several times its MFMA work).
   uint4 ra0[2 * MB], rb0[4], ra1[2 * MB], rb1[4];
   auto load = [&](int k0, uint4 (&ra)[2 * MB], uint4 (&rb)[4]) __attribute__((always_inline)) {
+    const uint32_t kb = (uint32_t)k0 * 2u;
 #pragma unroll
-    for (int i = 0; i < 2 * MB; ++i)
-      ra[i] = arow[i] ? *reinterpret_cast<const uint4*>(arow[i] + k0 + kc) : make_uint4(0, 0, 0, 0);
+    for (int i = 0; i < 2 * MB; ++i) {
+      const auto v = __builtin_amdgcn_raw_buffer_load_b128(rsa, aoff[i] + kb, 0, 0);
+      ra[i] = make_uint4(v[0], v[1], v[2], v[3]);
+    }
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      rb[i] = brow[i] ? *reinterpret_cast<const uint4*>(brow[i] + k0 + kc) : make_uint4(0, 0, 0, 0);
+    for (int i = 0; i < 4; ++i) {
+      const auto v = __builtin_amdgcn_raw_buffer_load_b128(rsb, boff[i] + kb, 0, 0);
+      rb[i] = make_uint4(v[0], v[1], v[2], v[3]);
+    }
   };
   const int ko = 8 * (lane >> 5);
   // one K chunk: its loads to LDS, the load of the chunk two ahead into the
@@ -277,7 +302,9 @@ __device__ __forceinline__ void tile_gemm(const uint16_t* const (&arow)[2 * MB],
     for (int i = 0; i < 4; ++i)
       *reinterpret_cast<uint4*>(s.b + (rr + 32 * i) * LDK + kc) = rb[i];
     __syncthreads();
-    if (k0 + 2 * BK < H) load(k0 + 2 * BK, ra, rb);
+    // (issued every time, the last chunk again past the end, so that every
+    // wait counts the same loads)
+    load(min(k0 + 2 * BK, H - BK), ra, rb);
 #pragma unroll
     for (int st = 0; st < BK / 16; ++st) {
       bf16x8 af[MB];
@@ -295,7 +322,7 @@ __device__ __forceinline__ void tile_gemm(const uint16_t* const (&arow)[2 * MB],
     }
   };
   load(0, ra0, rb0);
-  if (BK < H) load(BK, ra1, rb1);
+  load(min(BK, H - BK), ra1, rb1);
   int k0 = 0;
   for (; k0 + BK < H; k0 += 2 * BK) {
     chunk(k0, ra0, rb0);
@@ -351,9 +378,15 @@ __device__ __forceinline__ bool tile_of(int nm, int nn, int& m, int& n) {
   return true;
 }
 
-// Hidden-state row pointer of listed row `li` (target or draft list).
-__device__ __forceinline__ const uint16_t* hidden_row(const LmArgs& a, bool target, int enc) {
-  return target ? a.th + (int64_t)enc * a.Ht : a.dh + (int64_t)enc * a.Hd;
+// The tile engine's view of the target or draft hidden states, no row yet.
+template <int MB>
+__device__ __forceinline__ ARows<MB> hidden_rows(const LmArgs& a, bool target) {
+  ARows<MB> r;
+  r.base = target ? a.th : a.dh;
+  r.bytes = (uint32_t)((int64_t)a.B * (target ? a.K_max + 1 : a.K_max) * (target ? a.Ht : a.Hd) * 2);
+#pragma unroll
+  for (int i = 0; i < 2 * MB; ++i) r.row[i] = -1;
+  return r;
 }
 
 // ---------------------------------------------------------------------------
@@ -373,15 +406,15 @@ __global__ __launch_bounds__(NT_L, 2) void k_lm_stats(LmArgs a, LmWs w, int nm, 
   if (m0 >= nrows) return;
   const int* list = TGT ? w.tlist : w.dlist;
   const int rr = threadIdx.x >> 3;
-  const uint16_t* arow[2 * MBS];
+  ARows<MBS> ar = hidden_rows<MBS>(a, TGT);
 #pragma unroll
   for (int i = 0; i < 2 * MBS; ++i) {
     const int li = m0 + rr + 32 * i;
-    arow[i] = li < nrows ? hidden_row(a, TGT, list[li]) : nullptr;
+    ar.row[i] = li < nrows ? list[li] : -1;
   }
   const int Vs = TGT ? a.V : a.Vd;
   f32x16 acc[MBS][2];
-  tile_gemm<MBS>(arow, TGT ? a.wt : a.wd, n0, Vs, TGT ? a.Ht : a.Hd, TileLds{sa, sb}, acc);
+  tile_gemm<MBS>(ar, TGT ? a.wt : a.wd, n0, Vs, TGT ? a.Ht : a.Hd, TileLds{sa, sb}, acc);
   const int nv = min(TN, Vs - n0);
   // (unrolled: each part reads its own accumulators where it stashes them)
 #pragma unroll
@@ -514,23 +547,23 @@ __global__ __launch_bounds__(NT_L) void k_lm_tv(LmArgs a, LmWs w, int nm, int nn
   TileLds s{reinterpret_cast<uint16_t*>(U), reinterpret_cast<uint16_t*>(U) + TM * LDK};
   f32x16 acc[1][2];
   {
-    const uint16_t* arow[2];
+    ARows<1> ar = hidden_rows<1>(a, true);
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       const int tli = s_tli[rr + 32 * i];
-      arow[i] = tli >= 0 ? hidden_row(a, true, w.tlist[tli]) : nullptr;
+      ar.row[i] = tli >= 0 ? w.tlist[tli] : -1;
     }
-    tile_gemm<1>(arow, a.wt, n0, a.V, a.Ht, s, acc);
+    tile_gemm<1>(ar, a.wt, n0, a.V, a.Ht, s, acc);
     stash(acc[0], Ct);
   }
   {
-    const uint16_t* arow[2];
+    ARows<1> ar = hidden_rows<1>(a, false);
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       const int p = m0 + rr + 32 * i;
-      arow[i] = p < npairs ? hidden_row(a, false, w.dlist[p]) : nullptr;
+      ar.row[i] = p < npairs ? w.dlist[p] : -1;
     }
-    tile_gemm<1>(arow, a.wd, n0, a.Vd, a.Hd, s, acc);
+    tile_gemm<1>(ar, a.wd, n0, a.Vd, a.Hd, s, acc);
   }
   __syncthreads();
   stash(acc[0], U);
@@ -650,31 +683,29 @@ __device__ __forceinline__ void draw_tiles_gemm(const LmArgs& a, const LmWs& w, 
   const int rr = threadIdx.x >> 3;
   TileLds s{reinterpret_cast<uint16_t*>(U), reinterpret_cast<uint16_t*>(U) + TM * LDK};
   {
-    const uint16_t* arow[2];
+    ARows<1> ar = hidden_rows<1>(a, true);
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       const int r = reqs[rr + 32 * i];
-      arow[i] = nullptr;
       if (r >= 0) {
         const int2 dr = w.drw[r];
-        arow[i] = hidden_row(a, true, w.tlist[w.toff[r] + dr.y]);
+        ar.row[i] = w.tlist[w.toff[r] + dr.y];
       }
     }
-    tile_gemm<1>(arow, a.wt, n0, a.V, a.Ht, s, acc);
+    tile_gemm<1>(ar, a.wt, n0, a.V, a.Ht, s, acc);
     stash(acc[0], Ct);
   }
   {
-    const uint16_t* arow[2];
+    ARows<1> ar = hidden_rows<1>(a, false);
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       const int r = reqs[rr + 32 * i];
-      arow[i] = nullptr;
       if (r >= 0) {
         const int2 dr = w.drw[r];
-        if (dr.x == 0) arow[i] = hidden_row(a, false, w.dlist[w.doff[r] + dr.y]);
+        if (dr.x == 0) ar.row[i] = w.dlist[w.doff[r] + dr.y];
       }
     }
-    tile_gemm<1>(arow, a.wd, n0, a.Vd, a.Hd, s, acc);
+    tile_gemm<1>(ar, a.wd, n0, a.Vd, a.Hd, s, acc);
   }
   __syncthreads();
   stash(acc[0], U);
@@ -858,14 +889,14 @@ __global__ __launch_bounds__(NT_L, 2) void k_lm_greedy_part(LmArgs a, LmWs w, in
   const int m0 = mb * TMS, n0 = nb * TN;
   if (m0 >= nrows) return;
   const int rr = threadIdx.x >> 3;
-  const uint16_t* arow[2 * MBS];
+  ARows<MBS> ar = hidden_rows<MBS>(a, true);
 #pragma unroll
   for (int i = 0; i < 2 * MBS; ++i) {
     const int li = m0 + rr + 32 * i;
-    arow[i] = li < nrows ? hidden_row(a, true, w.tlist[li]) : nullptr;
+    ar.row[i] = li < nrows ? w.tlist[li] : -1;
   }
   f32x16 acc[MBS][2];
-  tile_gemm<MBS>(arow, a.wt, n0, a.V, a.Ht, TileLds{sa, sb}, acc);
+  tile_gemm<MBS>(ar, a.wt, n0, a.V, a.Ht, TileLds{sa, sb}, acc);
   const int nv = min(TN, a.V - n0);
   // (unrolled: each part reads its own accumulators where it stashes them)
 #pragma unroll
@@ -960,15 +991,15 @@ __global__ __launch_bounds__(NT_L) void k_lm_dump(LmArgs a, LmWs w, int nm, int 
   if (m0 >= nrows) return;
   const int* list = TGT ? w.tlist : w.dlist;
   const int rr = threadIdx.x >> 3;
-  const uint16_t* arow[2];
+  ARows<1> ar = hidden_rows<1>(a, TGT);
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
     const int li = m0 + rr + 32 * i;
-    arow[i] = li < nrows ? hidden_row(a, TGT, list[li]) : nullptr;
+    ar.row[i] = li < nrows ? list[li] : -1;
   }
   const int Vs = TGT ? a.V : a.Vd;
   f32x16 acc[1][2];
-  tile_gemm<1>(arow, TGT ? a.wt : a.wd, n0, Vs, TGT ? a.Ht : a.Hd, TileLds{sa, sb}, acc);
+  tile_gemm<1>(ar, TGT ? a.wt : a.wd, n0, Vs, TGT ? a.Ht : a.Hd, TileLds{sa, sb}, acc);
   __syncthreads();
   stash(acc[0], C);
   __syncthreads();
@@ -991,6 +1022,8 @@ int lm_check(const sd_lmhead_args_t* s, bool sample) {
     return SD_EINVAL;
   if (s->K_max > 0 && !s->draft_ids) return SD_EINVAL;
   if ((int64_t)s->B * (s->K_max + 1) > INT_MAX / 4) return SD_EUNSUPPORTED;
+  // (the tile engine addresses a hidden-state array by 32-bit byte offsets)
+  if ((int64_t)s->B * (s->K_max + 1) * s->H_target * 2 > INT_MAX) return SD_EUNSUPPORTED;
   if ((s->flags & ~(uint32_t)SD_NO_BONUS)) return SD_EINVAL;
   if (sample) {
     if (s->V_draft < 0 || s->V_draft > s->V) return SD_EINVAL;
@@ -998,6 +1031,7 @@ int lm_check(const sd_lmhead_args_t* s, bool sample) {
     if (s->K_max > 0) {
       if (!s->draft_hidden || !s->draft_weight) return SD_EINVAL;
       if (s->H_draft < BK || s->H_draft % BK) return SD_EINVAL;
+      if ((int64_t)s->B * s->K_max * s->H_draft * 2 > INT_MAX) return SD_EUNSUPPORTED;
       if ((reinterpret_cast<uintptr_t>(s->draft_hidden) | reinterpret_cast<uintptr_t>(s->draft_weight)) & 15u)
         return SD_EINVAL;
     }
