@@ -198,3 +198,35 @@ def test_noalloc_rejects_on_host_before_touching_the_device():
     assert sdv.workspace_bytes(a) > sdv.SD_NOALLOC_MAX_WORKSPACE
     assert f(ctypes.byref(a), out, out, None, None, None) == sdv.SD_ESCRATCH
     assert "scratch" in sdv.strerror(sdv.SD_ESCRATCH)
+
+
+def _lm_args(sdv, B, K, H):
+    a = sdv.SdLmHeadArgs()
+    a.target_hidden, a.target_weight = 0x100000, 0x200000
+    a.draft_hidden, a.draft_weight = 0x300000, 0x400000
+    a.draft_ids = 0x500000
+    a.H_target = a.H_draft = H
+    a.B, a.K_max, a.V = B, K, 1000
+    return a
+
+
+def test_lmhead_rejects_bad_arguments_on_host():
+    """Every check of the LM-head calls runs on the host before any work is
+    enqueued: hidden sizes that are not multiples of 64, misaligned pointers,
+    and hidden-state arrays of 2 GiB or more (the tile engine addresses them
+    by 32-bit byte offsets)."""
+    import speculative_sampling_verify_temp_amd as sdv
+    lib = sdv.lib
+    acc = (ctypes.c_int32 * 1)()
+    call = lambda a: lib.sd_lmhead_verify_sample(ctypes.byref(a), None, 0, acc, acc, None, None, None)
+    assert call(_lm_args(sdv, 4, 2, 96)) == -1                # H not a multiple of 64
+    a = _lm_args(sdv, 4, 2, 128)
+    a.target_weight += 8
+    assert call(a) == -1                                       # misaligned
+    assert call(_lm_args(sdv, 4, 2, 128)) == sdv.SD_EWORKSPACE   # passes the checks
+    big = 1 << 20   # B (K + 1) H 2 bytes: 2^20 * 3 * 1024 * 2 > 2^31
+    assert call(_lm_args(sdv, big, 2, 1024)) == -4
+    a = _lm_args(sdv, 1 << 18, 2, 1024)   # target 1.5 GiB, draft 1 GiB: fits
+    assert call(a) == sdv.SD_EWORKSPACE
+    a.H_draft = 4096                      # draft 4 GiB
+    assert call(a) == -4
