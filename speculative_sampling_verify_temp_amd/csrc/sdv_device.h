@@ -130,19 +130,30 @@ struct RawVec {
   uint4 w[DT == SD_BF16 ? 1 : 2];
 };
 
-// Issues the loads of vector k of a row of Vr logits and returns their
-// destination registers without waiting; a vector past the row end reads
-// nothing (zero words, which unpack turns into -inf).
+// A row of Vr logits as a buffer resource over the 16-byte words that hold
+// them (ceil(Vr / 8) for bf16, ceil(Vr / 4) for fp32): loads past those
+// words return zeros and touch no memory.  row must be the same for every
+// lane of the workgroup.
 template <int DT>
-__device__ __forceinline__ RawVec<DT> load_raw(const char* row, int k, int Vr) {
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t raw_rsrc(const char* row, int Vr) {
+  const int words = DT == SD_BF16 ? (Vr + 7) / 8 : (Vr + 3) / 4;
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(row), (short)0, words * 16, 0x00020000);
+}
+
+// Issues the loads of vector k of a row (its resource from raw_rsrc) and
+// returns their destination registers without waiting; a vector past the
+// row end, or any vector when !in, reads zero words (which unpack turns
+// into -inf) without a memory access.  The loads are issued whatever k and
+// in are, so a wait for them counts exactly the loads issued after them.
+template <int DT>
+__device__ __forceinline__ RawVec<DT> load_raw(__amdgpu_buffer_rsrc_t rs, int k, bool in) {
   RawVec<DT> r;
-  const uint4* p = reinterpret_cast<const uint4*>(row);
-  const bool in = k * VEC < Vr;
-  if constexpr (DT == SD_BF16) {
-    r.w[0] = in ? p[k] : make_uint4(0, 0, 0, 0);
-  } else {
-    r.w[0] = in ? p[2 * k] : make_uint4(0, 0, 0, 0);
-    r.w[1] = (in && k * VEC + 4 < Vr) ? p[2 * k + 1] : make_uint4(0, 0, 0, 0);
+  const uint32_t off = in ? (uint32_t)k * (DT == SD_BF16 ? 16u : 32u) : 0x80000000u;
+  const auto v0 = __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0);
+  r.w[0] = make_uint4(v0[0], v0[1], v0[2], v0[3]);
+  if constexpr (DT != SD_BF16) {
+    const auto v1 = __builtin_amdgcn_raw_buffer_load_b128(rs, off + 16u, 0, 0);
+    r.w[1] = make_uint4(v1[0], v1[1], v1[2], v1[3]);
   }
   return r;
 }

@@ -109,13 +109,15 @@ template <int DT, int NT, int RUX, bool TWO, class KV, class STEP>
 __device__ __forceinline__ void stream_steps(const char* r1, int V1, const char* r2, int V2, int nvec,
                                              KV&& kv, STEP&& step) {
   RawVec<DT> a1[RUX], a2[RUX], b1[RUX], b2[RUX];
+  const __amdgpu_buffer_rsrc_t rs1 = raw_rsrc<DT>(r1, V1);
+  const __amdgpu_buffer_rsrc_t rs2 = raw_rsrc<DT>(r2, TWO ? V2 : 0);
   auto issue = [&](int base, RawVec<DT> (&x1)[RUX], RawVec<DT> (&x2)[RUX]) __attribute__((always_inline)) {
 #pragma unroll
     for (int u = 0; u < RUX; ++u) {
       const int k = kv(base, u);
       const bool in = base < nvec && k < nvec;
-      x1[u] = load_raw<DT>(r1, k, in ? V1 : 0);
-      if constexpr (TWO) x2[u] = load_raw<DT>(r2, k, in ? V2 : 0);
+      x1[u] = load_raw<DT>(rs1, k, in);
+      if constexpr (TWO) x2[u] = load_raw<DT>(rs2, k, in);
     }
   };
   auto run = [&](int base, const RawVec<DT> (&x1)[RUX], const RawVec<DT> (&x2)[RUX]) __attribute__((always_inline)) {
