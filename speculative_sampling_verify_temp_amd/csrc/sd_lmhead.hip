@@ -95,7 +95,7 @@ static_assert(sizeof(RowSL) == 32, "RowSL layout");
 
 // Workspace carve-up.
 struct LmLayout {
-  size_t cnt, toff, doff, tlist, dlist, tpart, dpart, trs, drs, tvp, dvec, drw, wpart, gpart, total;
+  size_t cnt, toff, doff, tlist, dlist, tcx, dcx, tpart, dpart, trs, drs, tvp, dvec, drw, wpart, gpart, total;
   int ntt, ntd;   // token tiles of the target and draft heads
 };
 
@@ -112,6 +112,8 @@ LmLayout lm_layout(int B, int K, int V, int Vd) {
   L.doff = o;  o = al256(o + (size_t)B * sizeof(int));
   L.tlist = o; o = al256(o + nt * sizeof(int));
   L.dlist = o; o = al256(o + (nd ? nd : 1) * sizeof(int));
+  L.tcx = o;   o = al256(o + nt * sizeof(int2));
+  L.dcx = o;   o = al256(o + (nd ? nd : 1) * sizeof(int2));
   L.tpart = o; o = al256(o + nt * L.ntt * sizeof(float2));
   L.dpart = o; o = al256(o + (nd ? nd : 1) * L.ntd * sizeof(float2));
   L.trs = o;   o = al256(o + nt * sizeof(RowSL));
@@ -131,6 +133,8 @@ struct LmWs {
   int* doff;     // per request: its first draft row in the list
   int* tlist;    // listed target rows: r (K_max + 1) + j
   int* dlist;    // listed draft rows: r K_max + j
+  int2* tcx;     // per listed target row: (bits of c = log2(e) / T, draft token x_j or -1)
+  int2* dcx;     // per listed draft row: the same
   float2* tpart; // [listed target row][token tile] (max l, sum 2^(l - max))
   float2* dpart;
   RowSL* trs;
@@ -149,6 +153,8 @@ LmWs carve(char* ws, const LmLayout& L) {
   w.doff = reinterpret_cast<int*>(ws + L.doff);
   w.tlist = reinterpret_cast<int*>(ws + L.tlist);
   w.dlist = reinterpret_cast<int*>(ws + L.dlist);
+  w.tcx = reinterpret_cast<int2*>(ws + L.tcx);
+  w.dcx = reinterpret_cast<int2*>(ws + L.dcx);
   w.tpart = reinterpret_cast<float2*>(ws + L.tpart);
   w.dpart = reinterpret_cast<float2*>(ws + L.dpart);
   w.trs = reinterpret_cast<RowSL*>(ws + L.trs);
@@ -206,8 +212,17 @@ __global__ __launch_bounds__(1024) void k_lm_lists(LmArgs a, LmWs w, int sample)
     if (r < a.B) {
       w.toff[r] = nt ? bt + et : -1;
       w.doff[r] = nd ? bd + ed : -1;
-      for (int j = 0; j < nt; ++j) w.tlist[bt + et + j] = r * (a.K_max + 1) + j;
-      for (int j = 0; j < nd; ++j) w.dlist[bd + ed + j] = r * a.K_max + j;
+      // (each row's c and draft token, for the statistics pass to load with
+      // one access before its product)
+      const int cb = __float_as_int(1.4426950408889634f / req_t(a, r));
+      for (int j = 0; j < nt; ++j) {
+        w.tlist[bt + et + j] = r * (a.K_max + 1) + j;
+        w.tcx[bt + et + j] = make_int2(cb, j < nt - 1 ? a.ids[(int64_t)r * a.K_max + j] : -1);
+      }
+      for (int j = 0; j < nd; ++j) {
+        w.dlist[bd + ed + j] = r * a.K_max + j;
+        w.dcx[bd + ed + j] = make_int2(cb, a.ids[(int64_t)r * a.K_max + j]);
+      }
     }
     __syncthreads();
     if (threadIdx.x == 0) { base_t += tot_t; base_d += tot_d; }
@@ -413,6 +428,14 @@ __global__ __launch_bounds__(NT_L, 2) void k_lm_stats(LmArgs a, LmWs w, int nm, 
     ar.row[i] = li < nrows ? list[li] : -1;
   }
   const int Vs = TGT ? a.V : a.Vd;
+  // the epilogue's (c, draft token) of this thread's row in each part,
+  // loaded now so that their latency hides behind the product
+  int2 cx[MBS];
+#pragma unroll
+  for (int p = 0; p < MBS; ++p) {
+    const int li = m0 + 64 * p + (int)(threadIdx.x >> 2);
+    cx[p] = li < nrows ? (TGT ? w.tcx : w.dcx)[li] : make_int2(__float_as_int(1.0f), -1);
+  }
   f32x16 acc[MBS][2];
   tile_gemm<MBS>(ar, TGT ? a.wt : a.wd, n0, Vs, TGT ? a.Ht : a.Hd, TileLds{sa, sb}, acc);
   const int nv = min(TN, Vs - n0);
@@ -427,16 +450,8 @@ __global__ __launch_bounds__(NT_L, 2) void k_lm_stats(LmArgs a, LmWs w, int nm, 
     const int row = threadIdx.x >> 2, q4 = threadIdx.x & 3;
     const int li = m0 + 64 * part + row;
     const bool live = li < nrows;
-    int r = 0, j = 0;
-    float c = 1.0f;
-    int x = -1;
-    if (live) {
-      const int enc = list[li];
-      r = TGT ? enc / (a.K_max + 1) : enc / a.K_max;
-      j = TGT ? enc % (a.K_max + 1) : enc % a.K_max;
-      c = 1.4426950408889634f / req_t(a, r);
-      if (j < req_k(a, r)) x = a.ids[(int64_t)r * a.K_max + j];
-    }
+    const float c = __int_as_float(cx[part].x);
+    const int x = live ? cx[part].y : -1;
     float m = -INFINITY;
     int bad = 0;
     for (int e = 0; e < 32; ++e) {
