@@ -234,6 +234,15 @@ __global__ __launch_bounds__(1024) void k_lm_lists(LmArgs a, LmWs w, int sample)
 // ---------------------------------------------------------------------------
 // The tile engine.
 // ---------------------------------------------------------------------------
+// Compile-time loop: f.template operator()<I>() for I = 0 .. N-1, so that
+// register arrays indexed by I stay in registers.
+template <int N, class F>
+__device__ __forceinline__ void unroll_for(F&& f) {
+  [&]<int... I>(std::integer_sequence<int, I...>) {
+    (f.template operator()<I>(), ...);
+  }(std::make_integer_sequence<int, N>{});
+}
+
 struct TileLds {
   uint16_t* a;   // [TM][LDK]
   uint16_t* b;   // [TN][LDK]
@@ -288,10 +297,13 @@ __device__ __forceinline__ void tile_gemm(const ARows<MB>& ar, const uint16_t* w
     for (int b = 0; b < 2; ++b)
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[mb][b][v] = 0.0f;
-  // Two register sets of chunk loads: chunk k + 2 is loaded while chunk k
-  // is multiplied, so two chunks' loads are in flight behind the matrix
-  // cores (one chunk's latency is several times its MFMA work).
-  uint4 ra0[2 * MB], rb0[4], ra1[2 * MB], rb1[4];
+  // NS register sets of chunk loads: chunk k + NS is loaded while chunk k
+  // is multiplied, so NS chunks' loads are in flight behind the matrix
+  // cores (one chunk's latency is several times its MFMA work).  Three for
+  // the 64-row tiles, whose passes stream each head tile once (their
+  // registers allow it); two for the taller tiles.
+  constexpr int NS = MB == 1 ? 3 : 2;
+  uint4 ra[NS][2 * MB], rb[NS][4];
   auto load = [&](int k0, uint4 (&ra)[2 * MB], uint4 (&rb)[4]) __attribute__((always_inline)) {
     const uint32_t kb = (uint32_t)k0 * 2u;
 #pragma unroll
@@ -306,7 +318,7 @@ __device__ __forceinline__ void tile_gemm(const ARows<MB>& ar, const uint16_t* w
     }
   };
   const int ko = 8 * (lane >> 5);
-  // one K chunk: its loads to LDS, the load of the chunk two ahead into the
+  // one K chunk: its loads to LDS, the load of the chunk NS ahead into the
   // same registers, then the products
   auto chunk = [&](int k0, uint4 (&ra)[2 * MB], uint4 (&rb)[4]) __attribute__((always_inline)) {
     __syncthreads();   // the previous chunk's fragments are read
@@ -319,7 +331,7 @@ __device__ __forceinline__ void tile_gemm(const ARows<MB>& ar, const uint16_t* w
     __syncthreads();
     // (issued every time, the last chunk again past the end, so that every
     // wait counts the same loads)
-    load(min(k0 + 2 * BK, H - BK), ra, rb);
+    load(min(k0 + NS * BK, H - BK), ra, rb);
 #pragma unroll
     for (int st = 0; st < BK / 16; ++st) {
       bf16x8 af[MB];
@@ -336,14 +348,14 @@ __device__ __forceinline__ void tile_gemm(const ARows<MB>& ar, const uint16_t* w
       }
     }
   };
-  load(0, ra0, rb0);
-  load(min(BK, H - BK), ra1, rb1);
+  unroll_for<NS>([&]<int I>() __attribute__((always_inline)) { load(min(I * BK, H - BK), ra[I], rb[I]); });
   int k0 = 0;
-  for (; k0 + BK < H; k0 += 2 * BK) {
-    chunk(k0, ra0, rb0);
-    chunk(k0 + BK, ra1, rb1);
-  }
-  if (k0 < H) chunk(k0, ra0, rb0);
+  for (; k0 + (NS - 1) * BK < H; k0 += NS * BK)
+    unroll_for<NS>([&]<int I>() __attribute__((always_inline)) { chunk(k0 + I * BK, ra[I], rb[I]); });
+  // (fewer than NS chunks left, in the sets that hold them)
+  unroll_for<NS - 1>([&]<int I>() __attribute__((always_inline)) {
+    if (k0 + I * BK < H) chunk(k0 + I * BK, ra[I], rb[I]);
+  });
 }
 
 // Rows 64 p .. 64 p + 63 of a tile of 64 MB rows into an fp32 LDS tile
