@@ -263,9 +263,8 @@ struct ARows {
 // n0 .. n0 + TN - 1 past nrows_w read 0.  The chunk loads are buffer loads:
 // a row past the list or the head reads zeros without a memory access, and
 // every load is issued unconditionally, so the wait before a chunk's LDS
-// writes counts only that chunk's loads and the other set's stay in flight.
-// Wave
-// (wr, wc) = (wave / 2, wave % 2) holds rows 32 (MB wr + mb) + m and tokens
+// writes counts only that chunk's loads and the other sets' stay in flight.
+// Wave (wr, wc) = (wave / 2, wave % 2) holds rows 32 (MB wr + mb) + m and tokens
 // 64 wc + 32 b + n (b = 0, 1) in the MFMA 32x32 output layout: lane l, value
 // v: n = l % 32, m = 8 (v / 4) + 4 (l / 32) + v % 4.  Every logit is the
 // same K-ordered chain of MFMA steps whatever MB is, so tiles of any height
