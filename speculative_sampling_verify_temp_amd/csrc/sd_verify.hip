@@ -43,6 +43,7 @@ namespace {
 constexpr int NT_ROW = 512;                  // general-path row kernels
 constexpr int NT_G = 256;                    // greedy partial kernel
 constexpr int G_SLICE = 8192;                // logits per greedy workgroup
+static_assert(G_SLICE % (8 * NT_G) == 0, "greedy slice geometry");
 constexpr int MAX_V = 1 << 19;
 
 __device__ __forceinline__ int row_index(const Args& a, int r, bool target, int j) {
@@ -2726,13 +2727,28 @@ __global__ __launch_bounds__(NT_G) void k_greedy_partial(Args a, GPart* parts, i
   if (K < 0 || K > a.K_max || j > K) return;
   const int V = a.V, lo = s * G_SLICE, hi = min(V, lo + G_SLICE);
   const char* row = target_row(a, r, j);
+  const int k0 = lo / VEC, k1 = (hi + VEC - 1) / VEC;
+  // every vector of the thread's share is requested at once, before the
+  // penalty bitmap is built (buffer loads issued whatever the range; a
+  // vector past the slice reads nothing), so the slice costs one memory
+  // latency instead of one per vector
+  constexpr int GU = G_SLICE / VEC / NT;
+  const __amdgpu_buffer_rsrc_t rs = raw_rsrc<DT>(row, V);
+  RawVec<DT> rv[GU];
+#pragma unroll
+  for (int u = 0; u < GU; ++u) {
+    const int k = k0 + (int)threadIdx.x + u * NT;
+    rv[u] = load_raw<DT>(rs, k, k < k1);
+  }
   const bool pen = build_penalty_bitmap<NT>(a, r, j, lo, G_SLICE, bm);
   uint32_t bo = 0;
   int bi = INT_MAX, nan = 0;
-  const int k0 = lo / VEC, k1 = (hi + VEC - 1) / VEC;
-  for (int k = k0 + threadIdx.x; k < k1; k += NT) {
+#pragma unroll
+  for (int u = 0; u < GU; ++u) {
+    const int k = k0 + (int)threadIdx.x + u * NT;
+    if (k >= k1) break;
     float z[VEC];
-    load8<DT>(row, k, V, z);
+    unpack<DT>(rv[u], k, V, z);
     if (pen) apply_penalty8(bm, k, lo, a.rep, z);
 #pragma unroll
     for (int e = 0; e < VEC; ++e) {
