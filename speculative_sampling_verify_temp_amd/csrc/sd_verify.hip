@@ -2784,48 +2784,69 @@ __global__ __launch_bounds__(64) void k_greedy_final(Args a, const GPart* parts,
                                                      int32_t* out_acc, int32_t* out_tok,
                                                      uint32_t* out_status, int32_t* out_argmax) {
   constexpr int NT = 64;
+  static_assert(NT == WAVE && SD_MAX_K + 1 <= NT, "one wave per request, one lane per position");
   __shared__ int g[SD_MAX_K + 1];
   __shared__ int si[NT / WAVE + 4];
   const int r = blockIdx.x;
   const int K1 = a.K_max + 1;
   const int K = request_k(a, r);
   uint32_t st = request_status<NT>(a, r, K, 1.0f, false, si);
-  int nan = 0;
-  if (!(st & SD_ST_INVALID_MASK) && (int)threadIdx.x <= K) {
-    const int jj = threadIdx.x;
+  // Lane jj <= K reduces position jj's slice partials (the order of the
+  // reduction does not matter: larger key, then lower id) and compares the
+  // argmax with the draft token it loaded beforehand; the first mismatch is
+  // the first set bit of a ballot, so no lane waits on a chain of loads.
+  const int jj = threadIdx.x;
+  int nan = 0, mism = 0, idv = -1;
+  if (!(st & SD_ST_INVALID_MASK) && jj <= K) {
+    if (jj < K) idv = a.ids[(int64_t)r * a.K_max + jj];
+    const GPart* pj = parts + ((int64_t)r * K1 + jj) * ns;
     uint32_t bo = 0;
     int bi = INT_MAX;
-    for (int s = 0; s < ns; ++s) {
-      const GPart p = parts[((int64_t)r * K1 + jj) * ns + s];
+    int s = 0;
+    for (; s + 4 <= ns; s += 4) {
+      GPart p[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) p[u] = pj[s + u];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        nan |= (int)p[u].nan;
+        if (better(p[u].ord, p[u].id, bo, bi)) { bo = p[u].ord; bi = p[u].id; }
+      }
+    }
+    for (; s < ns; ++s) {
+      const GPart p = pj[s];
       nan |= (int)p.nan;
       if (better(p.ord, p.id, bo, bi)) { bo = p.ord; bi = p.id; }
     }
     g[jj] = bi;
+    mism = jj < K && idv != bi;
   }
-  if (block_or<NT>(nan, si)) st |= SD_ST_NONFINITE;
-  if (threadIdx.x != 0) return;
+  if (block_or<NT>(nan, si)) st |= SD_ST_NONFINITE;   // (its barrier also publishes g)
   const int64_t base = (int64_t)r * K1;
   if (st & SD_ST_INVALID_MASK) {
-    for (int t = 0; t < K1; ++t) {
-      out_tok[base + t] = -1;
-      if (out_argmax) out_argmax[base + t] = -1;
+    if (jj < K1) {
+      out_tok[base + jj] = -1;
+      if (out_argmax) out_argmax[base + jj] = -1;
     }
-    out_acc[r] = -1;
-    if (out_status) out_status[r] = st;
+    if (jj == 0) {
+      out_acc[r] = -1;
+      if (out_status) out_status[r] = st;
+    }
     return;
   }
-  int n = K;
-  for (int jj = 0; jj < K; ++jj)
-    if (a.ids[(int64_t)r * a.K_max + jj] != g[jj]) { n = jj; break; }
-  for (int t = 0; t < K1; ++t) {
+  const uint64_t mm = __ballot(mism != 0);
+  const int n = mm ? __builtin_ctzll(mm) : K;
+  if (jj < K1) {
     int v = -1;
-    if (t < n) v = a.ids[(int64_t)r * a.K_max + t];
-    else if (t == n && !(n == K && (a.flags & SD_NO_BONUS))) v = g[n];
-    out_tok[base + t] = v;
-    if (out_argmax) out_argmax[base + t] = (t <= K) ? g[t] : -1;
+    if (jj < n) v = idv;
+    else if (jj == n && !(n == K && (a.flags & SD_NO_BONUS))) v = g[n];
+    out_tok[base + jj] = v;
+    if (out_argmax) out_argmax[base + jj] = (jj <= K) ? g[jj] : -1;
   }
-  out_acc[r] = n;
-  if (out_status) out_status[r] = st;
+  if (jj == 0) {
+    out_acc[r] = n;
+    if (out_status) out_status[r] = st;
+  }
 }
 
 // ---------------------------------------------------------------------------
