@@ -2585,6 +2585,7 @@ __global__ __launch_bounds__(64) void k_fast_finalize(Args a, const UnitOut* uo,
                                                       int32_t* out_tok, uint32_t* out_status,
                                                       float* out_stats) {
   constexpr int NT = 64;
+  static_assert(NT == WAVE && SD_MAX_K + 1 <= NT, "one wave per request, one lane per position");
   __shared__ int si[NT / WAVE + 4];
   const int r = blockIdx.x;
   const int K1 = a.K_max + 1;
@@ -2592,64 +2593,69 @@ __global__ __launch_bounds__(64) void k_fast_finalize(Args a, const UnitOut* uo,
   const float T = request_t(a, r);
   uint32_t st = request_status<NT>(a, r, K, T, true, si);
   const int64_t bonus_idx = (int64_t)a.B * a.K_max + r;
-  int nonfin = 0;
-  // (units of a request with an invalidating bit may hold no record of this
-  // call: k_pair_fast skips requests with a bad K, temperature or parameter)
-  if (!(st & SD_ST_INVALID_MASK)) {
-    for (int t = threadIdx.x; t < K; t += NT)
-      nonfin |= (uo[(int64_t)r * a.K_max + t].flags & UO_NONFINITE) ? 1 : 0;
-    if (threadIdx.x == 0) nonfin |= (uo[bonus_idx].flags & UO_NONFINITE) ? 1 : 0;
+  // Lane jj < K holds pair jj's record and draft token, lane K the bonus
+  // row's record, all loaded at once; the first rejection is the first bit
+  // of a ballot and the drawn token comes from its lane.  (Units of a
+  // request with an invalidating bit may hold no record of this call:
+  // k_pair_fast skips requests with a bad K, temperature or parameter.)
+  const int jj = threadIdx.x;
+  UnitOut o;
+  o.d = o.th = o.px = o.qx = o.pix = o.u = o.v = o.S = 0.0f;
+  o.accept = 1;
+  o.y = -1;
+  o.flags = o.why = 0u;
+  int idv = -1;
+  if (!(st & SD_ST_INVALID_MASK) && jj <= K) {
+    o = uo[jj < K ? (int64_t)r * a.K_max + jj : bonus_idx];
+    if (jj < K) idv = a.ids[(int64_t)r * a.K_max + jj];
   }
-  if (block_or<NT>(nonfin, si)) st |= SD_ST_NONFINITE;
+  if (block_or<NT>((o.flags & UO_NONFINITE) ? 1 : 0, si)) st |= SD_ST_NONFINITE;
   const int64_t base = (int64_t)r * K1;
   if (st & SD_ST_INVALID_MASK) {
-    for (int t = threadIdx.x; t < K1; t += NT) out_tok[base + t] = -1;
-    if (out_stats)
-      for (int t = threadIdx.x; t < K1 * SD_NSTAT; t += NT) out_stats[base * SD_NSTAT + t] = 0.0f;
-    if (threadIdx.x == 0) {
+    if (jj < K1) {
+      out_tok[base + jj] = -1;
+      if (out_stats)
+        for (int s = 0; s < SD_NSTAT; ++s) out_stats[(base + jj) * SD_NSTAT + s] = 0.0f;
+    }
+    if (jj == 0) {
       out_acc[r] = -1;
       if (out_status) out_status[r] = st;
     }
     return;
   }
-  if (threadIdx.x != 0) return;
-  int n = K;
-  for (int jj = 0; jj < K; ++jj) {
-    const UnitOut& o = uo[(int64_t)r * a.K_max + jj];
-    if (o.flags & UO_QZERO) st |= SD_ST_Q_ZERO;
-    if (n == K && !o.accept) n = jj;
-  }
+  if (__any(jj < K && (o.flags & UO_QZERO))) st |= SD_ST_Q_ZERO;
+  const uint64_t rej = __ballot(jj < K && !o.accept);
+  const int n = rej ? __builtin_ctzll(rej) : K;
+  const int y = __shfl(o.y, n);
+  const float S = __shfl(o.S, n);
+  if (n < K && (__shfl((int)o.flags, n) & UO_RESID_ZERO)) st |= SD_ST_RESID_ZERO;
   const bool emit = !(n == K && (a.flags & SD_NO_BONUS));
-  const UnitOut& src = (n < K) ? uo[(int64_t)r * a.K_max + n] : uo[bonus_idx];
-  if (n < K && (src.flags & UO_RESID_ZERO)) st |= SD_ST_RESID_ZERO;
-  for (int t = 0; t < K1; ++t) {
-    int v = -1;
-    if (t < n) v = a.ids[(int64_t)r * a.K_max + t];
-    else if (t == n && emit) v = src.y;
-    out_tok[base + t] = v;
-  }
-  if (out_stats) {
-    for (int t = 0; t < K1; ++t) {
-      float* sv = out_stats + (base + t) * SD_NSTAT;
+  if (jj < K1) {
+    out_tok[base + jj] = jj < n ? idv : (jj == n && emit) ? y : -1;
+    if (out_stats) {
+      float sv[SD_NSTAT];
+#pragma unroll
       for (int s = 0; s < SD_NSTAT; ++s) sv[s] = 0.0f;
-      if (t < K) {
-        const UnitOut& o = uo[(int64_t)r * a.K_max + t];
+      if (jj < K) {
         sv[SD_STAT_D] = o.d;
         sv[SD_STAT_THETA] = o.th;
         sv[SD_STAT_PX] = o.px;
         sv[SD_STAT_QX] = o.qx;
         sv[SD_STAT_PIX] = o.pix;
+      }
+      if (jj <= K) {
         sv[SD_STAT_U] = o.u;
         sv[SD_STAT_V] = o.v;
-      } else if (t == K) {
-        sv[SD_STAT_U] = uo[bonus_idx].u;
-        sv[SD_STAT_V] = uo[bonus_idx].v;
       }
-      if (t == n && emit) sv[SD_STAT_S] = src.S;
+      if (jj == n && emit) sv[SD_STAT_S] = S;
+#pragma unroll
+      for (int s = 0; s < SD_NSTAT; ++s) out_stats[(base + jj) * SD_NSTAT + s] = sv[s];
     }
   }
-  out_acc[r] = n;
-  if (out_status) out_status[r] = st;
+  if (jj == 0) {
+    out_acc[r] = n;
+    if (out_status) out_status[r] = st;
+  }
 }
 
 // ---------------------------------------------------------------------------
