@@ -17,7 +17,8 @@
 //   k_lm_tv         per (pair, tile): sum |p - q| (target and draft tiles
 //                   of the same pair in one workgroup), only when a budget
 //                   strictly between 0 and 1 needs d
-//   k_lm_decide     per request: theta, pi(x), acceptance, first rejection
+//   k_lm_decide     per request (one lane per position): theta, pi(x),
+//                   acceptance, first rejection
 //   k_lm_draw_tiles per (request, tile): fixed-point totals of the draw
 //                   weights (the residual max(p - q, 0) and p)
 //   k_lm_draw_pick  per request: the crossing tile, recomputed, scanned
@@ -630,39 +631,48 @@ __device__ __forceinline__ double prob_x(const RowSL& s) {
   return exp2((double)s.zx * (double)s.c - (double)s.M) / s.Z;
 }
 
-// Decisions of one request: one thread per request.
+// Decisions of one request: one wave per request, lane jj for position jj
+// (its uniforms, p(x), q(x), d and acceptance); the first rejection is the
+// first bit of a ballot.
 __global__ __launch_bounds__(64) void k_lm_decide(LmArgs a, LmWs w, int tv_valid, int32_t* out_acc,
                                                   int32_t* out_tok, uint32_t* out_status,
                                                   float* out_stats) {
-  const int r = blockIdx.x * 64 + threadIdx.x;
-  if (r >= a.B) return;
+  static_assert(WAVE == 64 && SD_MAX_K + 1 <= WAVE, "one lane per position");
+  const int r = blockIdx.x;
+  const int jj = threadIdx.x;
   const int K1 = a.K_max + 1;
   const int64_t base = (int64_t)r * K1;
   uint32_t st = lm_status(a, r, true);
   const int K = st ? 0 : req_k(a, r);
-  int n = K;
+  int nonf = 0;
   if (!st) {
     const int t0 = w.toff[r], d0 = w.doff[r];
-    for (int jj = 0; jj <= K; ++jj)
-      if (w.trs[t0 + jj].flags) st |= SD_ST_NONFINITE;
-    for (int jj = 0; jj < K; ++jj)
-      if (w.drs[d0 + jj].flags) st |= SD_ST_NONFINITE;
+    if (jj <= K && w.trs[t0 + jj].flags) nonf = 1;
+    if (jj < K && w.drs[d0 + jj].flags) nonf = 1;
   }
+  if (__any(nonf)) st |= SD_ST_NONFINITE;
   if (st & SD_ST_INVALID_MASK) {
-    for (int t = 0; t < K1; ++t) out_tok[base + t] = -1;
-    if (out_stats)
-      for (int t = 0; t < K1 * SD_NSTAT; ++t) out_stats[base * SD_NSTAT + t] = 0.0f;
-    out_acc[r] = -1;
-    if (out_status) out_status[r] = st;
-    w.drw[r] = make_int2(-1, 0);
+    if (jj < K1) {
+      out_tok[base + jj] = -1;
+      if (out_stats)
+        for (int s2 = 0; s2 < SD_NSTAT; ++s2) out_stats[(base + jj) * SD_NSTAT + s2] = 0.0f;
+    }
+    if (jj == 0) {
+      out_acc[r] = -1;
+      if (out_status) out_status[r] = st;
+      w.drw[r] = make_int2(-1, 0);
+    }
     return;
   }
-  const int t0 = w.toff[r], d0 = w.doff[r];
-  for (int jj = 0; jj <= K; ++jj) {
+  float sv[SD_NSTAT] = {0, 0, 0, 0, 0, 0, 0, 0};
+  bool acc = true, qzero = false;
+  if (jj <= K) {
     float u, v;
     uniforms(a.seed, a.offset, r, jj, u, v);
-    float sv[SD_NSTAT] = {0, 0, 0, 0, 0, u, v, 0};
+    sv[SD_STAT_U] = u;
+    sv[SD_STAT_V] = v;
     if (jj < K) {
+      const int t0 = w.toff[r], d0 = w.doff[r];
       const double px = prob_x(w.trs[t0 + jj]);
       const double qx = prob_x(w.drs[d0 + jj]);
       const double d = tv_valid ? w.dvec[d0 + jj] : 0.0;
@@ -670,26 +680,29 @@ __global__ __launch_bounds__(64) void k_lm_decide(LmArgs a, LmWs w, int tv_valid
       if (tv_valid) th = (d <= (double)a.D) ? 1.0 : (double)a.D / d;
       else th = (a.D >= 1.0f) ? 1.0 : 0.0;   // D = 0: theta matters only where p = q
       const double pix = (1.0 - th) * px + th * qx;
-      const bool acc = (double)u * qx < pix;
-      if (qx == 0.0) st |= SD_ST_Q_ZERO;
+      acc = (double)u * qx < pix;
+      qzero = qx == 0.0;
       sv[SD_STAT_D] = (float)d;
       sv[SD_STAT_THETA] = (float)th;
       sv[SD_STAT_PX] = (float)px;
       sv[SD_STAT_QX] = (float)qx;
       sv[SD_STAT_PIX] = (float)pix;
-      if (n == K && !acc) n = jj;
     }
+  }
+  if (__any(qzero)) st |= SD_ST_Q_ZERO;
+  const uint64_t rej = __ballot(jj < K && !acc);
+  const int n = rej ? __builtin_ctzll(rej) : K;
+  if (jj < K1) {
     if (out_stats)
       for (int s2 = 0; s2 < SD_NSTAT; ++s2) out_stats[(base + jj) * SD_NSTAT + s2] = sv[s2];
+    out_tok[base + jj] = jj < n ? a.ids[(int64_t)r * a.K_max + jj] : -1;
   }
-  if (out_stats)
-    for (int t = K + 1; t < K1; ++t)
-      for (int s2 = 0; s2 < SD_NSTAT; ++s2) out_stats[(base + t) * SD_NSTAT + s2] = 0.0f;
-  const bool emit = !(n == K && (a.flags & SD_NO_BONUS));
-  for (int t = 0; t < K1; ++t) out_tok[base + t] = t < n ? a.ids[(int64_t)r * a.K_max + t] : -1;
-  out_acc[r] = n;
-  if (out_status) out_status[r] = st;
-  w.drw[r] = make_int2(emit ? (n < K ? 0 : 1) : -1, n);
+  if (jj == 0) {
+    const bool emit = !(n == K && (a.flags & SD_NO_BONUS));
+    out_acc[r] = n;
+    if (out_status) out_status[r] = st;
+    w.drw[r] = make_int2(emit ? (n < K ? 0 : 1) : -1, n);
+  }
 }
 
 // Draw weights of one token: residual max(p - q, 0) (mode 0) and p.
@@ -1147,7 +1160,7 @@ int sd_lmhead_verify_sample(const sd_lmhead_args_t* args, void* workspace, size_
     hipLaunchKernelGGL(k_lm_tv, dim3(tile_grid(nmd, L.ntt)), dim3(NT_L), 0, st, a, w, nmd, L.ntt);
     hipLaunchKernelGGL(k_lm_tv_reduce, dim3(nd_max), dim3(256), 0, st, w, L.ntt);
   }
-  hipLaunchKernelGGL(k_lm_decide, dim3((a.B + 63) / 64), dim3(64), 0, st, a, w, tv ? 1 : 0,
+  hipLaunchKernelGGL(k_lm_decide, dim3(a.B), dim3(64), 0, st, a, w, tv ? 1 : 0,
                      out_accepted, out_tokens, out_status, out_stats);
   const int nmr = (a.B + TM - 1) / TM;
   hipLaunchKernelGGL(k_lm_draw_tiles, dim3(tile_grid(nmr, L.ntt)), dim3(NT_L), 0, st, a, w, nmr, L.ntt);
