@@ -968,50 +968,68 @@ __global__ __launch_bounds__(NT_L, 2) void k_lm_greedy_part(LmArgs a, LmWs w, in
   }
 }
 
+// One wave per request: for each position, the lanes reduce the tile
+// partials (larger key, then lower id: any order gives the same result),
+// lane jj keeps position jj's argmax, and the first mismatch with the draft
+// tokens is the first bit of a ballot.
 __global__ __launch_bounds__(64) void k_lm_greedy_final(LmArgs a, LmWs w, int nn, int32_t* out_acc,
                                                         int32_t* out_tok, uint32_t* out_status,
                                                         int32_t* out_argmax) {
-  const int r = blockIdx.x * 64 + threadIdx.x;
-  if (r >= a.B) return;
+  static_assert(WAVE == 64 && SD_MAX_K + 1 <= WAVE, "one lane per position");
+  const int r = blockIdx.x;
+  const int lane = threadIdx.x;
   const int K1 = a.K_max + 1;
   const int64_t base = (int64_t)r * K1;
   uint32_t st = lm_status(a, r, false);
   const int K = st ? 0 : req_k(a, r);
-  int g[SD_MAX_K + 1];
+  int myg = INT_MAX;
   if (!st) {
     const int t0 = w.toff[r];
     for (int jj = 0; jj <= K; ++jj) {
+      const uint2* pj = w.gpart + (int64_t)(t0 + jj) * nn;
       uint32_t bo = 0u;
-      int bi = INT_MAX;
-      for (int t = 0; t < nn; ++t) {
-        const uint2 p = w.gpart[(int64_t)(t0 + jj) * nn + t];
-        if (p.x == 0xFFFFFFFFu) { st |= SD_ST_NONFINITE; continue; }
+      int bi = INT_MAX, nan = 0;
+      for (int t = lane; t < nn; t += WAVE) {
+        const uint2 p = pj[t];
+        if (p.x == 0xFFFFFFFFu) { nan = 1; continue; }
         if (p.x > bo || (p.x == bo && (int)p.y < bi)) { bo = p.x; bi = (int)p.y; }
       }
-      g[jj] = bi;
+#pragma unroll
+      for (int off = WAVE / 2; off > 0; off >>= 1) {
+        const uint32_t o2 = __shfl_xor(bo, off);
+        const int i2 = __shfl_xor(bi, off);
+        if (o2 > bo || (o2 == bo && i2 < bi)) { bo = o2; bi = i2; }
+      }
+      if (__any(nan)) st |= SD_ST_NONFINITE;
+      if (lane == jj) myg = bi;
     }
   }
   if (st & SD_ST_INVALID_MASK) {
-    for (int t = 0; t < K1; ++t) {
-      out_tok[base + t] = -1;
-      if (out_argmax) out_argmax[base + t] = -1;
+    if (lane < K1) {
+      out_tok[base + lane] = -1;
+      if (out_argmax) out_argmax[base + lane] = -1;
     }
-    out_acc[r] = -1;
-    if (out_status) out_status[r] = st;
+    if (lane == 0) {
+      out_acc[r] = -1;
+      if (out_status) out_status[r] = st;
+    }
     return;
   }
-  int n = K;
-  for (int jj = 0; jj < K; ++jj)
-    if (a.ids[(int64_t)r * a.K_max + jj] != g[jj]) { n = jj; break; }
-  for (int t = 0; t < K1; ++t) {
+  const int idv = lane < K ? a.ids[(int64_t)r * a.K_max + lane] : -1;
+  const uint64_t mis = __ballot(lane < K && idv != myg);
+  const int n = mis ? __builtin_ctzll(mis) : K;
+  const int gn = __shfl(myg, n);
+  if (lane < K1) {
     int v = -1;
-    if (t < n) v = a.ids[(int64_t)r * a.K_max + t];
-    else if (t == n && !(n == K && (a.flags & SD_NO_BONUS))) v = g[n];
-    out_tok[base + t] = v;
-    if (out_argmax) out_argmax[base + t] = t <= K ? g[t] : -1;
+    if (lane < n) v = idv;
+    else if (lane == n && !(n == K && (a.flags & SD_NO_BONUS))) v = gn;
+    out_tok[base + lane] = v;
+    if (out_argmax) out_argmax[base + lane] = lane <= K ? myg : -1;
   }
-  out_acc[r] = n;
-  if (out_status) out_status[r] = st;
+  if (lane == 0) {
+    out_acc[r] = n;
+    if (out_status) out_status[r] = st;
+  }
 }
 
 // Test export: the logits of every listed row, written densely.
@@ -1184,7 +1202,7 @@ int sd_lmhead_verify_greedy(const sd_lmhead_args_t* args, void* workspace, size_
   if (rc) return rc;
   const int nmt = (a.B * (a.K_max + 1) + TMS - 1) / TMS;
   hipLaunchKernelGGL(k_lm_greedy_part, dim3(tile_grid(nmt, L.ntt)), dim3(NT_L), 0, st, a, w, nmt, L.ntt);
-  hipLaunchKernelGGL(k_lm_greedy_final, dim3((a.B + 63) / 64), dim3(64), 0, st, a, w, L.ntt,
+  hipLaunchKernelGGL(k_lm_greedy_final, dim3(a.B), dim3(64), 0, st, a, w, L.ntt,
                      out_accepted, out_tokens, out_status, out_argmax);
   return lm_launch_status();
 }
